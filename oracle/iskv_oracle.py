@@ -1,0 +1,405 @@
+"""Literal CPU oracle of the iS-KV hot path (test infrastructure only).
+
+Only tests, the smoke check and the benchmark's CPU-baseline leg may use this
+module; the GPU path never does.
+
+Source: Zhongzhu Zhou, reading notes on "iS-KV: Online Low-Rank KV Cache
+Compression via Block-Incremental SVD" ("iS-KV notes" below). Symbols follow
+the notes: the compressed history of one (layer, K-or-V) path is
+U diag(sigma) B^T with U (n x k) and B (D x k) having orthonormal columns,
+k <= r; a pending exact block F (b x D) is folded in by Algorithm 2.
+
+Readings where the notes are silent or their formulas were lost:
+  * residual threshold: keep rho_j > tau with
+    tau = max(delta * s, max(D, b) * eps * s), s = max(sigma_1, rho_1),
+    eps = 2**-23 (machine epsilon of the FP32 compute precision, §4.4), delta
+    defaults to 0; p is capped at min(b, D - k);
+  * ties between equal singular values are broken by LAPACK's order;
+  * RoPE pairs feature j with j + d_h/2 inside each head, angle
+    pos * theta**(-2j/d_h), no frequency scaling;
+  * attention applies no causal mask at decode; query head h reads KV head
+    floor(h / (H_q / H_kv)); queries arrive already rotated.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = [
+    "EPS_FP32",
+    "Factor",
+    "empty_factor",
+    "merge",
+    "reorth",
+    "represented",
+    "stored_rows",
+    "fresh_truncated_svd",
+    "rope",
+    "bf16_round",
+    "reconstruct",
+    "attend",
+    "persistent_bytes",
+    "breakeven_rows",
+    "dense_kv_bytes",
+    "factor_drift",
+    "one_step_drift",
+    "run_stream",
+]
+
+# Machine epsilon of FP32, the compute precision of the update (iS-KV notes §4.4).
+EPS_FP32 = 2.0 ** -23
+
+
+@dataclass
+class Factor:
+    """One compressed path: history rows approximated by U diag(sigma) B^T.
+
+    iS-KV notes §2.2: U (n x k) holds one row of coordinates per token, B
+    (D x k) is the shared dictionary, sigma the k singular values, k <= r.
+    ``pos`` keeps each row's original token position (§3.2, Algorithm 3).
+    ``folded`` counts regular folded rows for the re-orthogonalisation
+    schedule (§4.4). ``C_stale`` is set only in the basis-only ablation
+    (§2.3): the stored coordinates of old rows are then never rewritten.
+    """
+
+    U: np.ndarray
+    sigma: np.ndarray
+    B: np.ndarray
+    pos: np.ndarray
+    folded: int = 0
+    C_stale: np.ndarray | None = None
+    dtype: type = np.float64
+
+    @property
+    def n(self) -> int:
+        return self.U.shape[0]
+
+    @property
+    def k(self) -> int:
+        return self.sigma.shape[0]
+
+    @property
+    def D(self) -> int:
+        return self.B.shape[0]
+
+
+def empty_factor(D: int, dtype=np.float64, sync: bool = True) -> Factor:
+    """An empty history (n = k = 0)."""
+    return Factor(U=np.zeros((0, 0), dtype), sigma=np.zeros((0,), dtype),
+                  B=np.zeros((D, 0), dtype), pos=np.zeros((0,), np.int64), folded=0,
+                  C_stale=None if sync else np.zeros((0, 0), dtype), dtype=dtype)
+
+
+def _svd(a):
+    u, s, vt = np.linalg.svd(a, full_matrices=False)
+    return u, s, vt
+
+
+def merge(fac: Factor, F: np.ndarray, pos_F, r: int, delta: float = 0.0,
+          diag: dict | None = None) -> Factor:
+    """Fold one pending exact block F (b x D) into the history (Algorithm 2).
+
+    iS-KV notes §4.1-§4.2 and Algorithm 2:
+      * empty history: the rank-r truncated SVD of F;
+      * project onto the old basis, Q = F B, residual E = F - Q B^T, and
+        subtract E's leftover component along B once more;
+      * reduced QR of E^T = P_E R_E, SVD R_E = W diag(rho) V_E^T, keep the
+        residual directions above the threshold: P = P_E W[:, :p];
+        no residual directions when E = 0 or k = D;
+      * core Z = [[diag(sigma), 0], [F B, F P]] of size (k+b) x (k+p), eq.(7);
+      * truncated SVD of the core, Z ~ G diag(sigma+) H^T, keep r' = min(r, k+p);
+      * old rows U <- U G_top, new rows G_bot, B+ = [B, P] H.
+    The basis-only ablation (§2.3, eq.(3)) keeps the old rows' stored
+    coordinates instead of rewriting them.
+    """
+    dt = fac.dtype
+    F = np.asarray(F).astype(dt)
+    b, D = F.shape
+    assert D == fac.D
+    pos_F = np.asarray(pos_F, dtype=np.int64).reshape(b)
+    k = fac.k
+    sync = fac.C_stale is None
+
+    if k == 0:
+        # Empty history: the rank-r truncated SVD of F (Algorithm 2, first case).
+        G, s, Vt = _svd(F)
+        rp = min(r, s.shape[0])
+        U_new = G[:, :rp]
+        sig_new = s[:rp]
+        B_new = Vt[:rp].T
+        if diag is not None:
+            diag.update(dict(p=None, empty=True, s_plus=s, r_prime=rp))
+        C_stale = None if sync else (U_new * sig_new[None, :])
+        return Factor(U=U_new.astype(dt), sigma=sig_new.astype(dt), B=B_new.astype(dt),
+                      pos=pos_F.copy(), folded=fac.folded + b, C_stale=C_stale, dtype=dt)
+
+    B = fac.B
+    # Projection and residual, with the second subtraction of the leftover
+    # component along B (§4.1).
+    Q = F @ B
+    E = F - Q @ B.T
+    E = E - (E @ B) @ B.T
+
+    normE = np.linalg.norm(E)
+    if k >= D or normE == 0.0:
+        p = 0
+        P = np.zeros((D, 0), dt)
+        rho = np.zeros((0,), dt)
+        tau = 0.0
+    else:
+        PE, RE = np.linalg.qr(E.T, mode="reduced")          # E^T = P_E R_E
+        W, rho, _VEt = _svd(RE)                              # R_E = W diag(rho) V_E^T
+        s_scale = max(float(fac.sigma[0]) if k > 0 else 0.0, float(rho[0]))
+        tau = max(delta * s_scale, max(D, b) * EPS_FP32 * s_scale)
+        p = int(np.count_nonzero(rho > tau))
+        p = min(p, b, D - k)
+        P = PE @ W[:, :p]
+
+    FP = F @ P
+    Z = np.zeros((k + b, k + p), dt)
+    Z[:k, :k] = np.diag(fac.sigma)
+    Z[k:, :k] = Q
+    Z[k:, k:] = FP
+
+    G, s_plus, Ht = _svd(Z)
+    # Sign convention (the notes leave it open): each singular pair whose index
+    # is an old direction is oriented so that H[j, j] >= 0, i.e. the basis
+    # moves continuously. The synced product does not depend on it; the
+    # basis-only ablation does.
+    for j in range(min(k, Ht.shape[0])):
+        if Ht[j, j] < 0:
+            Ht[j] = -Ht[j]
+            G[:, j] = -G[:, j]
+    rp = min(r, k + p)
+    Hc = Ht[:rp].T                      # (k+p) x r'
+    G_top = G[:k, :rp]
+    G_bot = G[k:, :rp]
+    sig_new = s_plus[:rp]
+
+    U_new = np.vstack([fac.U @ G_top, G_bot])
+    B_new = np.hstack([B, P]) @ Hc
+
+    C_stale = None
+    if not sync:
+        # Basis-only ablation: old rows keep their stored coordinates, padded
+        # with zero columns when the rank grows; new rows get G_bot diag(sigma+).
+        old = fac.C_stale
+        pad = np.zeros((old.shape[0], rp), dt)
+        w = min(rp, old.shape[1])
+        pad[:, :w] = old[:, :w]
+        C_stale = np.vstack([pad, G_bot * sig_new[None, :]])
+
+    if diag is not None:
+        diag.update(dict(empty=False, Q=Q, E=E, P=P, rho=rho, tau=tau, p=p, Z=Z, G=G,
+                         s_plus=s_plus, Hc=Hc, r_prime=rp, FP=FP))
+    return Factor(U=U_new, sigma=sig_new, B=B_new,
+                  pos=np.concatenate([fac.pos, pos_F]), folded=fac.folded + b,
+                  C_stale=C_stale, dtype=dt)
+
+
+def reorth(fac: Factor) -> Factor:
+    """Periodic re-orthogonalisation (iS-KV notes §4.4).
+
+    Thin QR U = Q_U R_U and B = Q_B R_B, SVD of the small matrix
+    R_U diag(sigma) R_B^T = W S V^T, then U <- Q_U W, sigma <- S, B <- Q_B V.
+    The product U diag(sigma) B^T is unchanged in exact arithmetic.
+    """
+    if fac.k == 0:
+        return fac
+    QU, RU = np.linalg.qr(fac.U, mode="reduced")
+    QB, RB = np.linalg.qr(fac.B, mode="reduced")
+    M = RU @ np.diag(fac.sigma) @ RB.T
+    W, S, Vt = _svd(M)
+    return Factor(U=QU @ W, sigma=S, B=QB @ Vt.T, pos=fac.pos.copy(), folded=fac.folded,
+                  C_stale=fac.C_stale, dtype=fac.dtype)
+
+
+def represented(fac: Factor) -> np.ndarray:
+    """The history the factors represent, U diag(sigma) B^T (n x D)."""
+    return (fac.U * fac.sigma[None, :]) @ fac.B.T
+
+
+def stored_rows(fac: Factor) -> np.ndarray:
+    """Rows as stored: equal to ``represented`` unless coordinates are stale."""
+    if fac.C_stale is None:
+        return represented(fac)
+    return fac.C_stale @ fac.B.T
+
+
+def fresh_truncated_svd(X: np.ndarray, r: int):
+    """Best rank-r approximation of X in the Frobenius norm (iS-KV notes §2.2).
+
+    Returns (X_r, discarded singular values).
+    """
+    u, s, vt = _svd(np.asarray(X, dtype=np.float64))
+    rr = min(r, s.shape[0])
+    Xr = (u[:, :rr] * s[:rr]) @ vt[:rr]
+    return Xr, s[rr:]
+
+
+def rope(X: np.ndarray, pos, head_dim: int, theta: float) -> np.ndarray:
+    """Rotate each head's pre-RoPE key at its own position (iS-KV notes §3.1, §5.2).
+
+    Rows of X are concatenated heads (D = H_kv * head_dim). Inside a head,
+    feature j < head_dim/2 pairs with j + head_dim/2 and the pair turns by
+    pos * theta**(-2j/head_dim). Computed in float64.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    n, D = X.shape
+    half = head_dim // 2
+    pos = np.asarray(pos, dtype=np.float64).reshape(n)
+    j = np.arange(half, dtype=np.float64)
+    inv = theta ** (-2.0 * j / head_dim)
+    ang = pos[:, None] * inv[None, :]            # n x half
+    c, s = np.cos(ang), np.sin(ang)
+    out = np.empty_like(X)
+    for h in range(D // head_dim):
+        a = X[:, h * head_dim:h * head_dim + half]
+        bb = X[:, h * head_dim + half:(h + 1) * head_dim]
+        out[:, h * head_dim:h * head_dim + half] = a * c - bb * s
+        out[:, h * head_dim + half:(h + 1) * head_dim] = bb * c + a * s
+    return out
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round to bfloat16 (via float32, round-to-nearest-even); returns float64 values."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    u = ((u + 0x7FFF + lsb) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def reconstruct(fac: Factor, X_exact, pos_exact, n_total: int, head_dim: int,
+                apply_rope: bool, theta: float = 500000.0) -> np.ndarray:
+    """Dense cache in original position order (iS-KV notes §3.2, §5, Algorithm 3).
+
+    Compressed rows are rebuilt from the factors and scattered to their own
+    original positions, exact rows are placed at theirs, and keys are rotated
+    per token at that position. Every position 0 .. n_total-1 must be covered
+    exactly once. Returns float64 (n_total x D).
+    """
+    D = fac.D
+    out = np.full((n_total, D), np.nan)
+    covered = np.zeros(n_total, dtype=np.int64)
+    if fac.n > 0:
+        rows = stored_rows(fac)
+        out[fac.pos] = rows
+        np.add.at(covered, fac.pos, 1)
+    X_exact = np.asarray(X_exact, dtype=np.float64).reshape(-1, D)
+    pos_exact = np.asarray(pos_exact, dtype=np.int64).reshape(-1)
+    if pos_exact.size:
+        out[pos_exact] = X_exact
+        np.add.at(covered, pos_exact, 1)
+    if not np.all(covered == 1):
+        raise ValueError("compressed and exact positions must partition 0..n_total-1")
+    if apply_rope:
+        out = rope(out, np.arange(n_total), head_dim, theta)
+    return out
+
+
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """Dense GQA decode attention over the whole cache (iS-KV notes §2.1, Algorithm 3).
+
+    q: (batch, H_q, d_h); K, V: (batch, n, H_kv, d_h). Query head h reads KV
+    head floor(h / (H_q / H_kv)); softmax over every cached position, float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    Bt, Hq, dh = q.shape
+    Hkv = K.shape[2]
+    grp = Hq // Hkv
+    out = np.zeros((Bt, Hq, dh))
+    for bi in range(Bt):
+        for h in range(Hq):
+            g = h // grp
+            logits = (K[bi, :, g, :] @ q[bi, h]) * scale
+            m = logits.max()
+            w = np.exp(logits - m)
+            out[bi, h] = (w @ V[bi, :, g, :]) / w.sum()
+    return out
+
+
+def persistent_bytes(n_c: int, n_e: int, D: int, r: int, beta_f: int, beta_e: int) -> int:
+    """Persistent bytes of one path in one layer, eq.(12) (iS-KV notes §5.1).
+
+    beta_f (n_c r + D r + r) for U, the shared basis B and the singular values,
+    plus beta_e n_e D for the exact rows.
+    """
+    return beta_f * (n_c * r + D * r + r) + beta_e * n_e * D
+
+
+def breakeven_rows(D: int, r: int) -> int:
+    """Smallest compressed row count that saves bytes over dense storage (§5.1).
+
+    With equal scalar widths the exact rows cancel and the factored history
+    n r + D r + r undercuts the dense n D once n > r (D + 1) / (D - r).
+    """
+    n = 0
+    while not (n * D > n * r + D * r + r):
+        n += 1
+    return n
+
+
+def dense_kv_bytes(tokens: int, layers: int, D: int, bytes_per: int) -> int:
+    """Dense K and V cache bytes of a model: tokens x layers x 2 x D x bytes."""
+    return tokens * layers * 2 * D * bytes_per
+
+
+def factor_drift(X: np.ndarray, X_inc: np.ndarray, r: int) -> float:
+    """Excess relative error over a fresh same-rank SVD, eq.(14) (iS-KV notes §7.3)."""
+    X = np.asarray(X, dtype=np.float64)
+    nx = np.linalg.norm(X)
+    Xr, _ = fresh_truncated_svd(X, r)
+    return np.linalg.norm(X - X_inc) / nx - np.linalg.norm(X - Xr) / nx
+
+
+def one_step_drift(fac: Factor, F, pos_F, r: int, delta: float = 0.0):
+    """History drift of one merge, with and without coordinate sync (§2.3, eq.(3)).
+
+    The reference is the history represented before the merge. Synced old rows
+    are U G_top diag(sigma+) B+^T; basis-only old rows keep the old coordinates
+    U diag(sigma) (zero-padded) and read them in the new basis B+.
+    Returns (drift_sync, drift_basis_only, merged factor).
+    """
+    before = represented(fac)
+    d = {}
+    new = merge(fac, F, pos_F, r, delta, diag=d)
+    n_old = fac.n
+    synced_old = represented(new)[:n_old]
+    C_old = fac.U * fac.sigma[None, :]
+    rp = new.k
+    pad = np.zeros((n_old, rp))
+    w = min(rp, C_old.shape[1])
+    pad[:, :w] = C_old[:, :w]
+    basis_only_old = pad @ new.B.T
+    nb = np.linalg.norm(before)
+    return (np.linalg.norm(synced_old - before) / nb,
+            np.linalg.norm(basis_only_old - before) / nb, new)
+
+
+def run_stream(X: np.ndarray, b: int, r: int, reorth_every_rows: int = 0, delta: float = 0.0,
+               dtype=np.float64, sync: bool = True, pos0: int = 0, fac: Factor | None = None,
+               callback=None) -> Factor:
+    """Fold the rows of X block by block (b rows each), in order.
+
+    Re-orthogonalises whenever the folded-row counter reaches a multiple of
+    ``reorth_every_rows`` (iS-KV notes §4.4; 0 disables it). ``callback`` is
+    called after every merge with (merge index, factor).
+    """
+    X = np.asarray(X)
+    n = X.shape[0]
+    if fac is None:
+        fac = empty_factor(X.shape[1], dtype=dtype, sync=sync)
+    for t, s in enumerate(range(0, n, b)):
+        F = X[s:s + b]
+        pos_F = np.arange(pos0 + s, pos0 + s + F.shape[0])
+        before = fac.folded
+        fac = merge(fac, F, pos_F, r, delta)
+        if reorth_every_rows and sync and (fac.folded // reorth_every_rows) > (before // reorth_every_rows):
+            fac = reorth(fac)
+        if callback is not None:
+            callback(t, fac)
+    return fac

@@ -1,0 +1,339 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: a closed
+form, an invariant, a worked example the pages print (``tests/golden``), or a
+textbook routine applied to a different matrix (brute force on tiny inputs).
+None of them needs a GPU.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _orth(rng, n, k):
+    q, _ = np.linalg.qr(rng.standard_normal((n, k)))
+    return q
+
+
+def _factor_from(U, s, B, pos=None):
+    n = U.shape[0]
+    return O.Factor(U=U.copy(), sigma=np.asarray(s, float).copy(), B=B.copy(),
+                    pos=np.arange(n) if pos is None else np.asarray(pos))
+
+
+# ---------------------------------------------------------------- Eckart-Young
+def test_eckart_young_known_spectrum():
+    """Fresh truncated SVD error equals the root of the discarded sigma^2 (§2.2)."""
+    rng = np.random.default_rng(1)
+    n, d, r = 40, 12, 5
+    s0 = np.array([9.0, 7.5, 5.0, 4.0, 3.0, 2.0, 1.5, 1.0, 0.5, 0.25, 0.125, 0.0625])
+    X = _orth(rng, n, d) @ np.diag(s0) @ _orth(rng, d, d).T
+    Xr, disc = O.fresh_truncated_svd(X, r)
+    expect = math.sqrt(float(np.sum(s0[r:] ** 2)))
+    assert abs(np.linalg.norm(X - Xr) - expect) <= 1e-12 * np.linalg.norm(X)
+    assert np.allclose(np.sort(disc)[::-1], s0[r:], rtol=1e-12, atol=1e-13)
+
+
+def test_empty_history_merge_is_truncated_svd_of_block():
+    """Empty history: the merge returns the rank-r SVD of F (Algorithm 2, first case)."""
+    rng = np.random.default_rng(2)
+    b, D, r = 8, 10, 3
+    s0 = np.array([5.0, 4.0, 3.0, 2.0, 1.0, 0.5, 0.25, 0.1])
+    F = _orth(rng, b, b) @ np.diag(s0) @ _orth(rng, D, b).T
+    fac = O.merge(O.empty_factor(D), F, np.arange(b), r)
+    assert fac.k == r and fac.n == b
+    err = np.linalg.norm(O.represented(fac) - F)
+    assert abs(err - math.sqrt(float(np.sum(s0[r:] ** 2)))) < 1e-12 * np.linalg.norm(F)
+    assert np.allclose(fac.sigma, s0[:r], rtol=1e-12)
+
+
+# ------------------------------------------------------- within the rank budget
+def test_merge_within_budget_reproduces_stacked_matrix():
+    """k + p <= r: the merge reproduces [U S B^T; F] exactly (§4.2, eq.(7))."""
+    rng = np.random.default_rng(3)
+    D, r = 16, 12
+    U = _orth(rng, 9, 4)
+    B = _orth(rng, D, 4)
+    fac = _factor_from(U, [4.0, 3.0, 2.0, 1.0], B)
+    target_old = O.represented(fac)
+    F = rng.standard_normal((5, D))
+    d = {}
+    new = O.merge(fac, F, np.arange(9, 14), r, diag=d)
+    assert d["p"] == 5 and new.k == 9
+    stacked = np.vstack([target_old, F])
+    assert np.linalg.norm(O.represented(new) - stacked) <= 1e-12 * np.linalg.norm(stacked)
+    # orthonormal factors
+    assert np.abs(new.U.T @ new.U - np.eye(new.k)).max() < 1e-12
+    assert np.abs(new.B.T @ new.B - np.eye(new.k)).max() < 1e-12
+    assert list(new.pos) == list(range(14))
+
+
+def test_many_merges_exact_when_data_rank_fits():
+    """A stream of rank-3 rows folded at r = 8 is reproduced exactly after every merge."""
+    rng = np.random.default_rng(4)
+    D = 20
+    X = rng.standard_normal((64, 3)) @ rng.standard_normal((3, D))
+
+    def cb(t, fac):
+        seen = X[: fac.n]
+        assert fac.k <= 8
+        assert np.linalg.norm(O.represented(fac) - seen) <= 1e-11 * np.linalg.norm(seen)
+
+    O.run_stream(X, 4, 8, callback=cb)
+
+
+# ------------------------------------------------------------- pure rotation
+def test_pure_rotation_merge_keeps_history_exact():
+    """F inside span(B): no residual direction, synced history unchanged (§2.3, eq.(3))."""
+    rng = np.random.default_rng(5)
+    D, k = 12, 4
+    U = _orth(rng, 10, k)
+    B = _orth(rng, D, k)
+    fac = _factor_from(U, [3.0, 2.5, 2.0, 1.5], B)
+    F = rng.standard_normal((3, k)) @ B.T                     # F = A B^T
+    ds, db, new = O.one_step_drift(fac, F, np.arange(10, 13), r=k)
+    assert new.k == k
+    stacked = np.vstack([O.represented(fac), F])
+    assert np.linalg.norm(O.represented(new) - stacked) <= 1e-12 * np.linalg.norm(stacked)
+    assert ds < 1e-13
+    # the basis turned, so stale coordinates read in the new basis drift by O(1)
+    assert db > 1e-2
+
+
+def test_basis_only_drift_two_dim_closed_form():
+    """2-D example (Fig. 3): a basis turned by theta moves stale rows by 2 sin(theta/2).
+
+    History rows diag(2, 1) with B = I; one new row (1, 1); D = r = 2 so there
+    is no residual. The core's right singular vectors are the eigenvectors of
+    [[5, 1], [1, 2]], a rotation by theta with tan(2 theta) = 2/3.
+    """
+    fac = _factor_from(np.eye(2), [2.0, 1.0], np.eye(2))
+    theta = 0.5 * math.atan2(2.0, 3.0)
+    ds, db, new = O.one_step_drift(fac, np.array([[1.0, 1.0]]), [2], r=2)
+    assert abs(db - 2.0 * math.sin(theta / 2.0)) < 1e-12
+    assert ds < 1e-14
+    assert abs(abs(new.B[0, 0]) - math.cos(theta)) < 1e-12
+    # the same drift measured on the stored rows of a basis-only stream
+    f2 = O.Factor(U=np.eye(2), sigma=np.array([2.0, 1.0]), B=np.eye(2), pos=np.arange(2),
+                  C_stale=np.diag([2.0, 1.0]))
+    m = O.merge(f2, np.array([[1.0, 1.0]]), [2], r=2)
+    old = O.stored_rows(m)[:2]
+    assert abs(np.linalg.norm(old - np.diag([2.0, 1.0])) / math.sqrt(5.0)
+               - 2.0 * math.sin(theta / 2.0)) < 1e-12
+
+
+# ------------------------------------------------------ local optimality, brute force
+@pytest.mark.parametrize("seed", range(6))
+def test_one_merge_is_best_rank_r_of_stacked_target(seed):
+    """With the whole residual kept, one merge = best rank-r of [U S B^T; F] (§4.3)."""
+    rng = np.random.default_rng(100 + seed)
+    D, k, r, b = 7, 3, 4, 2
+    fac = _factor_from(_orth(rng, 6, k), np.sort(rng.uniform(0.5, 3.0, k))[::-1], _orth(rng, D, k))
+    F = rng.standard_normal((b, D))
+    stacked = np.vstack([O.represented(fac), F])
+    s_all = np.linalg.svd(stacked, compute_uv=False)
+    if s_all[r - 1] - s_all[r] < 1e-6 * s_all[0]:
+        pytest.skip("truncation tie: several best approximations")
+    new = O.merge(fac, F, [6, 7], r)
+    best, _ = O.fresh_truncated_svd(stacked, r)
+    assert np.linalg.norm(O.represented(new) - best) <= 1e-11 * np.linalg.norm(stacked)
+    # brute force: no other rank-r projection of the rows does better
+    err_new = np.linalg.norm(O.represented(new) - stacked)
+    for _ in range(50):
+        V = _orth(rng, D, r)
+        assert np.linalg.norm(stacked @ V @ V.T - stacked) >= err_new - 1e-12
+
+
+def test_error_split_with_dropped_residual():
+    """Dropped residual E_perp: error^2 = core tail + ||E_perp||^2 (§4.3)."""
+    rng = np.random.default_rng(7)
+    D, k, r, b = 10, 3, 4, 4
+    fac = _factor_from(_orth(rng, 5, k), [4.0, 2.0, 1.0], _orth(rng, D, k))
+    # residual singular values spread over decades so a threshold drops some
+    base = fac.B @ rng.standard_normal((k, b))
+    Pp = np.linalg.qr(np.hstack([fac.B, rng.standard_normal((D, b))]))[0][:, k:]
+    F = (base + Pp @ np.diag([2.0, 0.5, 1e-3, 1e-4]) @ _orth(rng, b, b).T).T
+    d = {}
+    new = O.merge(fac, F, np.arange(5, 9), r, delta=1e-2, diag=d)
+    assert d["p"] == 2
+    stacked = np.vstack([O.represented(fac), F])
+    E = d["E"]
+    E_perp = E - E @ d["P"] @ d["P"].T
+    lhs = np.linalg.norm(stacked - O.represented(new)) ** 2
+    rhs = np.sum(d["s_plus"][r:] ** 2) + np.linalg.norm(E_perp) ** 2
+    assert abs(lhs - rhs) <= 1e-10 * np.linalg.norm(stacked) ** 2
+    # and E_perp carries exactly the two dropped residual singular values
+    assert abs(np.linalg.norm(E_perp) ** 2 - (1e-3 ** 2 + 1e-4 ** 2)) < 1e-14
+
+
+def test_residual_threshold_floor():
+    """The scale-dependent floor keeps a real new direction and drops rounding-size ones (§4.1)."""
+    rng = np.random.default_rng(8)
+    D = 64
+    B = _orth(rng, D, 4)
+    fac = _factor_from(_orth(rng, 6, 4), [10.0, 8.0, 6.0, 4.0], B)
+    Pp = np.linalg.qr(np.hstack([B, rng.standard_normal((D, 2))]))[0][:, 4:]
+    tau = 64 * O.EPS_FP32 * 10.0
+    for amp, expect_p in [(0.3 * tau, 0), (3.0 * tau, 1)]:
+        F = (B @ rng.standard_normal(4) + amp * Pp[:, 0])[None, :]
+        d = {}
+        O.merge(fac, F, [6], r=8, diag=d)
+        assert d["p"] == expect_p, (amp, d["rho"], d["tau"])
+
+
+def test_full_rank_basis_adds_no_residual():
+    """k = D: no residual direction is added, the merge still rotates (§4.2)."""
+    rng = np.random.default_rng(9)
+    D = 5
+    fac = _factor_from(_orth(rng, 8, D), [5, 4, 3, 2, 1.0], _orth(rng, D, D))
+    F = rng.standard_normal((2, D))
+    d = {}
+    new = O.merge(fac, F, [8, 9], r=D, diag=d)
+    assert d["p"] == 0
+    stacked = np.vstack([O.represented(fac), F])
+    assert np.linalg.norm(O.represented(new) - stacked) <= 1e-12 * np.linalg.norm(stacked)
+
+
+# ------------------------------------------------------------ worked example
+def test_rank1_counterexample_matches_pages():
+    """Path dependence (§4.3, Fig. 4): incremental sees 16 and 9, fresh best error 4."""
+    g = json.load(open(os.path.join(GOLDEN, "rank1_counterexample.json")))
+    r = g["rank_budget"]
+    X1 = np.array(g["first_batch"])
+    Fn = np.array(g["new_rows"])
+    fac = O.merge(O.empty_factor(2), X1, [0, 1], r)
+    d = {}
+    new = O.merge(fac, Fn, [2], r, diag=d)
+    assert np.allclose(np.sort(d["s_plus"] ** 2)[::-1], g["incremental_core_sigma_sq"], atol=1e-12)
+    assert np.allclose(np.abs(new.B[:, 0]), g["incremental_keeps"], atol=1e-12)
+    full = np.vstack([X1, Fn])
+    best, disc = O.fresh_truncated_svd(full, r)
+    assert abs(np.linalg.norm(full - best) - g["fresh_best_error"]) < 1e-12
+    _, _, vt = np.linalg.svd(full)
+    assert np.allclose(np.abs(vt[0]), g["fresh_keeps"], atol=1e-12)
+    # incremental error against the whole history: the dropped e2 energy 9 + 9
+    assert abs(np.linalg.norm(full - O.represented(new)) - math.sqrt(18.0)) < 1e-12
+
+
+# --------------------------------------------------------------- reorth
+def test_reorth_keeps_product_and_restores_orthogonality():
+    """Re-orthogonalisation: same product, orthonormal U and B (§4.4)."""
+    rng = np.random.default_rng(10)
+    n, D, k = 50, 30, 6
+    U = _orth(rng, n, k) + 1e-3 * rng.standard_normal((n, k))
+    B = _orth(rng, D, k) + 1e-3 * rng.standard_normal((D, k))
+    fac = _factor_from(U, np.linspace(3, 1, k), B)
+    before = O.represented(fac)
+    new = O.reorth(fac)
+    assert np.linalg.norm(O.represented(new) - before) <= 1e-13 * np.linalg.norm(before)
+    assert np.abs(new.U.T @ new.U - np.eye(k)).max() < 1e-13
+    assert np.abs(new.B.T @ new.B - np.eye(k)).max() < 1e-13
+    assert np.all(np.diff(new.sigma) <= 0)
+    # an already-orthonormal factorisation keeps its singular values
+    clean = _factor_from(_orth(rng, n, k), np.linspace(3, 1, k), _orth(rng, D, k))
+    assert np.allclose(O.reorth(clean).sigma, np.linspace(3, 1, k), rtol=1e-13)
+
+
+# ---------------------------------------------------------------- RoPE, bf16
+def test_rope_closed_forms():
+    hd, theta = 8, 10000.0
+    rng = np.random.default_rng(11)
+    X = rng.standard_normal((5, 2 * hd))
+    # position 0 is the identity
+    assert np.array_equal(O.rope(X, np.zeros(5), hd, theta), X)
+    # a unit vector on feature j of head 1 turns into cos/sin on features j, j + hd/2
+    for j in range(hd // 2):
+        e = np.zeros((1, 2 * hd)); e[0, hd + j] = 1.0
+        p = 37
+        ang = p * theta ** (-2.0 * j / hd)
+        out = O.rope(e, [p], hd, theta)
+        exp = np.zeros(2 * hd); exp[hd + j] = math.cos(ang); exp[hd + j + hd // 2] = math.sin(ang)
+        assert np.allclose(out[0], exp, atol=1e-15)
+    # each pair keeps its norm; dot products depend only on the offset
+    Y = O.rope(X, np.arange(5) * 11, hd, theta)
+    for h in range(2):
+        for j in range(hd // 2):
+            a, b = h * hd + j, h * hd + j + hd // 2
+            assert np.allclose(X[:, a] ** 2 + X[:, b] ** 2, Y[:, a] ** 2 + Y[:, b] ** 2)
+    x, y = rng.standard_normal((1, hd)), rng.standard_normal((1, hd))
+    d1 = O.rope(x, [100], hd, theta) @ O.rope(y, [90], hd, theta).T
+    d2 = O.rope(x, [17], hd, theta) @ O.rope(y, [7], hd, theta).T
+    assert abs(d1 - d2).max() < 1e-12
+
+
+def test_bf16_round_known_values():
+    vals = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, -2.5, 3.0e38, 1e-40])
+    got = O.bf16_round(vals)
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: even mantissa wins (1.0)
+    assert got[0] == 1.0 and got[1] == 1.0
+    assert got[2] == 1.0 + 2 ** -6           # tie between 1+2^-7 and 1+2^-6 -> even
+    assert got[3] == 1.0
+    assert got[4] == -2.5
+    assert np.isfinite(got[5])
+
+
+# ---------------------------------------------------------------- attention
+def test_attend_special_cases():
+    rng = np.random.default_rng(12)
+    Bt, n, Hq, Hkv, dh = 2, 9, 8, 2, 4
+    q = rng.standard_normal((Bt, Hq, dh))
+    V = rng.standard_normal((Bt, n, Hkv, dh))
+    # equal keys: the output is the mean of the values of the head's group
+    K = np.broadcast_to(rng.standard_normal((1, 1, Hkv, dh)), (Bt, n, Hkv, dh)).copy()
+    out = O.attend(q, K, V, 0.5)
+    for h in range(Hq):
+        assert np.allclose(out[:, h], V[:, :, h // (Hq // Hkv)].mean(axis=1), atol=1e-14)
+    # a planted needle: one key along q with a huge logit picks its value row
+    K = rng.standard_normal((Bt, n, Hkv, dh)) * 0.01
+    K[:, 4, :, :] = 0.0
+    for h in (0, 4):
+        K[:, 4, h // 4, :] = 100.0 * q[:, h, :]
+    out = O.attend(q, K, V, 1.0)
+    assert np.allclose(out[:, 0], V[:, 4, 0], atol=1e-10)
+    assert np.allclose(out[:, 4], V[:, 4, 1], atol=1e-10)
+
+
+# ---------------------------------------------------------------- storage
+def test_storage_accounting_matches_pages():
+    g = json.load(open(os.path.join(GOLDEN, "storage_eq12.json")))
+    be = g["breakeven"]
+    assert O.breakeven_rows(be["D"], be["r"]) == be["rows"]
+    for row in g["dense"]:
+        tokens = row["input_tokens"] + row["generated"]
+        got = O.dense_kv_bytes(tokens, g["layers"], g["D"], g["bytes_per_scalar"]) / 2 ** 30
+        assert got == row["GiB"]
+    # eq.(12) at the break-even: compressed payload below dense exactly from 147 rows
+    D, r = be["D"], be["r"]
+    assert O.persistent_bytes(147, 0, D, r, 2, 2) < 2 * 147 * D
+    assert O.persistent_bytes(146, 0, D, r, 2, 2) >= 2 * 146 * D
+
+
+def test_factor_drift_zero_without_truncation():
+    rng = np.random.default_rng(13)
+    X = rng.standard_normal((24, 3)) @ rng.standard_normal((3, 10))
+    fac = O.run_stream(X, 4, 6)
+    assert abs(O.factor_drift(X, O.represented(fac), 6)) < 1e-12
+
+
+# ---------------------------------------------------------------- tiny stream
+def test_tiny_stream_fp32_tracks_fp64_and_near_fresh_svd():
+    """The 32-merge tiny stream: fp32 and fp64 oracles agree; drift vs fresh SVD is small."""
+    X = synth.kv_stream(synth.CONFIG_TINY)
+    f64 = O.run_stream(X, 8, 8)
+    f32 = O.run_stream(X, 8, 8, dtype=np.float32)
+    R64 = O.represented(f64)
+    R32 = (f32.U.astype(float) * f32.sigma.astype(float)) @ f32.B.astype(float).T
+    assert np.linalg.norm(R64 - R32) / np.linalg.norm(R64) < 1e-4
+    Xr, _ = O.fresh_truncated_svd(X, 8)
+    rel_fresh = np.linalg.norm(X - Xr) / np.linalg.norm(X)
+    drift = O.factor_drift(X, R64, 8)
+    assert 0.0 <= drift < 0.5 * rel_fresh
+    assert f64.n == 256 and f64.k == 8
