@@ -1,0 +1,224 @@
+/*
+ * iskv.h - C ABI of the MI355X (gfx950) hot path of iS-KV online low-rank KV
+ * compression: block-incremental SVD merges of pending exact KV blocks into a
+ * truncated history, periodic re-orthogonalisation, reconstruction of the
+ * dense cache with per-position RoPE, and GQA decode attention over it.
+ *
+ * Source of the method: Zhongzhu Zhou, reading notes on "iS-KV: Online
+ * Low-Rank KV Cache Compression via Block-Incremental SVD" ("iS-KV notes"
+ * below), sections 2-5, Algorithms 1-3, eq.(3), eq.(7), eq.(12).
+ *
+ * Conventions shared by every entry point
+ *  - Plain C: no C++ or torch types cross this boundary. Device buffers are
+ *    plain device pointers; streams are hipStream_t passed as void*
+ *    (NULL = the null stream).
+ *  - Ownership: the caller allocates and owns every device buffer (factors,
+ *    positions, workspace, outputs). The library never allocates device
+ *    memory; it only malloc()s the small host-side handle objects.
+ *  - Asynchrony: every call only enqueues kernels on the handle's stream and
+ *    returns without waiting, except isvd_query(), which synchronises that
+ *    stream to read the device-side counters.
+ *  - Errors: 0 on success, a negative ISKV_E* code otherwise. Arguments are
+ *    checked before anything is enqueued, and a call that fails its checks
+ *    leaves every buffer and the handle unchanged. Numerical trouble found on
+ *    the device (non-finite input, a core eigensolver that did not converge)
+ *    is latched in the device status word and reported by isvd_query() and by
+ *    the next call on that handle. No C++ exception crosses the ABI.
+ *  - Threading: a handle is not thread-safe; drive it from one host thread
+ *    and one stream.
+ *  - Layouts are row-major. Floating point is IEEE fp32 unless stated;
+ *    bf16 values are passed as their uint16_t bit patterns.
+ */
+#ifndef ISKV_H
+#define ISKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+enum iskv_status {
+  ISKV_OK = 0,
+  ISKV_EINVAL = -1,      /* bad shape, null pointer, inconsistent argument     */
+  ISKV_ECAPACITY = -2,   /* n + b would exceed n_cap, or a window is full      */
+  ISKV_EWORKSPACE = -3,  /* workspace too small or misaligned                  */
+  ISKV_EHIP = -4,        /* a HIP runtime call failed                          */
+  ISKV_ENONFINITE = -5,  /* a merged block or the core held NaN/Inf (latched)  */
+  ISKV_ENOCONV = -6,     /* the core eigensolver hit its sweep cap (latched)   */
+  ISKV_EMODE = -7        /* operation not available in this handle's mode      */
+};
+
+/* Device status word bits (isvd_query's *status). */
+#define ISKV_DEV_NONFINITE 1
+#define ISKV_DEV_NOCONV 2
+
+/* Config flags. */
+#define ISKV_NO_COORD_SYNC 1 /* basis-only ablation (iS-KV notes §2.3): merges
+                                replace the basis but never rewrite the stored
+                                coordinates of old rows */
+
+/* Output dtypes of kv_reconstruct. */
+#define ISKV_OUT_BF16 0
+#define ISKV_OUT_FP32 1
+
+/* ---- iSVD handle --------------------------------------------------------- */
+typedef struct iskv_config {
+  int32_t D;                 /* feature width H_kv * d_h (iS-KV notes §2.1), a multiple
+                                of 64 in 64..8192                                         */
+  int32_t r_max;             /* rank budget r, 1..1024, r <= D                            */
+  int32_t b_max;             /* largest pending block b, 1..64                            */
+  int32_t n_cap;             /* row capacity of the compressed history                    */
+  int32_t reorth_every_rows; /* re-orthogonalise whenever the folded-row counter crosses
+                                a multiple of this (notes §4.4: 256); 0 = only on request */
+  float resid_rel_tol;       /* delta of the residual threshold (notes §4.1), default 0:
+                                keep residual direction j when
+                                rho_j > max(delta*s, max(D,b)*2^-23*s),
+                                s = max(sigma_1, rho_1)                                   */
+  int32_t flags;             /* ISKV_NO_COORD_SYNC or 0                                   */
+} iskv_config;
+
+typedef struct isvd_handle isvd_handle;
+
+/* Bytes of device workspace one handle needs for `cfg` (256-byte aligned
+ * sub-buffers). Returns 0 if cfg is invalid. */
+size_t isvd_workspace_bytes(const iskv_config* cfg);
+
+/* Create a handle over caller-owned device buffers and reset the history to
+ * empty (n = k = 0). iS-KV notes §2.2: the history is X^ = C B^T where
+ * C = U diag(sigma) holds one row of coordinates per token.
+ *   C         device fp32 [n_cap x r_max]: coordinates; zero-filled here.
+ *   sigma     device fp32 [r_max]: singular values, descending.
+ *   B         device fp32 [D x r_max]: shared orthonormal basis, column j is
+ *             basis vector j (row d holds feature d's k coefficients).
+ *   pos       device int32 [n_cap]: original token position of each row.
+ *   workspace device buffer of >= isvd_workspace_bytes(cfg) bytes, 256-aligned.
+ *   stream    hipStream_t as void*; all later calls on the handle use it.
+ * On success *out receives the handle. Errors: EINVAL, EWORKSPACE, EHIP. */
+int isvd_init(isvd_handle** out, const iskv_config* cfg, float* C, float* sigma, float* B,
+              int32_t* pos, void* workspace, size_t ws_bytes, void* stream);
+
+/* Fold one pending exact block into the history: Algorithm 2 and §4.1-§4.2 of
+ * the iS-KV notes. Projects F on B, takes the residual (subtracting its
+ * component along B twice), finds the residual basis P by a rank-revealing
+ * eigendecomposition of E E^T with the threshold above, forms the core
+ * Z = [[diag(sigma), 0], [F B, F P]] of eq.(7), takes its truncated SVD
+ * (keeping r' = min(r_max, k + p)), rewrites every old row's coordinates
+ * C <- C H[:k] (skipped under ISKV_NO_COORD_SYNC), appends the new rows
+ * [F B, F P] H, and sets B <- [B, P] H, sigma <- sigma+. Re-orthogonalises
+ * afterwards when the folded-row counter crosses a multiple of
+ * reorth_every_rows.
+ *   F      device fp32 [b x D], the b oldest pending exact rows.
+ *   pos_F  device int32 [b], their original positions (copied into pos).
+ *   b      1..b_max.
+ * Errors: EINVAL (null pointer, b out of range), ECAPACITY (n + b > n_cap),
+ * ENONFINITE / ENOCONV latched by an earlier call. */
+int isvd_merge_block(isvd_handle* h, const float* F, const int32_t* pos_F, int32_t b);
+
+/* Re-orthogonalise the factors: iS-KV notes §4.4. Equivalent to the notes'
+ * thin QR of U and B and SVD of R_U diag(sigma) R_B^T: the product C B^T is
+ * kept, B becomes orthonormal and C's columns orthogonal with norms sigma.
+ * Errors: EMODE under ISKV_NO_COORD_SYNC (the stale rows have no consistent
+ * factorisation to re-orthogonalise). */
+int isvd_reorth(isvd_handle* h);
+
+/* Synchronise the handle's stream and read the device counters: rows n,
+ * current rank k and the device status word (ISKV_DEV_* bits). Any pointer
+ * may be NULL. Errors: EHIP. */
+int isvd_query(isvd_handle* h, int32_t* n, int32_t* k, int32_t* status);
+
+/* Rows folded so far (host-side, no sync). */
+int32_t isvd_rows(const isvd_handle* h);
+
+/* Release the host handle (device buffers stay the caller's). NULL is a no-op. */
+void isvd_destroy(isvd_handle* h);
+
+/* ---- reconstruction ------------------------------------------------------ */
+/* Rebuild the dense cache in original position order: Algorithm 3 and §3.2 /
+ * §5 of the iS-KV notes. Row pos[i] of `out` gets the compressed row C_i B^T
+ * (i < n); row pos_exact[e] gets X_exact[e]; with apply_rope every row t is
+ * then turned per head at position t (pairs (j, j + head_dim/2) by angle
+ * t * rope_theta^(-2j/head_dim)), which is how the notes restore pre-RoPE
+ * keys. Exact slots with pos_exact[e] < 0 are skipped, so a window buffer
+ * with empty slots can be passed as is.
+ *   h           handle whose history is read (not modified).
+ *   X_exact     device fp32 [n_exact x D] or NULL when n_exact == 0.
+ *   pos_exact   device int32 [n_exact].
+ *   n_total     rows of out; the compressed and valid exact positions must
+ *               partition 0..n_total-1 (the caller's contract; not checked on
+ *               the device).
+ *   head_dim    d_h, even, dividing 128 when D % 128 == 0, else dividing 64.
+ *   out         device [n_total x D], bf16 bits (ISKV_OUT_BF16) or fp32
+ *               (ISKV_OUT_FP32); fp32 output computes the product in fp32.
+ *   stream      hipStream_t as void* (NULL = the handle's stream).
+ * Errors: EINVAL. */
+int kv_reconstruct(const isvd_handle* h, const float* X_exact, const int32_t* pos_exact,
+                   int32_t n_exact, int32_t n_total, int32_t head_dim, int32_t apply_rope,
+                   float rope_theta, void* out, int32_t out_dtype, void* stream);
+
+/* ---- attention ----------------------------------------------------------- */
+/* Dense GQA decode attention over a reconstructed cache: Algorithm 3 and
+ * §2.1 of the iS-KV notes. For every batch row and query head h,
+ *   o_h = softmax_t(scale * q_h . K[t, g]) V[t, g],  g = h / (Hq / Hkv),
+ * over all n cached positions (no causal mask at decode; queries already
+ * rotated). fp32 accumulation, bf16 output.
+ *   q    device bf16 [batch x Hq x dh];  K, V device bf16 [batch x n x Hkv x dh]
+ *   out  device bf16 [batch x Hq x dh]
+ *   workspace  >= decode_attend_workspace_bytes(batch, n, Hq, dh) bytes.
+ * Limits: dh == 128, Hq % Hkv == 0, Hq / Hkv <= 16, n >= 1.
+ * Errors: EINVAL, EWORKSPACE. */
+size_t decode_attend_workspace_bytes(int32_t batch, int32_t n, int32_t Hq, int32_t dh);
+int decode_attend(const uint16_t* q, const uint16_t* K, const uint16_t* V, int32_t batch,
+                  int32_t n, int32_t Hq, int32_t Hkv, int32_t dh, float scale, uint16_t* out,
+                  void* workspace, size_t ws_bytes, void* stream);
+
+/* ---- exact window and pending FIFO --------------------------------------- */
+/* The cache policy of §3.2 and Algorithm 3 (iS-KV notes): every new row is
+ * stored exactly in a recent window of `window` rows; an unprotected row
+ * leaving the window joins the pending FIFO and stays exact; once `block`
+ * rows are pending they are folded by isvd_merge_block. Protected rows
+ * (§3.1) stay exact for good.
+ * The exact rows live in one caller-owned device buffer laid out as
+ * [protected (prot_cap) | window ring (window) | pending (block)] rows of D
+ * fp32, with a matching int32 position array (-1 marks an empty slot), so
+ * that the whole buffer can be handed to kv_reconstruct as X_exact. */
+typedef struct iskv_window iskv_window;
+
+/* Rows of the exact buffer: prot_cap + window + block. */
+int32_t iskv_window_rows(int32_t prot_cap, int32_t window, int32_t block);
+
+/* rows: device fp32 [iskv_window_rows() x D]; pos: device int32 [same].
+ * block must equal the b used for merges and be <= the handle's b_max.
+ * Clears the position array. Errors: EINVAL, EHIP. */
+int iskv_window_init(iskv_window** out, isvd_handle* h, int32_t prot_cap, int32_t window,
+                     int32_t block, float* rows, int32_t* pos, void* stream);
+
+/* Store `count` protected rows (device fp32 [count x D]) at host positions
+ * pos_host[0..count-1]. Errors: ECAPACITY past prot_cap, EINVAL. */
+int iskv_window_protect(iskv_window* w, const float* rows, const int32_t* pos_host,
+                        int32_t count);
+
+/* Append `count` new exact rows (device fp32 [count x D]) at consecutive
+ * positions pos0, pos0+1, ...; rows pushed out of the window become pending
+ * and every full block is merged into the handle. *merges (may be NULL)
+ * receives the number of merges this call enqueued. Errors: EINVAL, and any
+ * error of isvd_merge_block. */
+int iskv_window_append(iskv_window* w, const float* rows, int32_t pos0, int32_t count,
+                       int32_t* merges);
+
+/* The exact buffer for kv_reconstruct: its rows, positions and slot count. */
+int iskv_window_exact(const iskv_window* w, const float** rows, const int32_t** pos,
+                      int32_t* count);
+
+void iskv_window_destroy(iskv_window* w);
+
+/* ---- misc ---------------------------------------------------------------- */
+const char* iskv_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ISKV_H */

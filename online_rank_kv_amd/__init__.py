@@ -1,0 +1,306 @@
+"""Python binding of the gfx950 iS-KV hot path (libiskv.so).
+
+Argument marshalling only: every step runs in the HIP kernels behind the C
+ABI declared in ``include/iskv.h``. PyTorch supplies device memory and
+streams. The names follow the C entry points (``isvd_init``,
+``isvd_merge_block``, ``isvd_reorth``, ``isvd_query``, ``kv_reconstruct``,
+``decode_attend`` and the ``iskv_window_*`` calls); ``IsvdPath`` and
+``ExactWindow`` own the torch tensors that back one handle.
+
+Importing the package loads the shared library and fails loudly when it has
+not been built (``python -m online_rank_kv_amd.build`` or
+``__graft_entry__.build()``); there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "LIB_PATH", "lib", "IskvError", "IskvConfig", "ISKV_NO_COORD_SYNC", "ISKV_OUT_BF16",
+    "ISKV_OUT_FP32", "ISKV_DEV_NONFINITE", "ISKV_DEV_NOCONV", "EXPORTED_SYMBOLS",
+    "isvd_workspace_bytes", "isvd_init", "isvd_merge_block", "isvd_reorth", "isvd_query",
+    "isvd_rows", "isvd_destroy", "kv_reconstruct", "decode_attend_workspace_bytes",
+    "decode_attend", "iskv_window_rows", "iskv_window_init", "iskv_window_protect",
+    "iskv_window_append", "iskv_window_exact", "iskv_window_destroy", "iskv_strerror",
+    "IsvdPath", "ExactWindow",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libiskv.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first "
+        "(python -m online_rank_kv_amd.build)")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+ISKV_NO_COORD_SYNC = 1
+ISKV_OUT_BF16 = 0
+ISKV_OUT_FP32 = 1
+ISKV_DEV_NONFINITE = 1
+ISKV_DEV_NOCONV = 2
+
+EXPORTED_SYMBOLS = (
+    "isvd_workspace_bytes", "isvd_init", "isvd_merge_block", "isvd_reorth", "isvd_query",
+    "isvd_rows", "isvd_destroy", "kv_reconstruct", "decode_attend_workspace_bytes",
+    "decode_attend", "iskv_window_rows", "iskv_window_init", "iskv_window_protect",
+    "iskv_window_append", "iskv_window_exact", "iskv_window_destroy", "iskv_strerror",
+)
+
+
+class IskvConfig(ctypes.Structure):
+    _fields_ = [
+        ("D", ctypes.c_int32),
+        ("r_max", ctypes.c_int32),
+        ("b_max", ctypes.c_int32),
+        ("n_cap", ctypes.c_int32),
+        ("reorth_every_rows", ctypes.c_int32),
+        ("resid_rel_tol", ctypes.c_float),
+        ("flags", ctypes.c_int32),
+    ]
+
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_pi32 = ctypes.POINTER(ctypes.c_int32)
+
+lib.iskv_strerror.restype = ctypes.c_char_p
+lib.iskv_strerror.argtypes = [ctypes.c_int]
+lib.isvd_workspace_bytes.restype = ctypes.c_size_t
+lib.isvd_workspace_bytes.argtypes = [ctypes.POINTER(IskvConfig)]
+lib.isvd_init.restype = ctypes.c_int
+lib.isvd_init.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(IskvConfig), _vp, _vp, _vp, _vp, _vp,
+                          ctypes.c_size_t, _vp]
+lib.isvd_merge_block.restype = ctypes.c_int
+lib.isvd_merge_block.argtypes = [_vp, _vp, _vp, _i32]
+lib.isvd_reorth.restype = ctypes.c_int
+lib.isvd_reorth.argtypes = [_vp]
+lib.isvd_query.restype = ctypes.c_int
+lib.isvd_query.argtypes = [_vp, _pi32, _pi32, _pi32]
+lib.isvd_rows.restype = _i32
+lib.isvd_rows.argtypes = [_vp]
+lib.isvd_destroy.restype = None
+lib.isvd_destroy.argtypes = [_vp]
+lib.kv_reconstruct.restype = ctypes.c_int
+lib.kv_reconstruct.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, ctypes.c_float, _vp, _i32, _vp]
+lib.decode_attend_workspace_bytes.restype = ctypes.c_size_t
+lib.decode_attend_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
+lib.decode_attend.restype = ctypes.c_int
+lib.decode_attend.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _vp, _vp,
+                              ctypes.c_size_t, _vp]
+lib.iskv_window_rows.restype = _i32
+lib.iskv_window_rows.argtypes = [_i32, _i32, _i32]
+lib.iskv_window_init.restype = ctypes.c_int
+lib.iskv_window_init.argtypes = [ctypes.POINTER(_vp), _vp, _i32, _i32, _i32, _vp, _vp, _vp]
+lib.iskv_window_protect.restype = ctypes.c_int
+lib.iskv_window_protect.argtypes = [_vp, _vp, _pi32, _i32]
+lib.iskv_window_append.restype = ctypes.c_int
+lib.iskv_window_append.argtypes = [_vp, _vp, _i32, _i32, _pi32]
+lib.iskv_window_exact.restype = ctypes.c_int
+lib.iskv_window_exact.argtypes = [_vp, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _pi32]
+lib.iskv_window_destroy.restype = None
+lib.iskv_window_destroy.argtypes = [_vp]
+
+
+class IskvError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {iskv_strerror(code)} ({code})")
+        self.code = code
+
+
+def iskv_strerror(code: int) -> str:
+    return lib.iskv_strerror(int(code)).decode()
+
+
+def _check(code: int, what: str) -> None:
+    if code != 0:
+        raise IskvError(code, what)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    return int(t.data_ptr())
+
+
+def _stream_ptr(stream) -> int | None:
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) or None
+
+
+# ---- raw entry points (same names as the C ABI) ------------------------------
+def isvd_workspace_bytes(cfg: IskvConfig) -> int:
+    return int(lib.isvd_workspace_bytes(ctypes.byref(cfg)))
+
+
+def isvd_init(cfg: IskvConfig, C, sigma, B, pos, workspace, stream=None) -> int:
+    h = _vp()
+    _check(lib.isvd_init(ctypes.byref(h), ctypes.byref(cfg), _ptr(C), _ptr(sigma), _ptr(B), _ptr(pos),
+                         _ptr(workspace), workspace.numel() * workspace.element_size(),
+                         _stream_ptr(stream)), "isvd_init")
+    return h.value
+
+
+def isvd_merge_block(h: int, F, pos_F, b: int) -> None:
+    _check(lib.isvd_merge_block(h, _ptr(F), _ptr(pos_F), int(b)), "isvd_merge_block")
+
+
+def isvd_reorth(h: int) -> None:
+    _check(lib.isvd_reorth(h), "isvd_reorth")
+
+
+def isvd_query(h: int):
+    n, k, st = _i32(), _i32(), _i32()
+    _check(lib.isvd_query(h, ctypes.byref(n), ctypes.byref(k), ctypes.byref(st)), "isvd_query")
+    return n.value, k.value, st.value
+
+
+def isvd_rows(h: int) -> int:
+    return int(lib.isvd_rows(h))
+
+
+def isvd_destroy(h: int) -> None:
+    lib.isvd_destroy(h)
+
+
+def kv_reconstruct(h: int, X_exact, pos_exact, n_exact: int, n_total: int, head_dim: int,
+                   apply_rope: bool, rope_theta: float, out, out_dtype: int, stream=None) -> None:
+    _check(lib.kv_reconstruct(h, _ptr(X_exact), _ptr(pos_exact), int(n_exact), int(n_total),
+                              int(head_dim), int(bool(apply_rope)), float(rope_theta), _ptr(out),
+                              int(out_dtype), _stream_ptr(stream)), "kv_reconstruct")
+
+
+def decode_attend_workspace_bytes(batch: int, n: int, Hq: int, dh: int) -> int:
+    return int(lib.decode_attend_workspace_bytes(batch, n, Hq, dh))
+
+
+def decode_attend(q, K, V, batch: int, n: int, Hq: int, Hkv: int, dh: int, scale: float, out,
+                  workspace, stream=None) -> None:
+    _check(lib.decode_attend(_ptr(q), _ptr(K), _ptr(V), int(batch), int(n), int(Hq), int(Hkv),
+                             int(dh), float(scale), _ptr(out), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream_ptr(stream)),
+           "decode_attend")
+
+
+def iskv_window_rows(prot_cap: int, window: int, block: int) -> int:
+    return int(lib.iskv_window_rows(prot_cap, window, block))
+
+
+def iskv_window_init(h: int, prot_cap: int, window: int, block: int, rows, pos, stream=None) -> int:
+    w = _vp()
+    _check(lib.iskv_window_init(ctypes.byref(w), h, prot_cap, window, block, _ptr(rows), _ptr(pos),
+                                _stream_ptr(stream)), "iskv_window_init")
+    return w.value
+
+
+def iskv_window_protect(w: int, rows, positions) -> None:
+    arr = (ctypes.c_int32 * len(positions))(*[int(p) for p in positions])
+    _check(lib.iskv_window_protect(w, _ptr(rows), arr, len(positions)), "iskv_window_protect")
+
+
+def iskv_window_append(w: int, rows, pos0: int, count: int) -> int:
+    m = _i32()
+    _check(lib.iskv_window_append(w, _ptr(rows), int(pos0), int(count), ctypes.byref(m)),
+           "iskv_window_append")
+    return m.value
+
+
+def iskv_window_exact(w: int):
+    r, p, c = _vp(), _vp(), _i32()
+    _check(lib.iskv_window_exact(w, ctypes.byref(r), ctypes.byref(p), ctypes.byref(c)),
+           "iskv_window_exact")
+    return r.value, p.value, c.value
+
+
+def iskv_window_destroy(w: int) -> None:
+    lib.iskv_window_destroy(w)
+
+
+# ---- owners of the device buffers behind one handle --------------------------
+class IsvdPath:
+    """One compressed (layer, K-or-V) path: torch tensors + the C handle."""
+
+    def __init__(self, D: int, r_max: int, b_max: int, n_cap: int, reorth_every_rows: int = 0,
+                 resid_rel_tol: float = 0.0, sync: bool = True, device="cuda", stream=None):
+        import torch
+        self.cfg = IskvConfig(D, r_max, b_max, n_cap, reorth_every_rows, resid_rel_tol,
+                              0 if sync else ISKV_NO_COORD_SYNC)
+        ws = isvd_workspace_bytes(self.cfg)
+        if ws == 0:
+            raise ValueError("invalid iskv configuration")
+        dev = torch.device(device)
+        self.C = torch.empty((n_cap, r_max), dtype=torch.float32, device=dev)
+        self.sigma = torch.empty((r_max,), dtype=torch.float32, device=dev)
+        self.B = torch.empty((D, r_max), dtype=torch.float32, device=dev)
+        self.pos = torch.empty((n_cap,), dtype=torch.int32, device=dev)
+        self.workspace = torch.empty((ws + 256,), dtype=torch.uint8, device=dev)
+        off = (-self.workspace.data_ptr()) % 256
+        self._ws_view = self.workspace[off:off + ws]
+        self.stream = stream
+        self.h = isvd_init(self.cfg, self.C, self.sigma, self.B, self.pos, self._ws_view, stream)
+
+    def merge(self, F, pos_F) -> None:
+        isvd_merge_block(self.h, F, pos_F, F.shape[0])
+
+    def reorth(self) -> None:
+        isvd_reorth(self.h)
+
+    def query(self):
+        return isvd_query(self.h)
+
+    @property
+    def n(self) -> int:
+        return isvd_rows(self.h)
+
+    def reconstruct(self, out, n_total: int, X_exact=None, pos_exact=None, head_dim: int = 128,
+                    rope: bool = False, theta: float = 500000.0, stream=None) -> None:
+        import torch
+        dt = ISKV_OUT_BF16 if out.dtype == torch.bfloat16 else ISKV_OUT_FP32
+        n_exact = 0 if X_exact is None else int(X_exact.shape[0])
+        kv_reconstruct(self.h, X_exact, pos_exact, n_exact, n_total, head_dim, rope, theta, out, dt,
+                       stream if stream is not None else self.stream)
+
+    def close(self) -> None:
+        if getattr(self, "h", None):
+            isvd_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class ExactWindow:
+    """Exact recent window + pending FIFO feeding one IsvdPath (iS-KV notes §3.2)."""
+
+    def __init__(self, path: IsvdPath, window: int, block: int, prot_cap: int = 0, stream=None):
+        import torch
+        self.path = path
+        rows = iskv_window_rows(prot_cap, window, block)
+        dev = path.C.device
+        self.rows = torch.empty((rows, path.cfg.D), dtype=torch.float32, device=dev)
+        self.pos = torch.empty((rows,), dtype=torch.int32, device=dev)
+        self.w = iskv_window_init(path.h, prot_cap, window, block, self.rows, self.pos,
+                                  stream if stream is not None else path.stream)
+
+    def protect(self, rows, positions) -> None:
+        iskv_window_protect(self.w, rows, positions)
+
+    def append(self, rows, pos0: int) -> int:
+        return iskv_window_append(self.w, rows, pos0, rows.shape[0])
+
+    def close(self) -> None:
+        if getattr(self, "w", None):
+            iskv_window_destroy(self.w)
+            self.w = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,325 @@
+// C ABI of the gfx950 iS-KV library: argument checks, workspace carving,
+// host-side bookkeeping of the exact window / pending FIFO, and dispatch to
+// the kernel launchers. See include/iskv.h for the contract of every call.
+#include "iskv_internal.h"
+
+#include <new>
+#include <stdlib.h>
+#include <string.h>
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kGramSplits = 17;  // 16 row chunks of C + 1 slice for B
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+bool cfg_ok(const iskv_config* c) {
+  if (!c) return false;
+  if (c->D < 64 || c->D > 8192 || (c->D % 64) != 0) return false;
+  if (c->r_max < 1 || c->r_max > c->D) return false;
+  if (c->b_max < 1 || c->b_max > 64) return false;
+  if (c->r_max + c->b_max > 1024) return false;
+  if (c->n_cap < 1) return false;
+  if (c->reorth_every_rows < 0) return false;
+  if (!(c->resid_rel_tol >= 0.f)) return false;
+  if (c->flags & ~ISKV_NO_COORD_SYNC) return false;
+  return true;
+}
+
+// Layout of the workspace; when base == nullptr only the size is computed.
+size_t carve(const iskv_config* c, char* base, isvd_ws* w) {
+  const size_t D = c->D, R = c->r_max, Bm = c->b_max, M = c->r_max + c->b_max;
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    char* p = base ? base + off : nullptr;
+    off = align_up(off + bytes);
+    return p;
+  };
+  isvd_ws tmp;
+  isvd_ws& x = w ? *w : tmp;
+  x.st = (int32_t*)take(ST_COUNT * sizeof(int32_t));
+  x.Bbf = (uint16_t*)take(D * R * 2);
+  x.Q = (float*)take(Bm * R * 4);
+  x.E = (float*)take(Bm * D * 4);
+  x.EB = (float*)take(Bm * R * 4);
+  x.GE = (double*)take(Bm * Bm * 8);
+  x.VE = (double*)take(Bm * Bm * 8);
+  x.rho = (double*)take(Bm * 8);
+  x.P = (float*)take(D * Bm * 4);
+  x.FP = (float*)take(Bm * Bm * 4);
+  x.A = (double*)take(M * M * 8);
+  x.V = (double*)take(M * M * 8);
+  x.lam = (double*)take(M * 8);
+  x.rot_cap = 0;
+  x.rot = nullptr;
+  x.Hc = (float*)take(M * R * 4);
+  x.T2 = (float*)take(R * R * 4);
+  x.sig_new = (float*)take(M * 4);
+  x.gram_splits = kGramSplits;
+  x.GC = (double*)take((size_t)kGramSplits * R * R * 8);
+  x.GB = (double*)take(R * R * 8);
+  x.RB = (double*)take(R * R * 8);
+  x.order = (int32_t*)take(M * 4);
+  return off;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* iskv_strerror(int status) {
+  switch (status) {
+    case ISKV_OK: return "ok";
+    case ISKV_EINVAL: return "invalid argument";
+    case ISKV_ECAPACITY: return "capacity exceeded";
+    case ISKV_EWORKSPACE: return "workspace too small or misaligned";
+    case ISKV_EHIP: return "HIP runtime error";
+    case ISKV_ENONFINITE: return "non-finite values met on the device";
+    case ISKV_ENOCONV: return "core eigensolver did not converge";
+    case ISKV_EMODE: return "operation not available in this mode";
+    default: return "unknown status";
+  }
+}
+
+size_t isvd_workspace_bytes(const iskv_config* cfg) {
+  if (!cfg_ok(cfg)) return 0;
+  return carve(cfg, nullptr, nullptr) + kAlign;
+}
+
+int isvd_init(isvd_handle** out, const iskv_config* cfg, float* C, float* sigma, float* B,
+              int32_t* pos, void* workspace, size_t ws_bytes, void* stream) {
+  if (!out || !cfg_ok(cfg) || !C || !sigma || !B || !pos || !workspace) return ISKV_EINVAL;
+  if (((uintptr_t)workspace) % kAlign != 0) return ISKV_EWORKSPACE;
+  if (ws_bytes < carve(cfg, nullptr, nullptr)) return ISKV_EWORKSPACE;
+  if (iskv_kernel_setup() != ISKV_OK) return ISKV_EHIP;
+  isvd_handle* h = new (std::nothrow) isvd_handle();
+  if (!h) return ISKV_EINVAL;
+  h->cfg = *cfg;
+  h->C = C; h->sigma = sigma; h->B = B; h->pos = pos;
+  h->ws_base = workspace; h->ws_bytes = ws_bytes;
+  h->stream = (hipStream_t)stream;
+  h->m_max = cfg->r_max + cfg->b_max;
+  carve(cfg, (char*)workspace, &h->w);
+  h->n_host = 0;
+  h->folded_host = 0;
+  hipStream_t s = h->stream;
+  const size_t R = cfg->r_max;
+  if (hipMemsetAsync(h->w.st, 0, ST_COUNT * sizeof(int32_t), s) != hipSuccess ||
+      hipMemsetAsync(C, 0, (size_t)cfg->n_cap * R * sizeof(float), s) != hipSuccess ||
+      hipMemsetAsync(sigma, 0, R * sizeof(float), s) != hipSuccess ||
+      hipMemsetAsync(B, 0, (size_t)cfg->D * R * sizeof(float), s) != hipSuccess ||
+      hipMemsetAsync(h->w.Bbf, 0, (size_t)cfg->D * R * 2, s) != hipSuccess ||
+      hipMemsetAsync(pos, 0xff, (size_t)cfg->n_cap * sizeof(int32_t), s) != hipSuccess) {
+    delete h;
+    return ISKV_EHIP;
+  }
+  *out = h;
+  return ISKV_OK;
+}
+
+int32_t isvd_rows(const isvd_handle* h) { return h ? h->n_host : 0; }
+
+int isvd_merge_block(isvd_handle* h, const float* F, const int32_t* pos_F, int32_t b) {
+  if (!h || !F || !pos_F) return ISKV_EINVAL;
+  if (b < 1 || b > h->cfg.b_max) return ISKV_EINVAL;
+  if ((int64_t)h->n_host + b > h->cfg.n_cap) return ISKV_ECAPACITY;
+  int rc = iskv_launch_merge(h, F, pos_F, b);
+  if (rc) return rc;
+  const int before = h->folded_host;
+  h->n_host += b;
+  h->folded_host += b;
+  const int T = h->cfg.reorth_every_rows;
+  if (T > 0 && !(h->cfg.flags & ISKV_NO_COORD_SYNC) && (h->folded_host / T) > (before / T)) {
+    rc = iskv_launch_reorth(h);
+    if (rc) return rc;
+  }
+  return ISKV_OK;
+}
+
+int isvd_reorth(isvd_handle* h) {
+  if (!h) return ISKV_EINVAL;
+  if (h->cfg.flags & ISKV_NO_COORD_SYNC) return ISKV_EMODE;
+  return iskv_launch_reorth(h);
+}
+
+int isvd_query(isvd_handle* h, int32_t* n, int32_t* k, int32_t* status) {
+  if (!h) return ISKV_EINVAL;
+  int32_t st[ST_COUNT];
+  ISKV_HIP_CHECK(hipStreamSynchronize(h->stream));
+  ISKV_HIP_CHECK(hipMemcpy(st, h->w.st, sizeof(st), hipMemcpyDeviceToHost));
+  if (n) *n = st[ST_N];
+  if (k) *k = st[ST_K];
+  if (status) *status = st[ST_STATUS];
+  return ISKV_OK;
+}
+
+void isvd_destroy(isvd_handle* h) { delete h; }
+
+int kv_reconstruct(const isvd_handle* h, const float* X_exact, const int32_t* pos_exact,
+                   int32_t n_exact, int32_t n_total, int32_t head_dim, int32_t apply_rope,
+                   float rope_theta, void* out, int32_t out_dtype, void* stream) {
+  if (!h || !out) return ISKV_EINVAL;
+  if (n_exact < 0 || (n_exact > 0 && (!X_exact || !pos_exact))) return ISKV_EINVAL;
+  if (n_total < h->n_host || n_total < 0) return ISKV_EINVAL;
+  if (head_dim < 2 || (head_dim & 1) || h->cfg.D % head_dim != 0) return ISKV_EINVAL;
+  {
+    const int W = (h->cfg.D % 128 == 0 && 128 % head_dim == 0) ? 128 : 64;
+    if (W % head_dim != 0) return ISKV_EINVAL;
+  }
+  if (out_dtype != ISKV_OUT_BF16 && out_dtype != ISKV_OUT_FP32) return ISKV_EINVAL;
+  if (apply_rope && !(rope_theta > 1.f)) return ISKV_EINVAL;
+  hipStream_t s = stream ? (hipStream_t)stream : h->stream;
+  return iskv_launch_reconstruct(h, X_exact, pos_exact, n_exact, n_total, head_dim, apply_rope,
+                                 rope_theta, out, out_dtype, s);
+}
+
+size_t decode_attend_workspace_bytes(int32_t batch, int32_t n, int32_t Hq, int32_t dh) {
+  if (batch < 1 || n < 1 || Hq < 1 || dh != 128) return 0;
+  return iskv_attend_ws_bytes(batch, n, Hq, dh);
+}
+
+int decode_attend(const uint16_t* q, const uint16_t* K, const uint16_t* V, int32_t batch,
+                  int32_t n, int32_t Hq, int32_t Hkv, int32_t dh, float scale, uint16_t* out,
+                  void* workspace, size_t ws_bytes, void* stream) {
+  if (!q || !K || !V || !out || !workspace) return ISKV_EINVAL;
+  if (batch < 1 || n < 1 || Hq < 1 || Hkv < 1 || dh != 128) return ISKV_EINVAL;
+  if (Hq % Hkv != 0 || Hq / Hkv > 16) return ISKV_EINVAL;
+  if (ws_bytes < decode_attend_workspace_bytes(batch, n, Hq, dh)) return ISKV_EWORKSPACE;
+  return iskv_launch_attend(q, K, V, batch, n, Hq, Hkv, dh, scale, out, workspace, ws_bytes,
+                            (hipStream_t)stream);
+}
+
+// ---- exact window and pending FIFO ----------------------------------------
+int32_t iskv_window_rows(int32_t prot_cap, int32_t window, int32_t block) {
+  if (prot_cap < 0 || window < 0 || block < 1) return 0;
+  return prot_cap + window + block;
+}
+
+int iskv_window_init(iskv_window** out, isvd_handle* h, int32_t prot_cap, int32_t window,
+                     int32_t block, float* rows, int32_t* pos, void* stream) {
+  if (!out || !h || !rows || !pos) return ISKV_EINVAL;
+  if (prot_cap < 0 || window < 0 || block < 1 || block > h->cfg.b_max) return ISKV_EINVAL;
+  iskv_window* w = new (std::nothrow) iskv_window();
+  if (!w) return ISKV_EINVAL;
+  w->h = h;
+  w->D = h->cfg.D;
+  w->prot_cap = prot_cap;
+  w->window = window;
+  w->block = block;
+  w->rows = rows;
+  w->pos = pos;
+  w->stream = (hipStream_t)stream;
+  w->n_prot = 0;
+  w->appended = 0;
+  w->pending = 0;
+  int total = prot_cap + window + block;
+  if (iskv_launch_fill_pos(pos, total, -1, 0, w->stream) != ISKV_OK) {
+    delete w;
+    return ISKV_EHIP;
+  }
+  *out = w;
+  return ISKV_OK;
+}
+
+int iskv_window_protect(iskv_window* w, const float* rows, const int32_t* pos_host, int32_t count) {
+  if (!w || count < 0 || (count > 0 && (!rows || !pos_host))) return ISKV_EINVAL;
+  if (w->n_prot + count > w->prot_cap) return ISKV_ECAPACITY;
+  if (count == 0) return ISKV_OK;
+  float* dst = w->rows + (size_t)w->n_prot * w->D;
+  int rc = iskv_launch_window_move(dst, nullptr, rows, nullptr, 0, count, w->D, w->stream);
+  if (rc) return rc;
+  for (int i = 0; i < count; ++i) {
+    rc = iskv_launch_fill_pos(w->pos + w->n_prot + i, 1, pos_host[i], 0, w->stream);
+    if (rc) return rc;
+  }
+  w->n_prot += count;
+  return ISKV_OK;
+}
+
+// Move `count` consecutive window slots starting at `slot` (wrapping) to dst.
+static int move_from_ring(iskv_window* w, int slot, int count, float* dst, int32_t* dpos) {
+  const int D = w->D;
+  float* win_rows = w->rows + (size_t)w->prot_cap * D;
+  int32_t* win_pos = w->pos + w->prot_cap;
+  int first = count < w->window - slot ? count : w->window - slot;
+  int rc = iskv_launch_window_move(dst, dpos, win_rows + (size_t)slot * D, win_pos + slot, 0, first, D,
+                                   w->stream);
+  if (rc || first == count) return rc;
+  return iskv_launch_window_move(dst + (size_t)first * D, dpos + first, win_rows, win_pos, 0,
+                                 count - first, D, w->stream);
+}
+
+// Write `count` new rows (positions pos0..) into consecutive slots from `slot`.
+static int write_to_ring(iskv_window* w, int slot, const float* src, int32_t pos0, int count) {
+  const int D = w->D;
+  float* win_rows = w->rows + (size_t)w->prot_cap * D;
+  int32_t* win_pos = w->pos + w->prot_cap;
+  int first = count < w->window - slot ? count : w->window - slot;
+  int rc = iskv_launch_window_move(win_rows + (size_t)slot * D, win_pos + slot, src, nullptr, pos0,
+                                   first, D, w->stream);
+  if (rc || first == count) return rc;
+  return iskv_launch_window_move(win_rows, win_pos, src + (size_t)first * D, nullptr, pos0 + first,
+                                 count - first, D, w->stream);
+}
+
+int iskv_window_append(iskv_window* w, const float* rows, int32_t pos0, int32_t count,
+                       int32_t* merges) {
+  if (merges) *merges = 0;
+  if (!w || count < 0 || (count > 0 && !rows)) return ISKV_EINVAL;
+  const int D = w->D;
+  float* pend_rows = w->rows + (size_t)(w->prot_cap + w->window) * D;
+  int32_t* pend_pos = w->pos + w->prot_cap + w->window;
+  int done = 0;
+  while (done < count) {
+    // rows handled in this chunk: never more than fill the pending area once
+    int c = count - done;
+    if (c > w->block - w->pending) c = w->block - w->pending;
+    const int64_t r = w->appended;
+    if (w->window > 0) {
+      if (w->window < c) c = w->window;
+      // rows r - window .. r - window + c - 1 leave the window (those that exist)
+      int64_t first_out = r - w->window;
+      int leave = 0;
+      int64_t lo = first_out < 0 ? 0 : first_out;
+      int64_t hi = first_out + c;  // exclusive
+      if (hi > lo) leave = (int)(hi - lo);
+      if (leave > 0) {
+        int rc = move_from_ring(w, (int)(lo % w->window), leave,
+                                pend_rows + (size_t)w->pending * D, pend_pos + w->pending);
+        if (rc) return rc;
+        w->pending += leave;
+      }
+      int rc = write_to_ring(w, (int)(r % w->window), rows + (size_t)done * D, pos0 + done, c);
+      if (rc) return rc;
+    } else {
+      int rc = iskv_launch_window_move(pend_rows + (size_t)w->pending * D, pend_pos + w->pending,
+                                       rows + (size_t)done * D, nullptr, pos0 + done, c, D, w->stream);
+      if (rc) return rc;
+      w->pending += c;
+    }
+    w->appended += c;
+    done += c;
+    if (w->pending == w->block) {
+      int rc = isvd_merge_block(w->h, pend_rows, pend_pos, w->block);
+      if (rc) return rc;
+      rc = iskv_launch_fill_pos(pend_pos, w->block, -1, 0, w->stream);
+      if (rc) return rc;
+      w->pending = 0;
+      if (merges) (*merges)++;
+    }
+  }
+  return ISKV_OK;
+}
+
+int iskv_window_exact(const iskv_window* w, const float** rows, const int32_t** pos, int32_t* count) {
+  if (!w) return ISKV_EINVAL;
+  if (rows) *rows = w->rows;
+  if (pos) *pos = w->pos;
+  if (count) *count = w->prot_cap + w->window + w->block;
+  return ISKV_OK;
+}
+
+void iskv_window_destroy(iskv_window* w) { delete w; }
+
+}  // extern "C"

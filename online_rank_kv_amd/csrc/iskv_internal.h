@@ -1,0 +1,106 @@
+// Internal declarations of the gfx950 iS-KV library: handle layout, device
+// state slots and the launch helpers shared by the translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/iskv.h"
+
+// ---- device state word slots (int32 array at the head of the workspace) ----
+enum {
+  ST_N = 0,        // rows in the compressed history
+  ST_K = 1,        // current rank k
+  ST_P = 2,        // residual directions kept by the last merge
+  ST_FOLDED = 3,   // regular folded rows (re-orthogonalisation schedule)
+  ST_STATUS = 4,   // ISKV_DEV_* bits
+  ST_M = 5,        // core width k + p of the merge in flight
+  ST_KNEW = 6,     // r' = min(r, k + p) of the merge in flight
+  ST_SWEEPS = 7,   // Jacobi sweeps used by the last eigensolve
+  ST_EZERO = 8,    // 1 when the residual of the merge in flight is exactly zero
+  ST_JM = 9,       // order of the matrix handed to the Jacobi eigensolver
+  ST_ROUNDS = 10,  // rounds logged by the last Jacobi solve
+  ST_COUNT = 16
+};
+
+// Sub-buffers carved out of the caller's workspace (all 256-byte aligned).
+struct isvd_ws {
+  int32_t* st;        // [ST_COUNT]
+  uint16_t* Bbf;      // [D x r_max] bf16 copy of B for reconstruction
+  float* Q;           // [b_max x r_max]  F B
+  float* E;           // [b_max x D]      residual
+  float* EB;          // [b_max x r_max]  E B
+  double* GE;         // [b_max x b_max]  E E^T
+  double* VE;         // [b_max x b_max]  its eigenvectors (sorted)
+  double* rho;        // [b_max]          residual singular values
+  float* P;           // [D x b_max]      residual basis
+  float* FP;          // [b_max x b_max]  F P
+  double* A;          // [m_max x m_max]  core Gram / reorth matrix
+  double* V;          // [m_max x m_max]  eigenvectors
+  double* lam;        // [m_max]
+  double* rot;        // [rot_cap] Jacobi rotation log (c, s) pairs
+  float* Hc;          // [m_max x r_max]  kept right singular vectors of the core
+  float* T2;          // [r_max x r_max]  second transform (reorth: basis side)
+  float* sig_new;     // [m_max]
+  double* GC;         // [gram_splits x r_max x r_max] partial Grams for reorth
+  double* GB;         // [r_max x r_max]
+  double* RB;         // [r_max x r_max]  Cholesky factor of B^T B
+  int32_t* order;     // [m_max]
+  size_t rot_cap;     // doubles in rot
+  int gram_splits;
+};
+
+struct isvd_handle {
+  iskv_config cfg;
+  float* C;
+  float* sigma;
+  float* B;
+  int32_t* pos;
+  void* ws_base;
+  size_t ws_bytes;
+  hipStream_t stream;
+  isvd_ws w;
+  int32_t m_max;       // r_max + b_max
+  int32_t n_host;      // rows folded (host mirror, exact)
+  int32_t folded_host; // folded-row counter (host mirror, exact)
+};
+
+struct iskv_window {
+  isvd_handle* h;
+  int32_t D, prot_cap, window, block;
+  float* rows;
+  int32_t* pos;
+  hipStream_t stream;
+  int32_t n_prot;      // protected rows stored
+  int64_t appended;    // rows appended through the window
+  int32_t pending;     // rows waiting in the pending area
+  int32_t prot_flags;  // unused, reserved
+};
+
+#define ISKV_JACOBI_MAX_SWEEPS 40
+#define ISKV_RESID_MAX_SWEEPS 60
+
+// ---- launch helpers implemented in the kernel translation units ----
+int iskv_kernel_setup();
+int iskv_launch_merge(isvd_handle* h, const float* F, const int32_t* pos_F, int32_t b);
+int iskv_launch_reorth(isvd_handle* h);
+int iskv_launch_reconstruct(const isvd_handle* h, const float* X_exact, const int32_t* pos_exact,
+                            int32_t n_exact, int32_t n_total, int32_t head_dim, int32_t apply_rope,
+                            float rope_theta, void* out, int32_t out_dtype, hipStream_t s);
+int iskv_launch_attend(const uint16_t* q, const uint16_t* K, const uint16_t* V, int32_t batch,
+                       int32_t n, int32_t Hq, int32_t Hkv, int32_t dh, float scale, uint16_t* out,
+                       void* ws, size_t ws_bytes, hipStream_t s);
+size_t iskv_attend_ws_bytes(int32_t batch, int32_t n, int32_t Hq, int32_t dh);
+int iskv_launch_window_move(float* dst_rows, int32_t* dst_pos, const float* src_rows,
+                            const int32_t* src_pos, int32_t src_pos_base, int32_t count, int32_t D,
+                            hipStream_t s);
+int iskv_launch_fill_pos(int32_t* pos, int32_t count, int32_t value0, int32_t step, hipStream_t s);
+int iskv_launch_copy_pos_host(int32_t* pos_dev, const int32_t* pos_host, int32_t count,
+                              hipStream_t s);
+
+#define ISKV_HIP_CHECK(expr)                 \
+  do {                                       \
+    hipError_t _e = (expr);                  \
+    if (_e != hipSuccess) return ISKV_EHIP;  \
+  } while (0)

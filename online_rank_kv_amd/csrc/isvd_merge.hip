@@ -1,0 +1,821 @@
+// Block-incremental SVD merge and re-orthogonalisation on gfx950.
+//
+// Method: iS-KV notes (Zhou), §4.1-§4.4 and Algorithm 2. The history is kept
+// as coordinates C = U diag(sigma) (n x k, fp32) and an orthonormal basis B
+// (D x k, fp32). One merge of a pending block F (b x D):
+//   Q = F B;  E = F - Q B^T;  E -= (E B) B^T            (projection, residual)
+//   E E^T = V_E diag(rho^2) V_E^T, keep rho_j > tau      (residual basis)
+//   P = E^T V_E[:, :p] diag(1/rho)                       (= P_E W of the notes)
+//   M = [Q, F P];  Z^T Z = diag(sigma^2, 0) + M^T M      (core Gram, eq.(7))
+//   Z^T Z = H diag(sigma+^2) H^T, keep r' = min(r, k+p)  (core SVD via Jacobi)
+//   C_old <- C_old H[:k];  C_new = M H;  B <- [B, P] H   (coordinate sync)
+// Storing C = U Sigma makes the old rows' update C H[:k] (= U G_top Sigma+)
+// and the new rows M H (= G_bot Sigma+), so G is never formed and nothing is
+// divided by a small singular value.
+#include "iskv_internal.h"
+
+#include <math.h>
+#include <string.h>
+
+namespace {
+
+// ----------------------------------------------------------------------------
+// Device-side dimension: value = dev ? (*dev) * mul + add : v. Lets kernels be
+// launched for the maximal shape while the actual extent (k, p, k+p, ...)
+// lives in device memory, so a merge never waits for the host.
+struct Dim {
+  int v;
+  const int32_t* dev;
+  int mul;
+  int add;
+};
+__device__ __forceinline__ int dval(const Dim& d) { return d.dev ? (*d.dev) * d.mul + d.add : d.v; }
+static inline Dim hdim(int v) { return Dim{v, nullptr, 0, 0}; }
+static inline Dim ddim(const int32_t* p, int mul = 1, int add = 0) { return Dim{0, p, mul, add}; }
+
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ----------------------------------------------------------------------------
+// Small fp32 GEMM, 64x64 tile, 256 threads, 4x4 outputs per thread:
+//   C(i, j) = alpha * sum_k opA(i, k) opB(k, j) + beta * Cin(i, j)
+// opA(i, k) = TA ? A[k*lda + i] : A[i*lda + k]; likewise opB with TB.
+// Cin may alias C (each element is read and written by the same thread).
+template <bool TA, bool TB>
+__global__ __launch_bounds__(256) void sgemm64_kernel(const float* __restrict__ A, int lda,
+                                                      const float* __restrict__ Bm, int ldb,
+                                                      float* C, int ldc, const float* Cin,
+                                                      int ldcin, Dim Md, Dim Nd, Dim Kd,
+                                                      float alpha, float beta) {
+  const int M = dval(Md), N = dval(Nd), K = dval(Kd);
+  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+  if (i0 >= M || j0 >= N) return;
+  __shared__ float As[16][68];
+  __shared__ float Bs[16][68];
+  const int t = threadIdx.x, tx = t & 15, ty = t >> 4;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += 16) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      int idx = t + e * 256;
+      int r, c;
+      float v;
+      if (!TA) {
+        r = idx >> 4; c = idx & 15;
+        v = (i0 + r < M && k0 + c < K) ? A[(size_t)(i0 + r) * lda + k0 + c] : 0.f;
+      } else {
+        c = idx >> 6; r = idx & 63;
+        v = (i0 + r < M && k0 + c < K) ? A[(size_t)(k0 + c) * lda + i0 + r] : 0.f;
+      }
+      As[c][r] = v;
+      if (!TB) {
+        c = idx >> 6; r = idx & 63;
+        v = (j0 + r < N && k0 + c < K) ? Bm[(size_t)(k0 + c) * ldb + j0 + r] : 0.f;
+      } else {
+        r = idx >> 4; c = idx & 15;
+        v = (j0 + r < N && k0 + c < K) ? Bm[(size_t)(j0 + r) * ldb + k0 + c] : 0.f;
+      }
+      Bs[c][r] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) { a[u] = As[kk][ty * 4 + u]; b[u] = Bs[kk][tx * 4 + u]; }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(a[u], b[v], acc[u][v]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    int i = i0 + ty * 4 + u;
+    if (i >= M) continue;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      int j = j0 + tx * 4 + v;
+      if (j >= N) continue;
+      float o = alpha * acc[u][v];
+      if (beta != 0.f) o += beta * Cin[(size_t)i * ldcin + j];
+      C[(size_t)i * ldc + j] = o;
+    }
+  }
+}
+
+template <bool TA, bool TB>
+static void sgemm(hipStream_t s, int Mmax, int Nmax, const float* A, int lda, const float* B,
+                  int ldb, float* C, int ldc, const float* Cin, int ldcin, Dim M, Dim N, Dim K,
+                  float alpha, float beta) {
+  dim3 grid((Nmax + 63) / 64, (Mmax + 63) / 64);
+  hipLaunchKernelGGL((sgemm64_kernel<TA, TB>), grid, dim3(256), 0, s, A, lda, B, ldb, C, ldc, Cin,
+                     ldcin, M, N, K, alpha, beta);
+}
+
+// ----------------------------------------------------------------------------
+// Residual Gram E E^T in fp64 (b x b), one workgroup per row i. Also latches
+// the non-finite flag when the block (hence E) holds NaN or Inf.
+__global__ __launch_bounds__(256) void resid_gram_kernel(const float* __restrict__ E, int D,
+                                                         int b, double* GE, int32_t* st) {
+  const int i = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int bad = 0;
+  for (int j = wave; j < b; j += 4) {
+    double acc = 0.0;
+    for (int d = lane; d < D; d += 64) {
+      float x = E[(size_t)i * D + d], y = E[(size_t)j * D + d];
+      if (j == i && !isfinite(x)) bad = 1;
+      acc = fma((double)x, (double)y, acc);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (lane == 0) GE[i * b + j] = acc;
+  }
+  if (bad) atomicOr(&st[ST_STATUS], ISKV_DEV_NONFINITE);
+}
+
+// ----------------------------------------------------------------------------
+// Cyclic Jacobi for a small symmetric fp64 matrix held in LDS, parallel
+// (round-robin) ordering, executed by the whole block. S is n x n with
+// leading dimension ld, V receives the eigenvectors (columns). Returns the
+// number of sweeps; a sweep with no rotation above the relative threshold
+// |s_pq| <= tol * sqrt(|s_pp s_qq|) ends the iteration.
+__device__ int jacobi_lds(double* S, double* V, int n, int ld, double tol, int max_sweeps,
+                          double* cs, double* sn, int* pp, int* qq, int* active) {
+  const int t = threadIdx.x, nt = blockDim.x;
+  for (int idx = t; idx < n * n; idx += nt) V[(idx / n) * ld + idx % n] = (idx / n == idx % n) ? 1.0 : 0.0;
+  __syncthreads();
+  if (n < 2) return 0;
+  const int N = (n + 1) & ~1, half = N / 2;
+  int sweep = 0;
+  for (; sweep < max_sweeps; ++sweep) {
+    int rot_this_sweep = 0;
+    for (int round = 0; round < N - 1; ++round) {
+      if (t == 0) *active = 0;
+      __syncthreads();
+      for (int i = t; i < half; i += nt) {
+        int a = (i == 0) ? round % (N - 1) : (round + i) % (N - 1);
+        int b = (i == 0) ? N - 1 : (round - i + (N - 1)) % (N - 1);
+        int p = a < b ? a : b, q = a < b ? b : a;
+        double c = 1.0, s = 0.0;
+        if (q < n) {
+          double app = S[p * ld + p], aqq = S[q * ld + q], apq = S[p * ld + q];
+          if (apq != 0.0 && fabs(apq) > tol * sqrt(fabs(app * aqq))) {
+            double tau = (aqq - app) / (2.0 * apq);
+            double tt = (tau >= 0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
+            c = 1.0 / sqrt(1.0 + tt * tt);
+            s = tt * c;
+            atomicAdd(active, 1);
+          }
+        }
+        cs[i] = c; sn[i] = s; pp[i] = p; qq[i] = q;
+      }
+      __syncthreads();
+      int act = *active;
+      if (act) {
+        rot_this_sweep = 1;
+        // S <- J^T S J over 2x2 blocks (pairs a <= b), mirrored; V <- V J.
+        for (int blk = t; blk < half * half; blk += nt) {
+          int a = blk / half, bb = blk % half;
+          if (a > bb) continue;
+          int pa = pp[a], qa = qq[a], pb = pp[bb], qb = qq[bb];
+          if (qa >= n || qb >= n) continue;
+          double ca = cs[a], sa = sn[a], cb = cs[bb], sb = sn[bb];
+          if (sa == 0.0 && sb == 0.0) continue;
+          double x11 = S[pa * ld + pb], x12 = S[pa * ld + qb], x21 = S[qa * ld + pb],
+                 x22 = S[qa * ld + qb];
+          double y11 = ca * x11 - sa * x21, y12 = ca * x12 - sa * x22;
+          double y21 = sa * x11 + ca * x21, y22 = sa * x12 + ca * x22;
+          double z11 = y11 * cb - y12 * sb, z12 = y11 * sb + y12 * cb;
+          double z21 = y21 * cb - y22 * sb, z22 = y21 * sb + y22 * cb;
+          if (a == bb) { z12 = 0.0; z21 = 0.0; }
+          S[pa * ld + pb] = z11; S[pa * ld + qb] = z12; S[qa * ld + pb] = z21; S[qa * ld + qb] = z22;
+          if (a != bb) {
+            S[pb * ld + pa] = z11; S[qb * ld + pa] = z12; S[pb * ld + qa] = z21; S[qb * ld + qa] = z22;
+          }
+        }
+        for (int e = t; e < n * half; e += nt) {
+          int x = e / half, a = e % half;
+          int p = pp[a], q = qq[a];
+          if (q >= n) continue;
+          double c = cs[a], s = sn[a];
+          if (s == 0.0) continue;
+          double vp = V[x * ld + p], vq = V[x * ld + q];
+          V[x * ld + p] = c * vp - s * vq;
+          V[x * ld + q] = s * vp + c * vq;
+        }
+      }
+      __syncthreads();
+    }
+    if (!rot_this_sweep) break;
+  }
+  return sweep;
+}
+
+// ----------------------------------------------------------------------------
+// Residual basis: eigen-decompose E E^T (b x b), sort descending, apply the
+// threshold of §4.1 and publish p. One workgroup.
+__global__ __launch_bounds__(256) void resid_basis_kernel(const double* __restrict__ GE, int b,
+                                                          int D, const float* __restrict__ sigma,
+                                                          float delta, double* VE, double* rho,
+                                                          int32_t* st) {
+  extern __shared__ double smem[];
+  const int ld = b + 1;
+  double* S = smem;
+  double* V = S + b * ld;
+  double* lam = V + b * ld;
+  double* cs = lam + b;
+  double* sn = cs + 32;
+  int* pp = (int*)(sn + 32);
+  int* qq = pp + 32;
+  int* active = qq + 32;
+  int* order = active + 1;
+  __shared__ int any_nonzero;
+  const int t = threadIdx.x;
+  if (t == 0) any_nonzero = 0;
+  __syncthreads();
+  for (int idx = t; idx < b * b; idx += blockDim.x) {
+    double v = GE[idx];
+    S[(idx / b) * ld + idx % b] = v;
+    if (v != 0.0) any_nonzero = 1;
+  }
+  __syncthreads();
+  const int k = st[ST_K];
+  if (!any_nonzero || k >= D) {
+    if (t == 0) { st[ST_P] = 0; st[ST_M] = k; st[ST_EZERO] = any_nonzero ? 0 : 1; }
+    return;
+  }
+  jacobi_lds(S, V, b, ld, 1e-15, ISKV_RESID_MAX_SWEEPS, cs, sn, pp, qq, active);
+  for (int i = t; i < b; i += blockDim.x) lam[i] = S[i * ld + i];
+  __syncthreads();
+  // rank by descending eigenvalue, ties by index
+  for (int i = t; i < b; i += blockDim.x) {
+    int rnk = 0;
+    for (int j = 0; j < b; ++j) rnk += (lam[j] > lam[i]) || (lam[j] == lam[i] && j < i);
+    order[rnk] = i;
+  }
+  __syncthreads();
+  for (int idx = t; idx < b * b; idx += blockDim.x) {
+    int row = idx / b, col = idx % b;
+    VE[row * b + col] = V[row * ld + order[col]];
+  }
+  for (int j = t; j < b; j += blockDim.x) rho[j] = sqrt(fmax(lam[order[j]], 0.0));
+  __syncthreads();
+  if (t == 0) {
+    double rho1 = sqrt(fmax(lam[order[0]], 0.0));
+    double s1 = (k > 0) ? (double)sigma[0] : 0.0;
+    double sc = fmax(s1, rho1);
+    double floor_ = (double)(D > b ? D : b) * 1.1920928955078125e-07 * sc;
+    double tau = fmax((double)delta * sc, floor_);
+    int p = 0;
+    for (int j = 0; j < b; ++j) p += sqrt(fmax(lam[order[j]], 0.0)) > tau;
+    if (p > D - k) p = D - k;
+    st[ST_P] = p;
+    st[ST_M] = k + p;
+    st[ST_EZERO] = 0;
+  }
+}
+
+// P[:, j] = E^T V_E[:, j] / rho_j for j < p (D x b_max, fp64 accumulation).
+__global__ __launch_bounds__(256) void make_p_kernel(const float* __restrict__ E, int D, int b,
+                                                     const double* __restrict__ VE,
+                                                     const double* __restrict__ rho, float* P,
+                                                     int ldp, const int32_t* st) {
+  const int p = st[ST_P];
+  const int d = blockIdx.x * blockDim.x + threadIdx.x;
+  if (d >= D) return;
+  for (int j = 0; j < p; ++j) {
+    double acc = 0.0;
+    for (int i = 0; i < b; ++i) acc = fma((double)E[(size_t)i * D + d], VE[i * b + j], acc);
+    P[(size_t)d * ldp + j] = (float)(acc / rho[j]);
+  }
+}
+
+// Core Gram A = diag(sigma^2, 0_p) + M^T M in fp64, M = [Q[:, :k], FP[:, :p]] (b x m).
+__global__ __launch_bounds__(256) void core_gram_kernel(const float* __restrict__ Q, int ldq,
+                                                        const float* __restrict__ FP, int ldfp,
+                                                        const float* __restrict__ sigma, int b,
+                                                        double* A, int lda, const int32_t* st) {
+  const int k = st[ST_K], m = st[ST_M];
+  const int i = blockIdx.y * 16 + (threadIdx.x >> 4);
+  const int j = blockIdx.x * 16 + (threadIdx.x & 15);
+  if (i >= m || j >= m) return;
+  double acc = 0.0;
+  for (int r = 0; r < b; ++r) {
+    float mi = i < k ? Q[r * ldq + i] : FP[r * ldfp + (i - k)];
+    float mj = j < k ? Q[r * ldq + j] : FP[r * ldfp + (j - k)];
+    acc = fma((double)mi, (double)mj, acc);
+  }
+  if (i == j && i < k) acc += (double)sigma[i] * (double)sigma[i];
+  A[(size_t)i * lda + j] = acc;
+}
+
+// ----------------------------------------------------------------------------
+// Single-workgroup cyclic Jacobi eigensolver for the core (or the re-orth
+// matrix): S (m x m fp64, global, overwritten) and V (m x m fp64, global).
+// Parallel round-robin ordering; every round applies up to m/2 disjoint
+// rotations as 2x2 block updates. Threshold |s_pq| <= tol sqrt(s_pp s_qq).
+__global__ __launch_bounds__(1024) void core_jacobi_kernel(double* S, double* V, int ld,
+                                                           int32_t* st, double tol, int max_sweeps) {
+  __shared__ double cs[640], sn[640];
+  __shared__ int pp[640], qq[640];
+  __shared__ int active;
+  const int n = st[ST_JM];
+  const int t = threadIdx.x, nt = blockDim.x;
+  for (int idx = t; idx < n * n; idx += nt) V[(size_t)(idx / n) * ld + idx % n] = (idx / n == idx % n) ? 1.0 : 0.0;
+  __syncthreads();
+  int sweep = 0;
+  if (n >= 2) {
+    const int N = (n + 1) & ~1, half = N / 2;
+    for (; sweep < max_sweeps; ++sweep) {
+      int rot_sweep = 0;
+      for (int round = 0; round < N - 1; ++round) {
+        if (t == 0) active = 0;
+        __syncthreads();
+        for (int i = t; i < half; i += nt) {
+          int a = (i == 0) ? round % (N - 1) : (round + i) % (N - 1);
+          int b = (i == 0) ? N - 1 : (round - i + (N - 1)) % (N - 1);
+          int p = a < b ? a : b, q = a < b ? b : a;
+          double c = 1.0, s = 0.0;
+          if (q < n) {
+            double app = S[(size_t)p * ld + p], aqq = S[(size_t)q * ld + q], apq = S[(size_t)p * ld + q];
+            if (apq != 0.0 && fabs(apq) > tol * sqrt(fabs(app * aqq))) {
+              double tau = (aqq - app) / (2.0 * apq);
+              double tt = (tau >= 0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
+              c = 1.0 / sqrt(1.0 + tt * tt);
+              s = tt * c;
+              atomicAdd(&active, 1);
+            }
+          }
+          cs[i] = c; sn[i] = s; pp[i] = p; qq[i] = q;
+        }
+        __syncthreads();
+        if (active) {
+          rot_sweep = 1;
+          for (int blk = t; blk < half * half; blk += nt) {
+            int a = blk / half, bb = blk % half;
+            if (a > bb) continue;
+            int pa = pp[a], qa = qq[a], pb = pp[bb], qb = qq[bb];
+            if (qa >= n || qb >= n) continue;
+            double ca = cs[a], sa = sn[a], cb = cs[bb], sb = sn[bb];
+            if (sa == 0.0 && sb == 0.0) continue;
+            double x11 = S[(size_t)pa * ld + pb], x12 = S[(size_t)pa * ld + qb];
+            double x21 = S[(size_t)qa * ld + pb], x22 = S[(size_t)qa * ld + qb];
+            double y11 = ca * x11 - sa * x21, y12 = ca * x12 - sa * x22;
+            double y21 = sa * x11 + ca * x21, y22 = sa * x12 + ca * x22;
+            double z11 = y11 * cb - y12 * sb, z12 = y11 * sb + y12 * cb;
+            double z21 = y21 * cb - y22 * sb, z22 = y21 * sb + y22 * cb;
+            if (a == bb) { z12 = 0.0; z21 = 0.0; }
+            S[(size_t)pa * ld + pb] = z11; S[(size_t)pa * ld + qb] = z12;
+            S[(size_t)qa * ld + pb] = z21; S[(size_t)qa * ld + qb] = z22;
+            if (a != bb) {
+              S[(size_t)pb * ld + pa] = z11; S[(size_t)qb * ld + pa] = z12;
+              S[(size_t)pb * ld + qa] = z21; S[(size_t)qb * ld + qa] = z22;
+            }
+          }
+          for (int e = t; e < n * half; e += nt) {
+            int x = e / half, a = e % half;
+            int p = pp[a], q = qq[a];
+            if (q >= n) continue;
+            double c = cs[a], s = sn[a];
+            if (s == 0.0) continue;
+            double vp = V[(size_t)x * ld + p], vq = V[(size_t)x * ld + q];
+            V[(size_t)x * ld + p] = c * vp - s * vq;
+            V[(size_t)x * ld + q] = s * vp + c * vq;
+          }
+        }
+        __syncthreads();
+      }
+      if (!rot_sweep) break;
+    }
+  }
+  if (t == 0) {
+    st[ST_SWEEPS] = sweep;
+    if (sweep >= max_sweeps) atomicOr(&st[ST_STATUS], ISKV_DEV_NOCONV);
+  }
+}
+
+// Sort eigenpairs by descending eigenvalue, keep `keep` of them:
+// Hc[:, t] = V[:, order[t]] (fp32, ld r_max), sig_new[t] = sqrt(max(lambda, 0)).
+// keep = min(r_max, n) for a merge; n for re-orthogonalisation.
+__global__ __launch_bounds__(1024) void eig_finish_kernel(const double* __restrict__ S,
+                                                          const double* __restrict__ V, int ld,
+                                                          float* Hc, int ldh, float* sig_new,
+                                                          int32_t* order, int32_t* st, int r_max,
+                                                          int for_merge) {
+  __shared__ double lam[1024];
+  const int n = st[ST_JM];
+  const int t = threadIdx.x;
+  for (int i = t; i < n; i += blockDim.x) lam[i] = S[(size_t)i * ld + i];
+  __syncthreads();
+  for (int i = t; i < n; i += blockDim.x) {
+    int rnk = 0;
+    double li = lam[i];
+    for (int j = 0; j < n; ++j) rnk += (lam[j] > li) || (lam[j] == li && j < i);
+    order[rnk] = i;
+  }
+  __syncthreads();
+  const int keep = for_merge ? (n < r_max ? n : r_max) : n;
+  // Orientation: a kept column whose index is an old direction (col < k) is
+  // signed so that H[col, col] >= 0, i.e. the basis moves continuously. The
+  // synced product does not depend on it; the basis-only ablation does.
+  const int kold = for_merge ? st[ST_K] : 0;
+  for (int idx = t; idx < n * keep; idx += blockDim.x) {
+    int row = idx / keep, col = idx % keep;
+    double v = V[(size_t)row * ld + order[col]];
+    if (col < kold && V[(size_t)col * ld + order[col]] < 0.0) v = -v;
+    Hc[(size_t)row * ldh + col] = (float)v;
+  }
+  for (int c = t; c < keep; c += blockDim.x) sig_new[c] = (float)sqrt(fmax(lam[order[c]], 0.0));
+  if (t == 0 && for_merge) st[ST_KNEW] = keep;
+}
+
+// ----------------------------------------------------------------------------
+// Coordinate update (in place): rows [row0, row0 + rows) of C become
+// C[i, :kin] H[:kin, :kout]. One workgroup owns 32 rows for all output
+// columns, so the in-place rewrite is race-free. H is streamed through LDS.
+// kin/kout come from device memory (Dim).
+__global__ __launch_bounds__(256) void coord_update_kernel(float* C, int ldc, const float* __restrict__ H,
+                                                           int ldh, Dim kin_d, Dim kout_d,
+                                                           Dim rows_d, int r_max) {
+  const int kin = dval(kin_d), kout = dval(kout_d), rows = dval(rows_d);
+  const int i0 = blockIdx.x * 32;
+  if (i0 >= rows || kout == 0) return;
+  extern __shared__ float sm[];
+  float* Cs = sm;                 // [32][kin]
+  float* Hs = Cs + 32 * r_max;    // [32][64]
+  const int t = threadIdx.x;
+  const int nr = min(32, rows - i0);
+  for (int idx = t; idx < 32 * kin; idx += 256) {
+    int r = idx / kin, c = idx % kin;
+    Cs[r * r_max + c] = r < nr ? C[(size_t)(i0 + r) * ldc + c] : 0.f;
+  }
+  __syncthreads();
+  // thread: row group (t >> 6) * 8 .. +8, column (t & 63) within a 64-col tile
+  const int rg = (t >> 6) * 8, cc = t & 63;
+  for (int j0 = 0; j0 < kout; j0 += 64) {
+    float acc[8] = {};
+    for (int k0 = 0; k0 < kin; k0 += 32) {
+      __syncthreads();
+      for (int idx = t; idx < 32 * 64; idx += 256) {
+        int kk = idx >> 6, jj = idx & 63;
+        Hs[kk * 64 + jj] = (k0 + kk < kin && j0 + jj < kout) ? H[(size_t)(k0 + kk) * ldh + j0 + jj] : 0.f;
+      }
+      __syncthreads();
+      const int kl = min(32, kin - k0);
+      for (int kk = 0; kk < kl; ++kk) {
+        float h = Hs[kk * 64 + cc];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[u] = fmaf(Cs[(rg + u) * r_max + k0 + kk], h, acc[u]);
+      }
+    }
+    __syncthreads();
+    if (j0 + cc < kout) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (rg + u < nr) C[(size_t)(i0 + rg + u) * ldc + j0 + cc] = acc[u];
+    }
+  }
+}
+
+// New rows: C[n + i, :r'] = M[i, :] H (M = [Q, FP], b x m); pos[n + i] = pos_F[i].
+__global__ __launch_bounds__(256) void new_rows_kernel(const float* __restrict__ Q, int ldq,
+                                                       const float* __restrict__ FP, int ldfp,
+                                                       const float* __restrict__ H, int ldh,
+                                                       float* C, int ldc, int32_t* pos,
+                                                       const int32_t* __restrict__ pos_F, int b,
+                                                       const int32_t* st, int n_rows_before) {
+  const int k = st[ST_K], m = st[ST_M], kout = st[ST_KNEW];
+  const int i = blockIdx.x;
+  for (int j = threadIdx.x; j < kout; j += blockDim.x) {
+    float acc = 0.f;
+    for (int x = 0; x < m; ++x) {
+      float mx = x < k ? Q[i * ldq + x] : FP[i * ldfp + (x - k)];
+      acc = fmaf(mx, H[(size_t)x * ldh + j], acc);
+    }
+    C[(size_t)(n_rows_before + i) * ldc + j] = acc;
+  }
+  if (threadIdx.x == 0) pos[n_rows_before + i] = pos_F[i];
+}
+
+// Basis update (in place): B[d, :kout] = B[d, :k] H[:k] + P[d, :p] H[k:k+p],
+// and the bf16 copy of the new rows. One workgroup per 32 rows of B.
+// mode 0 (merge): kin = k, extra = p from st; mode 1 (reorth): kin = k, extra 0.
+__global__ __launch_bounds__(256) void basis_update_kernel(float* B, int ldb, const float* __restrict__ P,
+                                                           int ldp, const float* __restrict__ H,
+                                                           int ldh, uint16_t* Bbf, int D,
+                                                           const int32_t* st, int mode, int r_max) {
+  const int k = st[ST_K];
+  const int p = mode == 0 ? st[ST_P] : 0;
+  const int kout = mode == 0 ? st[ST_KNEW] : k;
+  const int m = k + p;
+  const int d0 = blockIdx.x * 32;
+  if (d0 >= D) return;
+  extern __shared__ float sm[];
+  float* Xs = sm;                       // [32][m_max]
+  const int ldx = r_max + 64;
+  float* Hs = Xs + 32 * ldx;            // [32][64]
+  const int t = threadIdx.x;
+  const int nr = min(32, D - d0);
+  for (int idx = t; idx < 32 * m; idx += 256) {
+    int r = idx / m, c = idx % m;
+    float v = 0.f;
+    if (r < nr) v = c < k ? B[(size_t)(d0 + r) * ldb + c] : P[(size_t)(d0 + r) * ldp + (c - k)];
+    Xs[r * ldx + c] = v;
+  }
+  __syncthreads();
+  const int rg = (t >> 6) * 8, cc = t & 63;
+  for (int j0 = 0; j0 < kout; j0 += 64) {
+    float acc[8] = {};
+    for (int k0 = 0; k0 < m; k0 += 32) {
+      __syncthreads();
+      for (int idx = t; idx < 32 * 64; idx += 256) {
+        int kk = idx >> 6, jj = idx & 63;
+        Hs[kk * 64 + jj] = (k0 + kk < m && j0 + jj < kout) ? H[(size_t)(k0 + kk) * ldh + j0 + jj] : 0.f;
+      }
+      __syncthreads();
+      const int kl = min(32, m - k0);
+      for (int kk = 0; kk < kl; ++kk) {
+        float h = Hs[kk * 64 + cc];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[u] = fmaf(Xs[(rg + u) * ldx + k0 + kk], h, acc[u]);
+      }
+    }
+    __syncthreads();
+    if (j0 + cc < kout) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (rg + u < nr) {
+          B[(size_t)(d0 + rg + u) * ldb + j0 + cc] = acc[u];
+          Bbf[(size_t)(d0 + rg + u) * r_max + j0 + cc] = f2bf(acc[u]);
+        }
+      }
+    }
+  }
+}
+
+// Commit a merge: sigma <- sigma+, k <- r', n += b, folded += b.
+__global__ void merge_commit_kernel(float* sigma, const float* __restrict__ sig_new, int32_t* st,
+                                    int b, int r_max) {
+  const int kout = st[ST_KNEW];
+  for (int j = threadIdx.x; j < r_max; j += blockDim.x) sigma[j] = j < kout ? sig_new[j] : 0.f;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    st[ST_K] = kout;
+    st[ST_N] += b;
+    st[ST_FOLDED] += b;
+  }
+}
+
+// Copy k (or another slot) into ST_JM so the eigensolver knows its order.
+__global__ void set_jm_kernel(int32_t* st, int from_slot) { st[ST_JM] = st[from_slot]; }
+
+// ----------------------------------------------------------------------------
+// Re-orthogonalisation helpers.
+// Partial Gram of the columns of X (rows x k, fp32) over a row chunk, fp64:
+// G_part[s][i][j] = sum_{rows in chunk s} X[r, i] X[r, j]. Grid: (tiles of
+// 16x16 over k x k, chunks). 256 threads.
+__global__ __launch_bounds__(256) void gram_partial_kernel(const float* __restrict__ X, int ldx,
+                                                           int rows, const int32_t* st,
+                                                           double* Gpart, int ldg,
+                                                           int rows_per_chunk) {
+  const int k = st[ST_K];
+  const int tiles = (k + 15) / 16;
+  const int ti = blockIdx.x / tiles, tj = blockIdx.x % tiles;
+  if (ti >= tiles) return;
+  const int i = ti * 16 + (threadIdx.x >> 4), j = tj * 16 + (threadIdx.x & 15);
+  const int r0 = blockIdx.y * rows_per_chunk, r1 = min(rows, r0 + rows_per_chunk);
+  __shared__ float Xi[64][17], Xj[64][17];
+  double acc = 0.0;
+  for (int rb = r0; rb < r1; rb += 64) {
+    for (int idx = threadIdx.x; idx < 64 * 16; idx += 256) {
+      int rr = idx >> 4, cc = idx & 15;
+      int row = rb + rr;
+      int ci = ti * 16 + cc, cj = tj * 16 + cc;
+      Xi[rr][cc] = (row < r1 && ci < k) ? X[(size_t)row * ldx + ci] : 0.f;
+      Xj[rr][cc] = (row < r1 && cj < k) ? X[(size_t)row * ldx + cj] : 0.f;
+    }
+    __syncthreads();
+    for (int rr = 0; rr < 64; ++rr)
+      acc = fma((double)Xi[rr][threadIdx.x >> 4], (double)Xj[rr][threadIdx.x & 15], acc);
+    __syncthreads();
+  }
+  if (i < k && j < k) Gpart[((size_t)blockIdx.y * ldg + i) * ldg + j] = acc;
+}
+
+// Sum the partial Grams of C, Cholesky of G_B = R_B^T R_B (upper R_B), and
+// H = R_B G_C R_B^T into S (k x k) for the eigensolver. One workgroup.
+__global__ __launch_bounds__(1024) void reorth_prep_kernel(double* GCpart,
+                                                           int nchunks, const double* __restrict__ GBpart,
+                                                           int nchunks_b, int ldg, double* GC,
+                                                           double* RB, double* S, int lds,
+                                                           int32_t* st) {
+  const int k = st[ST_K];
+  const int t = threadIdx.x, nt = blockDim.x;
+  for (int idx = t; idx < k * k; idx += nt) {
+    int i = idx / k, j = idx % k;
+    double a = 0.0, bsum = 0.0;
+    for (int s = 0; s < nchunks; ++s) a += GCpart[((size_t)s * ldg + i) * ldg + j];
+    for (int s = 0; s < nchunks_b; ++s) bsum += GBpart[((size_t)s * ldg + i) * ldg + j];
+    GC[(size_t)i * ldg + j] = a;
+    RB[(size_t)i * ldg + j] = bsum;  // G_B, factored in place below
+  }
+  __syncthreads();
+  // Right-looking Cholesky, upper factor stored in the upper triangle of RB.
+  for (int c = 0; c < k; ++c) {
+    if (t == 0) RB[(size_t)c * ldg + c] = sqrt(fmax(RB[(size_t)c * ldg + c], 1e-300));
+    __syncthreads();
+    double dcc = RB[(size_t)c * ldg + c];
+    for (int j = c + 1 + t; j < k; j += nt) RB[(size_t)c * ldg + j] /= dcc;
+    __syncthreads();
+    for (int idx = t; idx < (k - c - 1) * (k - c - 1); idx += nt) {
+      int i = c + 1 + idx / (k - c - 1), j = c + 1 + idx % (k - c - 1);
+      if (j >= i) RB[(size_t)i * ldg + j] -= RB[(size_t)c * ldg + i] * RB[(size_t)c * ldg + j];
+    }
+    __syncthreads();
+  }
+  for (int idx = t; idx < k * k; idx += nt) {
+    int i = idx / k, j = idx % k;
+    if (j < i) RB[(size_t)i * ldg + j] = 0.0;
+  }
+  __syncthreads();
+  // T = R_B G_C into the (now free) partial-Gram slice 0, then H = T R_B^T.
+  double* T = (double*)GCpart;
+  for (int idx = t; idx < k * k; idx += nt) {
+    int i = idx / k, j = idx % k;
+    double acc = 0.0;
+    for (int a = i; a < k; ++a) acc = fma(RB[(size_t)i * ldg + a], GC[(size_t)a * ldg + j], acc);
+    T[(size_t)i * ldg + j] = acc;
+  }
+  __syncthreads();
+  for (int idx = t; idx < k * k; idx += nt) {
+    int i = idx / k, j = idx % k;
+    double acc = 0.0;
+    for (int bb = j; bb < k; ++bb) acc = fma(T[(size_t)i * ldg + bb], RB[(size_t)j * ldg + bb], acc);
+    S[(size_t)i * lds + j] = acc;
+  }
+  if (t == 0) st[ST_JM] = k;
+}
+
+// After the eigensolve of H = Y Lambda Y^T (Y in Hc, sorted):
+//   T1 = R_B^T Y  (coordinate transform, into Hc region "H1")
+//   T2 = R_B^{-1} Y (basis transform)
+// One workgroup; k x k each, fp32 outputs with ld r_max.
+__global__ __launch_bounds__(1024) void reorth_transforms_kernel(const double* __restrict__ V,
+                                                                 int ldv, const int32_t* __restrict__ order,
+                                                                 const double* __restrict__ RB, int ldg,
+                                                                 float* T1, float* T2, int ldt,
+                                                                 double* X, const int32_t* st) {
+  const int k = st[ST_K];
+  const int t = threadIdx.x, nt = blockDim.x;
+  // T1[i][c] = sum_{a <= i} RB[a][i] * Y[a][c]
+  for (int idx = t; idx < k * k; idx += nt) {
+    int i = idx / k, c = idx % k;
+    int oc = order[c];
+    double acc = 0.0;
+    for (int a = 0; a <= i; ++a) acc = fma(RB[(size_t)a * ldg + i], V[(size_t)a * ldv + oc], acc);
+    T1[(size_t)i * ldt + c] = (float)acc;
+  }
+  // T2 = R_B^{-1} Y: back substitution per column c (one thread per column).
+  for (int c = t; c < k; c += nt) {
+    int oc = order[c];
+    for (int i = k - 1; i >= 0; --i) {
+      double acc = V[(size_t)i * ldv + oc];
+      for (int a = i + 1; a < k; ++a) acc -= RB[(size_t)i * ldg + a] * X[(size_t)a * ldg + c];
+      X[(size_t)i * ldg + c] = acc / RB[(size_t)i * ldg + i];
+      T2[(size_t)i * ldt + c] = (float)X[(size_t)i * ldg + c];
+    }
+  }
+}
+
+__global__ void reorth_commit_kernel(float* sigma, const float* __restrict__ sig_new, int32_t* st,
+                                     int r_max) {
+  const int k = st[ST_K];
+  for (int j = threadIdx.x; j < r_max; j += blockDim.x) sigma[j] = j < k ? sig_new[j] : 0.f;
+}
+
+}  // namespace
+
+// ============================================================================
+// Host launchers.
+
+// Allow the LDS-staged update kernels to use more than 64 KB of dynamic LDS.
+int iskv_kernel_setup() {
+  static int done = 0;
+  if (done) return ISKV_OK;
+  const int lds = 160 * 1024;
+  ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)coord_update_kernel,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds));
+  ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)basis_update_kernel,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds));
+  done = 1;
+  return ISKV_OK;
+}
+
+static int launch_jacobi(isvd_handle* h) {
+  const isvd_ws& w = h->w;
+  hipLaunchKernelGGL(core_jacobi_kernel, dim3(1), dim3(1024), 0, h->stream, w.A, w.V, h->m_max,
+                     w.st, 1e-13, ISKV_JACOBI_MAX_SWEEPS);
+  return ISKV_OK;
+}
+
+int iskv_launch_merge(isvd_handle* h, const float* F, const int32_t* pos_F, int32_t b) {
+  const iskv_config& c = h->cfg;
+  const isvd_ws& w = h->w;
+  hipStream_t s = h->stream;
+  const int D = c.D, R = c.r_max;
+  const int32_t* dk = w.st + ST_K;
+  const int32_t* dp = w.st + ST_P;
+  // 1. Q = F B (b x k)
+  sgemm<false, false>(s, b, R, F, D, h->B, R, w.Q, R, nullptr, 0, hdim(b), ddim(dk), hdim(D), 1.f, 0.f);
+  // 2. E = F - Q B^T (b x D)
+  sgemm<false, true>(s, b, D, w.Q, R, h->B, R, w.E, D, F, D, hdim(b), hdim(D), ddim(dk), -1.f, 1.f);
+  // 3. EB = E B; 4. E -= EB B^T (second projection, §4.1)
+  sgemm<false, false>(s, b, R, w.E, D, h->B, R, w.EB, R, nullptr, 0, hdim(b), ddim(dk), hdim(D), 1.f, 0.f);
+  sgemm<false, true>(s, b, D, w.EB, R, h->B, R, w.E, D, w.E, D, hdim(b), hdim(D), ddim(dk), -1.f, 1.f);
+  // 5. E E^T (fp64) and the residual basis
+  hipLaunchKernelGGL(resid_gram_kernel, dim3(b), dim3(256), 0, s, w.E, D, b, w.GE, w.st);
+  {
+    const int ld = b + 1;
+    size_t smem = (size_t)(2 * b * ld + b + 64) * sizeof(double) + (size_t)(32 * 2 + 1 + b) * sizeof(int) + 64;
+    hipLaunchKernelGGL(resid_basis_kernel, dim3(1), dim3(256), smem, s, w.GE, b, D, h->sigma,
+                       c.resid_rel_tol, w.VE, w.rho, w.st);
+  }
+  hipLaunchKernelGGL(make_p_kernel, dim3((D + 255) / 256), dim3(256), 0, s, w.E, D, b, w.VE, w.rho,
+                     w.P, c.b_max, w.st);
+  // 6. FP = F P (b x p)
+  sgemm<false, false>(s, b, c.b_max, F, D, w.P, c.b_max, w.FP, c.b_max, nullptr, 0, hdim(b), ddim(dp), hdim(D), 1.f, 0.f);
+  // 7. core Gram and its eigendecomposition
+  {
+    dim3 grid((h->m_max + 15) / 16, (h->m_max + 15) / 16);
+    hipLaunchKernelGGL(core_gram_kernel, grid, dim3(256), 0, s, w.Q, R, w.FP, c.b_max, h->sigma, b,
+                       w.A, h->m_max, w.st);
+  }
+  hipLaunchKernelGGL(set_jm_kernel, dim3(1), dim3(1), 0, s, w.st, (int)ST_M);
+  launch_jacobi(h);
+  hipLaunchKernelGGL(eig_finish_kernel, dim3(1), dim3(1024), 0, s, w.A, w.V, h->m_max, w.Hc, R,
+                     w.sig_new, w.order, w.st, R, 1);
+  // 8. coordinate sync of old rows, new rows, basis update
+  const int n0 = h->n_host;
+  if (!(c.flags & ISKV_NO_COORD_SYNC) && n0 > 0) {
+    size_t smem = (size_t)(32 * R + 32 * 64) * sizeof(float);
+    hipLaunchKernelGGL(coord_update_kernel, dim3((n0 + 31) / 32), dim3(256), smem, s, h->C, R, w.Hc,
+                       R, ddim(dk), ddim(w.st + ST_KNEW), hdim(n0), R);
+  }
+  hipLaunchKernelGGL(new_rows_kernel, dim3(b), dim3(256), 0, s, w.Q, R, w.FP, c.b_max, w.Hc, R, h->C,
+                     R, h->pos, pos_F, b, w.st, n0);
+  {
+    size_t smem = (size_t)(32 * (R + 64) + 32 * 64) * sizeof(float);
+    hipLaunchKernelGGL(basis_update_kernel, dim3((D + 31) / 32), dim3(256), smem, s, h->B, R, w.P,
+                       c.b_max, w.Hc, R, w.Bbf, D, w.st, 0, R);
+  }
+  hipLaunchKernelGGL(merge_commit_kernel, dim3(1), dim3(256), 0, s, h->sigma, w.sig_new, w.st, b, R);
+  ISKV_HIP_CHECK(hipGetLastError());
+  return ISKV_OK;
+}
+
+int iskv_launch_reorth(isvd_handle* h) {
+  const iskv_config& c = h->cfg;
+  const isvd_ws& w = h->w;
+  hipStream_t s = h->stream;
+  const int R = c.r_max, D = c.D;
+  const int n = h->n_host;
+  if (n == 0) return ISKV_OK;
+  const int tiles = (R + 15) / 16;
+  const int rows_per_chunk = 1024;
+  int nchunks = (n + rows_per_chunk - 1) / rows_per_chunk;
+  if (nchunks > w.gram_splits - 1) nchunks = w.gram_splits - 1;
+  const int rpc = (n + nchunks - 1) / nchunks;
+  int nchunks_b = 1;
+  // partial Grams: C into slices [0, nchunks), B into slice nchunks
+  hipLaunchKernelGGL(gram_partial_kernel, dim3(tiles * tiles, nchunks), dim3(256), 0, s, h->C, R, n,
+                     w.st, w.GC, R, rpc);
+  hipLaunchKernelGGL(gram_partial_kernel, dim3(tiles * tiles, nchunks_b), dim3(256), 0, s, h->B, R, D,
+                     w.st, w.GC + (size_t)nchunks * R * R, R, D);
+  hipLaunchKernelGGL(reorth_prep_kernel, dim3(1), dim3(1024), 0, s, w.GC, nchunks,
+                     w.GC + (size_t)nchunks * R * R, nchunks_b, R, w.GB, w.RB, w.A, h->m_max, w.st);
+  launch_jacobi(h);
+  hipLaunchKernelGGL(eig_finish_kernel, dim3(1), dim3(1024), 0, s, w.A, w.V, h->m_max, w.Hc, R,
+                     w.sig_new, w.order, w.st, R, 0);
+  hipLaunchKernelGGL(reorth_transforms_kernel, dim3(1), dim3(1024), 0, s, w.V, h->m_max, w.order,
+                     w.RB, R, w.Hc, w.T2, R, w.GC, w.st);
+  {
+    size_t smem = (size_t)(32 * R + 32 * 64) * sizeof(float);
+    hipLaunchKernelGGL(coord_update_kernel, dim3((n + 31) / 32), dim3(256), smem, s, h->C, R, w.Hc, R,
+                       ddim(w.st + ST_K), ddim(w.st + ST_K), hdim(n), R);
+  }
+  {
+    size_t smem = (size_t)(32 * (R + 64) + 32 * 64) * sizeof(float);
+    hipLaunchKernelGGL(basis_update_kernel, dim3((D + 31) / 32), dim3(256), smem, s, h->B, R, w.P,
+                       c.b_max, w.T2, R, w.Bbf, D, w.st, 1, R);
+  }
+  hipLaunchKernelGGL(reorth_commit_kernel, dim3(1), dim3(256), 0, s, h->sigma, w.sig_new, w.st, R);
+  ISKV_HIP_CHECK(hipGetLastError());
+  return ISKV_OK;
+}

@@ -1,0 +1,203 @@
+// Reconstruction of the dense KV cache from the factors, with per-position
+// RoPE on keys, and the exact-row scatter (iS-KV notes §3.2, §5.2,
+// Algorithm 3). Output row t holds the token at original position t.
+#include "iskv_internal.h"
+
+#include <math.h>
+
+namespace {
+
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_out(void* out, size_t idx, float v) {
+  if (BF16) ((uint16_t*)out)[idx] = f2bf(v);
+  else ((float*)out)[idx] = v;
+}
+
+// Angle of rotary pair j at position pos: pos * theta^(-2j/dh), formed and
+// reduced modulo 2 pi in fp64 so that positions in the tens of thousands keep
+// fp32-level accuracy, then sin/cos of the reduced fp32 angle.
+__device__ __forceinline__ void rope_cs(int pos, double inv_freq, float* c, float* s) {
+  const double two_pi = 6.283185307179586476925286766559;
+  double phi = (double)pos * inv_freq;
+  double red = phi - two_pi * rint(phi / two_pi);
+  sincosf((float)red, s, c);
+}
+
+// Column tile of W (128 or 64) features; rotary pair q (0 .. W/2-1) of the
+// tile is (lo, lo + dh/2) with lo = (q / (dh/2)) * dh + q % (dh/2).
+// Requires W % dh == 0.
+__device__ __forceinline__ int pair_lo(int q, int dh) {
+  const int half = dh >> 1;
+  return (q / half) * dh + (q % half);
+}
+
+// Compressed rows: out[pos[i], tile] = RoPE(C[i, :k] B[tile, :k]^T).
+// Grid (D / W, ceil(n / 32)); 256 threads; thread owns 4 rows x 2 pairs
+// (one pair when W == 64).
+template <bool BF16>
+__global__ __launch_bounds__(256) void recon_kernel(const float* __restrict__ C, int ldc,
+                                                    const float* __restrict__ B, int ldb,
+                                                    const int32_t* __restrict__ pos,
+                                                    const int32_t* __restrict__ st, int n, int D,
+                                                    int dh, int W, int apply_rope,
+                                                    double log_theta, void* out, int n_total) {
+  const int k = st[ST_K];
+  const int c0 = blockIdx.x * W;
+  const int i0 = blockIdx.y * 32;
+  if (i0 >= n) return;
+  __shared__ float Cs[32][33];
+  __shared__ float Bs[128][33];
+  const int t = threadIdx.x;
+  const int rg = (t >> 5) * 4;       // rows rg .. rg+3
+  const int q0 = t & 31;
+  const bool two = W == 128;
+  const int q1 = two ? q0 + 32 : q0;
+  const int lo0 = pair_lo(q0, dh), hi0 = lo0 + dh / 2;
+  const int lo1 = pair_lo(q1, dh), hi1 = lo1 + dh / 2;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < k; k0 += 32) {
+    for (int idx = t; idx < 32 * 32; idx += 256) {
+      int r = idx >> 5, c = idx & 31;
+      Cs[r][c] = (i0 + r < n && k0 + c < k) ? C[(size_t)(i0 + r) * ldc + k0 + c] : 0.f;
+    }
+    for (int idx = t; idx < W * 32; idx += 256) {
+      int r = idx >> 5, c = idx & 31;
+      Bs[r][c] = (k0 + c < k) ? B[(size_t)(c0 + r) * ldb + k0 + c] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int kk = 0; kk < 32; ++kk) {
+      float b0 = Bs[lo0][kk], b1 = Bs[hi0][kk], b2 = Bs[lo1][kk], b3 = Bs[hi1][kk];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float a = Cs[rg + u][kk];
+        acc[u][0] = fmaf(a, b0, acc[u][0]);
+        acc[u][1] = fmaf(a, b1, acc[u][1]);
+        acc[u][2] = fmaf(a, b2, acc[u][2]);
+        acc[u][3] = fmaf(a, b3, acc[u][3]);
+      }
+    }
+    __syncthreads();
+  }
+  const int half = dh / 2;
+  const double inv0 = exp(-(2.0 * (q0 % half) / dh) * log_theta);
+  const double inv1 = exp(-(2.0 * (q1 % half) / dh) * log_theta);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    int i = i0 + rg + u;
+    if (i >= n) continue;
+    int p = pos[i];
+    if (p < 0 || p >= n_total) continue;  // outside the output: dropped, never written
+    float x0 = acc[u][0], y0 = acc[u][1], x1 = acc[u][2], y1 = acc[u][3];
+    if (apply_rope) {
+      float c, s;
+      rope_cs(p, inv0, &c, &s);
+      float a0 = x0 * c - y0 * s, b0 = y0 * c + x0 * s;
+      rope_cs(p, inv1, &c, &s);
+      float a1 = x1 * c - y1 * s, b1 = y1 * c + x1 * s;
+      x0 = a0; y0 = b0; x1 = a1; y1 = b1;
+    }
+    size_t base = (size_t)p * D + c0;
+    store_out<BF16>(out, base + lo0, x0);
+    store_out<BF16>(out, base + hi0, y0);
+    if (two) {
+      store_out<BF16>(out, base + lo1, x1);
+      store_out<BF16>(out, base + hi1, y1);
+    }
+  }
+}
+
+// Exact rows: out[pos_e] = RoPE(X_exact[e]); slots with pos_e < 0 are empty.
+// Grid (n_exact), 64 threads x pairs.
+template <bool BF16>
+__global__ __launch_bounds__(256) void exact_rows_kernel(const float* __restrict__ X,
+                                                         const int32_t* __restrict__ pe, int D,
+                                                         int dh, int apply_rope, double log_theta,
+                                                         void* out, int n_total) {
+  const int e = blockIdx.x;
+  const int p = pe[e];
+  if (p < 0 || p >= n_total) return;
+  const int half = dh / 2;
+  for (int q = threadIdx.x; q < D / 2; q += blockDim.x) {
+    int head = q / half, j = q % half;
+    int lo = head * dh + j, hi = lo + half;
+    float x = X[(size_t)e * D + lo], y = X[(size_t)e * D + hi];
+    if (apply_rope) {
+      float c, s;
+      rope_cs(p, exp(-(2.0 * j / dh) * log_theta), &c, &s);
+      float a = x * c - y * s, b = y * c + x * s;
+      x = a; y = b;
+    }
+    store_out<BF16>(out, (size_t)p * D + lo, x);
+    store_out<BF16>(out, (size_t)p * D + hi, y);
+  }
+}
+
+// Window bookkeeping: copy `count` rows and their positions.
+__global__ void move_rows_kernel(float* dst, int32_t* dpos, const float* __restrict__ src,
+                                 const int32_t* __restrict__ spos, int32_t pos_base, int D) {
+  const int r = blockIdx.x;
+  for (int c = threadIdx.x; c < D; c += blockDim.x) dst[(size_t)r * D + c] = src[(size_t)r * D + c];
+  if (threadIdx.x == 0 && dpos) dpos[r] = spos ? spos[r] : pos_base + r;
+}
+
+__global__ void fill_pos_kernel(int32_t* pos, int count, int32_t v0, int32_t step) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) pos[i] = v0 + step * i;
+}
+
+}  // namespace
+
+int iskv_launch_reconstruct(const isvd_handle* h, const float* X_exact, const int32_t* pos_exact,
+                            int32_t n_exact, int32_t n_total, int32_t head_dim, int32_t apply_rope,
+                            float rope_theta, void* out, int32_t out_dtype, hipStream_t s) {
+  const int D = h->cfg.D, R = h->cfg.r_max;
+  const int n = h->n_host;
+  const double lt = log((double)rope_theta);
+  const bool bf = out_dtype == ISKV_OUT_BF16;
+  if (n > 0) {
+    const int W = (D % 128 == 0 && 128 % head_dim == 0) ? 128 : 64;
+    dim3 grid(D / W, (n + 31) / 32);
+    if (bf)
+      hipLaunchKernelGGL(recon_kernel<true>, grid, dim3(256), 0, s, h->C, R, h->B, R, h->pos,
+                         h->w.st, n, D, head_dim, W, apply_rope, lt, out, n_total);
+    else
+      hipLaunchKernelGGL(recon_kernel<false>, grid, dim3(256), 0, s, h->C, R, h->B, R, h->pos,
+                         h->w.st, n, D, head_dim, W, apply_rope, lt, out, n_total);
+  }
+  if (n_exact > 0) {
+    if (bf)
+      hipLaunchKernelGGL(exact_rows_kernel<true>, dim3(n_exact), dim3(256), 0, s, X_exact,
+                         pos_exact, D, head_dim, apply_rope, lt, out, n_total);
+    else
+      hipLaunchKernelGGL(exact_rows_kernel<false>, dim3(n_exact), dim3(256), 0, s, X_exact,
+                         pos_exact, D, head_dim, apply_rope, lt, out, n_total);
+  }
+  ISKV_HIP_CHECK(hipGetLastError());
+  return ISKV_OK;
+}
+
+int iskv_launch_window_move(float* dst_rows, int32_t* dst_pos, const float* src_rows,
+                            const int32_t* src_pos, int32_t src_pos_base, int32_t count, int32_t D,
+                            hipStream_t s) {
+  if (count <= 0) return ISKV_OK;
+  hipLaunchKernelGGL(move_rows_kernel, dim3(count), dim3(256), 0, s, dst_rows, dst_pos, src_rows,
+                     src_pos, src_pos_base, D);
+  ISKV_HIP_CHECK(hipGetLastError());
+  return ISKV_OK;
+}
+
+int iskv_launch_fill_pos(int32_t* pos, int32_t count, int32_t value0, int32_t step, hipStream_t s) {
+  if (count <= 0) return ISKV_OK;
+  hipLaunchKernelGGL(fill_pos_kernel, dim3((count + 255) / 256), dim3(256), 0, s, pos, count, value0,
+                     step);
+  ISKV_HIP_CHECK(hipGetLastError());
+  return ISKV_OK;
+}

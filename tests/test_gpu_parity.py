@@ -1,0 +1,321 @@
+"""GPU parity of the HIP hot path against the CPU oracle, through the C ABI.
+
+Factors are compared by reconstruction (never by sign-ambiguous singular
+vectors). Tolerances:
+  * merges: relative Frobenius <= 1e-3 of the fp32 reconstruction against the
+    float64 oracle (the bar the method's own acceptance states);
+  * reconstruction and RoPE: fp32 output within 2e-6 relative of the oracle's
+    float64 rebuild of the GPU's own factors; bf16 output within 5e-3
+    relative (bf16 rounding alone is ~1.7e-3);
+  * attention: 2e-2 absolute and 2e-2 relative in bf16.
+"""
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import oracle as O  # noqa: E402
+import synth  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def K():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import online_rank_kv_amd as mod
+    return mod
+
+
+DEV = "cuda"
+
+
+def rel(a, b):
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def gpu_factors(path):
+    """(C, B, sigma, pos) of the first n rows / k columns, on the host."""
+    n, k, st = path.query()
+    C = path.C[:n, :k].double().cpu().numpy()
+    B = path.B[:, :k].double().cpu().numpy()
+    s = path.sigma[:k].double().cpu().numpy()
+    pos = path.pos[:n].cpu().numpy()
+    return C, B, s, pos, st
+
+
+def run_gpu_stream(K, X, b, r, T=0, sync=True, n_cap=None):
+    n, D = X.shape
+    path = K.IsvdPath(D=D, r_max=r, b_max=b, n_cap=n_cap or n, reorth_every_rows=T, sync=sync,
+                      device=DEV)
+    Xd = torch.from_numpy(np.ascontiguousarray(X)).to(DEV)
+    pos = torch.arange(n, dtype=torch.int32, device=DEV)
+    for s in range(0, n, b):
+        e = min(n, s + b)
+        path.merge(Xd[s:e], pos[s:e])
+    return path
+
+
+def gpu_recon_fp32(path, n_total, head_dim=64, rope=False, X_exact=None, pos_exact=None):
+    D = path.cfg.D
+    out = torch.full((n_total, D), float("nan"), dtype=torch.float32, device=DEV)
+    path.reconstruct(out, n_total, X_exact=X_exact, pos_exact=pos_exact, head_dim=head_dim, rope=rope)
+    torch.cuda.synchronize()
+    return out.double().cpu().numpy()
+
+
+# --------------------------------------------------------------------------- merges
+def test_tiny_stream_every_merge(K):
+    """Tiny stream (D=64, r=8, b=8, 256 rows): every one of the 32 merges matches the oracle."""
+    X = synth.kv_stream(synth.CONFIG_TINY)
+    path = K.IsvdPath(D=64, r_max=8, b_max=8, n_cap=256, device=DEV)
+    Xd = torch.from_numpy(X).to(DEV)
+    pos = torch.arange(256, dtype=torch.int32, device=DEV)
+    fac = O.empty_factor(64)
+    for t, s in enumerate(range(0, 256, 8)):
+        path.merge(Xd[s:s + 8], pos[s:s + 8])
+        fac = O.merge(fac, X[s:s + 8], np.arange(s, s + 8), 8)
+        C, B, sg, p, st = gpu_factors(path)
+        assert st == 0
+        assert C.shape == (s + 8, 8)
+        got = C @ B.T
+        ref = O.represented(fac)
+        assert rel(got, ref) < 1e-4, (t, rel(got, ref))
+        assert np.allclose(sg, fac.sigma, rtol=1e-4)
+        assert list(p) == list(range(s + 8))
+    assert np.abs(B.T @ B - np.eye(8)).max() < 1e-4
+
+
+def test_tiny_stream_factor_drift_vs_fresh_svd(K):
+    X = synth.kv_stream(synth.CONFIG_TINY)
+    path = run_gpu_stream(K, X, 8, 8)
+    C, B, _, _, _ = gpu_factors(path)
+    drift = O.factor_drift(X, C @ B.T, 8)
+    ref_drift = O.factor_drift(X, O.represented(O.run_stream(X, 8, 8)), 8)
+    assert abs(drift - ref_drift) < 1e-4
+
+
+@pytest.mark.parametrize("D,r,b,n", [(128, 16, 8, 200), (256, 40, 16, 420), (128, 128, 32, 300)])
+def test_ragged_and_full_rank_streams(K, D, r, b, n):
+    """Several tiles, a ragged last block, and r = D (k reaches D: no residual)."""
+    rng = np.random.default_rng(D + r)
+    sig = np.exp(-np.arange(D) / 10.0) + 0.01
+    X = (rng.standard_normal((n, D)) * sig) @ np.linalg.qr(rng.standard_normal((D, D)))[0].T
+    X = X.astype(np.float32)
+    path = run_gpu_stream(K, X, b, r)
+    C, B, _, _, st = gpu_factors(path)
+    assert st == 0
+    ref = O.represented(O.run_stream(X, b, r))
+    assert rel(C @ B.T, ref) < 1e-3
+    assert np.abs(B.T @ B - np.eye(B.shape[1])).max() < 1e-3
+
+
+def test_pure_rotation_and_zero_blocks(K):
+    """F in span(B) adds no direction; an all-zero block leaves the history unchanged."""
+    rng = np.random.default_rng(3)
+    D, r, b = 128, 12, 8
+    basis = np.linalg.qr(rng.standard_normal((D, 6)))[0]
+    X = (rng.standard_normal((64, 6)) * [5, 4, 3, 2, 1, 0.5]) @ basis.T
+    X[40:48] = 0.0
+    X = X.astype(np.float32)
+    path = run_gpu_stream(K, X, b, r)
+    C, B, _, _, st = gpu_factors(path)
+    assert st == 0
+    assert C.shape[1] <= 8  # rank of the data (6) plus at most threshold-level extras
+    assert rel(C @ B.T, X.astype(float)) < 1e-5
+
+
+def test_kstream_512_merges(K):
+    """Llama-8B-shaped key stream: 16,384 rows, D=1024, r=256, b=32 folded as 512 blocks."""
+    X = synth.kv_stream(synth.CONFIG_KSTREAM)
+    path = run_gpu_stream(K, X, 32, 256)
+    C, B, sg, p, st = gpu_factors(path)
+    assert st == 0 and C.shape == (16384, 256)
+    fac = O.run_stream(X, 32, 256)
+    ref = O.represented(fac)
+    err = rel(C @ B.T, ref)
+    print(f"kstream 512 merges: rel {err:.3e}")
+    assert err < 1e-3
+    assert np.abs(B.T @ B - np.eye(256)).max() < 1e-3
+    assert np.allclose(sg, fac.sigma, rtol=1e-3)
+
+
+# --------------------------------------------------------------------------- reorth
+def test_reorth_keeps_product_and_orthonormalises(K):
+    X = synth.kv_stream(synth.StreamSpec(D=256, n=1024, spectrum="exp40+0.01", noise_std=0.0, seed=2))
+    path = run_gpu_stream(K, X, 32, 64)
+    C0, B0, _, _, _ = gpu_factors(path)
+    before = C0 @ B0.T
+    path.reorth()
+    C1, B1, s1, _, st = gpu_factors(path)
+    assert st == 0
+    assert rel(C1 @ B1.T, before) < 1e-5
+    assert np.abs(B1.T @ B1 - np.eye(64)).max() < 1e-4
+    G = C1.T @ C1
+    assert np.abs(G - np.diag(np.diag(G))).max() < 1e-4 * G[0, 0]
+    assert np.allclose(np.sqrt(np.diag(G)), s1, rtol=1e-4)
+
+
+def test_kv_streams_with_reorth_schedule(K):
+    """K and V paths (r_K=192, r_V=320, b=64), re-orthogonalised every 16 merges (prefix of 4096 rows)."""
+    for spec, r in ((synth.CONFIG_KV_K, 192), (synth.CONFIG_KV_V, 320)):
+        X = synth.kv_stream(spec, 4096)
+        path = run_gpu_stream(K, X, 64, r, T=1024)
+        C, B, _, _, st = gpu_factors(path)
+        assert st == 0
+        ref = O.represented(O.run_stream(X, 64, r, reorth_every_rows=1024))
+        err = rel(C @ B.T, ref)
+        print(f"spectrum {spec.spectrum} r={r}: rel {err:.3e}")
+        assert err < 1e-3
+        assert np.abs(B.T @ B - np.eye(B.shape[1])).max() < 1e-4
+
+
+def test_basis_only_ablation_matches_oracle(K):
+    """ISKV_NO_COORD_SYNC: stored rows drift like the oracle's stale coordinates."""
+    X = synth.kv_stream(synth.StreamSpec(D=128, n=512, spectrum="exp40+0.01", noise_std=0.0, seed=4))
+    path = run_gpu_stream(K, X, 32, 24, sync=False)
+    C, B, _, _, _ = gpu_factors(path)
+    fac = O.run_stream(X, 32, 24, sync=False)
+    stored_ref = O.stored_rows(fac)
+    synced = O.represented(O.run_stream(X, 32, 24))
+    err_vs_oracle = rel(C @ B.T, stored_ref)
+    drift = rel(stored_ref, synced)
+    print(f"basis-only: gpu vs oracle {err_vs_oracle:.3e}, drift vs synced {drift:.3e}")
+    assert drift > 0.1
+    assert err_vs_oracle < 1e-3
+    with pytest.raises(K.IskvError):
+        path.reorth()
+
+
+# --------------------------------------------------------------------------- reconstruction
+def test_reconstruct_rope_and_exact_rows(K):
+    """Scatter by position, exact rows, per-position RoPE (fp32 and bf16 outputs)."""
+    D, hd, theta = 1024, 128, 500000.0
+    X = synth.kv_stream(synth.CONFIG_KSTREAM, 2048)
+    rng = np.random.default_rng(9)
+    perm = rng.permutation(2048 + 96)
+    comp_pos, ex_pos = np.sort(perm[:2048]), np.sort(perm[2048:])
+    path = K.IsvdPath(D=D, r_max=256, b_max=32, n_cap=2048, device=DEV)
+    Xd = torch.from_numpy(X).to(DEV)
+    pd = torch.from_numpy(comp_pos.astype(np.int32)).to(DEV)
+    for s in range(0, 2048, 32):
+        path.merge(Xd[s:s + 32], pd[s:s + 32])
+    Xe = rng.standard_normal((96, D)).astype(np.float32)
+    pe = ex_pos.astype(np.int32).copy()
+    pe_with_hole = np.concatenate([pe, [-1]]).astype(np.int32)
+    Xe_with_hole = np.vstack([Xe, np.full((1, D), 7.0, np.float32)])
+    Xed = torch.from_numpy(Xe_with_hole).to(DEV)
+    ped = torch.from_numpy(pe_with_hole).to(DEV)
+    C, B, _, pos, _ = gpu_factors(path)
+    fac = O.Factor(U=C, sigma=np.ones(C.shape[1]), B=B, pos=pos)
+    n_total = 2048 + 96
+    for rope in (False, True):
+        ref = O.reconstruct(fac, Xe, pe, n_total, hd, rope, theta)
+        got = gpu_recon_fp32(path, n_total, head_dim=hd, rope=rope, X_exact=Xed, pos_exact=ped)
+        assert np.isfinite(got).all()
+        assert rel(got, ref) < 2e-6, rel(got, ref)
+        out = torch.empty((n_total, D), dtype=torch.bfloat16, device=DEV)
+        path.reconstruct(out, n_total, X_exact=Xed, pos_exact=ped, head_dim=hd, rope=rope)
+        torch.cuda.synchronize()
+        gb = out.double().cpu().numpy()
+        assert rel(gb, O.bf16_round(ref)) < 5e-3
+        assert rel(gb, ref) < 5e-3
+
+
+def test_reconstruct_high_positions_rope(K):
+    """RoPE angles at positions near 64K keep fp32 accuracy (angles reduced in fp64)."""
+    D, hd = 256, 128
+    rng = np.random.default_rng(11)
+    path = K.IsvdPath(D=D, r_max=32, b_max=16, n_cap=16, device=DEV)
+    X = rng.standard_normal((16, D)).astype(np.float32)
+    p = np.arange(65520, 65536).astype(np.int32)
+    path.merge(torch.from_numpy(X).to(DEV), torch.from_numpy(p).to(DEV))
+    C, B, _, pos, _ = gpu_factors(path)
+    out = torch.zeros((65536, D), dtype=torch.float32, device=DEV)
+    path.reconstruct(out, 65536, head_dim=hd, rope=True)
+    torch.cuda.synchronize()
+    got = out[65520:].double().cpu().numpy()
+    ref = O.rope(C @ B.T, pos, hd, 500000.0)
+    assert rel(got, ref) < 2e-6
+
+
+# --------------------------------------------------------------------------- attention
+@pytest.mark.parametrize("batch,n,hq,hkv", [(1, 1000, 32, 8), (2, 4096, 32, 8), (1, 63, 8, 8)])
+def test_decode_attend_matches_oracle(K, batch, n, hq, hkv):
+    rng = np.random.default_rng(n)
+    Kc = torch.from_numpy(rng.standard_normal((batch, n, hkv, 128)).astype(np.float32)).to(DEV).bfloat16()
+    Vc = torch.from_numpy(rng.standard_normal((batch, n, hkv, 128)).astype(np.float32)).to(DEV).bfloat16()
+    q = torch.from_numpy(rng.standard_normal((batch, hq, 128)).astype(np.float32)).to(DEV).bfloat16()
+    out = torch.empty((batch, hq, 128), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(K.decode_attend_workspace_bytes(batch, n, hq, 128), dtype=torch.uint8, device=DEV)
+    K.decode_attend(q, Kc, Vc, batch, n, hq, hkv, 128, 128 ** -0.5, out, ws)
+    torch.cuda.synchronize()
+    ref = O.attend(q.float().cpu().numpy(), Kc.float().cpu().numpy(), Vc.float().cpu().numpy(), 128 ** -0.5)
+    got = out.float().cpu().numpy()
+    assert np.abs(got - ref).max() < 2e-2
+    assert rel(got, ref) < 2e-2
+
+
+def test_decode_attend_needle(K):
+    """A planted key aligned with the query dominates: the output is that value row."""
+    rng = np.random.default_rng(1)
+    n = 5000
+    Kn = rng.standard_normal((1, n, 8, 128)).astype(np.float32) * 0.1
+    Vn = rng.standard_normal((1, n, 8, 128)).astype(np.float32)
+    qn = rng.standard_normal((1, 32, 128)).astype(np.float32)
+    Kn[0, 4321, 2, :] = qn[0, 9] * 2.0
+    q = torch.from_numpy(qn).to(DEV).bfloat16()
+    out = torch.empty((1, 32, 128), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(K.decode_attend_workspace_bytes(1, n, 32, 128), dtype=torch.uint8, device=DEV)
+    K.decode_attend(q, torch.from_numpy(Kn).to(DEV).bfloat16(), torch.from_numpy(Vn).to(DEV).bfloat16(),
+                    1, n, 32, 8, 128, 128 ** -0.5 * 4.0, out, ws)
+    torch.cuda.synchronize()
+    v = torch.from_numpy(Vn[0, 4321, 2]).bfloat16().float().numpy()
+    assert np.abs(out[0, 9].float().cpu().numpy() - v).max() < 2e-2
+
+
+# --------------------------------------------------------------------------- window
+def test_window_pending_and_merge(K):
+    """Exact window (w=128) + pending FIFO: 508 merges for 16,384 rows? here 2,048 rows -> 60 merges."""
+    D, r, b, w = 1024, 256, 32, 128
+    X = synth.kv_stream(synth.CONFIG_KSTREAM, 2048)
+    path = K.IsvdPath(D=D, r_max=r, b_max=b, n_cap=2048, device=DEV)
+    win = K.ExactWindow(path, window=w, block=b)
+    Xd = torch.from_numpy(X).to(DEV)
+    merges = 0
+    for s in range(0, 2048, 32):
+        merges += win.append(Xd[s:s + 32], s)
+    assert merges == (2048 - w) // b
+    n, k, st = path.query()
+    assert n == 2048 - w and st == 0
+    rows, pos, count = K.iskv_window_exact(win.w)
+    ex_pos = win.pos.cpu().numpy()
+    valid = ex_pos >= 0
+    assert sorted(ex_pos[valid]) == list(range(2048 - w, 2048))
+    got = gpu_recon_fp32(path, 2048, head_dim=128, X_exact=win.rows, pos_exact=win.pos)
+    fac = O.run_stream(X[:2048 - w], b, r)
+    ref = O.reconstruct(fac, X[2048 - w:], np.arange(2048 - w, 2048), 2048, 128, False)
+    assert rel(got, ref) < 1e-3
+
+
+# --------------------------------------------------------------------------- errors
+def test_error_paths(K):
+    path = K.IsvdPath(D=128, r_max=8, b_max=8, n_cap=16, device=DEV)
+    F = torch.zeros((8, 128), dtype=torch.float32, device=DEV)
+    p = torch.arange(8, dtype=torch.int32, device=DEV)
+    with pytest.raises(K.IskvError) as e:
+        K.isvd_merge_block(path.h, F, p, 9)  # b > b_max
+    assert e.value.code == -1
+    path.merge(F, p)
+    path.merge(F, p)
+    with pytest.raises(K.IskvError) as e:
+        path.merge(F, p)  # n_cap exceeded
+    assert e.value.code == -2
+    bad = K.IsvdPath(D=128, r_max=8, b_max=8, n_cap=16, device=DEV)
+    Fn = torch.randn((8, 128), device=DEV)
+    Fn[3, 5] = float("nan")
+    bad.merge(Fn, p)
+    _, _, st = bad.query()
+    assert st & K.ISKV_DEV_NONFINITE
