@@ -22,8 +22,9 @@
  *    checked before anything is enqueued, and a call that fails its checks
  *    leaves every buffer and the handle unchanged. Numerical trouble found on
  *    the device (non-finite input, a core eigensolver that did not converge)
- *    is latched in the device status word and reported by isvd_query() and by
- *    the next call on that handle. No C++ exception crosses the ABI.
+ *    is latched in the device status word and reported by isvd_query(); the
+ *    kernels never index memory with data-derived values that such input could
+ *    corrupt. No C++ exception crosses the ABI.
  *  - Threading: a handle is not thread-safe; drive it from one host thread
  *    and one stream.
  *  - Layouts are row-major. Floating point is IEEE fp32 unless stated;
@@ -113,8 +114,9 @@ int isvd_init(isvd_handle** out, const iskv_config* cfg, float* C, float* sigma,
  *   F      device fp32 [b x D], the b oldest pending exact rows.
  *   pos_F  device int32 [b], their original positions (copied into pos).
  *   b      1..b_max.
- * Errors: EINVAL (null pointer, b out of range), ECAPACITY (n + b > n_cap),
- * ENONFINITE / ENOCONV latched by an earlier call. */
+ * Errors: EINVAL (null pointer, b out of range), ECAPACITY (n + b > n_cap).
+ * Non-finite input and a non-converged core are latched on the device
+ * (ISKV_DEV_NONFINITE / ISKV_DEV_NOCONV, read by isvd_query). */
 int isvd_merge_block(isvd_handle* h, const float* F, const int32_t* pos_F, int32_t b);
 
 /* Re-orthogonalise the factors: iS-KV notes §4.4. Equivalent to the notes'
@@ -147,8 +149,8 @@ void isvd_destroy(isvd_handle* h);
  *   X_exact     device fp32 [n_exact x D] or NULL when n_exact == 0.
  *   pos_exact   device int32 [n_exact].
  *   n_total     rows of out; the compressed and valid exact positions must
- *               partition 0..n_total-1 (the caller's contract; not checked on
- *               the device).
+ *               partition 0..n_total-1 (the caller's contract); a position
+ *               outside 0..n_total-1 is dropped, never written.
  *   head_dim    d_h, even, dividing 128 when D % 128 == 0, else dividing 64.
  *   out         device [n_total x D], bf16 bits (ISKV_OUT_BF16) or fp32
  *               (ISKV_OUT_FP32); fp32 output computes the product in fp32.

@@ -33,6 +33,11 @@ __device__ __forceinline__ int dval(const Dim& d) { return d.dev ? (*d.dev) * d.
 static inline Dim hdim(int v) { return Dim{v, nullptr, 0, 0}; }
 static inline Dim ddim(const int32_t* p, int mul = 1, int add = 0) { return Dim{0, p, mul, add}; }
 
+// Ordering key of an eigenvalue: NaN sorts last as -inf, so that the rank
+// "greater key, or equal key and lower index" is a strict total order and the
+// ranks always form a permutation (a NaN must never leave a rank unassigned).
+__device__ __forceinline__ double rank_key(double x) { return isnan(x) ? -INFINITY : x; }
+
 __device__ __forceinline__ uint16_t f2bf(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);  // quiet NaN
@@ -257,24 +262,28 @@ __global__ __launch_bounds__(256) void resid_basis_kernel(const double* __restri
   // rank by descending eigenvalue, ties by index
   for (int i = t; i < b; i += blockDim.x) {
     int rnk = 0;
-    for (int j = 0; j < b; ++j) rnk += (lam[j] > lam[i]) || (lam[j] == lam[i] && j < i);
+    const double ki = rank_key(lam[i]);
+    for (int j = 0; j < b; ++j) {
+      const double kj = rank_key(lam[j]);
+      rnk += (kj > ki) || (kj == ki && j < i);
+    }
     order[rnk] = i;
   }
   __syncthreads();
   for (int idx = t; idx < b * b; idx += blockDim.x) {
     int row = idx / b, col = idx % b;
-    VE[row * b + col] = V[row * ld + order[col]];
+    VE[row * b + col] = V[row * ld + min(max(order[col], 0), b - 1)];
   }
-  for (int j = t; j < b; j += blockDim.x) rho[j] = sqrt(fmax(lam[order[j]], 0.0));
+  for (int j = t; j < b; j += blockDim.x) rho[j] = sqrt(fmax(lam[min(max(order[j], 0), b - 1)], 0.0));
   __syncthreads();
   if (t == 0) {
-    double rho1 = sqrt(fmax(lam[order[0]], 0.0));
+    double rho1 = sqrt(fmax(lam[min(max(order[0], 0), b - 1)], 0.0));
     double s1 = (k > 0) ? (double)sigma[0] : 0.0;
     double sc = fmax(s1, rho1);
     double floor_ = (double)(D > b ? D : b) * 1.1920928955078125e-07 * sc;
     double tau = fmax((double)delta * sc, floor_);
     int p = 0;
-    for (int j = 0; j < b; ++j) p += sqrt(fmax(lam[order[j]], 0.0)) > tau;
+    for (int j = 0; j < b; ++j) p += sqrt(fmax(lam[min(max(order[j], 0), b - 1)], 0.0)) > tau;
     if (p > D - k) p = D - k;
     st[ST_P] = p;
     st[ST_M] = k + p;
@@ -416,8 +425,11 @@ __global__ __launch_bounds__(1024) void eig_finish_kernel(const double* __restri
   __syncthreads();
   for (int i = t; i < n; i += blockDim.x) {
     int rnk = 0;
-    double li = lam[i];
-    for (int j = 0; j < n; ++j) rnk += (lam[j] > li) || (lam[j] == li && j < i);
+    const double ki = rank_key(lam[i]);
+    for (int j = 0; j < n; ++j) {
+      const double kj = rank_key(lam[j]);
+      rnk += (kj > ki) || (kj == ki && j < i);
+    }
     order[rnk] = i;
   }
   __syncthreads();
@@ -428,11 +440,12 @@ __global__ __launch_bounds__(1024) void eig_finish_kernel(const double* __restri
   const int kold = for_merge ? st[ST_K] : 0;
   for (int idx = t; idx < n * keep; idx += blockDim.x) {
     int row = idx / keep, col = idx % keep;
-    double v = V[(size_t)row * ld + order[col]];
-    if (col < kold && V[(size_t)col * ld + order[col]] < 0.0) v = -v;
+    const int oc = min(max(order[col], 0), n - 1);
+    double v = V[(size_t)row * ld + oc];
+    if (col < kold && V[(size_t)col * ld + oc] < 0.0) v = -v;
     Hc[(size_t)row * ldh + col] = (float)v;
   }
-  for (int c = t; c < keep; c += blockDim.x) sig_new[c] = (float)sqrt(fmax(lam[order[c]], 0.0));
+  for (int c = t; c < keep; c += blockDim.x) sig_new[c] = (float)sqrt(fmax(lam[min(max(order[c], 0), n - 1)], 0.0));
   if (t == 0 && for_merge) st[ST_KNEW] = keep;
 }
 
@@ -677,14 +690,14 @@ __global__ __launch_bounds__(1024) void reorth_transforms_kernel(const double* _
   // T1[i][c] = sum_{a <= i} RB[a][i] * Y[a][c]
   for (int idx = t; idx < k * k; idx += nt) {
     int i = idx / k, c = idx % k;
-    int oc = order[c];
+    int oc = min(max(order[c], 0), k - 1);
     double acc = 0.0;
     for (int a = 0; a <= i; ++a) acc = fma(RB[(size_t)a * ldg + i], V[(size_t)a * ldv + oc], acc);
     T1[(size_t)i * ldt + c] = (float)acc;
   }
   // T2 = R_B^{-1} Y: back substitution per column c (one thread per column).
   for (int c = t; c < k; c += nt) {
-    int oc = order[c];
+    int oc = min(max(order[c], 0), k - 1);
     for (int i = k - 1; i >= 0; --i) {
       double acc = V[(size_t)i * ldv + oc];
       for (int a = i + 1; a < k; ++a) acc -= RB[(size_t)i * ldg + a] * X[(size_t)a * ldg + c];
