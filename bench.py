@@ -121,8 +121,9 @@ def main():
         # fill both paths with the first N0 rows (+ window)
         t_fill = time.perf_counter()
         for s in range(0, N0 + WIN, 512):
+            e = min(s + 512, N0 + WIN)
             for i in range(2):
-                wins[i].append(Xd[i][s:s + 512], s)
+                wins[i].append(Xd[i][s:e], s)
         stream.synchronize()
         fill_s = time.perf_counter() - t_fill
         rng = np.random.default_rng(5)
