@@ -179,6 +179,7 @@ def main():
         return float(np.mean([a.elapsed_time(b) for a, b in ev[key]]))
 
     ms = {k: avg_ms(k) for k in ev}
+    core = [p.state() for p in paths]
     merges = 2 * steps
     n_mid = cursor[0] - BLK * steps // 2
     # algorithmic bytes of one K reconstruction: read C (n x r fp32) and B^T
@@ -210,6 +211,7 @@ def main():
                      "kernel": "kv_reconstruct (K, bf16 + RoPE)",
                      "mfma_frac": recon_flops / (ms["recon_k"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
         "setup_s": {"generate": gen_s, "fill_16k_rows": fill_s},
+        "core_solver_last_merge": [{"flags": c[11], "steps": c[12], "k": c[1], "n": c[0]} for c in core],
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(Xk, Xv, args.cpu_seconds)

@@ -131,6 +131,14 @@ int isvd_reorth(isvd_handle* h);
  * may be NULL. Errors: EHIP. */
 int isvd_query(isvd_handle* h, int32_t* n, int32_t* k, int32_t* status);
 
+/* Diagnostic: synchronise the stream and copy the first `count` (<= 16)
+ * device state words of the handle: [0] n, [1] k, [2] p of the last merge,
+ * [3] folded rows, [4] status bits, [5] core width k + p, [6] r',
+ * [7] Jacobi sweeps of the last fallback solve, [11] core eigensolver flags
+ * (1 converged by parallel refinement, 2 single-workgroup Jacobi fallback),
+ * [12] refinement steps of the last core solve. Errors: EINVAL, EHIP. */
+int isvd_query_state(isvd_handle* h, int32_t* state, int32_t count);
+
 /* Rows folded so far (host-side, no sync). */
 int32_t isvd_rows(const isvd_handle* h);
 

@@ -20,8 +20,8 @@ __all__ = [
     "LIB_PATH", "lib", "IskvError", "IskvConfig", "ISKV_NO_COORD_SYNC", "ISKV_OUT_BF16",
     "ISKV_OUT_FP32", "ISKV_DEV_NONFINITE", "ISKV_DEV_NOCONV", "EXPORTED_SYMBOLS",
     "isvd_workspace_bytes", "isvd_init", "isvd_merge_block", "isvd_reorth", "isvd_query",
-    "isvd_rows", "isvd_destroy", "kv_reconstruct", "decode_attend_workspace_bytes",
-    "decode_attend", "iskv_window_rows", "iskv_window_init", "iskv_window_protect",
+    "isvd_rows", "isvd_destroy", "isvd_query_state", "kv_reconstruct",
+    "decode_attend_workspace_bytes", "decode_attend", "iskv_window_rows", "iskv_window_init", "iskv_window_protect",
     "iskv_window_append", "iskv_window_exact", "iskv_window_destroy", "iskv_strerror",
     "IsvdPath", "ExactWindow",
 ]
@@ -46,6 +46,7 @@ EXPORTED_SYMBOLS = (
     "isvd_rows", "isvd_destroy", "kv_reconstruct", "decode_attend_workspace_bytes",
     "decode_attend", "iskv_window_rows", "iskv_window_init", "iskv_window_protect",
     "iskv_window_append", "iskv_window_exact", "iskv_window_destroy", "iskv_strerror",
+    "isvd_query_state",
 )
 
 
@@ -78,6 +79,8 @@ lib.isvd_reorth.restype = ctypes.c_int
 lib.isvd_reorth.argtypes = [_vp]
 lib.isvd_query.restype = ctypes.c_int
 lib.isvd_query.argtypes = [_vp, _pi32, _pi32, _pi32]
+lib.isvd_query_state.restype = ctypes.c_int
+lib.isvd_query_state.argtypes = [_vp, _pi32, _i32]
 lib.isvd_rows.restype = _i32
 lib.isvd_rows.argtypes = [_vp]
 lib.isvd_destroy.restype = None
@@ -156,6 +159,12 @@ def isvd_query(h: int):
     n, k, st = _i32(), _i32(), _i32()
     _check(lib.isvd_query(h, ctypes.byref(n), ctypes.byref(k), ctypes.byref(st)), "isvd_query")
     return n.value, k.value, st.value
+
+
+def isvd_query_state(h: int, count: int = 16):
+    arr = (ctypes.c_int32 * count)()
+    _check(lib.isvd_query_state(h, arr, count), "isvd_query_state")
+    return list(arr)
 
 
 def isvd_rows(h: int) -> int:
@@ -250,6 +259,9 @@ class IsvdPath:
 
     def query(self):
         return isvd_query(self.h)
+
+    def state(self):
+        return isvd_query_state(self.h)
 
     @property
     def n(self) -> int:

@@ -1,0 +1,567 @@
+// Symmetric eigensolver for the merge core Z^T Z = diag(sigma^2, 0) + M^T M
+// and for the re-orthogonalisation matrix (iS-KV notes §4.2 / §4.4 need the
+// top singular triplets of the small core; its size does not grow with n).
+//
+// gfx950 design. At r = 256, b = 32 the core is 288 x 288: a single-workgroup
+// Jacobi cannot keep it in 160 KB of LDS and takes tens of ms through L2. The
+// core is, however, nearly diagonal after the first merges (old directions
+// are decoupled up to O(b/n)), so it is solved by a parallel refinement of
+// the eigenvector matrix W (initially I), every step run on many workgroups:
+//   S = W^T A W                                   (two fp64 GEMMs)
+//   pairs with |s_ij| > omega |s_jj - s_ii| ("strongly coupled", near ties)
+//     form connected clusters; clusters of <= 6 indices are diagonalised
+//     exactly by a small cyclic Jacobi, larger ones get exact 2x2 rotations
+//     on a greedy matching of their strong pairs;          (one workgroup)
+//   every other pair gets the first-order Jacobi angle
+//     K_ij = s_ij / (s_jj - s_ii) (K antisymmetric, clipped),
+//   W <- W R exp(K) with exp(K) = I + K(I + K/2(I + K/3(I + K/4)))
+//                                                  (three GEMMs + one)
+// until every scaled coupling |s_ij| / sqrt(s_ii s_jj) is below 1e-12. This
+// is the first-order eigenvector refinement of the Jacobi family (all
+// rotations of a sweep at once), with near-ties handled exactly. A final
+// Newton-Schulz step restores W^T W = I. Cores that do not converge in
+// PCJ_MAXIT steps (strongly mixed early merges) fall back to the
+// single-workgroup cyclic Jacobi.
+#include "iskv_internal.h"
+
+#include <math.h>
+
+namespace {
+
+constexpr int PCJ_MAXIT = 10;
+constexpr double PCJ_TOL = 1e-12;
+constexpr double PCJ_OMEGA = 0.1;
+constexpr double PCJ_CLIP = 0.2;
+constexpr int CMAX_S = 6;      // largest cluster diagonalised exactly
+constexpr int NCL_MAX = 64;    // clusters handled exactly per step
+constexpr int EMAX = 4096;     // strong pairs recorded per step
+constexpr int NPAIR_MAX = 512; // matched pairs per step
+
+constexpr int FLAG_CONV = 1;
+constexpr int FLAG_FALLBACK = 2;
+
+// ----------------------------------------------------------------------------
+// C = alpha * opA(A) opB(B) + beta * Cin + gamma * I, all m x m (m from
+// st[ST_JM]), fp64, 16x16 output tiles, 256 threads, one output each.
+// mode 0: skip the launch when (st[ST_PCJ] & FLAG_CONV).
+// mode 1: when converged, copy Cin (the current W) to C instead.
+// mode 2: always run.
+template <bool TA, bool TB>
+__global__ __launch_bounds__(256) void dgemm16_kernel(const double* __restrict__ A, int lda,
+                                                      const double* __restrict__ B, int ldb,
+                                                      double* C, int ldc, const double* Cin, int ldcin,
+                                                      double alpha, double beta, double gamma,
+                                                      const int32_t* __restrict__ st, int mode) {
+  const int m = st[ST_JM];
+  const int i0 = blockIdx.y * 16, j0 = blockIdx.x * 16;
+  if (i0 >= m || j0 >= m) return;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int i = i0 + ty, j = j0 + tx;
+  const bool conv = (st[ST_PCJ] & FLAG_CONV) != 0;
+  if (mode == 0 && conv) return;
+  if (mode == 1 && conv) {
+    if (i < m && j < m) C[(size_t)i * ldc + j] = Cin[(size_t)i * ldcin + j];
+    return;
+  }
+  __shared__ double As[32][17];
+  __shared__ double Bs[32][17];
+  double acc = 0.0;
+  for (int k0 = 0; k0 < m; k0 += 32) {
+    // coalesced loads: along i for A^T / along k for A, along j for B / along k for B^T
+    for (int e = threadIdx.x; e < 512; e += 256) {
+      int kk, rr;
+      if (TA) { kk = e >> 4; rr = e & 15; } else { rr = e >> 5; kk = e & 31; }
+      int kg = k0 + kk, ia = i0 + rr;
+      double a = 0.0;
+      if (kg < m && ia < m) a = TA ? A[(size_t)kg * lda + ia] : A[(size_t)ia * lda + kg];
+      As[kk][rr] = a;
+    }
+    for (int e = threadIdx.x; e < 512; e += 256) {
+      int kk, rr;
+      if (!TB) { kk = e >> 4; rr = e & 15; } else { rr = e >> 5; kk = e & 31; }
+      int kg = k0 + kk, jb = j0 + rr;
+      double b = 0.0;
+      if (kg < m && jb < m) b = TB ? B[(size_t)jb * ldb + kg] : B[(size_t)kg * ldb + jb];
+      Bs[kk][rr] = b;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int kk = 0; kk < 32; ++kk) acc = fma(As[kk][ty], Bs[kk][tx], acc);
+    __syncthreads();
+  }
+  if (i < m && j < m) {
+    double o = alpha * acc;
+    if (beta != 0.0) o += beta * Cin[(size_t)i * ldcin + j];
+    if (i == j) o += gamma;
+    C[(size_t)i * ldc + j] = o;
+  }
+}
+
+template <bool TA, bool TB>
+void dgemm(hipStream_t s, int m_max, const double* A, const double* B, double* C, const double* Cin,
+           int ld, double alpha, double beta, double gamma, const int32_t* st, int mode) {
+  dim3 grid((m_max + 15) / 16, (m_max + 15) / 16);
+  hipLaunchKernelGGL((dgemm16_kernel<TA, TB>), grid, dim3(256), 0, s, A, ld, B, ld, C, ld, Cin, ld,
+                     alpha, beta, gamma, st, mode);
+}
+
+// S = A, W = I, flags cleared.
+__global__ __launch_bounds__(256) void pcj_init_kernel(const double* __restrict__ A, double* S,
+                                                       double* W, int ld, int32_t* st) {
+  const int m = st[ST_JM];
+  const size_t total = (size_t)m * m;
+  for (size_t e = blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
+    int i = (int)(e / m), j = (int)(e % m);
+    S[(size_t)i * ld + j] = A[(size_t)i * ld + j];
+    W[(size_t)i * ld + j] = (i == j) ? 1.0 : 0.0;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) { st[ST_PCJ] = 0; st[ST_PCJIT] = 0; }
+}
+
+__device__ __forceinline__ double coupling(double sij, double di, double dj) {
+  double dd = di * dj;
+  double a = fabs(sij);
+  if (dd > 0.0) return a / sqrt(dd);
+  return a > 0.0 ? INFINITY : 0.0;
+}
+
+__device__ __forceinline__ void rot2(double app, double aqq, double apq, double* c, double* s) {
+  double tau = (aqq - app) / (2.0 * apq);
+  double tt = (tau >= 0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
+  *c = 1.0 / sqrt(1.0 + tt * tt);
+  *s = tt * (*c);
+}
+
+// Serial cyclic Jacobi on a c x c block (c <= CMAX_S) held in LDS by one thread.
+__device__ void jacobi_serial(double* S, double* V, int c) {
+  for (int i = 0; i < c * c; ++i) V[i] = (i / c == i % c) ? 1.0 : 0.0;
+  for (int sweep = 0; sweep < 30; ++sweep) {
+    int rot = 0;
+    for (int p = 0; p < c - 1; ++p)
+      for (int q = p + 1; q < c; ++q) {
+        double apq = S[p * c + q];
+        if (apq == 0.0 || !(fabs(apq) > 1e-15 * sqrt(fabs(S[p * c + p] * S[q * c + q])))) continue;
+        double cs, sn;
+        rot2(S[p * c + p], S[q * c + q], apq, &cs, &sn);
+        ++rot;
+        for (int x = 0; x < c; ++x) {  // columns p, q
+          double sp = S[x * c + p], sq = S[x * c + q];
+          S[x * c + p] = cs * sp - sn * sq;
+          S[x * c + q] = sn * sp + cs * sq;
+        }
+        for (int x = 0; x < c; ++x) {  // rows p, q
+          double sp = S[p * c + x], sq = S[q * c + x];
+          S[p * c + x] = cs * sp - sn * sq;
+          S[q * c + x] = sn * sp + cs * sq;
+        }
+        for (int x = 0; x < c; ++x) {
+          double vp = V[x * c + p], vq = V[x * c + q];
+          V[x * c + p] = cs * vp - sn * vq;
+          V[x * c + q] = sn * vp + cs * vq;
+        }
+      }
+    if (!rot) break;
+  }
+}
+
+struct AnalyzeLds {
+  double d[1024];
+  double red[32];
+  double cmat[NCL_MAX][CMAX_S * CMAX_S];
+  double vmat[NCL_MAX][CMAX_S * CMAX_S];
+  double pc[NPAIR_MAX], ps[NPAIR_MAX];
+  int lab[1024];
+  int size[1024];
+  int cid[1024];
+  int cnt[1024];
+  short ei[EMAX], ej[EMAX];
+  int members[NCL_MAX][CMAX_S];
+  int ccount[NCL_MAX];
+  int pi[NPAIR_MAX], pj[NPAIR_MAX];
+  unsigned char used[1024];
+  int nedge, ncl, npair, changed, anybig;
+};
+
+// One refinement step (see the file header), one workgroup of 1024 threads.
+// S (m x m, global) is overwritten; W gets the cluster rotations in place;
+// Km receives K and Pa = I + K/4.
+__global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W, int ld, double* Km,
+                                                           double* Pa, int32_t* st, int it) {
+  extern __shared__ unsigned char smem_raw[];
+  AnalyzeLds& L = *reinterpret_cast<AnalyzeLds*>(smem_raw);
+  const int m = st[ST_JM];
+  const int t = threadIdx.x, nt = blockDim.x;
+  if (st[ST_PCJ] & FLAG_CONV) return;
+  for (int i = t; i < m; i += nt) L.d[i] = S[(size_t)i * ld + i];
+  if (t < 32) L.red[t] = 0.0;
+  __syncthreads();
+  // 1. largest scaled coupling; strong pair count per thread
+  double cmax = 0.0;
+  int nstrong = 0;
+  const size_t tot = (size_t)m * m;
+  for (size_t e = t; e < tot; e += nt) {
+    int i = (int)(e / m), j = (int)(e % m);
+    if (j <= i) continue;
+    double sij = S[(size_t)i * ld + j];
+    double c = coupling(sij, L.d[i], L.d[j]);
+    if (c > cmax) cmax = c;
+    if (c > PCJ_TOL && fabs(sij) > PCJ_OMEGA * fabs(L.d[j] - L.d[i])) ++nstrong;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) cmax = fmax(cmax, __shfl_xor(cmax, o, 64));
+  if ((t & 63) == 0) L.red[t >> 6] = cmax;
+  L.cnt[t] = nstrong;
+  __syncthreads();
+  if (t == 0) {
+    double c = 0.0;
+    for (int w = 0; w < (nt >> 6); ++w) c = fmax(c, L.red[w]);
+    L.red[16] = c;
+    // exclusive scan of per-thread strong counts (deterministic edge order)
+    int run = 0;
+    for (int w = 0; w < nt; ++w) { int v = L.cnt[w]; L.cnt[w] = run; run += v; }
+    L.nedge = run < EMAX ? run : EMAX;
+    L.ncl = 0; L.npair = 0; L.anybig = 0;
+  }
+  __syncthreads();
+  if (!(L.red[16] >= PCJ_TOL)) {
+    // converged (a NaN coupling never counts as converged: it falls back)
+    if (L.red[16] < PCJ_TOL) {
+      if (t == 0) { st[ST_PCJ] |= FLAG_CONV; st[ST_PCJIT] = it; }
+      return;
+    }
+  }
+  // 2. strong pairs, in scan order
+  {
+    int off = L.cnt[t];
+    for (size_t e = t; e < tot; e += nt) {
+      int i = (int)(e / m), j = (int)(e % m);
+      if (j <= i) continue;
+      double sij = S[(size_t)i * ld + j];
+      double c = coupling(sij, L.d[i], L.d[j]);
+      if (c > PCJ_TOL && fabs(sij) > PCJ_OMEGA * fabs(L.d[j] - L.d[i])) {
+        if (off < EMAX) { L.ei[off] = (short)i; L.ej[off] = (short)j; }
+        ++off;
+      }
+    }
+  }
+  for (int i = t; i < m; i += nt) { L.lab[i] = i; L.size[i] = 0; L.used[i] = 0; L.cid[i] = -1; }
+  __syncthreads();
+  const int ne = L.nedge;
+  // 3. connected components by min-label propagation
+  for (int guard = 0; guard < 1024; ++guard) {
+    if (t == 0) L.changed = 0;
+    __syncthreads();
+    for (int e = t; e < ne; e += nt) {
+      int a = L.ei[e], b = L.ej[e];
+      int la = L.lab[a], lb = L.lab[b];
+      if (la != lb) {
+        int l = la < lb ? la : lb;
+        atomicMin(&L.lab[a], l);
+        atomicMin(&L.lab[b], l);
+        L.changed = 1;
+      }
+    }
+    __syncthreads();
+    for (int i = t; i < m; i += nt) L.lab[i] = L.lab[L.lab[i]];  // pointer jumping
+    __syncthreads();
+    if (!L.changed) break;
+  }
+  for (int i = t; i < m; i += nt) atomicAdd(&L.size[L.lab[i]], 1);
+  __syncthreads();
+  // 4. small clusters (2..CMAX_S) get ids in root order; the rest are "big"
+  if (t == 0) {
+    int n = 0;
+    for (int i = 0; i < m; ++i) {
+      if (L.lab[i] == i && L.size[i] >= 2) {
+        if (L.size[i] <= CMAX_S && n < NCL_MAX) { L.cid[i] = n; L.ccount[n] = 0; ++n; }
+        else L.anybig = 1;
+      }
+    }
+    L.ncl = n;
+  }
+  __syncthreads();
+  if (t == 0) {
+    // members in index order (deterministic)
+    for (int i = 0; i < m; ++i) {
+      int c = L.cid[L.lab[i]];
+      if (c >= 0 && L.size[L.lab[i]] >= 2) L.members[c][L.ccount[c]++] = i;
+    }
+    // greedy matching on strong pairs inside big components
+    int np = 0;
+    if (L.anybig) {
+      for (int e = 0; e < ne && np < NPAIR_MAX; ++e) {
+        int a = L.ei[e], b = L.ej[e];
+        if (L.cid[L.lab[a]] >= 0) continue;  // in a small cluster
+        if (L.used[a] || L.used[b]) continue;
+        L.used[a] = 1; L.used[b] = 1;
+        L.pi[np] = a; L.pj[np] = b;
+        ++np;
+      }
+    }
+    L.npair = np;
+  }
+  __syncthreads();
+  const int ncl = L.ncl, npair = L.npair;
+  // 5. exact solves: one thread per small cluster, one per matched pair
+  if (t < ncl) {
+    const int c = L.ccount[t];
+    double* Sc = L.cmat[t];
+    for (int a = 0; a < c; ++a)
+      for (int b = 0; b < c; ++b)
+        Sc[a * c + b] = S[(size_t)L.members[t][a] * ld + L.members[t][b]];
+    jacobi_serial(Sc, L.vmat[t], c);
+  }
+  for (int q = t; q < npair; q += nt) {
+    int a = L.pi[q], b = L.pj[q];
+    double cs = 1.0, sn = 0.0;
+    double apq = S[(size_t)a * ld + b];
+    if (apq != 0.0) rot2(L.d[a], L.d[b], apq, &cs, &sn);
+    L.pc[q] = cs; L.ps[q] = sn;
+  }
+  __syncthreads();
+  // 6. rows of S: S[C, :] <- R_C^T S[C, :]
+  for (int e = t; e < ncl * m; e += nt) {
+    int g = e / m, j = e % m;
+    int c = L.ccount[g];
+    double x[CMAX_S], y[CMAX_S];
+    for (int a = 0; a < c; ++a) x[a] = S[(size_t)L.members[g][a] * ld + j];
+    for (int b = 0; b < c; ++b) {
+      double acc = 0.0;
+      for (int a = 0; a < c; ++a) acc = fma(L.vmat[g][a * c + b], x[a], acc);
+      y[b] = acc;
+    }
+    for (int b = 0; b < c; ++b) S[(size_t)L.members[g][b] * ld + j] = y[b];
+  }
+  for (int e = t; e < npair * m; e += nt) {
+    int q = e / m, j = e % m;
+    int a = L.pi[q], b = L.pj[q];
+    double cs = L.pc[q], sn = L.ps[q];
+    double xa = S[(size_t)a * ld + j], xb = S[(size_t)b * ld + j];
+    S[(size_t)a * ld + j] = cs * xa - sn * xb;
+    S[(size_t)b * ld + j] = sn * xa + cs * xb;
+  }
+  __syncthreads();
+  // 7. columns of S and of W: X[:, C] <- X[:, C] R_C
+  for (int e = t; e < ncl * m; e += nt) {
+    int g = e / m, i = e % m;
+    int c = L.ccount[g];
+    double x[CMAX_S], w[CMAX_S];
+    for (int a = 0; a < c; ++a) {
+      x[a] = S[(size_t)i * ld + L.members[g][a]];
+      w[a] = W[(size_t)i * ld + L.members[g][a]];
+    }
+    for (int b = 0; b < c; ++b) {
+      double s1 = 0.0, s2 = 0.0;
+      for (int a = 0; a < c; ++a) {
+        s1 = fma(x[a], L.vmat[g][a * c + b], s1);
+        s2 = fma(w[a], L.vmat[g][a * c + b], s2);
+      }
+      S[(size_t)i * ld + L.members[g][b]] = s1;
+      W[(size_t)i * ld + L.members[g][b]] = s2;
+    }
+  }
+  for (int e = t; e < npair * m; e += nt) {
+    int q = e / m, i = e % m;
+    int a = L.pi[q], b = L.pj[q];
+    double cs = L.pc[q], sn = L.ps[q];
+    double xa = S[(size_t)i * ld + a], xb = S[(size_t)i * ld + b];
+    S[(size_t)i * ld + a] = cs * xa - sn * xb;
+    S[(size_t)i * ld + b] = sn * xa + cs * xb;
+    double wa = W[(size_t)i * ld + a], wb = W[(size_t)i * ld + b];
+    W[(size_t)i * ld + a] = cs * wa - sn * wb;
+    W[(size_t)i * ld + b] = sn * wa + cs * wb;
+  }
+  __syncthreads();
+  for (int i = t; i < m; i += nt) L.d[i] = S[(size_t)i * ld + i];
+  __syncthreads();
+  // 8. first-order angles for every other pair; K antisymmetric
+  for (size_t e = t; e < tot; e += nt) {
+    int i = (int)(e / m), j = (int)(e % m);
+    double k = 0.0;
+    if (i < j) {
+      double sij = S[(size_t)i * ld + j];
+      double den = L.d[j] - L.d[i];
+      if (den != 0.0 && fabs(sij) <= PCJ_OMEGA * fabs(den)) k = fmin(fmax(sij / den, -PCJ_CLIP), PCJ_CLIP);
+      if (!isfinite(k)) k = 0.0;
+    } else if (i > j) {
+      double sji = S[(size_t)j * ld + i];
+      double den = L.d[i] - L.d[j];
+      if (den != 0.0 && fabs(sji) <= PCJ_OMEGA * fabs(den)) k = -fmin(fmax(sji / den, -PCJ_CLIP), PCJ_CLIP);
+      if (!isfinite(k)) k = 0.0;
+    }
+    Km[(size_t)i * ld + j] = k;
+    Pa[(size_t)i * ld + j] = (i == j ? 1.0 : 0.0) + 0.25 * k;
+  }
+  if (t == 0) st[ST_PCJIT] = it + 1;
+}
+
+// Eigenvalues lambda_i = w_i^T (A w_i) from T = A W; V = W when converged,
+// otherwise hand the matrix to the Jacobi fallback (S = A, flag). Grid (m).
+__global__ __launch_bounds__(256) void pcj_final_kernel(const double* __restrict__ Wf,
+                                                        const double* __restrict__ T,
+                                                        const double* __restrict__ A, double* S,
+                                                        double* V, int ld, int32_t* st) {
+  const int m = st[ST_JM];
+  const int j = blockIdx.x;
+  if (j >= m) return;
+  const bool conv = (st[ST_PCJ] & FLAG_CONV) != 0;
+  __shared__ double red[4];
+  if (conv) {
+    double acc = 0.0;
+    for (int r = threadIdx.x; r < m; r += 256) {
+      double w = Wf[(size_t)r * ld + j];
+      acc = fma(w, T[(size_t)r * ld + j], acc);
+      V[(size_t)r * ld + j] = w;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) S[(size_t)j * ld + j] = red[0] + red[1] + red[2] + red[3];
+  } else {
+    for (int r = threadIdx.x; r < m; r += 256) S[(size_t)j * ld + r] = A[(size_t)j * ld + r];
+    if (j == 0 && threadIdx.x == 0) st[ST_PCJ] |= FLAG_FALLBACK;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Fallback: single-workgroup cyclic Jacobi on S (m x m fp64, global) with the
+// eigenvectors accumulated in V; parallel round-robin ordering, each round
+// applying up to m/2 disjoint rotations as 2x2 block updates. Runs only when
+// the refinement did not converge.
+__global__ __launch_bounds__(1024) void core_jacobi_kernel(double* S, double* V, int ld,
+                                                           int32_t* st, double tol, int max_sweeps) {
+  if (!(st[ST_PCJ] & FLAG_FALLBACK)) return;
+  __shared__ double cs[640], sn[640];
+  __shared__ int pp[640], qq[640];
+  __shared__ int active;
+  const int n = st[ST_JM];
+  const int t = threadIdx.x, nt = blockDim.x;
+  for (int idx = t; idx < n * n; idx += nt) V[(size_t)(idx / n) * ld + idx % n] = (idx / n == idx % n) ? 1.0 : 0.0;
+  __syncthreads();
+  int sweep = 0;
+  if (n >= 2) {
+    const int N = (n + 1) & ~1, half = N / 2;
+    for (; sweep < max_sweeps; ++sweep) {
+      int rot_sweep = 0;
+      for (int round = 0; round < N - 1; ++round) {
+        if (t == 0) active = 0;
+        __syncthreads();
+        for (int i = t; i < half; i += nt) {
+          int a = (i == 0) ? round % (N - 1) : (round + i) % (N - 1);
+          int b = (i == 0) ? N - 1 : (round - i + (N - 1)) % (N - 1);
+          int p = a < b ? a : b, q = a < b ? b : a;
+          double c = 1.0, s = 0.0;
+          if (q < n) {
+            double app = S[(size_t)p * ld + p], aqq = S[(size_t)q * ld + q], apq = S[(size_t)p * ld + q];
+            if (apq != 0.0 && fabs(apq) > tol * sqrt(fabs(app * aqq))) {
+              rot2(app, aqq, apq, &c, &s);
+              atomicAdd(&active, 1);
+            }
+          }
+          cs[i] = c; sn[i] = s; pp[i] = p; qq[i] = q;
+        }
+        __syncthreads();
+        if (active) {
+          rot_sweep = 1;
+          for (int blk = t; blk < half * half; blk += nt) {
+            int a = blk / half, bb = blk % half;
+            if (a > bb) continue;
+            int pa = pp[a], qa = qq[a], pb = pp[bb], qb = qq[bb];
+            if (qa >= n || qb >= n) continue;
+            double ca = cs[a], sa = sn[a], cb = cs[bb], sb = sn[bb];
+            if (sa == 0.0 && sb == 0.0) continue;
+            double x11 = S[(size_t)pa * ld + pb], x12 = S[(size_t)pa * ld + qb];
+            double x21 = S[(size_t)qa * ld + pb], x22 = S[(size_t)qa * ld + qb];
+            double y11 = ca * x11 - sa * x21, y12 = ca * x12 - sa * x22;
+            double y21 = sa * x11 + ca * x21, y22 = sa * x12 + ca * x22;
+            double z11 = y11 * cb - y12 * sb, z12 = y11 * sb + y12 * cb;
+            double z21 = y21 * cb - y22 * sb, z22 = y21 * sb + y22 * cb;
+            if (a == bb) { z12 = 0.0; z21 = 0.0; }
+            S[(size_t)pa * ld + pb] = z11; S[(size_t)pa * ld + qb] = z12;
+            S[(size_t)qa * ld + pb] = z21; S[(size_t)qa * ld + qb] = z22;
+            if (a != bb) {
+              S[(size_t)pb * ld + pa] = z11; S[(size_t)qb * ld + pa] = z12;
+              S[(size_t)pb * ld + qa] = z21; S[(size_t)qb * ld + qa] = z22;
+            }
+          }
+          for (int e = t; e < n * half; e += nt) {
+            int x = e / half, a = e % half;
+            int p = pp[a], q = qq[a];
+            if (q >= n) continue;
+            double c = cs[a], s = sn[a];
+            if (s == 0.0) continue;
+            double vp = V[(size_t)x * ld + p], vq = V[(size_t)x * ld + q];
+            V[(size_t)x * ld + p] = c * vp - s * vq;
+            V[(size_t)x * ld + q] = s * vp + c * vq;
+          }
+        }
+        __syncthreads();
+      }
+      if (!rot_sweep) break;
+    }
+  }
+  if (t == 0) {
+    st[ST_SWEEPS] = sweep;
+    if (sweep >= max_sweeps) atomicOr(&st[ST_STATUS], ISKV_DEV_NOCONV);
+  }
+}
+
+}  // namespace
+
+void iskv_dgemm(hipStream_t s, int m_max, const double* A, bool ta, const double* B, bool tb, double* C,
+                const double* Cin, int ld, double alpha, double beta, double gamma, const int32_t* st,
+                int mode) {
+  if (!ta && !tb) dgemm<false, false>(s, m_max, A, B, C, Cin, ld, alpha, beta, gamma, st, mode);
+  else if (ta && !tb) dgemm<true, false>(s, m_max, A, B, C, Cin, ld, alpha, beta, gamma, st, mode);
+  else if (!ta && tb) dgemm<false, true>(s, m_max, A, B, C, Cin, ld, alpha, beta, gamma, st, mode);
+  else dgemm<true, true>(s, m_max, A, B, C, Cin, ld, alpha, beta, gamma, st, mode);
+}
+
+int iskv_core_eig_setup() {
+  ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)pcj_analyze_kernel,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)sizeof(AnalyzeLds)));
+  return ISKV_OK;
+}
+
+// Eigen-decompose the m x m matrix in w.A (m = st[ST_JM]): on return the
+// diagonal of w.S holds the eigenvalues and w.V the eigenvectors (columns),
+// unsorted. Fixed launch sequence; no host synchronisation.
+int iskv_launch_core_eig(isvd_handle* h) {
+  const isvd_ws& w = h->w;
+  hipStream_t s = h->stream;
+  const int mm = h->m_max, ld = h->m_max;
+  int32_t* st = w.st;
+  hipLaunchKernelGGL(pcj_init_kernel, dim3(128), dim3(256), 0, s, w.A, w.S, w.W0, ld, st);
+  double* cur = w.W0;
+  double* nxt = w.W1;
+  const size_t lds = sizeof(AnalyzeLds);
+  for (int it = 0; it < PCJ_MAXIT; ++it) {
+    if (it > 0) {
+      dgemm<false, false>(s, mm, w.A, cur, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 0);
+      dgemm<true, false>(s, mm, cur, w.T, w.S, nullptr, ld, 1.0, 0.0, 0.0, st, 0);
+    }
+    hipLaunchKernelGGL(pcj_analyze_kernel, dim3(1), dim3(1024), lds, s, w.S, cur, ld, w.Km, w.Pa, st, it);
+    // exp(K) = I + K (I + K/2 (I + K/3 (I + K/4)))
+    dgemm<false, false>(s, mm, w.Km, w.Pa, w.Pb, nullptr, ld, 1.0 / 3.0, 0.0, 1.0, st, 0);
+    dgemm<false, false>(s, mm, w.Km, w.Pb, w.Pa, nullptr, ld, 0.5, 0.0, 1.0, st, 0);
+    dgemm<false, false>(s, mm, w.Km, w.Pa, w.Pb, nullptr, ld, 1.0, 0.0, 1.0, st, 0);
+    dgemm<false, false>(s, mm, cur, w.Pb, nxt, cur, ld, 1.0, 0.0, 0.0, st, 1);
+    double* tmp = cur; cur = nxt; nxt = tmp;
+  }
+  // one step past the last iteration so a convergence reached there is seen
+  dgemm<false, false>(s, mm, w.A, cur, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 0);
+  dgemm<true, false>(s, mm, cur, w.T, w.S, nullptr, ld, 1.0, 0.0, 0.0, st, 0);
+  hipLaunchKernelGGL(pcj_analyze_kernel, dim3(1), dim3(1024), lds, s, w.S, cur, ld, w.Km, w.Pa, st,
+                     PCJ_MAXIT);
+  // Newton-Schulz: W <- 1.5 W - 0.5 W (W^T W); then T = A W for the eigenvalues
+  dgemm<true, false>(s, mm, cur, cur, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 2);
+  dgemm<false, false>(s, mm, cur, w.T, nxt, cur, ld, -0.5, 1.5, 0.0, st, 2);
+  dgemm<false, false>(s, mm, w.A, nxt, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 2);
+  hipLaunchKernelGGL(pcj_final_kernel, dim3(mm), dim3(256), 0, s, nxt, w.T, w.A, w.S, w.V, ld, st);
+  hipLaunchKernelGGL(core_jacobi_kernel, dim3(1), dim3(1024), 0, s, w.S, w.V, ld, st, 1e-13,
+                     ISKV_JACOBI_MAX_SWEEPS);
+  ISKV_HIP_CHECK(hipGetLastError());
+  return ISKV_OK;
+}

@@ -50,6 +50,15 @@ size_t carve(const iskv_config* c, char* base, isvd_ws* w) {
   x.FP = (float*)take(Bm * Bm * 4);
   x.A = (double*)take(M * M * 8);
   x.V = (double*)take(M * M * 8);
+  x.S = (double*)take(M * M * 8);
+  x.W0 = (double*)take(M * M * 8);
+  x.W1 = (double*)take(M * M * 8);
+  x.T = (double*)take(M * M * 8);
+  x.Km = (double*)take(M * M * 8);
+  x.Pa = (double*)take(M * M * 8);
+  x.Pb = (double*)take(M * M * 8);
+  x.MB = (double*)take(M * M * 8);
+  x.Zb = (double*)take(M * M * 8);
   x.lam = (double*)take(M * 8);
   x.rot_cap = 0;
   x.rot = nullptr;
@@ -119,6 +128,15 @@ int isvd_init(isvd_handle** out, const iskv_config* cfg, float* C, float* sigma,
 }
 
 int32_t isvd_rows(const isvd_handle* h) { return h ? h->n_host : 0; }
+
+int isvd_query_state(isvd_handle* h, int32_t* state, int32_t count) {
+  if (!h || !state || count < 1 || count > ST_COUNT) return ISKV_EINVAL;
+  int32_t st[ST_COUNT];
+  ISKV_HIP_CHECK(hipStreamSynchronize(h->stream));
+  ISKV_HIP_CHECK(hipMemcpy(st, h->w.st, sizeof(st), hipMemcpyDeviceToHost));
+  for (int i = 0; i < count; ++i) state[i] = st[i];
+  return ISKV_OK;
+}
 
 int isvd_merge_block(isvd_handle* h, const float* F, const int32_t* pos_F, int32_t b) {
   if (!h || !F || !pos_F) return ISKV_EINVAL;

@@ -20,7 +20,9 @@ enum {
   ST_SWEEPS = 7,   // Jacobi sweeps used by the last eigensolve
   ST_EZERO = 8,    // 1 when the residual of the merge in flight is exactly zero
   ST_JM = 9,       // order of the matrix handed to the Jacobi eigensolver
-  ST_ROUNDS = 10,  // rounds logged by the last Jacobi solve
+  ST_ROUNDS = 10,  // reserved
+  ST_PCJ = 11,     // core eigensolver flags: 1 converged, 2 Jacobi fallback used
+  ST_PCJIT = 12,   // refinement steps used by the last core eigensolve
   ST_COUNT = 16
 };
 
@@ -38,6 +40,15 @@ struct isvd_ws {
   float* FP;          // [b_max x b_max]  F P
   double* A;          // [m_max x m_max]  core Gram / reorth matrix
   double* V;          // [m_max x m_max]  eigenvectors
+  double* S;          // [m_max x m_max]  W^T A W / Jacobi working matrix
+  double* W0;         // [m_max x m_max]  eigenvector iterate (ping)
+  double* W1;         // [m_max x m_max]  eigenvector iterate (pong)
+  double* T;          // [m_max x m_max]  A W
+  double* Km;         // [m_max x m_max]  first-order angles K
+  double* Pa;         // [m_max x m_max]  exp(K) partial products
+  double* Pb;         // [m_max x m_max]
+  double* MB;         // [m_max x m_max]  reorth: (B^T B)^(1/2)
+  double* Zb;         // [m_max x m_max]  reorth: (B^T B)^(-1/2)
   double* lam;        // [m_max]
   double* rot;        // [rot_cap] Jacobi rotation log (c, s) pairs
   float* Hc;          // [m_max x r_max]  kept right singular vectors of the core
@@ -83,6 +94,11 @@ struct iskv_window {
 
 // ---- launch helpers implemented in the kernel translation units ----
 int iskv_kernel_setup();
+int iskv_core_eig_setup();
+int iskv_launch_core_eig(isvd_handle* h);
+void iskv_dgemm(hipStream_t s, int m_max, const double* A, bool ta, const double* B, bool tb, double* C,
+                const double* Cin, int ld, double alpha, double beta, double gamma, const int32_t* st,
+                int mode);
 int iskv_launch_merge(isvd_handle* h, const float* F, const int32_t* pos_F, int32_t b);
 int iskv_launch_reorth(isvd_handle* h);
 int iskv_launch_reconstruct(const isvd_handle* h, const float* X_exact, const int32_t* pos_exact,

@@ -325,91 +325,6 @@ __global__ __launch_bounds__(256) void core_gram_kernel(const float* __restrict_
   A[(size_t)i * lda + j] = acc;
 }
 
-// ----------------------------------------------------------------------------
-// Single-workgroup cyclic Jacobi eigensolver for the core (or the re-orth
-// matrix): S (m x m fp64, global, overwritten) and V (m x m fp64, global).
-// Parallel round-robin ordering; every round applies up to m/2 disjoint
-// rotations as 2x2 block updates. Threshold |s_pq| <= tol sqrt(s_pp s_qq).
-__global__ __launch_bounds__(1024) void core_jacobi_kernel(double* S, double* V, int ld,
-                                                           int32_t* st, double tol, int max_sweeps) {
-  __shared__ double cs[640], sn[640];
-  __shared__ int pp[640], qq[640];
-  __shared__ int active;
-  const int n = st[ST_JM];
-  const int t = threadIdx.x, nt = blockDim.x;
-  for (int idx = t; idx < n * n; idx += nt) V[(size_t)(idx / n) * ld + idx % n] = (idx / n == idx % n) ? 1.0 : 0.0;
-  __syncthreads();
-  int sweep = 0;
-  if (n >= 2) {
-    const int N = (n + 1) & ~1, half = N / 2;
-    for (; sweep < max_sweeps; ++sweep) {
-      int rot_sweep = 0;
-      for (int round = 0; round < N - 1; ++round) {
-        if (t == 0) active = 0;
-        __syncthreads();
-        for (int i = t; i < half; i += nt) {
-          int a = (i == 0) ? round % (N - 1) : (round + i) % (N - 1);
-          int b = (i == 0) ? N - 1 : (round - i + (N - 1)) % (N - 1);
-          int p = a < b ? a : b, q = a < b ? b : a;
-          double c = 1.0, s = 0.0;
-          if (q < n) {
-            double app = S[(size_t)p * ld + p], aqq = S[(size_t)q * ld + q], apq = S[(size_t)p * ld + q];
-            if (apq != 0.0 && fabs(apq) > tol * sqrt(fabs(app * aqq))) {
-              double tau = (aqq - app) / (2.0 * apq);
-              double tt = (tau >= 0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
-              c = 1.0 / sqrt(1.0 + tt * tt);
-              s = tt * c;
-              atomicAdd(&active, 1);
-            }
-          }
-          cs[i] = c; sn[i] = s; pp[i] = p; qq[i] = q;
-        }
-        __syncthreads();
-        if (active) {
-          rot_sweep = 1;
-          for (int blk = t; blk < half * half; blk += nt) {
-            int a = blk / half, bb = blk % half;
-            if (a > bb) continue;
-            int pa = pp[a], qa = qq[a], pb = pp[bb], qb = qq[bb];
-            if (qa >= n || qb >= n) continue;
-            double ca = cs[a], sa = sn[a], cb = cs[bb], sb = sn[bb];
-            if (sa == 0.0 && sb == 0.0) continue;
-            double x11 = S[(size_t)pa * ld + pb], x12 = S[(size_t)pa * ld + qb];
-            double x21 = S[(size_t)qa * ld + pb], x22 = S[(size_t)qa * ld + qb];
-            double y11 = ca * x11 - sa * x21, y12 = ca * x12 - sa * x22;
-            double y21 = sa * x11 + ca * x21, y22 = sa * x12 + ca * x22;
-            double z11 = y11 * cb - y12 * sb, z12 = y11 * sb + y12 * cb;
-            double z21 = y21 * cb - y22 * sb, z22 = y21 * sb + y22 * cb;
-            if (a == bb) { z12 = 0.0; z21 = 0.0; }
-            S[(size_t)pa * ld + pb] = z11; S[(size_t)pa * ld + qb] = z12;
-            S[(size_t)qa * ld + pb] = z21; S[(size_t)qa * ld + qb] = z22;
-            if (a != bb) {
-              S[(size_t)pb * ld + pa] = z11; S[(size_t)qb * ld + pa] = z12;
-              S[(size_t)pb * ld + qa] = z21; S[(size_t)qb * ld + qa] = z22;
-            }
-          }
-          for (int e = t; e < n * half; e += nt) {
-            int x = e / half, a = e % half;
-            int p = pp[a], q = qq[a];
-            if (q >= n) continue;
-            double c = cs[a], s = sn[a];
-            if (s == 0.0) continue;
-            double vp = V[(size_t)x * ld + p], vq = V[(size_t)x * ld + q];
-            V[(size_t)x * ld + p] = c * vp - s * vq;
-            V[(size_t)x * ld + q] = s * vp + c * vq;
-          }
-        }
-        __syncthreads();
-      }
-      if (!rot_sweep) break;
-    }
-  }
-  if (t == 0) {
-    st[ST_SWEEPS] = sweep;
-    if (sweep >= max_sweeps) atomicOr(&st[ST_STATUS], ISKV_DEV_NOCONV);
-  }
-}
-
 // Sort eigenpairs by descending eigenvalue, keep `keep` of them:
 // Hc[:, t] = V[:, order[t]] (fp32, ld r_max), sig_new[t] = sqrt(max(lambda, 0)).
 // keep = min(r_max, n) for a merge; n for re-orthogonalisation.
@@ -622,88 +537,47 @@ __global__ __launch_bounds__(256) void gram_partial_kernel(const float* __restri
   if (i < k && j < k) Gpart[((size_t)blockIdx.y * ldg + i) * ldg + j] = acc;
 }
 
-// Sum the partial Grams of C, Cholesky of G_B = R_B^T R_B (upper R_B), and
-// H = R_B G_C R_B^T into S (k x k) for the eigensolver. One workgroup.
-__global__ __launch_bounds__(1024) void reorth_prep_kernel(double* GCpart,
-                                                           int nchunks, const double* __restrict__ GBpart,
-                                                           int nchunks_b, int ldg, double* GC,
-                                                           double* RB, double* S, int lds,
-                                                           int32_t* st) {
+// Sum the partial Grams: G_C = sum of the C slices, G_B = the B slice, both
+// into m_max-ld fp64 matrices, and Z0 = 1.5 I - 0.5 G_B (first Newton-Schulz
+// step towards G_B^(-1/2)). Grid-stride over k x k.
+__global__ __launch_bounds__(256) void reorth_sum_kernel(const double* __restrict__ Gpart, int nchunks,
+                                                         int ldg, double* GC, double* GB, double* Z0,
+                                                         int ld, const int32_t* st) {
   const int k = st[ST_K];
-  const int t = threadIdx.x, nt = blockDim.x;
-  for (int idx = t; idx < k * k; idx += nt) {
-    int i = idx / k, j = idx % k;
-    double a = 0.0, bsum = 0.0;
-    for (int s = 0; s < nchunks; ++s) a += GCpart[((size_t)s * ldg + i) * ldg + j];
-    for (int s = 0; s < nchunks_b; ++s) bsum += GBpart[((size_t)s * ldg + i) * ldg + j];
-    GC[(size_t)i * ldg + j] = a;
-    RB[(size_t)i * ldg + j] = bsum;  // G_B, factored in place below
+  const size_t tot = (size_t)k * k;
+  for (size_t e = blockIdx.x * 256 + threadIdx.x; e < tot; e += (size_t)gridDim.x * 256) {
+    int i = (int)(e / k), j = (int)(e % k);
+    double a = 0.0;
+    for (int c = 0; c < nchunks; ++c) a += Gpart[((size_t)c * ldg + i) * ldg + j];
+    double gb = Gpart[((size_t)nchunks * ldg + i) * ldg + j];
+    GC[(size_t)i * ld + j] = a;
+    GB[(size_t)i * ld + j] = gb;
+    Z0[(size_t)i * ld + j] = (i == j ? 1.5 : 0.0) - 0.5 * gb;
   }
-  __syncthreads();
-  // Right-looking Cholesky, upper factor stored in the upper triangle of RB.
-  for (int c = 0; c < k; ++c) {
-    if (t == 0) RB[(size_t)c * ldg + c] = sqrt(fmax(RB[(size_t)c * ldg + c], 1e-300));
-    __syncthreads();
-    double dcc = RB[(size_t)c * ldg + c];
-    for (int j = c + 1 + t; j < k; j += nt) RB[(size_t)c * ldg + j] /= dcc;
-    __syncthreads();
-    for (int idx = t; idx < (k - c - 1) * (k - c - 1); idx += nt) {
-      int i = c + 1 + idx / (k - c - 1), j = c + 1 + idx % (k - c - 1);
-      if (j >= i) RB[(size_t)i * ldg + j] -= RB[(size_t)c * ldg + i] * RB[(size_t)c * ldg + j];
-    }
-    __syncthreads();
-  }
-  for (int idx = t; idx < k * k; idx += nt) {
-    int i = idx / k, j = idx % k;
-    if (j < i) RB[(size_t)i * ldg + j] = 0.0;
-  }
-  __syncthreads();
-  // T = R_B G_C into the (now free) partial-Gram slice 0, then H = T R_B^T.
-  double* T = (double*)GCpart;
-  for (int idx = t; idx < k * k; idx += nt) {
-    int i = idx / k, j = idx % k;
-    double acc = 0.0;
-    for (int a = i; a < k; ++a) acc = fma(RB[(size_t)i * ldg + a], GC[(size_t)a * ldg + j], acc);
-    T[(size_t)i * ldg + j] = acc;
-  }
-  __syncthreads();
-  for (int idx = t; idx < k * k; idx += nt) {
-    int i = idx / k, j = idx % k;
-    double acc = 0.0;
-    for (int bb = j; bb < k; ++bb) acc = fma(T[(size_t)i * ldg + bb], RB[(size_t)j * ldg + bb], acc);
-    S[(size_t)i * lds + j] = acc;
-  }
-  if (t == 0) st[ST_JM] = k;
 }
 
-// After the eigensolve of H = Y Lambda Y^T (Y in Hc, sorted):
-//   T1 = R_B^T Y  (coordinate transform, into Hc region "H1")
-//   T2 = R_B^{-1} Y (basis transform)
-// One workgroup; k x k each, fp32 outputs with ld r_max.
-__global__ __launch_bounds__(1024) void reorth_transforms_kernel(const double* __restrict__ V,
-                                                                 int ldv, const int32_t* __restrict__ order,
-                                                                 const double* __restrict__ RB, int ldg,
-                                                                 float* T1, float* T2, int ldt,
-                                                                 double* X, const int32_t* st) {
-  const int k = st[ST_K];
-  const int t = threadIdx.x, nt = blockDim.x;
-  // T1[i][c] = sum_{a <= i} RB[a][i] * Y[a][c]
-  for (int idx = t; idx < k * k; idx += nt) {
-    int i = idx / k, c = idx % k;
-    int oc = min(max(order[c], 0), k - 1);
-    double acc = 0.0;
-    for (int a = 0; a <= i; ++a) acc = fma(RB[(size_t)a * ldg + i], V[(size_t)a * ldv + oc], acc);
-    T1[(size_t)i * ldt + c] = (float)acc;
+// Y[:, t] = V[:, order[t]] (fp64, sorted eigenvectors). Grid-stride.
+__global__ __launch_bounds__(256) void permute_cols_kernel(const double* __restrict__ V,
+                                                           const int32_t* __restrict__ order,
+                                                           double* Y, int ld, const int32_t* st) {
+  const int k = st[ST_JM];
+  const size_t tot = (size_t)k * k;
+  for (size_t e = blockIdx.x * 256 + threadIdx.x; e < tot; e += (size_t)gridDim.x * 256) {
+    int i = (int)(e / k), t = (int)(e % k);
+    Y[(size_t)i * ld + t] = V[(size_t)i * ld + min(max(order[t], 0), k - 1)];
   }
-  // T2 = R_B^{-1} Y: back substitution per column c (one thread per column).
-  for (int c = t; c < k; c += nt) {
-    int oc = min(max(order[c], 0), k - 1);
-    for (int i = k - 1; i >= 0; --i) {
-      double acc = V[(size_t)i * ldv + oc];
-      for (int a = i + 1; a < k; ++a) acc -= RB[(size_t)i * ldg + a] * X[(size_t)a * ldg + c];
-      X[(size_t)i * ldg + c] = acc / RB[(size_t)i * ldg + i];
-      T2[(size_t)i * ldt + c] = (float)X[(size_t)i * ldg + c];
-    }
+}
+
+// fp64 (ld) -> fp32 (ld r_max) for the two k x k transforms.
+__global__ __launch_bounds__(256) void to_f32_kernel(const double* __restrict__ X1,
+                                                     const double* __restrict__ X2, int ld, float* Y1,
+                                                     float* Y2, int ldy, const int32_t* st) {
+  const int k = st[ST_K];
+  const size_t tot = (size_t)k * k;
+  for (size_t e = blockIdx.x * 256 + threadIdx.x; e < tot; e += (size_t)gridDim.x * 256) {
+    int i = (int)(e / k), j = (int)(e % k);
+    Y1[(size_t)i * ldy + j] = (float)X1[(size_t)i * ld + j];
+    Y2[(size_t)i * ldy + j] = (float)X2[(size_t)i * ld + j];
   }
 }
 
@@ -727,14 +601,8 @@ int iskv_kernel_setup() {
                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds));
   ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)basis_update_kernel,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds));
+  if (iskv_core_eig_setup() != ISKV_OK) return ISKV_EHIP;
   done = 1;
-  return ISKV_OK;
-}
-
-static int launch_jacobi(isvd_handle* h) {
-  const isvd_ws& w = h->w;
-  hipLaunchKernelGGL(core_jacobi_kernel, dim3(1), dim3(1024), 0, h->stream, w.A, w.V, h->m_max,
-                     w.st, 1e-13, ISKV_JACOBI_MAX_SWEEPS);
   return ISKV_OK;
 }
 
@@ -771,7 +639,7 @@ int iskv_launch_merge(isvd_handle* h, const float* F, const int32_t* pos_F, int3
                        w.A, h->m_max, w.st);
   }
   hipLaunchKernelGGL(set_jm_kernel, dim3(1), dim3(1), 0, s, w.st, (int)ST_M);
-  launch_jacobi(h);
+  iskv_launch_core_eig(h);
   hipLaunchKernelGGL(eig_finish_kernel, dim3(1), dim3(1024), 0, s, w.A, w.V, h->m_max, w.Hc, R,
                      w.sig_new, w.order, w.st, R, 1);
   // 8. coordinate sync of old rows, new rows, basis update
@@ -793,11 +661,18 @@ int iskv_launch_merge(isvd_handle* h, const float* F, const int32_t* pos_F, int3
   return ISKV_OK;
 }
 
+// Re-orthogonalisation (iS-KV notes §4.4), written with Grams instead of the
+// notes' thin QRs: with G_B = B^T B = M_B^2 (M_B its symmetric square root,
+// Z = M_B^-1 by Newton-Schulz) and G_C = C^T C, the eigendecomposition
+// M_B G_C M_B = Y Lambda Y^T gives C' = C M_B Y (orthogonal columns, norms
+// sqrt(Lambda)) and B' = B Z Y (orthonormal), with C' B'^T = C B^T. This is
+// the notes' U <- Q_U W, B <- Q_B V with R_U Sigma R_B^T = W S V^T expressed
+// through M = R_U Sigma R_B^T's right singular vectors.
 int iskv_launch_reorth(isvd_handle* h) {
   const iskv_config& c = h->cfg;
   const isvd_ws& w = h->w;
   hipStream_t s = h->stream;
-  const int R = c.r_max, D = c.D;
+  const int R = c.r_max, D = c.D, mm = h->m_max, ld = h->m_max;
   const int n = h->n_host;
   if (n == 0) return ISKV_OK;
   const int tiles = (R + 15) / 16;
@@ -805,19 +680,30 @@ int iskv_launch_reorth(isvd_handle* h) {
   int nchunks = (n + rows_per_chunk - 1) / rows_per_chunk;
   if (nchunks > w.gram_splits - 1) nchunks = w.gram_splits - 1;
   const int rpc = (n + nchunks - 1) / nchunks;
-  int nchunks_b = 1;
-  // partial Grams: C into slices [0, nchunks), B into slice nchunks
+  hipLaunchKernelGGL(set_jm_kernel, dim3(1), dim3(1), 0, s, w.st, (int)ST_K);
   hipLaunchKernelGGL(gram_partial_kernel, dim3(tiles * tiles, nchunks), dim3(256), 0, s, h->C, R, n,
                      w.st, w.GC, R, rpc);
-  hipLaunchKernelGGL(gram_partial_kernel, dim3(tiles * tiles, nchunks_b), dim3(256), 0, s, h->B, R, D,
-                     w.st, w.GC + (size_t)nchunks * R * R, R, D);
-  hipLaunchKernelGGL(reorth_prep_kernel, dim3(1), dim3(1024), 0, s, w.GC, nchunks,
-                     w.GC + (size_t)nchunks * R * R, nchunks_b, R, w.GB, w.RB, w.A, h->m_max, w.st);
-  launch_jacobi(h);
-  hipLaunchKernelGGL(eig_finish_kernel, dim3(1), dim3(1024), 0, s, w.A, w.V, h->m_max, w.Hc, R,
-                     w.sig_new, w.order, w.st, R, 0);
-  hipLaunchKernelGGL(reorth_transforms_kernel, dim3(1), dim3(1024), 0, s, w.V, h->m_max, w.order,
-                     w.RB, R, w.Hc, w.T2, R, w.GC, w.st);
+  hipLaunchKernelGGL(gram_partial_kernel, dim3(tiles * tiles, 1), dim3(256), 0, s, h->B, R, D, w.st,
+                     w.GC + (size_t)nchunks * R * R, R, D);
+  hipLaunchKernelGGL(reorth_sum_kernel, dim3(128), dim3(256), 0, s, w.GC, nchunks, R, w.Km, w.Pa, w.Pb,
+                     ld, w.st);
+  const int32_t* st = w.st;
+  // Z = Z0 (3I - G_B Z0^2) / 2 = 1.5 Z0 - 0.5 Z0 (G_B Z0 Z0)   (second Newton-Schulz step)
+  iskv_dgemm(s, mm, w.Pa, false, w.Pb, false, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 2);
+  iskv_dgemm(s, mm, w.T, false, w.Pb, false, w.S, nullptr, ld, 1.0, 0.0, 0.0, st, 2);
+  iskv_dgemm(s, mm, w.Pb, false, w.S, false, w.Zb, w.Pb, ld, -0.5, 1.5, 0.0, st, 2);
+  // M_B = G_B Z;  H = M_B G_C M_B^T -> A
+  iskv_dgemm(s, mm, w.Pa, false, w.Zb, false, w.MB, nullptr, ld, 1.0, 0.0, 0.0, st, 2);
+  iskv_dgemm(s, mm, w.MB, false, w.Km, false, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 2);
+  iskv_dgemm(s, mm, w.T, false, w.MB, true, w.A, nullptr, ld, 1.0, 0.0, 0.0, st, 2);
+  iskv_launch_core_eig(h);
+  hipLaunchKernelGGL(eig_finish_kernel, dim3(1), dim3(1024), 0, s, w.S, w.V, mm, w.Hc, R, w.sig_new,
+                     w.order, w.st, R, 0);
+  hipLaunchKernelGGL(permute_cols_kernel, dim3(128), dim3(256), 0, s, w.V, w.order, w.W1, ld, w.st);
+  // T1 = M_B^T Y (coordinates), T2 = Z Y (basis)
+  iskv_dgemm(s, mm, w.MB, true, w.W1, false, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 2);
+  iskv_dgemm(s, mm, w.Zb, false, w.W1, false, w.Pa, nullptr, ld, 1.0, 0.0, 0.0, st, 2);
+  hipLaunchKernelGGL(to_f32_kernel, dim3(128), dim3(256), 0, s, w.T, w.Pa, ld, w.Hc, w.T2, R, w.st);
   {
     size_t smem = (size_t)(32 * R + 32 * 64) * sizeof(float);
     hipLaunchKernelGGL(coord_update_kernel, dim3((n + 31) / 32), dim3(256), smem, s, h->C, R, w.Hc, R,
