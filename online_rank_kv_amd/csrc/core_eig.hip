@@ -264,7 +264,11 @@ __global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W,
     __syncthreads();
     for (int i = t; i < m; i += nt) L.lab[i] = L.lab[L.lab[i]];  // pointer jumping
     __syncthreads();
-    if (!L.changed) break;
+    // every thread reads the flag before thread 0 may reset it for the next
+    // pass, so the loop exit is uniform across the workgroup
+    const int ch = L.changed;
+    __syncthreads();
+    if (!ch) break;
   }
   for (int i = t; i < m; i += nt) atomicAdd(&L.size[L.lab[i]], 1);
   __syncthreads();
