@@ -139,6 +139,16 @@ int isvd_query(isvd_handle* h, int32_t* n, int32_t* k, int32_t* status);
  * [12] refinement steps of the last core solve. Errors: EINVAL, EHIP. */
 int isvd_query_state(isvd_handle* h, int32_t* state, int32_t count);
 
+/* Run the handle's core eigensolver on a caller matrix (the step of
+ * Algorithm 2 that takes the SVD of the core, iS-KV notes §4.2, exposed so it
+ * can be checked on its own): A is device fp64 [m x m], symmetric,
+ * row-major; on return lam (device fp64 [m]) holds its eigenvalues in
+ * descending order and V (device fp64 [m x m], row-major) the matching
+ * orthonormal eigenvectors as columns. m <= r_max + b_max. Uses the handle's
+ * workspace and stream (do not interleave with a merge in flight); leaves
+ * the factors untouched. Errors: EINVAL, EHIP. */
+int isvd_sym_eig(isvd_handle* h, const double* A, int32_t m, double* lam, double* V);
+
 /* Rows folded so far (host-side, no sync). */
 int32_t isvd_rows(const isvd_handle* h);
 

@@ -20,7 +20,7 @@ __all__ = [
     "LIB_PATH", "lib", "IskvError", "IskvConfig", "ISKV_NO_COORD_SYNC", "ISKV_OUT_BF16",
     "ISKV_OUT_FP32", "ISKV_DEV_NONFINITE", "ISKV_DEV_NOCONV", "EXPORTED_SYMBOLS",
     "isvd_workspace_bytes", "isvd_init", "isvd_merge_block", "isvd_reorth", "isvd_query",
-    "isvd_rows", "isvd_destroy", "isvd_query_state", "kv_reconstruct",
+    "isvd_rows", "isvd_destroy", "isvd_query_state", "isvd_sym_eig", "kv_reconstruct",
     "decode_attend_workspace_bytes", "decode_attend", "iskv_window_rows", "iskv_window_init", "iskv_window_protect",
     "iskv_window_append", "iskv_window_exact", "iskv_window_destroy", "iskv_strerror",
     "IsvdPath", "ExactWindow",
@@ -46,7 +46,7 @@ EXPORTED_SYMBOLS = (
     "isvd_rows", "isvd_destroy", "kv_reconstruct", "decode_attend_workspace_bytes",
     "decode_attend", "iskv_window_rows", "iskv_window_init", "iskv_window_protect",
     "iskv_window_append", "iskv_window_exact", "iskv_window_destroy", "iskv_strerror",
-    "isvd_query_state",
+    "isvd_query_state", "isvd_sym_eig",
 )
 
 
@@ -81,6 +81,8 @@ lib.isvd_query.restype = ctypes.c_int
 lib.isvd_query.argtypes = [_vp, _pi32, _pi32, _pi32]
 lib.isvd_query_state.restype = ctypes.c_int
 lib.isvd_query_state.argtypes = [_vp, _pi32, _i32]
+lib.isvd_sym_eig.restype = ctypes.c_int
+lib.isvd_sym_eig.argtypes = [_vp, _vp, _i32, _vp, _vp]
 lib.isvd_rows.restype = _i32
 lib.isvd_rows.argtypes = [_vp]
 lib.isvd_destroy.restype = None
@@ -165,6 +167,10 @@ def isvd_query_state(h: int, count: int = 16):
     arr = (ctypes.c_int32 * count)()
     _check(lib.isvd_query_state(h, arr, count), "isvd_query_state")
     return list(arr)
+
+
+def isvd_sym_eig(h: int, A, m: int, lam, V) -> None:
+    _check(lib.isvd_sym_eig(h, _ptr(A), int(m), _ptr(lam), _ptr(V)), "isvd_sym_eig")
 
 
 def isvd_rows(h: int) -> int:
@@ -262,6 +268,15 @@ class IsvdPath:
 
     def state(self):
         return isvd_query_state(self.h)
+
+    def sym_eig(self, A):
+        """Eigenpairs of a symmetric fp64 device matrix with the core eigensolver."""
+        import torch
+        m = A.shape[0]
+        lam = torch.empty((m,), dtype=torch.float64, device=A.device)
+        V = torch.empty((m, m), dtype=torch.float64, device=A.device)
+        isvd_sym_eig(self.h, A.contiguous(), m, lam, V)
+        return lam, V
 
     @property
     def n(self) -> int:

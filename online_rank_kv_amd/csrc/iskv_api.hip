@@ -174,6 +174,12 @@ int isvd_query(isvd_handle* h, int32_t* n, int32_t* k, int32_t* status) {
 
 void isvd_destroy(isvd_handle* h) { delete h; }
 
+int isvd_sym_eig(isvd_handle* h, const double* A, int32_t m, double* lam, double* V) {
+  if (!h || !A || !lam || !V) return ISKV_EINVAL;
+  if (m < 1 || m > h->m_max) return ISKV_EINVAL;
+  return iskv_launch_sym_eig(h, A, m, lam, V);
+}
+
 int kv_reconstruct(const isvd_handle* h, const float* X_exact, const int32_t* pos_exact,
                    int32_t n_exact, int32_t n_total, int32_t head_dim, int32_t apply_rope,
                    float rope_theta, void* out, int32_t out_dtype, void* stream) {

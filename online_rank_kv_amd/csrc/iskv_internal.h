@@ -101,6 +101,7 @@ void iskv_dgemm(hipStream_t s, int m_max, const double* A, bool ta, const double
                 int mode);
 int iskv_launch_merge(isvd_handle* h, const float* F, const int32_t* pos_F, int32_t b);
 int iskv_launch_reorth(isvd_handle* h);
+int iskv_launch_sym_eig(isvd_handle* h, const double* A, int32_t m, double* lam, double* V);
 int iskv_launch_reconstruct(const isvd_handle* h, const float* X_exact, const int32_t* pos_exact,
                             int32_t n_exact, int32_t n_total, int32_t head_dim, int32_t apply_rope,
                             float rope_theta, void* out, int32_t out_dtype, hipStream_t s);

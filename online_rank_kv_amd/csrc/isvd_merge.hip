@@ -589,8 +589,46 @@ __global__ void reorth_commit_kernel(float* sigma, const float* __restrict__ sig
 
 }  // namespace
 
+// Copy a caller matrix (ld m) into the workspace (ld m_max) and set ST_JM.
+__global__ __launch_bounds__(256) void load_sym_kernel(const double* __restrict__ Ain, int m, double* A,
+                                                       int ld, int32_t* st) {
+  const size_t tot = (size_t)m * m;
+  for (size_t e = blockIdx.x * 256 + threadIdx.x; e < tot; e += (size_t)gridDim.x * 256) {
+    int i = (int)(e / m), j = (int)(e % m);
+    A[(size_t)i * ld + j] = Ain[e];
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) st[ST_JM] = m;
+}
+
+// lam[t] = S[order[t], order[t]], Vout[:, t] = V[:, order[t]] (ld m).
+__global__ __launch_bounds__(256) void store_sym_kernel(const double* __restrict__ S,
+                                                        const double* __restrict__ V, int ld,
+                                                        const int32_t* __restrict__ order, int m,
+                                                        double* lam, double* Vout) {
+  const size_t tot = (size_t)m * m;
+  for (size_t e = blockIdx.x * 256 + threadIdx.x; e < tot; e += (size_t)gridDim.x * 256) {
+    int i = (int)(e / m), t = (int)(e % m);
+    int o = min(max(order[t], 0), m - 1);
+    Vout[e] = V[(size_t)i * ld + o];
+    if (i == 0) lam[t] = S[(size_t)o * ld + o];
+  }
+}
+
 // ============================================================================
 // Host launchers.
+
+int iskv_launch_sym_eig(isvd_handle* h, const double* A, int32_t m, double* lam, double* V) {
+  const isvd_ws& w = h->w;
+  hipStream_t s = h->stream;
+  hipLaunchKernelGGL(load_sym_kernel, dim3(128), dim3(256), 0, s, A, m, w.A, h->m_max, w.st);
+  int rc = iskv_launch_core_eig(h);
+  if (rc) return rc;
+  hipLaunchKernelGGL(eig_finish_kernel, dim3(1), dim3(1024), 0, s, w.S, w.V, h->m_max, w.Hc,
+                     h->cfg.r_max, w.sig_new, w.order, w.st, h->cfg.r_max, 0);
+  hipLaunchKernelGGL(store_sym_kernel, dim3(128), dim3(256), 0, s, w.S, w.V, h->m_max, w.order, m, lam, V);
+  ISKV_HIP_CHECK(hipGetLastError());
+  return ISKV_OK;
+}
 
 // Allow the LDS-staged update kernels to use more than 64 KB of dynamic LDS.
 int iskv_kernel_setup() {
@@ -639,7 +677,10 @@ int iskv_launch_merge(isvd_handle* h, const float* F, const int32_t* pos_F, int3
                        w.A, h->m_max, w.st);
   }
   hipLaunchKernelGGL(set_jm_kernel, dim3(1), dim3(1), 0, s, w.st, (int)ST_M);
-  iskv_launch_core_eig(h);
+  {
+    int rc = iskv_launch_core_eig(h);
+    if (rc) return rc;
+  }
   hipLaunchKernelGGL(eig_finish_kernel, dim3(1), dim3(1024), 0, s, w.A, w.V, h->m_max, w.Hc, R,
                      w.sig_new, w.order, w.st, R, 1);
   // 8. coordinate sync of old rows, new rows, basis update
@@ -696,7 +737,10 @@ int iskv_launch_reorth(isvd_handle* h) {
   iskv_dgemm(s, mm, w.Pa, false, w.Zb, false, w.MB, nullptr, ld, 1.0, 0.0, 0.0, st, 2);
   iskv_dgemm(s, mm, w.MB, false, w.Km, false, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 2);
   iskv_dgemm(s, mm, w.T, false, w.MB, true, w.A, nullptr, ld, 1.0, 0.0, 0.0, st, 2);
-  iskv_launch_core_eig(h);
+  {
+    int rc = iskv_launch_core_eig(h);
+    if (rc) return rc;
+  }
   hipLaunchKernelGGL(eig_finish_kernel, dim3(1), dim3(1024), 0, s, w.S, w.V, mm, w.Hc, R, w.sig_new,
                      w.order, w.st, R, 0);
   hipLaunchKernelGGL(permute_cols_kernel, dim3(128), dim3(256), 0, s, w.V, w.order, w.W1, ld, w.st);
