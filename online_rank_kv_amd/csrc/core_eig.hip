@@ -28,7 +28,7 @@
 
 namespace {
 
-constexpr int PCJ_MAXIT = 10;
+constexpr int PCJ_MAXIT = 8;
 constexpr double PCJ_TOL = 1e-12;
 constexpr double PCJ_OMEGA = 0.1;
 constexpr double PCJ_CLIP = 0.2;
@@ -543,6 +543,11 @@ int iskv_launch_core_eig(isvd_handle* h) {
   const size_t lds = sizeof(AnalyzeLds);
   for (int it = 0; it < PCJ_MAXIT; ++it) {
     if (it > 0) {
+      // Newton-Schulz: W <- 1.5 W - 0.5 W (W^T W) keeps W orthonormal to
+      // O(defect^2), so S is measured in an orthonormal basis
+      dgemm<true, false>(s, mm, cur, cur, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 0);
+      dgemm<false, false>(s, mm, cur, w.T, nxt, cur, ld, -0.5, 1.5, 0.0, st, 1);
+      { double* tmp = cur; cur = nxt; nxt = tmp; }
       dgemm<false, false>(s, mm, w.A, cur, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 0);
       dgemm<true, false>(s, mm, cur, w.T, w.S, nullptr, ld, 1.0, 0.0, 0.0, st, 0);
     }

@@ -681,7 +681,7 @@ int iskv_launch_merge(isvd_handle* h, const float* F, const int32_t* pos_F, int3
     int rc = iskv_launch_core_eig(h);
     if (rc) return rc;
   }
-  hipLaunchKernelGGL(eig_finish_kernel, dim3(1), dim3(1024), 0, s, w.A, w.V, h->m_max, w.Hc, R,
+  hipLaunchKernelGGL(eig_finish_kernel, dim3(1), dim3(1024), 0, s, w.S, w.V, h->m_max, w.Hc, R,
                      w.sig_new, w.order, w.st, R, 1);
   // 8. coordinate sync of old rows, new rows, basis update
   const int n0 = h->n_host;
