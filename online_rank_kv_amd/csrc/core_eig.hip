@@ -28,7 +28,7 @@
 
 namespace {
 
-constexpr int PCJ_MAXIT = 8;
+constexpr int PCJ_MAXIT = 7;
 constexpr double PCJ_TOL = 1e-12;
 constexpr double PCJ_OMEGA = 0.1;
 constexpr double PCJ_CLIP = 0.2;
@@ -42,66 +42,83 @@ constexpr int FLAG_FALLBACK = 2;
 
 // ----------------------------------------------------------------------------
 // C = alpha * opA(A) opB(B) + beta * Cin + gamma * I, all m x m (m from
-// st[ST_JM]), fp64, 16x16 output tiles, 256 threads, one output each.
+// st[ST_JM]), fp64 on the matrix cores: a workgroup of four waves owns a
+// 32 x 32 output tile, each wave a 16 x 16 block accumulated with
+// V_MFMA_F64_16X16X4F64 (A fragment: lane l holds A[l % 16][l / 16]; B
+// fragment: lane l holds B[l / 16][l % 16]; result: lane l, element e holds
+// C[4 (l / 16) + e][l % 16]). Operand tiles of 32 x 16 are staged in LDS.
 // mode 0: skip the launch when (st[ST_PCJ] & FLAG_CONV).
 // mode 1: when converged, copy Cin (the current W) to C instead.
 // mode 2: always run.
+typedef double v4d __attribute__((ext_vector_type(4)));
+
 template <bool TA, bool TB>
-__global__ __launch_bounds__(256) void dgemm16_kernel(const double* __restrict__ A, int lda,
-                                                      const double* __restrict__ B, int ldb,
-                                                      double* C, int ldc, const double* Cin, int ldcin,
-                                                      double alpha, double beta, double gamma,
-                                                      const int32_t* __restrict__ st, int mode) {
+__global__ __launch_bounds__(256) void dgemm_kernel(const double* __restrict__ A, int lda,
+                                                    const double* __restrict__ B, int ldb, double* C,
+                                                    int ldc, const double* Cin, int ldcin,
+                                                    double alpha, double beta, double gamma,
+                                                    const int32_t* __restrict__ st, int mode) {
   const int m = st[ST_JM];
-  const int i0 = blockIdx.y * 16, j0 = blockIdx.x * 16;
+  const int i0 = blockIdx.y * 32, j0 = blockIdx.x * 32;
   if (i0 >= m || j0 >= m) return;
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  const int i = i0 + ty, j = j0 + tx;
   const bool conv = (st[ST_PCJ] & FLAG_CONV) != 0;
   if (mode == 0 && conv) return;
+  const int t = threadIdx.x;
   if (mode == 1 && conv) {
-    if (i < m && j < m) C[(size_t)i * ldc + j] = Cin[(size_t)i * ldcin + j];
+    for (int e = t; e < 1024; e += 256) {
+      int i = i0 + (e >> 5), j = j0 + (e & 31);
+      if (i < m && j < m) C[(size_t)i * ldc + j] = Cin[(size_t)i * ldcin + j];
+    }
     return;
   }
-  __shared__ double As[32][17];
-  __shared__ double Bs[32][17];
-  double acc = 0.0;
-  for (int k0 = 0; k0 < m; k0 += 32) {
-    // coalesced loads: along i for A^T / along k for A, along j for B / along k for B^T
-    for (int e = threadIdx.x; e < 512; e += 256) {
-      int kk, rr;
-      if (TA) { kk = e >> 4; rr = e & 15; } else { rr = e >> 5; kk = e & 31; }
-      int kg = k0 + kk, ia = i0 + rr;
+  __shared__ double As[32][17];  // [row][k]
+  __shared__ double Bs[16][33];  // [k][col]
+  const int lane = t & 63, wave = t >> 6;
+  const int wi = (wave >> 1) * 16, wj = (wave & 1) * 16;
+  v4d acc = {0.0, 0.0, 0.0, 0.0};
+  for (int k0 = 0; k0 < m; k0 += 16) {
+    for (int e = t; e < 512; e += 256) {
+      int r, k;
+      if (TA) { k = e >> 5; r = e & 31; } else { r = e >> 4; k = e & 15; }
+      int ig = i0 + r, kg = k0 + k;
       double a = 0.0;
-      if (kg < m && ia < m) a = TA ? A[(size_t)kg * lda + ia] : A[(size_t)ia * lda + kg];
-      As[kk][rr] = a;
+      if (ig < m && kg < m) a = TA ? A[(size_t)kg * lda + ig] : A[(size_t)ig * lda + kg];
+      As[r][k] = a;
     }
-    for (int e = threadIdx.x; e < 512; e += 256) {
-      int kk, rr;
-      if (!TB) { kk = e >> 4; rr = e & 15; } else { rr = e >> 5; kk = e & 31; }
-      int kg = k0 + kk, jb = j0 + rr;
+    for (int e = t; e < 512; e += 256) {
+      int c, k;
+      if (!TB) { k = e >> 5; c = e & 31; } else { c = e >> 4; k = e & 15; }
+      int jg = j0 + c, kg = k0 + k;
       double b = 0.0;
-      if (kg < m && jb < m) b = TB ? B[(size_t)jb * ldb + kg] : B[(size_t)kg * ldb + jb];
-      Bs[kk][rr] = b;
+      if (jg < m && kg < m) b = TB ? B[(size_t)jg * ldb + kg] : B[(size_t)kg * ldb + jg];
+      Bs[k][c] = b;
     }
     __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < 32; ++kk) acc = fma(As[kk][ty], Bs[kk][tx], acc);
+#pragma unroll
+    for (int kk = 0; kk < 16; kk += 4) {
+      double a = As[wi + (lane & 15)][kk + (lane >> 4)];
+      double b = Bs[kk + (lane >> 4)][wj + (lane & 15)];
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc, 0, 0, 0);
+    }
     __syncthreads();
   }
-  if (i < m && j < m) {
-    double o = alpha * acc;
-    if (beta != 0.0) o += beta * Cin[(size_t)i * ldcin + j];
-    if (i == j) o += gamma;
-    C[(size_t)i * ldc + j] = o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    int i = i0 + wi + 4 * (lane >> 4) + e, j = j0 + wj + (lane & 15);
+    if (i < m && j < m) {
+      double o = alpha * acc[e];
+      if (beta != 0.0) o += beta * Cin[(size_t)i * ldcin + j];
+      if (i == j) o += gamma;
+      C[(size_t)i * ldc + j] = o;
+    }
   }
 }
 
 template <bool TA, bool TB>
 void dgemm(hipStream_t s, int m_max, const double* A, const double* B, double* C, const double* Cin,
            int ld, double alpha, double beta, double gamma, const int32_t* st, int mode) {
-  dim3 grid((m_max + 15) / 16, (m_max + 15) / 16);
-  hipLaunchKernelGGL((dgemm16_kernel<TA, TB>), grid, dim3(256), 0, s, A, ld, B, ld, C, ld, Cin, ld,
+  dim3 grid((m_max + 31) / 32, (m_max + 31) / 32);
+  hipLaunchKernelGGL((dgemm_kernel<TA, TB>), grid, dim3(256), 0, s, A, ld, B, ld, C, ld, Cin, ld,
                      alpha, beta, gamma, st, mode);
 }
 
@@ -115,7 +132,7 @@ __global__ __launch_bounds__(256) void pcj_init_kernel(const double* __restrict_
     S[(size_t)i * ld + j] = A[(size_t)i * ld + j];
     W[(size_t)i * ld + j] = (i == j) ? 1.0 : 0.0;
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) { st[ST_PCJ] = 0; st[ST_PCJIT] = 0; }
+  if (blockIdx.x == 0 && threadIdx.x == 0) { st[ST_PCJ] = 0; st[ST_PCJIT] = 0; st[ST_NEDGE] = 0; }
 }
 
 __device__ __forceinline__ double coupling(double sij, double di, double dj) {
@@ -164,95 +181,119 @@ __device__ void jacobi_serial(double* S, double* V, int c) {
   }
 }
 
+// Strong pairs and per-block maxima of the scaled coupling, many workgroups.
+// Block b scans rows [16 b, 16 b + 16) against every column j > i. Strong
+// pairs are appended to a global list (order fixed later by sorting).
+// aux layout: [0, 256) doubles = block maxima, then EMAX int pairs.
+__global__ __launch_bounds__(256) void pcj_detect_kernel(const double* __restrict__ S, int ld,
+                                                         double* aux, int32_t* st) {
+  if (st[ST_PCJ] & FLAG_CONV) return;
+  const int m = st[ST_JM];
+  const int r0 = blockIdx.x * 16;
+  __shared__ double red[4];
+  double cmax = 0.0;
+  if (r0 < m) {
+    int* edges = (int*)(aux + 256);
+    const int rows = min(16, m - r0);
+    for (int e = threadIdx.x; e < rows * m; e += 256) {
+      int i = r0 + e / m, j = e % m;
+      if (j <= i) continue;
+      double sij = S[(size_t)i * ld + j];
+      double di = S[(size_t)i * ld + i], dj = S[(size_t)j * ld + j];
+      double c = coupling(sij, di, dj);
+      if (c > cmax) cmax = c;
+      if (c > PCJ_TOL && fabs(sij) > PCJ_OMEGA * fabs(dj - di)) {
+        int slot = atomicAdd(&st[ST_NEDGE], 1);
+        if (slot < EMAX) { edges[2 * slot] = i; edges[2 * slot + 1] = j; }
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) cmax = fmax(cmax, __shfl_xor(cmax, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = cmax;
+  __syncthreads();
+  if (threadIdx.x == 0 && blockIdx.x < 256)
+    aux[blockIdx.x] = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+}
+
 struct AnalyzeLds {
   double d[1024];
-  double red[32];
   double cmat[NCL_MAX][CMAX_S * CMAX_S];
   double vmat[NCL_MAX][CMAX_S * CMAX_S];
   double pc[NPAIR_MAX], ps[NPAIR_MAX];
+  int key[EMAX];
   int lab[1024];
   int size[1024];
   int cid[1024];
-  int cnt[1024];
-  short ei[EMAX], ej[EMAX];
   int members[NCL_MAX][CMAX_S];
   int ccount[NCL_MAX];
   int pi[NPAIR_MAX], pj[NPAIR_MAX];
   unsigned char used[1024];
+  double cmax;
   int nedge, ncl, npair, changed, anybig;
 };
 
-// One refinement step (see the file header), one workgroup of 1024 threads.
-// S (m x m, global) is overwritten; W gets the cluster rotations in place;
-// Km receives K and Pa = I + K/4.
-__global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W, int ld, double* Km,
-                                                           double* Pa, int32_t* st, int it) {
+// The serial part of one refinement step, one workgroup of 1024 threads:
+// convergence test, clusters of strongly coupled indices (components of the
+// strong-pair graph), exact rotations (small clusters: cyclic Jacobi; big
+// ones: 2x2 rotations on a greedy matching), applied to S and W in place.
+__global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W, int ld,
+                                                           const double* __restrict__ aux,
+                                                           int32_t* st, int it) {
   extern __shared__ unsigned char smem_raw[];
   AnalyzeLds& L = *reinterpret_cast<AnalyzeLds*>(smem_raw);
+  if (st[ST_PCJ] & FLAG_CONV) return;
   const int m = st[ST_JM];
   const int t = threadIdx.x, nt = blockDim.x;
-  if (st[ST_PCJ] & FLAG_CONV) return;
-  for (int i = t; i < m; i += nt) L.d[i] = S[(size_t)i * ld + i];
-  if (t < 32) L.red[t] = 0.0;
-  __syncthreads();
-  // 1. largest scaled coupling; strong pair count per thread
-  double cmax = 0.0;
-  int nstrong = 0;
-  const size_t tot = (size_t)m * m;
-  for (size_t e = t; e < tot; e += nt) {
-    int i = (int)(e / m), j = (int)(e % m);
-    if (j <= i) continue;
-    double sij = S[(size_t)i * ld + j];
-    double c = coupling(sij, L.d[i], L.d[j]);
-    if (c > cmax) cmax = c;
-    if (c > PCJ_TOL && fabs(sij) > PCJ_OMEGA * fabs(L.d[j] - L.d[i])) ++nstrong;
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) cmax = fmax(cmax, __shfl_xor(cmax, o, 64));
-  if ((t & 63) == 0) L.red[t >> 6] = cmax;
-  L.cnt[t] = nstrong;
-  __syncthreads();
-  if (t == 0) {
+  const int nblk = (m + 15) / 16;
+  if (t < 64) {
     double c = 0.0;
-    for (int w = 0; w < (nt >> 6); ++w) c = fmax(c, L.red[w]);
-    L.red[16] = c;
-    // exclusive scan of per-thread strong counts (deterministic edge order)
-    int run = 0;
-    for (int w = 0; w < nt; ++w) { int v = L.cnt[w]; L.cnt[w] = run; run += v; }
-    L.nedge = run < EMAX ? run : EMAX;
-    L.ncl = 0; L.npair = 0; L.anybig = 0;
+    for (int b = t; b < nblk && b < 256; b += 64) c = fmax(c, aux[b]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) c = fmax(c, __shfl_xor(c, o, 64));
+    if (t == 0) {
+      L.cmax = c;
+      int ne = st[ST_NEDGE];
+      L.nedge = ne < EMAX ? ne : EMAX;
+      L.ncl = 0; L.npair = 0; L.anybig = 0;
+    }
   }
+  for (int i = t; i < m; i += nt) L.d[i] = S[(size_t)i * ld + i];
   __syncthreads();
-  if (!(L.red[16] >= PCJ_TOL)) {
-    // converged (a NaN coupling never counts as converged: it falls back)
-    if (L.red[16] < PCJ_TOL) {
-      if (t == 0) { st[ST_PCJ] |= FLAG_CONV; st[ST_PCJIT] = it; }
-      return;
-    }
+  const double cmax = L.cmax;
+  if (cmax < PCJ_TOL) {  // NaN couplings never pass: they end in the fallback
+    __syncthreads();
+    if (t == 0) { st[ST_PCJ] |= FLAG_CONV; st[ST_PCJIT] = it; st[ST_NEDGE] = 0; }
+    return;
   }
-  // 2. strong pairs, in scan order
-  {
-    int off = L.cnt[t];
-    for (size_t e = t; e < tot; e += nt) {
-      int i = (int)(e / m), j = (int)(e % m);
-      if (j <= i) continue;
-      double sij = S[(size_t)i * ld + j];
-      double c = coupling(sij, L.d[i], L.d[j]);
-      if (c > PCJ_TOL && fabs(sij) > PCJ_OMEGA * fabs(L.d[j] - L.d[i])) {
-        if (off < EMAX) { L.ei[off] = (short)i; L.ej[off] = (short)j; }
-        ++off;
-      }
-    }
-  }
+  const int ne = L.nedge;
+  // sorted edge keys i * 1024 + j: a deterministic order for the matching
+  const int* edges = (const int*)(aux + 256);
+  int npow = 1;
+  while (npow < ne) npow <<= 1;
+  for (int e = t; e < npow; e += nt)
+    L.key[e] = e < ne ? edges[2 * e] * 1024 + edges[2 * e + 1] : 0x7fffffff;
   for (int i = t; i < m; i += nt) { L.lab[i] = i; L.size[i] = 0; L.used[i] = 0; L.cid[i] = -1; }
   __syncthreads();
-  const int ne = L.nedge;
-  // 3. connected components by min-label propagation
+  for (int k = 2; k <= npow; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int e = t; e < npow; e += nt) {
+        int p = e ^ j;
+        if (p > e) {
+          int a = L.key[e], b = L.key[p];
+          bool up = (e & k) == 0;
+          if ((a > b) == up) { L.key[e] = b; L.key[p] = a; }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // connected components by min-label propagation
   for (int guard = 0; guard < 1024; ++guard) {
     if (t == 0) L.changed = 0;
     __syncthreads();
     for (int e = t; e < ne; e += nt) {
-      int a = L.ei[e], b = L.ej[e];
+      int a = L.key[e] >> 10, b = L.key[e] & 1023;
       int la = L.lab[a], lb = L.lab[b];
       if (la != lb) {
         int l = la < lb ? la : lb;
@@ -272,8 +313,8 @@ __global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W,
   }
   for (int i = t; i < m; i += nt) atomicAdd(&L.size[L.lab[i]], 1);
   __syncthreads();
-  // 4. small clusters (2..CMAX_S) get ids in root order; the rest are "big"
   if (t == 0) {
+    // small clusters (2..CMAX_S) get ids in root order; the rest are "big"
     int n = 0;
     for (int i = 0; i < m; ++i) {
       if (L.lab[i] == i && L.size[i] >= 2) {
@@ -282,20 +323,15 @@ __global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W,
       }
     }
     L.ncl = n;
-  }
-  __syncthreads();
-  if (t == 0) {
-    // members in index order (deterministic)
-    for (int i = 0; i < m; ++i) {
+    for (int i = 0; i < m; ++i) {  // members in index order
       int c = L.cid[L.lab[i]];
-      if (c >= 0 && L.size[L.lab[i]] >= 2) L.members[c][L.ccount[c]++] = i;
+      if (c >= 0) L.members[c][L.ccount[c]++] = i;
     }
-    // greedy matching on strong pairs inside big components
-    int np = 0;
+    int np = 0;  // greedy matching on strong pairs inside big components
     if (L.anybig) {
       for (int e = 0; e < ne && np < NPAIR_MAX; ++e) {
-        int a = L.ei[e], b = L.ej[e];
-        if (L.cid[L.lab[a]] >= 0) continue;  // in a small cluster
+        int a = L.key[e] >> 10, b = L.key[e] & 1023;
+        if (L.cid[L.lab[a]] >= 0) continue;
         if (L.used[a] || L.used[b]) continue;
         L.used[a] = 1; L.used[b] = 1;
         L.pi[np] = a; L.pj[np] = b;
@@ -303,16 +339,15 @@ __global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W,
       }
     }
     L.npair = np;
+    st[ST_NEDGE] = 0;  // the next detect pass starts a new list
   }
   __syncthreads();
   const int ncl = L.ncl, npair = L.npair;
-  // 5. exact solves: one thread per small cluster, one per matched pair
   if (t < ncl) {
     const int c = L.ccount[t];
     double* Sc = L.cmat[t];
     for (int a = 0; a < c; ++a)
-      for (int b = 0; b < c; ++b)
-        Sc[a * c + b] = S[(size_t)L.members[t][a] * ld + L.members[t][b]];
+      for (int b = 0; b < c; ++b) Sc[a * c + b] = S[(size_t)L.members[t][a] * ld + L.members[t][b]];
     jacobi_serial(Sc, L.vmat[t], c);
   }
   for (int q = t; q < npair; q += nt) {
@@ -323,7 +358,7 @@ __global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W,
     L.pc[q] = cs; L.ps[q] = sn;
   }
   __syncthreads();
-  // 6. rows of S: S[C, :] <- R_C^T S[C, :]
+  // rows of S: S[C, :] <- R_C^T S[C, :]
   for (int e = t; e < ncl * m; e += nt) {
     int g = e / m, j = e % m;
     int c = L.ccount[g];
@@ -345,7 +380,7 @@ __global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W,
     S[(size_t)b * ld + j] = sn * xa + cs * xb;
   }
   __syncthreads();
-  // 7. columns of S and of W: X[:, C] <- X[:, C] R_C
+  // columns of S and of W: X[:, C] <- X[:, C] R_C
   for (int e = t; e < ncl * m; e += nt) {
     int g = e / m, i = e % m;
     int c = L.ccount[g];
@@ -375,28 +410,32 @@ __global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W,
     W[(size_t)i * ld + a] = cs * wa - sn * wb;
     W[(size_t)i * ld + b] = sn * wa + cs * wb;
   }
-  __syncthreads();
-  for (int i = t; i < m; i += nt) L.d[i] = S[(size_t)i * ld + i];
-  __syncthreads();
-  // 8. first-order angles for every other pair; K antisymmetric
-  for (size_t e = t; e < tot; e += nt) {
+  if (t == 0) st[ST_PCJIT] = it + 1;
+}
+
+// First-order angles for every pair that is not strongly coupled, from the
+// rotated S: K_ij = s_ij / (s_jj - s_ii), K antisymmetric, clipped; writes
+// Km = K and Pa = I + K/2 (X = I + K (I + K/2) is formed by one GEMM).
+// Grid-stride over m x m, many workgroups.
+__global__ __launch_bounds__(256) void pcj_kmat_kernel(const double* __restrict__ S, int ld, double* Km,
+                                                       double* Pa, const int32_t* __restrict__ st) {
+  if (st[ST_PCJ] & FLAG_CONV) return;
+  const int m = st[ST_JM];
+  const size_t tot = (size_t)m * m;
+  for (size_t e = blockIdx.x * 256 + threadIdx.x; e < tot; e += (size_t)gridDim.x * 256) {
     int i = (int)(e / m), j = (int)(e % m);
     double k = 0.0;
-    if (i < j) {
-      double sij = S[(size_t)i * ld + j];
-      double den = L.d[j] - L.d[i];
-      if (den != 0.0 && fabs(sij) <= PCJ_OMEGA * fabs(den)) k = fmin(fmax(sij / den, -PCJ_CLIP), PCJ_CLIP);
+    if (i != j) {
+      int lo = i < j ? i : j, hi = i < j ? j : i;
+      double slh = S[(size_t)lo * ld + hi];
+      double den = S[(size_t)hi * ld + hi] - S[(size_t)lo * ld + lo];
+      if (den != 0.0 && fabs(slh) <= PCJ_OMEGA * fabs(den)) k = fmin(fmax(slh / den, -PCJ_CLIP), PCJ_CLIP);
       if (!isfinite(k)) k = 0.0;
-    } else if (i > j) {
-      double sji = S[(size_t)j * ld + i];
-      double den = L.d[i] - L.d[j];
-      if (den != 0.0 && fabs(sji) <= PCJ_OMEGA * fabs(den)) k = -fmin(fmax(sji / den, -PCJ_CLIP), PCJ_CLIP);
-      if (!isfinite(k)) k = 0.0;
+      if (i > j) k = -k;
     }
     Km[(size_t)i * ld + j] = k;
-    Pa[(size_t)i * ld + j] = (i == j ? 1.0 : 0.0) + 0.25 * k;
+    Pa[(size_t)i * ld + j] = (i == j ? 1.0 : 0.0) + 0.5 * k;
   }
-  if (t == 0) st[ST_PCJIT] = it + 1;
 }
 
 // Eigenvalues lambda_i = w_i^T (A w_i) from T = A W; V = W when converged,
@@ -537,11 +576,12 @@ int iskv_launch_core_eig(isvd_handle* h) {
   hipStream_t s = h->stream;
   const int mm = h->m_max, ld = h->m_max;
   int32_t* st = w.st;
+  const int nblk = (mm + 15) / 16;
   hipLaunchKernelGGL(pcj_init_kernel, dim3(128), dim3(256), 0, s, w.A, w.S, w.W0, ld, st);
   double* cur = w.W0;
   double* nxt = w.W1;
   const size_t lds = sizeof(AnalyzeLds);
-  for (int it = 0; it < PCJ_MAXIT; ++it) {
+  for (int it = 0; it <= PCJ_MAXIT; ++it) {
     if (it > 0) {
       // Newton-Schulz: W <- 1.5 W - 0.5 W (W^T W) keeps W orthonormal to
       // O(defect^2), so S is measured in an orthonormal basis
@@ -551,20 +591,16 @@ int iskv_launch_core_eig(isvd_handle* h) {
       dgemm<false, false>(s, mm, w.A, cur, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 0);
       dgemm<true, false>(s, mm, cur, w.T, w.S, nullptr, ld, 1.0, 0.0, 0.0, st, 0);
     }
-    hipLaunchKernelGGL(pcj_analyze_kernel, dim3(1), dim3(1024), lds, s, w.S, cur, ld, w.Km, w.Pa, st, it);
-    // exp(K) = I + K (I + K/2 (I + K/3 (I + K/4)))
-    dgemm<false, false>(s, mm, w.Km, w.Pa, w.Pb, nullptr, ld, 1.0 / 3.0, 0.0, 1.0, st, 0);
-    dgemm<false, false>(s, mm, w.Km, w.Pb, w.Pa, nullptr, ld, 0.5, 0.0, 1.0, st, 0);
+    hipLaunchKernelGGL(pcj_detect_kernel, dim3(nblk), dim3(256), 0, s, w.S, ld, w.aux, st);
+    hipLaunchKernelGGL(pcj_analyze_kernel, dim3(1), dim3(1024), lds, s, w.S, cur, ld, w.aux, st, it);
+    if (it == PCJ_MAXIT) break;  // last pass only tests convergence
+    hipLaunchKernelGGL(pcj_kmat_kernel, dim3(128), dim3(256), 0, s, w.S, ld, w.Km, w.Pa, st);
+    // X = I + K (I + K/2); W <- W X
     dgemm<false, false>(s, mm, w.Km, w.Pa, w.Pb, nullptr, ld, 1.0, 0.0, 1.0, st, 0);
     dgemm<false, false>(s, mm, cur, w.Pb, nxt, cur, ld, 1.0, 0.0, 0.0, st, 1);
-    double* tmp = cur; cur = nxt; nxt = tmp;
+    { double* tmp = cur; cur = nxt; nxt = tmp; }
   }
-  // one step past the last iteration so a convergence reached there is seen
-  dgemm<false, false>(s, mm, w.A, cur, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 0);
-  dgemm<true, false>(s, mm, cur, w.T, w.S, nullptr, ld, 1.0, 0.0, 0.0, st, 0);
-  hipLaunchKernelGGL(pcj_analyze_kernel, dim3(1), dim3(1024), lds, s, w.S, cur, ld, w.Km, w.Pa, st,
-                     PCJ_MAXIT);
-  // Newton-Schulz: W <- 1.5 W - 0.5 W (W^T W); then T = A W for the eigenvalues
+  // final Newton-Schulz, then T = A W for the eigenvalues
   dgemm<true, false>(s, mm, cur, cur, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 2);
   dgemm<false, false>(s, mm, cur, w.T, nxt, cur, ld, -0.5, 1.5, 0.0, st, 2);
   dgemm<false, false>(s, mm, w.A, nxt, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 2);

@@ -23,6 +23,7 @@ enum {
   ST_ROUNDS = 10,  // reserved
   ST_PCJ = 11,     // core eigensolver flags: 1 converged, 2 Jacobi fallback used
   ST_PCJIT = 12,   // refinement steps used by the last core eigensolve
+  ST_NEDGE = 13,   // strong pairs found by the current detection pass
   ST_COUNT = 16
 };
 
@@ -49,6 +50,7 @@ struct isvd_ws {
   double* Pb;         // [m_max x m_max]
   double* MB;         // [m_max x m_max]  reorth: (B^T B)^(1/2)
   double* Zb;         // [m_max x m_max]  reorth: (B^T B)^(-1/2)
+  double* aux;        // [256 doubles + 4096 int pairs] detection results
   double* lam;        // [m_max]
   double* rot;        // [rot_cap] Jacobi rotation log (c, s) pairs
   float* Hc;          // [m_max x r_max]  kept right singular vectors of the core
