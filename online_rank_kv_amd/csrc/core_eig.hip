@@ -46,7 +46,8 @@ constexpr int FLAG_FALLBACK = 2;
 // 32 x 32 output tile, each wave a 16 x 16 block accumulated with
 // V_MFMA_F64_16X16X4F64 (A fragment: lane l holds A[l % 16][l / 16]; B
 // fragment: lane l holds B[l / 16][l % 16]; result: lane l, element e holds
-// C[4 (l / 16) + e][l % 16]). Operand tiles of 32 x 16 are staged in LDS.
+// C[l / 16 + 4 e][l % 16], as measured on gfx950). Operand tiles of 32 x 16
+// are staged in LDS.
 // mode 0: skip the launch when (st[ST_PCJ] & FLAG_CONV).
 // mode 1: when converged, copy Cin (the current W) to C instead.
 // mode 2: always run.
@@ -104,7 +105,7 @@ __global__ __launch_bounds__(256) void dgemm_kernel(const double* __restrict__ A
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    int i = i0 + wi + 4 * (lane >> 4) + e, j = j0 + wj + (lane & 15);
+    int i = i0 + wi + (lane >> 4) + 4 * e, j = j0 + wj + (lane & 15);
     if (i < m && j < m) {
       double o = alpha * acc[e];
       if (beta != 0.0) o += beta * Cin[(size_t)i * ldcin + j];
