@@ -72,31 +72,31 @@ __global__ __launch_bounds__(256) void dgemm_kernel(const double* __restrict__ A
     }
     return;
   }
-  __shared__ double As[32][17];  // [row][k]
-  __shared__ double Bs[16][33];  // [k][col]
+  __shared__ double As[32][65];  // [row][k]
+  __shared__ double Bs[64][33];  // [k][col]
   const int lane = t & 63, wave = t >> 6;
   const int wi = (wave >> 1) * 16, wj = (wave & 1) * 16;
   v4d acc = {0.0, 0.0, 0.0, 0.0};
-  for (int k0 = 0; k0 < m; k0 += 16) {
-    for (int e = t; e < 512; e += 256) {
+  for (int k0 = 0; k0 < m; k0 += 64) {
+    for (int e = t; e < 2048; e += 256) {
       int r, k;
-      if (TA) { k = e >> 5; r = e & 31; } else { r = e >> 4; k = e & 15; }
+      if (TA) { k = e >> 5; r = e & 31; } else { r = e >> 6; k = e & 63; }
       int ig = i0 + r, kg = k0 + k;
       double a = 0.0;
       if (ig < m && kg < m) a = TA ? A[(size_t)kg * lda + ig] : A[(size_t)ig * lda + kg];
       As[r][k] = a;
     }
-    for (int e = t; e < 512; e += 256) {
+    for (int e = t; e < 2048; e += 256) {
       int c, k;
-      if (!TB) { k = e >> 5; c = e & 31; } else { c = e >> 4; k = e & 15; }
+      if (!TB) { k = e >> 5; c = e & 31; } else { c = e >> 6; k = e & 63; }
       int jg = j0 + c, kg = k0 + k;
       double b = 0.0;
       if (jg < m && kg < m) b = TB ? B[(size_t)jg * ldb + kg] : B[(size_t)kg * ldb + jg];
       Bs[k][c] = b;
     }
     __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 16; kk += 4) {
+    const int kl = min(64, m - k0);
+    for (int kk = 0; kk < kl; kk += 4) {
       double a = As[wi + (lane & 15)][kk + (lane >> 4)];
       double b = Bs[kk + (lane >> 4)][wj + (lane & 15)];
       acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc, 0, 0, 0);
@@ -153,12 +153,12 @@ __device__ __forceinline__ void rot2(double app, double aqq, double apq, double*
 // Serial cyclic Jacobi on a c x c block (c <= CMAX_S) held in LDS by one thread.
 __device__ void jacobi_serial(double* S, double* V, int c) {
   for (int i = 0; i < c * c; ++i) V[i] = (i / c == i % c) ? 1.0 : 0.0;
-  for (int sweep = 0; sweep < 30; ++sweep) {
+  for (int sweep = 0; sweep < 20; ++sweep) {
     int rot = 0;
     for (int p = 0; p < c - 1; ++p)
       for (int q = p + 1; q < c; ++q) {
         double apq = S[p * c + q];
-        if (apq == 0.0 || !(fabs(apq) > 1e-15 * sqrt(fabs(S[p * c + p] * S[q * c + q])))) continue;
+        if (apq == 0.0 || !(fabs(apq) > 1e-14 * sqrt(fabs(S[p * c + p] * S[q * c + q])))) continue;
         double cs, sn;
         rot2(S[p * c + p], S[q * c + q], apq, &cs, &sn);
         ++rot;

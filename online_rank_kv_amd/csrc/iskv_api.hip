@@ -60,6 +60,7 @@ size_t carve(const iskv_config* c, char* base, isvd_ws* w) {
   x.MB = (double*)take(M * M * 8);
   x.Zb = (double*)take(M * M * 8);
   x.aux = (double*)take(256 * 8 + 4096 * 8);
+  x.part = (float*)take((size_t)16 * Bm * (D > R ? D : R) * 4);
   x.lam = (double*)take(M * 8);
   x.rot_cap = 0;
   x.rot = nullptr;

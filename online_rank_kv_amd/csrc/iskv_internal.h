@@ -51,6 +51,7 @@ struct isvd_ws {
   double* MB;         // [m_max x m_max]  reorth: (B^T B)^(1/2)
   double* Zb;         // [m_max x m_max]  reorth: (B^T B)^(-1/2)
   double* aux;        // [256 doubles + 4096 int pairs] detection results
+  float* part;        // [16 x b_max x max(D, r_max)] split-K partial sums
   double* lam;        // [m_max]
   double* rot;        // [rot_cap] Jacobi rotation log (c, s) pairs
   float* Hc;          // [m_max x r_max]  kept right singular vectors of the core
@@ -92,7 +93,7 @@ struct iskv_window {
 };
 
 #define ISKV_JACOBI_MAX_SWEEPS 40
-#define ISKV_RESID_MAX_SWEEPS 60
+#define ISKV_RESID_MAX_SWEEPS 30
 
 // ---- launch helpers implemented in the kernel translation units ----
 int iskv_kernel_setup();

@@ -124,6 +124,70 @@ static void sgemm(hipStream_t s, int Mmax, int Nmax, const float* A, int lda, co
 }
 
 // ----------------------------------------------------------------------------
+// Skinny products of the merge (M = b rows): partial sums over K chunks on
+// many workgroups, then a deterministic reduction (no float atomics).
+//   part[s][i][j] = sum_{k in chunk s} X[i, k] Y(k, j),  Y(k, j) = TY ? Y[j, k] : Y[k, j]
+// Grid (ceil(Nmax / 32), nsplit, ceil(M / 32)); 256 threads, 2 x 2 outputs each.
+template <bool TY>
+__global__ __launch_bounds__(256) void skinny_partial_kernel(const float* __restrict__ X, int ldx,
+                                                             const float* __restrict__ Y, int ldy,
+                                                             float* part, int ldp, int M, Dim Nd,
+                                                             Dim Kd, int kchunk) {
+  const int N = dval(Nd), K = dval(Kd);
+  const int j0 = blockIdx.x * 32, i0 = blockIdx.z * 32, s = blockIdx.y;
+  if (j0 >= N) return;
+  const int kb = s * kchunk, ke = min(K, kb + kchunk);
+  __shared__ float Xs[32][65];
+  __shared__ float Ys[64][33];
+  const int t = threadIdx.x, tx = t & 15, ty = t >> 4;
+  float acc[2][2] = {};
+  for (int k0 = kb; k0 < ke; k0 += 64) {
+    for (int e = t; e < 2048; e += 256) {
+      int r = e >> 6, c = e & 63;
+      Xs[r][c] = (i0 + r < M && k0 + c < ke) ? X[(size_t)(i0 + r) * ldx + k0 + c] : 0.f;
+    }
+    for (int e = t; e < 2048; e += 256) {
+      int k, c;
+      if (TY) { c = e >> 6; k = e & 63; } else { k = e >> 5; c = e & 31; }
+      float v = 0.f;
+      if (j0 + c < N && k0 + k < ke) v = TY ? Y[(size_t)(j0 + c) * ldy + k0 + k] : Y[(size_t)(k0 + k) * ldy + j0 + c];
+      Ys[k][c] = v;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int kk = 0; kk < 64; ++kk) {
+      float a0 = Xs[ty * 2][kk], a1 = Xs[ty * 2 + 1][kk];
+      float b0 = Ys[kk][tx * 2], b1 = Ys[kk][tx * 2 + 1];
+      acc[0][0] = fmaf(a0, b0, acc[0][0]); acc[0][1] = fmaf(a0, b1, acc[0][1]);
+      acc[1][0] = fmaf(a1, b0, acc[1][0]); acc[1][1] = fmaf(a1, b1, acc[1][1]);
+    }
+    __syncthreads();
+  }
+  for (int u = 0; u < 2; ++u)
+    for (int v = 0; v < 2; ++v) {
+      int i = i0 + ty * 2 + u, j = j0 + tx * 2 + v;
+      if (i < M && j < N) part[((size_t)s * M + i) * ldp + j] = acc[u][v];
+    }
+}
+
+// out[i, j] = alpha * sum_s part[s][i][j] + beta * Z[i, j]   (Z may alias out)
+__global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restrict__ part, int nsplit,
+                                                            int ldp, int M, Dim Nd, float alpha,
+                                                            float beta, const float* Z, int ldz,
+                                                            float* out, int ldo) {
+  const int N = dval(Nd);
+  const int tot = M * N;
+  for (int e = blockIdx.x * 256 + threadIdx.x; e < tot; e += gridDim.x * 256) {
+    int i = e / N, j = e % N;
+    float acc = 0.f;
+    for (int s = 0; s < nsplit; ++s) acc += part[((size_t)s * M + i) * ldp + j];
+    float o = alpha * acc;
+    if (beta != 0.f) o += beta * Z[(size_t)i * ldz + j];
+    out[(size_t)i * ldo + j] = o;
+  }
+}
+
+// ----------------------------------------------------------------------------
 // Residual Gram E E^T in fp64 (b x b), one workgroup per row i. Also latches
 // the non-finite flag when the block (hence E) holds NaN or Inf.
 __global__ __launch_bounds__(256) void resid_gram_kernel(const float* __restrict__ E, int D,
@@ -256,7 +320,7 @@ __global__ __launch_bounds__(256) void resid_basis_kernel(const double* __restri
     if (t == 0) { st[ST_P] = 0; st[ST_M] = k; st[ST_EZERO] = any_nonzero ? 0 : 1; }
     return;
   }
-  jacobi_lds(S, V, b, ld, 1e-15, ISKV_RESID_MAX_SWEEPS, cs, sn, pp, qq, active);
+  jacobi_lds(S, V, b, ld, 1e-13, ISKV_RESID_MAX_SWEEPS, cs, sn, pp, qq, active);
   for (int i = t; i < b; i += blockDim.x) lam[i] = S[i * ld + i];
   __syncthreads();
   // rank by descending eigenvalue, ties by index
@@ -291,19 +355,19 @@ __global__ __launch_bounds__(256) void resid_basis_kernel(const double* __restri
   }
 }
 
-// P[:, j] = E^T V_E[:, j] / rho_j for j < p (D x b_max, fp64 accumulation).
+// P[:, j] = E^T V_E[:, j] / rho_j for j < p (D x b_max, fp64 accumulation);
+// one thread per (d, j).
 __global__ __launch_bounds__(256) void make_p_kernel(const float* __restrict__ E, int D, int b,
                                                      const double* __restrict__ VE,
                                                      const double* __restrict__ rho, float* P,
                                                      int ldp, const int32_t* st) {
   const int p = st[ST_P];
-  const int d = blockIdx.x * blockDim.x + threadIdx.x;
-  if (d >= D) return;
-  for (int j = 0; j < p; ++j) {
-    double acc = 0.0;
-    for (int i = 0; i < b; ++i) acc = fma((double)E[(size_t)i * D + d], VE[i * b + j], acc);
-    P[(size_t)d * ldp + j] = (float)(acc / rho[j]);
-  }
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  const int d = e / ldp, j = e % ldp;
+  if (d >= D || j >= p) return;
+  double acc = 0.0;
+  for (int i = 0; i < b; ++i) acc = fma((double)E[(size_t)i * D + d], VE[i * b + j], acc);
+  P[(size_t)d * ldp + j] = (float)(acc / rho[j]);
 }
 
 // Core Gram A = diag(sigma^2, 0_p) + M^T M in fp64, M = [Q[:, :k], FP[:, :p]] (b x m).
@@ -326,13 +390,11 @@ __global__ __launch_bounds__(256) void core_gram_kernel(const float* __restrict_
 }
 
 // Sort eigenpairs by descending eigenvalue, keep `keep` of them:
-// Hc[:, t] = V[:, order[t]] (fp32, ld r_max), sig_new[t] = sqrt(max(lambda, 0)).
-// keep = min(r_max, n) for a merge; n for re-orthogonalisation.
-__global__ __launch_bounds__(1024) void eig_finish_kernel(const double* __restrict__ S,
-                                                          const double* __restrict__ V, int ld,
-                                                          float* Hc, int ldh, float* sig_new,
-                                                          int32_t* order, int32_t* st, int r_max,
-                                                          int for_merge) {
+// order[t] (rank order), sig_new[t] = sqrt(max(lambda, 0)), ST_KNEW = keep.
+// keep = min(r_max, n) for a merge; n for re-orthogonalisation. One workgroup.
+__global__ __launch_bounds__(1024) void eig_order_kernel(const double* __restrict__ S, int ld,
+                                                         float* sig_new, int32_t* order, int32_t* st,
+                                                         int r_max, int for_merge) {
   __shared__ double lam[1024];
   const int n = st[ST_JM];
   const int t = threadIdx.x;
@@ -349,19 +411,30 @@ __global__ __launch_bounds__(1024) void eig_finish_kernel(const double* __restri
   }
   __syncthreads();
   const int keep = for_merge ? (n < r_max ? n : r_max) : n;
-  // Orientation: a kept column whose index is an old direction (col < k) is
-  // signed so that H[col, col] >= 0, i.e. the basis moves continuously. The
-  // synced product does not depend on it; the basis-only ablation does.
+  for (int c = t; c < keep; c += blockDim.x) sig_new[c] = (float)sqrt(fmax(lam[min(max(order[c], 0), n - 1)], 0.0));
+  if (t == 0 && for_merge) st[ST_KNEW] = keep;
+}
+
+// Hc[:, t] = V[:, order[t]] (fp32, ld r_max) for the kept columns. A kept
+// column whose index is an old direction (t < k) is signed so that
+// H[t, t] >= 0, i.e. the basis moves continuously; the synced product does
+// not depend on it, the basis-only ablation does. Grid-stride, many blocks.
+__global__ __launch_bounds__(256) void eig_gather_kernel(const double* __restrict__ V, int ld,
+                                                         float* Hc, int ldh,
+                                                         const int32_t* __restrict__ order,
+                                                         const int32_t* __restrict__ st, int r_max,
+                                                         int for_merge) {
+  const int n = st[ST_JM];
+  const int keep = for_merge ? (n < r_max ? n : r_max) : n;
   const int kold = for_merge ? st[ST_K] : 0;
-  for (int idx = t; idx < n * keep; idx += blockDim.x) {
-    int row = idx / keep, col = idx % keep;
+  const size_t tot = (size_t)n * keep;
+  for (size_t e = blockIdx.x * 256 + threadIdx.x; e < tot; e += (size_t)gridDim.x * 256) {
+    int row = (int)(e / keep), col = (int)(e % keep);
     const int oc = min(max(order[col], 0), n - 1);
     double v = V[(size_t)row * ld + oc];
     if (col < kold && V[(size_t)col * ld + oc] < 0.0) v = -v;
     Hc[(size_t)row * ldh + col] = (float)v;
   }
-  for (int c = t; c < keep; c += blockDim.x) sig_new[c] = (float)sqrt(fmax(lam[min(max(order[c], 0), n - 1)], 0.0));
-  if (t == 0 && for_merge) st[ST_KNEW] = keep;
 }
 
 // ----------------------------------------------------------------------------
@@ -617,14 +690,43 @@ __global__ __launch_bounds__(256) void store_sym_kernel(const double* __restrict
 // ============================================================================
 // Host launchers.
 
+// out (M x N) = alpha * X (M x K) op(Y) + beta * Z, split over K.
+template <bool TY>
+static void skinny(isvd_handle* h, int M, int Nmax, const float* X, int ldx, const float* Y, int ldy,
+                   Dim N, int Kmax, float alpha, float beta, const float* Z, int ldz, float* out,
+                   int ldo) {
+  hipStream_t s = h->stream;
+  Dim K = TY ? ddim(h->w.st + ST_K) : hdim(Kmax);
+  int nsplit = Kmax / 128;
+  if (nsplit < 1) nsplit = 1;
+  if (nsplit > 16) nsplit = 16;
+  const int kchunk = ((Kmax + nsplit - 1) / nsplit + 63) / 64 * 64;
+  nsplit = (Kmax + kchunk - 1) / kchunk;
+  dim3 grid((Nmax + 31) / 32, nsplit, (M + 31) / 32);
+  hipLaunchKernelGGL((skinny_partial_kernel<TY>), grid, dim3(256), 0, s, X, ldx, Y, ldy, h->w.part, Nmax,
+                     M, N, K, kchunk);
+  int nb = (M * Nmax + 255) / 256;
+  if (nb > 256) nb = 256;
+  hipLaunchKernelGGL(skinny_reduce_kernel, dim3(nb), dim3(256), 0, s, h->w.part, nsplit, Nmax, M, N,
+                     alpha, beta, Z, ldz, out, ldo);
+}
+
+static void eig_finish(isvd_handle* h, int for_merge) {
+  const isvd_ws& w = h->w;
+  const int R = h->cfg.r_max;
+  hipLaunchKernelGGL(eig_order_kernel, dim3(1), dim3(1024), 0, h->stream, w.S, h->m_max, w.sig_new,
+                     w.order, w.st, R, for_merge);
+  hipLaunchKernelGGL(eig_gather_kernel, dim3(128), dim3(256), 0, h->stream, w.V, h->m_max, w.Hc, R,
+                     w.order, w.st, R, for_merge);
+}
+
 int iskv_launch_sym_eig(isvd_handle* h, const double* A, int32_t m, double* lam, double* V) {
   const isvd_ws& w = h->w;
   hipStream_t s = h->stream;
   hipLaunchKernelGGL(load_sym_kernel, dim3(128), dim3(256), 0, s, A, m, w.A, h->m_max, w.st);
   int rc = iskv_launch_core_eig(h);
   if (rc) return rc;
-  hipLaunchKernelGGL(eig_finish_kernel, dim3(1), dim3(1024), 0, s, w.S, w.V, h->m_max, w.Hc,
-                     h->cfg.r_max, w.sig_new, w.order, w.st, h->cfg.r_max, 0);
+  eig_finish(h, 0);
   hipLaunchKernelGGL(store_sym_kernel, dim3(128), dim3(256), 0, s, w.S, w.V, h->m_max, w.order, m, lam, V);
   ISKV_HIP_CHECK(hipGetLastError());
   return ISKV_OK;
@@ -652,12 +754,12 @@ int iskv_launch_merge(isvd_handle* h, const float* F, const int32_t* pos_F, int3
   const int32_t* dk = w.st + ST_K;
   const int32_t* dp = w.st + ST_P;
   // 1. Q = F B (b x k)
-  sgemm<false, false>(s, b, R, F, D, h->B, R, w.Q, R, nullptr, 0, hdim(b), ddim(dk), hdim(D), 1.f, 0.f);
+  skinny<false>(h, b, R, F, D, h->B, R, ddim(dk), D, 1.f, 0.f, nullptr, 0, w.Q, R);
   // 2. E = F - Q B^T (b x D)
-  sgemm<false, true>(s, b, D, w.Q, R, h->B, R, w.E, D, F, D, hdim(b), hdim(D), ddim(dk), -1.f, 1.f);
+  skinny<true>(h, b, D, w.Q, R, h->B, R, hdim(D), R, -1.f, 1.f, F, D, w.E, D);
   // 3. EB = E B; 4. E -= EB B^T (second projection, §4.1)
-  sgemm<false, false>(s, b, R, w.E, D, h->B, R, w.EB, R, nullptr, 0, hdim(b), ddim(dk), hdim(D), 1.f, 0.f);
-  sgemm<false, true>(s, b, D, w.EB, R, h->B, R, w.E, D, w.E, D, hdim(b), hdim(D), ddim(dk), -1.f, 1.f);
+  skinny<false>(h, b, R, w.E, D, h->B, R, ddim(dk), D, 1.f, 0.f, nullptr, 0, w.EB, R);
+  skinny<true>(h, b, D, w.EB, R, h->B, R, hdim(D), R, -1.f, 1.f, w.E, D, w.E, D);
   // 5. E E^T (fp64) and the residual basis
   hipLaunchKernelGGL(resid_gram_kernel, dim3(b), dim3(256), 0, s, w.E, D, b, w.GE, w.st);
   {
@@ -666,10 +768,10 @@ int iskv_launch_merge(isvd_handle* h, const float* F, const int32_t* pos_F, int3
     hipLaunchKernelGGL(resid_basis_kernel, dim3(1), dim3(256), smem, s, w.GE, b, D, h->sigma,
                        c.resid_rel_tol, w.VE, w.rho, w.st);
   }
-  hipLaunchKernelGGL(make_p_kernel, dim3((D + 255) / 256), dim3(256), 0, s, w.E, D, b, w.VE, w.rho,
-                     w.P, c.b_max, w.st);
+  hipLaunchKernelGGL(make_p_kernel, dim3((D * c.b_max + 255) / 256), dim3(256), 0, s, w.E, D, b, w.VE,
+                     w.rho, w.P, c.b_max, w.st);
   // 6. FP = F P (b x p)
-  sgemm<false, false>(s, b, c.b_max, F, D, w.P, c.b_max, w.FP, c.b_max, nullptr, 0, hdim(b), ddim(dp), hdim(D), 1.f, 0.f);
+  skinny<false>(h, b, c.b_max, F, D, w.P, c.b_max, ddim(dp), D, 1.f, 0.f, nullptr, 0, w.FP, c.b_max);
   // 7. core Gram and its eigendecomposition
   {
     dim3 grid((h->m_max + 15) / 16, (h->m_max + 15) / 16);
@@ -681,8 +783,7 @@ int iskv_launch_merge(isvd_handle* h, const float* F, const int32_t* pos_F, int3
     int rc = iskv_launch_core_eig(h);
     if (rc) return rc;
   }
-  hipLaunchKernelGGL(eig_finish_kernel, dim3(1), dim3(1024), 0, s, w.S, w.V, h->m_max, w.Hc, R,
-                     w.sig_new, w.order, w.st, R, 1);
+  eig_finish(h, 1);
   // 8. coordinate sync of old rows, new rows, basis update
   const int n0 = h->n_host;
   if (!(c.flags & ISKV_NO_COORD_SYNC) && n0 > 0) {
@@ -741,8 +842,7 @@ int iskv_launch_reorth(isvd_handle* h) {
     int rc = iskv_launch_core_eig(h);
     if (rc) return rc;
   }
-  hipLaunchKernelGGL(eig_finish_kernel, dim3(1), dim3(1024), 0, s, w.S, w.V, mm, w.Hc, R, w.sig_new,
-                     w.order, w.st, R, 0);
+  eig_finish(h, 0);
   hipLaunchKernelGGL(permute_cols_kernel, dim3(128), dim3(256), 0, s, w.V, w.order, w.W1, ld, w.st);
   // T1 = M_B^T Y (coordinates), T2 = Z Y (basis)
   iskv_dgemm(s, mm, w.MB, true, w.W1, false, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 2);
