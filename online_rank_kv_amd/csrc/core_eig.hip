@@ -78,21 +78,38 @@ __global__ __launch_bounds__(256) void dgemm_kernel(const double* __restrict__ A
   const int wi = (wave >> 1) * 16, wj = (wave & 1) * 16;
   v4d acc = {0.0, 0.0, 0.0, 0.0};
   for (int k0 = 0; k0 < m; k0 += 64) {
-    for (int e = t; e < 2048; e += 256) {
-      int r, k;
+    // all 16 loads of the step in flight at once: addresses are clamped into
+    // the matrix (always in bounds) and out-of-range values zeroed after
+    double ra[8], rb[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      int e = t + 256 * u, r, k;
       if (TA) { k = e >> 5; r = e & 31; } else { r = e >> 6; k = e & 63; }
       int ig = i0 + r, kg = k0 + k;
-      double a = 0.0;
-      if (ig < m && kg < m) a = TA ? A[(size_t)kg * lda + ig] : A[(size_t)ig * lda + kg];
-      As[r][k] = a;
+      int igc = min(ig, m - 1), kgc = min(kg, m - 1);
+      double a = TA ? A[(size_t)kgc * lda + igc] : A[(size_t)igc * lda + kgc];
+      ra[u] = (ig < m && kg < m) ? a : 0.0;
     }
-    for (int e = t; e < 2048; e += 256) {
-      int c, k;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      int e = t + 256 * u, c, k;
       if (!TB) { k = e >> 5; c = e & 31; } else { c = e >> 6; k = e & 63; }
       int jg = j0 + c, kg = k0 + k;
-      double b = 0.0;
-      if (jg < m && kg < m) b = TB ? B[(size_t)jg * ldb + kg] : B[(size_t)kg * ldb + jg];
-      Bs[k][c] = b;
+      int jgc = min(jg, m - 1), kgc = min(kg, m - 1);
+      double b = TB ? B[(size_t)jgc * ldb + kgc] : B[(size_t)kgc * ldb + jgc];
+      rb[u] = (jg < m && kg < m) ? b : 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      int e = t + 256 * u, r, k;
+      if (TA) { k = e >> 5; r = e & 31; } else { r = e >> 6; k = e & 63; }
+      As[r][k] = ra[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      int e = t + 256 * u, c, k;
+      if (!TB) { k = e >> 5; c = e & 31; } else { c = e >> 6; k = e & 63; }
+      Bs[k][c] = rb[u];
     }
     __syncthreads();
     const int kl = min(64, m - k0);

@@ -288,12 +288,23 @@ __device__ int jacobi_lds(double* S, double* V, int n, int ld, double tol, int m
 }
 
 // ----------------------------------------------------------------------------
-// Residual basis: eigen-decompose E E^T (b x b), sort descending, apply the
-// threshold of §4.1 and publish p. One workgroup.
-__global__ __launch_bounds__(256) void resid_basis_kernel(const double* __restrict__ GE, int b,
-                                                          int D, const float* __restrict__ sigma,
-                                                          float delta, double* VE, double* rho,
-                                                          int32_t* st) {
+// Residual basis (iS-KV notes §4.1): the residual directions of E^T with
+// singular values rho_j above tau = max(delta s, max(D, b) 2^-23 s),
+// s = max(sigma_1, rho_1), capped at p <= min(b, D - k). Published through
+// V_E (b x b) and rho so that P = E^T V_E diag(1/rho) (make_p_kernel).
+//
+// Fast path: when s = sigma_1 is certain (sigma_1^2 >= trace(E E^T) >= rho_1^2)
+// and every rho_j exceeds tau (Cholesky of E E^T - tau^2 I succeeds: all its
+// eigenvalues are positive), all b directions are kept and any orthonormal
+// basis of span(E^T) yields the same core up to a rotation of its last b
+// columns, hence the same truncated factors. The Cholesky factor L of E E^T
+// gives one: P = E^T L^-T (V_E = L^-T, rho = 1). Otherwise the eigenvectors of
+// E E^T are computed by cyclic Jacobi and thresholded as written.
+// One workgroup of 64 threads (a single wave).
+__global__ __launch_bounds__(64) void resid_basis_kernel(const double* __restrict__ GE, int b,
+                                                         int D, const float* __restrict__ sigma,
+                                                         float delta, double* VE, double* rho,
+                                                         int32_t* st) {
   extern __shared__ double smem[];
   const int ld = b + 1;
   double* S = smem;
@@ -305,11 +316,12 @@ __global__ __launch_bounds__(256) void resid_basis_kernel(const double* __restri
   int* qq = pp + 32;
   int* active = qq + 32;
   int* order = active + 1;
-  __shared__ int any_nonzero;
-  const int t = threadIdx.x;
-  if (t == 0) any_nonzero = 0;
+  __shared__ int any_nonzero, fast_ok;
+  __shared__ double trace;
+  const int t = threadIdx.x, nt = blockDim.x;
+  if (t == 0) { any_nonzero = 0; fast_ok = 1; trace = 0.0; }
   __syncthreads();
-  for (int idx = t; idx < b * b; idx += blockDim.x) {
+  for (int idx = t; idx < b * b; idx += nt) {
     double v = GE[idx];
     S[(idx / b) * ld + idx % b] = v;
     if (v != 0.0) any_nonzero = 1;
@@ -320,11 +332,81 @@ __global__ __launch_bounds__(256) void resid_basis_kernel(const double* __restri
     if (t == 0) { st[ST_P] = 0; st[ST_M] = k; st[ST_EZERO] = any_nonzero ? 0 : 1; }
     return;
   }
+  if (t == 0) {
+    double tr = 0.0;
+    for (int i = 0; i < b; ++i) tr += S[i * ld + i];
+    trace = tr;
+  }
+  __syncthreads();
+  const double s1 = (k > 0) ? (double)sigma[0] : 0.0;
+  const double floor_scale = (double)(D > b ? D : b) * 1.1920928955078125e-07;
+  bool fast = (k > 0) && (s1 * s1 >= trace) && (b <= D - k) && isfinite(trace);
+  if (fast) {
+    const double tau = fmax((double)delta * s1, floor_scale * s1);
+    // Cholesky of E E^T - tau^2 I in V (lower): succeeds iff every rho_j > tau
+    for (int idx = t; idx < b * b; idx += nt) {
+      int i = idx / b, j = idx % b;
+      V[i * ld + j] = S[i * ld + j] - (i == j ? tau * tau : 0.0);
+    }
+    __syncthreads();
+    for (int c = 0; c < b; ++c) {
+      if (t == 0) {
+        double dcc = V[c * ld + c];
+        if (!(dcc > 0.0)) fast_ok = 0;
+        V[c * ld + c] = sqrt(fmax(dcc, 1e-300));
+      }
+      __syncthreads();
+      const double dc = V[c * ld + c];
+      for (int i = c + 1 + t; i < b; i += nt) V[i * ld + c] /= dc;
+      __syncthreads();
+      for (int idx = t; idx < (b - c - 1) * (b - c - 1); idx += nt) {
+        int i = c + 1 + idx / (b - c - 1), j = c + 1 + idx % (b - c - 1);
+        if (j <= i) V[i * ld + j] -= V[i * ld + c] * V[j * ld + c];
+      }
+      __syncthreads();
+    }
+    fast = fast_ok != 0;
+  }
+  if (fast) {
+    // L = chol(E E^T) in V (lower), then V_E = L^-T (upper) by columns of L^-1
+    for (int idx = t; idx < b * b; idx += nt) V[(idx / b) * ld + idx % b] = S[(idx / b) * ld + idx % b];
+    __syncthreads();
+    for (int c = 0; c < b; ++c) {
+      if (t == 0) V[c * ld + c] = sqrt(fmax(V[c * ld + c], 1e-300));
+      __syncthreads();
+      const double dc = V[c * ld + c];
+      for (int i = c + 1 + t; i < b; i += nt) V[i * ld + c] /= dc;
+      __syncthreads();
+      for (int idx = t; idx < (b - c - 1) * (b - c - 1); idx += nt) {
+        int i = c + 1 + idx / (b - c - 1), j = c + 1 + idx % (b - c - 1);
+        if (j <= i) V[i * ld + j] -= V[i * ld + c] * V[j * ld + c];
+      }
+      __syncthreads();
+    }
+    // X = L^-1 by forward substitution, one column per thread, into S (E E^T
+    // is no longer needed); V_E[i][j] = X[j][i]
+    for (int j = t; j < b; j += nt) {
+      for (int i = 0; i < b; ++i) {
+        double acc = (i == j) ? 1.0 : 0.0;
+        for (int a = j; a < i; ++a) acc -= V[i * ld + a] * S[a * ld + j];
+        S[i * ld + j] = (i < j) ? 0.0 : acc / V[i * ld + i];
+      }
+    }
+    __syncthreads();
+    for (int idx = t; idx < b * b; idx += nt) {
+      int i = idx / b, j = idx % b;
+      VE[i * b + j] = S[j * ld + i];
+    }
+    for (int j = t; j < b; j += nt) rho[j] = 1.0;
+    if (t == 0) { st[ST_P] = b; st[ST_M] = k + b; st[ST_EZERO] = 0; }
+    return;
+  }
+  // exact path: eigenvectors of E E^T by cyclic Jacobi
   jacobi_lds(S, V, b, ld, 1e-13, ISKV_RESID_MAX_SWEEPS, cs, sn, pp, qq, active);
-  for (int i = t; i < b; i += blockDim.x) lam[i] = S[i * ld + i];
+  for (int i = t; i < b; i += nt) lam[i] = S[i * ld + i];
   __syncthreads();
   // rank by descending eigenvalue, ties by index
-  for (int i = t; i < b; i += blockDim.x) {
+  for (int i = t; i < b; i += nt) {
     int rnk = 0;
     const double ki = rank_key(lam[i]);
     for (int j = 0; j < b; ++j) {
@@ -334,18 +416,16 @@ __global__ __launch_bounds__(256) void resid_basis_kernel(const double* __restri
     order[rnk] = i;
   }
   __syncthreads();
-  for (int idx = t; idx < b * b; idx += blockDim.x) {
+  for (int idx = t; idx < b * b; idx += nt) {
     int row = idx / b, col = idx % b;
     VE[row * b + col] = V[row * ld + min(max(order[col], 0), b - 1)];
   }
-  for (int j = t; j < b; j += blockDim.x) rho[j] = sqrt(fmax(lam[min(max(order[j], 0), b - 1)], 0.0));
+  for (int j = t; j < b; j += nt) rho[j] = sqrt(fmax(lam[min(max(order[j], 0), b - 1)], 0.0));
   __syncthreads();
   if (t == 0) {
     double rho1 = sqrt(fmax(lam[min(max(order[0], 0), b - 1)], 0.0));
-    double s1 = (k > 0) ? (double)sigma[0] : 0.0;
     double sc = fmax(s1, rho1);
-    double floor_ = (double)(D > b ? D : b) * 1.1920928955078125e-07 * sc;
-    double tau = fmax((double)delta * sc, floor_);
+    double tau = fmax((double)delta * sc, floor_scale * sc);
     int p = 0;
     for (int j = 0; j < b; ++j) p += sqrt(fmax(lam[min(max(order[j], 0), b - 1)], 0.0)) > tau;
     if (p > D - k) p = D - k;
@@ -765,7 +845,7 @@ int iskv_launch_merge(isvd_handle* h, const float* F, const int32_t* pos_F, int3
   {
     const int ld = b + 1;
     size_t smem = (size_t)(2 * b * ld + b + 64) * sizeof(double) + (size_t)(32 * 2 + 1 + b) * sizeof(int) + 64;
-    hipLaunchKernelGGL(resid_basis_kernel, dim3(1), dim3(256), smem, s, w.GE, b, D, h->sigma,
+    hipLaunchKernelGGL(resid_basis_kernel, dim3(1), dim3(64), smem, s, w.GE, b, D, h->sigma,
                        c.resid_rel_tol, w.VE, w.rho, w.st);
   }
   hipLaunchKernelGGL(make_p_kernel, dim3((D * c.b_max + 255) / 256), dim3(256), 0, s, w.E, D, b, w.VE,
