@@ -300,8 +300,8 @@ __device__ int jacobi_lds(double* S, double* V, int n, int ld, double tol, int m
 // columns, hence the same truncated factors. The Cholesky factor L of E E^T
 // gives one: P = E^T L^-T (V_E = L^-T, rho = 1). Otherwise the eigenvectors of
 // E E^T are computed by cyclic Jacobi and thresholded as written.
-// One workgroup of 64 threads (a single wave).
-__global__ __launch_bounds__(64) void resid_basis_kernel(const double* __restrict__ GE, int b,
+// One workgroup of 256 threads.
+__global__ __launch_bounds__(256) void resid_basis_kernel(const double* __restrict__ GE, int b,
                                                          int D, const float* __restrict__ sigma,
                                                          float delta, double* VE, double* rho,
                                                          int32_t* st) {
@@ -309,7 +309,8 @@ __global__ __launch_bounds__(64) void resid_basis_kernel(const double* __restric
   const int ld = b + 1;
   double* S = smem;
   double* V = S + b * ld;
-  double* lam = V + b * ld;
+  double* Mx = V + b * ld;
+  double* lam = Mx + b * ld;
   double* cs = lam + b;
   double* sn = cs + 32;
   int* pp = (int*)(sn + 32);
@@ -384,7 +385,7 @@ __global__ __launch_bounds__(64) void resid_basis_kernel(const double* __restric
       __syncthreads();
     }
     // X = L^-1 by forward substitution, one column per thread, into S (E E^T
-    // is no longer needed); V_E[i][j] = X[j][i]
+    // is no longer needed)
     for (int j = t; j < b; j += nt) {
       for (int i = 0; i < b; ++i) {
         double acc = (i == j) ? 1.0 : 0.0;
@@ -393,9 +394,25 @@ __global__ __launch_bounds__(64) void resid_basis_kernel(const double* __restric
       }
     }
     __syncthreads();
+    // With P0 = E^T L^-T the new block of the core is F P0 = L (lower), so its
+    // Gram is L^T L. A few Jacobi sweeps on L^T L give an exactly orthogonal
+    // R that nearly diagonalises it; P = P0 R keeps the new directions of the
+    // core decoupled (as the singular-vector basis of the notes would), which
+    // the core eigensolver needs. V_E = L^-T R.
     for (int idx = t; idx < b * b; idx += nt) {
       int i = idx / b, j = idx % b;
-      VE[i * b + j] = S[j * ld + i];
+      double acc = 0.0;
+      for (int a = (i > j ? i : j); a < b; ++a) acc += V[a * ld + i] * V[a * ld + j];
+      Mx[i * ld + j] = acc;
+    }
+    __syncthreads();
+    jacobi_lds(Mx, V, b, ld, 1e-13, 3, cs, sn, pp, qq, active);
+    // V_E[i][j] = sum_a (L^-1)[a][i] R[a][j]
+    for (int idx = t; idx < b * b; idx += nt) {
+      int i = idx / b, j = idx % b;
+      double acc = 0.0;
+      for (int a = i; a < b; ++a) acc += S[a * ld + i] * V[a * ld + j];
+      VE[i * b + j] = acc;
     }
     for (int j = t; j < b; j += nt) rho[j] = 1.0;
     if (t == 0) { st[ST_P] = b; st[ST_M] = k + b; st[ST_EZERO] = 0; }
@@ -844,8 +861,8 @@ int iskv_launch_merge(isvd_handle* h, const float* F, const int32_t* pos_F, int3
   hipLaunchKernelGGL(resid_gram_kernel, dim3(b), dim3(256), 0, s, w.E, D, b, w.GE, w.st);
   {
     const int ld = b + 1;
-    size_t smem = (size_t)(2 * b * ld + b + 64) * sizeof(double) + (size_t)(32 * 2 + 1 + b) * sizeof(int) + 64;
-    hipLaunchKernelGGL(resid_basis_kernel, dim3(1), dim3(64), smem, s, w.GE, b, D, h->sigma,
+    size_t smem = (size_t)(3 * b * ld + b + 64) * sizeof(double) + (size_t)(32 * 2 + 1 + b) * sizeof(int) + 64;
+    hipLaunchKernelGGL(resid_basis_kernel, dim3(1), dim3(256), smem, s, w.GE, b, D, h->sigma,
                        c.resid_rel_tol, w.VE, w.rho, w.st);
   }
   hipLaunchKernelGGL(make_p_kernel, dim3((D * c.b_max + 255) / 256), dim3(256), 0, s, w.E, D, b, w.VE,
