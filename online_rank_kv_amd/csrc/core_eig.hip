@@ -16,7 +16,7 @@
 //     K_ij = s_ij / (s_jj - s_ii) (K antisymmetric, clipped),
 //   W <- W R exp(K) with exp(K) = I + K(I + K/2(I + K/3(I + K/4)))
 //                                                  (three GEMMs + one)
-// until every scaled coupling |s_ij| / sqrt(s_ii s_jj) is below 1e-12. This
+// until every scaled coupling |s_ij| / sqrt(s_ii s_jj) is below 1e-10. This
 // is the first-order eigenvector refinement of the Jacobi family (all
 // rotations of a sweep at once), with near-ties handled exactly. A final
 // Newton-Schulz step restores W^T W = I. Cores that do not converge in
@@ -29,7 +29,7 @@
 namespace {
 
 constexpr int PCJ_MAXIT = 7;
-constexpr double PCJ_TOL = 1e-12;
+constexpr double PCJ_TOL = 1e-10;
 constexpr double PCJ_OMEGA = 0.1;
 constexpr double PCJ_CLIP = 0.2;
 constexpr int CMAX_S = 6;      // largest cluster diagonalised exactly
@@ -52,6 +52,8 @@ constexpr int FLAG_FALLBACK = 2;
 // mode 1: when converged, copy Cin (the current W) to C instead.
 // mode 2: always run.
 typedef double v4d __attribute__((ext_vector_type(4)));
+constexpr int KP = 288;  // K panel depth of the fp64 GEMM (multiple of 32)
+constexpr size_t DGEMM_LDS = (size_t)(32 * (KP + 1) + KP * 33) * sizeof(double);
 
 template <bool TA, bool TB>
 __global__ __launch_bounds__(256) void dgemm_kernel(const double* __restrict__ A, int lda,
@@ -72,53 +74,60 @@ __global__ __launch_bounds__(256) void dgemm_kernel(const double* __restrict__ A
     }
     return;
   }
-  __shared__ double As[32][65];  // [row][k]
-  __shared__ double Bs[64][33];  // [k][col]
+  // The whole K panel (up to KP = 288 deep) of both operands is staged at
+  // once: every load of the panel is in flight together, then one barrier
+  // and the MFMA chain. Larger m loops over panels.
+  extern __shared__ double dsm[];
+  double* As = dsm;                    // [32][KP + 1]
+  double* Bs = dsm + 32 * (KP + 1);    // [KP][33]
   const int lane = t & 63, wave = t >> 6;
   const int wi = (wave >> 1) * 16, wj = (wave & 1) * 16;
   v4d acc = {0.0, 0.0, 0.0, 0.0};
-  for (int k0 = 0; k0 < m; k0 += 64) {
-    // all 16 loads of the step in flight at once: addresses are clamped into
-    // the matrix (always in bounds) and out-of-range values zeroed after
-    double ra[8], rb[8];
+  for (int k0 = 0; k0 < m; k0 += KP) {
+    const int kl = min(KP, m - k0);
+    if (k0 > 0) __syncthreads();
+    {
+      double ra[KP * 32 / 256];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      int e = t + 256 * u, r, k;
-      if (TA) { k = e >> 5; r = e & 31; } else { r = e >> 6; k = e & 63; }
-      int ig = i0 + r, kg = k0 + k;
-      int igc = min(ig, m - 1), kgc = min(kg, m - 1);
-      double a = TA ? A[(size_t)kgc * lda + igc] : A[(size_t)igc * lda + kgc];
-      ra[u] = (ig < m && kg < m) ? a : 0.0;
+      for (int u = 0; u < KP * 32 / 256; ++u) {
+        int e = t + 256 * u, r, k;
+        if (TA) { k = e >> 5; r = e & 31; } else { r = e / KP; k = e % KP; }
+        int ig = i0 + r, kg = k0 + k;
+        int igc = min(ig, m - 1), kgc = min(kg, m - 1);
+        double a = TA ? A[(size_t)kgc * lda + igc] : A[(size_t)igc * lda + kgc];
+        ra[u] = (ig < m && kg < m) ? a : 0.0;
+      }
+#pragma unroll
+      for (int u = 0; u < KP * 32 / 256; ++u) {
+        int e = t + 256 * u, r, k;
+        if (TA) { k = e >> 5; r = e & 31; } else { r = e / KP; k = e % KP; }
+        As[r * (KP + 1) + k] = ra[u];
+      }
     }
+    {
+      double rb[KP * 32 / 256];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      int e = t + 256 * u, c, k;
-      if (!TB) { k = e >> 5; c = e & 31; } else { c = e >> 6; k = e & 63; }
-      int jg = j0 + c, kg = k0 + k;
-      int jgc = min(jg, m - 1), kgc = min(kg, m - 1);
-      double b = TB ? B[(size_t)jgc * ldb + kgc] : B[(size_t)kgc * ldb + jgc];
-      rb[u] = (jg < m && kg < m) ? b : 0.0;
-    }
+      for (int u = 0; u < KP * 32 / 256; ++u) {
+        int e = t + 256 * u, c, k;
+        if (!TB) { k = e >> 5; c = e & 31; } else { c = e / KP; k = e % KP; }
+        int jg = j0 + c, kg = k0 + k;
+        int jgc = min(jg, m - 1), kgc = min(kg, m - 1);
+        double b = TB ? B[(size_t)jgc * ldb + kgc] : B[(size_t)kgc * ldb + jgc];
+        rb[u] = (jg < m && kg < m) ? b : 0.0;
+      }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      int e = t + 256 * u, r, k;
-      if (TA) { k = e >> 5; r = e & 31; } else { r = e >> 6; k = e & 63; }
-      As[r][k] = ra[u];
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      int e = t + 256 * u, c, k;
-      if (!TB) { k = e >> 5; c = e & 31; } else { c = e >> 6; k = e & 63; }
-      Bs[k][c] = rb[u];
+      for (int u = 0; u < KP * 32 / 256; ++u) {
+        int e = t + 256 * u, c, k;
+        if (!TB) { k = e >> 5; c = e & 31; } else { c = e / KP; k = e % KP; }
+        Bs[k * 33 + c] = rb[u];
+      }
     }
     __syncthreads();
-    const int kl = min(64, m - k0);
     for (int kk = 0; kk < kl; kk += 4) {
-      double a = As[wi + (lane & 15)][kk + (lane >> 4)];
-      double b = Bs[kk + (lane >> 4)][wj + (lane & 15)];
+      double a = As[(wi + (lane & 15)) * (KP + 1) + kk + (lane >> 4)];
+      double b = Bs[(kk + (lane >> 4)) * 33 + wj + (lane & 15)];
       acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc, 0, 0, 0);
     }
-    __syncthreads();
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -136,8 +145,8 @@ template <bool TA, bool TB>
 void dgemm(hipStream_t s, int m_max, const double* A, const double* B, double* C, const double* Cin,
            int ld, double alpha, double beta, double gamma, const int32_t* st, int mode) {
   dim3 grid((m_max + 31) / 32, (m_max + 31) / 32);
-  hipLaunchKernelGGL((dgemm_kernel<TA, TB>), grid, dim3(256), 0, s, A, ld, B, ld, C, ld, Cin, ld,
-                     alpha, beta, gamma, st, mode);
+  hipLaunchKernelGGL((dgemm_kernel<TA, TB>), grid, dim3(256), DGEMM_LDS, s, A, ld, B, ld, C, ld, Cin,
+                     ld, alpha, beta, gamma, st, mode);
 }
 
 // S = A, W = I, flags cleared.
@@ -285,27 +294,10 @@ __global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W,
     return;
   }
   const int ne = L.nedge;
-  // sorted edge keys i * 1024 + j: a deterministic order for the matching
   const int* edges = (const int*)(aux + 256);
-  int npow = 1;
-  while (npow < ne) npow <<= 1;
-  for (int e = t; e < npow; e += nt)
-    L.key[e] = e < ne ? edges[2 * e] * 1024 + edges[2 * e + 1] : 0x7fffffff;
+  for (int e = t; e < ne; e += nt) L.key[e] = edges[2 * e] * 1024 + edges[2 * e + 1];
   for (int i = t; i < m; i += nt) { L.lab[i] = i; L.size[i] = 0; L.used[i] = 0; L.cid[i] = -1; }
   __syncthreads();
-  for (int k = 2; k <= npow; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int e = t; e < npow; e += nt) {
-        int p = e ^ j;
-        if (p > e) {
-          int a = L.key[e], b = L.key[p];
-          bool up = (e & k) == 0;
-          if ((a > b) == up) { L.key[e] = b; L.key[p] = a; }
-        }
-      }
-      __syncthreads();
-    }
-  }
   // connected components by min-label propagation
   for (int guard = 0; guard < 1024; ++guard) {
     if (t == 0) L.changed = 0;
@@ -331,22 +323,61 @@ __global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W,
   }
   for (int i = t; i < m; i += nt) atomicAdd(&L.size[L.lab[i]], 1);
   __syncthreads();
-  if (t == 0) {
-    // small clusters (2..CMAX_S) get ids in root order; the rest are "big"
-    int n = 0;
-    for (int i = 0; i < m; ++i) {
-      if (L.lab[i] == i && L.size[i] >= 2) {
-        if (L.size[i] <= CMAX_S && n < NCL_MAX) { L.cid[i] = n; L.ccount[n] = 0; ++n; }
+  // small clusters (2..CMAX_S) get ids in root order (prefix count over
+  // roots); larger components are "big"
+  if (t < 64) {
+    int base = 0;
+    for (int i0 = 0; i0 < m; i0 += 64) {
+      int i = i0 + t;
+      bool small = i < m && L.lab[i] == i && L.size[i] >= 2 && L.size[i] <= CMAX_S;
+      bool big = i < m && L.lab[i] == i && L.size[i] > CMAX_S;
+      unsigned long long ms = __ballot(small);
+      if (__ballot(big)) L.anybig = 1;
+      int id = base + __popcll(ms & ((1ull << t) - 1ull));
+      if (small) {
+        if (id < NCL_MAX) { L.cid[i] = id; L.ccount[id] = 0; }
         else L.anybig = 1;
       }
+      base += __popcll(ms);
     }
-    L.ncl = n;
-    for (int i = 0; i < m; ++i) {  // members in index order
-      int c = L.cid[L.lab[i]];
-      if (c >= 0) L.members[c][L.ccount[c]++] = i;
+    if (t == 0) L.ncl = base < NCL_MAX ? base : NCL_MAX;
+  }
+  __syncthreads();
+  for (int i = t; i < m; i += nt) {
+    int c = L.cid[L.lab[i]];
+    if (c >= 0) L.members[c][atomicAdd(&L.ccount[c], 1)] = i;
+  }
+  __syncthreads();
+  if (t < L.ncl) {  // members in index order (deterministic)
+    const int c = L.ccount[t];
+    for (int a = 1; a < c; ++a) {
+      int v = L.members[t][a], b2 = a - 1;
+      while (b2 >= 0 && L.members[t][b2] > v) { L.members[t][b2 + 1] = L.members[t][b2]; --b2; }
+      L.members[t][b2 + 1] = v;
     }
-    int np = 0;  // greedy matching on strong pairs inside big components
-    if (L.anybig) {
+  }
+  if (L.anybig) {
+    // greedy matching on strong pairs inside big components, in sorted pair
+    // order so the result does not depend on the detection order
+    int npow = 1;
+    while (npow < ne) npow <<= 1;
+    for (int e = ne + t; e < npow; e += nt) L.key[e] = 0x7fffffff;
+    __syncthreads();
+    for (int k = 2; k <= npow; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int e = t; e < npow; e += nt) {
+          int p = e ^ j;
+          if (p > e) {
+            int a = L.key[e], b = L.key[p];
+            bool up = (e & k) == 0;
+            if ((a > b) == up) { L.key[e] = b; L.key[p] = a; }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    if (t == 0) {
+      int np = 0;
       for (int e = 0; e < ne && np < NPAIR_MAX; ++e) {
         int a = L.key[e] >> 10, b = L.key[e] & 1023;
         if (L.cid[L.lab[a]] >= 0) continue;
@@ -355,10 +386,10 @@ __global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W,
         L.pi[np] = a; L.pj[np] = b;
         ++np;
       }
+      L.npair = np;
     }
-    L.npair = np;
-    st[ST_NEDGE] = 0;  // the next detect pass starts a new list
   }
+  if (t == 0) st[ST_NEDGE] = 0;  // the next detect pass starts a new list
   __syncthreads();
   const int ncl = L.ncl, npair = L.npair;
   if (t < ncl) {
@@ -580,6 +611,14 @@ void iskv_dgemm(hipStream_t s, int m_max, const double* A, bool ta, const double
 }
 
 int iskv_core_eig_setup() {
+  ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)dgemm_kernel<false, false>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)DGEMM_LDS));
+  ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)dgemm_kernel<true, false>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)DGEMM_LDS));
+  ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)dgemm_kernel<false, true>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)DGEMM_LDS));
+  ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)dgemm_kernel<true, true>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)DGEMM_LDS));
   ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)pcj_analyze_kernel,
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)sizeof(AnalyzeLds)));
