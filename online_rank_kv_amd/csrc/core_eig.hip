@@ -52,11 +52,28 @@ constexpr int FLAG_FALLBACK = 2;
 // mode 1: when converged, copy Cin (the current W) to C instead.
 // mode 2: always run.
 typedef double v4d __attribute__((ext_vector_type(4)));
-constexpr int KP = 288;  // K panel depth of the fp64 GEMM (multiple of 32)
-constexpr size_t DGEMM_LDS = (size_t)(32 * (KP + 1) + KP * 33) * sizeof(double);
+// Branch-free masking of a loaded value: the bits are ANDed with 0 or
+// all-ones, so the load itself is never placed under a branch and every load
+// of a panel can be in flight at once.
+__device__ __forceinline__ double keep_if(double v, bool keep) {
+  return __longlong_as_double(__double_as_longlong(v) & -(long long)keep);
+}
+
+// One 32 x 32 output tile per 512-thread workgroup. The whole K panel of
+// both operands (ISKV_DGEMM_KP deep) is staged in LDS with all of its loads
+// in flight together, then 8 waves run the fp64 MFMA chain: waves 0-3 take
+// the four 16 x 16 quadrants over the even 4-deep k steps, waves 4-7 the odd
+// ones, and the two halves are summed through LDS. Matrices have a leading
+// dimension that is a multiple of the panel depth, so every address of a
+// panel lies inside the allocation; entries with k >= m are zeroed (the
+// padding may hold anything), rows and columns >= m are computed and dropped.
+constexpr int KP = ISKV_DGEMM_KP;
+constexpr int SA = KP + 4;  // LDS row stride (doubles) of both staged operands
+constexpr size_t DGEMM_LDS = (size_t)2 * 32 * SA * sizeof(double);
+static_assert(KP % 32 == 0, "panel depth must be a multiple of 32");
 
 template <bool TA, bool TB>
-__global__ __launch_bounds__(256) void dgemm_kernel(const double* __restrict__ A, int lda,
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void dgemm_kernel(const double* __restrict__ A, int lda,
                                                     const double* __restrict__ B, int ldb, double* C,
                                                     int ldc, const double* Cin, int ldcin,
                                                     double alpha, double beta, double gamma,
@@ -68,67 +85,76 @@ __global__ __launch_bounds__(256) void dgemm_kernel(const double* __restrict__ A
   if (mode == 0 && conv) return;
   const int t = threadIdx.x;
   if (mode == 1 && conv) {
-    for (int e = t; e < 1024; e += 256) {
+    for (int e = t; e < 1024; e += 512) {
       int i = i0 + (e >> 5), j = j0 + (e & 31);
       if (i < m && j < m) C[(size_t)i * ldc + j] = Cin[(size_t)i * ldcin + j];
     }
     return;
   }
-  // The whole K panel (up to KP = 288 deep) of both operands is staged at
-  // once: every load of the panel is in flight together, then one barrier
-  // and the MFMA chain. Larger m loops over panels.
   extern __shared__ double dsm[];
-  double* As = dsm;                    // [32][KP + 1]
-  double* Bs = dsm + 32 * (KP + 1);    // [KP][33]
+  double* As = dsm;            // As[i][k]: A(i0 + i, k0 + k)
+  double* Bt = dsm + 32 * SA;  // Bt[j][k]: B(k0 + k, j0 + j)
   const int lane = t & 63, wave = t >> 6;
-  const int wi = (wave >> 1) * 16, wj = (wave & 1) * 16;
+  const int q = wave & 3, h = wave >> 2;
+  const int wi = (q >> 1) * 16, wj = (q & 1) * 16;
+  const int c = t & 31, rr = t >> 5;  // 32 lanes along the contiguous index, 16 groups
+  constexpr int NL = KP * 32 / 512;   // loads per thread per operand
   v4d acc = {0.0, 0.0, 0.0, 0.0};
   for (int k0 = 0; k0 < m; k0 += KP) {
     const int kl = min(KP, m - k0);
     if (k0 > 0) __syncthreads();
-    {
-      double ra[KP * 32 / 256];
+    double ra[NL], rb[NL];
+    // element (row x, depth k) of the tile for load u: contiguous-in-k
+    // operands walk k in 32-wide chunks over two 16-row groups; transposed
+    // ones walk k in steps of 16 with the 32 lanes along the row index
 #pragma unroll
-      for (int u = 0; u < KP * 32 / 256; ++u) {
-        int e = t + 256 * u, r, k;
-        if (TA) { k = e >> 5; r = e & 31; } else { r = e / KP; k = e % KP; }
-        int ig = i0 + r, kg = k0 + k;
-        int igc = min(ig, m - 1), kgc = min(kg, m - 1);
-        double a = TA ? A[(size_t)kgc * lda + igc] : A[(size_t)igc * lda + kgc];
-        ra[u] = (ig < m && kg < m) ? a : 0.0;
-      }
-#pragma unroll
-      for (int u = 0; u < KP * 32 / 256; ++u) {
-        int e = t + 256 * u, r, k;
-        if (TA) { k = e >> 5; r = e & 31; } else { r = e / KP; k = e % KP; }
-        As[r * (KP + 1) + k] = ra[u];
-      }
+    for (int u = 0; u < NL; ++u) {
+      int x, k;
+      if (TA) { x = c; k = rr + 16 * u; } else { x = rr + 16 * (u / (KP / 32)); k = c + 32 * (u % (KP / 32)); }
+      const double* pa = TA ? A + (size_t)(k0 + k) * lda + (i0 + x) : A + (size_t)(i0 + x) * lda + (k0 + k);
+      ra[u] = keep_if(*pa, k < kl);
     }
-    {
-      double rb[KP * 32 / 256];
 #pragma unroll
-      for (int u = 0; u < KP * 32 / 256; ++u) {
-        int e = t + 256 * u, c, k;
-        if (!TB) { k = e >> 5; c = e & 31; } else { c = e / KP; k = e % KP; }
-        int jg = j0 + c, kg = k0 + k;
-        int jgc = min(jg, m - 1), kgc = min(kg, m - 1);
-        double b = TB ? B[(size_t)jgc * ldb + kgc] : B[(size_t)kgc * ldb + jgc];
-        rb[u] = (jg < m && kg < m) ? b : 0.0;
-      }
+    for (int u = 0; u < NL; ++u) {
+      int x, k;
+      if (!TB) { x = c; k = rr + 16 * u; } else { x = rr + 16 * (u / (KP / 32)); k = c + 32 * (u % (KP / 32)); }
+      const double* pb = TB ? B + (size_t)(j0 + x) * ldb + (k0 + k) : B + (size_t)(k0 + k) * ldb + (j0 + x);
+      rb[u] = keep_if(*pb, k < kl);
+    }
+    // keep the scheduler from interleaving the LDS stores with the loads:
+    // all loads of the panel are issued before the first store waits
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int u = 0; u < KP * 32 / 256; ++u) {
-        int e = t + 256 * u, c, k;
-        if (!TB) { k = e >> 5; c = e & 31; } else { c = e / KP; k = e % KP; }
-        Bs[k * 33 + c] = rb[u];
-      }
+    for (int u = 0; u < NL; ++u) {
+      int x, k;
+      if (TA) { x = c; k = rr + 16 * u; } else { x = rr + 16 * (u / (KP / 32)); k = c + 32 * (u % (KP / 32)); }
+      As[x * SA + k] = ra[u];
+    }
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      int x, k;
+      if (!TB) { x = c; k = rr + 16 * u; } else { x = rr + 16 * (u / (KP / 32)); k = c + 32 * (u % (KP / 32)); }
+      Bt[x * SA + k] = rb[u];
     }
     __syncthreads();
-    for (int kk = 0; kk < kl; kk += 4) {
-      double a = As[(wi + (lane & 15)) * (KP + 1) + kk + (lane >> 4)];
-      double b = Bs[(kk + (lane >> 4)) * 33 + wj + (lane & 15)];
-      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc, 0, 0, 0);
-    }
+    // MFMA f64 16x16x4: lane l holds A(l%16, l/16) and B(l/16, l%16)
+    const double* ap = As + (wi + (lane & 15)) * SA + (lane >> 4);
+    const double* bp = Bt + (wj + (lane & 15)) * SA + (lane >> 4);
+    for (int kk = 4 * h; kk < kl; kk += 8)
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(ap[kk], bp[kk], acc, 0, 0, 0);
   }
+  // sum the two k halves: waves 4-7 hand their quadrant to waves 0-3
+  __syncthreads();
+  double* red = dsm;  // [4 quadrants][4][64]
+  if (h == 1) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[(q * 4 + e) * 64 + lane] = acc[e];
+  }
+  __syncthreads();
+  if (h == 1) return;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc[e] += red[(q * 4 + e) * 64 + lane];
+  // result lane l, element e is D(l/16 + 4e, l%16)
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     int i = i0 + wi + (lane >> 4) + 4 * e, j = j0 + wj + (lane & 15);
@@ -145,7 +171,7 @@ template <bool TA, bool TB>
 void dgemm(hipStream_t s, int m_max, const double* A, const double* B, double* C, const double* Cin,
            int ld, double alpha, double beta, double gamma, const int32_t* st, int mode) {
   dim3 grid((m_max + 31) / 32, (m_max + 31) / 32);
-  hipLaunchKernelGGL((dgemm_kernel<TA, TB>), grid, dim3(256), DGEMM_LDS, s, A, ld, B, ld, C, ld, Cin,
+  hipLaunchKernelGGL((dgemm_kernel<TA, TB>), grid, dim3(512), DGEMM_LDS, s, A, ld, B, ld, C, ld, Cin,
                      ld, alpha, beta, gamma, st, mode);
 }
 
@@ -631,7 +657,7 @@ int iskv_core_eig_setup() {
 int iskv_launch_core_eig(isvd_handle* h) {
   const isvd_ws& w = h->w;
   hipStream_t s = h->stream;
-  const int mm = h->m_max, ld = h->m_max;
+  const int mm = h->m_max, ld = h->ldm;
   int32_t* st = w.st;
   const int nblk = (mm + 15) / 16;
   hipLaunchKernelGGL(pcj_init_kernel, dim3(128), dim3(256), 0, s, w.A, w.S, w.W0, ld, st);

@@ -30,6 +30,7 @@ bool cfg_ok(const iskv_config* c) {
 // Layout of the workspace; when base == nullptr only the size is computed.
 size_t carve(const iskv_config* c, char* base, isvd_ws* w) {
   const size_t D = c->D, R = c->r_max, Bm = c->b_max, M = c->r_max + c->b_max;
+  const size_t LM = iskv_core_ld((int)M);
   size_t off = 0;
   auto take = [&](size_t bytes) -> char* {
     char* p = base ? base + off : nullptr;
@@ -48,17 +49,17 @@ size_t carve(const iskv_config* c, char* base, isvd_ws* w) {
   x.rho = (double*)take(Bm * 8);
   x.P = (float*)take(D * Bm * 4);
   x.FP = (float*)take(Bm * Bm * 4);
-  x.A = (double*)take(M * M * 8);
-  x.V = (double*)take(M * M * 8);
-  x.S = (double*)take(M * M * 8);
-  x.W0 = (double*)take(M * M * 8);
-  x.W1 = (double*)take(M * M * 8);
-  x.T = (double*)take(M * M * 8);
-  x.Km = (double*)take(M * M * 8);
-  x.Pa = (double*)take(M * M * 8);
-  x.Pb = (double*)take(M * M * 8);
-  x.MB = (double*)take(M * M * 8);
-  x.Zb = (double*)take(M * M * 8);
+  x.A = (double*)take(LM * LM * 8);
+  x.V = (double*)take(LM * LM * 8);
+  x.S = (double*)take(LM * LM * 8);
+  x.W0 = (double*)take(LM * LM * 8);
+  x.W1 = (double*)take(LM * LM * 8);
+  x.T = (double*)take(LM * LM * 8);
+  x.Km = (double*)take(LM * LM * 8);
+  x.Pa = (double*)take(LM * LM * 8);
+  x.Pb = (double*)take(LM * LM * 8);
+  x.MB = (double*)take(LM * LM * 8);
+  x.Zb = (double*)take(LM * LM * 8);
   x.aux = (double*)take(256 * 8 + 4096 * 8);
   x.part = (float*)take((size_t)16 * Bm * (D > R ? D : R) * 4);
   x.lam = (double*)take(M * 8);
@@ -111,6 +112,7 @@ int isvd_init(isvd_handle** out, const iskv_config* cfg, float* C, float* sigma,
   h->ws_base = workspace; h->ws_bytes = ws_bytes;
   h->stream = (hipStream_t)stream;
   h->m_max = cfg->r_max + cfg->b_max;
+  h->ldm = iskv_core_ld(h->m_max);
   carve(cfg, (char*)workspace, &h->w);
   h->n_host = 0;
   h->folded_host = 0;

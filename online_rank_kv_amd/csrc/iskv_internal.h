@@ -39,17 +39,17 @@ struct isvd_ws {
   double* rho;        // [b_max]          residual singular values
   float* P;           // [D x b_max]      residual basis
   float* FP;          // [b_max x b_max]  F P
-  double* A;          // [m_max x m_max]  core Gram / reorth matrix
-  double* V;          // [m_max x m_max]  eigenvectors
-  double* S;          // [m_max x m_max]  W^T A W / Jacobi working matrix
-  double* W0;         // [m_max x m_max]  eigenvector iterate (ping)
-  double* W1;         // [m_max x m_max]  eigenvector iterate (pong)
-  double* T;          // [m_max x m_max]  A W
-  double* Km;         // [m_max x m_max]  first-order angles K
-  double* Pa;         // [m_max x m_max]  exp(K) partial products
-  double* Pb;         // [m_max x m_max]
-  double* MB;         // [m_max x m_max]  reorth: (B^T B)^(1/2)
-  double* Zb;         // [m_max x m_max]  reorth: (B^T B)^(-1/2)
+  double* A;          // [ldm x ldm]  core Gram / reorth matrix
+  double* V;          // [ldm x ldm]  eigenvectors
+  double* S;          // [ldm x ldm]  W^T A W / Jacobi working matrix
+  double* W0;         // [ldm x ldm]  eigenvector iterate (ping)
+  double* W1;         // [ldm x ldm]  eigenvector iterate (pong)
+  double* T;          // [ldm x ldm]  A W
+  double* Km;         // [ldm x ldm]  first-order angles K
+  double* Pa;         // [ldm x ldm]  exp(K) partial products
+  double* Pb;         // [ldm x ldm]
+  double* MB;         // [ldm x ldm]  reorth: (B^T B)^(1/2)
+  double* Zb;         // [ldm x ldm]  reorth: (B^T B)^(-1/2)
   double* aux;        // [256 doubles + 4096 int pairs] detection results
   float* part;        // [16 x b_max x max(D, r_max)] split-K partial sums
   double* lam;        // [m_max]
@@ -76,6 +76,7 @@ struct isvd_handle {
   hipStream_t stream;
   isvd_ws w;
   int32_t m_max;       // r_max + b_max
+  int32_t ldm;         // leading dimension of the fp64 core matrices
   int32_t n_host;      // rows folded (host mirror, exact)
   int32_t folded_host; // folded-row counter (host mirror, exact)
 };
@@ -93,6 +94,10 @@ struct iskv_window {
 };
 
 #define ISKV_JACOBI_MAX_SWEEPS 40
+// K-panel depth of the fp64 core GEMM; the leading dimension of every fp64
+// core matrix in the workspace is a multiple of it.
+#define ISKV_DGEMM_KP 288
+inline int iskv_core_ld(int m_max) { return (m_max + ISKV_DGEMM_KP - 1) / ISKV_DGEMM_KP * ISKV_DGEMM_KP; }
 #define ISKV_RESID_MAX_SWEEPS 30
 
 // ---- launch helpers implemented in the kernel translation units ----

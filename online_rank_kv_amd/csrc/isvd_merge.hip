@@ -811,20 +811,20 @@ static void skinny(isvd_handle* h, int M, int Nmax, const float* X, int ldx, con
 static void eig_finish(isvd_handle* h, int for_merge) {
   const isvd_ws& w = h->w;
   const int R = h->cfg.r_max;
-  hipLaunchKernelGGL(eig_order_kernel, dim3(1), dim3(1024), 0, h->stream, w.S, h->m_max, w.sig_new,
+  hipLaunchKernelGGL(eig_order_kernel, dim3(1), dim3(1024), 0, h->stream, w.S, h->ldm, w.sig_new,
                      w.order, w.st, R, for_merge);
-  hipLaunchKernelGGL(eig_gather_kernel, dim3(128), dim3(256), 0, h->stream, w.V, h->m_max, w.Hc, R,
+  hipLaunchKernelGGL(eig_gather_kernel, dim3(128), dim3(256), 0, h->stream, w.V, h->ldm, w.Hc, R,
                      w.order, w.st, R, for_merge);
 }
 
 int iskv_launch_sym_eig(isvd_handle* h, const double* A, int32_t m, double* lam, double* V) {
   const isvd_ws& w = h->w;
   hipStream_t s = h->stream;
-  hipLaunchKernelGGL(load_sym_kernel, dim3(128), dim3(256), 0, s, A, m, w.A, h->m_max, w.st);
+  hipLaunchKernelGGL(load_sym_kernel, dim3(128), dim3(256), 0, s, A, m, w.A, h->ldm, w.st);
   int rc = iskv_launch_core_eig(h);
   if (rc) return rc;
   eig_finish(h, 0);
-  hipLaunchKernelGGL(store_sym_kernel, dim3(128), dim3(256), 0, s, w.S, w.V, h->m_max, w.order, m, lam, V);
+  hipLaunchKernelGGL(store_sym_kernel, dim3(128), dim3(256), 0, s, w.S, w.V, h->ldm, w.order, m, lam, V);
   ISKV_HIP_CHECK(hipGetLastError());
   return ISKV_OK;
 }
@@ -873,7 +873,7 @@ int iskv_launch_merge(isvd_handle* h, const float* F, const int32_t* pos_F, int3
   {
     dim3 grid((h->m_max + 15) / 16, (h->m_max + 15) / 16);
     hipLaunchKernelGGL(core_gram_kernel, grid, dim3(256), 0, s, w.Q, R, w.FP, c.b_max, h->sigma, b,
-                       w.A, h->m_max, w.st);
+                       w.A, h->ldm, w.st);
   }
   hipLaunchKernelGGL(set_jm_kernel, dim3(1), dim3(1), 0, s, w.st, (int)ST_M);
   {
@@ -911,7 +911,7 @@ int iskv_launch_reorth(isvd_handle* h) {
   const iskv_config& c = h->cfg;
   const isvd_ws& w = h->w;
   hipStream_t s = h->stream;
-  const int R = c.r_max, D = c.D, mm = h->m_max, ld = h->m_max;
+  const int R = c.r_max, D = c.D, mm = h->m_max, ld = h->ldm;
   const int n = h->n_host;
   if (n == 0) return ISKV_OK;
   const int tiles = (R + 15) / 16;
