@@ -535,126 +535,136 @@ __global__ __launch_bounds__(256) void eig_gather_kernel(const double* __restric
 }
 
 // ----------------------------------------------------------------------------
-// Coordinate update (in place): rows [row0, row0 + rows) of C become
-// C[i, :kin] H[:kin, :kout]. One workgroup owns 32 rows for all output
-// columns, so the in-place rewrite is race-free. H is streamed through LDS.
-// kin/kout come from device memory (Dim).
-__global__ __launch_bounds__(256) void coord_update_kernel(float* C, int ldc, const float* __restrict__ H,
-                                                           int ldh, Dim kin_d, Dim kout_d,
-                                                           Dim rows_d, int r_max) {
-  const int kin = dval(kin_d), kout = dval(kout_d), rows = dval(rows_d);
-  const int i0 = blockIdx.x * 32;
-  if (i0 >= rows || kout == 0) return;
-  extern __shared__ float sm[];
-  float* Cs = sm;                 // [32][kin]
-  float* Hs = Cs + 32 * r_max;    // [32][64]
-  const int t = threadIdx.x;
-  const int nr = min(32, rows - i0);
-  for (int idx = t; idx < 32 * kin; idx += 256) {
-    int r = idx / kin, c = idx % kin;
-    Cs[r * r_max + c] = r < nr ? C[(size_t)(i0 + r) * ldc + c] : 0.f;
-  }
-  __syncthreads();
-  // thread: row group (t >> 6) * 8 .. +8, column (t & 63) within a 64-col tile
-  const int rg = (t >> 6) * 8, cc = t & 63;
-  for (int j0 = 0; j0 < kout; j0 += 64) {
-    float acc[8] = {};
-    for (int k0 = 0; k0 < kin; k0 += 32) {
-      __syncthreads();
-      for (int idx = t; idx < 32 * 64; idx += 256) {
-        int kk = idx >> 6, jj = idx & 63;
-        Hs[kk * 64 + jj] = (k0 + kk < kin && j0 + jj < kout) ? H[(size_t)(k0 + kk) * ldh + j0 + jj] : 0.f;
-      }
-      __syncthreads();
-      const int kl = min(32, kin - k0);
-      for (int kk = 0; kk < kl; ++kk) {
-        float h = Hs[kk * 64 + cc];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) acc[u] = fmaf(Cs[(rg + u) * r_max + k0 + kk], h, acc[u]);
-      }
-    }
-    __syncthreads();
-    if (j0 + cc < kout) {
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (rg + u < nr) C[(size_t)(i0 + rg + u) * ldc + j0 + cc] = acc[u];
-    }
-  }
+// Right-multiplication by a small matrix on fp32 MFMA (v_mfma_f32_16x16x4f32):
+//   Y[i, :kout] = X[i, :kin] H[:kin, :kout],   X = [X1[:, :k1] | X2[:, :kin-k1]].
+// Serves the coordinate update C <- C H (in place), the basis update
+// B <- [B | P] H (in place, with the bf16 copy) and the new rows
+// [Q | F P] H. A workgroup owns BM (16 or 32) rows: it stages all kin columns
+// of its rows in LDS before writing any output, so in-place use is safe
+// (workgroups own disjoint rows). H streams through LDS in 32-deep chunks,
+// the next chunk's loads in flight while the current one is multiplied.
+// Output columns go in tiles of 256; wave w owns 16-column blocks 4w .. 4w+3.
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+constexpr int XH_KC = 32;             // H chunk depth
+constexpr int XH_NT = 256;            // output column tile
+constexpr int XH_HS = XH_NT + 16;     // LDS row stride of the H chunk (floats)
+
+__host__ __device__ inline int xh_ldx(int kin_max) { return (kin_max + 7) / 8 * 8 + 4; }
+static inline size_t xh_lds_bytes(int bm, int kin_max) {
+  return ((size_t)bm * xh_ldx(kin_max) + (size_t)XH_KC * XH_HS) * sizeof(float);
 }
 
-// New rows: C[n + i, :r'] = M[i, :] H (M = [Q, FP], b x m); pos[n + i] = pos_F[i].
-__global__ __launch_bounds__(256) void new_rows_kernel(const float* __restrict__ Q, int ldq,
-                                                       const float* __restrict__ FP, int ldfp,
-                                                       const float* __restrict__ H, int ldh,
-                                                       float* C, int ldc, int32_t* pos,
-                                                       const int32_t* __restrict__ pos_F, int b,
-                                                       const int32_t* st, int n_rows_before) {
-  const int k = st[ST_K], m = st[ST_M], kout = st[ST_KNEW];
-  const int i = blockIdx.x;
-  for (int j = threadIdx.x; j < kout; j += blockDim.x) {
-    float acc = 0.f;
-    for (int x = 0; x < m; ++x) {
-      float mx = x < k ? Q[i * ldq + x] : FP[i * ldfp + (x - k)];
-      acc = fmaf(mx, H[(size_t)x * ldh + j], acc);
-    }
-    C[(size_t)(n_rows_before + i) * ldc + j] = acc;
-  }
-  if (threadIdx.x == 0) pos[n_rows_before + i] = pos_F[i];
-}
-
-// Basis update (in place): B[d, :kout] = B[d, :k] H[:k] + P[d, :p] H[k:k+p],
-// and the bf16 copy of the new rows. One workgroup per 32 rows of B.
-// mode 0 (merge): kin = k, extra = p from st; mode 1 (reorth): kin = k, extra 0.
-__global__ __launch_bounds__(256) void basis_update_kernel(float* B, int ldb, const float* __restrict__ P,
-                                                           int ldp, const float* __restrict__ H,
-                                                           int ldh, uint16_t* Bbf, int D,
-                                                           const int32_t* st, int mode, int r_max) {
-  const int k = st[ST_K];
-  const int p = mode == 0 ? st[ST_P] : 0;
-  const int kout = mode == 0 ? st[ST_KNEW] : k;
-  const int m = k + p;
-  const int d0 = blockIdx.x * 32;
-  if (d0 >= D) return;
+template <int BM>
+__global__ __launch_bounds__(256) void xh_mfma_kernel(const float* X1, int ld1, const float* X2, int ld2,
+                                                      Dim k1_d, Dim kin_d, const float* __restrict__ H,
+                                                      int ldh, int hcols, Dim kout_d, Dim rows_d,
+                                                      float* Y, int ldy, uint16_t* Ybf, int ldbf,
+                                                      int ldx, int32_t* pos, const int32_t* pos_src) {
+  const int k1 = dval(k1_d), kin = dval(kin_d), kout = dval(kout_d), rows = dval(rows_d);
+  const int i0 = blockIdx.x * BM;
+  if (i0 >= rows || kout <= 0) return;
   extern __shared__ float sm[];
-  float* Xs = sm;                       // [32][m_max]
-  const int ldx = r_max + 64;
-  float* Hs = Xs + 32 * ldx;            // [32][64]
-  const int t = threadIdx.x;
-  const int nr = min(32, D - d0);
-  for (int idx = t; idx < 32 * m; idx += 256) {
-    int r = idx / m, c = idx % m;
-    float v = 0.f;
-    if (r < nr) v = c < k ? B[(size_t)(d0 + r) * ldb + c] : P[(size_t)(d0 + r) * ldp + (c - k)];
-    Xs[r * ldx + c] = v;
-  }
-  __syncthreads();
-  const int rg = (t >> 6) * 8, cc = t & 63;
-  for (int j0 = 0; j0 < kout; j0 += 64) {
-    float acc[8] = {};
-    for (int k0 = 0; k0 < m; k0 += 32) {
-      __syncthreads();
-      for (int idx = t; idx < 32 * 64; idx += 256) {
-        int kk = idx >> 6, jj = idx & 63;
-        Hs[kk * 64 + jj] = (k0 + kk < m && j0 + jj < kout) ? H[(size_t)(k0 + kk) * ldh + j0 + jj] : 0.f;
-      }
-      __syncthreads();
-      const int kl = min(32, m - k0);
-      for (int kk = 0; kk < kl; ++kk) {
-        float h = Hs[kk * 64 + cc];
+  float* Xs = sm;               // [BM][ldx]
+  float* Hs = sm + BM * ldx;    // [XH_KC][XH_HS]
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int nr = min(BM, rows - i0);
+  // X tile: all loads issued, then stored; zero beyond kin and nr
+  {
+    const int kin4 = (kin + 3) & ~3;
+    for (int base = 0; base < BM * kin4; base += 256 * 16) {
+      float xv[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) acc[u] = fmaf(Xs[(rg + u) * ldx + k0 + kk], h, acc[u]);
+      for (int u = 0; u < 16; ++u) {
+        int e = base + t + 256 * u, r = e / kin4, c = e - r * kin4;
+        int rc = min(r, nr - 1);
+        float v = 0.f;
+        if (e < BM * kin4 && c < kin)
+          v = c < k1 ? X1[(size_t)(i0 + rc) * ld1 + c] : X2[(size_t)(i0 + rc) * ld2 + (c - k1)];
+        xv[u] = (r < nr) ? v : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        int e = base + t + 256 * u, r = e / kin4, c = e - r * kin4;
+        if (e < BM * kin4) Xs[r * ldx + c] = xv[u];
       }
     }
-    __syncthreads();
-    if (j0 + cc < kout) {
+  }
+  if (pos && t < nr) pos[i0 + t] = pos_src[t + i0];
+  constexpr int RB = BM / 16;
+  const int nch = (kin + XH_KC - 1) / XH_KC;
+  for (int j0 = 0; j0 < kout; j0 += XH_NT) {
+    v4f_t acc[RB][4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (rg + u < nr) {
-          B[(size_t)(d0 + rg + u) * ldb + j0 + cc] = acc[u];
-          Bbf[(size_t)(d0 + rg + u) * r_max + j0 + cc] = f2bf(acc[u]);
+    for (int a = 0; a < RB; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[a][b] = v4f_t{0.f, 0.f, 0.f, 0.f};
+    // H chunk element (kk, jj): e = t + 256 u, kk = e / 256, jj = e % 256
+    float hr[XH_KC];
+    auto load_h = [&](int kc) {
+#pragma unroll
+      for (int u = 0; u < XH_KC; ++u) {
+        int kk = kc + u, jj = min(j0 + t, hcols - 1);
+        int kr = min(kk, kin - 1);
+        float v = H[(size_t)kr * ldh + jj];
+        hr[u] = kk < kin ? v : 0.f;
+      }
+    };
+    if (nch > 0) load_h(0);
+    for (int c = 0; c < nch; ++c) {
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < XH_KC; ++u) Hs[u * XH_HS + t] = hr[u];
+      __syncthreads();
+      if (c + 1 < nch) load_h((c + 1) * XH_KC);
+      const int kc = c * XH_KC;
+      const int kl = min(XH_KC, kin - kc);
+      // A: lane holds X(row l%16, k l/16); B: lane holds H(k l/16, col l%16)
+      for (int kk = 0; kk < kl; kk += 4) {
+        float av[RB];
+#pragma unroll
+        for (int a = 0; a < RB; ++a) av[a] = Xs[(a * 16 + (lane & 15)) * ldx + kc + kk + (lane >> 4)];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          float bv = Hs[(kk + (lane >> 4)) * XH_HS + (wave * 4 + b) * 16 + (lane & 15)];
+#pragma unroll
+          for (int a = 0; a < RB; ++a)
+            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a], bv, acc[a][b], 0, 0, 0);
         }
       }
     }
+    // result lane l, element e: row 4(l/16) + e, column l%16 of the block
+#pragma unroll
+    for (int a = 0; a < RB; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int j = j0 + (wave * 4 + b) * 16 + (lane & 15);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = a * 16 + 4 * (lane >> 4) + e;
+          if (r < nr && j < kout) {
+            Y[(size_t)(i0 + r) * ldy + j] = acc[a][b][e];
+            if (Ybf) Ybf[(size_t)(i0 + r) * ldbf + j] = f2bf(acc[a][b][e]);
+          }
+        }
+      }
+  }
+}
+
+// Launch Y = [X1 | X2] H over `rows_host` rows (an upper bound when rows_d is
+// a device value); kin_max bounds kin for the LDS layout.
+static void xh_launch(hipStream_t s, int rows_host, const float* X1, int ld1, const float* X2, int ld2,
+                      Dim k1, Dim kin, int kin_max, const float* H, int ldh, int hcols, Dim kout,
+                      Dim rows, float* Y, int ldy, uint16_t* Ybf, int ldbf, int32_t* pos = nullptr,
+                      const int32_t* pos_src = nullptr, bool prefer16 = false) {
+  const int ldx = xh_ldx(kin_max);
+  if (!prefer16 && xh_lds_bytes(32, kin_max) <= 80 * 1024) {
+    hipLaunchKernelGGL(xh_mfma_kernel<32>, dim3((rows_host + 31) / 32), dim3(256),
+                       xh_lds_bytes(32, kin_max), s, X1, ld1, X2, ld2, k1, kin, H, ldh, hcols, kout,
+                       rows, Y, ldy, Ybf, ldbf, ldx, pos, pos_src);
+  } else {
+    hipLaunchKernelGGL(xh_mfma_kernel<16>, dim3((rows_host + 15) / 16), dim3(256),
+                       xh_lds_bytes(16, kin_max), s, X1, ld1, X2, ld2, k1, kin, H, ldh, hcols, kout,
+                       rows, Y, ldy, Ybf, ldbf, ldx, pos, pos_src);
   }
 }
 
@@ -834,9 +844,9 @@ int iskv_kernel_setup() {
   static int done = 0;
   if (done) return ISKV_OK;
   const int lds = 160 * 1024;
-  ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)coord_update_kernel,
+  ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)xh_mfma_kernel<32>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds));
-  ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)basis_update_kernel,
+  ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)xh_mfma_kernel<16>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds));
   if (iskv_core_eig_setup() != ISKV_OK) return ISKV_EHIP;
   done = 1;
@@ -883,18 +893,14 @@ int iskv_launch_merge(isvd_handle* h, const float* F, const int32_t* pos_F, int3
   eig_finish(h, 1);
   // 8. coordinate sync of old rows, new rows, basis update
   const int n0 = h->n_host;
-  if (!(c.flags & ISKV_NO_COORD_SYNC) && n0 > 0) {
-    size_t smem = (size_t)(32 * R + 32 * 64) * sizeof(float);
-    hipLaunchKernelGGL(coord_update_kernel, dim3((n0 + 31) / 32), dim3(256), smem, s, h->C, R, w.Hc,
-                       R, ddim(dk), ddim(w.st + ST_KNEW), hdim(n0), R);
-  }
-  hipLaunchKernelGGL(new_rows_kernel, dim3(b), dim3(256), 0, s, w.Q, R, w.FP, c.b_max, w.Hc, R, h->C,
-                     R, h->pos, pos_F, b, w.st, n0);
-  {
-    size_t smem = (size_t)(32 * (R + 64) + 32 * 64) * sizeof(float);
-    hipLaunchKernelGGL(basis_update_kernel, dim3((D + 31) / 32), dim3(256), smem, s, h->B, R, w.P,
-                       c.b_max, w.Hc, R, w.Bbf, D, w.st, 0, R);
-  }
+  const int M = h->m_max;
+  if (!(c.flags & ISKV_NO_COORD_SYNC) && n0 > 0)
+    xh_launch(s, n0, h->C, R, nullptr, 0, ddim(dk), ddim(dk), R, w.Hc, R, R, ddim(w.st + ST_KNEW),
+              hdim(n0), h->C, R, nullptr, 0);
+  xh_launch(s, b, w.Q, R, w.FP, c.b_max, ddim(dk), ddim(w.st + ST_M), M, w.Hc, R, R,
+            ddim(w.st + ST_KNEW), hdim(b), h->C + (size_t)n0 * R, R, nullptr, 0, h->pos + n0, pos_F);
+  xh_launch(s, D, h->B, R, w.P, c.b_max, ddim(dk), ddim(w.st + ST_M), M, w.Hc, R, R,
+            ddim(w.st + ST_KNEW), hdim(D), h->B, R, w.Bbf, R, nullptr, nullptr, true);
   hipLaunchKernelGGL(merge_commit_kernel, dim3(1), dim3(256), 0, s, h->sigma, w.sig_new, w.st, b, R);
   ISKV_HIP_CHECK(hipGetLastError());
   return ISKV_OK;
@@ -945,16 +951,10 @@ int iskv_launch_reorth(isvd_handle* h) {
   iskv_dgemm(s, mm, w.MB, true, w.W1, false, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 2);
   iskv_dgemm(s, mm, w.Zb, false, w.W1, false, w.Pa, nullptr, ld, 1.0, 0.0, 0.0, st, 2);
   hipLaunchKernelGGL(to_f32_kernel, dim3(128), dim3(256), 0, s, w.T, w.Pa, ld, w.Hc, w.T2, R, w.st);
-  {
-    size_t smem = (size_t)(32 * R + 32 * 64) * sizeof(float);
-    hipLaunchKernelGGL(coord_update_kernel, dim3((n + 31) / 32), dim3(256), smem, s, h->C, R, w.Hc, R,
-                       ddim(w.st + ST_K), ddim(w.st + ST_K), hdim(n), R);
-  }
-  {
-    size_t smem = (size_t)(32 * (R + 64) + 32 * 64) * sizeof(float);
-    hipLaunchKernelGGL(basis_update_kernel, dim3((D + 31) / 32), dim3(256), smem, s, h->B, R, w.P,
-                       c.b_max, w.T2, R, w.Bbf, D, w.st, 1, R);
-  }
+  xh_launch(s, n, h->C, R, nullptr, 0, ddim(w.st + ST_K), ddim(w.st + ST_K), R, w.Hc, R, R,
+            ddim(w.st + ST_K), hdim(n), h->C, R, nullptr, 0);
+  xh_launch(s, D, h->B, R, nullptr, 0, ddim(w.st + ST_K), ddim(w.st + ST_K), R, w.T2, R, R,
+            ddim(w.st + ST_K), hdim(D), h->B, R, w.Bbf, R, nullptr, nullptr, true);
   hipLaunchKernelGGL(reorth_commit_kernel, dim3(1), dim3(256), 0, s, h->sigma, w.sig_new, w.st, R);
   ISKV_HIP_CHECK(hipGetLastError());
   return ISKV_OK;

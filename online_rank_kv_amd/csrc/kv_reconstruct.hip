@@ -114,6 +114,164 @@ __global__ __launch_bounds__(256) void recon_kernel(const float* __restrict__ C,
   }
 }
 
+// bf16 MFMA reconstruction of the compressed rows (bf16 output):
+// out[pos[i], c0 .. c0+127] = RoPE(C[i, :k] B[c0 .. c0+127, :k]^T).
+// C (fp32) is rounded to bf16 while it is staged, B comes from its bf16 copy;
+// products accumulate in fp32 (v_mfma_f32_16x16x32_bf16).
+// Workgroup: 64 rows x 128 features, 4 waves; wave (wr, wc) owns rows
+// wr*32 .. +31 and four 16-feature blocks: two "lo" blocks and the blocks
+// half a head further, so both members of every rotary pair (j, j + dh/2)
+// sit in the same lane and accumulator element and RoPE is applied in
+// registers. Workgroup w maps to row block g*8 + w%8 and feature tile
+// (w / 8) % T, with g = w / (8T): the T feature tiles of one row block are
+// dispatched to the same XCD and share its L2 copy of the C rows.
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+constexpr int RM_BM = 64, RM_BN = 128, RM_KC = 64;
+constexpr int RM_RS = RM_KC + 8;    // LDS row stride (bf16) of the staged operands
+constexpr int RM_OS = RM_BN + 8;    // LDS row stride (bf16) of the output tile
+constexpr int RM_LDS = (RM_BM + RM_BN) * RM_RS;  // bf16 elements
+static_assert(RM_BM * RM_OS <= RM_LDS, "output tile must fit in the staging area");
+
+__global__ __launch_bounds__(256) void recon_mfma_kernel(const float* __restrict__ C, int ldc,
+                                                         const uint16_t* __restrict__ Bbf, int ldb,
+                                                         const int32_t* __restrict__ pos,
+                                                         const int32_t* __restrict__ st, int n,
+                                                         int D, int dh, int apply_rope,
+                                                         double log_theta, uint16_t* out,
+                                                         int n_total, int tiles) {
+  const int k = st[ST_K];
+  const int w = blockIdx.x;
+  const int g = w / (8 * tiles), rem = w % (8 * tiles);
+  const int i0 = (g * 8 + rem % 8) * RM_BM, c0 = (rem / 8) * RM_BN;
+  if (i0 >= n) return;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[RM_LDS];
+  uint16_t* Cs = lds;                  // [64][RM_RS]   C rows, k chunk
+  uint16_t* Bs = lds + RM_BM * RM_RS;  // [128][RM_RS]  B rows (features), k chunk
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int half = dh >> 1;
+  // the tile's "lo" 16-feature blocks in order; this wave takes two of them
+  int lob0 = 0, lob1 = 0;
+  {
+    int cnt = 0;
+    for (int b = 0; b < RM_BN / 16; ++b) {
+      if ((b * 16) % dh < half) {
+        if (cnt == 2 * wc) lob0 = b;
+        if (cnt == 2 * wc + 1) lob1 = b;
+        ++cnt;
+      }
+    }
+  }
+  const int blk[4] = {lob0, lob1, lob0 + half / 16, lob1 + half / 16};
+  v4f acc[2][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < k; k0 += RM_KC) {
+    if (k0 > 0) __syncthreads();
+    // C: 64 x 64 fp32 -> bf16; columns >= k (and rows >= n) are zero
+    float4 cv[4];
+    uint4 bv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      int e = t + 256 * u, r = e >> 4, col = k0 + (e & 15) * 4;
+      int row = min(i0 + r, n - 1), colc = min(col, ldc - 4);
+      cv[u] = *(const float4*)(C + (size_t)row * ldc + colc);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      int e = t + 256 * u, r = e >> 3, col = k0 + (e & 7) * 8;
+      int colc = min(col, ldb - 8);
+      bv[u] = *(const uint4*)(Bbf + (size_t)(c0 + r) * ldb + colc);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      int e = t + 256 * u, r = e >> 4, cl = (e & 15) * 4, col = k0 + cl;
+      float x0 = col < k ? cv[u].x : 0.f, x1 = col + 1 < k ? cv[u].y : 0.f;
+      float x2 = col + 2 < k ? cv[u].z : 0.f, x3 = col + 3 < k ? cv[u].w : 0.f;
+      uint2 pk;
+      pk.x = (uint32_t)f2bf(x0) | ((uint32_t)f2bf(x1) << 16);
+      pk.y = (uint32_t)f2bf(x2) | ((uint32_t)f2bf(x3) << 16);
+      *(uint2*)(Cs + r * RM_RS + cl) = pk;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      int e = t + 256 * u, r = e >> 3, cl = (e & 7) * 8, col = k0 + cl;
+      uint4 v = bv[u];
+      if (col + 8 > k) {  // partial chunk at the rank boundary: zero k >= rank
+        uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (col + q >= k) wv[q >> 1] &= (q & 1) ? 0x0000ffffu : 0xffff0000u;
+        v = uint4{wv[0], wv[1], wv[2], wv[3]};
+      }
+      *(uint4*)(Bs + r * RM_RS + cl) = v;
+    }
+    __syncthreads();
+    // A operand: lane holds C(row l%16, k 8(l/16) .. +7); B operand: lane
+    // holds B(feature l%16, same k range)
+#pragma unroll
+    for (int ks = 0; ks < RM_KC; ks += 32) {
+      const int ko = ks + 8 * (lane >> 4);
+      v8bf a0 = __builtin_bit_cast(v8bf, *(const uint4*)(Cs + (wr * 32 + (lane & 15)) * RM_RS + ko));
+      v8bf a1 = __builtin_bit_cast(v8bf, *(const uint4*)(Cs + (wr * 32 + 16 + (lane & 15)) * RM_RS + ko));
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        v8bf bb = __builtin_bit_cast(v8bf, *(const uint4*)(Bs + (blk[b] * 16 + (lane & 15)) * RM_RS + ko));
+        acc[0][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bb, acc[0][b], 0, 0, 0);
+        acc[1][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bb, acc[1][b], 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();
+  // epilogue: lane l, element e holds row 4(l/16) + e, feature l%16 of each block.
+  // RoPE: the angle pos * theta^(-2j/dh) is formed in revolutions in fp64 and
+  // reduced to [-1/2, 1/2]; sin and cos of the reduced fp32 value (the
+  // hardware sine/cosine take revolutions) are far below bf16 resolution.
+  uint16_t* Os = lds;  // [64][RM_OS] output tile
+  double rev_per_pos[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int j = (blk[b] * 16 + (lane & 15)) % dh;
+    rev_per_pos[b] = exp(-(2.0 * j / dh) * log_theta) * 0.15915494309189533577;  // / (2 pi)
+  }
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int rl = wr * 32 + a * 16 + 4 * (lane >> 4) + e;
+      const int i = i0 + rl;
+      const int p = pos[min(i, n - 1)];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        float x = acc[a][b][e], y = acc[a][b + 2][e];
+        const int flo = blk[b] * 16 + (lane & 15);
+        if (apply_rope) {
+          double rv = (double)p * rev_per_pos[b];
+          float r = (float)(rv - rint(rv));
+          float c = __builtin_amdgcn_cosf(r), s = __builtin_amdgcn_sinf(r);
+          float xr = x * c - y * s, yr = y * c + x * s;
+          x = xr; y = yr;
+        }
+        Os[rl * RM_OS + flo] = f2bf(x);
+        Os[rl * RM_OS + flo + half] = f2bf(y);
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    int e = t + 256 * u, r = e >> 4, cl = (e & 15) * 8;
+    int i = i0 + r;
+    if (i >= n) continue;
+    int p = pos[i];
+    if (p < 0 || p >= n_total) continue;  // outside the output: dropped, never written
+    *(uint4*)(out + (size_t)p * D + c0 + cl) = *(const uint4*)(Os + r * RM_OS + cl);
+  }
+}
+
 // Exact rows: out[pos_e] = RoPE(X_exact[e]); slots with pos_e < 0 are empty.
 // Grid (n_exact), 64 threads x pairs.
 template <bool BF16>
@@ -165,7 +323,15 @@ int iskv_launch_reconstruct(const isvd_handle* h, const float* X_exact, const in
   if (n > 0) {
     const int W = (D % 128 == 0 && 128 % head_dim == 0) ? 128 : 64;
     dim3 grid(D / W, (n + 31) / 32);
-    if (bf)
+    const bool mfma = bf && D % RM_BN == 0 && head_dim % 32 == 0 && RM_BN % head_dim == 0 &&
+                      R % 8 == 0;
+    if (mfma) {
+      const int tiles = D / RM_BN, nrb = (n + RM_BM - 1) / RM_BM;
+      const int nwg = (nrb + 7) / 8 * 8 * tiles;
+      hipLaunchKernelGGL(recon_mfma_kernel, dim3(nwg), dim3(256), 0, s, h->C, R, h->w.Bbf, R,
+                         h->pos, h->w.st, n, D, head_dim, apply_rope, lt, (uint16_t*)out, n_total,
+                         tiles);
+    } else if (bf)
       hipLaunchKernelGGL(recon_kernel<true>, grid, dim3(256), 0, s, h->C, R, h->B, R, h->pos,
                          h->w.st, n, D, head_dim, W, apply_rope, lt, out, n_total);
     else
