@@ -109,71 +109,78 @@ def main():
     Xv = synth.kv_stream(synth.StreamSpec(D, n_rows, "invsqrt", 0.0, 1))
     gen_s = time.perf_counter() - t_gen
 
-    stream = torch.cuda.Stream()
+    # one HIP stream per path: the K and V merges (and their reconstructions)
+    # are independent chains of small launches and run concurrently
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
     paths, wins, Xd = [], [], []
-    with torch.cuda.stream(stream):
-        for X in (Xk, Xv):
+    for X, st in zip((Xk, Xv), streams):
+        with torch.cuda.stream(st):
             p = K.IsvdPath(D=D, r_max=R, b_max=BLK, n_cap=n_rows, reorth_every_rows=256, device=dev,
-                           stream=stream)
+                           stream=st)
             paths.append(p)
-            wins.append(K.ExactWindow(p, window=WIN, block=BLK, stream=stream))
+            wins.append(K.ExactWindow(p, window=WIN, block=BLK, stream=st))
             Xd.append(torch.from_numpy(X).to(dev))
-        # fill both paths with the first N0 rows (+ window)
-        t_fill = time.perf_counter()
-        for s in range(0, N0 + WIN, 512):
-            e = min(s + 512, N0 + WIN)
-            for i in range(2):
-                wins[i].append(Xd[i][s:e], s)
-        stream.synchronize()
-        fill_s = time.perf_counter() - t_fill
-        rng = np.random.default_rng(5)
-        q = torch.from_numpy(rng.standard_normal((1, HQ, DH)).astype(np.float32)).to(dev).bfloat16()
-        o = torch.empty((1, HQ, DH), dtype=torch.bfloat16, device=dev)
-        n_total_max = n_rows
-        Kc = torch.empty((n_total_max, D), dtype=torch.bfloat16, device=dev)
-        Vc = torch.empty((n_total_max, D), dtype=torch.bfloat16, device=dev)
-        ws = torch.empty(K.decode_attend_workspace_bytes(1, n_total_max, HQ, DH), dtype=torch.uint8,
-                         device=dev)
-        cursor = [N0 + WIN]
-        ev = {k: [] for k in ("merge", "recon_k", "recon_v", "attend")}
+            st.synchronize()
+    # fill both paths with the first N0 rows (+ window)
+    t_fill = time.perf_counter()
+    for s in range(0, N0 + WIN, 512):
+        e = min(s + 512, N0 + WIN)
+        for i in range(2):
+            wins[i].append(Xd[i][s:e], s)
+    for st in streams:
+        st.synchronize()
+    fill_s = time.perf_counter() - t_fill
+    rng = np.random.default_rng(5)
+    q = torch.from_numpy(rng.standard_normal((1, HQ, DH)).astype(np.float32)).to(dev).bfloat16()
+    o = torch.empty((1, HQ, DH), dtype=torch.bfloat16, device=dev)
+    Kc = torch.empty((n_rows, D), dtype=torch.bfloat16, device=dev)
+    Vc = torch.empty((n_rows, D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(K.decode_attend_workspace_bytes(1, n_rows, HQ, DH), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    cursor = [N0 + WIN]
+    ev = {k: [] for k in ("merge_k", "merge_v", "recon_k", "recon_v", "attend")}
+    attend_done = [None]
 
-        def step(record):
-            s0 = cursor[0]
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e2 = torch.cuda.Event(enable_timing=True)
-            e3 = torch.cuda.Event(enable_timing=True)
-            e4 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(2):
-                wins[i].append(Xd[i][s0:s0 + BLK], s0)
-            e1.record(stream)
-            n_total = s0 + BLK
-            paths[0].reconstruct(Kc, n_total, X_exact=wins[0].rows, pos_exact=wins[0].pos, head_dim=DH,
-                                 rope=True, theta=THETA, stream=stream)
-            e2.record(stream)
-            paths[1].reconstruct(Vc, n_total, X_exact=wins[1].rows, pos_exact=wins[1].pos, head_dim=DH,
-                                 rope=False, stream=stream)
-            e3.record(stream)
-            K.decode_attend(q, Kc, Vc, 1, n_total, HQ, HKV, DH, DH ** -0.5, o, ws, stream=stream)
-            e4.record(stream)
-            if record:
-                ev["merge"].append((e0, e1))
-                ev["recon_k"].append((e1, e2))
-                ev["recon_v"].append((e2, e3))
-                ev["attend"].append((e3, e4))
-            cursor[0] += BLK
+    def step(record):
+        s0 = cursor[0]
+        n_total = s0 + BLK
+        sk, sv = streams
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+        if attend_done[0] is not None:
+            sv.wait_event(attend_done[0])  # V cache is rewritten only after the last attention read it
+        e[0].record(sk)
+        e[3].record(sv)
+        wins[0].append(Xd[0][s0:s0 + BLK], s0)   # K merge (stream K)
+        wins[1].append(Xd[1][s0:s0 + BLK], s0)   # V merge (stream V)
+        e[1].record(sk)
+        e[4].record(sv)
+        paths[0].reconstruct(Kc, n_total, X_exact=wins[0].rows, pos_exact=wins[0].pos, head_dim=DH,
+                             rope=True, theta=THETA, stream=sk)
+        paths[1].reconstruct(Vc, n_total, X_exact=wins[1].rows, pos_exact=wins[1].pos, head_dim=DH,
+                             rope=False, stream=sv)
+        e[2].record(sk)
+        e[5].record(sv)
+        sk.wait_event(e[5])
+        e[7].record(sk)
+        K.decode_attend(q, Kc, Vc, 1, n_total, HQ, HKV, DH, DH ** -0.5, o, ws, stream=sk)
+        e[6].record(sk)
+        attend_done[0] = e[6]
+        if record:
+            ev["merge_k"].append((e[0], e[1]))
+            ev["merge_v"].append((e[3], e[4]))
+            ev["recon_k"].append((e[1], e[2]))
+            ev["recon_v"].append((e[4], e[5]))
+            ev["attend"].append((e[7], e[6]))
+        cursor[0] += BLK
 
-        for _ in range(warm):
-            step(False)
-        stream.synchronize()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            step(True)
-        stream.synchronize()
-        torch.cuda.synchronize()
-        dt = time.perf_counter() - t0
+    for _ in range(warm):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
 
     def avg_ms(key):
         return float(np.mean([a.elapsed_time(b) for a, b in ev[key]]))
@@ -183,8 +190,8 @@ def main():
     merges = 2 * steps
     n_mid = cursor[0] - BLK * steps // 2
     # algorithmic bytes of one K reconstruction: read C (n x r fp32) and B^T
-    # (r x D fp32), write n_total x D bf16; flops 2 n r D
-    recon_bytes = n_mid * R * 4 + R * D * 4 + n_mid * D * 2
+    # (its bf16 copy, D x r), write n_total x D bf16; flops 2 n r D
+    recon_bytes = n_mid * R * 4 + R * D * 2 + n_mid * D * 2
     recon_flops = 2.0 * n_mid * R * D
     recon_gbps = recon_bytes / (ms["recon_k"] * 1e-3) / 1e9
     result = {
@@ -211,7 +218,8 @@ def main():
                      "kernel": "kv_reconstruct (K, bf16 + RoPE)",
                      "mfma_frac": recon_flops / (ms["recon_k"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
         "setup_s": {"generate": gen_s, "fill_16k_rows": fill_s},
-        "core_solver_last_merge": [{"flags": c[11], "steps": c[12], "k": c[1], "n": c[0]} for c in core],
+        "core_solver_last_merge": [{"flags": c[11], "steps": c[12], "resid_sweeps": c[14], "k": c[1], "n": c[0]}
+                                   for c in core],
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(Xk, Xv, args.cpu_seconds)

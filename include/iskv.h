@@ -136,7 +136,8 @@ int isvd_query(isvd_handle* h, int32_t* n, int32_t* k, int32_t* status);
  * [3] folded rows, [4] status bits, [5] core width k + p, [6] r',
  * [7] Jacobi sweeps of the last fallback solve, [11] core eigensolver flags
  * (1 converged by parallel refinement, 2 single-workgroup Jacobi fallback),
- * [12] refinement steps of the last core solve. Errors: EINVAL, EHIP. */
+ * [12] refinement steps of the last core solve, [14] Jacobi sweeps of the last
+ * residual eigensolve. Errors: EINVAL, EHIP. */
 int isvd_query_state(isvd_handle* h, int32_t* state, int32_t count);
 
 /* Run the handle's core eigensolver on a caller matrix (the step of

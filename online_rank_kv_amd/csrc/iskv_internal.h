@@ -24,6 +24,7 @@ enum {
   ST_PCJ = 11,     // core eigensolver flags: 1 converged, 2 Jacobi fallback used
   ST_PCJIT = 12,   // refinement steps used by the last core eigensolve
   ST_NEDGE = 13,   // strong pairs found by the current detection pass
+  ST_RSWEEPS = 14, // Jacobi sweeps of the last residual eigensolve
   ST_COUNT = 16
 };
 

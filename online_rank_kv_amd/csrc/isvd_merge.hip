@@ -210,239 +210,164 @@ __global__ __launch_bounds__(256) void resid_gram_kernel(const float* __restrict
 }
 
 // ----------------------------------------------------------------------------
-// Cyclic Jacobi for a small symmetric fp64 matrix held in LDS, parallel
-// (round-robin) ordering, executed by the whole block. S is n x n with
-// leading dimension ld, V receives the eigenvectors (columns). Returns the
-// number of sweeps; a sweep with no rotation above the relative threshold
-// |s_pq| <= tol * sqrt(|s_pp s_qq|) ends the iteration.
-__device__ int jacobi_lds(double* S, double* V, int n, int ld, double tol, int max_sweeps,
-                          double* cs, double* sn, int* pp, int* qq, int* active) {
-  const int t = threadIdx.x, nt = blockDim.x;
-  for (int idx = t; idx < n * n; idx += nt) V[(idx / n) * ld + idx % n] = (idx / n == idx % n) ? 1.0 : 0.0;
-  __syncthreads();
-  if (n < 2) return 0;
-  const int N = (n + 1) & ~1, half = N / 2;
-  int sweep = 0;
-  for (; sweep < max_sweeps; ++sweep) {
-    int rot_this_sweep = 0;
-    for (int round = 0; round < N - 1; ++round) {
-      if (t == 0) *active = 0;
-      __syncthreads();
-      for (int i = t; i < half; i += nt) {
-        int a = (i == 0) ? round % (N - 1) : (round + i) % (N - 1);
-        int b = (i == 0) ? N - 1 : (round - i + (N - 1)) % (N - 1);
-        int p = a < b ? a : b, q = a < b ? b : a;
-        double c = 1.0, s = 0.0;
-        if (q < n) {
-          double app = S[p * ld + p], aqq = S[q * ld + q], apq = S[p * ld + q];
-          if (apq != 0.0 && fabs(apq) > tol * sqrt(fabs(app * aqq))) {
-            double tau = (aqq - app) / (2.0 * apq);
-            double tt = (tau >= 0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
-            c = 1.0 / sqrt(1.0 + tt * tt);
-            s = tt * c;
-            atomicAdd(active, 1);
-          }
-        }
-        cs[i] = c; sn[i] = s; pp[i] = p; qq[i] = q;
-      }
-      __syncthreads();
-      int act = *active;
-      if (act) {
-        rot_this_sweep = 1;
-        // S <- J^T S J over 2x2 blocks (pairs a <= b), mirrored; V <- V J.
-        for (int blk = t; blk < half * half; blk += nt) {
-          int a = blk / half, bb = blk % half;
-          if (a > bb) continue;
-          int pa = pp[a], qa = qq[a], pb = pp[bb], qb = qq[bb];
-          if (qa >= n || qb >= n) continue;
-          double ca = cs[a], sa = sn[a], cb = cs[bb], sb = sn[bb];
-          if (sa == 0.0 && sb == 0.0) continue;
-          double x11 = S[pa * ld + pb], x12 = S[pa * ld + qb], x21 = S[qa * ld + pb],
-                 x22 = S[qa * ld + qb];
-          double y11 = ca * x11 - sa * x21, y12 = ca * x12 - sa * x22;
-          double y21 = sa * x11 + ca * x21, y22 = sa * x12 + ca * x22;
-          double z11 = y11 * cb - y12 * sb, z12 = y11 * sb + y12 * cb;
-          double z21 = y21 * cb - y22 * sb, z22 = y21 * sb + y22 * cb;
-          if (a == bb) { z12 = 0.0; z21 = 0.0; }
-          S[pa * ld + pb] = z11; S[pa * ld + qb] = z12; S[qa * ld + pb] = z21; S[qa * ld + qb] = z22;
-          if (a != bb) {
-            S[pb * ld + pa] = z11; S[qb * ld + pa] = z12; S[pb * ld + qa] = z21; S[qb * ld + qa] = z22;
-          }
-        }
-        for (int e = t; e < n * half; e += nt) {
-          int x = e / half, a = e % half;
-          int p = pp[a], q = qq[a];
-          if (q >= n) continue;
-          double c = cs[a], s = sn[a];
-          if (s == 0.0) continue;
-          double vp = V[x * ld + p], vq = V[x * ld + q];
-          V[x * ld + p] = c * vp - s * vq;
-          V[x * ld + q] = s * vp + c * vq;
-        }
-      }
-      __syncthreads();
-    }
-    if (!rot_this_sweep) break;
-  }
-  return sweep;
-}
-
-// ----------------------------------------------------------------------------
 // Residual basis (iS-KV notes §4.1): the residual directions of E^T with
 // singular values rho_j above tau = max(delta s, max(D, b) 2^-23 s),
 // s = max(sigma_1, rho_1), capped at p <= min(b, D - k). Published through
-// V_E (b x b) and rho so that P = E^T V_E diag(1/rho) (make_p_kernel).
+// V_E (b x b, eigenvectors of E E^T by descending eigenvalue) and rho, so that
+// P = E^T V_E diag(1/rho) (make_p_kernel).
 //
-// Fast path: when s = sigma_1 is certain (sigma_1^2 >= trace(E E^T) >= rho_1^2)
-// and every rho_j exceeds tau (Cholesky of E E^T - tau^2 I succeeds: all its
-// eigenvalues are positive), all b directions are kept and any orthonormal
-// basis of span(E^T) yields the same core up to a rotation of its last b
-// columns, hence the same truncated factors. The Cholesky factor L of E E^T
-// gives one: P = E^T L^-T (V_E = L^-T, rho = 1). Otherwise the eigenvectors of
-// E E^T are computed by cyclic Jacobi and thresholded as written.
-// One workgroup of 256 threads.
-__global__ __launch_bounds__(256) void resid_basis_kernel(const double* __restrict__ GE, int b,
-                                                         int D, const float* __restrict__ sigma,
-                                                         float delta, double* VE, double* rho,
-                                                         int32_t* st) {
-  extern __shared__ double smem[];
-  const int ld = b + 1;
-  double* S = smem;
-  double* V = S + b * ld;
-  double* Mx = V + b * ld;
-  double* lam = Mx + b * ld;
-  double* cs = lam + b;
-  double* sn = cs + 32;
-  int* pp = (int*)(sn + 32);
-  int* qq = pp + 32;
-  int* active = qq + 32;
-  int* order = active + 1;
-  __shared__ int any_nonzero, fast_ok;
-  __shared__ double trace;
-  const int t = threadIdx.x, nt = blockDim.x;
-  if (t == 0) { any_nonzero = 0; fast_ok = 1; trace = 0.0; }
-  __syncthreads();
-  for (int idx = t; idx < b * b; idx += nt) {
-    double v = GE[idx];
-    S[(idx / b) * ld + idx % b] = v;
-    if (v != 0.0) any_nonzero = 1;
-  }
-  __syncthreads();
+// The eigendecomposition of the b x b Gram E E^T (b <= 2 HB) is a parallel
+// two-sided Jacobi in the systolic (Brent-Luk) arrangement: thread (I, J) of
+// the HB x HB workgroup owns the 2 x 2 blocks at rows 2I, 2I+1 and columns
+// 2J, 2J+1 of the working matrix S and of the eigenvector matrix V. Each
+// round, every thread computes from the diagonal blocks the rotations of its
+// pairs I and J (the symmetric 2 x 2 Schur rotation of Golub-Van Loan; each
+// rotation is computed by every thread that needs it, from the same data, so
+// all agree), applies S <- J_I^T S J_J and V <- V J_J to its blocks, and
+// writes them to the positions of the next pairing of the round-robin
+// (circle) schedule, so that 2 HB - 1 rounds pair every two indices once (one
+// sweep). S and V are double-buffered in LDS: one barrier per round. Sweeps
+// repeat until none rotates; an off-diagonal is rotated away when it exceeds
+// 1e-13 of the geometric mean of its diagonal pair and 1e-15 of the trace
+// (below that it is at round-off level of the whole Gram). The Gram is
+// zero-padded to 2 HB; padded indices never couple and are dropped.
+// Round-robin move of position x: pairs are (2k, 2k+1); position 0 stays, the
+// others cycle 1 -> 2 -> 4 -> ... -> 2h-2 -> 2h-1 -> 2h-3 -> ... -> 3 -> 1.
+__device__ __forceinline__ int rr_next(int x, int h) {
+  if (x == 0) return 0;
+  if (x == 1) return 2;
+  if ((x & 1) == 0) return x == 2 * (h - 1) ? x + 1 : x + 2;
+  return x - 2;
+}
+
+// Rotation [[c, s], [-s, c]] with J^T [[app, apq], [apq, aqq]] J diagonal:
+// with d = aqq - app, r = sqrt(d^2 + 4 apq^2) and w = |d| + r, the tangent is
+// t = sign(d) 2 apq / w and c = w / sqrt(2 r w), s = t c (2 r w = w^2 + 4 apq^2),
+// which needs one square root and one reciprocal square root. tq = t apq is
+// the shift of the diagonal pair. Below threshold the identity is returned
+// (selected after the arithmetic, so the code has no branch and two calls
+// can be interleaved).
+__device__ __forceinline__ bool schur2(double app, double apq, double aqq, double abs_tol, double& c,
+                                       double& sn, double& tq) {
+  const bool rot = fabs(apq) > abs_tol && apq * apq > 1e-26 * fabs(app * aqq);
+  const double d = aqq - app;
+  const double r = sqrt(fma(d, d, 4.0 * apq * apq));
+  const double w = fabs(d) + r;
+  const double q = rsqrt(2.0 * r * w);
+  const double sg = d >= 0.0 ? 2.0 : -2.0;
+  c = rot ? w * q : 1.0;
+  sn = rot ? sg * apq * q : 0.0;
+  tq = rot ? sg * apq * apq / w : 0.0;
+  return rot;
+}
+
+static inline size_t resid_lds_bytes(int hb) { return (size_t)4 * (2 * hb) * (2 * hb + 1) * sizeof(double); }
+
+template <int HB>
+__global__ __launch_bounds__(HB * HB) void resid_basis_kernel(const double* __restrict__ GE, int b,
+                                                              int D, const float* __restrict__ sigma,
+                                                              float delta, double* VE, double* rho,
+                                                              int32_t* st, int max_sweeps) {
+  constexpr int N = 2 * HB, L = N + 1;
+  extern __shared__ double rb_lds[];
+  double* Sb = rb_lds;              // [2][N][L]
+  double* Vb = rb_lds + 2 * N * L;  // [2][N][L]
+  __shared__ double lam[N];
+  __shared__ int posof[N], order[N];
+  const int t = threadIdx.x, I = t / HB, J = t % HB;
+  const int r0 = 2 * I, r1 = r0 + 1, c0 = 2 * J, c1 = c0 + 1;
+  auto g = [&](int i, int j) { return (i < b && j < b) ? GE[i * b + j] : 0.0; };
+  double x11 = g(r0, c0), x12 = g(r0, c1), x21 = g(r1, c0), x22 = g(r1, c1);
+  const int nonzero = __syncthreads_or(x11 != 0.0 || x12 != 0.0 || x21 != 0.0 || x22 != 0.0);
   const int k = st[ST_K];
-  if (!any_nonzero || k >= D) {
-    if (t == 0) { st[ST_P] = 0; st[ST_M] = k; st[ST_EZERO] = any_nonzero ? 0 : 1; }
+  if (!nonzero || k >= D) {
+    if (t == 0) { st[ST_P] = 0; st[ST_M] = k; st[ST_EZERO] = nonzero ? 0 : 1; }
     return;
   }
-  if (t == 0) {
-    double tr = 0.0;
-    for (int i = 0; i < b; ++i) tr += S[i * ld + i];
-    trace = tr;
-  }
+  Sb[r0 * L + c0] = x11; Sb[r0 * L + c1] = x12; Sb[r1 * L + c0] = x21; Sb[r1 * L + c1] = x22;
+  Vb[r0 * L + c0] = r0 == c0; Vb[r0 * L + c1] = 0.0; Vb[r1 * L + c0] = 0.0; Vb[r1 * L + c1] = r1 == c1;
+  if (I == J) { lam[r0] = x11; lam[r1] = x22; }
   __syncthreads();
-  const double s1 = (k > 0) ? (double)sigma[0] : 0.0;
-  const double floor_scale = (double)(D > b ? D : b) * 1.1920928955078125e-07;
-  bool fast = (k > 0) && (s1 * s1 >= trace) && (b <= D - k) && isfinite(trace);
-  if (fast) {
-    const double tau = fmax((double)delta * s1, floor_scale * s1);
-    // Cholesky of E E^T - tau^2 I in V (lower): succeeds iff every rho_j > tau
-    for (int idx = t; idx < b * b; idx += nt) {
-      int i = idx / b, j = idx % b;
-      V[i * ld + j] = S[i * ld + j] - (i == j ? tau * tau : 0.0);
-    }
-    __syncthreads();
-    for (int c = 0; c < b; ++c) {
-      if (t == 0) {
-        double dcc = V[c * ld + c];
-        if (!(dcc > 0.0)) fast_ok = 0;
-        V[c * ld + c] = sqrt(fmax(dcc, 1e-300));
+  double trace = 0.0;
+  for (int i = 0; i < N; ++i) trace += fabs(lam[i]);
+  const double abs_tol = 1e-15 * trace;
+  int mypos = t;  // threads t < N follow where original index t sits
+  int cur = 0, sweeps = 0;
+  for (int sweep = 0; sweep < max_sweeps; ++sweep) {
+    ++sweeps;
+    int rotated = 0;
+    for (int round = 0; round < N - 1; ++round) {
+      const double* S = Sb + cur * N * L;
+      const double* V = Vb + cur * N * L;
+      // every LDS value of the round is read up front
+      const double ap = S[r0 * L + r0], apq = S[r0 * L + r1], aq = S[r1 * L + r1];
+      const double bp = S[c0 * L + c0], bpq = S[c0 * L + c1], bq = S[c1 * L + c1];
+      x11 = S[r0 * L + c0]; x12 = S[r0 * L + c1]; x21 = S[r1 * L + c0]; x22 = S[r1 * L + c1];
+      double v11 = V[r0 * L + c0], v12 = V[r0 * L + c1], v21 = V[r1 * L + c0], v22 = V[r1 * L + c1];
+      double ca, sa, ta, cb, sb, tb;
+      const bool rot_a = schur2(ap, apq, aq, abs_tol, ca, sa, ta);
+      schur2(bp, bpq, bq, abs_tol, cb, sb, tb);
+      rotated |= rot_a;
+      if (I == J) {
+        if (rot_a) {
+          x11 -= ta;
+          x22 += ta;
+          x12 = 0.0; x21 = 0.0;
+        }
+      } else {  // S <- J_I^T S J_J on this block
+        const double y11 = ca * x11 - sa * x21, y12 = ca * x12 - sa * x22;
+        const double y21 = sa * x11 + ca * x21, y22 = sa * x12 + ca * x22;
+        x11 = y11 * cb - y12 * sb; x12 = y11 * sb + y12 * cb;
+        x21 = y21 * cb - y22 * sb; x22 = y21 * sb + y22 * cb;
       }
-      __syncthreads();
-      const double dc = V[c * ld + c];
-      for (int i = c + 1 + t; i < b; i += nt) V[i * ld + c] /= dc;
-      __syncthreads();
-      for (int idx = t; idx < (b - c - 1) * (b - c - 1); idx += nt) {
-        int i = c + 1 + idx / (b - c - 1), j = c + 1 + idx % (b - c - 1);
-        if (j <= i) V[i * ld + j] -= V[i * ld + c] * V[j * ld + c];
+      {  // V <- V J_J
+        const double w11 = v11 * cb - v12 * sb, w12 = v11 * sb + v12 * cb;
+        const double w21 = v21 * cb - v22 * sb, w22 = v21 * sb + v22 * cb;
+        v11 = w11; v12 = w12; v21 = w21; v22 = w22;
       }
+      // next pairing: S'[pi(i)][pi(j)] = S[i][j], V'[i][pi(j)] = V[i][j]
+      cur ^= 1;
+      double* So = Sb + cur * N * L;
+      double* Vo = Vb + cur * N * L;
+      const int pr0 = rr_next(r0, HB), pr1 = rr_next(r1, HB);
+      const int pc0 = rr_next(c0, HB), pc1 = rr_next(c1, HB);
+      So[pr0 * L + pc0] = x11; So[pr0 * L + pc1] = x12; So[pr1 * L + pc0] = x21; So[pr1 * L + pc1] = x22;
+      Vo[r0 * L + pc0] = v11; Vo[r0 * L + pc1] = v12; Vo[r1 * L + pc0] = v21; Vo[r1 * L + pc1] = v22;
+      if (t < N) mypos = rr_next(mypos, HB);
       __syncthreads();
     }
-    fast = fast_ok != 0;
+    if (!__syncthreads_or(rotated)) break;
   }
-  if (fast) {
-    // L = chol(E E^T) in V (lower), then V_E = L^-T (upper) by columns of L^-1
-    for (int idx = t; idx < b * b; idx += nt) V[(idx / b) * ld + idx % b] = S[(idx / b) * ld + idx % b];
-    __syncthreads();
-    for (int c = 0; c < b; ++c) {
-      if (t == 0) V[c * ld + c] = sqrt(fmax(V[c * ld + c], 1e-300));
-      __syncthreads();
-      const double dc = V[c * ld + c];
-      for (int i = c + 1 + t; i < b; i += nt) V[i * ld + c] /= dc;
-      __syncthreads();
-      for (int idx = t; idx < (b - c - 1) * (b - c - 1); idx += nt) {
-        int i = c + 1 + idx / (b - c - 1), j = c + 1 + idx % (b - c - 1);
-        if (j <= i) V[i * ld + j] -= V[i * ld + c] * V[j * ld + c];
-      }
-      __syncthreads();
-    }
-    // X = L^-1 by forward substitution, one column per thread, into S (E E^T
-    // is no longer needed)
-    for (int j = t; j < b; j += nt) {
-      for (int i = 0; i < b; ++i) {
-        double acc = (i == j) ? 1.0 : 0.0;
-        for (int a = j; a < i; ++a) acc -= V[i * ld + a] * S[a * ld + j];
-        S[i * ld + j] = (i < j) ? 0.0 : acc / V[i * ld + i];
-      }
-    }
-    __syncthreads();
-    // With P0 = E^T L^-T the new block of the core is F P0 = L (lower), so its
-    // Gram is L^T L. A few Jacobi sweeps on L^T L give an exactly orthogonal
-    // R that nearly diagonalises it; P = P0 R keeps the new directions of the
-    // core decoupled (as the singular-vector basis of the notes would), which
-    // the core eigensolver needs. V_E = L^-T R.
-    for (int idx = t; idx < b * b; idx += nt) {
-      int i = idx / b, j = idx % b;
-      double acc = 0.0;
-      for (int a = (i > j ? i : j); a < b; ++a) acc += V[a * ld + i] * V[a * ld + j];
-      Mx[i * ld + j] = acc;
-    }
-    __syncthreads();
-    jacobi_lds(Mx, V, b, ld, 1e-13, 3, cs, sn, pp, qq, active);
-    // V_E[i][j] = sum_a (L^-1)[a][i] R[a][j]
-    for (int idx = t; idx < b * b; idx += nt) {
-      int i = idx / b, j = idx % b;
-      double acc = 0.0;
-      for (int a = i; a < b; ++a) acc += S[a * ld + i] * V[a * ld + j];
-      VE[i * b + j] = acc;
-    }
-    for (int j = t; j < b; j += nt) rho[j] = 1.0;
-    if (t == 0) { st[ST_P] = b; st[ST_M] = k + b; st[ST_EZERO] = 0; }
-    return;
-  }
-  // exact path: eigenvectors of E E^T by cyclic Jacobi
-  jacobi_lds(S, V, b, ld, 1e-13, ISKV_RESID_MAX_SWEEPS, cs, sn, pp, qq, active);
-  for (int i = t; i < b; i += nt) lam[i] = S[i * ld + i];
+  const double* S = Sb + cur * N * L;
+  const double* V = Vb + cur * N * L;
+  // original index j < b sits at position posof[j]
+  if (t < N) posof[t] = mypos;
+  if (t == 0) st[ST_RSWEEPS] = sweeps;
   __syncthreads();
-  // rank by descending eigenvalue, ties by index
-  for (int i = t; i < b; i += nt) {
+  if (t < b) lam[t] = S[posof[t] * L + posof[t]];
+  __syncthreads();
+  // rank by descending eigenvalue, ties by index (NaN last)
+  if (t < b) {
     int rnk = 0;
-    const double ki = rank_key(lam[i]);
+    const double ki = rank_key(lam[t]);
     for (int j = 0; j < b; ++j) {
       const double kj = rank_key(lam[j]);
-      rnk += (kj > ki) || (kj == ki && j < i);
+      rnk += (kj > ki) || (kj == ki && j < t);
     }
-    order[rnk] = i;
+    order[rnk] = t;
   }
   __syncthreads();
-  for (int idx = t; idx < b * b; idx += nt) {
-    int row = idx / b, col = idx % b;
-    VE[row * b + col] = V[row * ld + min(max(order[col], 0), b - 1)];
+  for (int idx = t; idx < b * b; idx += HB * HB) {
+    const int row = idx / b, col = idx % b;
+    VE[row * b + col] = V[row * L + posof[min(max(order[col], 0), b - 1)]];
   }
-  for (int j = t; j < b; j += nt) rho[j] = sqrt(fmax(lam[min(max(order[j], 0), b - 1)], 0.0));
-  __syncthreads();
+  if (t < b) rho[t] = sqrt(fmax(lam[min(max(order[t], 0), b - 1)], 0.0));
   if (t == 0) {
-    double rho1 = sqrt(fmax(lam[min(max(order[0], 0), b - 1)], 0.0));
-    double sc = fmax(s1, rho1);
-    double tau = fmax((double)delta * sc, floor_scale * sc);
+    const double s1 = (k > 0) ? (double)sigma[0] : 0.0;
+    const double floor_scale = (double)(D > b ? D : b) * 1.1920928955078125e-07;
+    const double rho1 = sqrt(fmax(lam[min(max(order[0], 0), b - 1)], 0.0));
+    const double sc = fmax(s1, rho1);
+    const double tau = fmax((double)delta * sc, floor_scale * sc);
     int p = 0;
     for (int j = 0; j < b; ++j) p += sqrt(fmax(lam[min(max(order[j], 0), b - 1)], 0.0)) > tau;
     if (p > D - k) p = D - k;
@@ -844,6 +769,9 @@ int iskv_kernel_setup() {
   static int done = 0;
   if (done) return ISKV_OK;
   const int lds = 160 * 1024;
+  ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)resid_basis_kernel<32>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)resid_lds_bytes(32)));
   ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)xh_mfma_kernel<32>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds));
   ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)xh_mfma_kernel<16>,
@@ -869,12 +797,12 @@ int iskv_launch_merge(isvd_handle* h, const float* F, const int32_t* pos_F, int3
   skinny<true>(h, b, D, w.EB, R, h->B, R, hdim(D), R, -1.f, 1.f, w.E, D, w.E, D);
   // 5. E E^T (fp64) and the residual basis
   hipLaunchKernelGGL(resid_gram_kernel, dim3(b), dim3(256), 0, s, w.E, D, b, w.GE, w.st);
-  {
-    const int ld = b + 1;
-    size_t smem = (size_t)(3 * b * ld + b + 64) * sizeof(double) + (size_t)(32 * 2 + 1 + b) * sizeof(int) + 64;
-    hipLaunchKernelGGL(resid_basis_kernel, dim3(1), dim3(256), smem, s, w.GE, b, D, h->sigma,
-                       c.resid_rel_tol, w.VE, w.rho, w.st);
-  }
+  if (b <= 32)
+    hipLaunchKernelGGL(resid_basis_kernel<16>, dim3(1), dim3(256), resid_lds_bytes(16), s, w.GE, b,
+                       D, h->sigma, c.resid_rel_tol, w.VE, w.rho, w.st, ISKV_RESID_MAX_SWEEPS);
+  else
+    hipLaunchKernelGGL(resid_basis_kernel<32>, dim3(1), dim3(1024), resid_lds_bytes(32), s, w.GE, b,
+                       D, h->sigma, c.resid_rel_tol, w.VE, w.rho, w.st, ISKV_RESID_MAX_SWEEPS);
   hipLaunchKernelGGL(make_p_kernel, dim3((D * c.b_max + 255) / 256), dim3(256), 0, s, w.E, D, b, w.VE,
                      w.rho, w.P, c.b_max, w.st);
   // 6. FP = F P (b x p)
