@@ -172,7 +172,11 @@ void isvd_destroy(isvd_handle* h);
  *               outside 0..n_total-1 is dropped, never written.
  *   head_dim    d_h, even, dividing 128 when D % 128 == 0, else dividing 64.
  *   out         device [n_total x D], bf16 bits (ISKV_OUT_BF16) or fp32
- *               (ISKV_OUT_FP32); fp32 output computes the product in fp32.
+ *               (ISKV_OUT_FP32). fp32 output computes the product in fp32.
+ *               bf16 output rounds C and B to bf16 (round to nearest even)
+ *               and accumulates in fp32 on the matrix cores when
+ *               D % 128 == 0, head_dim is 32, 64 or 128 and r_max % 8 == 0;
+ *               otherwise it computes in fp32 and rounds the result.
  *   stream      hipStream_t as void* (NULL = the handle's stream).
  * Errors: EINVAL. */
 int kv_reconstruct(const isvd_handle* h, const float* X_exact, const int32_t* pos_exact,
