@@ -10,8 +10,6 @@
 namespace {
 
 constexpr int DH = 128;
-constexpr int TILE = 64;
-constexpr int MAXG = 16;
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
@@ -33,138 +31,206 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Split kernel: workgroup (split, g, b) folds rows [split * ROWS, +ROWS) of
+// KV head g for its G query heads into a partial (max m, sum l, output o).
+// Lane l of wave w handles 8 features (chunk l % 16) of row
+// w * 32 + 4 i + l / 16 for i = 0..7; all K and V loads of the workgroup are
+// issued up front and stay in registers as bf16. Logits reduce over the 16
+// lanes of a row; softmax statistics per head over the workgroup's rows;
+// P V accumulates per lane and reduces over lanes and waves through LDS.
 // Partials layout: part[((b * Hq + h) * nsplit + s) * (DH + 2) + {0: m, 1: l, 2..: o}].
+constexpr int ROWS = 128;      // rows per workgroup (4 waves x 32)
+constexpr int HG = 4;          // query heads handled per pass
+
+__device__ __forceinline__ void bf8(const uint4& v, float* f) {
+  f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
+  f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xffff0000u);
+  f[4] = __uint_as_float(v.z << 16); f[5] = __uint_as_float(v.z & 0xffff0000u);
+  f[6] = __uint_as_float(v.w << 16); f[7] = __uint_as_float(v.w & 0xffff0000u);
+}
+
 __global__ __launch_bounds__(256) void attend_split_kernel(const uint16_t* __restrict__ q,
                                                            const uint16_t* __restrict__ K,
                                                            const uint16_t* __restrict__ V, int n,
-                                                           int Hq, int Hkv, float scale,
-                                                           int rows_per_split, float* part) {
+                                                           int Hq, int Hkv, float scale, float* part) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int nsplit = gridDim.x;
   const int G = Hq / Hkv;
-  __shared__ float Ks[TILE][DH + 1];
-  __shared__ float Vs[TILE][DH];
-  __shared__ float qs[MAXG][DH];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  for (int idx = t; idx < G * DH; idx += 256) {
-    int hh = idx / DH, c = idx % DH;
-    qs[hh][c] = bf2f(q[((size_t)b * Hq + g * G + hh) * DH + c]) * scale;
-  }
-  const int r0 = split * rows_per_split;
-  const int r1 = min(n, r0 + rows_per_split);
-  // per-wave running state for heads wave, wave+4, ... (at most 4 per wave)
-  float m_run[MAXG / 4], l_run[MAXG / 4], o0[MAXG / 4], o1[MAXG / 4];
-#pragma unroll
-  for (int u = 0; u < MAXG / 4; ++u) { m_run[u] = -INFINITY; l_run[u] = 0.f; o0[u] = 0.f; o1[u] = 0.f; }
+  const int c = lane & 15, sr = lane >> 4;
+  const int r0 = split * ROWS;
+  __shared__ float logit[HG][ROWS];
+  __shared__ float red[4][HG][DH];
+  __shared__ float stat[HG][2];
   const size_t rstride = (size_t)Hkv * DH;
-  const uint16_t* Kb = K + ((size_t)b * n) * rstride + (size_t)g * DH;
-  const uint16_t* Vb = V + ((size_t)b * n) * rstride + (size_t)g * DH;
-  for (int tr = r0; tr < r1; tr += TILE) {
-    __syncthreads();
-    // 64 rows x 16 chunks of 8 bf16
-    for (int idx = t; idx < TILE * 16; idx += 256) {
-      int rr = idx >> 4, ch = idx & 15;
-      int row = tr + rr;
-      if (row < r1) {
-        uint4 kv = *(const uint4*)(Kb + (size_t)row * rstride + ch * 8);
-        uint4 vv = *(const uint4*)(Vb + (size_t)row * rstride + ch * 8);
-        const uint16_t* kp = (const uint16_t*)&kv;
-        const uint16_t* vp = (const uint16_t*)&vv;
+  const uint16_t* Kb = K + ((size_t)b * n) * rstride + (size_t)g * DH + c * 8;
+  const uint16_t* Vb = V + ((size_t)b * n) * rstride + (size_t)g * DH + c * 8;
+  uint4 kr[8], vr[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { Ks[rr][ch * 8 + e] = bf2f(kp[e]); Vs[rr][ch * 8 + e] = bf2f(vp[e]); }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { Ks[rr][ch * 8 + e] = 0.f; Vs[rr][ch * 8 + e] = 0.f; }
-      }
-    }
-    __syncthreads();
-    const int row = tr + lane;
-#pragma unroll
-    for (int u = 0; u < MAXG / 4; ++u) {
-      const int hh = wave + 4 * u;
-      if (hh >= G) break;
-      float logit = -INFINITY;
-      if (row < r1) {
-        float acc = 0.f;
-#pragma unroll 16
-        for (int c = 0; c < DH; ++c) acc = fmaf(qs[hh][c], Ks[lane][c], acc);
-        logit = acc;
-      }
-      float mt = wave_max(logit);
-      float mnew = fmaxf(m_run[u], mt);
-      float p = (row < r1) ? __expf(logit - mnew) : 0.f;
-      float alpha = (m_run[u] == -INFINITY) ? 0.f : __expf(m_run[u] - mnew);
-      l_run[u] = l_run[u] * alpha + wave_sum(p);
-      float a0 = o0[u] * alpha, a1 = o1[u] * alpha;
-      for (int rr = 0; rr < TILE; ++rr) {
-        float pr = __shfl(p, rr, 64);
-        a0 = fmaf(pr, Vs[rr][lane], a0);
-        a1 = fmaf(pr, Vs[rr][lane + 64], a1);
-      }
-      o0[u] = a0; o1[u] = a1;
-      m_run[u] = mnew;
-    }
+  for (int i = 0; i < 8; ++i) {
+    const int row = min(r0 + wave * 32 + 4 * i + sr, n - 1);
+    kr[i] = *(const uint4*)(Kb + (size_t)row * rstride);
   }
 #pragma unroll
-  for (int u = 0; u < MAXG / 4; ++u) {
-    const int hh = wave + 4 * u;
-    if (hh >= G) break;
-    const int h = g * G + hh;
-    float* dst = part + (((size_t)b * Hq + h) * nsplit + split) * (DH + 2);
-    if (lane == 0) { dst[0] = m_run[u]; dst[1] = l_run[u]; }
-    dst[2 + lane] = o0[u];
-    dst[2 + lane + 64] = o1[u];
+  for (int i = 0; i < 8; ++i) {
+    const int row = min(r0 + wave * 32 + 4 * i + sr, n - 1);
+    vr[i] = *(const uint4*)(Vb + (size_t)row * rstride);
+  }
+  for (int h0 = 0; h0 < G; h0 += HG) {
+    const int hn = min(HG, G - h0);
+    // query chunk of each head of this pass, pre-scaled
+    float qf[HG][8];
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+      const int h = g * G + h0 + min(hh, hn - 1);
+      bf8(*(const uint4*)(q + ((size_t)b * Hq + h) * DH + c * 8), qf[hh]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[hh][e] *= scale;
+    }
+    // logits
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float kf[8];
+      bf8(kr[i], kf);
+      const int rl = wave * 32 + 4 * i + sr;
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh) {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf(qf[hh][e], kf[e], acc);
+        acc += __shfl_xor(acc, 8, 64);
+        acc += __shfl_xor(acc, 4, 64);
+        acc += __shfl_xor(acc, 2, 64);
+        acc += __shfl_xor(acc, 1, 64);
+        if (c == 0) logit[hh][rl] = (r0 + rl < n) ? acc : -INFINITY;
+      }
+    }
+    __syncthreads();
+    // softmax statistics: wave w handles head w of the pass
+    if (wave < hn) {
+      float a = logit[wave][lane], bq = logit[wave][lane + 64];
+      float m = wave_max(fmaxf(a, bq));
+      float pa = (a == -INFINITY) ? 0.f : __expf(a - m);
+      float pb = (bq == -INFINITY) ? 0.f : __expf(bq - m);
+      float l = wave_sum(pa + pb);
+      logit[wave][lane] = pa;
+      logit[wave][lane + 64] = pb;
+      if (lane == 0) { stat[wave][0] = m; stat[wave][1] = l; }
+    }
+    __syncthreads();
+    // P V
+    float acc[HG][8];
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float vf[8];
+      bf8(vr[i], vf);
+      const int rl = wave * 32 + 4 * i + sr;
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh) {
+        const float pr = logit[hh][rl];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(pr, vf[e], acc[hh][e]);
+      }
+    }
+    // reduce over the 4 row lanes of each chunk, then over waves
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float v = acc[hh][e];
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        acc[hh][e] = v;
+      }
+    if (sr == 0) {
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[wave][hh][c * 8 + e] = acc[hh][e];
+    }
+    __syncthreads();
+    for (int idx = t; idx < hn * DH; idx += 256) {
+      const int hh = idx / DH, d = idx % DH;
+      const float o = red[0][hh][d] + red[1][hh][d] + red[2][hh][d] + red[3][hh][d];
+      const int h = g * G + h0 + hh;
+      float* dst = part + (((size_t)b * Hq + h) * nsplit + split) * (DH + 2);
+      dst[2 + d] = o;
+      if (d == 0) { dst[0] = stat[hh][0]; dst[1] = stat[hh][1]; }
+    }
+    __syncthreads();
   }
 }
 
-__global__ __launch_bounds__(128) void attend_combine_kernel(const float* __restrict__ part,
+// Combine: one workgroup per (batch, query head). Split weights
+// w_s = exp(m_s - M) and L = sum w_s l_s are formed in parallel; each wave
+// then sums a quarter of the splits for all 128 features and the quarters are
+// added through LDS.
+__global__ __launch_bounds__(256) void attend_combine_kernel(const float* __restrict__ part,
                                                              int nsplit, uint16_t* out) {
   const int bh = blockIdx.x;
   const float* src = part + (size_t)bh * nsplit * (DH + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, src[s * (DH + 2)]);
-  float L = 0.f, acc = 0.f;
-  const int c = threadIdx.x;
-  for (int s = 0; s < nsplit; ++s) {
-    float ms = src[s * (DH + 2)];
-    if (ms == -INFINITY) continue;
-    float w = __expf(ms - M);
-    L += w * src[s * (DH + 2) + 1];
-    acc += w * src[s * (DH + 2) + 2 + c];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  extern __shared__ float cw[];  // [nsplit] weights
+  __shared__ float redm[4], redl[4];
+  __shared__ float acc4[4][DH];
+  float m = -INFINITY;
+  for (int s = t; s < nsplit; s += 256) m = fmaxf(m, src[(size_t)s * (DH + 2)]);
+  m = wave_max(m);
+  if (lane == 0) redm[wave] = m;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(redm[0], redm[1]), fmaxf(redm[2], redm[3]));
+  float l = 0.f;
+  for (int s = t; s < nsplit; s += 256) {
+    const float ms = src[(size_t)s * (DH + 2)];
+    const float w = (ms == -INFINITY) ? 0.f : __expf(ms - M);
+    cw[s] = w;
+    l += w * src[(size_t)s * (DH + 2) + 1];
   }
-  out[(size_t)bh * DH + c] = f2bf(acc / L);
+  l = wave_sum(l);
+  if (lane == 0) redl[wave] = l;
+  __syncthreads();
+  const float L = redl[0] + redl[1] + redl[2] + redl[3];
+  const int per = (nsplit + 3) / 4;
+  const int s0 = wave * per, s1 = min(nsplit, s0 + per);
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll 8
+  for (int s = s0; s < s1; ++s) {
+    const float w = cw[s];
+    a0 = fmaf(w, src[(size_t)s * (DH + 2) + 2 + lane], a0);
+    a1 = fmaf(w, src[(size_t)s * (DH + 2) + 2 + 64 + lane], a1);
+  }
+  acc4[wave][lane] = a0;
+  acc4[wave][lane + 64] = a1;
+  __syncthreads();
+  if (t < DH) {
+    const float o = acc4[0][t] + acc4[1][t] + acc4[2][t] + acc4[3][t];
+    out[(size_t)bh * DH + t] = f2bf(o / L);
+  }
 }
 
-static int pick_splits(int batch, int n, int Hkv) {
-  int tiles = (n + TILE - 1) / TILE;
-  int want = (2048 + batch * Hkv - 1) / (batch * Hkv);
-  int ns = tiles < want ? tiles : want;
-  return ns < 1 ? 1 : ns;
-}
+static int num_splits(int n) { return (n + ROWS - 1) / ROWS; }
 
 }  // namespace
 
 size_t iskv_attend_ws_bytes(int32_t batch, int32_t n, int32_t Hq, int32_t dh) {
   (void)dh;
-  int ns = pick_splits(batch, n, 1);
-  return (size_t)batch * Hq * ns * (DH + 2) * sizeof(float);
+  return (size_t)batch * Hq * num_splits(n) * (DH + 2) * sizeof(float);
 }
 
 int iskv_launch_attend(const uint16_t* q, const uint16_t* K, const uint16_t* V, int32_t batch,
                        int32_t n, int32_t Hq, int32_t Hkv, int32_t dh, float scale, uint16_t* out,
                        void* ws, size_t ws_bytes, hipStream_t s) {
   (void)dh;
-  int ns = pick_splits(batch, n, Hkv);
-  size_t need = (size_t)batch * Hq * ns * (DH + 2) * sizeof(float);
-  if (ws_bytes < need) return ISKV_EWORKSPACE;
-  int tiles = (n + TILE - 1) / TILE;
-  int tiles_per = (tiles + ns - 1) / ns;
-  int rows_per = tiles_per * TILE;
-  ns = (n + rows_per - 1) / rows_per;
+  const int ns = num_splits(n);
+  if (ws_bytes < iskv_attend_ws_bytes(batch, n, Hq, dh)) return ISKV_EWORKSPACE;
   hipLaunchKernelGGL(attend_split_kernel, dim3(ns, Hkv, batch), dim3(256), 0, s, q, K, V, n, Hq, Hkv,
-                     scale, rows_per, (float*)ws);
-  hipLaunchKernelGGL(attend_combine_kernel, dim3(batch * Hq), dim3(128), 0, s, (const float*)ws, ns,
-                     out);
+                     scale, (float*)ws);
+  hipLaunchKernelGGL(attend_combine_kernel, dim3(batch * Hq), dim3(256), (size_t)ns * sizeof(float), s,
+                     (const float*)ws, ns, out);
   ISKV_HIP_CHECK(hipGetLastError());
   return ISKV_OK;
 }

@@ -575,6 +575,86 @@ __global__ __launch_bounds__(256) void xh_mfma_kernel(const float* X1, int ld1, 
   }
 }
 
+// Same product with H held in registers (kin <= 288, kout <= 256): a
+// 1024-thread workgroup, wave w owns output columns 16w .. 16w+15 and keeps
+// its H slice as the B operand of v_mfma_f32_16x16x4f32 (lane l holds
+// H(4kk + l/16, 16w + l%16) for kk < 72). Workgroups loop over 16-row blocks
+// (block, block + grid, ...); each block's X rows are staged in LDS (double
+// buffered, the next block's loads in flight during the current product)
+// before any of its outputs is written, so in-place use stays safe.
+constexpr int XR_LDX = 292; // LDS row stride (floats) of a staged X block
+
+template <int XR_KS>  // k steps of 4 held per lane: kin <= 4 XR_KS
+__global__ __launch_bounds__(1024) void xh_reg_kernel(const float* X1, int ld1, const float* X2, int ld2,
+                                                      Dim k1_d, Dim kin_d, const float* __restrict__ H,
+                                                      int ldh, int hcols, Dim kout_d, Dim rows_d, float* Y,
+                                                      int ldy, uint16_t* Ybf, int ldbf, int32_t* pos,
+                                                      const int32_t* pos_src) {
+  constexpr int KW = 4 * XR_KS;                // staged columns (zero beyond kin)
+  constexpr int PER = (16 * KW + 1023) / 1024;  // staged elements per thread
+  const int k1 = dval(k1_d), kin = dval(kin_d), kout = dval(kout_d), rows = dval(rows_d);
+  const int nblk = (rows + 15) / 16;
+  if ((int)blockIdx.x >= nblk || kout <= 0 || kin <= 0) return;
+  __shared__ float Xs[2][16 * XR_LDX];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int col = wave * 16 + (lane & 15);
+  float hreg[XR_KS];
+  {
+    const int cc = min(col, hcols - 1);
+    const char* hb = (const char*)H;
+#pragma unroll
+    for (int kk = 0; kk < XR_KS; ++kk) {
+      const int kr = 4 * kk + (lane >> 4);
+      const float v = *(const float*)(hb + 4u * (unsigned)(min(kr, kin - 1) * ldh + cc));
+      hreg[kk] = kr < kin ? v : 0.f;
+    }
+  }
+  // staged element u of this thread: e = t + 1024 u, row e / KW, column e % KW;
+  // every load is issued from a valid address and masked when stored
+  float xr[PER];
+  auto load_x = [&](int blk) {
+    const int i0 = blk * 16;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = min(t + 1024 * u, 16 * KW - 1), r = e / KW, c = e % KW;
+      const int row = min(i0 + r, rows - 1);
+      const float* src = c < k1 ? X1 + (size_t)row * ld1 + c
+                                : (c < kin ? X2 + (size_t)row * ld2 + (c - k1) : X1 + (size_t)row * ld1);
+      xr[u] = *src;
+    }
+  };
+  load_x(blockIdx.x);
+  int buf = 0;
+  for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    float* xs = Xs[buf];
+    const int i0 = blk * 16;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = t + 1024 * u, r = e / KW, c = e % KW;
+      if (e < 16 * KW) xs[r * XR_LDX + c] = (c < kin && i0 + r < rows) ? xr[u] : 0.f;
+    }
+    __syncthreads();
+    if (blk + (int)gridDim.x < nblk) load_x(blk + gridDim.x);
+    v4f_t acc = {0.f, 0.f, 0.f, 0.f};
+    const float* xa = xs + (lane & 15) * XR_LDX + (lane >> 4);
+#pragma unroll
+    for (int kk = 0; kk < XR_KS; ++kk)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[4 * kk], hreg[kk], acc, 0, 0, 0);
+    if (col < kout) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = i0 + 4 * (lane >> 4) + e;
+        if (row < rows) {
+          Y[(size_t)row * ldy + col] = acc[e];
+          if (Ybf) Ybf[(size_t)row * ldbf + col] = f2bf(acc[e]);
+        }
+      }
+    }
+    if (pos && t < 16 && i0 + t < rows) pos[i0 + t] = pos_src[i0 + t];
+    buf ^= 1;
+  }
+}
+
 // Launch Y = [X1 | X2] H over `rows_host` rows (an upper bound when rows_d is
 // a device value); kin_max bounds kin for the LDS layout.
 static void xh_launch(hipStream_t s, int rows_host, const float* X1, int ld1, const float* X2, int ld2,
@@ -582,6 +662,19 @@ static void xh_launch(hipStream_t s, int rows_host, const float* X1, int ld1, co
                       Dim rows, float* Y, int ldy, uint16_t* Ybf, int ldbf, int32_t* pos = nullptr,
                       const int32_t* pos_src = nullptr, bool prefer16 = false) {
   const int ldx = xh_ldx(kin_max);
+  if (kin_max <= 288 && hcols <= 256) {
+    const int nblk = (rows_host + 15) / 16;
+    const int grid = nblk < 256 ? nblk : 256;
+    if (grid > 0) {
+      if (kin_max <= 256)
+        hipLaunchKernelGGL(xh_reg_kernel<64>, dim3(grid), dim3(1024), 0, s, X1, ld1, X2, ld2, k1, kin, H,
+                           ldh, hcols, kout, rows, Y, ldy, Ybf, ldbf, pos, pos_src);
+      else
+        hipLaunchKernelGGL(xh_reg_kernel<72>, dim3(grid), dim3(1024), 0, s, X1, ld1, X2, ld2, k1, kin, H,
+                           ldh, hcols, kout, rows, Y, ldy, Ybf, ldbf, pos, pos_src);
+    }
+    return;
+  }
   if (!prefer16 && xh_lds_bytes(32, kin_max) <= 80 * 1024) {
     hipLaunchKernelGGL(xh_mfma_kernel<32>, dim3((rows_host + 31) / 32), dim3(256),
                        xh_lds_bytes(32, kin_max), s, X1, ld1, X2, ld2, k1, kin, H, ldh, hcols, kout,
