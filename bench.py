@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-graphs", action="store_true",
+                    help="enqueue every kernel directly instead of replaying recorded HIP graphs "
+                         "(same kernels; for kernel-trace profilers)")
     return ap.parse_args()
 
 
@@ -116,7 +119,7 @@ def main():
     for X, st in zip((Xk, Xv), streams):
         with torch.cuda.stream(st):
             p = K.IsvdPath(D=D, r_max=R, b_max=BLK, n_cap=n_rows, reorth_every_rows=256, device=dev,
-                           stream=st)
+                           stream=st, graphs=not args.no_graphs)
             paths.append(p)
             wins.append(K.ExactWindow(p, window=WIN, block=BLK, stream=st))
             Xd.append(torch.from_numpy(X).to(dev))
@@ -179,6 +182,7 @@ def main():
     t0 = time.perf_counter()
     for _ in range(steps):
         step(True)
+    t_issue = time.perf_counter() - t0
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
 
@@ -210,9 +214,10 @@ def main():
         "config": {"workload": "kv stream n=16384 (+decode), D=1024 (8x128), r=256, b=32, w=128, "
                                "K (exp(-i/40)+0.01) and V ((1+i)^-1/2) paths, bf16 RoPE reconstruction, "
                                "GQA 32q/8kv decode", "n_rows_start": N0, "rank": R, "block": BLK,
-                   "window": WIN, "reorth_every_rows": 256},
+                   "window": WIN, "reorth_every_rows": 256, "hip_graphs": not args.no_graphs},
         "reconstructed_GBps": n_mid * D * 2 / (ms["recon_k"] * 1e-3) / 1e9,
         "stage_ms": ms,
+        "host_issue_ms_per_step": t_issue * 1e3 / steps,
         "roofline": {"bound": "hbm", "achieved": recon_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": recon_gbps / HBM_PEAK_GBPS, "traffic": None,
                      "kernel": "kv_reconstruct (K, bf16 + RoPE)",

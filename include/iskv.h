@@ -60,6 +60,11 @@ enum iskv_status {
 #define ISKV_NO_COORD_SYNC 1 /* basis-only ablation (iS-KV notes §2.3): merges
                                 replace the basis but never rewrite the stored
                                 coordinates of old rows */
+#define ISKV_NO_GRAPH 2      /* enqueue every kernel of a merge or
+                                re-orthogonalisation directly. By default, on a
+                                non-null stream, the fixed launch sequence is
+                                recorded once into a HIP graph (per block size)
+                                and replayed; results are the same. */
 
 /* Output dtypes of kv_reconstruct. */
 #define ISKV_OUT_BF16 0
@@ -78,7 +83,7 @@ typedef struct iskv_config {
                                 keep residual direction j when
                                 rho_j > max(delta*s, max(D,b)*2^-23*s),
                                 s = max(sigma_1, rho_1)                                   */
-  int32_t flags;             /* ISKV_NO_COORD_SYNC or 0                                   */
+  int32_t flags;             /* ISKV_NO_COORD_SYNC | ISKV_NO_GRAPH, or 0                  */
 } iskv_config;
 
 typedef struct isvd_handle isvd_handle;

@@ -17,7 +17,7 @@ import ctypes
 import os
 
 __all__ = [
-    "LIB_PATH", "lib", "IskvError", "IskvConfig", "ISKV_NO_COORD_SYNC", "ISKV_OUT_BF16",
+    "LIB_PATH", "lib", "IskvError", "IskvConfig", "ISKV_NO_COORD_SYNC", "ISKV_NO_GRAPH", "ISKV_OUT_BF16",
     "ISKV_OUT_FP32", "ISKV_DEV_NONFINITE", "ISKV_DEV_NOCONV", "EXPORTED_SYMBOLS",
     "isvd_workspace_bytes", "isvd_init", "isvd_merge_block", "isvd_reorth", "isvd_query",
     "isvd_rows", "isvd_destroy", "isvd_query_state", "isvd_sym_eig", "kv_reconstruct",
@@ -36,6 +36,7 @@ if not os.path.exists(LIB_PATH):
 lib = ctypes.CDLL(LIB_PATH)
 
 ISKV_NO_COORD_SYNC = 1
+ISKV_NO_GRAPH = 2
 ISKV_OUT_BF16 = 0
 ISKV_OUT_FP32 = 1
 ISKV_DEV_NONFINITE = 1
@@ -239,10 +240,11 @@ class IsvdPath:
     """One compressed (layer, K-or-V) path: torch tensors + the C handle."""
 
     def __init__(self, D: int, r_max: int, b_max: int, n_cap: int, reorth_every_rows: int = 0,
-                 resid_rel_tol: float = 0.0, sync: bool = True, device="cuda", stream=None):
+                 resid_rel_tol: float = 0.0, sync: bool = True, device="cuda", stream=None,
+                 graphs: bool = True):
         import torch
-        self.cfg = IskvConfig(D, r_max, b_max, n_cap, reorth_every_rows, resid_rel_tol,
-                              0 if sync else ISKV_NO_COORD_SYNC)
+        flags = (0 if sync else ISKV_NO_COORD_SYNC) | (0 if graphs else ISKV_NO_GRAPH)
+        self.cfg = IskvConfig(D, r_max, b_max, n_cap, reorth_every_rows, resid_rel_tol, flags)
         ws = isvd_workspace_bytes(self.cfg)
         if ws == 0:
             raise ValueError("invalid iskv configuration")

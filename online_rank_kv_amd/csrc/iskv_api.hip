@@ -23,7 +23,7 @@ bool cfg_ok(const iskv_config* c) {
   if (c->n_cap < 1) return false;
   if (c->reorth_every_rows < 0) return false;
   if (!(c->resid_rel_tol >= 0.f)) return false;
-  if (c->flags & ~ISKV_NO_COORD_SYNC) return false;
+  if (c->flags & ~(ISKV_NO_COORD_SYNC | ISKV_NO_GRAPH)) return false;
   return true;
 }
 
@@ -73,6 +73,8 @@ size_t carve(const iskv_config* c, char* base, isvd_ws* w) {
   x.GB = (double*)take(R * R * 8);
   x.RB = (double*)take(R * R * 8);
   x.order = (int32_t*)take(M * 4);
+  x.Fs = (float*)take(Bm * D * 4);
+  x.posFs = (int32_t*)take(Bm * 4);
   return off;
 }
 
@@ -176,7 +178,11 @@ int isvd_query(isvd_handle* h, int32_t* n, int32_t* k, int32_t* status) {
   return ISKV_OK;
 }
 
-void isvd_destroy(isvd_handle* h) { delete h; }
+void isvd_destroy(isvd_handle* h) {
+  if (!h) return;
+  iskv_release_graphs(h);
+  delete h;
+}
 
 int isvd_sym_eig(isvd_handle* h, const double* A, int32_t m, double* lam, double* V) {
   if (!h || !A || !lam || !V) return ISKV_EINVAL;

@@ -62,6 +62,8 @@ struct isvd_ws {
   double* GB;         // [r_max x r_max]
   double* RB;         // [r_max x r_max]  Cholesky factor of B^T B
   int32_t* order;     // [m_max]
+  float* Fs;          // [b_max x D]  staged pending block (graph replays read it)
+  int32_t* posFs;     // [b_max]      its positions
   size_t rot_cap;     // doubles in rot
   int gram_splits;
 };
@@ -80,6 +82,12 @@ struct isvd_handle {
   int32_t ldm;         // leading dimension of the fp64 core matrices
   int32_t n_host;      // rows folded (host mirror, exact)
   int32_t folded_host; // folded-row counter (host mirror, exact)
+  // recorded launch sequences (HIP graphs) of a merge and of a reorth
+  hipGraphExec_t g_merge = nullptr;
+  int32_t g_merge_b = 0;
+  const float* g_merge_F = nullptr;      // block pointers the merge graph reads
+  const int32_t* g_merge_posF = nullptr;
+  hipGraphExec_t g_reorth = nullptr;
 };
 
 struct iskv_window {
@@ -110,6 +118,7 @@ void iskv_dgemm(hipStream_t s, int m_max, const double* A, bool ta, const double
                 int mode);
 int iskv_launch_merge(isvd_handle* h, const float* F, const int32_t* pos_F, int32_t b);
 int iskv_launch_reorth(isvd_handle* h);
+void iskv_release_graphs(isvd_handle* h);
 int iskv_launch_sym_eig(isvd_handle* h, const double* A, int32_t m, double* lam, double* V);
 int iskv_launch_reconstruct(const isvd_handle* h, const float* X_exact, const int32_t* pos_exact,
                             int32_t n_exact, int32_t n_total, int32_t head_dim, int32_t apply_rope,

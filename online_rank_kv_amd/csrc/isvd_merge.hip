@@ -221,9 +221,10 @@ __global__ __launch_bounds__(256) void resid_gram_kernel(const float* __restrict
 // the HB x HB workgroup owns the 2 x 2 blocks at rows 2I, 2I+1 and columns
 // 2J, 2J+1 of the working matrix S and of the eigenvector matrix V. Each
 // round, every thread computes from the diagonal blocks the rotations of its
-// pairs I and J (the symmetric 2 x 2 Schur rotation of Golub-Van Loan; each
-// rotation is computed by every thread that needs it, from the same data, so
-// all agree), applies S <- J_I^T S J_J and V <- V J_J to its blocks, and
+// pairs I and J (the symmetric 2 x 2 Schur rotation of Golub-Van Loan, see
+// schur2; each rotation is computed by every thread that needs it, from the
+// same data, so all agree), applies S <- J_I^T S J_J and V <- V J_J to its
+// blocks, and
 // writes them to the positions of the next pairing of the round-robin
 // (circle) schedule, so that 2 HB - 1 rounds pair every two indices once (one
 // sweep). S and V are double-buffered in LDS: one barrier per round. Sweeps
@@ -240,24 +241,30 @@ __device__ __forceinline__ int rr_next(int x, int h) {
   return x - 2;
 }
 
-// Rotation [[c, s], [-s, c]] with J^T [[app, apq], [apq, aqq]] J diagonal:
-// with d = aqq - app, r = sqrt(d^2 + 4 apq^2) and w = |d| + r, the tangent is
-// t = sign(d) 2 apq / w and c = w / sqrt(2 r w), s = t c (2 r w = w^2 + 4 apq^2),
-// which needs one square root and one reciprocal square root. tq = t apq is
-// the shift of the diagonal pair. Below threshold the identity is returned
-// (selected after the arithmetic, so the code has no branch and two calls
-// can be interleaved).
-__device__ __forceinline__ bool schur2(double app, double apq, double aqq, double abs_tol, double& c,
-                                       double& sn, double& tq) {
+// Rotation [[c, s], [-s, c]] with J^T [[app, apq], [apq, aqq]] J (nearly)
+// diagonal. With d = aqq - app, r = sqrt(d^2 + 4 apq^2) and w = |d| + r, the
+// annihilating rotation has c = w / sqrt(2 r w), s = sign(d) 2 apq / sqrt(2 r w).
+// The angle is computed in fp32 on the inputs scaled by 1/trace (so they lie
+// in [1e-15, 1]); (c, s) is then normalised in fp64 by two Newton steps for
+// 1/sqrt(c^2 + s^2), so the rotation is orthogonal to fp64 precision. It
+// leaves an off-diagonal of about 1e-7 of the old one, which later sweeps
+// remove. Below threshold the identity is returned (selected after the
+// arithmetic: no branch).
+__device__ __forceinline__ bool schur2(double app, double apq, double aqq, double abs_tol, double inv_tr,
+                                       double& c, double& sn) {
   const bool rot = fabs(apq) > abs_tol && apq * apq > 1e-26 * fabs(app * aqq);
-  const double d = aqq - app;
-  const double r = sqrt(fma(d, d, 4.0 * apq * apq));
-  const double w = fabs(d) + r;
-  const double q = rsqrt(2.0 * r * w);
-  const double sg = d >= 0.0 ? 2.0 : -2.0;
-  c = rot ? w * q : 1.0;
-  sn = rot ? sg * apq * q : 0.0;
-  tq = rot ? sg * apq * apq / w : 0.0;
+  const float p = (float)(app * inv_tr), q = (float)(aqq * inv_tr), o = (float)(apq * inv_tr);
+  const float d = q - p;
+  const float r = __fsqrt_rn(fmaf(d, d, 4.0f * o * o));
+  const float w = fabsf(d) + r;
+  const float rq = __frsqrt_rn(2.0f * r * w);
+  const double c0 = (double)(w * rq);
+  const double s0 = (double)((d >= 0.0f ? 2.0f : -2.0f) * o * rq);
+  const double n2 = c0 * c0 + s0 * s0;
+  double y = 1.5 - 0.5 * n2;
+  y = y * (1.5 - 0.5 * n2 * y * y);
+  c = rot ? c0 * y : 1.0;
+  sn = rot ? s0 * y : 0.0;
   return rot;
 }
 
@@ -291,8 +298,14 @@ __global__ __launch_bounds__(HB * HB) void resid_basis_kernel(const double* __re
   double trace = 0.0;
   for (int i = 0; i < N; ++i) trace += fabs(lam[i]);
   const double abs_tol = 1e-15 * trace;
+  const double inv_tr = 1.0 / trace;
   int mypos = t;  // threads t < N follow where original index t sits
   int cur = 0, sweeps = 0;
+  const double s1 = (k > 0) ? (double)sigma[0] : 0.0;
+  const double tfac = fmax((double)delta, (double)(D > b ? D : b) * 1.1920928955078125e-07);
+  __shared__ int orig_at[N];
+  __shared__ double wred[3][HB * HB / 64];
+  bool fast = false;
   for (int sweep = 0; sweep < max_sweeps; ++sweep) {
     ++sweeps;
     int rotated = 0;
@@ -304,21 +317,19 @@ __global__ __launch_bounds__(HB * HB) void resid_basis_kernel(const double* __re
       const double bp = S[c0 * L + c0], bpq = S[c0 * L + c1], bq = S[c1 * L + c1];
       x11 = S[r0 * L + c0]; x12 = S[r0 * L + c1]; x21 = S[r1 * L + c0]; x22 = S[r1 * L + c1];
       double v11 = V[r0 * L + c0], v12 = V[r0 * L + c1], v21 = V[r1 * L + c0], v22 = V[r1 * L + c1];
-      double ca, sa, ta, cb, sb, tb;
-      const bool rot_a = schur2(ap, apq, aq, abs_tol, ca, sa, ta);
-      schur2(bp, bpq, bq, abs_tol, cb, sb, tb);
+      double ca, sa, cb, sb;
+      const bool rot_a = schur2(ap, apq, aq, abs_tol, inv_tr, ca, sa);
+      schur2(bp, bpq, bq, abs_tol, inv_tr, cb, sb);
       rotated |= rot_a;
-      if (I == J) {
-        if (rot_a) {
-          x11 -= ta;
-          x22 += ta;
-          x12 = 0.0; x21 = 0.0;
-        }
-      } else {  // S <- J_I^T S J_J on this block
+      {  // S <- J_I^T S J_J on this block
         const double y11 = ca * x11 - sa * x21, y12 = ca * x12 - sa * x22;
         const double y21 = sa * x11 + ca * x21, y22 = sa * x12 + ca * x22;
         x11 = y11 * cb - y12 * sb; x12 = y11 * sb + y12 * cb;
         x21 = y21 * cb - y22 * sb; x22 = y21 * sb + y22 * cb;
+      }
+      if (I == J) {  // keep the diagonal blocks exactly symmetric
+        const double m = 0.5 * (x12 + x21);
+        x12 = m; x21 = m;
       }
       {  // V <- V J_J
         const double w11 = v11 * cb - v12 * sb, w12 = v11 * sb + v12 * cb;
@@ -337,6 +348,58 @@ __global__ __launch_bounds__(HB * HB) void resid_basis_kernel(const double* __re
       __syncthreads();
     }
     if (!__syncthreads_or(rotated)) break;
+    // Early exit when every residual direction is kept (no threshold decision
+    // is close): with S = V^T (E E^T) V nearly diagonal (largest off-diagonal
+    // below 1e-4 of the geometric mean of its diagonal pair) and Gershgorin's
+    // lower bound of its spectrum above tau^2 (tau from the upper bound of
+    // rho_1), p = b and P only has to be an orthonormal basis of span(E^T),
+    // whose choice does not change the merge (the core changes by a rotation
+    // of its last b columns). P = E^T V S^-1/2 is one; its block of the core,
+    // (F P)^T (F P) = S, stays nearly diagonal for the core eigensolver.
+    if (sweep >= 1 && b <= D - k) {
+      if (t < N) orig_at[mypos] = t;
+      __syncthreads();
+      const double* S = Sb + cur * N * L;
+      const double d0 = S[r0 * L + r0], d1 = S[r1 * L + r1], e0 = S[c0 * L + c0], e1 = S[c1 * L + c1];
+      const bool q0 = orig_at[r0] < b, q1 = orig_at[r1] < b, p0 = orig_at[c0] < b, p1 = orig_at[c1] < b;
+      const double y11 = S[r0 * L + c0], y12 = S[r0 * L + c1], y21 = S[r1 * L + c0], y22 = S[r1 * L + c1];
+      double offm = 0.0;
+      auto relo = [&](double v, double da, double db, bool ra, bool cb, bool diag) {
+        return (ra && cb && !diag) ? fabs(v) / sqrt(fabs(da * db)) : 0.0;
+      };
+      offm = fmax(fmax(relo(y11, d0, e0, q0, p0, r0 == c0), relo(y12, d0, e1, q0, p1, r0 == c1)),
+                  fmax(relo(y21, d1, e0, q1, p0, r1 == c0), relo(y22, d1, e1, q1, p1, r1 == c1)));
+      double rs0 = ((p0 && c0 != r0) ? fabs(y11) : 0.0) + ((p1 && c1 != r0) ? fabs(y12) : 0.0);
+      double rs1 = ((p0 && c0 != r1) ? fabs(y21) : 0.0) + ((p1 && c1 != r1) ? fabs(y22) : 0.0);
+#pragma unroll
+      for (int o = 1; o < HB; o <<= 1) {
+        rs0 += __shfl_xor(rs0, o, 64);
+        rs1 += __shfl_xor(rs1, o, 64);
+      }
+      double lo = INFINITY, hi = 0.0;
+      if (J == 0) {
+        if (q0) { lo = fmin(lo, d0 - rs0); hi = fmax(hi, d0 + rs0); }
+        if (q1) { lo = fmin(lo, d1 - rs1); hi = fmax(hi, d1 + rs1); }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        offm = fmax(offm, __shfl_xor(offm, o, 64));
+        lo = fmin(lo, __shfl_xor(lo, o, 64));
+        hi = fmax(hi, __shfl_xor(hi, o, 64));
+      }
+      if ((t & 63) == 0) { wred[0][t >> 6] = offm; wred[1][t >> 6] = lo; wred[2][t >> 6] = hi; }
+      __syncthreads();
+      double om = 0.0, lm = INFINITY, hm = 0.0;
+      for (int w = 0; w < HB * HB / 64; ++w) {
+        om = fmax(om, wred[0][w]);
+        lm = fmin(lm, wred[1][w]);
+        hm = fmax(hm, wred[2][w]);
+      }
+      const double tau_hi = tfac * fmax(s1, sqrt(hm));
+      fast = om < 1e-4 && lm > tau_hi * tau_hi;  // same value in every thread
+      __syncthreads();
+      if (fast) break;
+    }
   }
   const double* S = Sb + cur * N * L;
   const double* V = Vb + cur * N * L;
@@ -344,6 +407,41 @@ __global__ __launch_bounds__(HB * HB) void resid_basis_kernel(const double* __re
   if (t < N) posof[t] = mypos;
   if (t == 0) st[ST_RSWEEPS] = sweeps;
   __syncthreads();
+  if (fast) {
+    // O = D^-1/2 S D^-1/2 - I over the real positions; Z = D^-1/2 (I - O/2 + 3 O^2/8)
+    // approximates S^-1/2 (error 5/16 |O|^3); V_E = V Z, rho = 1.
+    double* Ob = Sb + (cur ^ 1) * N * L;
+    double* Zb = Vb + (cur ^ 1) * N * L;
+    auto rsd = [&](int x) { return orig_at[x] < b ? 1.0 / sqrt(S[x * L + x]) : 0.0; };
+    const double sr0 = rsd(r0), sr1 = rsd(r1), sc0 = rsd(c0), sc1 = rsd(c1);
+    Ob[r0 * L + c0] = r0 == c0 ? 0.0 : S[r0 * L + c0] * sr0 * sc0;
+    Ob[r0 * L + c1] = r0 == c1 ? 0.0 : S[r0 * L + c1] * sr0 * sc1;
+    Ob[r1 * L + c0] = r1 == c0 ? 0.0 : S[r1 * L + c0] * sr1 * sc0;
+    Ob[r1 * L + c1] = r1 == c1 ? 0.0 : S[r1 * L + c1] * sr1 * sc1;
+    __syncthreads();
+    double o11 = 0.0, o12 = 0.0, o21 = 0.0, o22 = 0.0;
+    for (int x = 0; x < N; ++x) {
+      const double a0 = Ob[r0 * L + x], a1 = Ob[r1 * L + x], b0 = Ob[x * L + c0], b1 = Ob[x * L + c1];
+      o11 = fma(a0, b0, o11); o12 = fma(a0, b1, o12); o21 = fma(a1, b0, o21); o22 = fma(a1, b1, o22);
+    }
+    auto zv = [&](int r, int c, double o, double o2, double sr) {
+      return sr * ((r == c ? 1.0 : 0.0) - 0.5 * o + 0.375 * o2);
+    };
+    Zb[r0 * L + c0] = zv(r0, c0, Ob[r0 * L + c0], o11, sr0);
+    Zb[r0 * L + c1] = zv(r0, c1, Ob[r0 * L + c1], o12, sr0);
+    Zb[r1 * L + c0] = zv(r1, c0, Ob[r1 * L + c0], o21, sr1);
+    Zb[r1 * L + c1] = zv(r1, c1, Ob[r1 * L + c1], o22, sr1);
+    __syncthreads();
+    for (int idx = t; idx < b * b; idx += HB * HB) {
+      const int row = idx / b, j = idx % b, pj = posof[j];
+      double acc = 0.0;
+      for (int x = 0; x < N; ++x) acc = fma(V[row * L + x], Zb[x * L + pj], acc);
+      VE[row * b + j] = acc;
+    }
+    if (t < b) rho[t] = 1.0;
+    if (t == 0) { st[ST_P] = b; st[ST_M] = k + b; st[ST_EZERO] = 0; }
+    return;
+  }
   if (t < b) lam[t] = S[posof[t] * L + posof[t]];
   __syncthreads();
   // rank by descending eigenvalue, ties by index (NaN last)
@@ -363,11 +461,8 @@ __global__ __launch_bounds__(HB * HB) void resid_basis_kernel(const double* __re
   }
   if (t < b) rho[t] = sqrt(fmax(lam[min(max(order[t], 0), b - 1)], 0.0));
   if (t == 0) {
-    const double s1 = (k > 0) ? (double)sigma[0] : 0.0;
-    const double floor_scale = (double)(D > b ? D : b) * 1.1920928955078125e-07;
     const double rho1 = sqrt(fmax(lam[min(max(order[0], 0), b - 1)], 0.0));
-    const double sc = fmax(s1, rho1);
-    const double tau = fmax((double)delta * sc, floor_scale * sc);
+    const double tau = tfac * fmax(s1, rho1);
     int p = 0;
     for (int j = 0; j < b; ++j) p += sqrt(fmax(lam[min(max(order[j], 0), b - 1)], 0.0)) > tau;
     if (p > D - k) p = D - k;
@@ -484,8 +579,10 @@ __global__ __launch_bounds__(256) void xh_mfma_kernel(const float* X1, int ld1, 
                                                       Dim k1_d, Dim kin_d, const float* __restrict__ H,
                                                       int ldh, int hcols, Dim kout_d, Dim rows_d,
                                                       float* Y, int ldy, uint16_t* Ybf, int ldbf,
-                                                      int ldx, int32_t* pos, const int32_t* pos_src) {
+                                                      int ldx, int32_t* pos, const int32_t* pos_src,
+                                                      Dim yoff_d) {
   const int k1 = dval(k1_d), kin = dval(kin_d), kout = dval(kout_d), rows = dval(rows_d);
+  const int yo = dval(yoff_d);
   const int i0 = blockIdx.x * BM;
   if (i0 >= rows || kout <= 0) return;
   extern __shared__ float sm[];
@@ -514,7 +611,7 @@ __global__ __launch_bounds__(256) void xh_mfma_kernel(const float* X1, int ld1, 
       }
     }
   }
-  if (pos && t < nr) pos[i0 + t] = pos_src[t + i0];
+  if (pos && t < nr) pos[yo + i0 + t] = pos_src[t + i0];
   constexpr int RB = BM / 16;
   const int nch = (kin + XH_KC - 1) / XH_KC;
   for (int j0 = 0; j0 < kout; j0 += XH_NT) {
@@ -567,8 +664,8 @@ __global__ __launch_bounds__(256) void xh_mfma_kernel(const float* X1, int ld1, 
         for (int e = 0; e < 4; ++e) {
           const int r = a * 16 + 4 * (lane >> 4) + e;
           if (r < nr && j < kout) {
-            Y[(size_t)(i0 + r) * ldy + j] = acc[a][b][e];
-            if (Ybf) Ybf[(size_t)(i0 + r) * ldbf + j] = f2bf(acc[a][b][e]);
+            Y[(size_t)(yo + i0 + r) * ldy + j] = acc[a][b][e];
+            if (Ybf) Ybf[(size_t)(yo + i0 + r) * ldbf + j] = f2bf(acc[a][b][e]);
           }
         }
       }
@@ -589,10 +686,11 @@ __global__ __launch_bounds__(1024) void xh_reg_kernel(const float* X1, int ld1, 
                                                       Dim k1_d, Dim kin_d, const float* __restrict__ H,
                                                       int ldh, int hcols, Dim kout_d, Dim rows_d, float* Y,
                                                       int ldy, uint16_t* Ybf, int ldbf, int32_t* pos,
-                                                      const int32_t* pos_src) {
+                                                      const int32_t* pos_src, Dim yoff_d) {
   constexpr int KW = 4 * XR_KS;                // staged columns (zero beyond kin)
   constexpr int PER = (16 * KW + 1023) / 1024;  // staged elements per thread
   const int k1 = dval(k1_d), kin = dval(kin_d), kout = dval(kout_d), rows = dval(rows_d);
+  const int yo = dval(yoff_d);
   const int nblk = (rows + 15) / 16;
   if ((int)blockIdx.x >= nblk || kout <= 0 || kin <= 0) return;
   __shared__ float Xs[2][16 * XR_LDX];
@@ -645,12 +743,12 @@ __global__ __launch_bounds__(1024) void xh_reg_kernel(const float* X1, int ld1, 
       for (int e = 0; e < 4; ++e) {
         const int row = i0 + 4 * (lane >> 4) + e;
         if (row < rows) {
-          Y[(size_t)row * ldy + col] = acc[e];
-          if (Ybf) Ybf[(size_t)row * ldbf + col] = f2bf(acc[e]);
+          Y[(size_t)(yo + row) * ldy + col] = acc[e];
+          if (Ybf) Ybf[(size_t)(yo + row) * ldbf + col] = f2bf(acc[e]);
         }
       }
     }
-    if (pos && t < 16 && i0 + t < rows) pos[i0 + t] = pos_src[i0 + t];
+    if (pos && t < 16 && i0 + t < rows) pos[yo + i0 + t] = pos_src[i0 + t];
     buf ^= 1;
   }
 }
@@ -660,7 +758,7 @@ __global__ __launch_bounds__(1024) void xh_reg_kernel(const float* X1, int ld1, 
 static void xh_launch(hipStream_t s, int rows_host, const float* X1, int ld1, const float* X2, int ld2,
                       Dim k1, Dim kin, int kin_max, const float* H, int ldh, int hcols, Dim kout,
                       Dim rows, float* Y, int ldy, uint16_t* Ybf, int ldbf, int32_t* pos = nullptr,
-                      const int32_t* pos_src = nullptr, bool prefer16 = false) {
+                      const int32_t* pos_src = nullptr, bool prefer16 = false, Dim yoff = hdim(0)) {
   const int ldx = xh_ldx(kin_max);
   if (kin_max <= 288 && hcols <= 256) {
     const int nblk = (rows_host + 15) / 16;
@@ -668,21 +766,21 @@ static void xh_launch(hipStream_t s, int rows_host, const float* X1, int ld1, co
     if (grid > 0) {
       if (kin_max <= 256)
         hipLaunchKernelGGL(xh_reg_kernel<64>, dim3(grid), dim3(1024), 0, s, X1, ld1, X2, ld2, k1, kin, H,
-                           ldh, hcols, kout, rows, Y, ldy, Ybf, ldbf, pos, pos_src);
+                           ldh, hcols, kout, rows, Y, ldy, Ybf, ldbf, pos, pos_src, yoff);
       else
         hipLaunchKernelGGL(xh_reg_kernel<72>, dim3(grid), dim3(1024), 0, s, X1, ld1, X2, ld2, k1, kin, H,
-                           ldh, hcols, kout, rows, Y, ldy, Ybf, ldbf, pos, pos_src);
+                           ldh, hcols, kout, rows, Y, ldy, Ybf, ldbf, pos, pos_src, yoff);
     }
     return;
   }
   if (!prefer16 && xh_lds_bytes(32, kin_max) <= 80 * 1024) {
     hipLaunchKernelGGL(xh_mfma_kernel<32>, dim3((rows_host + 31) / 32), dim3(256),
                        xh_lds_bytes(32, kin_max), s, X1, ld1, X2, ld2, k1, kin, H, ldh, hcols, kout,
-                       rows, Y, ldy, Ybf, ldbf, ldx, pos, pos_src);
+                       rows, Y, ldy, Ybf, ldbf, ldx, pos, pos_src, yoff);
   } else {
     hipLaunchKernelGGL(xh_mfma_kernel<16>, dim3((rows_host + 15) / 16), dim3(256),
                        xh_lds_bytes(16, kin_max), s, X1, ld1, X2, ld2, k1, kin, H, ldh, hcols, kout,
-                       rows, Y, ldy, Ybf, ldbf, ldx, pos, pos_src);
+                       rows, Y, ldy, Ybf, ldbf, ldx, pos, pos_src, yoff);
   }
 }
 
@@ -708,10 +806,11 @@ __global__ void set_jm_kernel(int32_t* st, int from_slot) { st[ST_JM] = st[from_
 // G_part[s][i][j] = sum_{rows in chunk s} X[r, i] X[r, j]. Grid: (tiles of
 // 16x16 over k x k, chunks). 256 threads.
 __global__ __launch_bounds__(256) void gram_partial_kernel(const float* __restrict__ X, int ldx,
-                                                           int rows, const int32_t* st,
+                                                           Dim rows_d, const int32_t* st,
                                                            double* Gpart, int ldg,
                                                            int rows_per_chunk) {
   const int k = st[ST_K];
+  const int rows = dval(rows_d);
   const int tiles = (k + 15) / 16;
   const int ti = blockIdx.x / tiles, tj = blockIdx.x % tiles;
   if (ti >= tiles) return;
@@ -874,7 +973,10 @@ int iskv_kernel_setup() {
   return ISKV_OK;
 }
 
-int iskv_launch_merge(isvd_handle* h, const float* F, const int32_t* pos_F, int32_t b) {
+// The launch sequence of one merge. It depends on the host only through b
+// and the handle's fixed buffers: the row count n is read on the device, so
+// the sequence can be recorded once and replayed.
+static int merge_body(isvd_handle* h, const float* F, const int32_t* pos_F, int32_t b) {
   const iskv_config& c = h->cfg;
   const isvd_ws& w = h->w;
   hipStream_t s = h->stream;
@@ -912,14 +1014,15 @@ int iskv_launch_merge(isvd_handle* h, const float* F, const int32_t* pos_F, int3
     if (rc) return rc;
   }
   eig_finish(h, 1);
-  // 8. coordinate sync of old rows, new rows, basis update
-  const int n0 = h->n_host;
+  // 8. coordinate sync of old rows (n of them, read on the device), new rows
+  // appended at row n, basis update
   const int M = h->m_max;
-  if (!(c.flags & ISKV_NO_COORD_SYNC) && n0 > 0)
-    xh_launch(s, n0, h->C, R, nullptr, 0, ddim(dk), ddim(dk), R, w.Hc, R, R, ddim(w.st + ST_KNEW),
-              hdim(n0), h->C, R, nullptr, 0);
+  const Dim dn = ddim(w.st + ST_N);
+  if (!(c.flags & ISKV_NO_COORD_SYNC))
+    xh_launch(s, c.n_cap, h->C, R, nullptr, 0, ddim(dk), ddim(dk), R, w.Hc, R, R, ddim(w.st + ST_KNEW),
+              dn, h->C, R, nullptr, 0);
   xh_launch(s, b, w.Q, R, w.FP, c.b_max, ddim(dk), ddim(w.st + ST_M), M, w.Hc, R, R,
-            ddim(w.st + ST_KNEW), hdim(b), h->C + (size_t)n0 * R, R, nullptr, 0, h->pos + n0, pos_F);
+            ddim(w.st + ST_KNEW), hdim(b), h->C, R, nullptr, 0, h->pos, pos_F, false, dn);
   xh_launch(s, D, h->B, R, w.P, c.b_max, ddim(dk), ddim(w.st + ST_M), M, w.Hc, R, R,
             ddim(w.st + ST_KNEW), hdim(D), h->B, R, w.Bbf, R, nullptr, nullptr, true);
   hipLaunchKernelGGL(merge_commit_kernel, dim3(1), dim3(256), 0, s, h->sigma, w.sig_new, w.st, b, R);
@@ -934,22 +1037,24 @@ int iskv_launch_merge(isvd_handle* h, const float* F, const int32_t* pos_F, int3
 // sqrt(Lambda)) and B' = B Z Y (orthonormal), with C' B'^T = C B^T. This is
 // the notes' U <- Q_U W, B <- Q_B V with R_U Sigma R_B^T = W S V^T expressed
 // through M = R_U Sigma R_B^T's right singular vectors.
-int iskv_launch_reorth(isvd_handle* h) {
+// Launch sequence of one re-orthogonalisation; the row count n is read on
+// the device (chunks of C beyond n contribute zero Grams).
+static int reorth_body(isvd_handle* h) {
   const iskv_config& c = h->cfg;
   const isvd_ws& w = h->w;
   hipStream_t s = h->stream;
   const int R = c.r_max, D = c.D, mm = h->m_max, ld = h->ldm;
-  const int n = h->n_host;
-  if (n == 0) return ISKV_OK;
+  const int ncap = c.n_cap;
   const int tiles = (R + 15) / 16;
   const int rows_per_chunk = 1024;
-  int nchunks = (n + rows_per_chunk - 1) / rows_per_chunk;
+  int nchunks = (ncap + rows_per_chunk - 1) / rows_per_chunk;
   if (nchunks > w.gram_splits - 1) nchunks = w.gram_splits - 1;
-  const int rpc = (n + nchunks - 1) / nchunks;
+  const int rpc = (ncap + nchunks - 1) / nchunks;
+  const Dim dn = ddim(w.st + ST_N);
   hipLaunchKernelGGL(set_jm_kernel, dim3(1), dim3(1), 0, s, w.st, (int)ST_K);
-  hipLaunchKernelGGL(gram_partial_kernel, dim3(tiles * tiles, nchunks), dim3(256), 0, s, h->C, R, n,
+  hipLaunchKernelGGL(gram_partial_kernel, dim3(tiles * tiles, nchunks), dim3(256), 0, s, h->C, R, dn,
                      w.st, w.GC, R, rpc);
-  hipLaunchKernelGGL(gram_partial_kernel, dim3(tiles * tiles, 1), dim3(256), 0, s, h->B, R, D, w.st,
+  hipLaunchKernelGGL(gram_partial_kernel, dim3(tiles * tiles, 1), dim3(256), 0, s, h->B, R, hdim(D), w.st,
                      w.GC + (size_t)nchunks * R * R, R, D);
   hipLaunchKernelGGL(reorth_sum_kernel, dim3(128), dim3(256), 0, s, w.GC, nchunks, R, w.Km, w.Pa, w.Pb,
                      ld, w.st);
@@ -972,11 +1077,105 @@ int iskv_launch_reorth(isvd_handle* h) {
   iskv_dgemm(s, mm, w.MB, true, w.W1, false, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 2);
   iskv_dgemm(s, mm, w.Zb, false, w.W1, false, w.Pa, nullptr, ld, 1.0, 0.0, 0.0, st, 2);
   hipLaunchKernelGGL(to_f32_kernel, dim3(128), dim3(256), 0, s, w.T, w.Pa, ld, w.Hc, w.T2, R, w.st);
-  xh_launch(s, n, h->C, R, nullptr, 0, ddim(w.st + ST_K), ddim(w.st + ST_K), R, w.Hc, R, R,
-            ddim(w.st + ST_K), hdim(n), h->C, R, nullptr, 0);
+  xh_launch(s, ncap, h->C, R, nullptr, 0, ddim(w.st + ST_K), ddim(w.st + ST_K), R, w.Hc, R, R,
+            ddim(w.st + ST_K), dn, h->C, R, nullptr, 0);
   xh_launch(s, D, h->B, R, nullptr, 0, ddim(w.st + ST_K), ddim(w.st + ST_K), R, w.T2, R, R,
             ddim(w.st + ST_K), hdim(D), h->B, R, w.Bbf, R, nullptr, nullptr, true);
   hipLaunchKernelGGL(reorth_commit_kernel, dim3(1), dim3(256), 0, s, h->sigma, w.sig_new, w.st, R);
   ISKV_HIP_CHECK(hipGetLastError());
+  return ISKV_OK;
+}
+
+namespace {
+
+// Stage a pending block in the workspace (the recorded merge reads it there).
+__global__ void stage_block_kernel(const float* __restrict__ F, const int32_t* __restrict__ pos_F,
+                                   float* Fs, int32_t* posFs, int count, int b) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) Fs[i] = F[i];
+  if (i < b) posFs[i] = pos_F[i];
+}
+
+bool use_graphs(const isvd_handle* h) {
+  return h->stream != nullptr && !(h->cfg.flags & ISKV_NO_GRAPH);
+}
+
+// Record `body` on the handle's stream into an executable graph.
+template <class Body>
+int record(isvd_handle* h, hipGraphExec_t* exec, Body body) {
+  hipGraph_t g = nullptr;
+  ISKV_HIP_CHECK(hipStreamBeginCapture(h->stream, hipStreamCaptureModeThreadLocal));
+  const int rc = body();
+  const hipError_t ec = hipStreamEndCapture(h->stream, &g);
+  if (rc != ISKV_OK) {
+    if (g) (void)hipGraphDestroy(g);
+    return rc;
+  }
+  if (ec != hipSuccess || !g) return ISKV_EHIP;
+  const hipError_t ei = hipGraphInstantiate(exec, g, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(g);
+  if (ei != hipSuccess) {
+    *exec = nullptr;
+    return ISKV_EHIP;
+  }
+  return ISKV_OK;
+}
+
+}  // namespace
+
+void iskv_release_graphs(isvd_handle* h) {
+  if (h->g_merge) (void)hipGraphExecDestroy(h->g_merge);
+  if (h->g_reorth) (void)hipGraphExecDestroy(h->g_reorth);
+  h->g_merge = nullptr;
+  h->g_reorth = nullptr;
+}
+
+// One merge. Without graphs the sequence is enqueued directly. With graphs,
+// the sequence recorded for (b, block pointers) is replayed; a caller whose
+// block pointers change between calls gets its block staged in the workspace
+// and a sequence recorded once over the staged copy.
+int iskv_launch_merge(isvd_handle* h, const float* F, const int32_t* pos_F, int32_t b) {
+  if (!use_graphs(h)) return merge_body(h, F, pos_F, b);
+  const bool same = h->g_merge && h->g_merge_b == b && h->g_merge_F == F && h->g_merge_posF == pos_F;
+  if (!same) {
+    const float* gF = F;
+    const int32_t* gP = pos_F;
+    if (h->g_merge && h->g_merge_b == b && h->g_merge_F == h->w.Fs) {
+      gF = h->w.Fs;
+      gP = h->w.posFs;
+    } else if (h->g_merge) {
+      // pointers or b changed since the last recording: record over the
+      // staged copy from now on
+      gF = h->w.Fs;
+      gP = h->w.posFs;
+      (void)hipGraphExecDestroy(h->g_merge);
+      h->g_merge = nullptr;
+    }
+    if (gF == h->w.Fs) {
+      const int count = b * h->cfg.D;
+      hipLaunchKernelGGL(stage_block_kernel, dim3((count + 255) / 256), dim3(256), 0, h->stream, F, pos_F,
+                         h->w.Fs, h->w.posFs, count, b);
+      ISKV_HIP_CHECK(hipGetLastError());
+    }
+    if (!h->g_merge) {
+      int rc = record(h, &h->g_merge, [&]() { return merge_body(h, gF, gP, b); });
+      if (rc) return rc;
+      h->g_merge_b = b;
+      h->g_merge_F = gF;
+      h->g_merge_posF = gP;
+    }
+  }
+  ISKV_HIP_CHECK(hipGraphLaunch(h->g_merge, h->stream));
+  return ISKV_OK;
+}
+
+int iskv_launch_reorth(isvd_handle* h) {
+  if (h->n_host == 0) return ISKV_OK;
+  if (!use_graphs(h)) return reorth_body(h);
+  if (!h->g_reorth) {
+    int rc = record(h, &h->g_reorth, [&]() { return reorth_body(h); });
+    if (rc) return rc;
+  }
+  ISKV_HIP_CHECK(hipGraphLaunch(h->g_reorth, h->stream));
   return ISKV_OK;
 }

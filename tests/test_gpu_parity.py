@@ -46,15 +46,25 @@ def gpu_factors(path):
     return C, B, s, pos, st
 
 
-def run_gpu_stream(K, X, b, r, T=0, sync=True, n_cap=None):
+def run_gpu_stream(K, X, b, r, T=0, sync=True, n_cap=None, graphs=False):
+    """Fold X in blocks of b. graphs=True runs the path on its own stream, where
+    merges and re-orthogonalisations are recorded once and replayed as HIP
+    graphs (the way the benchmark runs); otherwise kernels are enqueued one by
+    one on the null stream."""
     n, D = X.shape
-    path = K.IsvdPath(D=D, r_max=r, b_max=b, n_cap=n_cap or n, reorth_every_rows=T, sync=sync,
-                      device=DEV)
     Xd = torch.from_numpy(np.ascontiguousarray(X)).to(DEV)
     pos = torch.arange(n, dtype=torch.int32, device=DEV)
+    stream = None
+    if graphs:
+        torch.cuda.synchronize()  # inputs resident before the path's stream reads them
+        stream = torch.cuda.Stream()
+    path = K.IsvdPath(D=D, r_max=r, b_max=b, n_cap=n_cap or n, reorth_every_rows=T, sync=sync,
+                      device=DEV, stream=stream, graphs=graphs)
     for s in range(0, n, b):
         e = min(n, s + b)
         path.merge(Xd[s:e], pos[s:e])
+    if graphs:
+        stream.synchronize()
     return path
 
 
@@ -128,9 +138,10 @@ def test_pure_rotation_and_zero_blocks(K):
 
 
 def test_kstream_512_merges(K):
-    """Llama-8B-shaped key stream: 16,384 rows, D=1024, r=256, b=32 folded as 512 blocks."""
+    """Llama-8B-shaped key stream: 16,384 rows, D=1024, r=256, b=32 folded as 512 blocks
+    (graph replays, as in the benchmark)."""
     X = synth.kv_stream(synth.CONFIG_KSTREAM)
-    path = run_gpu_stream(K, X, 32, 256)
+    path = run_gpu_stream(K, X, 32, 256, graphs=True)
     C, B, sg, p, st = gpu_factors(path)
     assert st == 0 and C.shape == (16384, 256)
     fac = O.run_stream(X, 32, 256)
@@ -143,6 +154,46 @@ def test_kstream_512_merges(K):
     assert state[11] == 1 and state[12] <= 10
     assert np.abs(B.T @ B - np.eye(256)).max() < 1e-3
     assert np.allclose(sg, fac.sigma, rtol=1e-3)
+
+
+def test_graph_replays_match_eager(K):
+    """Recorded merges / reorths replayed many times, with other work and host
+    synchronisations between replays, give the eager sequence's results after
+    every replay: once with a fixed block buffer (the sequence reads it in
+    place) and once with a new block slice each call (staged copy)."""
+    X = synth.kv_stream(synth.CONFIG_TINY)
+    Xd = torch.from_numpy(X).to(DEV)
+    posd = torch.arange(256, dtype=torch.int32, device=DEV)
+    torch.cuda.synchronize()
+    for fixed_buffer in (True, False):
+        sg, se = torch.cuda.Stream(), torch.cuda.Stream()
+        pg = K.IsvdPath(D=64, r_max=8, b_max=8, n_cap=256, reorth_every_rows=64, device=DEV, stream=sg)
+        pe = K.IsvdPath(D=64, r_max=8, b_max=8, n_cap=256, reorth_every_rows=64, device=DEV, stream=se,
+                        graphs=False)
+        Fbuf = torch.empty((8, 64), dtype=torch.float32, device=DEV)
+        pbuf = torch.empty((8,), dtype=torch.int32, device=DEV)
+        out_g = torch.empty((256, 64), dtype=torch.float32, device=DEV)
+        out_e = torch.empty((256, 64), dtype=torch.float32, device=DEV)
+        for s in range(0, 256, 8):
+            if fixed_buffer:
+                with torch.cuda.stream(sg):
+                    Fbuf.copy_(Xd[s:s + 8])
+                    pbuf.copy_(posd[s:s + 8])
+                pg.merge(Fbuf, pbuf)
+            else:
+                pg.merge(Xd[s:s + 8], posd[s:s + 8])
+            pe.merge(Xd[s:s + 8], posd[s:s + 8])
+            n = s + 8
+            pg.reconstruct(out_g, n, head_dim=64, rope=True)   # other work between replays
+            pe.reconstruct(out_e, n, head_dim=64, rope=True)
+            torch.cuda.synchronize()
+            g = out_g[:n].double().cpu().numpy()
+            e = out_e[:n].double().cpu().numpy()
+            assert np.isfinite(g).all()
+            assert rel(g, e) < 1e-6, (fixed_buffer, s, rel(g, e))
+        assert pg.query() == pe.query()
+        pg.close()
+        pe.close()
 
 
 # --------------------------------------------------------------------------- reorth
@@ -165,7 +216,7 @@ def test_kv_streams_with_reorth_schedule(K):
     """K and V paths (r_K=192, r_V=320, b=64), re-orthogonalised every 16 merges (prefix of 4096 rows)."""
     for spec, r in ((synth.CONFIG_KV_K, 192), (synth.CONFIG_KV_V, 320)):
         X = synth.kv_stream(spec, 4096)
-        path = run_gpu_stream(K, X, 64, r, T=1024)
+        path = run_gpu_stream(K, X, 64, r, T=1024, graphs=True)
         C, B, _, _, st = gpu_factors(path)
         assert st == 0
         ref = O.represented(O.run_stream(X, 64, r, reorth_every_rows=1024))
