@@ -188,6 +188,19 @@ int kv_reconstruct(const isvd_handle* h, const float* X_exact, const int32_t* po
                    int32_t n_exact, int32_t n_total, int32_t head_dim, int32_t apply_rope,
                    float rope_theta, void* out, int32_t out_dtype, void* stream);
 
+/* The exact-row half of kv_reconstruct on its own (Algorithm 3 and §3.2 of
+ * the iS-KV notes): row pos_exact[e] of `out` gets X_exact[e], turned per
+ * head at that position when apply_rope (same convention as kv_reconstruct);
+ * slots with a position outside 0..n_total-1 (e.g. empty window slots, -1)
+ * are skipped. Together with kv_reconstruct(h, NULL, NULL, 0, ...) it writes
+ * exactly what kv_reconstruct with the exact rows writes.
+ *   X_exact device fp32 [n_exact x D]; pos_exact device int32 [n_exact];
+ *   head_dim even and dividing D; out device [n_total x D] of out_dtype.
+ * Errors: EINVAL. */
+int kv_scatter_exact(const float* X_exact, const int32_t* pos_exact, int32_t n_exact, int32_t D,
+                     int32_t n_total, int32_t head_dim, int32_t apply_rope, float rope_theta,
+                     void* out, int32_t out_dtype, void* stream);
+
 /* ---- attention ----------------------------------------------------------- */
 /* Dense GQA decode attention over a reconstructed cache: Algorithm 3 and
  * §2.1 of the iS-KV notes. For every batch row and query head h,

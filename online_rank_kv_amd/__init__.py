@@ -20,7 +20,7 @@ __all__ = [
     "LIB_PATH", "lib", "IskvError", "IskvConfig", "ISKV_NO_COORD_SYNC", "ISKV_NO_GRAPH", "ISKV_OUT_BF16",
     "ISKV_OUT_FP32", "ISKV_DEV_NONFINITE", "ISKV_DEV_NOCONV", "EXPORTED_SYMBOLS",
     "isvd_workspace_bytes", "isvd_init", "isvd_merge_block", "isvd_reorth", "isvd_query",
-    "isvd_rows", "isvd_destroy", "isvd_query_state", "isvd_sym_eig", "kv_reconstruct",
+    "isvd_rows", "isvd_destroy", "isvd_query_state", "isvd_sym_eig", "kv_reconstruct", "kv_scatter_exact",
     "decode_attend_workspace_bytes", "decode_attend", "iskv_window_rows", "iskv_window_init", "iskv_window_protect",
     "iskv_window_append", "iskv_window_exact", "iskv_window_destroy", "iskv_strerror",
     "IsvdPath", "ExactWindow",
@@ -47,7 +47,7 @@ EXPORTED_SYMBOLS = (
     "isvd_rows", "isvd_destroy", "kv_reconstruct", "decode_attend_workspace_bytes",
     "decode_attend", "iskv_window_rows", "iskv_window_init", "iskv_window_protect",
     "iskv_window_append", "iskv_window_exact", "iskv_window_destroy", "iskv_strerror",
-    "isvd_query_state", "isvd_sym_eig",
+    "isvd_query_state", "isvd_sym_eig", "kv_scatter_exact",
 )
 
 
@@ -90,6 +90,8 @@ lib.isvd_destroy.restype = None
 lib.isvd_destroy.argtypes = [_vp]
 lib.kv_reconstruct.restype = ctypes.c_int
 lib.kv_reconstruct.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, ctypes.c_float, _vp, _i32, _vp]
+lib.kv_scatter_exact.restype = ctypes.c_int
+lib.kv_scatter_exact.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _vp, _i32, _vp]
 lib.decode_attend_workspace_bytes.restype = ctypes.c_size_t
 lib.decode_attend_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
 lib.decode_attend.restype = ctypes.c_int
@@ -187,6 +189,13 @@ def kv_reconstruct(h: int, X_exact, pos_exact, n_exact: int, n_total: int, head_
     _check(lib.kv_reconstruct(h, _ptr(X_exact), _ptr(pos_exact), int(n_exact), int(n_total),
                               int(head_dim), int(bool(apply_rope)), float(rope_theta), _ptr(out),
                               int(out_dtype), _stream_ptr(stream)), "kv_reconstruct")
+
+
+def kv_scatter_exact(X_exact, pos_exact, n_exact: int, D: int, n_total: int, head_dim: int,
+                     apply_rope: bool, rope_theta: float, out, out_dtype: int, stream=None) -> None:
+    _check(lib.kv_scatter_exact(_ptr(X_exact), _ptr(pos_exact), int(n_exact), int(D), int(n_total),
+                                int(head_dim), int(bool(apply_rope)), float(rope_theta), _ptr(out),
+                                int(out_dtype), _stream_ptr(stream)), "kv_scatter_exact")
 
 
 def decode_attend_workspace_bytes(batch: int, n: int, Hq: int, dh: int) -> int:

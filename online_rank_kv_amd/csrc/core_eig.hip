@@ -59,107 +59,91 @@ __device__ __forceinline__ double keep_if(double v, bool keep) {
   return __longlong_as_double(__double_as_longlong(v) & -(long long)keep);
 }
 
-// One 32 x 32 output tile per 512-thread workgroup. The whole K panel of
-// both operands (ISKV_DGEMM_KP deep) is staged in LDS with all of its loads
-// in flight together, then 8 waves run the fp64 MFMA chain: waves 0-3 take
-// the four 16 x 16 quadrants over the even 4-deep k steps, waves 4-7 the odd
-// ones, and the two halves are summed through LDS. Matrices have a leading
-// dimension that is a multiple of the panel depth, so every address of a
-// panel lies inside the allocation; entries with k >= m are zeroed (the
-// padding may hold anything), rows and columns >= m are computed and dropped.
-constexpr int KP = ISKV_DGEMM_KP;
-constexpr int SA = KP + 4;  // LDS row stride (doubles) of both staged operands
-constexpr size_t DGEMM_LDS = (size_t)2 * 32 * SA * sizeof(double);
-static_assert(KP % 32 == 0, "panel depth must be a multiple of 32");
+// fp64 GEMM on the matrix cores (v_mfma_f64_16x16x4f64) for the core
+// eigensolver:  C = alpha op(A) op(B) + beta Cin + gamma I  over the m x m
+// leading block (m = st[ST_JM]), op = transpose when TA / TB.
+// One 16 x 16 output tile per 256-thread workgroup; its 4 waves split the
+// depth in chunks of 16 (wave w takes chunks w, w+4, ...), load their
+// operands straight from global memory into registers (no LDS staging), and
+// the four partial tiles are summed through LDS. Inside a chunk, lane l
+// (row or column l%16, group g = l/16) takes depths 16 c + 4 g + q for MFMA
+// step q, so that the operands stored along k are contiguous per lane.
+// Matrices have a leading dimension that is a multiple of 16 and at least
+// m_max rounded up to 16, so every index below that lies in the allocation:
+// the loads of the first chunks are issued before m is read, entries with
+// depth >= m are zeroed, rows and columns >= m are computed and dropped.
+constexpr int DG_CH = 5;  // chunks per wave kept in flight (m <= 320 in one pass)
 
 template <bool TA, bool TB>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void dgemm_kernel(const double* __restrict__ A, int lda,
+__global__ __launch_bounds__(256) void dgemm_kernel(const double* __restrict__ A, int lda,
                                                     const double* __restrict__ B, int ldb, double* C,
                                                     int ldc, const double* Cin, int ldcin,
                                                     double alpha, double beta, double gamma,
-                                                    const int32_t* __restrict__ st, int mode) {
+                                                    const int32_t* __restrict__ st, int mode,
+                                                    int m_max) {
+  const int i0 = blockIdx.y * 16, j0 = blockIdx.x * 16;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int nch_max = (m_max + 15) / 16;
+  double av[DG_CH][4], bv[DG_CH][4];
+  // A(i0 + r, k) and B(k, j0 + r) for k = 16 c + 4 g + q
+  auto load = [&](int u, int c) {
+    const int kb = 16 * c + 4 * g;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      av[u][q] = TA ? A[(size_t)(kb + q) * lda + i0 + r] : A[(size_t)(i0 + r) * lda + kb + q];
+      bv[u][q] = TB ? B[(size_t)(j0 + r) * ldb + kb + q] : B[(size_t)(kb + q) * ldb + j0 + r];
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < DG_CH; ++u)
+    if (wave + 4 * u < nch_max) load(u, wave + 4 * u);
   const int m = st[ST_JM];
-  const int i0 = blockIdx.y * 32, j0 = blockIdx.x * 32;
   if (i0 >= m || j0 >= m) return;
   const bool conv = (st[ST_PCJ] & FLAG_CONV) != 0;
   if (mode == 0 && conv) return;
-  const int t = threadIdx.x;
   if (mode == 1 && conv) {
-    for (int e = t; e < 1024; e += 512) {
-      int i = i0 + (e >> 5), j = j0 + (e & 31);
-      if (i < m && j < m) C[(size_t)i * ldc + j] = Cin[(size_t)i * ldcin + j];
-    }
+    const int i = i0 + (t >> 4), j = j0 + (t & 15);
+    if (i < m && j < m) C[(size_t)i * ldc + j] = Cin[(size_t)i * ldcin + j];
     return;
   }
-  extern __shared__ double dsm[];
-  double* As = dsm;            // As[i][k]: A(i0 + i, k0 + k)
-  double* Bt = dsm + 32 * SA;  // Bt[j][k]: B(k0 + k, j0 + j)
-  const int lane = t & 63, wave = t >> 6;
-  const int q = wave & 3, h = wave >> 2;
-  const int wi = (q >> 1) * 16, wj = (q & 1) * 16;
-  const int c = t & 31, rr = t >> 5;  // 32 lanes along the contiguous index, 16 groups
-  constexpr int NL = KP * 32 / 512;   // loads per thread per operand
-  v4d acc = {0.0, 0.0, 0.0, 0.0};
-  for (int k0 = 0; k0 < m; k0 += KP) {
-    const int kl = min(KP, m - k0);
-    if (k0 > 0) __syncthreads();
-    double ra[NL], rb[NL];
-    // element (row x, depth k) of the tile for load u: contiguous-in-k
-    // operands walk k in 32-wide chunks over two 16-row groups; transposed
-    // ones walk k in steps of 16 with the 32 lanes along the row index
+  const int nch = (m + 15) / 16;
+  v4d acc = {0.0, 0.0, 0.0, 0.0}, acc2 = {0.0, 0.0, 0.0, 0.0};
+  for (int c0 = wave; c0 < nch; c0 += 4 * DG_CH) {
+    if (c0 != wave) {
 #pragma unroll
-    for (int u = 0; u < NL; ++u) {
-      int x, k;
-      if (TA) { x = c; k = rr + 16 * u; } else { x = rr + 16 * (u / (KP / 32)); k = c + 32 * (u % (KP / 32)); }
-      const double* pa = TA ? A + (size_t)(k0 + k) * lda + (i0 + x) : A + (size_t)(i0 + x) * lda + (k0 + k);
-      ra[u] = keep_if(*pa, k < kl);
+      for (int u = 0; u < DG_CH; ++u)
+        if (c0 + 4 * u < nch) load(u, c0 + 4 * u);
     }
 #pragma unroll
-    for (int u = 0; u < NL; ++u) {
-      int x, k;
-      if (!TB) { x = c; k = rr + 16 * u; } else { x = rr + 16 * (u / (KP / 32)); k = c + 32 * (u % (KP / 32)); }
-      const double* pb = TB ? B + (size_t)(j0 + x) * ldb + (k0 + k) : B + (size_t)(k0 + k) * ldb + (j0 + x);
-      rb[u] = keep_if(*pb, k < kl);
-    }
-    // keep the scheduler from interleaving the LDS stores with the loads:
-    // all loads of the panel are issued before the first store waits
-    __builtin_amdgcn_sched_barrier(0);
+    for (int u = 0; u < DG_CH; ++u) {
+      const int c = c0 + 4 * u;
+      if (c < nch) {
+        const int kb = 16 * c + 4 * g;
 #pragma unroll
-    for (int u = 0; u < NL; ++u) {
-      int x, k;
-      if (TA) { x = c; k = rr + 16 * u; } else { x = rr + 16 * (u / (KP / 32)); k = c + 32 * (u % (KP / 32)); }
-      As[x * SA + k] = ra[u];
+        for (int q = 0; q < 4; ++q) {
+          const bool in = kb + q < m;
+          const double a = keep_if(av[u][q], in), bb = keep_if(bv[u][q], in);
+          if (q & 1) acc2 = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bb, acc2, 0, 0, 0);
+          else acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bb, acc, 0, 0, 0);
+        }
+      }
     }
-#pragma unroll
-    for (int u = 0; u < NL; ++u) {
-      int x, k;
-      if (!TB) { x = c; k = rr + 16 * u; } else { x = rr + 16 * (u / (KP / 32)); k = c + 32 * (u % (KP / 32)); }
-      Bt[x * SA + k] = rb[u];
-    }
-    __syncthreads();
-    // MFMA f64 16x16x4: lane l holds A(l%16, l/16) and B(l/16, l%16)
-    const double* ap = As + (wi + (lane & 15)) * SA + (lane >> 4);
-    const double* bp = Bt + (wj + (lane & 15)) * SA + (lane >> 4);
-    for (int kk = 4 * h; kk < kl; kk += 8)
-      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(ap[kk], bp[kk], acc, 0, 0, 0);
   }
-  // sum the two k halves: waves 4-7 hand their quadrant to waves 0-3
-  __syncthreads();
-  double* red = dsm;  // [4 quadrants][4][64]
-  if (h == 1) {
+  acc += acc2;
+  __shared__ double red[3][4][64];
+  if (wave > 0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) red[(q * 4 + e) * 64 + lane] = acc[e];
+    for (int e = 0; e < 4; ++e) red[wave - 1][e][lane] = acc[e];
   }
   __syncthreads();
-  if (h == 1) return;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) acc[e] += red[(q * 4 + e) * 64 + lane];
+  if (wave > 0) return;
   // result lane l, element e is D(l/16 + 4e, l%16)
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    int i = i0 + wi + (lane >> 4) + 4 * e, j = j0 + wj + (lane & 15);
+    const int i = i0 + g + 4 * e, j = j0 + r;
     if (i < m && j < m) {
-      double o = alpha * acc[e];
+      double o = alpha * (acc[e] + red[0][e][lane] + red[1][e][lane] + red[2][e][lane]);
       if (beta != 0.0) o += beta * Cin[(size_t)i * ldcin + j];
       if (i == j) o += gamma;
       C[(size_t)i * ldc + j] = o;
@@ -170,9 +154,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 template <bool TA, bool TB>
 void dgemm(hipStream_t s, int m_max, const double* A, const double* B, double* C, const double* Cin,
            int ld, double alpha, double beta, double gamma, const int32_t* st, int mode) {
-  dim3 grid((m_max + 31) / 32, (m_max + 31) / 32);
-  hipLaunchKernelGGL((dgemm_kernel<TA, TB>), grid, dim3(512), DGEMM_LDS, s, A, ld, B, ld, C, ld, Cin,
-                     ld, alpha, beta, gamma, st, mode);
+  dim3 grid((m_max + 15) / 16, (m_max + 15) / 16);
+  hipLaunchKernelGGL((dgemm_kernel<TA, TB>), grid, dim3(256), 0, s, A, ld, B, ld, C, ld, Cin, ld, alpha,
+                     beta, gamma, st, mode, m_max);
 }
 
 // S = A, W = I, flags cleared.
@@ -637,14 +621,6 @@ void iskv_dgemm(hipStream_t s, int m_max, const double* A, bool ta, const double
 }
 
 int iskv_core_eig_setup() {
-  ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)dgemm_kernel<false, false>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)DGEMM_LDS));
-  ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)dgemm_kernel<true, false>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)DGEMM_LDS));
-  ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)dgemm_kernel<false, true>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)DGEMM_LDS));
-  ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)dgemm_kernel<true, true>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)DGEMM_LDS));
   ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)pcj_analyze_kernel,
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)sizeof(AnalyzeLds)));

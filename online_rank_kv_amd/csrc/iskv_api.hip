@@ -61,7 +61,6 @@ size_t carve(const iskv_config* c, char* base, isvd_ws* w) {
   x.MB = (double*)take(LM * LM * 8);
   x.Zb = (double*)take(LM * LM * 8);
   x.aux = (double*)take(256 * 8 + 4096 * 8);
-  x.part = (float*)take((size_t)16 * Bm * (D > R ? D : R) * 4);
   x.lam = (double*)take(M * 8);
   x.rot_cap = 0;
   x.rot = nullptr;
@@ -206,6 +205,18 @@ int kv_reconstruct(const isvd_handle* h, const float* X_exact, const int32_t* po
   hipStream_t s = stream ? (hipStream_t)stream : h->stream;
   return iskv_launch_reconstruct(h, X_exact, pos_exact, n_exact, n_total, head_dim, apply_rope,
                                  rope_theta, out, out_dtype, s);
+}
+
+int kv_scatter_exact(const float* X_exact, const int32_t* pos_exact, int32_t n_exact, int32_t D,
+                     int32_t n_total, int32_t head_dim, int32_t apply_rope, float rope_theta,
+                     void* out, int32_t out_dtype, void* stream) {
+  if (!out || n_exact < 0 || (n_exact > 0 && (!X_exact || !pos_exact))) return ISKV_EINVAL;
+  if (D < 2 || n_total < 0) return ISKV_EINVAL;
+  if (head_dim < 2 || (head_dim & 1) || D % head_dim != 0) return ISKV_EINVAL;
+  if (out_dtype != ISKV_OUT_BF16 && out_dtype != ISKV_OUT_FP32) return ISKV_EINVAL;
+  if (apply_rope && !(rope_theta > 1.f)) return ISKV_EINVAL;
+  return iskv_launch_exact_rows(X_exact, pos_exact, n_exact, D, n_total, head_dim, apply_rope,
+                                rope_theta, out, out_dtype, (hipStream_t)stream);
 }
 
 size_t decode_attend_workspace_bytes(int32_t batch, int32_t n, int32_t Hq, int32_t dh) {

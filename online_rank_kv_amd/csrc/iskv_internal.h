@@ -52,7 +52,6 @@ struct isvd_ws {
   double* MB;         // [ldm x ldm]  reorth: (B^T B)^(1/2)
   double* Zb;         // [ldm x ldm]  reorth: (B^T B)^(-1/2)
   double* aux;        // [256 doubles + 4096 int pairs] detection results
-  float* part;        // [16 x b_max x max(D, r_max)] split-K partial sums
   double* lam;        // [m_max]
   double* rot;        // [rot_cap] Jacobi rotation log (c, s) pairs
   float* Hc;          // [m_max x r_max]  kept right singular vectors of the core
@@ -120,6 +119,9 @@ int iskv_launch_merge(isvd_handle* h, const float* F, const int32_t* pos_F, int3
 int iskv_launch_reorth(isvd_handle* h);
 void iskv_release_graphs(isvd_handle* h);
 int iskv_launch_sym_eig(isvd_handle* h, const double* A, int32_t m, double* lam, double* V);
+int iskv_launch_exact_rows(const float* X_exact, const int32_t* pos_exact, int32_t n_exact, int32_t D,
+                           int32_t n_total, int32_t head_dim, int32_t apply_rope, float rope_theta,
+                           void* out, int32_t out_dtype, hipStream_t s);
 int iskv_launch_reconstruct(const isvd_handle* h, const float* X_exact, const int32_t* pos_exact,
                             int32_t n_exact, int32_t n_total, int32_t head_dim, int32_t apply_rope,
                             float rope_theta, void* out, int32_t out_dtype, hipStream_t s);

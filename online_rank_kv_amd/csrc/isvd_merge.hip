@@ -124,89 +124,42 @@ static void sgemm(hipStream_t s, int Mmax, int Nmax, const float* A, int lda, co
 }
 
 // ----------------------------------------------------------------------------
-// Skinny products of the merge (M = b rows): partial sums over K chunks on
-// many workgroups, then a deterministic reduction (no float atomics).
-//   part[s][i][j] = sum_{k in chunk s} X[i, k] Y(k, j),  Y(k, j) = TY ? Y[j, k] : Y[k, j]
-// Grid (ceil(Nmax / 32), nsplit, ceil(M / 32)); 256 threads, 2 x 2 outputs each.
-template <bool TY>
-__global__ __launch_bounds__(256) void skinny_partial_kernel(const float* __restrict__ X, int ldx,
-                                                             const float* __restrict__ Y, int ldy,
-                                                             float* part, int ldp, int M, Dim Nd,
-                                                             Dim Kd, int kchunk) {
-  const int N = dval(Nd), K = dval(Kd);
-  const int j0 = blockIdx.x * 32, i0 = blockIdx.z * 32, s = blockIdx.y;
-  if (j0 >= N) return;
-  const int kb = s * kchunk, ke = min(K, kb + kchunk);
-  __shared__ float Xs[32][65];
-  __shared__ float Ys[64][33];
-  const int t = threadIdx.x, tx = t & 15, ty = t >> 4;
-  float acc[2][2] = {};
-  for (int k0 = kb; k0 < ke; k0 += 64) {
-    for (int e = t; e < 2048; e += 256) {
-      int r = e >> 6, c = e & 63;
-      Xs[r][c] = (i0 + r < M && k0 + c < ke) ? X[(size_t)(i0 + r) * ldx + k0 + c] : 0.f;
-    }
-    for (int e = t; e < 2048; e += 256) {
-      int k, c;
-      if (TY) { c = e >> 6; k = e & 63; } else { k = e >> 5; c = e & 31; }
-      float v = 0.f;
-      if (j0 + c < N && k0 + k < ke) v = TY ? Y[(size_t)(j0 + c) * ldy + k0 + k] : Y[(size_t)(k0 + k) * ldy + j0 + c];
-      Ys[k][c] = v;
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < 64; ++kk) {
-      float a0 = Xs[ty * 2][kk], a1 = Xs[ty * 2 + 1][kk];
-      float b0 = Ys[kk][tx * 2], b1 = Ys[kk][tx * 2 + 1];
-      acc[0][0] = fmaf(a0, b0, acc[0][0]); acc[0][1] = fmaf(a0, b1, acc[0][1]);
-      acc[1][0] = fmaf(a1, b0, acc[1][0]); acc[1][1] = fmaf(a1, b1, acc[1][1]);
-    }
-    __syncthreads();
-  }
-  for (int u = 0; u < 2; ++u)
-    for (int v = 0; v < 2; ++v) {
-      int i = i0 + ty * 2 + u, j = j0 + tx * 2 + v;
-      if (i < M && j < N) part[((size_t)s * M + i) * ldp + j] = acc[u][v];
-    }
-}
-
-// out[i, j] = alpha * sum_s part[s][i][j] + beta * Z[i, j]   (Z may alias out)
-__global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restrict__ part, int nsplit,
-                                                            int ldp, int M, Dim Nd, float alpha,
-                                                            float beta, const float* Z, int ldz,
-                                                            float* out, int ldo) {
-  const int N = dval(Nd);
-  const int tot = M * N;
-  for (int e = blockIdx.x * 256 + threadIdx.x; e < tot; e += gridDim.x * 256) {
-    int i = e / N, j = e % N;
-    float acc = 0.f;
-    for (int s = 0; s < nsplit; ++s) acc += part[((size_t)s * M + i) * ldp + j];
-    float o = alpha * acc;
-    if (beta != 0.f) o += beta * Z[(size_t)i * ldz + j];
-    out[(size_t)i * ldo + j] = o;
-  }
-}
-
-// ----------------------------------------------------------------------------
-// Residual Gram E E^T in fp64 (b x b), one workgroup per row i. Also latches
-// the non-finite flag when the block (hence E) holds NaN or Inf.
+// Residual Gram E E^T in fp64 (b x b): workgroup (i, jb) forms row i against
+// rows 8 jb .. 8 jb + 7, each thread over 4 consecutive features (D % 4 == 0),
+// reduced over the wave and the 4 waves. Also latches the non-finite flag when
+// the block (hence E) holds NaN or Inf.
 __global__ __launch_bounds__(256) void resid_gram_kernel(const float* __restrict__ E, int D,
                                                          int b, double* GE, int32_t* st) {
-  const int i = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = blockIdx.x, jb = blockIdx.y * 8;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  double acc[8] = {};
   int bad = 0;
-  for (int j = wave; j < b; j += 4) {
-    double acc = 0.0;
-    for (int d = lane; d < D; d += 64) {
-      float x = E[(size_t)i * D + d], y = E[(size_t)j * D + d];
-      if (j == i && !isfinite(x)) bad = 1;
-      acc = fma((double)x, (double)y, acc);
-    }
+  for (int d = 4 * t; d < D; d += 1024) {
+    const float4 x = *(const float4*)(E + (size_t)i * D + d);
+    if (!(isfinite(x.x) && isfinite(x.y) && isfinite(x.z) && isfinite(x.w))) bad = 1;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-    if (lane == 0) GE[i * b + j] = acc;
+    for (int u = 0; u < 8; ++u) {
+      const int j = min(jb + u, b - 1);
+      const float4 y = *(const float4*)(E + (size_t)j * D + d);
+      double a = acc[u];
+      a = fma((double)x.x, (double)y.x, a);
+      a = fma((double)x.y, (double)y.y, a);
+      a = fma((double)x.z, (double)y.z, a);
+      a = fma((double)x.w, (double)y.w, a);
+      acc[u] = a;
+    }
   }
-  if (bad) atomicOr(&st[ST_STATUS], ISKV_DEV_NONFINITE);
+  __shared__ double red[4][8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    double v = acc[u];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (lane == 0) red[wave][u] = v;
+  }
+  __syncthreads();
+  if (t < 8 && jb + t < b) GE[i * b + jb + t] = red[0][t] + red[1][t] + red[2][t] + red[3][t];
+  if (bad && blockIdx.y == 0) atomicOr(&st[ST_STATUS], ISKV_DEV_NONFINITE);
 }
 
 // ----------------------------------------------------------------------------
@@ -915,24 +868,73 @@ __global__ __launch_bounds__(256) void store_sym_kernel(const double* __restrict
 // Host launchers.
 
 // out (M x N) = alpha * X (M x K) op(Y) + beta * Z, split over K.
+// Skinny products on fp32 MFMA (v_mfma_f32_16x16x4f32), one launch each:
+//   out[i, j] = alpha * sum_k X[i, k] Y'(k, j) + beta * Z[i, j],  i < M (<= 64),
+//   Y'(k, j) = TY ? Y[j, k] : Y[k, j].
+// A workgroup owns one 16 x 16 output block; its 4 waves split K in chunks
+// of 16 (wave w takes chunks w, w+4, ...) and the partial blocks are summed
+// through LDS. Inside a chunk, lane l (row or column l%16, group g = l/16)
+// takes depths 16 s + 4 g + q for MFMA step q: the summation order over k is
+// permuted so that each lane's four operands are consecutive in memory.
+// Depths >= K, rows >= M and columns >= N are masked or dropped.
+template <bool TY>
+__global__ __launch_bounds__(256) void skinny_mfma_kernel(const float* __restrict__ X, int ldx,
+                                                          const float* __restrict__ Y, int ldy, int M,
+                                                          int Nmax, Dim Nd, Dim Kd, float alpha,
+                                                          float beta, const float* Z, int ldz,
+                                                          float* out, int ldo) {
+  const int N = dval(Nd), K = dval(Kd);
+  const int j0 = blockIdx.x * 16, i0 = blockIdx.y * 16;
+  if (j0 >= N) return;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int row = min(i0 + r, M - 1), col = min(j0 + r, Nmax - 1);
+  const float* xr = X + (size_t)row * ldx;
+  v4f_t acc = {0.f, 0.f, 0.f, 0.f};
+  const int nch = (K + 15) / 16;
+#pragma unroll 2
+  for (int c = wave; c < nch; c += 4) {
+    const int kb = c * 16 + 4 * g;
+    float av[4], bv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int k = kb + q, kc = min(k, K - 1);
+      const float a = xr[kc];
+      const float bb = TY ? Y[(size_t)col * ldy + kc] : Y[(size_t)kc * ldy + col];
+      av[q] = k < K ? a : 0.f;
+      bv[q] = k < K ? bb : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], bv[q], acc, 0, 0, 0);
+  }
+  __shared__ float red[3][4][64];
+  if (wave > 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[wave - 1][e][lane] = acc[e];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+  // result lane l, element e: row 4(l/16) + e, column l%16
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float v = acc[e] + red[0][e][lane] + red[1][e][lane] + red[2][e][lane];
+    const int i = i0 + 4 * g + e, j = j0 + r;
+    if (i < M && j < N) {
+      float o = alpha * v;
+      if (beta != 0.f) o += beta * Z[(size_t)i * ldz + j];
+      out[(size_t)i * ldo + j] = o;
+    }
+  }
+}
+
 template <bool TY>
 static void skinny(isvd_handle* h, int M, int Nmax, const float* X, int ldx, const float* Y, int ldy,
                    Dim N, int Kmax, float alpha, float beta, const float* Z, int ldz, float* out,
                    int ldo) {
-  hipStream_t s = h->stream;
   Dim K = TY ? ddim(h->w.st + ST_K) : hdim(Kmax);
-  int nsplit = Kmax / 128;
-  if (nsplit < 1) nsplit = 1;
-  if (nsplit > 16) nsplit = 16;
-  const int kchunk = ((Kmax + nsplit - 1) / nsplit + 63) / 64 * 64;
-  nsplit = (Kmax + kchunk - 1) / kchunk;
-  dim3 grid((Nmax + 31) / 32, nsplit, (M + 31) / 32);
-  hipLaunchKernelGGL((skinny_partial_kernel<TY>), grid, dim3(256), 0, s, X, ldx, Y, ldy, h->w.part, Nmax,
-                     M, N, K, kchunk);
-  int nb = (M * Nmax + 255) / 256;
-  if (nb > 256) nb = 256;
-  hipLaunchKernelGGL(skinny_reduce_kernel, dim3(nb), dim3(256), 0, s, h->w.part, nsplit, Nmax, M, N,
-                     alpha, beta, Z, ldz, out, ldo);
+  dim3 grid((Nmax + 15) / 16, (M + 15) / 16);
+  hipLaunchKernelGGL((skinny_mfma_kernel<TY>), grid, dim3(256), 0, h->stream, X, ldx, Y, ldy, M, Nmax, N,
+                     K, alpha, beta, Z, ldz, out, ldo);
 }
 
 static void eig_finish(isvd_handle* h, int for_merge) {
@@ -991,7 +993,7 @@ static int merge_body(isvd_handle* h, const float* F, const int32_t* pos_F, int3
   skinny<false>(h, b, R, w.E, D, h->B, R, ddim(dk), D, 1.f, 0.f, nullptr, 0, w.EB, R);
   skinny<true>(h, b, D, w.EB, R, h->B, R, hdim(D), R, -1.f, 1.f, w.E, D, w.E, D);
   // 5. E E^T (fp64) and the residual basis
-  hipLaunchKernelGGL(resid_gram_kernel, dim3(b), dim3(256), 0, s, w.E, D, b, w.GE, w.st);
+  hipLaunchKernelGGL(resid_gram_kernel, dim3(b, (b + 7) / 8), dim3(256), 0, s, w.E, D, b, w.GE, w.st);
   if (b <= 32)
     hipLaunchKernelGGL(resid_basis_kernel<16>, dim3(1), dim3(256), resid_lds_bytes(16), s, w.GE, b,
                        D, h->sigma, c.resid_rel_tol, w.VE, w.rho, w.st, ISKV_RESID_MAX_SWEEPS);

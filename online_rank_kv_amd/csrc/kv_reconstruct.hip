@@ -350,6 +350,21 @@ int iskv_launch_reconstruct(const isvd_handle* h, const float* X_exact, const in
   return ISKV_OK;
 }
 
+int iskv_launch_exact_rows(const float* X_exact, const int32_t* pos_exact, int32_t n_exact, int32_t D,
+                           int32_t n_total, int32_t head_dim, int32_t apply_rope, float rope_theta,
+                           void* out, int32_t out_dtype, hipStream_t s) {
+  if (n_exact <= 0) return ISKV_OK;
+  const double lt = log((double)rope_theta);
+  if (out_dtype == ISKV_OUT_BF16)
+    hipLaunchKernelGGL(exact_rows_kernel<true>, dim3(n_exact), dim3(256), 0, s, X_exact, pos_exact, D,
+                       head_dim, apply_rope, lt, out, n_total);
+  else
+    hipLaunchKernelGGL(exact_rows_kernel<false>, dim3(n_exact), dim3(256), 0, s, X_exact, pos_exact, D,
+                       head_dim, apply_rope, lt, out, n_total);
+  ISKV_HIP_CHECK(hipGetLastError());
+  return ISKV_OK;
+}
+
 int iskv_launch_window_move(float* dst_rows, int32_t* dst_pos, const float* src_rows,
                             const int32_t* src_pos, int32_t src_pos_base, int32_t count, int32_t D,
                             hipStream_t s) {

@@ -276,6 +276,12 @@ def test_reconstruct_rope_and_exact_rows(K):
         gb = out.double().cpu().numpy()
         assert rel(gb, O.bf16_round(ref)) < 5e-3
         assert rel(gb, ref) < 5e-3
+        # the same output from the compressed rows alone plus the exact-row scatter
+        out2 = torch.full((n_total, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+        path.reconstruct(out2, n_total, head_dim=hd, rope=rope)
+        K.kv_scatter_exact(Xed, ped, Xed.shape[0], D, n_total, hd, rope, theta, out2, K.ISKV_OUT_BF16)
+        torch.cuda.synchronize()
+        assert torch.equal(out2, out)
 
 
 def test_reconstruct_high_positions_rope(K):
