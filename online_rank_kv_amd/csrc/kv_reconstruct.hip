@@ -5,6 +5,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace {
 
 __device__ __forceinline__ uint16_t f2bf(float f) {
@@ -28,6 +30,29 @@ __device__ __forceinline__ void rope_cs(int pos, double inv_freq, float* c, floa
   double phi = (double)pos * inv_freq;
   double red = phi - two_pi * rint(phi / two_pi);
   sincosf((float)red, s, c);
+}
+
+// Two fp32 values to packed bf16 (round to nearest even) with one
+// v_cvt_pk_bf16_f32.
+typedef float f2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{a, b}, bf2_t));
+}
+
+// RoPE angle in revolutions for the bf16 paths: f = theta^(-2j/dh) / (2 pi)
+// is held as a 64-bit binary fraction F (f < 1/2); the fractional part of
+// pos * f is then the top 32 bits of pos * F mod 2^64, read as a signed
+// fraction in [-1/2, 1/2). Exact integer arithmetic: the only errors are F's
+// rounding (2^-54 relative) and the final 2^-32 truncation, for any position
+// below 2^31.
+__device__ __forceinline__ uint64_t rope_fraction(double rev_per_pos) {
+  return (uint64_t)(rev_per_pos * 18446744073709551616.0);  // * 2^64
+}
+__device__ __forceinline__ float rope_rev(uint32_t p, uint64_t F) {
+  const uint32_t flo = (uint32_t)F, fhi = (uint32_t)(F >> 32);
+  const uint32_t top = p * fhi + __umulhi(p, flo);
+  return (float)(int32_t)top * 2.3283064365386963e-10f;  // * 2^-32
 }
 
 // Column tile of W (128 or 64) features; rotary pair q (0 .. W/2-1) of the
@@ -272,6 +297,171 @@ __global__ __launch_bounds__(256) void recon_mfma_kernel(const float* __restrict
   }
 }
 
+// Streaming form of the bf16 MFMA reconstruction for k <= 256 (r_max a
+// multiple of 32, at most 256): each workgroup keeps one 128-feature tile of
+// B^T in registers for the whole launch (wave w holds the MFMA B operands of
+// its two 16-feature blocks, the "lo" block and the one half a head further,
+// for every k step) and streams 32-row blocks of C through LDS: the next
+// block's loads are in flight while the current block is multiplied, rotated
+// (RoPE in registers, as above) and written through an LDS tile with 16-byte
+// stores. Workgroup w serves feature tile (w / 8) % T and row blocks
+// rs, rs + S, ... with rs = w % 8 + 8 (w / 8T): the T tiles of a row block run
+// on the same XCD and share its L2 copy of the C rows.
+constexpr int RS_BM = 32;            // rows per block
+constexpr int RS_CS = 256 + 8;       // LDS row stride (bf16) of a staged C block
+constexpr int RS_OS = 128 + 8;       // LDS row stride (bf16) of the output block
+
+__global__ __launch_bounds__(256) void recon_stream_kernel(const float* __restrict__ C, int ldc,
+                                                           const uint16_t* __restrict__ Bbf, int ldb,
+                                                           const int32_t* __restrict__ pos,
+                                                           const int32_t* __restrict__ st, int n, int D,
+                                                           int dh, int apply_rope, double log_theta,
+                                                           uint16_t* out, int n_total, int T, int S) {
+  const int kdev = st[ST_K];
+  const int wg = blockIdx.x;
+  const int ct = (wg / 8) % T, rs = wg % 8 + 8 * (wg / (8 * T));
+  const int c0 = ct * 128;
+  const int nblk = (n + RS_BM - 1) / RS_BM;
+  if (rs >= nblk) return;
+  __shared__ __attribute__((aligned(16))) uint16_t Cs[2][RS_BM * RS_CS];
+  __shared__ __attribute__((aligned(16))) uint16_t Os[RS_BM * RS_OS];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int half = dh >> 1;
+  const int ks = (kdev + 31) / 32;
+  // this wave's "lo" block (the wave-th block with (16 b) % dh < dh/2) and its partner
+  int lob = 0;
+  {
+    int cnt = 0;
+    for (int b = 0; b < 8; ++b)
+      if ((b * 16) % dh < half) {
+        if (cnt == wave) lob = b;
+        ++cnt;
+      }
+  }
+  const int blk0 = lob, blk1 = lob + half / 16;
+  // B operands: lane holds B(feature 16 blk + l%16, k 32 s + 8 (l/16) .. +7)
+  uint4 breg[2][8];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int f = c0 + 16 * (cb ? blk1 : blk0) + (lane & 15);
+#pragma unroll
+    for (int sk = 0; sk < 8; ++sk) {
+      const int kk = 32 * sk + 8 * (lane >> 4);
+      uint4 v = *(const uint4*)(Bbf + (size_t)f * ldb + min(kk, ldb - 8));
+      if (kk + 8 > kdev) {  // zero depths >= k
+        uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (kk + q >= kdev) wv[q >> 1] &= (q & 1) ? 0x0000ffffu : 0xffff0000u;
+        v = uint4{wv[0], wv[1], wv[2], wv[3]};
+      }
+      breg[cb][sk] = v;
+    }
+  }
+  const int flo = 16 * blk0 + (lane & 15);  // tile-local feature of the lo member
+  const uint64_t rope_F =
+      rope_fraction(exp(-(2.0 * (flo % dh) / dh) * log_theta) * 0.15915494309189533577);
+  // C block staging: element u of this thread is row (t + 256 u) / 64,
+  // columns 4 ((t + 256 u) % 64) .. +3; thread t < 32 also carries row t's
+  // position. Loads run two blocks ahead (a ring of two register sets).
+  __shared__ int posS[2][RS_BM];
+  float4 creg[2][8];
+  int preg[2];
+  auto load_c = [&](int slot, int blk) {
+    const int i0 = blk * RS_BM;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = t + 256 * u, r = e >> 6, c4 = (e & 63) * 4;
+      const int row = min(i0 + r, n - 1);
+      creg[slot][u] = *(const float4*)(C + (size_t)row * ldc + min(c4, ldc - 4));
+    }
+    preg[slot] = pos[min(i0 + (t & 31), n - 1)];
+  };
+  auto store_c = [&](int slot, uint16_t* cs, int* ps, int blk) {
+    const int i0 = blk * RS_BM;
+    if (i0 + RS_BM <= n && kdev >= ldc) {  // full block: nothing to mask
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = t + 256 * u, r = e >> 6, c4 = (e & 63) * 4;
+        const float4 v = creg[slot][u];
+        *(uint2*)(cs + r * RS_CS + c4) = uint2{pk_bf16(v.x, v.y), pk_bf16(v.z, v.w)};
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = t + 256 * u, r = e >> 6, c4 = (e & 63) * 4;
+        const bool rv = i0 + r < n;
+        const float4 v = creg[slot][u];
+        const float x0 = (rv && c4 < kdev) ? v.x : 0.f, x1 = (rv && c4 + 1 < kdev) ? v.y : 0.f;
+        const float x2 = (rv && c4 + 2 < kdev) ? v.z : 0.f, x3 = (rv && c4 + 3 < kdev) ? v.w : 0.f;
+        *(uint2*)(cs + r * RS_CS + c4) = uint2{pk_bf16(x0, x1), pk_bf16(x2, x3)};
+      }
+    }
+    if (t < RS_BM) ps[t] = (i0 + t < n) ? preg[slot] : -1;
+  };
+  // one block through the pipeline; `slot` is a compile-time constant at each
+  // call, so the register ring is never indexed at run time
+  auto process = [&](auto slot_c, int blk) {
+    constexpr int slot = decltype(slot_c)::value;
+    uint16_t* cs = Cs[slot];
+    int* ps = posS[slot];
+    store_c(slot, cs, ps, blk);
+    __syncthreads();
+    if (blk + 2 * S < nblk) load_c(slot, blk + 2 * S);
+    v4f acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) acc[a][cb] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sk = 0; sk < 8; ++sk) {
+      if (sk < ks) {
+        const int ko = 32 * sk + 8 * (lane >> 4);
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          const v8bf av = __builtin_bit_cast(v8bf, *(const uint4*)(cs + (16 * a + (lane & 15)) * RS_CS + ko));
+          acc[a][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(v8bf, breg[0][sk]),
+                                                              acc[a][0], 0, 0, 0);
+          acc[a][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(v8bf, breg[1][sk]),
+                                                              acc[a][1], 0, 0, 0);
+        }
+      }
+    }
+    // epilogue: lane l, element e holds row 4(l/16) + e of each 16-row half a
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rl = 16 * a + 4 * (lane >> 4) + e;
+        float x = acc[a][0][e], y = acc[a][1][e];
+        if (apply_rope) {
+          const float rr = rope_rev((uint32_t)ps[rl], rope_F);
+          const float c = __builtin_amdgcn_cosf(rr), sn = __builtin_amdgcn_sinf(rr);
+          const float xr = x * c - y * sn, yr = y * c + x * sn;
+          x = xr; y = yr;
+        }
+        const uint32_t xy = pk_bf16(x, y);
+        Os[rl * RS_OS + flo] = (uint16_t)xy;
+        Os[rl * RS_OS + flo + half] = (uint16_t)(xy >> 16);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = t + 256 * u, r = e >> 4, cc = (e & 15) * 8;
+      const int p = ps[r];
+      if (p >= 0 && p < n_total)  // rows past n and positions outside the output: dropped
+        *(uint4*)(out + (size_t)p * D + c0 + cc) = *(const uint4*)(Os + r * RS_OS + cc);
+    }
+  };
+  load_c(0, rs);
+  if (rs + S < nblk) load_c(1, rs + S);
+  for (int blk = rs; blk < nblk; blk += 2 * S) {
+    process(std::integral_constant<int, 0>{}, blk);
+    if (blk + S < nblk) process(std::integral_constant<int, 1>{}, blk + S);
+  }
+}
+
 // Exact rows: out[pos_e] = RoPE(X_exact[e]); slots with pos_e < 0 are empty.
 // Grid (n_exact), 64 threads x pairs.
 template <bool BF16>
@@ -325,7 +515,13 @@ int iskv_launch_reconstruct(const isvd_handle* h, const float* X_exact, const in
     dim3 grid(D / W, (n + 31) / 32);
     const bool mfma = bf && D % RM_BN == 0 && head_dim % 32 == 0 && RM_BN % head_dim == 0 &&
                       R % 8 == 0;
-    if (mfma) {
+    if (mfma && R % 32 == 0 && R <= 256) {
+      const int T = D / 128;
+      const int G = T >= 64 ? 1 : 64 / T;  // 512 workgroups when T divides 64
+      hipLaunchKernelGGL(recon_stream_kernel, dim3(8 * T * G), dim3(256), 0, s, h->C, R, h->w.Bbf, R,
+                         h->pos, h->w.st, n, D, head_dim, apply_rope, lt, (uint16_t*)out, n_total, T,
+                         8 * G);
+    } else if (mfma) {
       const int tiles = D / RM_BN, nrb = (n + RM_BM - 1) / RM_BM;
       const int nwg = (nrb + 7) / 8 * 8 * tiles;
       hipLaunchKernelGGL(recon_mfma_kernel, dim3(nwg), dim3(256), 0, s, h->C, R, h->w.Bbf, R,

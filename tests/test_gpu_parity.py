@@ -299,6 +299,19 @@ def test_reconstruct_high_positions_rope(K):
     got = out[65520:].double().cpu().numpy()
     ref = O.rope(C @ B.T, pos, hd, 500000.0)
     assert rel(got, ref) < 2e-6
+    # bf16 output (matrix-core path, fixed-point angles) at the same positions,
+    # and far beyond them (positions near 2^20)
+    for base in (65520, (1 << 20) - 16):
+        p2 = np.arange(base, base + 16).astype(np.int32)
+        path2 = K.IsvdPath(D=D, r_max=32, b_max=16, n_cap=16, device=DEV)
+        path2.merge(torch.from_numpy(X).to(DEV), torch.from_numpy(p2).to(DEV))
+        C2, B2, _, pos2, _ = gpu_factors(path2)
+        ob = torch.zeros((base + 16, D), dtype=torch.bfloat16, device=DEV)
+        path2.reconstruct(ob, base + 16, head_dim=hd, rope=True)
+        torch.cuda.synchronize()
+        gb = ob[base:].double().cpu().numpy()
+        refb = O.rope(C2 @ B2.T, pos2, hd, 500000.0)
+        assert rel(gb, refb) < 5e-3, (base, rel(gb, refb))
 
 
 # --------------------------------------------------------------------------- attention
