@@ -124,6 +124,22 @@ int isvd_init(isvd_handle** out, const iskv_config* cfg, float* C, float* sigma,
  * (ISKV_DEV_NONFINITE / ISKV_DEV_NOCONV, read by isvd_query). */
 int isvd_merge_block(isvd_handle* h, const float* F, const int32_t* pos_F, int32_t b);
 
+/* One merge on each of `count` paths in a single launch sequence (the
+ * data-parallel form of isvd_merge_block for many independent (sequence,
+ * layer, K/V) paths, iS-KV notes §2.2 and Algorithm 2): block z is
+ * F + z * F_stride (device fp32 [b x D]) with positions pos_F + z * pos_stride
+ * (device int32 [b]); every kernel of the merge runs once over all paths.
+ * Requirements: 1 <= count <= 4096; the handles are distinct, were created
+ * with identical configurations and the same stream, and share one buffer
+ * layout: each handle's C, sigma, B, pos and workspace lie at one common byte
+ * offset from handle 0's (e.g. all carved from one allocation with a fixed
+ * per-path stride). F_stride >= b * D, pos_stride >= b. Results equal `count`
+ * separate isvd_merge_block calls; paths that cross the re-orthogonalisation
+ * schedule together are re-orthogonalised in one batched sequence too.
+ * Errors: EINVAL (requirements), ECAPACITY (n + b > n_cap for a path). */
+int isvd_merge_block_batched(isvd_handle* const* hs, int32_t count, const float* F, int64_t F_stride,
+                             const int32_t* pos_F, int64_t pos_stride, int32_t b);
+
 /* Re-orthogonalise the factors: iS-KV notes §4.4. Equivalent to the notes'
  * thin QR of U and B and SVD of R_U diag(sigma) R_B^T: the product C B^T is
  * kept, B becomes orthonormal and C's columns orthogonal with norms sigma.

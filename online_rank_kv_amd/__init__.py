@@ -23,7 +23,7 @@ __all__ = [
     "isvd_rows", "isvd_destroy", "isvd_query_state", "isvd_sym_eig", "kv_reconstruct", "kv_scatter_exact",
     "decode_attend_workspace_bytes", "decode_attend", "iskv_window_rows", "iskv_window_init", "iskv_window_protect",
     "iskv_window_append", "iskv_window_exact", "iskv_window_destroy", "iskv_strerror",
-    "IsvdPath", "ExactWindow",
+    "isvd_merge_block_batched", "IsvdPath", "IsvdBatch", "ExactWindow",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libiskv.so")
@@ -47,7 +47,7 @@ EXPORTED_SYMBOLS = (
     "isvd_rows", "isvd_destroy", "kv_reconstruct", "decode_attend_workspace_bytes",
     "decode_attend", "iskv_window_rows", "iskv_window_init", "iskv_window_protect",
     "iskv_window_append", "iskv_window_exact", "iskv_window_destroy", "iskv_strerror",
-    "isvd_query_state", "isvd_sym_eig", "kv_scatter_exact",
+    "isvd_query_state", "isvd_sym_eig", "kv_scatter_exact", "isvd_merge_block_batched",
 )
 
 
@@ -76,6 +76,9 @@ lib.isvd_init.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(IskvConfig), _vp, 
                           ctypes.c_size_t, _vp]
 lib.isvd_merge_block.restype = ctypes.c_int
 lib.isvd_merge_block.argtypes = [_vp, _vp, _vp, _i32]
+lib.isvd_merge_block_batched.restype = ctypes.c_int
+lib.isvd_merge_block_batched.argtypes = [ctypes.POINTER(_vp), _i32, _vp, ctypes.c_int64, _vp, ctypes.c_int64,
+                                         _i32]
 lib.isvd_reorth.restype = ctypes.c_int
 lib.isvd_reorth.argtypes = [_vp]
 lib.isvd_query.restype = ctypes.c_int
@@ -154,6 +157,12 @@ def isvd_init(cfg: IskvConfig, C, sigma, B, pos, workspace, stream=None) -> int:
 
 def isvd_merge_block(h: int, F, pos_F, b: int) -> None:
     _check(lib.isvd_merge_block(h, _ptr(F), _ptr(pos_F), int(b)), "isvd_merge_block")
+
+
+def isvd_merge_block_batched(handles, F, F_stride: int, pos_F, pos_stride: int, b: int) -> None:
+    arr = (_vp * len(handles))(*handles)
+    _check(lib.isvd_merge_block_batched(arr, len(handles), _ptr(F), int(F_stride), _ptr(pos_F),
+                                        int(pos_stride), int(b)), "isvd_merge_block_batched")
 
 
 def isvd_reorth(h: int) -> None:
@@ -250,21 +259,26 @@ class IsvdPath:
 
     def __init__(self, D: int, r_max: int, b_max: int, n_cap: int, reorth_every_rows: int = 0,
                  resid_rel_tol: float = 0.0, sync: bool = True, device="cuda", stream=None,
-                 graphs: bool = True):
+                 graphs: bool = True, _buffers=None):
         import torch
         flags = (0 if sync else ISKV_NO_COORD_SYNC) | (0 if graphs else ISKV_NO_GRAPH)
         self.cfg = IskvConfig(D, r_max, b_max, n_cap, reorth_every_rows, resid_rel_tol, flags)
         ws = isvd_workspace_bytes(self.cfg)
         if ws == 0:
             raise ValueError("invalid iskv configuration")
-        dev = torch.device(device)
-        self.C = torch.empty((n_cap, r_max), dtype=torch.float32, device=dev)
-        self.sigma = torch.empty((r_max,), dtype=torch.float32, device=dev)
-        self.B = torch.empty((D, r_max), dtype=torch.float32, device=dev)
-        self.pos = torch.empty((n_cap,), dtype=torch.int32, device=dev)
-        self.workspace = torch.empty((ws + 256,), dtype=torch.uint8, device=dev)
-        off = (-self.workspace.data_ptr()) % 256
-        self._ws_view = self.workspace[off:off + ws]
+        if _buffers is not None:
+            # carved by IsvdBatch from its shared allocation
+            self.C, self.sigma, self.B, self.pos, self._ws_view = _buffers
+            self.workspace = None
+        else:
+            dev = torch.device(device)
+            self.C = torch.empty((n_cap, r_max), dtype=torch.float32, device=dev)
+            self.sigma = torch.empty((r_max,), dtype=torch.float32, device=dev)
+            self.B = torch.empty((D, r_max), dtype=torch.float32, device=dev)
+            self.pos = torch.empty((n_cap,), dtype=torch.int32, device=dev)
+            self.workspace = torch.empty((ws + 256,), dtype=torch.uint8, device=dev)
+            off = (-self.workspace.data_ptr()) % 256
+            self._ws_view = self.workspace[off:off + ws]
         self.stream = stream
         self.h = isvd_init(self.cfg, self.C, self.sigma, self.B, self.pos, self._ws_view, stream)
 
@@ -311,6 +325,75 @@ class IsvdPath:
             self.close()
         except Exception:
             pass
+
+
+def _round256(x: int) -> int:
+    return (x + 255) // 256 * 256
+
+
+class IsvdBatch:
+    """`count` paths with one configuration carved from one allocation at a
+    fixed per-path stride, so that one isvd_merge_block_batched call merges a
+    block into every path (iS-KV notes §2.2: each (sequence, layer, K/V) path
+    is compressed independently). ``paths[z]`` is an ordinary IsvdPath (its
+    C, sigma, B, pos and workspace are views into the shared allocation) and
+    can be merged, reconstructed and queried on its own as well."""
+
+    def __init__(self, count: int, D: int, r_max: int, b_max: int, n_cap: int, reorth_every_rows: int = 0,
+                 resid_rel_tol: float = 0.0, sync: bool = True, device="cuda", stream=None,
+                 graphs: bool = True):
+        import torch
+        if count < 1:
+            raise ValueError("count must be >= 1")
+        cfg = IskvConfig(D, r_max, b_max, n_cap, reorth_every_rows, resid_rel_tol, 0)
+        ws = isvd_workspace_bytes(cfg)
+        if ws == 0:
+            raise ValueError("invalid iskv configuration")
+        sizes = [n_cap * r_max * 4, r_max * 4, D * r_max * 4, n_cap * 4, ws]
+        offs = []
+        o = 0
+        for nb in sizes:
+            offs.append(o)
+            o += _round256(nb)
+        self.stride = o  # bytes from one path's buffers to the next one's
+        self.count = count
+        self.D, self.b_max = D, b_max
+        self.stream = stream
+        self.blob = torch.empty((count * self.stride + 256,), dtype=torch.uint8, device=torch.device(device))
+        base = (-self.blob.data_ptr()) % 256
+        self.paths = []
+        for z in range(count):
+            z0 = base + z * self.stride
+
+            def view(i, dtype, shape):
+                return self.blob[z0 + offs[i]:z0 + offs[i] + sizes[i]].view(dtype).view(shape)
+
+            bufs = (view(0, torch.float32, (n_cap, r_max)), view(1, torch.float32, (r_max,)),
+                    view(2, torch.float32, (D, r_max)), view(3, torch.int32, (n_cap,)),
+                    self.blob[z0 + offs[4]:z0 + offs[4] + ws])
+            self.paths.append(IsvdPath(D, r_max, b_max, n_cap, reorth_every_rows, resid_rel_tol, sync,
+                                       device, stream, graphs, _buffers=bufs))
+        self.handles = [p.h for p in self.paths]
+
+    def merge(self, F, pos_F) -> None:
+        """F: [count, b, D] fp32, pos_F: [count, b] int32 (contiguous in the
+        last two dimensions); block z goes to path z."""
+        if F.dim() != 3 or F.shape[0] != self.count or F.shape[2] != self.D:
+            raise ValueError("F must be [count, b, D]")
+        if F.stride(2) != 1 or F.stride(1) != self.D or pos_F.stride(-1) != 1:
+            raise ValueError("F rows and pos_F must be contiguous")
+        b = F.shape[1]
+        isvd_merge_block_batched(self.handles, F, F.stride(0), pos_F, pos_F.stride(0), b)
+
+    def __len__(self) -> int:
+        return self.count
+
+    def __getitem__(self, z: int) -> IsvdPath:
+        return self.paths[z]
+
+    def close(self) -> None:
+        for p in getattr(self, "paths", []):
+            p.close()
 
 
 class ExactWindow:

@@ -80,7 +80,14 @@ __global__ __launch_bounds__(256) void dgemm_kernel(const double* __restrict__ A
                                                     int ldc, const double* Cin, int ldcin,
                                                     double alpha, double beta, double gamma,
                                                     const int32_t* __restrict__ st, int mode,
-                                                    int m_max) {
+                                                    int m_max,
+    const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  A = iskv_rb(A, bdel);
+  B = iskv_rb(B, bdel);
+  C = iskv_rb(C, bdel);
+  Cin = iskv_rb(Cin, bdel);
+  st = iskv_rb(st, bdel);
   const int i0 = blockIdx.y * 16, j0 = blockIdx.x * 16;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int r = lane & 15, g = lane >> 4;
@@ -153,15 +160,22 @@ __global__ __launch_bounds__(256) void dgemm_kernel(const double* __restrict__ A
 
 template <bool TA, bool TB>
 void dgemm(hipStream_t s, int m_max, const double* A, const double* B, double* C, const double* Cin,
-           int ld, double alpha, double beta, double gamma, const int32_t* st, int mode) {
+           int ld, double alpha, double beta, double gamma, const int32_t* st, int mode,
+           const int64_t* bd, int bc) {
   dim3 grid((m_max + 15) / 16, (m_max + 15) / 16);
-  hipLaunchKernelGGL((dgemm_kernel<TA, TB>), grid, dim3(256), 0, s, A, ld, B, ld, C, ld, Cin, ld, alpha,
-                     beta, gamma, st, mode, m_max);
+  hipLaunchKernelGGL((dgemm_kernel<TA, TB>), bz(grid, bc), dim3(256), 0, s, A, ld, B, ld, C, ld, Cin, ld, alpha,
+                     beta, gamma, st, mode, m_max, bd);
 }
 
 // S = A, W = I, flags cleared.
 __global__ __launch_bounds__(256) void pcj_init_kernel(const double* __restrict__ A, double* S,
-                                                       double* W, int ld, int32_t* st) {
+                                                       double* W, int ld, int32_t* st,
+    const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  A = iskv_rb(A, bdel);
+  S = iskv_rb(S, bdel);
+  W = iskv_rb(W, bdel);
+  st = iskv_rb(st, bdel);
   const int m = st[ST_JM];
   const size_t total = (size_t)m * m;
   for (size_t e = blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
@@ -223,7 +237,12 @@ __device__ void jacobi_serial(double* S, double* V, int c) {
 // pairs are appended to a global list (order fixed later by sorting).
 // aux layout: [0, 256) doubles = block maxima, then EMAX int pairs.
 __global__ __launch_bounds__(256) void pcj_detect_kernel(const double* __restrict__ S, int ld,
-                                                         double* aux, int32_t* st) {
+                                                         double* aux, int32_t* st,
+    const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  S = iskv_rb(S, bdel);
+  aux = iskv_rb(aux, bdel);
+  st = iskv_rb(st, bdel);
   if (st[ST_PCJ] & FLAG_CONV) return;
   const int m = st[ST_JM];
   const int r0 = blockIdx.x * 16;
@@ -276,7 +295,13 @@ struct AnalyzeLds {
 // ones: 2x2 rotations on a greedy matching), applied to S and W in place.
 __global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W, int ld,
                                                            const double* __restrict__ aux,
-                                                           int32_t* st, int it) {
+                                                           int32_t* st, int it,
+    const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  S = iskv_rb(S, bdel);
+  W = iskv_rb(W, bdel);
+  aux = iskv_rb(aux, bdel);
+  st = iskv_rb(st, bdel);
   extern __shared__ unsigned char smem_raw[];
   AnalyzeLds& L = *reinterpret_cast<AnalyzeLds*>(smem_raw);
   if (st[ST_PCJ] & FLAG_CONV) return;
@@ -477,7 +502,13 @@ __global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W,
 // Km = K and Pa = I + K/2 (X = I + K (I + K/2) is formed by one GEMM).
 // Grid-stride over m x m, many workgroups.
 __global__ __launch_bounds__(256) void pcj_kmat_kernel(const double* __restrict__ S, int ld, double* Km,
-                                                       double* Pa, const int32_t* __restrict__ st) {
+                                                       double* Pa, const int32_t* __restrict__ st,
+    const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  S = iskv_rb(S, bdel);
+  Km = iskv_rb(Km, bdel);
+  Pa = iskv_rb(Pa, bdel);
+  st = iskv_rb(st, bdel);
   if (st[ST_PCJ] & FLAG_CONV) return;
   const int m = st[ST_JM];
   const size_t tot = (size_t)m * m;
@@ -502,7 +533,15 @@ __global__ __launch_bounds__(256) void pcj_kmat_kernel(const double* __restrict_
 __global__ __launch_bounds__(256) void pcj_final_kernel(const double* __restrict__ Wf,
                                                         const double* __restrict__ T,
                                                         const double* __restrict__ A, double* S,
-                                                        double* V, int ld, int32_t* st) {
+                                                        double* V, int ld, int32_t* st,
+    const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  Wf = iskv_rb(Wf, bdel);
+  T = iskv_rb(T, bdel);
+  A = iskv_rb(A, bdel);
+  S = iskv_rb(S, bdel);
+  V = iskv_rb(V, bdel);
+  st = iskv_rb(st, bdel);
   const int m = st[ST_JM];
   const int j = blockIdx.x;
   if (j >= m) return;
@@ -532,7 +571,12 @@ __global__ __launch_bounds__(256) void pcj_final_kernel(const double* __restrict
 // applying up to m/2 disjoint rotations as 2x2 block updates. Runs only when
 // the refinement did not converge.
 __global__ __launch_bounds__(1024) void core_jacobi_kernel(double* S, double* V, int ld,
-                                                           int32_t* st, double tol, int max_sweeps) {
+                                                           int32_t* st, double tol, int max_sweeps,
+    const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  S = iskv_rb(S, bdel);
+  V = iskv_rb(V, bdel);
+  st = iskv_rb(st, bdel);
   if (!(st[ST_PCJ] & FLAG_FALLBACK)) return;
   __shared__ double cs[640], sn[640];
   __shared__ int pp[640], qq[640];
@@ -613,11 +657,11 @@ __global__ __launch_bounds__(1024) void core_jacobi_kernel(double* S, double* V,
 
 void iskv_dgemm(hipStream_t s, int m_max, const double* A, bool ta, const double* B, bool tb, double* C,
                 const double* Cin, int ld, double alpha, double beta, double gamma, const int32_t* st,
-                int mode) {
-  if (!ta && !tb) dgemm<false, false>(s, m_max, A, B, C, Cin, ld, alpha, beta, gamma, st, mode);
-  else if (ta && !tb) dgemm<true, false>(s, m_max, A, B, C, Cin, ld, alpha, beta, gamma, st, mode);
-  else if (!ta && tb) dgemm<false, true>(s, m_max, A, B, C, Cin, ld, alpha, beta, gamma, st, mode);
-  else dgemm<true, true>(s, m_max, A, B, C, Cin, ld, alpha, beta, gamma, st, mode);
+                int mode, const int64_t* bd, int bc) {
+  if (!ta && !tb) dgemm<false, false>(s, m_max, A, B, C, Cin, ld, alpha, beta, gamma, st, mode, bd, bc);
+  else if (ta && !tb) dgemm<true, false>(s, m_max, A, B, C, Cin, ld, alpha, beta, gamma, st, mode, bd, bc);
+  else if (!ta && tb) dgemm<false, true>(s, m_max, A, B, C, Cin, ld, alpha, beta, gamma, st, mode, bd, bc);
+  else dgemm<true, true>(s, m_max, A, B, C, Cin, ld, alpha, beta, gamma, st, mode, bd, bc);
 }
 
 int iskv_core_eig_setup() {
@@ -636,7 +680,7 @@ int iskv_launch_core_eig(isvd_handle* h) {
   const int mm = h->m_max, ld = h->ldm;
   int32_t* st = w.st;
   const int nblk = (mm + 15) / 16;
-  hipLaunchKernelGGL(pcj_init_kernel, dim3(128), dim3(256), 0, s, w.A, w.S, w.W0, ld, st);
+  hipLaunchKernelGGL(pcj_init_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.A, w.S, w.W0, ld, st, h->bd);
   double* cur = w.W0;
   double* nxt = w.W1;
   const size_t lds = sizeof(AnalyzeLds);
@@ -644,28 +688,28 @@ int iskv_launch_core_eig(isvd_handle* h) {
     if (it > 0) {
       // Newton-Schulz: W <- 1.5 W - 0.5 W (W^T W) keeps W orthonormal to
       // O(defect^2), so S is measured in an orthonormal basis
-      dgemm<true, false>(s, mm, cur, cur, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 0);
-      dgemm<false, false>(s, mm, cur, w.T, nxt, cur, ld, -0.5, 1.5, 0.0, st, 1);
+      dgemm<true, false>(s, mm, cur, cur, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 0, h->bd, h->bcount);
+      dgemm<false, false>(s, mm, cur, w.T, nxt, cur, ld, -0.5, 1.5, 0.0, st, 1, h->bd, h->bcount);
       { double* tmp = cur; cur = nxt; nxt = tmp; }
-      dgemm<false, false>(s, mm, w.A, cur, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 0);
-      dgemm<true, false>(s, mm, cur, w.T, w.S, nullptr, ld, 1.0, 0.0, 0.0, st, 0);
+      dgemm<false, false>(s, mm, w.A, cur, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 0, h->bd, h->bcount);
+      dgemm<true, false>(s, mm, cur, w.T, w.S, nullptr, ld, 1.0, 0.0, 0.0, st, 0, h->bd, h->bcount);
     }
-    hipLaunchKernelGGL(pcj_detect_kernel, dim3(nblk), dim3(256), 0, s, w.S, ld, w.aux, st);
-    hipLaunchKernelGGL(pcj_analyze_kernel, dim3(1), dim3(1024), lds, s, w.S, cur, ld, w.aux, st, it);
+    hipLaunchKernelGGL(pcj_detect_kernel, bz(dim3(nblk), h->bcount), dim3(256), 0, s, w.S, ld, w.aux, st, h->bd);
+    hipLaunchKernelGGL(pcj_analyze_kernel, bz(dim3(1), h->bcount), dim3(1024), lds, s, w.S, cur, ld, w.aux, st, it, h->bd);
     if (it == PCJ_MAXIT) break;  // last pass only tests convergence
-    hipLaunchKernelGGL(pcj_kmat_kernel, dim3(128), dim3(256), 0, s, w.S, ld, w.Km, w.Pa, st);
+    hipLaunchKernelGGL(pcj_kmat_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.S, ld, w.Km, w.Pa, st, h->bd);
     // X = I + K (I + K/2); W <- W X
-    dgemm<false, false>(s, mm, w.Km, w.Pa, w.Pb, nullptr, ld, 1.0, 0.0, 1.0, st, 0);
-    dgemm<false, false>(s, mm, cur, w.Pb, nxt, cur, ld, 1.0, 0.0, 0.0, st, 1);
+    dgemm<false, false>(s, mm, w.Km, w.Pa, w.Pb, nullptr, ld, 1.0, 0.0, 1.0, st, 0, h->bd, h->bcount);
+    dgemm<false, false>(s, mm, cur, w.Pb, nxt, cur, ld, 1.0, 0.0, 0.0, st, 1, h->bd, h->bcount);
     { double* tmp = cur; cur = nxt; nxt = tmp; }
   }
   // final Newton-Schulz, then T = A W for the eigenvalues
-  dgemm<true, false>(s, mm, cur, cur, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 2);
-  dgemm<false, false>(s, mm, cur, w.T, nxt, cur, ld, -0.5, 1.5, 0.0, st, 2);
-  dgemm<false, false>(s, mm, w.A, nxt, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 2);
-  hipLaunchKernelGGL(pcj_final_kernel, dim3(mm), dim3(256), 0, s, nxt, w.T, w.A, w.S, w.V, ld, st);
-  hipLaunchKernelGGL(core_jacobi_kernel, dim3(1), dim3(1024), 0, s, w.S, w.V, ld, st, 1e-13,
-                     ISKV_JACOBI_MAX_SWEEPS);
+  dgemm<true, false>(s, mm, cur, cur, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 2, h->bd, h->bcount);
+  dgemm<false, false>(s, mm, cur, w.T, nxt, cur, ld, -0.5, 1.5, 0.0, st, 2, h->bd, h->bcount);
+  dgemm<false, false>(s, mm, w.A, nxt, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 2, h->bd, h->bcount);
+  hipLaunchKernelGGL(pcj_final_kernel, bz(dim3(mm), h->bcount), dim3(256), 0, s, nxt, w.T, w.A, w.S, w.V, ld, st, h->bd);
+  hipLaunchKernelGGL(core_jacobi_kernel, bz(dim3(1), h->bcount), dim3(1024), 0, s, w.S, w.V, ld, st, 1e-13,
+                     ISKV_JACOBI_MAX_SWEEPS, h->bd);
   ISKV_HIP_CHECK(hipGetLastError());
   return ISKV_OK;
 }

@@ -7,6 +7,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <vector>
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -74,6 +76,7 @@ size_t carve(const iskv_config* c, char* base, isvd_ws* w) {
   x.order = (int32_t*)take(M * 4);
   x.Fs = (float*)take(Bm * D * 4);
   x.posFs = (int32_t*)take(Bm * 4);
+  x.btab = (int64_t*)take(ISKV_MAX_BATCH * 8);
   return off;
 }
 
@@ -154,6 +157,49 @@ int isvd_merge_block(isvd_handle* h, const float* F, const int32_t* pos_F, int32
   h->folded_host += b;
   const int T = h->cfg.reorth_every_rows;
   if (T > 0 && !(h->cfg.flags & ISKV_NO_COORD_SYNC) && (h->folded_host / T) > (before / T)) {
+    rc = iskv_launch_reorth(h);
+    if (rc) return rc;
+  }
+  return ISKV_OK;
+}
+
+int isvd_merge_block_batched(isvd_handle* const* hs, int32_t count, const float* F, int64_t F_stride,
+                             const int32_t* pos_F, int64_t pos_stride, int32_t b) {
+  if (!hs || count < 1 || count > ISKV_MAX_BATCH || !F || !pos_F) return ISKV_EINVAL;
+  isvd_handle* h0 = hs[0];
+  if (!h0 || b < 1 || b > h0->cfg.b_max) return ISKV_EINVAL;
+  if (F_stride < (int64_t)b * h0->cfg.D || pos_stride < b) return ISKV_EINVAL;
+  const char* w0 = (const char*)h0->ws_base;
+  for (int z = 0; z < count; ++z) {
+    const isvd_handle* h = hs[z];
+    if (!h || memcmp(&h->cfg, &h0->cfg, sizeof(iskv_config)) != 0 || h->stream != h0->stream)
+      return ISKV_EINVAL;
+    for (int y = 0; y < z; ++y)
+      if (hs[y] == h) return ISKV_EINVAL;  // each handle once
+    // one buffer layout: every buffer at the workspace's offset from handle 0
+    const ptrdiff_t d = (const char*)h->ws_base - w0;
+    if ((const char*)h->C - (const char*)h0->C != d || (const char*)h->sigma - (const char*)h0->sigma != d ||
+        (const char*)h->B - (const char*)h0->B != d || (const char*)h->pos - (const char*)h0->pos != d)
+      return ISKV_EINVAL;
+    if ((int64_t)h->n_host + b > h->cfg.n_cap) return ISKV_ECAPACITY;
+  }
+  int rc = iskv_launch_merge_batched(hs, count, F, F_stride, pos_F, pos_stride, b);
+  if (rc) return rc;
+  const int T = h0->cfg.reorth_every_rows;
+  bool lockstep = true;
+  std::vector<isvd_handle*> due;
+  for (int z = 0; z < count; ++z) {
+    isvd_handle* h = hs[z];
+    const int before = h->folded_host;
+    h->n_host += b;
+    h->folded_host += b;
+    if (h->folded_host != h0->folded_host) lockstep = false;
+    if (T > 0 && !(h->cfg.flags & ISKV_NO_COORD_SYNC) && (h->folded_host / T) > (before / T))
+      due.push_back(h);
+  }
+  if (due.empty()) return ISKV_OK;
+  if (lockstep && (int)due.size() == count) return iskv_launch_reorth_batched(hs, count);
+  for (isvd_handle* h : due) {
     rc = iskv_launch_reorth(h);
     if (rc) return rc;
   }

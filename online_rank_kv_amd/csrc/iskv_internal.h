@@ -8,6 +8,8 @@
 
 #include "../../include/iskv.h"
 
+#include <vector>
+
 // ---- device state word slots (int32 array at the head of the workspace) ----
 enum {
   ST_N = 0,        // rows in the compressed history
@@ -63,6 +65,7 @@ struct isvd_ws {
   int32_t* order;     // [m_max]
   float* Fs;          // [b_max x D]  staged pending block (graph replays read it)
   int32_t* posFs;     // [b_max]      its positions
+  int64_t* btab;      // [ISKV_MAX_BATCH] per-handle byte offsets of a batched launch
   size_t rot_cap;     // doubles in rot
   int gram_splits;
 };
@@ -87,6 +90,16 @@ struct isvd_handle {
   const float* g_merge_F = nullptr;      // block pointers the merge graph reads
   const int32_t* g_merge_posF = nullptr;
   hipGraphExec_t g_reorth = nullptr;
+  // batched launches: every merge / reorth kernel runs grid.z = bcount copies,
+  // copy z rebasing each pointer it is given by bd[z] bytes (bd = nullptr for
+  // one handle); set only while a batched launch sequence is enqueued
+  const int64_t* bd = nullptr;
+  int32_t bcount = 1;
+  // recorded batched merge / reorth (kept by the first handle of the batch)
+  std::vector<isvd_handle*> g_batch_set;
+  int32_t g_batch_b = 0;
+  hipGraphExec_t g_batch_merge = nullptr;
+  hipGraphExec_t g_batch_reorth = nullptr;
 };
 
 struct iskv_window {
@@ -105,6 +118,8 @@ struct iskv_window {
 // K-panel depth of the fp64 core GEMM; the leading dimension of every fp64
 // core matrix in the workspace is a multiple of it.
 #define ISKV_DGEMM_KP 288
+// Largest number of handles one batched merge may serve.
+#define ISKV_MAX_BATCH 4096
 inline int iskv_core_ld(int m_max) { return (m_max + ISKV_DGEMM_KP - 1) / ISKV_DGEMM_KP * ISKV_DGEMM_KP; }
 #define ISKV_RESID_MAX_SWEEPS 30
 
@@ -114,8 +129,11 @@ int iskv_core_eig_setup();
 int iskv_launch_core_eig(isvd_handle* h);
 void iskv_dgemm(hipStream_t s, int m_max, const double* A, bool ta, const double* B, bool tb, double* C,
                 const double* Cin, int ld, double alpha, double beta, double gamma, const int32_t* st,
-                int mode);
+                int mode, const int64_t* bd, int bc);
 int iskv_launch_merge(isvd_handle* h, const float* F, const int32_t* pos_F, int32_t b);
+int iskv_launch_merge_batched(isvd_handle* const* hs, int32_t count, const float* F, int64_t F_stride,
+                              const int32_t* pos_F, int64_t pos_stride, int32_t b);
+int iskv_launch_reorth_batched(isvd_handle* const* hs, int32_t count);
 int iskv_launch_reorth(isvd_handle* h);
 void iskv_release_graphs(isvd_handle* h);
 int iskv_launch_sym_eig(isvd_handle* h, const double* A, int32_t m, double* lam, double* V);
@@ -135,6 +153,13 @@ int iskv_launch_window_move(float* dst_rows, int32_t* dst_pos, const float* src_
 int iskv_launch_fill_pos(int32_t* pos, int32_t count, int32_t value0, int32_t step, hipStream_t s);
 int iskv_launch_copy_pos_host(int32_t* pos_dev, const int32_t* pos_host, int32_t count,
                               hipStream_t s);
+
+// Batched launches: z copies of a grid, and the per-copy pointer rebase.
+inline dim3 bz(dim3 g, int count) { return dim3(g.x, g.y, (unsigned)count); }
+template <class T>
+__device__ __forceinline__ T* iskv_rb(T* p, int64_t d) {
+  return p ? (T*)((const char*)p + d) : p;
+}
 
 #define ISKV_HIP_CHECK(expr)                 \
   do {                                       \

@@ -17,6 +17,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
+
 namespace {
 
 // ----------------------------------------------------------------------------
@@ -31,6 +33,7 @@ struct Dim {
 };
 __device__ __forceinline__ int dval(const Dim& d) { return d.dev ? (*d.dev) * d.mul + d.add : d.v; }
 static inline Dim hdim(int v) { return Dim{v, nullptr, 0, 0}; }
+__device__ __forceinline__ void iskv_rb_dim(Dim& d, int64_t off) { d.dev = iskv_rb(d.dev, off); }
 static inline Dim ddim(const int32_t* p, int mul = 1, int add = 0) { return Dim{0, p, mul, add}; }
 
 // Ordering key of an eigenvalue: NaN sorts last as -inf, so that the rank
@@ -46,90 +49,17 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 }
 
 // ----------------------------------------------------------------------------
-// Small fp32 GEMM, 64x64 tile, 256 threads, 4x4 outputs per thread:
-//   C(i, j) = alpha * sum_k opA(i, k) opB(k, j) + beta * Cin(i, j)
-// opA(i, k) = TA ? A[k*lda + i] : A[i*lda + k]; likewise opB with TB.
-// Cin may alias C (each element is read and written by the same thread).
-template <bool TA, bool TB>
-__global__ __launch_bounds__(256) void sgemm64_kernel(const float* __restrict__ A, int lda,
-                                                      const float* __restrict__ Bm, int ldb,
-                                                      float* C, int ldc, const float* Cin,
-                                                      int ldcin, Dim Md, Dim Nd, Dim Kd,
-                                                      float alpha, float beta) {
-  const int M = dval(Md), N = dval(Nd), K = dval(Kd);
-  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
-  if (i0 >= M || j0 >= N) return;
-  __shared__ float As[16][68];
-  __shared__ float Bs[16][68];
-  const int t = threadIdx.x, tx = t & 15, ty = t >> 4;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += 16) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      int idx = t + e * 256;
-      int r, c;
-      float v;
-      if (!TA) {
-        r = idx >> 4; c = idx & 15;
-        v = (i0 + r < M && k0 + c < K) ? A[(size_t)(i0 + r) * lda + k0 + c] : 0.f;
-      } else {
-        c = idx >> 6; r = idx & 63;
-        v = (i0 + r < M && k0 + c < K) ? A[(size_t)(k0 + c) * lda + i0 + r] : 0.f;
-      }
-      As[c][r] = v;
-      if (!TB) {
-        c = idx >> 6; r = idx & 63;
-        v = (j0 + r < N && k0 + c < K) ? Bm[(size_t)(k0 + c) * ldb + j0 + r] : 0.f;
-      } else {
-        r = idx >> 4; c = idx & 15;
-        v = (j0 + r < N && k0 + c < K) ? Bm[(size_t)(j0 + r) * ldb + k0 + c] : 0.f;
-      }
-      Bs[c][r] = v;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      float a[4], b[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) { a[u] = As[kk][ty * 4 + u]; b[u] = Bs[kk][tx * 4 + u]; }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(a[u], b[v], acc[u][v]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    int i = i0 + ty * 4 + u;
-    if (i >= M) continue;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      int j = j0 + tx * 4 + v;
-      if (j >= N) continue;
-      float o = alpha * acc[u][v];
-      if (beta != 0.f) o += beta * Cin[(size_t)i * ldcin + j];
-      C[(size_t)i * ldc + j] = o;
-    }
-  }
-}
-
-template <bool TA, bool TB>
-static void sgemm(hipStream_t s, int Mmax, int Nmax, const float* A, int lda, const float* B,
-                  int ldb, float* C, int ldc, const float* Cin, int ldcin, Dim M, Dim N, Dim K,
-                  float alpha, float beta) {
-  dim3 grid((Nmax + 63) / 64, (Mmax + 63) / 64);
-  hipLaunchKernelGGL((sgemm64_kernel<TA, TB>), grid, dim3(256), 0, s, A, lda, B, ldb, C, ldc, Cin,
-                     ldcin, M, N, K, alpha, beta);
-}
-
-// ----------------------------------------------------------------------------
 // Residual Gram E E^T in fp64 (b x b): workgroup (i, jb) forms row i against
 // rows 8 jb .. 8 jb + 7, each thread over 4 consecutive features (D % 4 == 0),
 // reduced over the wave and the 4 waves. Also latches the non-finite flag when
 // the block (hence E) holds NaN or Inf.
 __global__ __launch_bounds__(256) void resid_gram_kernel(const float* __restrict__ E, int D,
-                                                         int b, double* GE, int32_t* st) {
+                                                         int b, double* GE, int32_t* st,
+    const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  E = iskv_rb(E, bdel);
+  GE = iskv_rb(GE, bdel);
+  st = iskv_rb(st, bdel);
   const int i = blockIdx.x, jb = blockIdx.y * 8;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   double acc[8] = {};
@@ -227,7 +157,14 @@ template <int HB>
 __global__ __launch_bounds__(HB * HB) void resid_basis_kernel(const double* __restrict__ GE, int b,
                                                               int D, const float* __restrict__ sigma,
                                                               float delta, double* VE, double* rho,
-                                                              int32_t* st, int max_sweeps) {
+                                                              int32_t* st, int max_sweeps,
+    const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  GE = iskv_rb(GE, bdel);
+  sigma = iskv_rb(sigma, bdel);
+  VE = iskv_rb(VE, bdel);
+  rho = iskv_rb(rho, bdel);
+  st = iskv_rb(st, bdel);
   constexpr int N = 2 * HB, L = N + 1;
   extern __shared__ double rb_lds[];
   double* Sb = rb_lds;              // [2][N][L]
@@ -430,7 +367,14 @@ __global__ __launch_bounds__(HB * HB) void resid_basis_kernel(const double* __re
 __global__ __launch_bounds__(256) void make_p_kernel(const float* __restrict__ E, int D, int b,
                                                      const double* __restrict__ VE,
                                                      const double* __restrict__ rho, float* P,
-                                                     int ldp, const int32_t* st) {
+                                                     int ldp, const int32_t* st,
+    const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  E = iskv_rb(E, bdel);
+  VE = iskv_rb(VE, bdel);
+  rho = iskv_rb(rho, bdel);
+  P = iskv_rb(P, bdel);
+  st = iskv_rb(st, bdel);
   const int p = st[ST_P];
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
   const int d = e / ldp, j = e % ldp;
@@ -444,7 +388,14 @@ __global__ __launch_bounds__(256) void make_p_kernel(const float* __restrict__ E
 __global__ __launch_bounds__(256) void core_gram_kernel(const float* __restrict__ Q, int ldq,
                                                         const float* __restrict__ FP, int ldfp,
                                                         const float* __restrict__ sigma, int b,
-                                                        double* A, int lda, const int32_t* st) {
+                                                        double* A, int lda, const int32_t* st,
+    const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  Q = iskv_rb(Q, bdel);
+  FP = iskv_rb(FP, bdel);
+  sigma = iskv_rb(sigma, bdel);
+  A = iskv_rb(A, bdel);
+  st = iskv_rb(st, bdel);
   const int k = st[ST_K], m = st[ST_M];
   const int i = blockIdx.y * 16 + (threadIdx.x >> 4);
   const int j = blockIdx.x * 16 + (threadIdx.x & 15);
@@ -464,7 +415,13 @@ __global__ __launch_bounds__(256) void core_gram_kernel(const float* __restrict_
 // keep = min(r_max, n) for a merge; n for re-orthogonalisation. One workgroup.
 __global__ __launch_bounds__(1024) void eig_order_kernel(const double* __restrict__ S, int ld,
                                                          float* sig_new, int32_t* order, int32_t* st,
-                                                         int r_max, int for_merge) {
+                                                         int r_max, int for_merge,
+    const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  S = iskv_rb(S, bdel);
+  sig_new = iskv_rb(sig_new, bdel);
+  order = iskv_rb(order, bdel);
+  st = iskv_rb(st, bdel);
   __shared__ double lam[1024];
   const int n = st[ST_JM];
   const int t = threadIdx.x;
@@ -493,7 +450,13 @@ __global__ __launch_bounds__(256) void eig_gather_kernel(const double* __restric
                                                          float* Hc, int ldh,
                                                          const int32_t* __restrict__ order,
                                                          const int32_t* __restrict__ st, int r_max,
-                                                         int for_merge) {
+                                                         int for_merge,
+    const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  V = iskv_rb(V, bdel);
+  Hc = iskv_rb(Hc, bdel);
+  order = iskv_rb(order, bdel);
+  st = iskv_rb(st, bdel);
   const int n = st[ST_JM];
   const int keep = for_merge ? (n < r_max ? n : r_max) : n;
   const int kold = for_merge ? st[ST_K] : 0;
@@ -533,7 +496,21 @@ __global__ __launch_bounds__(256) void xh_mfma_kernel(const float* X1, int ld1, 
                                                       int ldh, int hcols, Dim kout_d, Dim rows_d,
                                                       float* Y, int ldy, uint16_t* Ybf, int ldbf,
                                                       int ldx, int32_t* pos, const int32_t* pos_src,
-                                                      Dim yoff_d) {
+                                                      Dim yoff_d,
+    const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  X1 = iskv_rb(X1, bdel);
+  X2 = iskv_rb(X2, bdel);
+  iskv_rb_dim(k1_d, bdel);
+  iskv_rb_dim(kin_d, bdel);
+  H = iskv_rb(H, bdel);
+  iskv_rb_dim(kout_d, bdel);
+  iskv_rb_dim(rows_d, bdel);
+  Y = iskv_rb(Y, bdel);
+  Ybf = iskv_rb(Ybf, bdel);
+  pos = iskv_rb(pos, bdel);
+  pos_src = iskv_rb(pos_src, bdel);
+  iskv_rb_dim(yoff_d, bdel);
   const int k1 = dval(k1_d), kin = dval(kin_d), kout = dval(kout_d), rows = dval(rows_d);
   const int yo = dval(yoff_d);
   const int i0 = blockIdx.x * BM;
@@ -639,7 +616,21 @@ __global__ __launch_bounds__(1024) void xh_reg_kernel(const float* X1, int ld1, 
                                                       Dim k1_d, Dim kin_d, const float* __restrict__ H,
                                                       int ldh, int hcols, Dim kout_d, Dim rows_d, float* Y,
                                                       int ldy, uint16_t* Ybf, int ldbf, int32_t* pos,
-                                                      const int32_t* pos_src, Dim yoff_d) {
+                                                      const int32_t* pos_src, Dim yoff_d,
+    const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  X1 = iskv_rb(X1, bdel);
+  X2 = iskv_rb(X2, bdel);
+  iskv_rb_dim(k1_d, bdel);
+  iskv_rb_dim(kin_d, bdel);
+  H = iskv_rb(H, bdel);
+  iskv_rb_dim(kout_d, bdel);
+  iskv_rb_dim(rows_d, bdel);
+  Y = iskv_rb(Y, bdel);
+  Ybf = iskv_rb(Ybf, bdel);
+  pos = iskv_rb(pos, bdel);
+  pos_src = iskv_rb(pos_src, bdel);
+  iskv_rb_dim(yoff_d, bdel);
   constexpr int KW = 4 * XR_KS;                // staged columns (zero beyond kin)
   constexpr int PER = (16 * KW + 1023) / 1024;  // staged elements per thread
   const int k1 = dval(k1_d), kin = dval(kin_d), kout = dval(kout_d), rows = dval(rows_d);
@@ -708,7 +699,7 @@ __global__ __launch_bounds__(1024) void xh_reg_kernel(const float* X1, int ld1, 
 
 // Launch Y = [X1 | X2] H over `rows_host` rows (an upper bound when rows_d is
 // a device value); kin_max bounds kin for the LDS layout.
-static void xh_launch(hipStream_t s, int rows_host, const float* X1, int ld1, const float* X2, int ld2,
+static void xh_launch(hipStream_t s, const int64_t* bd, int bc, int rows_host, const float* X1, int ld1, const float* X2, int ld2,
                       Dim k1, Dim kin, int kin_max, const float* H, int ldh, int hcols, Dim kout,
                       Dim rows, float* Y, int ldy, uint16_t* Ybf, int ldbf, int32_t* pos = nullptr,
                       const int32_t* pos_src = nullptr, bool prefer16 = false, Dim yoff = hdim(0)) {
@@ -718,28 +709,33 @@ static void xh_launch(hipStream_t s, int rows_host, const float* X1, int ld1, co
     const int grid = nblk < 256 ? nblk : 256;
     if (grid > 0) {
       if (kin_max <= 256)
-        hipLaunchKernelGGL(xh_reg_kernel<64>, dim3(grid), dim3(1024), 0, s, X1, ld1, X2, ld2, k1, kin, H,
-                           ldh, hcols, kout, rows, Y, ldy, Ybf, ldbf, pos, pos_src, yoff);
+        hipLaunchKernelGGL(xh_reg_kernel<64>, bz(dim3(grid), bc), dim3(1024), 0, s, X1, ld1, X2, ld2, k1, kin, H,
+                           ldh, hcols, kout, rows, Y, ldy, Ybf, ldbf, pos, pos_src, yoff, bd);
       else
-        hipLaunchKernelGGL(xh_reg_kernel<72>, dim3(grid), dim3(1024), 0, s, X1, ld1, X2, ld2, k1, kin, H,
-                           ldh, hcols, kout, rows, Y, ldy, Ybf, ldbf, pos, pos_src, yoff);
+        hipLaunchKernelGGL(xh_reg_kernel<72>, bz(dim3(grid), bc), dim3(1024), 0, s, X1, ld1, X2, ld2, k1, kin, H,
+                           ldh, hcols, kout, rows, Y, ldy, Ybf, ldbf, pos, pos_src, yoff, bd);
     }
     return;
   }
   if (!prefer16 && xh_lds_bytes(32, kin_max) <= 80 * 1024) {
-    hipLaunchKernelGGL(xh_mfma_kernel<32>, dim3((rows_host + 31) / 32), dim3(256),
+    hipLaunchKernelGGL(xh_mfma_kernel<32>, bz(dim3((rows_host + 31) / 32), bc), dim3(256),
                        xh_lds_bytes(32, kin_max), s, X1, ld1, X2, ld2, k1, kin, H, ldh, hcols, kout,
-                       rows, Y, ldy, Ybf, ldbf, ldx, pos, pos_src, yoff);
+                       rows, Y, ldy, Ybf, ldbf, ldx, pos, pos_src, yoff, bd);
   } else {
-    hipLaunchKernelGGL(xh_mfma_kernel<16>, dim3((rows_host + 15) / 16), dim3(256),
+    hipLaunchKernelGGL(xh_mfma_kernel<16>, bz(dim3((rows_host + 15) / 16), bc), dim3(256),
                        xh_lds_bytes(16, kin_max), s, X1, ld1, X2, ld2, k1, kin, H, ldh, hcols, kout,
-                       rows, Y, ldy, Ybf, ldbf, ldx, pos, pos_src, yoff);
+                       rows, Y, ldy, Ybf, ldbf, ldx, pos, pos_src, yoff, bd);
   }
 }
 
 // Commit a merge: sigma <- sigma+, k <- r', n += b, folded += b.
 __global__ void merge_commit_kernel(float* sigma, const float* __restrict__ sig_new, int32_t* st,
-                                    int b, int r_max) {
+                                    int b, int r_max,
+    const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  sigma = iskv_rb(sigma, bdel);
+  sig_new = iskv_rb(sig_new, bdel);
+  st = iskv_rb(st, bdel);
   const int kout = st[ST_KNEW];
   for (int j = threadIdx.x; j < r_max; j += blockDim.x) sigma[j] = j < kout ? sig_new[j] : 0.f;
   __syncthreads();
@@ -751,7 +747,12 @@ __global__ void merge_commit_kernel(float* sigma, const float* __restrict__ sig_
 }
 
 // Copy k (or another slot) into ST_JM so the eigensolver knows its order.
-__global__ void set_jm_kernel(int32_t* st, int from_slot) { st[ST_JM] = st[from_slot]; }
+__global__ void set_jm_kernel(int32_t* st, int from_slot,
+    const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  st = iskv_rb(st, bdel);
+  st[ST_JM] = st[from_slot];
+}
 
 // ----------------------------------------------------------------------------
 // Re-orthogonalisation helpers.
@@ -761,7 +762,13 @@ __global__ void set_jm_kernel(int32_t* st, int from_slot) { st[ST_JM] = st[from_
 __global__ __launch_bounds__(256) void gram_partial_kernel(const float* __restrict__ X, int ldx,
                                                            Dim rows_d, const int32_t* st,
                                                            double* Gpart, int ldg,
-                                                           int rows_per_chunk) {
+                                                           int rows_per_chunk,
+    const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  X = iskv_rb(X, bdel);
+  iskv_rb_dim(rows_d, bdel);
+  st = iskv_rb(st, bdel);
+  Gpart = iskv_rb(Gpart, bdel);
   const int k = st[ST_K];
   const int rows = dval(rows_d);
   const int tiles = (k + 15) / 16;
@@ -792,7 +799,14 @@ __global__ __launch_bounds__(256) void gram_partial_kernel(const float* __restri
 // step towards G_B^(-1/2)). Grid-stride over k x k.
 __global__ __launch_bounds__(256) void reorth_sum_kernel(const double* __restrict__ Gpart, int nchunks,
                                                          int ldg, double* GC, double* GB, double* Z0,
-                                                         int ld, const int32_t* st) {
+                                                         int ld, const int32_t* st,
+    const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  Gpart = iskv_rb(Gpart, bdel);
+  GC = iskv_rb(GC, bdel);
+  GB = iskv_rb(GB, bdel);
+  Z0 = iskv_rb(Z0, bdel);
+  st = iskv_rb(st, bdel);
   const int k = st[ST_K];
   const size_t tot = (size_t)k * k;
   for (size_t e = blockIdx.x * 256 + threadIdx.x; e < tot; e += (size_t)gridDim.x * 256) {
@@ -809,7 +823,13 @@ __global__ __launch_bounds__(256) void reorth_sum_kernel(const double* __restric
 // Y[:, t] = V[:, order[t]] (fp64, sorted eigenvectors). Grid-stride.
 __global__ __launch_bounds__(256) void permute_cols_kernel(const double* __restrict__ V,
                                                            const int32_t* __restrict__ order,
-                                                           double* Y, int ld, const int32_t* st) {
+                                                           double* Y, int ld, const int32_t* st,
+    const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  V = iskv_rb(V, bdel);
+  order = iskv_rb(order, bdel);
+  Y = iskv_rb(Y, bdel);
+  st = iskv_rb(st, bdel);
   const int k = st[ST_JM];
   const size_t tot = (size_t)k * k;
   for (size_t e = blockIdx.x * 256 + threadIdx.x; e < tot; e += (size_t)gridDim.x * 256) {
@@ -821,7 +841,14 @@ __global__ __launch_bounds__(256) void permute_cols_kernel(const double* __restr
 // fp64 (ld) -> fp32 (ld r_max) for the two k x k transforms.
 __global__ __launch_bounds__(256) void to_f32_kernel(const double* __restrict__ X1,
                                                      const double* __restrict__ X2, int ld, float* Y1,
-                                                     float* Y2, int ldy, const int32_t* st) {
+                                                     float* Y2, int ldy, const int32_t* st,
+    const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  X1 = iskv_rb(X1, bdel);
+  X2 = iskv_rb(X2, bdel);
+  Y1 = iskv_rb(Y1, bdel);
+  Y2 = iskv_rb(Y2, bdel);
+  st = iskv_rb(st, bdel);
   const int k = st[ST_K];
   const size_t tot = (size_t)k * k;
   for (size_t e = blockIdx.x * 256 + threadIdx.x; e < tot; e += (size_t)gridDim.x * 256) {
@@ -832,7 +859,12 @@ __global__ __launch_bounds__(256) void to_f32_kernel(const double* __restrict__ 
 }
 
 __global__ void reorth_commit_kernel(float* sigma, const float* __restrict__ sig_new, int32_t* st,
-                                     int r_max) {
+                                     int r_max,
+    const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  sigma = iskv_rb(sigma, bdel);
+  sig_new = iskv_rb(sig_new, bdel);
+  st = iskv_rb(st, bdel);
   const int k = st[ST_K];
   for (int j = threadIdx.x; j < r_max; j += blockDim.x) sigma[j] = j < k ? sig_new[j] : 0.f;
 }
@@ -882,7 +914,15 @@ __global__ __launch_bounds__(256) void skinny_mfma_kernel(const float* __restric
                                                           const float* __restrict__ Y, int ldy, int M,
                                                           int Nmax, Dim Nd, Dim Kd, float alpha,
                                                           float beta, const float* Z, int ldz,
-                                                          float* out, int ldo) {
+                                                          float* out, int ldo,
+    const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  X = iskv_rb(X, bdel);
+  Y = iskv_rb(Y, bdel);
+  iskv_rb_dim(Nd, bdel);
+  iskv_rb_dim(Kd, bdel);
+  Z = iskv_rb(Z, bdel);
+  out = iskv_rb(out, bdel);
   const int N = dval(Nd), K = dval(Kd);
   const int j0 = blockIdx.x * 16, i0 = blockIdx.y * 16;
   if (j0 >= N) return;
@@ -933,17 +973,17 @@ static void skinny(isvd_handle* h, int M, int Nmax, const float* X, int ldx, con
                    int ldo) {
   Dim K = TY ? ddim(h->w.st + ST_K) : hdim(Kmax);
   dim3 grid((Nmax + 15) / 16, (M + 15) / 16);
-  hipLaunchKernelGGL((skinny_mfma_kernel<TY>), grid, dim3(256), 0, h->stream, X, ldx, Y, ldy, M, Nmax, N,
-                     K, alpha, beta, Z, ldz, out, ldo);
+  hipLaunchKernelGGL((skinny_mfma_kernel<TY>), bz(grid, h->bcount), dim3(256), 0, h->stream, X, ldx, Y, ldy, M, Nmax, N,
+                     K, alpha, beta, Z, ldz, out, ldo, h->bd);
 }
 
 static void eig_finish(isvd_handle* h, int for_merge) {
   const isvd_ws& w = h->w;
   const int R = h->cfg.r_max;
-  hipLaunchKernelGGL(eig_order_kernel, dim3(1), dim3(1024), 0, h->stream, w.S, h->ldm, w.sig_new,
-                     w.order, w.st, R, for_merge);
-  hipLaunchKernelGGL(eig_gather_kernel, dim3(128), dim3(256), 0, h->stream, w.V, h->ldm, w.Hc, R,
-                     w.order, w.st, R, for_merge);
+  hipLaunchKernelGGL(eig_order_kernel, bz(dim3(1), h->bcount), dim3(1024), 0, h->stream, w.S, h->ldm, w.sig_new,
+                     w.order, w.st, R, for_merge, h->bd);
+  hipLaunchKernelGGL(eig_gather_kernel, bz(dim3(128), h->bcount), dim3(256), 0, h->stream, w.V, h->ldm, w.Hc, R,
+                     w.order, w.st, R, for_merge, h->bd);
 }
 
 int iskv_launch_sym_eig(isvd_handle* h, const double* A, int32_t m, double* lam, double* V) {
@@ -993,24 +1033,24 @@ static int merge_body(isvd_handle* h, const float* F, const int32_t* pos_F, int3
   skinny<false>(h, b, R, w.E, D, h->B, R, ddim(dk), D, 1.f, 0.f, nullptr, 0, w.EB, R);
   skinny<true>(h, b, D, w.EB, R, h->B, R, hdim(D), R, -1.f, 1.f, w.E, D, w.E, D);
   // 5. E E^T (fp64) and the residual basis
-  hipLaunchKernelGGL(resid_gram_kernel, dim3(b, (b + 7) / 8), dim3(256), 0, s, w.E, D, b, w.GE, w.st);
+  hipLaunchKernelGGL(resid_gram_kernel, bz(dim3(b, (b + 7) / 8), h->bcount), dim3(256), 0, s, w.E, D, b, w.GE, w.st, h->bd);
   if (b <= 32)
-    hipLaunchKernelGGL(resid_basis_kernel<16>, dim3(1), dim3(256), resid_lds_bytes(16), s, w.GE, b,
-                       D, h->sigma, c.resid_rel_tol, w.VE, w.rho, w.st, ISKV_RESID_MAX_SWEEPS);
+    hipLaunchKernelGGL(resid_basis_kernel<16>, bz(dim3(1), h->bcount), dim3(256), resid_lds_bytes(16), s, w.GE, b,
+                       D, h->sigma, c.resid_rel_tol, w.VE, w.rho, w.st, ISKV_RESID_MAX_SWEEPS, h->bd);
   else
-    hipLaunchKernelGGL(resid_basis_kernel<32>, dim3(1), dim3(1024), resid_lds_bytes(32), s, w.GE, b,
-                       D, h->sigma, c.resid_rel_tol, w.VE, w.rho, w.st, ISKV_RESID_MAX_SWEEPS);
-  hipLaunchKernelGGL(make_p_kernel, dim3((D * c.b_max + 255) / 256), dim3(256), 0, s, w.E, D, b, w.VE,
-                     w.rho, w.P, c.b_max, w.st);
+    hipLaunchKernelGGL(resid_basis_kernel<32>, bz(dim3(1), h->bcount), dim3(1024), resid_lds_bytes(32), s, w.GE, b,
+                       D, h->sigma, c.resid_rel_tol, w.VE, w.rho, w.st, ISKV_RESID_MAX_SWEEPS, h->bd);
+  hipLaunchKernelGGL(make_p_kernel, bz(dim3((D * c.b_max + 255) / 256), h->bcount), dim3(256), 0, s, w.E, D, b, w.VE,
+                     w.rho, w.P, c.b_max, w.st, h->bd);
   // 6. FP = F P (b x p)
   skinny<false>(h, b, c.b_max, F, D, w.P, c.b_max, ddim(dp), D, 1.f, 0.f, nullptr, 0, w.FP, c.b_max);
   // 7. core Gram and its eigendecomposition
   {
     dim3 grid((h->m_max + 15) / 16, (h->m_max + 15) / 16);
-    hipLaunchKernelGGL(core_gram_kernel, grid, dim3(256), 0, s, w.Q, R, w.FP, c.b_max, h->sigma, b,
-                       w.A, h->ldm, w.st);
+    hipLaunchKernelGGL(core_gram_kernel, bz(grid, h->bcount), dim3(256), 0, s, w.Q, R, w.FP, c.b_max, h->sigma, b,
+                       w.A, h->ldm, w.st, h->bd);
   }
-  hipLaunchKernelGGL(set_jm_kernel, dim3(1), dim3(1), 0, s, w.st, (int)ST_M);
+  hipLaunchKernelGGL(set_jm_kernel, bz(dim3(1), h->bcount), dim3(1), 0, s, w.st, (int)ST_M, h->bd);
   {
     int rc = iskv_launch_core_eig(h);
     if (rc) return rc;
@@ -1021,13 +1061,13 @@ static int merge_body(isvd_handle* h, const float* F, const int32_t* pos_F, int3
   const int M = h->m_max;
   const Dim dn = ddim(w.st + ST_N);
   if (!(c.flags & ISKV_NO_COORD_SYNC))
-    xh_launch(s, c.n_cap, h->C, R, nullptr, 0, ddim(dk), ddim(dk), R, w.Hc, R, R, ddim(w.st + ST_KNEW),
+    xh_launch(s, h->bd, h->bcount, c.n_cap, h->C, R, nullptr, 0, ddim(dk), ddim(dk), R, w.Hc, R, R, ddim(w.st + ST_KNEW),
               dn, h->C, R, nullptr, 0);
-  xh_launch(s, b, w.Q, R, w.FP, c.b_max, ddim(dk), ddim(w.st + ST_M), M, w.Hc, R, R,
+  xh_launch(s, h->bd, h->bcount, b, w.Q, R, w.FP, c.b_max, ddim(dk), ddim(w.st + ST_M), M, w.Hc, R, R,
             ddim(w.st + ST_KNEW), hdim(b), h->C, R, nullptr, 0, h->pos, pos_F, false, dn);
-  xh_launch(s, D, h->B, R, w.P, c.b_max, ddim(dk), ddim(w.st + ST_M), M, w.Hc, R, R,
+  xh_launch(s, h->bd, h->bcount, D, h->B, R, w.P, c.b_max, ddim(dk), ddim(w.st + ST_M), M, w.Hc, R, R,
             ddim(w.st + ST_KNEW), hdim(D), h->B, R, w.Bbf, R, nullptr, nullptr, true);
-  hipLaunchKernelGGL(merge_commit_kernel, dim3(1), dim3(256), 0, s, h->sigma, w.sig_new, w.st, b, R);
+  hipLaunchKernelGGL(merge_commit_kernel, bz(dim3(1), h->bcount), dim3(256), 0, s, h->sigma, w.sig_new, w.st, b, R, h->bd);
   ISKV_HIP_CHECK(hipGetLastError());
   return ISKV_OK;
 }
@@ -1053,42 +1093,56 @@ static int reorth_body(isvd_handle* h) {
   if (nchunks > w.gram_splits - 1) nchunks = w.gram_splits - 1;
   const int rpc = (ncap + nchunks - 1) / nchunks;
   const Dim dn = ddim(w.st + ST_N);
-  hipLaunchKernelGGL(set_jm_kernel, dim3(1), dim3(1), 0, s, w.st, (int)ST_K);
-  hipLaunchKernelGGL(gram_partial_kernel, dim3(tiles * tiles, nchunks), dim3(256), 0, s, h->C, R, dn,
-                     w.st, w.GC, R, rpc);
-  hipLaunchKernelGGL(gram_partial_kernel, dim3(tiles * tiles, 1), dim3(256), 0, s, h->B, R, hdim(D), w.st,
-                     w.GC + (size_t)nchunks * R * R, R, D);
-  hipLaunchKernelGGL(reorth_sum_kernel, dim3(128), dim3(256), 0, s, w.GC, nchunks, R, w.Km, w.Pa, w.Pb,
-                     ld, w.st);
+  hipLaunchKernelGGL(set_jm_kernel, bz(dim3(1), h->bcount), dim3(1), 0, s, w.st, (int)ST_K, h->bd);
+  hipLaunchKernelGGL(gram_partial_kernel, bz(dim3(tiles * tiles, nchunks), h->bcount), dim3(256), 0, s, h->C, R, dn,
+                     w.st, w.GC, R, rpc, h->bd);
+  hipLaunchKernelGGL(gram_partial_kernel, bz(dim3(tiles * tiles, 1), h->bcount), dim3(256), 0, s, h->B, R, hdim(D), w.st,
+                     w.GC + (size_t)nchunks * R * R, R, D, h->bd);
+  hipLaunchKernelGGL(reorth_sum_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.GC, nchunks, R, w.Km, w.Pa, w.Pb,
+                     ld, w.st, h->bd);
   const int32_t* st = w.st;
   // Z = Z0 (3I - G_B Z0^2) / 2 = 1.5 Z0 - 0.5 Z0 (G_B Z0 Z0)   (second Newton-Schulz step)
-  iskv_dgemm(s, mm, w.Pa, false, w.Pb, false, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 2);
-  iskv_dgemm(s, mm, w.T, false, w.Pb, false, w.S, nullptr, ld, 1.0, 0.0, 0.0, st, 2);
-  iskv_dgemm(s, mm, w.Pb, false, w.S, false, w.Zb, w.Pb, ld, -0.5, 1.5, 0.0, st, 2);
+  iskv_dgemm(s, mm, w.Pa, false, w.Pb, false, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 2, h->bd, h->bcount);
+  iskv_dgemm(s, mm, w.T, false, w.Pb, false, w.S, nullptr, ld, 1.0, 0.0, 0.0, st, 2, h->bd, h->bcount);
+  iskv_dgemm(s, mm, w.Pb, false, w.S, false, w.Zb, w.Pb, ld, -0.5, 1.5, 0.0, st, 2, h->bd, h->bcount);
   // M_B = G_B Z;  H = M_B G_C M_B^T -> A
-  iskv_dgemm(s, mm, w.Pa, false, w.Zb, false, w.MB, nullptr, ld, 1.0, 0.0, 0.0, st, 2);
-  iskv_dgemm(s, mm, w.MB, false, w.Km, false, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 2);
-  iskv_dgemm(s, mm, w.T, false, w.MB, true, w.A, nullptr, ld, 1.0, 0.0, 0.0, st, 2);
+  iskv_dgemm(s, mm, w.Pa, false, w.Zb, false, w.MB, nullptr, ld, 1.0, 0.0, 0.0, st, 2, h->bd, h->bcount);
+  iskv_dgemm(s, mm, w.MB, false, w.Km, false, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 2, h->bd, h->bcount);
+  iskv_dgemm(s, mm, w.T, false, w.MB, true, w.A, nullptr, ld, 1.0, 0.0, 0.0, st, 2, h->bd, h->bcount);
   {
     int rc = iskv_launch_core_eig(h);
     if (rc) return rc;
   }
   eig_finish(h, 0);
-  hipLaunchKernelGGL(permute_cols_kernel, dim3(128), dim3(256), 0, s, w.V, w.order, w.W1, ld, w.st);
+  hipLaunchKernelGGL(permute_cols_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.V, w.order, w.W1, ld, w.st, h->bd);
   // T1 = M_B^T Y (coordinates), T2 = Z Y (basis)
-  iskv_dgemm(s, mm, w.MB, true, w.W1, false, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 2);
-  iskv_dgemm(s, mm, w.Zb, false, w.W1, false, w.Pa, nullptr, ld, 1.0, 0.0, 0.0, st, 2);
-  hipLaunchKernelGGL(to_f32_kernel, dim3(128), dim3(256), 0, s, w.T, w.Pa, ld, w.Hc, w.T2, R, w.st);
-  xh_launch(s, ncap, h->C, R, nullptr, 0, ddim(w.st + ST_K), ddim(w.st + ST_K), R, w.Hc, R, R,
+  iskv_dgemm(s, mm, w.MB, true, w.W1, false, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 2, h->bd, h->bcount);
+  iskv_dgemm(s, mm, w.Zb, false, w.W1, false, w.Pa, nullptr, ld, 1.0, 0.0, 0.0, st, 2, h->bd, h->bcount);
+  hipLaunchKernelGGL(to_f32_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.T, w.Pa, ld, w.Hc, w.T2, R, w.st, h->bd);
+  xh_launch(s, h->bd, h->bcount, ncap, h->C, R, nullptr, 0, ddim(w.st + ST_K), ddim(w.st + ST_K), R, w.Hc, R, R,
             ddim(w.st + ST_K), dn, h->C, R, nullptr, 0);
-  xh_launch(s, D, h->B, R, nullptr, 0, ddim(w.st + ST_K), ddim(w.st + ST_K), R, w.T2, R, R,
+  xh_launch(s, h->bd, h->bcount, D, h->B, R, nullptr, 0, ddim(w.st + ST_K), ddim(w.st + ST_K), R, w.T2, R, R,
             ddim(w.st + ST_K), hdim(D), h->B, R, w.Bbf, R, nullptr, nullptr, true);
-  hipLaunchKernelGGL(reorth_commit_kernel, dim3(1), dim3(256), 0, s, h->sigma, w.sig_new, w.st, R);
+  hipLaunchKernelGGL(reorth_commit_kernel, bz(dim3(1), h->bcount), dim3(256), 0, s, h->sigma, w.sig_new, w.st, R, h->bd);
   ISKV_HIP_CHECK(hipGetLastError());
   return ISKV_OK;
 }
 
 namespace {
+
+// Stage the pending blocks of a batch: copy z takes block z of the caller's
+// arrays (F + z F_stride, pos_F + z pos_stride) into its handle's workspace.
+__global__ void stage_batch_kernel(const float* __restrict__ F, int64_t F_stride,
+                                   const int32_t* __restrict__ pos_F, int64_t pos_stride, float* Fs,
+                                   int32_t* posFs, int count, int b, const int64_t* __restrict__ bd) {
+  const int z = blockIdx.z;
+  const int64_t d = bd[z];
+  Fs = iskv_rb(Fs, d);
+  posFs = iskv_rb(posFs, d);
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) Fs[i] = F[z * F_stride + i];
+  if (i < b) posFs[i] = pos_F[z * pos_stride + i];
+}
 
 // Stage a pending block in the workspace (the recorded merge reads it there).
 __global__ void stage_block_kernel(const float* __restrict__ F, const int32_t* __restrict__ pos_F,
@@ -1128,8 +1182,13 @@ int record(isvd_handle* h, hipGraphExec_t* exec, Body body) {
 void iskv_release_graphs(isvd_handle* h) {
   if (h->g_merge) (void)hipGraphExecDestroy(h->g_merge);
   if (h->g_reorth) (void)hipGraphExecDestroy(h->g_reorth);
+  if (h->g_batch_merge) (void)hipGraphExecDestroy(h->g_batch_merge);
+  if (h->g_batch_reorth) (void)hipGraphExecDestroy(h->g_batch_reorth);
   h->g_merge = nullptr;
   h->g_reorth = nullptr;
+  h->g_batch_merge = nullptr;
+  h->g_batch_reorth = nullptr;
+  h->g_batch_set.clear();
 }
 
 // One merge. Without graphs the sequence is enqueued directly. With graphs,
@@ -1180,4 +1239,75 @@ int iskv_launch_reorth(isvd_handle* h) {
   }
   ISKV_HIP_CHECK(hipGraphLaunch(h->g_reorth, h->stream));
   return ISKV_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Batched merges / reorths over handles with one configuration and one buffer
+// layout (every buffer of handle z lies at the same byte offset from the
+// corresponding buffer of handle 0; checked by the caller): the launch
+// sequence of one merge runs once with grid.z = count and each copy rebased
+// by its handle's offset. The offsets live in the first handle's workspace.
+namespace {
+
+int upload_offsets(isvd_handle* const* hs, int32_t count) {
+  isvd_handle* h0 = hs[0];
+  if ((int)h0->g_batch_set.size() == count &&
+      std::equal(h0->g_batch_set.begin(), h0->g_batch_set.end(), hs))
+    return ISKV_OK;
+  // a new set of handles: new offsets, and the recorded sequences are stale
+  if (h0->g_batch_merge) (void)hipGraphExecDestroy(h0->g_batch_merge);
+  if (h0->g_batch_reorth) (void)hipGraphExecDestroy(h0->g_batch_reorth);
+  h0->g_batch_merge = nullptr;
+  h0->g_batch_reorth = nullptr;
+  std::vector<int64_t> off(count);
+  for (int z = 0; z < count; ++z) off[z] = (const char*)hs[z]->ws_base - (const char*)h0->ws_base;
+  ISKV_HIP_CHECK(hipMemcpyAsync(h0->w.btab, off.data(), count * sizeof(int64_t), hipMemcpyHostToDevice,
+                                h0->stream));
+  ISKV_HIP_CHECK(hipStreamSynchronize(h0->stream));  // `off` is released on return
+  h0->g_batch_set.assign(hs, hs + count);
+  return ISKV_OK;
+}
+
+template <class Body>
+int run_batched(isvd_handle* h0, int32_t count, hipGraphExec_t* cache, Body body) {
+  h0->bd = h0->w.btab;
+  h0->bcount = count;
+  int rc = ISKV_OK;
+  if (!use_graphs(h0)) {
+    rc = body();
+  } else {
+    if (!*cache) rc = record(h0, cache, body);
+    if (rc == ISKV_OK && hipGraphLaunch(*cache, h0->stream) != hipSuccess) rc = ISKV_EHIP;
+  }
+  h0->bd = nullptr;
+  h0->bcount = 1;
+  return rc;
+}
+
+}  // namespace
+
+int iskv_launch_merge_batched(isvd_handle* const* hs, int32_t count, const float* F, int64_t F_stride,
+                              const int32_t* pos_F, int64_t pos_stride, int32_t b) {
+  isvd_handle* h0 = hs[0];
+  int rc = upload_offsets(hs, count);
+  if (rc) return rc;
+  if (h0->g_batch_merge && h0->g_batch_b != b) {
+    (void)hipGraphExecDestroy(h0->g_batch_merge);
+    h0->g_batch_merge = nullptr;
+  }
+  const int n = b * h0->cfg.D;
+  hipLaunchKernelGGL(stage_batch_kernel, dim3((n + 255) / 256, 1, count), dim3(256), 0, h0->stream, F, F_stride,
+                     pos_F, pos_stride, h0->w.Fs, h0->w.posFs, n, b, (const int64_t*)h0->w.btab);
+  ISKV_HIP_CHECK(hipGetLastError());
+  rc = run_batched(h0, count, &h0->g_batch_merge,
+                   [&]() { return merge_body(h0, h0->w.Fs, h0->w.posFs, b); });
+  if (rc == ISKV_OK) h0->g_batch_b = b;
+  return rc;
+}
+
+int iskv_launch_reorth_batched(isvd_handle* const* hs, int32_t count) {
+  isvd_handle* h0 = hs[0];
+  int rc = upload_offsets(hs, count);
+  if (rc) return rc;
+  return run_batched(h0, count, &h0->g_batch_reorth, [&]() { return reorth_body(h0); });
 }

@@ -196,6 +196,89 @@ def test_graph_replays_match_eager(K):
         pe.close()
 
 
+@pytest.mark.parametrize("graphs", [False, True])
+def test_batched_merges_match_separate(K, graphs):
+    """isvd_merge_block_batched over 5 paths (one allocation, fixed stride)
+    gives each path the factors of its own separate isvd_merge_block calls:
+    lockstep merges with a batched re-orthogonalisation every 4 merges, then
+    path 0 merged alone once (so the paths leave lockstep and later
+    re-orthogonalisations run per path), then batched merges again."""
+    cnt, D, r, b, T = 5, 128, 16, 8, 32
+    Xs = [synth.kv_stream(synth.StreamSpec(D=D, n=200, spectrum="exp4", noise_std=1e-3, seed=10 + z))
+          for z in range(cnt)]
+    Xd = torch.from_numpy(np.stack(Xs)).to(DEV)                     # [cnt, 200, D]
+    posd = torch.arange(200, dtype=torch.int32, device=DEV).repeat(cnt, 1).contiguous()
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream() if graphs else None
+    bat = K.IsvdBatch(cnt, D=D, r_max=r, b_max=b, n_cap=256, reorth_every_rows=T, device=DEV,
+                      stream=stream, graphs=graphs)
+    sep = [K.IsvdPath(D=D, r_max=r, b_max=b, n_cap=256, reorth_every_rows=T, device=DEV, graphs=False)
+           for _ in range(cnt)]
+
+    def both(z_rows):
+        s, e = z_rows
+        bat.merge(Xd[:, s:e], posd[:, s:e])
+        for z in range(cnt):
+            sep[z].merge(Xd[z, s:e], posd[z, s:e])
+
+    for s in range(0, 96, b):           # 12 lockstep merges (3 batched reorths)
+        both((s, s + b))
+    bat[0].merge(Xd[0, 96:104], posd[0, 96:104])
+    sep[0].merge(Xd[0, 96:104], posd[0, 96:104])
+    # path 0 is now one block ahead in rows: batched merges continue with
+    # staggered re-orthogonalisation; each path keeps its own row count
+    for s in range(104, 200 - b + 1, b):
+        bat.merge(Xd[:, s:s + b], posd[:, s:s + b])
+        for z in range(cnt):
+            sep[z].merge(Xd[z, s:s + b], posd[z, s:s + b])
+    if stream is not None:
+        stream.synchronize()
+    torch.cuda.synchronize()
+    for z in range(cnt):
+        Cb, Bb, sb, pb, stb = gpu_factors(bat[z])
+        Cs, Bs, ss, ps, sts = gpu_factors(sep[z])
+        assert stb == 0 and sts == 0
+        assert Cb.shape == Cs.shape and np.array_equal(pb, ps)
+        err = rel(Cb @ Bb.T, Cs @ Bs.T)
+        assert err < 1e-6, (z, err)
+        assert np.allclose(sb, ss, rtol=1e-6)
+        assert bat[z].query()[:2] == sep[z].query()[:2]
+    # against the oracle for one path that took the staggered schedule
+    C0, B0, _, _, _ = gpu_factors(bat[0])
+    n0 = C0.shape[0]
+    Xo = Xs[0][:n0]
+    ref = O.represented(O.run_stream(Xo, b, r, reorth_every_rows=T))
+    assert rel(C0 @ B0.T, ref) < 1e-3
+    bat.close()
+    for p in sep:
+        p.close()
+
+
+def test_batched_merge_rejects_bad_sets(K):
+    """Handles of separate allocations (no common offset), repeated handles and
+    a capacity overflow are refused before anything runs."""
+    a = K.IsvdPath(D=64, r_max=8, b_max=8, n_cap=16, device=DEV)
+    c = K.IsvdPath(D=64, r_max=8, b_max=8, n_cap=16, device=DEV)
+    bat = K.IsvdBatch(2, D=64, r_max=8, b_max=8, n_cap=16, device=DEV)
+    F = torch.randn((2, 8, 64), dtype=torch.float32, device=DEV)
+    P = torch.arange(16, dtype=torch.int32, device=DEV).view(2, 8)
+    with pytest.raises(K.IskvError):
+        K.isvd_merge_block_batched([a.h, c.h, bat[0].h], F, 512, P, 8, 8)
+    with pytest.raises(K.IskvError):
+        K.isvd_merge_block_batched([bat[0].h, bat[0].h], F, 512, P, 8, 8)
+    with pytest.raises(K.IskvError):
+        K.isvd_merge_block_batched(bat.handles, F, 100, P, 8, 8)   # F_stride < b*D
+    bat.merge(F, P)
+    bat.merge(F, P)
+    with pytest.raises(K.IskvError):
+        bat.merge(F, P)                                           # n + b > n_cap
+    torch.cuda.synchronize()
+    assert [p.query()[0] for p in bat.paths] == [16, 16]
+    for p in (a, c):
+        p.close()
+    bat.close()
+
+
 # --------------------------------------------------------------------------- reorth
 def test_reorth_keeps_product_and_orthonormalises(K):
     X = synth.kv_stream(synth.StreamSpec(D=256, n=1024, spectrum="exp40+0.01", noise_std=0.0, seed=2))
