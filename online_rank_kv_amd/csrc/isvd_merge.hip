@@ -96,25 +96,39 @@ __global__ __launch_bounds__(256) void resid_gram_kernel(const float* __restrict
 // Residual basis (iS-KV notes §4.1): the residual directions of E^T with
 // singular values rho_j above tau = max(delta s, max(D, b) 2^-23 s),
 // s = max(sigma_1, rho_1), capped at p <= min(b, D - k). Published through
-// V_E (b x b, eigenvectors of E E^T by descending eigenvalue) and rho, so that
-// P = E^T V_E diag(1/rho) (make_p_kernel).
+// V_E (b x b) and rho, so that P = E^T V_E diag(1/rho) (make_p_kernel).
 //
-// The eigendecomposition of the b x b Gram E E^T (b <= 2 HB) is a parallel
-// two-sided Jacobi in the systolic (Brent-Luk) arrangement: thread (I, J) of
-// the HB x HB workgroup owns the 2 x 2 blocks at rows 2I, 2I+1 and columns
-// 2J, 2J+1 of the working matrix S and of the eigenvector matrix V. Each
-// round, every thread computes from the diagonal blocks the rotations of its
-// pairs I and J (the symmetric 2 x 2 Schur rotation of Golub-Van Loan, see
-// schur2; each rotation is computed by every thread that needs it, from the
-// same data, so all agree), applies S <- J_I^T S J_J and V <- V J_J to its
-// blocks, and
+// Both phases below diagonalise the b x b Gram E E^T (b <= 2 HB) by a
+// parallel two-sided Jacobi in the systolic (Brent-Luk) arrangement: thread
+// (I, J) of the HB x HB workgroup owns the 2 x 2 blocks at rows 2I, 2I+1 and
+// columns 2J, 2J+1 of the working matrix S and of the eigenvector matrix V.
+// Each round, every thread computes from the diagonal blocks the rotations of
+// its pairs I and J (the symmetric 2 x 2 Schur rotation of Golub-Van Loan;
+// each rotation is computed by every thread that needs it, from the same data,
+// so all agree), applies S <- J_I^T S J_J and V <- V J_J to its blocks, and
 // writes them to the positions of the next pairing of the round-robin
 // (circle) schedule, so that 2 HB - 1 rounds pair every two indices once (one
-// sweep). S and V are double-buffered in LDS: one barrier per round. Sweeps
-// repeat until none rotates; an off-diagonal is rotated away when it exceeds
-// 1e-13 of the geometric mean of its diagonal pair and 1e-15 of the trace
-// (below that it is at round-off level of the whole Gram). The Gram is
-// zero-padded to 2 HB; padded indices never couple and are dropped.
+// sweep). S and V are double-buffered in LDS: one barrier per round. The
+// circle schedule moves every position through one cycle of length 2 HB - 1,
+// so after each whole sweep every index is back at its own position. The Gram
+// is zero-padded to 2 HB; padded indices never couple and are dropped.
+//
+// Phase 1 (when every residual direction can be kept, b <= D - k): sweeps in
+// fp32 on S / trace until every scaled coupling |s_ij| / sqrt(s_ii s_jj) is
+// below 3e-5, then S = V^T (E E^T) V is formed in fp64 from the fp32 V. If
+// its couplings are below 1e-4 and Gershgorin's lower bound of its spectrum
+// lies above tau^2 (tau from the upper bound of rho_1), then p = b and P only
+// has to be an orthonormal basis of span(E^T), whose choice does not change
+// the merge (the core changes by a rotation of its last b columns).
+// P = E^T V S^-1/2 is one for any nonsingular V; S^-1/2 is taken as
+// D^-1/2 (I - O/2 + 3 O^2 / 8) with D = diag(S), O = D^-1/2 S D^-1/2 - I
+// (error 5/16 |O|^3), so rho = 1, and the core block (F P)^T (F P) stays
+// nearly diagonal for the core eigensolver.
+// Phase 2 (otherwise: a rank decision is needed, the residual is nearly
+// degenerate, or phase 1 did not certify): fp64 sweeps from the Gram until
+// none rotates; an off-diagonal is rotated away when it exceeds 1e-13 of the
+// geometric mean of its diagonal pair and 1e-15 of the trace. Eigenvalues are
+// ranked and thresholded exactly.
 // Round-robin move of position x: pairs are (2k, 2k+1); position 0 stays, the
 // others cycle 1 -> 2 -> 4 -> ... -> 2h-2 -> 2h-1 -> 2h-3 -> ... -> 3 -> 1.
 __device__ __forceinline__ int rr_next(int x, int h) {
@@ -124,7 +138,7 @@ __device__ __forceinline__ int rr_next(int x, int h) {
   return x - 2;
 }
 
-// Rotation [[c, s], [-s, c]] with J^T [[app, apq], [apq, aqq]] J (nearly)
+// fp64 rotation [[c, s], [-s, c]] with J^T [[app, apq], [apq, aqq]] J (nearly)
 // diagonal. With d = aqq - app, r = sqrt(d^2 + 4 apq^2) and w = |d| + r, the
 // annihilating rotation has c = w / sqrt(2 r w), s = sign(d) 2 apq / sqrt(2 r w).
 // The angle is computed in fp32 on the inputs scaled by 1/trace (so they lie
@@ -151,7 +165,34 @@ __device__ __forceinline__ bool schur2(double app, double apq, double aqq, doubl
   return rot;
 }
 
-static inline size_t resid_lds_bytes(int hb) { return (size_t)4 * (2 * hb) * (2 * hb + 1) * sizeof(double); }
+// The same rotation in fp32 for phase 1 (orthogonal to fp32 precision, which
+// phase 1 does not need: V only has to be nonsingular). Rotates when the
+// scaled coupling exceeds 1e-5.
+__device__ __forceinline__ bool schur2f(float app, float apq, float aqq, float& c, float& sn) {
+  const bool rot = apq * apq > 1e-10f * fabsf(app * aqq) && apq != 0.0f;
+  const float d = aqq - app;
+  const float r = __builtin_amdgcn_sqrtf(fmaf(d, d, 4.0f * apq * apq));
+  const float w = fabsf(d) + r;
+  const float rq = __frsqrt_rn(2.0f * r * w);
+  c = rot ? w * rq : 1.0f;
+  sn = rot ? (d >= 0.0f ? 2.0f : -2.0f) * apq * rq : 0.0f;
+  return rot;
+}
+
+constexpr int RB32_MAX_SWEEPS = 12;
+
+// LDS layout (dynamic): phase 1 uses fp32 S[2][N][LF], V[2][N][LF] at the
+// start and fp64 G[N][L], T[N][L] after them; phase 2 reuses the start for
+// fp64 S[2][N][L], V[2][N][L]. LF = N + 16 for N = 32 puts the two rows a
+// 64-lane read touches on opposite halves of the banks; for N = 64 one row
+// fills a half-wave.
+template <int HB> constexpr int rb_lf() { return HB == 16 ? 48 : 2 * HB + 2; }
+static inline size_t resid_lds_bytes(int hb) {
+  const size_t n = 2 * hb, l = n + 1, lf = hb == 16 ? 48 : n + 2;
+  const size_t p1 = 4 * n * lf * sizeof(float) + 2 * n * l * sizeof(double);
+  const size_t p2 = 4 * n * l * sizeof(double);
+  return p1 > p2 ? p1 : p2;
+}
 
 template <int HB>
 __global__ __launch_bounds__(HB * HB) void resid_basis_kernel(const double* __restrict__ GE, int b,
@@ -165,37 +206,197 @@ __global__ __launch_bounds__(HB * HB) void resid_basis_kernel(const double* __re
   VE = iskv_rb(VE, bdel);
   rho = iskv_rb(rho, bdel);
   st = iskv_rb(st, bdel);
-  constexpr int N = 2 * HB, L = N + 1;
+  constexpr int N = 2 * HB, L = N + 1, LF = rb_lf<HB>();
+  constexpr int NW = HB * HB / 64;
   extern __shared__ double rb_lds[];
-  double* Sb = rb_lds;              // [2][N][L]
-  double* Vb = rb_lds + 2 * N * L;  // [2][N][L]
   __shared__ double lam[N];
-  __shared__ int posof[N], order[N];
+  __shared__ int order[N];
+  __shared__ double wred[3][NW];
   const int t = threadIdx.x, I = t / HB, J = t % HB;
   const int r0 = 2 * I, r1 = r0 + 1, c0 = 2 * J, c1 = c0 + 1;
+  const int pr0 = rr_next(r0, HB), pr1 = rr_next(r1, HB), pc0 = rr_next(c0, HB), pc1 = rr_next(c1, HB);
   auto g = [&](int i, int j) { return (i < b && j < b) ? GE[i * b + j] : 0.0; };
-  double x11 = g(r0, c0), x12 = g(r0, c1), x21 = g(r1, c0), x22 = g(r1, c1);
-  const int nonzero = __syncthreads_or(x11 != 0.0 || x12 != 0.0 || x21 != 0.0 || x22 != 0.0);
+  const double g11 = g(r0, c0), g12 = g(r0, c1), g21 = g(r1, c0), g22 = g(r1, c1);
+  const int nonzero = __syncthreads_or(g11 != 0.0 || g12 != 0.0 || g21 != 0.0 || g22 != 0.0);
   const int k = st[ST_K];
   if (!nonzero || k >= D) {
     if (t == 0) { st[ST_P] = 0; st[ST_M] = k; st[ST_EZERO] = nonzero ? 0 : 1; }
     return;
   }
-  Sb[r0 * L + c0] = x11; Sb[r0 * L + c1] = x12; Sb[r1 * L + c0] = x21; Sb[r1 * L + c1] = x22;
-  Vb[r0 * L + c0] = r0 == c0; Vb[r0 * L + c1] = 0.0; Vb[r1 * L + c0] = 0.0; Vb[r1 * L + c1] = r1 == c1;
-  if (I == J) { lam[r0] = x11; lam[r1] = x22; }
+  if (I == J) { lam[r0] = g11; lam[r1] = g22; }
   __syncthreads();
   double trace = 0.0;
   for (int i = 0; i < N; ++i) trace += fabs(lam[i]);
-  const double abs_tol = 1e-15 * trace;
   const double inv_tr = 1.0 / trace;
-  int mypos = t;  // threads t < N follow where original index t sits
-  int cur = 0, sweeps = 0;
   const double s1 = (k > 0) ? (double)sigma[0] : 0.0;
   const double tfac = fmax((double)delta, (double)(D > b ? D : b) * 1.1920928955078125e-07);
-  __shared__ int orig_at[N];
-  __shared__ double wred[3][HB * HB / 64];
-  bool fast = false;
+  int sweeps = 0;
+  __syncthreads();  // lam is rewritten below
+
+  // ---------------------------------------------------------------- phase 1
+  if (b <= D - k) {
+    float* Sf = (float*)rb_lds;  // [2][N][LF]
+    float* Vf = Sf + 2 * N * LF;  // [2][N][LF]
+    double* G64 = rb_lds + 2 * N * LF;  // [N][L] (after the fp32 buffers)
+    double* T64 = G64 + N * L;          // [N][L]
+    {
+      const float f = (float)inv_tr;
+      Sf[r0 * LF + c0] = (float)g11 * f; Sf[r0 * LF + c1] = (float)g12 * f;
+      Sf[r1 * LF + c0] = (float)g21 * f; Sf[r1 * LF + c1] = (float)g22 * f;
+      Vf[r0 * LF + c0] = r0 == c0; Vf[r0 * LF + c1] = 0.0f; Vf[r1 * LF + c0] = 0.0f; Vf[r1 * LF + c1] = r1 == c1;
+      G64[r0 * L + c0] = g11; G64[r0 * L + c1] = g12; G64[r1 * L + c0] = g21; G64[r1 * L + c1] = g22;
+    }
+    __syncthreads();
+    int cur = 0;
+    for (int sweep = 0; sweep < RB32_MAX_SWEEPS; ++sweep) {
+      ++sweeps;
+      int rotated = 0;
+      for (int round = 0; round < N - 1; ++round) {
+        const float* S = Sf + cur * N * LF;
+        const float* V = Vf + cur * N * LF;
+        const float ap = S[r0 * LF + r0], apq = S[r0 * LF + r1], aq = S[r1 * LF + r1];
+        const float bp = S[c0 * LF + c0], bpq = S[c0 * LF + c1], bq = S[c1 * LF + c1];
+        float x11 = S[r0 * LF + c0], x12 = S[r0 * LF + c1], x21 = S[r1 * LF + c0], x22 = S[r1 * LF + c1];
+        float v11 = V[r0 * LF + c0], v12 = V[r0 * LF + c1], v21 = V[r1 * LF + c0], v22 = V[r1 * LF + c1];
+        float ca, sa, cb, sb;
+        rotated |= schur2f(ap, apq, aq, ca, sa);
+        schur2f(bp, bpq, bq, cb, sb);
+        {
+          const float y11 = ca * x11 - sa * x21, y12 = ca * x12 - sa * x22;
+          const float y21 = sa * x11 + ca * x21, y22 = sa * x12 + ca * x22;
+          x11 = y11 * cb - y12 * sb; x12 = y11 * sb + y12 * cb;
+          x21 = y21 * cb - y22 * sb; x22 = y21 * sb + y22 * cb;
+        }
+        if (I == J) {
+          const float m = 0.5f * (x12 + x21);
+          x12 = m; x21 = m;
+        }
+        {
+          const float w11 = v11 * cb - v12 * sb, w12 = v11 * sb + v12 * cb;
+          const float w21 = v21 * cb - v22 * sb, w22 = v21 * sb + v22 * cb;
+          v11 = w11; v12 = w12; v21 = w21; v22 = w22;
+        }
+        cur ^= 1;
+        float* So = Sf + cur * N * LF;
+        float* Vo = Vf + cur * N * LF;
+        So[pr0 * LF + pc0] = x11; So[pr0 * LF + pc1] = x12; So[pr1 * LF + pc0] = x21; So[pr1 * LF + pc1] = x22;
+        Vo[r0 * LF + pc0] = v11; Vo[r0 * LF + pc1] = v12; Vo[r1 * LF + pc0] = v21; Vo[r1 * LF + pc1] = v22;
+        __syncthreads();
+      }
+      if (!__syncthreads_or(rotated)) break;
+      if (sweep >= 2) {  // largest scaled coupling left
+        const float* S = Sf + cur * N * LF;
+        auto cpl = [&](int i, int j) {
+          return (i != j && i < b && j < b)
+                     ? fabsf(S[i * LF + j]) / sqrtf(fabsf(S[i * LF + i] * S[j * LF + j]) + 1e-37f) : 0.0f;
+        };
+        float om = fmaxf(fmaxf(cpl(r0, c0), cpl(r0, c1)), fmaxf(cpl(r1, c0), cpl(r1, c1)));
+        if (__syncthreads_and(!(om >= 3e-5f))) break;  // NaN stays in the loop, fails below
+      }
+    }
+    const float* Vc = Vf + cur * N * LF;
+    // T = G V (fp64), then this thread's block of S = V^T T
+    {
+      double t11 = 0.0, t12 = 0.0, t21 = 0.0, t22 = 0.0;
+      for (int a = 0; a < N; ++a) {
+        const double ga0 = G64[r0 * L + a], ga1 = G64[r1 * L + a];
+        const double va0 = Vc[a * LF + c0], va1 = Vc[a * LF + c1];
+        t11 = fma(ga0, va0, t11); t12 = fma(ga0, va1, t12);
+        t21 = fma(ga1, va0, t21); t22 = fma(ga1, va1, t22);
+      }
+      T64[r0 * L + c0] = t11; T64[r0 * L + c1] = t12; T64[r1 * L + c0] = t21; T64[r1 * L + c1] = t22;
+    }
+    __syncthreads();
+    double y11 = 0.0, y12 = 0.0, y21 = 0.0, y22 = 0.0;
+    for (int a = 0; a < N; ++a) {
+      const double va0 = Vc[a * LF + r0], va1 = Vc[a * LF + r1];
+      const double ta0 = T64[a * L + c0], ta1 = T64[a * L + c1];
+      y11 = fma(va0, ta0, y11); y12 = fma(va0, ta1, y12);
+      y21 = fma(va1, ta0, y21); y22 = fma(va1, ta1, y22);
+    }
+    if (I == J) { lam[r0] = y11; lam[r1] = y22; }
+    __syncthreads();
+    const bool q0 = r0 < b, q1 = r1 < b, p0 = c0 < b, p1 = c1 < b;
+    const double d0 = lam[r0], d1 = lam[r1], e0 = lam[c0], e1 = lam[c1];
+    auto relo = [&](double v, double da, double db, bool ra, bool cb, bool diag) {
+      return (ra && cb && !diag) ? fabs(v) / sqrt(fabs(da * db)) : 0.0;
+    };
+    double offm = fmax(fmax(relo(y11, d0, e0, q0, p0, r0 == c0), relo(y12, d0, e1, q0, p1, r0 == c1)),
+                       fmax(relo(y21, d1, e0, q1, p0, r1 == c0), relo(y22, d1, e1, q1, p1, r1 == c1)));
+    double rs0 = ((p0 && c0 != r0) ? fabs(y11) : 0.0) + ((p1 && c1 != r0) ? fabs(y12) : 0.0);
+    double rs1 = ((p0 && c0 != r1) ? fabs(y21) : 0.0) + ((p1 && c1 != r1) ? fabs(y22) : 0.0);
+#pragma unroll
+    for (int o = 1; o < HB; o <<= 1) {
+      rs0 += __shfl_xor(rs0, o, 64);
+      rs1 += __shfl_xor(rs1, o, 64);
+    }
+    double lo = INFINITY, hi = 0.0;
+    if (J == 0) {
+      if (q0) { lo = fmin(lo, d0 - rs0); hi = fmax(hi, d0 + rs0); }
+      if (q1) { lo = fmin(lo, d1 - rs1); hi = fmax(hi, d1 + rs1); }
+    }
+    if (isnan(offm)) offm = INFINITY;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      offm = fmax(offm, __shfl_xor(offm, o, 64));
+      lo = fmin(lo, __shfl_xor(lo, o, 64));
+      hi = fmax(hi, __shfl_xor(hi, o, 64));
+    }
+    if ((t & 63) == 0) { wred[0][t >> 6] = offm; wred[1][t >> 6] = lo; wred[2][t >> 6] = hi; }
+    __syncthreads();
+    double om = 0.0, lm = INFINITY, hm = 0.0;
+    for (int w = 0; w < NW; ++w) {
+      om = fmax(om, wred[0][w]);
+      lm = fmin(lm, wred[1][w]);
+      hm = fmax(hm, wred[2][w]);
+    }
+    const double tau_hi = tfac * fmax(s1, sqrt(hm));
+    if (om < 1e-4 && lm > tau_hi * tau_hi) {  // same decision in every thread
+      // O = D^-1/2 S D^-1/2 - I over the real indices (into G64's place),
+      // Z = D^-1/2 (I - O/2 + 3 O^2 / 8) (into T64's place), V_E = V Z.
+      double* Ob = G64;
+      double* Zb = T64;
+      const double sr0 = q0 ? 1.0 / sqrt(d0) : 0.0, sr1 = q1 ? 1.0 / sqrt(d1) : 0.0;
+      const double sc0 = p0 ? 1.0 / sqrt(e0) : 0.0, sc1 = p1 ? 1.0 / sqrt(e1) : 0.0;
+      const double o11 = r0 == c0 ? 0.0 : y11 * sr0 * sc0, o12 = r0 == c1 ? 0.0 : y12 * sr0 * sc1;
+      const double o21 = r1 == c0 ? 0.0 : y21 * sr1 * sc0, o22 = r1 == c1 ? 0.0 : y22 * sr1 * sc1;
+      Ob[r0 * L + c0] = o11; Ob[r0 * L + c1] = o12; Ob[r1 * L + c0] = o21; Ob[r1 * L + c1] = o22;
+      __syncthreads();
+      double q11 = 0.0, q12 = 0.0, q21 = 0.0, q22 = 0.0;
+      for (int x = 0; x < N; ++x) {
+        const double a0 = Ob[r0 * L + x], a1 = Ob[r1 * L + x], b0 = Ob[x * L + c0], b1 = Ob[x * L + c1];
+        q11 = fma(a0, b0, q11); q12 = fma(a0, b1, q12); q21 = fma(a1, b0, q21); q22 = fma(a1, b1, q22);
+      }
+      auto zv = [&](int r, int c, double o, double o2, double sr) {
+        return sr * ((r == c ? 1.0 : 0.0) - 0.5 * o + 0.375 * o2);
+      };
+      Zb[r0 * L + c0] = zv(r0, c0, o11, q11, sr0);
+      Zb[r0 * L + c1] = zv(r0, c1, o12, q12, sr0);
+      Zb[r1 * L + c0] = zv(r1, c0, o21, q21, sr1);
+      Zb[r1 * L + c1] = zv(r1, c1, o22, q22, sr1);
+      __syncthreads();
+      for (int idx = t; idx < b * b; idx += HB * HB) {
+        const int row = idx / b, j = idx % b;
+        double acc = 0.0;
+        for (int x = 0; x < N; ++x) acc = fma((double)Vc[row * LF + x], Zb[x * L + j], acc);
+        VE[row * b + j] = acc;
+      }
+      if (t < b) rho[t] = 1.0;
+      if (t == 0) { st[ST_P] = b; st[ST_M] = k + b; st[ST_EZERO] = 0; st[ST_RSWEEPS] = sweeps; }
+      return;
+    }
+    __syncthreads();  // phase 2 reuses the LDS
+  }
+
+  // ---------------------------------------------------------------- phase 2
+  double* Sb = rb_lds;              // [2][N][L]
+  double* Vb = rb_lds + 2 * N * L;  // [2][N][L]
+  double x11 = g11, x12 = g12, x21 = g21, x22 = g22;
+  Sb[r0 * L + c0] = x11; Sb[r0 * L + c1] = x12; Sb[r1 * L + c0] = x21; Sb[r1 * L + c1] = x22;
+  Vb[r0 * L + c0] = r0 == c0; Vb[r0 * L + c1] = 0.0; Vb[r1 * L + c0] = 0.0; Vb[r1 * L + c1] = r1 == c1;
+  __syncthreads();
+  const double abs_tol = 1e-15 * trace;
+  int cur = 0;
   for (int sweep = 0; sweep < max_sweeps; ++sweep) {
     ++sweeps;
     int rotated = 0;
@@ -208,9 +409,8 @@ __global__ __launch_bounds__(HB * HB) void resid_basis_kernel(const double* __re
       x11 = S[r0 * L + c0]; x12 = S[r0 * L + c1]; x21 = S[r1 * L + c0]; x22 = S[r1 * L + c1];
       double v11 = V[r0 * L + c0], v12 = V[r0 * L + c1], v21 = V[r1 * L + c0], v22 = V[r1 * L + c1];
       double ca, sa, cb, sb;
-      const bool rot_a = schur2(ap, apq, aq, abs_tol, inv_tr, ca, sa);
+      rotated |= schur2(ap, apq, aq, abs_tol, inv_tr, ca, sa);
       schur2(bp, bpq, bq, abs_tol, inv_tr, cb, sb);
-      rotated |= rot_a;
       {  // S <- J_I^T S J_J on this block
         const double y11 = ca * x11 - sa * x21, y12 = ca * x12 - sa * x22;
         const double y21 = sa * x11 + ca * x21, y22 = sa * x12 + ca * x22;
@@ -230,109 +430,17 @@ __global__ __launch_bounds__(HB * HB) void resid_basis_kernel(const double* __re
       cur ^= 1;
       double* So = Sb + cur * N * L;
       double* Vo = Vb + cur * N * L;
-      const int pr0 = rr_next(r0, HB), pr1 = rr_next(r1, HB);
-      const int pc0 = rr_next(c0, HB), pc1 = rr_next(c1, HB);
       So[pr0 * L + pc0] = x11; So[pr0 * L + pc1] = x12; So[pr1 * L + pc0] = x21; So[pr1 * L + pc1] = x22;
       Vo[r0 * L + pc0] = v11; Vo[r0 * L + pc1] = v12; Vo[r1 * L + pc0] = v21; Vo[r1 * L + pc1] = v22;
-      if (t < N) mypos = rr_next(mypos, HB);
       __syncthreads();
     }
     if (!__syncthreads_or(rotated)) break;
-    // Early exit when every residual direction is kept (no threshold decision
-    // is close): with S = V^T (E E^T) V nearly diagonal (largest off-diagonal
-    // below 1e-4 of the geometric mean of its diagonal pair) and Gershgorin's
-    // lower bound of its spectrum above tau^2 (tau from the upper bound of
-    // rho_1), p = b and P only has to be an orthonormal basis of span(E^T),
-    // whose choice does not change the merge (the core changes by a rotation
-    // of its last b columns). P = E^T V S^-1/2 is one; its block of the core,
-    // (F P)^T (F P) = S, stays nearly diagonal for the core eigensolver.
-    if (sweep >= 1 && b <= D - k) {
-      if (t < N) orig_at[mypos] = t;
-      __syncthreads();
-      const double* S = Sb + cur * N * L;
-      const double d0 = S[r0 * L + r0], d1 = S[r1 * L + r1], e0 = S[c0 * L + c0], e1 = S[c1 * L + c1];
-      const bool q0 = orig_at[r0] < b, q1 = orig_at[r1] < b, p0 = orig_at[c0] < b, p1 = orig_at[c1] < b;
-      const double y11 = S[r0 * L + c0], y12 = S[r0 * L + c1], y21 = S[r1 * L + c0], y22 = S[r1 * L + c1];
-      double offm = 0.0;
-      auto relo = [&](double v, double da, double db, bool ra, bool cb, bool diag) {
-        return (ra && cb && !diag) ? fabs(v) / sqrt(fabs(da * db)) : 0.0;
-      };
-      offm = fmax(fmax(relo(y11, d0, e0, q0, p0, r0 == c0), relo(y12, d0, e1, q0, p1, r0 == c1)),
-                  fmax(relo(y21, d1, e0, q1, p0, r1 == c0), relo(y22, d1, e1, q1, p1, r1 == c1)));
-      double rs0 = ((p0 && c0 != r0) ? fabs(y11) : 0.0) + ((p1 && c1 != r0) ? fabs(y12) : 0.0);
-      double rs1 = ((p0 && c0 != r1) ? fabs(y21) : 0.0) + ((p1 && c1 != r1) ? fabs(y22) : 0.0);
-#pragma unroll
-      for (int o = 1; o < HB; o <<= 1) {
-        rs0 += __shfl_xor(rs0, o, 64);
-        rs1 += __shfl_xor(rs1, o, 64);
-      }
-      double lo = INFINITY, hi = 0.0;
-      if (J == 0) {
-        if (q0) { lo = fmin(lo, d0 - rs0); hi = fmax(hi, d0 + rs0); }
-        if (q1) { lo = fmin(lo, d1 - rs1); hi = fmax(hi, d1 + rs1); }
-      }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        offm = fmax(offm, __shfl_xor(offm, o, 64));
-        lo = fmin(lo, __shfl_xor(lo, o, 64));
-        hi = fmax(hi, __shfl_xor(hi, o, 64));
-      }
-      if ((t & 63) == 0) { wred[0][t >> 6] = offm; wred[1][t >> 6] = lo; wred[2][t >> 6] = hi; }
-      __syncthreads();
-      double om = 0.0, lm = INFINITY, hm = 0.0;
-      for (int w = 0; w < HB * HB / 64; ++w) {
-        om = fmax(om, wred[0][w]);
-        lm = fmin(lm, wred[1][w]);
-        hm = fmax(hm, wred[2][w]);
-      }
-      const double tau_hi = tfac * fmax(s1, sqrt(hm));
-      fast = om < 1e-4 && lm > tau_hi * tau_hi;  // same value in every thread
-      __syncthreads();
-      if (fast) break;
-    }
   }
+  // whole sweeps only: original index j sits at position j
   const double* S = Sb + cur * N * L;
   const double* V = Vb + cur * N * L;
-  // original index j < b sits at position posof[j]
-  if (t < N) posof[t] = mypos;
   if (t == 0) st[ST_RSWEEPS] = sweeps;
-  __syncthreads();
-  if (fast) {
-    // O = D^-1/2 S D^-1/2 - I over the real positions; Z = D^-1/2 (I - O/2 + 3 O^2/8)
-    // approximates S^-1/2 (error 5/16 |O|^3); V_E = V Z, rho = 1.
-    double* Ob = Sb + (cur ^ 1) * N * L;
-    double* Zb = Vb + (cur ^ 1) * N * L;
-    auto rsd = [&](int x) { return orig_at[x] < b ? 1.0 / sqrt(S[x * L + x]) : 0.0; };
-    const double sr0 = rsd(r0), sr1 = rsd(r1), sc0 = rsd(c0), sc1 = rsd(c1);
-    Ob[r0 * L + c0] = r0 == c0 ? 0.0 : S[r0 * L + c0] * sr0 * sc0;
-    Ob[r0 * L + c1] = r0 == c1 ? 0.0 : S[r0 * L + c1] * sr0 * sc1;
-    Ob[r1 * L + c0] = r1 == c0 ? 0.0 : S[r1 * L + c0] * sr1 * sc0;
-    Ob[r1 * L + c1] = r1 == c1 ? 0.0 : S[r1 * L + c1] * sr1 * sc1;
-    __syncthreads();
-    double o11 = 0.0, o12 = 0.0, o21 = 0.0, o22 = 0.0;
-    for (int x = 0; x < N; ++x) {
-      const double a0 = Ob[r0 * L + x], a1 = Ob[r1 * L + x], b0 = Ob[x * L + c0], b1 = Ob[x * L + c1];
-      o11 = fma(a0, b0, o11); o12 = fma(a0, b1, o12); o21 = fma(a1, b0, o21); o22 = fma(a1, b1, o22);
-    }
-    auto zv = [&](int r, int c, double o, double o2, double sr) {
-      return sr * ((r == c ? 1.0 : 0.0) - 0.5 * o + 0.375 * o2);
-    };
-    Zb[r0 * L + c0] = zv(r0, c0, Ob[r0 * L + c0], o11, sr0);
-    Zb[r0 * L + c1] = zv(r0, c1, Ob[r0 * L + c1], o12, sr0);
-    Zb[r1 * L + c0] = zv(r1, c0, Ob[r1 * L + c0], o21, sr1);
-    Zb[r1 * L + c1] = zv(r1, c1, Ob[r1 * L + c1], o22, sr1);
-    __syncthreads();
-    for (int idx = t; idx < b * b; idx += HB * HB) {
-      const int row = idx / b, j = idx % b, pj = posof[j];
-      double acc = 0.0;
-      for (int x = 0; x < N; ++x) acc = fma(V[row * L + x], Zb[x * L + pj], acc);
-      VE[row * b + j] = acc;
-    }
-    if (t < b) rho[t] = 1.0;
-    if (t == 0) { st[ST_P] = b; st[ST_M] = k + b; st[ST_EZERO] = 0; }
-    return;
-  }
-  if (t < b) lam[t] = S[posof[t] * L + posof[t]];
+  if (t < b) lam[t] = S[t * L + t];
   __syncthreads();
   // rank by descending eigenvalue, ties by index (NaN last)
   if (t < b) {
@@ -347,7 +455,7 @@ __global__ __launch_bounds__(HB * HB) void resid_basis_kernel(const double* __re
   __syncthreads();
   for (int idx = t; idx < b * b; idx += HB * HB) {
     const int row = idx / b, col = idx % b;
-    VE[row * b + col] = V[row * L + posof[min(max(order[col], 0), b - 1)]];
+    VE[row * b + col] = V[row * L + min(max(order[col], 0), b - 1)];
   }
   if (t < b) rho[t] = sqrt(fmax(lam[min(max(order[t], 0), b - 1)], 0.0));
   if (t == 0) {
