@@ -38,6 +38,8 @@ HQ, HKV, DH, THETA = 32, 8, 128, 500000.0
 HBM_PEAK_GBPS = 8000.0
 CALIB_BYTES = 256 << 20
 BF16_PEAK_TFLOPS = 2500.0
+FP32_PEAK_TFLOPS = 157.3
+TIMED_MERGES = 8  # K merges run once more with stage events after the timed region
 
 
 def parse():
@@ -53,12 +55,12 @@ def parse():
     return ap.parse_args()
 
 
-def recon_traffic():
-    """HBM bytes per reconstruction dispatch from the committed rocprofv3 counter
-    summary, or None when the kernel source changed since it was measured."""
+def profiled_traffic(name):
+    """HBM bytes per dispatch from a committed rocprofv3 counter summary under
+    profiles/, or None when the kernel source changed since it was measured."""
     import hashlib
     import re
-    prof = os.path.join(ROOT, "profiles", "recon_mfma_kernel_kv_n16k_traffic.md")
+    prof = os.path.join(ROOT, "profiles", name)
     try:
         text = open(prof).read()
         d = json.loads(re.search(r"```json\n(.*?)\n```", text, re.S).group(1))
@@ -124,7 +126,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     steps, warm = args.steps, args.warmup
-    n_rows = N0 + (steps + warm + 4) * BLK + WIN
+    n_rows = N0 + (steps + warm + 4 + TIMED_MERGES) * BLK + WIN
     t_gen = time.perf_counter()
     Xk = synth.kv_stream(synth.StreamSpec(D, n_rows, "exp40+0.01", 0.0, 0))
     Xv = synth.kv_stream(synth.StreamSpec(D, n_rows, "invsqrt", 0.0, 1))
@@ -215,6 +217,26 @@ def main():
     def avg_ms(key):
         return float(np.mean([a.elapsed_time(b) for a, b in ev[key]]))
 
+    # stage breakdown of K merges (outside the timed region): the handle runs
+    # its merges kernel by kernel with HIP events at the stage boundaries
+    stage_runs = []
+    n_before = []
+    paths[0].set_timing(True)
+    for _ in range(TIMED_MERGES):
+        s0 = cursor[0]
+        n_before.append(paths[0].n)
+        wins[0].append(Xd[0][s0:s0 + BLK], s0)
+        stage_runs.append(paths[0].stage_times())
+        cursor[0] += BLK
+    paths[0].set_timing(False)
+    torch.cuda.synchronize()
+    stage_k = {k: float(np.mean([r[k] for r in stage_runs])) for k in stage_runs[0]}
+    n_cu = float(np.mean(n_before))
+    # coordinate update of the old rows: read and write C (n x k fp32), 2 n k r flops
+    cu_bytes = 2.0 * n_cu * R * 4
+    cu_gbps = cu_bytes / (stage_k["coord_update"] * 1e-3) / 1e9
+    cu_tflops = 2.0 * n_cu * R * R / (stage_k["coord_update"] * 1e-3) / 1e12
+
     ms = {k: avg_ms(k) for k in ev}
     core = [p.state() for p in paths]
     merges = 2 * steps
@@ -245,10 +267,18 @@ def main():
         "stage_ms": ms,
         "host_issue_ms_per_step": t_issue * 1e3 / steps,
         "roofline": {"bound": "hbm", "achieved": recon_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": recon_gbps / HBM_PEAK_GBPS, "traffic": recon_traffic(),
+                     "frac": recon_gbps / HBM_PEAK_GBPS,
+                     "traffic": profiled_traffic("recon_stream_kernel_kv_n16k_traffic.md"),
                      "algorithmic_bytes": recon_bytes,
                      "kernel": "kv_reconstruct (K, bf16 + RoPE)",
                      "mfma_frac": recon_flops / (ms["recon_k"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+        "merge_stage_ms_k": stage_k,
+        "coord_update": {"bound": "hbm", "achieved": cu_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": cu_gbps / HBM_PEAK_GBPS, "algorithmic_bytes": cu_bytes, "rows": n_cu,
+                         "traffic": profiled_traffic("xh_reg_kernel_coord_update_kv_n16k_traffic.md"),
+                         "fp32_tflops": cu_tflops, "fp32_frac": cu_tflops / FP32_PEAK_TFLOPS,
+                         "kernel": "xh_reg_kernel (old rows C <- C H[:k], fp32 MFMA)",
+                         "merges_timed": TIMED_MERGES},
         "setup_s": {"generate": gen_s, "fill_16k_rows": fill_s},
         "core_solver_last_merge": [{"flags": c[11], "steps": c[12], "resid_sweeps": c[14], "k": c[1], "n": c[0]}
                                    for c in core],

@@ -171,6 +171,22 @@ int isvd_query_state(isvd_handle* h, int32_t* state, int32_t count);
  * the factors untouched. Errors: EINVAL, EHIP. */
 int isvd_sym_eig(isvd_handle* h, const double* A, int32_t m, double* lam, double* V);
 
+/* Instrumentation: with on != 0, the handle's following merges run their
+ * kernels one by one (no recorded launch sequence) with a HIP event at each
+ * of the five stage boundaries of Algorithm 2 (iS-KV notes §4.1-§4.3);
+ * on == 0 switches back. Creates the events on first use. Errors: EINVAL,
+ * EHIP. */
+int isvd_set_timing(isvd_handle* h, int32_t on);
+
+/* Waits for the last timed merge and writes the durations of its stages in
+ * milliseconds to ms[0..count-1] (entries past 5 get 0): [0] projection and
+ * residual (Q = F B, E = F - Q B^T twice), [1] residual basis (E E^T, its
+ * eigendecomposition, P, F P), [2] core Gram and its eigendecomposition,
+ * [3] coordinate update of the old rows (C <- C H[:k]), [4] new rows, basis
+ * update and bookkeeping. Errors: EINVAL, EMODE (timing off or no merge
+ * timed since it was switched on), EHIP. */
+int isvd_stage_times(isvd_handle* h, float* ms, int32_t count);
+
 /* Rows folded so far (host-side, no sync). */
 int32_t isvd_rows(const isvd_handle* h);
 

@@ -23,7 +23,7 @@ __all__ = [
     "isvd_rows", "isvd_destroy", "isvd_query_state", "isvd_sym_eig", "kv_reconstruct", "kv_scatter_exact",
     "decode_attend_workspace_bytes", "decode_attend", "iskv_window_rows", "iskv_window_init", "iskv_window_protect",
     "iskv_window_append", "iskv_window_exact", "iskv_window_destroy", "iskv_strerror",
-    "isvd_merge_block_batched", "IsvdPath", "IsvdBatch", "ExactWindow",
+    "isvd_merge_block_batched", "isvd_set_timing", "isvd_stage_times", "MERGE_STAGES", "IsvdPath", "IsvdBatch", "ExactWindow",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libiskv.so")
@@ -48,6 +48,7 @@ EXPORTED_SYMBOLS = (
     "decode_attend", "iskv_window_rows", "iskv_window_init", "iskv_window_protect",
     "iskv_window_append", "iskv_window_exact", "iskv_window_destroy", "iskv_strerror",
     "isvd_query_state", "isvd_sym_eig", "kv_scatter_exact", "isvd_merge_block_batched",
+    "isvd_set_timing", "isvd_stage_times",
 )
 
 
@@ -87,6 +88,10 @@ lib.isvd_query_state.restype = ctypes.c_int
 lib.isvd_query_state.argtypes = [_vp, _pi32, _i32]
 lib.isvd_sym_eig.restype = ctypes.c_int
 lib.isvd_sym_eig.argtypes = [_vp, _vp, _i32, _vp, _vp]
+lib.isvd_set_timing.restype = ctypes.c_int
+lib.isvd_set_timing.argtypes = [_vp, _i32]
+lib.isvd_stage_times.restype = ctypes.c_int
+lib.isvd_stage_times.argtypes = [_vp, ctypes.POINTER(ctypes.c_float), _i32]
 lib.isvd_rows.restype = _i32
 lib.isvd_rows.argtypes = [_vp]
 lib.isvd_destroy.restype = None
@@ -183,6 +188,19 @@ def isvd_query_state(h: int, count: int = 16):
 
 def isvd_sym_eig(h: int, A, m: int, lam, V) -> None:
     _check(lib.isvd_sym_eig(h, _ptr(A), int(m), _ptr(lam), _ptr(V)), "isvd_sym_eig")
+
+
+def isvd_set_timing(h: int, on: bool) -> None:
+    _check(lib.isvd_set_timing(h, int(bool(on))), "isvd_set_timing")
+
+
+MERGE_STAGES = ("project_residual", "residual_basis", "core_eig", "coord_update", "new_rows_basis")
+
+
+def isvd_stage_times(h: int) -> dict:
+    arr = (ctypes.c_float * len(MERGE_STAGES))()
+    _check(lib.isvd_stage_times(h, arr, len(MERGE_STAGES)), "isvd_stage_times")
+    return dict(zip(MERGE_STAGES, (float(x) for x in arr)))
 
 
 def isvd_rows(h: int) -> int:
@@ -293,6 +311,12 @@ class IsvdPath:
 
     def state(self):
         return isvd_query_state(self.h)
+
+    def set_timing(self, on: bool) -> None:
+        isvd_set_timing(self.h, on)
+
+    def stage_times(self) -> dict:
+        return isvd_stage_times(self.h)
 
     def sym_eig(self, A):
         """Eigenpairs of a symmetric fp64 device matrix with the core eigensolver."""

@@ -226,7 +226,30 @@ int isvd_query(isvd_handle* h, int32_t* n, int32_t* k, int32_t* status) {
 void isvd_destroy(isvd_handle* h) {
   if (!h) return;
   iskv_release_graphs(h);
+  for (hipEvent_t& e : h->tev)
+    if (e) (void)hipEventDestroy(e);
   delete h;
+}
+
+int isvd_set_timing(isvd_handle* h, int32_t on) {
+  if (!h) return ISKV_EINVAL;
+  if (on && !h->tev[0]) {
+    for (hipEvent_t& e : h->tev) ISKV_HIP_CHECK(hipEventCreate(&e));
+  }
+  h->timing = on != 0;
+  h->timed = false;
+  return ISKV_OK;
+}
+
+int isvd_stage_times(isvd_handle* h, float* ms, int32_t count) {
+  if (!h || !ms || count < 1) return ISKV_EINVAL;
+  if (!h->timing || !h->timed) return ISKV_EMODE;
+  ISKV_HIP_CHECK(hipEventSynchronize(h->tev[ISKV_STAGES]));
+  for (int i = 0; i < count; ++i) {
+    ms[i] = 0.0f;
+    if (i < ISKV_STAGES) ISKV_HIP_CHECK(hipEventElapsedTime(&ms[i], h->tev[i], h->tev[i + 1]));
+  }
+  return ISKV_OK;
 }
 
 int isvd_sym_eig(isvd_handle* h, const double* A, int32_t m, double* lam, double* V) {

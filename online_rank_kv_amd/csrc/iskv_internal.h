@@ -70,6 +70,9 @@ struct isvd_ws {
   int gram_splits;
 };
 
+// stage boundaries of a merge recorded by isvd_set_timing
+#define ISKV_STAGES 5
+
 struct isvd_handle {
   iskv_config cfg;
   float* C;
@@ -100,6 +103,11 @@ struct isvd_handle {
   int32_t g_batch_b = 0;
   hipGraphExec_t g_batch_merge = nullptr;
   hipGraphExec_t g_batch_reorth = nullptr;
+  // stage timing (isvd_set_timing): merges run eager with an event at every
+  // stage boundary
+  bool timing = false;
+  bool timed = false;  // a merge has been timed since timing was switched on
+  hipEvent_t tev[ISKV_STAGES + 1] = {};
 };
 
 struct iskv_window {

@@ -1133,6 +1133,10 @@ static int merge_body(isvd_handle* h, const float* F, const int32_t* pos_F, int3
   const int D = c.D, R = c.r_max;
   const int32_t* dk = w.st + ST_K;
   const int32_t* dp = w.st + ST_P;
+  auto mark = [&](int i) {
+    if (h->timing) (void)hipEventRecord(h->tev[i], s);
+  };
+  mark(0);
   // 1. Q = F B (b x k)
   skinny<false>(h, b, R, F, D, h->B, R, ddim(dk), D, 1.f, 0.f, nullptr, 0, w.Q, R);
   // 2. E = F - Q B^T (b x D)
@@ -1140,6 +1144,7 @@ static int merge_body(isvd_handle* h, const float* F, const int32_t* pos_F, int3
   // 3. EB = E B; 4. E -= EB B^T (second projection, §4.1)
   skinny<false>(h, b, R, w.E, D, h->B, R, ddim(dk), D, 1.f, 0.f, nullptr, 0, w.EB, R);
   skinny<true>(h, b, D, w.EB, R, h->B, R, hdim(D), R, -1.f, 1.f, w.E, D, w.E, D);
+  mark(1);
   // 5. E E^T (fp64) and the residual basis
   hipLaunchKernelGGL(resid_gram_kernel, bz(dim3(b, (b + 7) / 8), h->bcount), dim3(256), 0, s, w.E, D, b, w.GE, w.st, h->bd);
   if (b <= 32)
@@ -1152,6 +1157,7 @@ static int merge_body(isvd_handle* h, const float* F, const int32_t* pos_F, int3
                      w.rho, w.P, c.b_max, w.st, h->bd);
   // 6. FP = F P (b x p)
   skinny<false>(h, b, c.b_max, F, D, w.P, c.b_max, ddim(dp), D, 1.f, 0.f, nullptr, 0, w.FP, c.b_max);
+  mark(2);
   // 7. core Gram and its eigendecomposition
   {
     dim3 grid((h->m_max + 15) / 16, (h->m_max + 15) / 16);
@@ -1164,6 +1170,7 @@ static int merge_body(isvd_handle* h, const float* F, const int32_t* pos_F, int3
     if (rc) return rc;
   }
   eig_finish(h, 1);
+  mark(3);
   // 8. coordinate sync of old rows (n of them, read on the device), new rows
   // appended at row n, basis update
   const int M = h->m_max;
@@ -1171,11 +1178,14 @@ static int merge_body(isvd_handle* h, const float* F, const int32_t* pos_F, int3
   if (!(c.flags & ISKV_NO_COORD_SYNC))
     xh_launch(s, h->bd, h->bcount, c.n_cap, h->C, R, nullptr, 0, ddim(dk), ddim(dk), R, w.Hc, R, R, ddim(w.st + ST_KNEW),
               dn, h->C, R, nullptr, 0);
+  mark(4);
   xh_launch(s, h->bd, h->bcount, b, w.Q, R, w.FP, c.b_max, ddim(dk), ddim(w.st + ST_M), M, w.Hc, R, R,
             ddim(w.st + ST_KNEW), hdim(b), h->C, R, nullptr, 0, h->pos, pos_F, false, dn);
   xh_launch(s, h->bd, h->bcount, D, h->B, R, w.P, c.b_max, ddim(dk), ddim(w.st + ST_M), M, w.Hc, R, R,
             ddim(w.st + ST_KNEW), hdim(D), h->B, R, w.Bbf, R, nullptr, nullptr, true);
   hipLaunchKernelGGL(merge_commit_kernel, bz(dim3(1), h->bcount), dim3(256), 0, s, h->sigma, w.sig_new, w.st, b, R, h->bd);
+  mark(5);
+  if (h->timing) h->timed = true;
   ISKV_HIP_CHECK(hipGetLastError());
   return ISKV_OK;
 }
@@ -1261,7 +1271,7 @@ __global__ void stage_block_kernel(const float* __restrict__ F, const int32_t* _
 }
 
 bool use_graphs(const isvd_handle* h) {
-  return h->stream != nullptr && !(h->cfg.flags & ISKV_NO_GRAPH);
+  return h->stream != nullptr && !(h->cfg.flags & ISKV_NO_GRAPH) && !h->timing;
 }
 
 // Record `body` on the handle's stream into an executable graph.

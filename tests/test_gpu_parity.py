@@ -254,6 +254,36 @@ def test_batched_merges_match_separate(K, graphs):
         p.close()
 
 
+def test_stage_timing_matches_plain_merges(K):
+    """Merges with stage events give the same factors as plain merges, report
+    five positive stage durations, and refuse to report before a timed merge."""
+    X = synth.kv_stream(synth.StreamSpec(D=128, n=96, spectrum="exp4", noise_std=1e-3, seed=3))
+    Xd = torch.from_numpy(X).to(DEV)
+    posd = torch.arange(96, dtype=torch.int32, device=DEV)
+    st = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    a = K.IsvdPath(D=128, r_max=16, b_max=8, n_cap=96, device=DEV, stream=st)
+    b = K.IsvdPath(D=128, r_max=16, b_max=8, n_cap=96, device=DEV, graphs=False)
+    a.set_timing(True)
+    with pytest.raises(K.IskvError):
+        a.stage_times()
+    for s in range(0, 96, 8):
+        a.merge(Xd[s:s + 8], posd[s:s + 8])
+        b.merge(Xd[s:s + 8], posd[s:s + 8])
+        if s == 48:
+            t = a.stage_times()
+            assert list(t) == list(K.MERGE_STAGES)
+            assert all(v > 0.0 for v in t.values()), t
+            a.set_timing(False)
+    st.synchronize()
+    torch.cuda.synchronize()
+    Ca, Ba, _, _, _ = gpu_factors(a)
+    Cb, Bb, _, _, _ = gpu_factors(b)
+    assert rel(Ca @ Ba.T, Cb @ Bb.T) < 1e-6
+    a.close()
+    b.close()
+
+
 def test_batched_merge_rejects_bad_sets(K):
     """Handles of separate allocations (no common offset), repeated handles and
     a capacity overflow are refused before anything runs."""
