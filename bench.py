@@ -8,7 +8,10 @@ budget r = 256, block b = 32, exact recent window w = 128, with a key path
 timed step is one pass of the whole hot path at n ~ 16K:
   * ingest b new K rows and b new V rows through the exact window; the rows
     leaving the window become a pending block that is merged (one iSVD merge
-    per path; re-orthogonalisation every 256 folded rows);
+    per path; re-orthogonalisation every 256 folded rows). The K and V paths
+    are two handles on two HIP streams, so their merges overlap;
+    `--batched-kv` instead carves them from one allocation and runs both merges
+    as one batched launch sequence (iskv_window_append_batched);
   * reconstruct the dense K cache (bf16, RoPE theta = 500000 at every
     position) and V cache (bf16) from the factors plus the exact window;
   * GQA decode attention of one query (32 heads over 8 KV heads, d_h = 128)
@@ -39,7 +42,7 @@ HBM_PEAK_GBPS = 8000.0
 CALIB_BYTES = 256 << 20
 BF16_PEAK_TFLOPS = 2500.0
 FP32_PEAK_TFLOPS = 157.3
-TIMED_MERGES = 8  # K merges run once more with stage events after the timed region
+TIMED_MERGES = 8  # merges run once more with stage events after the timed region
 
 
 def parse():
@@ -49,6 +52,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--batched-kv", action="store_true",
+                    help="K and V carved from one allocation, merged as one batched launch sequence")
     ap.add_argument("--no-graphs", action="store_true",
                     help="enqueue every kernel directly instead of replaying recorded HIP graphs "
                          "(same kernels; for kernel-trace profilers)")
@@ -132,24 +137,43 @@ def main():
     Xv = synth.kv_stream(synth.StreamSpec(D, n_rows, "invsqrt", 0.0, 1))
     gen_s = time.perf_counter() - t_gen
 
-    # one HIP stream per path: the K and V merges (and their reconstructions)
-    # are independent chains of small launches and run concurrently
-    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
-    paths, wins, Xd = [], [], []
-    for X, st in zip((Xk, Xv), streams):
+    batched = args.batched_kv
+    if batched:
+        # K and V carved from one allocation: every merge / window kernel runs
+        # once over both paths (grid z = path) on one stream
+        st = torch.cuda.Stream()
+        streams = [st, torch.cuda.Stream()]  # the second only runs the V reconstruction
         with torch.cuda.stream(st):
-            p = K.IsvdPath(D=D, r_max=R, b_max=BLK, n_cap=n_rows, reorth_every_rows=256, device=dev,
-                           stream=st, graphs=not args.no_graphs)
-            paths.append(p)
-            wins.append(K.ExactWindow(p, window=WIN, block=BLK, stream=st))
-            Xd.append(torch.from_numpy(X).to(dev))
+            bat = K.IsvdBatch(2, D=D, r_max=R, b_max=BLK, n_cap=n_rows, reorth_every_rows=256, device=dev,
+                              stream=st, graphs=not args.no_graphs, window=WIN, block=BLK)
+            Xs = torch.from_numpy(np.stack([Xk, Xv])).to(dev)  # [2, n_rows, D]
             st.synchronize()
+        paths, wins = bat.paths, bat.windows
+        Xd = [Xs[0], Xs[1]]
+
+        def ingest(s0, e0):
+            bat.append(Xs[:, s0:e0], s0)
+    else:
+        # one HIP stream per path: the K and V merges (and their reconstructions)
+        # are independent chains of small launches and run concurrently
+        streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+        paths, wins, Xd = [], [], []
+        for X, st in zip((Xk, Xv), streams):
+            with torch.cuda.stream(st):
+                p = K.IsvdPath(D=D, r_max=R, b_max=BLK, n_cap=n_rows, reorth_every_rows=256, device=dev,
+                               stream=st, graphs=not args.no_graphs)
+                paths.append(p)
+                wins.append(K.ExactWindow(p, window=WIN, block=BLK, stream=st))
+                Xd.append(torch.from_numpy(X).to(dev))
+                st.synchronize()
+
+        def ingest(s0, e0):
+            for i in range(2):
+                wins[i].append(Xd[i][s0:e0], s0)
     # fill both paths with the first N0 rows (+ window)
     t_fill = time.perf_counter()
     for s in range(0, N0 + WIN, 512):
-        e = min(s + 512, N0 + WIN)
-        for i in range(2):
-            wins[i].append(Xd[i][s:e], s)
+        ingest(s, min(s + 512, N0 + WIN))
     for st in streams:
         st.synchronize()
     fill_s = time.perf_counter() - t_fill
@@ -178,11 +202,18 @@ def main():
         if attend_done[0] is not None:
             sv.wait_event(attend_done[0])  # V cache is rewritten only after the last attention read it
         e[0].record(sk)
-        e[3].record(sv)
-        wins[0].append(Xd[0][s0:s0 + BLK], s0)   # K merge (stream K)
-        wins[1].append(Xd[1][s0:s0 + BLK], s0)   # V merge (stream V)
-        e[1].record(sk)
-        e[4].record(sv)
+        if batched:
+            ingest(s0, s0 + BLK)                 # K and V merges, one batched sequence (stream K)
+            e[1].record(sk)
+            sv.wait_event(e[1])
+            e[3].record(sv)
+            e[4].record(sv)
+        else:
+            e[3].record(sv)
+            wins[0].append(Xd[0][s0:s0 + BLK], s0)   # K merge (stream K)
+            wins[1].append(Xd[1][s0:s0 + BLK], s0)   # V merge (stream V)
+            e[1].record(sk)
+            e[4].record(sv)
         # compressed rows (one kernel, bracketed by the events), then the exact window rows
         paths[0].reconstruct(Kc, n_total, head_dim=DH, rope=True, theta=THETA, stream=sk)
         paths[1].reconstruct(Vc, n_total, head_dim=DH, rope=False, stream=sv)
@@ -197,8 +228,8 @@ def main():
         e[6].record(sk)
         attend_done[0] = e[6]
         if record:
-            ev["merge_k"].append((e[0], e[1]))
-            ev["merge_v"].append((e[3], e[4]))
+            ev["merge_k"].append((e[0], e[1]))   # batched: the K + V merge sequence
+            ev["merge_v"].append((e[3], e[4]) if not batched else (e[0], e[1]))
             ev["recon_k"].append((e[1], e[2]))
             ev["recon_v"].append((e[4], e[5]))
             ev["attend"].append((e[7], e[6]))
@@ -217,25 +248,30 @@ def main():
     def avg_ms(key):
         return float(np.mean([a.elapsed_time(b) for a, b in ev[key]]))
 
-    # stage breakdown of K merges (outside the timed region): the handle runs
-    # its merges kernel by kernel with HIP events at the stage boundaries
+    # stage breakdown of merges (outside the timed region): the handle runs
+    # its merges kernel by kernel with HIP events at the stage boundaries; in
+    # the batched layout each stage covers both paths (one launch per kernel)
     stage_runs = []
     n_before = []
     paths[0].set_timing(True)
     for _ in range(TIMED_MERGES):
         s0 = cursor[0]
         n_before.append(paths[0].n)
-        wins[0].append(Xd[0][s0:s0 + BLK], s0)
+        if batched:
+            ingest(s0, s0 + BLK)
+        else:
+            wins[0].append(Xd[0][s0:s0 + BLK], s0)
         stage_runs.append(paths[0].stage_times())
         cursor[0] += BLK
     paths[0].set_timing(False)
     torch.cuda.synchronize()
     stage_k = {k: float(np.mean([r[k] for r in stage_runs])) for k in stage_runs[0]}
     n_cu = float(np.mean(n_before))
-    # coordinate update of the old rows: read and write C (n x k fp32), 2 n k r flops
-    cu_bytes = 2.0 * n_cu * R * 4
+    cu_paths = 2 if batched else 1
+    # coordinate update of the old rows: read and write C (n x k fp32), 2 n k r flops, per path
+    cu_bytes = cu_paths * 2.0 * n_cu * R * 4
     cu_gbps = cu_bytes / (stage_k["coord_update"] * 1e-3) / 1e9
-    cu_tflops = 2.0 * n_cu * R * R / (stage_k["coord_update"] * 1e-3) / 1e12
+    cu_tflops = cu_paths * 2.0 * n_cu * R * R / (stage_k["coord_update"] * 1e-3) / 1e12
 
     ms = {k: avg_ms(k) for k in ev}
     core = [p.state() for p in paths]
@@ -262,7 +298,8 @@ def main():
         "config": {"workload": "kv stream n=16384 (+decode), D=1024 (8x128), r=256, b=32, w=128, "
                                "K (exp(-i/40)+0.01) and V ((1+i)^-1/2) paths, bf16 RoPE reconstruction, "
                                "GQA 32q/8kv decode", "n_rows_start": N0, "rank": R, "block": BLK,
-                   "window": WIN, "reorth_every_rows": 256, "hip_graphs": not args.no_graphs},
+                   "window": WIN, "reorth_every_rows": 256, "hip_graphs": not args.no_graphs,
+                   "kv_merges": "batched" if batched else "two streams"},
         "reconstructed_GBps": n_mid * D * 2 / (ms["recon_k"] * 1e-3) / 1e9,
         "stage_ms": ms,
         "host_issue_ms_per_step": t_issue * 1e3 / steps,
@@ -272,13 +309,14 @@ def main():
                      "algorithmic_bytes": recon_bytes,
                      "kernel": "kv_reconstruct (K, bf16 + RoPE)",
                      "mfma_frac": recon_flops / (ms["recon_k"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
-        "merge_stage_ms_k": stage_k,
+        "merge_stage_ms": stage_k,
+        "merge_stage_paths": cu_paths,
         "coord_update": {"bound": "hbm", "achieved": cu_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": cu_gbps / HBM_PEAK_GBPS, "algorithmic_bytes": cu_bytes, "rows": n_cu,
                          "traffic": profiled_traffic("xh_reg_kernel_coord_update_kv_n16k_traffic.md"),
                          "fp32_tflops": cu_tflops, "fp32_frac": cu_tflops / FP32_PEAK_TFLOPS,
                          "kernel": "xh_reg_kernel (old rows C <- C H[:k], fp32 MFMA)",
-                         "merges_timed": TIMED_MERGES},
+                         "paths_per_launch": cu_paths, "merges_timed": TIMED_MERGES},
         "setup_s": {"generate": gen_s, "fill_16k_rows": fill_s},
         "core_solver_last_merge": [{"flags": c[11], "steps": c[12], "resid_sweeps": c[14], "k": c[1], "n": c[0]}
                                    for c in core],

@@ -283,6 +283,22 @@ int iskv_window_protect(iskv_window* w, const float* rows, const int32_t* pos_ho
 int iskv_window_append(iskv_window* w, const float* rows, int32_t pos0, int32_t count,
                        int32_t* merges);
 
+/* The same append on `count` windows in lockstep (one per independent path,
+ * iS-KV notes §2.2), with every kernel run once over all of them and every
+ * full block merged by isvd_merge_block_batched. Window z receives the n rows
+ * at rows + z * rows_stride (device fp32, rows_stride >= n * D floats) at
+ * positions pos0 .. pos0 + n - 1. Requirements (count >= 2): the windows are
+ * distinct, have equal (prot_cap, window, block, D), the same stream and the
+ * same history of appends and protected rows; their handles form a valid
+ * isvd_merge_block_batched set; and every buffer of path z (the handle's C,
+ * sigma, B, pos and workspace and the window's rows and pos) lies z * S
+ * bytes after path 0's, for one stride S > 0 (one allocation carved at a
+ * fixed per-path stride). count == 1 is iskv_window_append. Errors: EINVAL
+ * (requirements), ECAPACITY (a merge would exceed a handle's n_cap; checked
+ * before anything is enqueued), EHIP. */
+int iskv_window_append_batched(iskv_window* const* ws, int32_t count, const float* rows,
+                               int64_t rows_stride, int32_t pos0, int32_t n, int32_t* merges);
+
 /* The exact buffer for kv_reconstruct: its rows, positions and slot count. */
 int iskv_window_exact(const iskv_window* w, const float** rows, const int32_t** pos,
                       int32_t* count);

@@ -23,7 +23,7 @@ __all__ = [
     "isvd_rows", "isvd_destroy", "isvd_query_state", "isvd_sym_eig", "kv_reconstruct", "kv_scatter_exact",
     "decode_attend_workspace_bytes", "decode_attend", "iskv_window_rows", "iskv_window_init", "iskv_window_protect",
     "iskv_window_append", "iskv_window_exact", "iskv_window_destroy", "iskv_strerror",
-    "isvd_merge_block_batched", "isvd_set_timing", "isvd_stage_times", "MERGE_STAGES", "IsvdPath", "IsvdBatch", "ExactWindow",
+    "iskv_window_append_batched", "isvd_merge_block_batched", "isvd_set_timing", "isvd_stage_times", "MERGE_STAGES", "IsvdPath", "IsvdBatch", "ExactWindow",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libiskv.so")
@@ -48,7 +48,7 @@ EXPORTED_SYMBOLS = (
     "decode_attend", "iskv_window_rows", "iskv_window_init", "iskv_window_protect",
     "iskv_window_append", "iskv_window_exact", "iskv_window_destroy", "iskv_strerror",
     "isvd_query_state", "isvd_sym_eig", "kv_scatter_exact", "isvd_merge_block_batched",
-    "isvd_set_timing", "isvd_stage_times",
+    "isvd_set_timing", "isvd_stage_times", "iskv_window_append_batched",
 )
 
 
@@ -113,6 +113,8 @@ lib.iskv_window_protect.restype = ctypes.c_int
 lib.iskv_window_protect.argtypes = [_vp, _vp, _pi32, _i32]
 lib.iskv_window_append.restype = ctypes.c_int
 lib.iskv_window_append.argtypes = [_vp, _vp, _i32, _i32, _pi32]
+lib.iskv_window_append_batched.restype = ctypes.c_int
+lib.iskv_window_append_batched.argtypes = [ctypes.POINTER(_vp), _i32, _vp, ctypes.c_int64, _i32, _i32, _pi32]
 lib.iskv_window_exact.restype = ctypes.c_int
 lib.iskv_window_exact.argtypes = [_vp, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _pi32]
 lib.iskv_window_destroy.restype = None
@@ -260,6 +262,14 @@ def iskv_window_append(w: int, rows, pos0: int, count: int) -> int:
     return m.value
 
 
+def iskv_window_append_batched(windows, rows, rows_stride: int, pos0: int, n: int) -> int:
+    arr = (_vp * len(windows))(*windows)
+    m = _i32()
+    _check(lib.iskv_window_append_batched(arr, len(windows), _ptr(rows), int(rows_stride), int(pos0), int(n),
+                                          ctypes.byref(m)), "iskv_window_append_batched")
+    return m.value
+
+
 def iskv_window_exact(w: int):
     r, p, c = _vp(), _vp(), _i32()
     _check(lib.iskv_window_exact(w, ctypes.byref(r), ctypes.byref(p), ctypes.byref(c)),
@@ -365,7 +375,7 @@ class IsvdBatch:
 
     def __init__(self, count: int, D: int, r_max: int, b_max: int, n_cap: int, reorth_every_rows: int = 0,
                  resid_rel_tol: float = 0.0, sync: bool = True, device="cuda", stream=None,
-                 graphs: bool = True):
+                 graphs: bool = True, window: int | None = None, block: int | None = None, prot_cap: int = 0):
         import torch
         if count < 1:
             raise ValueError("count must be >= 1")
@@ -374,6 +384,10 @@ class IsvdBatch:
         if ws == 0:
             raise ValueError("invalid iskv configuration")
         sizes = [n_cap * r_max * 4, r_max * 4, D * r_max * 4, n_cap * 4, ws]
+        wrows = 0
+        if window is not None:  # exact window + pending FIFO of every path in the same slot
+            wrows = iskv_window_rows(prot_cap, window, block if block is not None else b_max)
+            sizes += [wrows * D * 4, wrows * 4]
         offs = []
         o = 0
         for nb in sizes:
@@ -386,6 +400,7 @@ class IsvdBatch:
         self.blob = torch.empty((count * self.stride + 256,), dtype=torch.uint8, device=torch.device(device))
         base = (-self.blob.data_ptr()) % 256
         self.paths = []
+        self.windows = []
         for z in range(count):
             z0 = base + z * self.stride
 
@@ -397,6 +412,11 @@ class IsvdBatch:
                     self.blob[z0 + offs[4]:z0 + offs[4] + ws])
             self.paths.append(IsvdPath(D, r_max, b_max, n_cap, reorth_every_rows, resid_rel_tol, sync,
                                        device, stream, graphs, _buffers=bufs))
+            if wrows:
+                self.windows.append(ExactWindow(self.paths[-1], window, block if block is not None else b_max,
+                                                prot_cap, stream,
+                                                _buffers=(view(5, torch.float32, (wrows, D)),
+                                                          view(6, torch.int32, (wrows,)))))
         self.handles = [p.h for p in self.paths]
 
     def merge(self, F, pos_F) -> None:
@@ -409,6 +429,18 @@ class IsvdBatch:
         b = F.shape[1]
         isvd_merge_block_batched(self.handles, F, F.stride(0), pos_F, pos_F.stride(0), b)
 
+    def append(self, rows, pos0: int) -> int:
+        """Append rows[z] (rows: [count, n, D] fp32, rows contiguous) to the
+        exact window of path z at positions pos0.., merging every full block
+        of all paths in one batched launch sequence; returns the merges made."""
+        if not self.windows:
+            raise ValueError("IsvdBatch was created without windows")
+        if rows.dim() != 3 or rows.shape[0] != self.count or rows.shape[2] != self.D:
+            raise ValueError("rows must be [count, n, D]")
+        if rows.stride(2) != 1 or rows.stride(1) != self.D:
+            raise ValueError("rows must be contiguous within each path")
+        return iskv_window_append_batched([w.w for w in self.windows], rows, rows.stride(0), pos0, rows.shape[1])
+
     def __len__(self) -> int:
         return self.count
 
@@ -416,6 +448,8 @@ class IsvdBatch:
         return self.paths[z]
 
     def close(self) -> None:
+        for w in getattr(self, "windows", []):
+            w.close()
         for p in getattr(self, "paths", []):
             p.close()
 
@@ -423,13 +457,17 @@ class IsvdBatch:
 class ExactWindow:
     """Exact recent window + pending FIFO feeding one IsvdPath (iS-KV notes §3.2)."""
 
-    def __init__(self, path: IsvdPath, window: int, block: int, prot_cap: int = 0, stream=None):
+    def __init__(self, path: IsvdPath, window: int, block: int, prot_cap: int = 0, stream=None,
+                 _buffers=None):
         import torch
         self.path = path
         rows = iskv_window_rows(prot_cap, window, block)
         dev = path.C.device
-        self.rows = torch.empty((rows, path.cfg.D), dtype=torch.float32, device=dev)
-        self.pos = torch.empty((rows,), dtype=torch.int32, device=dev)
+        if _buffers is not None:  # carved by IsvdBatch from its shared allocation
+            self.rows, self.pos = _buffers
+        else:
+            self.rows = torch.empty((rows, path.cfg.D), dtype=torch.float32, device=dev)
+            self.pos = torch.empty((rows,), dtype=torch.int32, device=dev)
         self.w = iskv_window_init(path.h, prot_cap, window, block, self.rows, self.pos,
                                   stream if stream is not None else path.stream)
 

@@ -351,79 +351,175 @@ int iskv_window_protect(iskv_window* w, const float* rows, const int32_t* pos_ho
   return ISKV_OK;
 }
 
+// Launch context of window moves: one window (bd = nullptr), or `bc` windows
+// in lockstep whose buffers lie bd[z] bytes from window 0's, with the caller's
+// rows of window z at src + z * src_stride floats.
+struct win_batch {
+  const int64_t* bd;
+  int32_t bc;
+  int64_t src_stride;
+};
+
 // Move `count` consecutive window slots starting at `slot` (wrapping) to dst.
-static int move_from_ring(iskv_window* w, int slot, int count, float* dst, int32_t* dpos) {
+static int move_from_ring(iskv_window* w, const win_batch& wb, int slot, int count, float* dst, int32_t* dpos) {
   const int D = w->D;
   float* win_rows = w->rows + (size_t)w->prot_cap * D;
   int32_t* win_pos = w->pos + w->prot_cap;
   int first = count < w->window - slot ? count : w->window - slot;
   int rc = iskv_launch_window_move(dst, dpos, win_rows + (size_t)slot * D, win_pos + slot, 0, first, D,
-                                   w->stream);
+                                   w->stream, wb.bd, wb.bc, 1, 0);
   if (rc || first == count) return rc;
   return iskv_launch_window_move(dst + (size_t)first * D, dpos + first, win_rows, win_pos, 0,
-                                 count - first, D, w->stream);
+                                 count - first, D, w->stream, wb.bd, wb.bc, 1, 0);
 }
 
 // Write `count` new rows (positions pos0..) into consecutive slots from `slot`.
-static int write_to_ring(iskv_window* w, int slot, const float* src, int32_t pos0, int count) {
+static int write_to_ring(iskv_window* w, const win_batch& wb, int slot, const float* src, int32_t pos0,
+                         int count) {
   const int D = w->D;
   float* win_rows = w->rows + (size_t)w->prot_cap * D;
   int32_t* win_pos = w->pos + w->prot_cap;
   int first = count < w->window - slot ? count : w->window - slot;
   int rc = iskv_launch_window_move(win_rows + (size_t)slot * D, win_pos + slot, src, nullptr, pos0,
-                                   first, D, w->stream);
+                                   first, D, w->stream, wb.bd, wb.bc, 0, wb.src_stride);
   if (rc || first == count) return rc;
   return iskv_launch_window_move(win_rows, win_pos, src + (size_t)first * D, nullptr, pos0 + first,
-                                 count - first, D, w->stream);
+                                 count - first, D, w->stream, wb.bd, wb.bc, 0, wb.src_stride);
+}
+
+// The append of Algorithm 1 (iS-KV notes §3.2): new rows enter the exact
+// window, rows leaving it go to the pending FIFO, and every full pending block
+// is merged. `ws` (count windows in lockstep, ws[0] == w) share w's counters;
+// for count > 1 the kernels run batched and the merges go through
+// isvd_merge_block_batched.
+static int window_append(iskv_window* w, iskv_window* const* ws, int32_t count, isvd_handle* const* hs,
+                         const win_batch& wb, const float* rows, int32_t pos0, int32_t n, int32_t* merges) {
+  const int D = w->D;
+  float* pend_rows = w->rows + (size_t)(w->prot_cap + w->window) * D;
+  int32_t* pend_pos = w->pos + w->prot_cap + w->window;
+  int done = 0;
+  while (done < n) {
+    // rows handled in this chunk: never more than fill the pending area once
+    int c = n - done;
+    if (c > w->block - w->pending) c = w->block - w->pending;
+    const int64_t r = w->appended;
+    int leave = 0;
+    if (w->window > 0) {
+      if (w->window < c) c = w->window;
+      // rows r - window .. r - window + c - 1 leave the window (those that exist)
+      int64_t first_out = r - w->window;
+      int64_t lo = first_out < 0 ? 0 : first_out;
+      int64_t hi = first_out + c;  // exclusive
+      if (hi > lo) leave = (int)(hi - lo);
+      if (leave > 0) {
+        int rc = move_from_ring(w, wb, (int)(lo % w->window), leave, pend_rows + (size_t)w->pending * D,
+                                pend_pos + w->pending);
+        if (rc) return rc;
+      }
+      int rc = write_to_ring(w, wb, (int)(r % w->window), rows + (size_t)done * D, pos0 + done, c);
+      if (rc) return rc;
+    } else {
+      int rc = iskv_launch_window_move(pend_rows + (size_t)w->pending * D, pend_pos + w->pending,
+                                       rows + (size_t)done * D, nullptr, pos0 + done, c, D, w->stream, wb.bd,
+                                       wb.bc, 0, wb.src_stride);
+      if (rc) return rc;
+      leave = c;
+    }
+    for (int z = 0; z < count; ++z) {
+      ws[z]->pending += leave;
+      ws[z]->appended += c;
+    }
+    done += c;
+    if (w->pending == w->block) {
+      int rc;
+      if (count == 1) {
+        rc = isvd_merge_block(w->h, pend_rows, pend_pos, w->block);
+      } else {
+        const int64_t fst = (const char*)hs[1]->ws_base - (const char*)hs[0]->ws_base;
+        // every window's pending block lies at the common per-path byte stride
+        rc = isvd_merge_block_batched(hs, count, pend_rows, fst / (int64_t)sizeof(float), pend_pos,
+                                      fst / (int64_t)sizeof(int32_t), w->block);
+      }
+      if (rc) return rc;
+      rc = iskv_launch_fill_pos(pend_pos, w->block, -1, 0, w->stream, wb.bd, wb.bc);
+      if (rc) return rc;
+      for (int z = 0; z < count; ++z) ws[z]->pending = 0;
+      if (merges) (*merges)++;
+    }
+  }
+  return ISKV_OK;
 }
 
 int iskv_window_append(iskv_window* w, const float* rows, int32_t pos0, int32_t count,
                        int32_t* merges) {
   if (merges) *merges = 0;
   if (!w || count < 0 || (count > 0 && !rows)) return ISKV_EINVAL;
-  const int D = w->D;
-  float* pend_rows = w->rows + (size_t)(w->prot_cap + w->window) * D;
-  int32_t* pend_pos = w->pos + w->prot_cap + w->window;
-  int done = 0;
-  while (done < count) {
-    // rows handled in this chunk: never more than fill the pending area once
-    int c = count - done;
-    if (c > w->block - w->pending) c = w->block - w->pending;
-    const int64_t r = w->appended;
-    if (w->window > 0) {
-      if (w->window < c) c = w->window;
-      // rows r - window .. r - window + c - 1 leave the window (those that exist)
-      int64_t first_out = r - w->window;
-      int leave = 0;
-      int64_t lo = first_out < 0 ? 0 : first_out;
-      int64_t hi = first_out + c;  // exclusive
-      if (hi > lo) leave = (int)(hi - lo);
-      if (leave > 0) {
-        int rc = move_from_ring(w, (int)(lo % w->window), leave,
-                                pend_rows + (size_t)w->pending * D, pend_pos + w->pending);
-        if (rc) return rc;
-        w->pending += leave;
+  const win_batch wb = {nullptr, 1, 0};
+  return window_append(w, &w, 1, &w->h, wb, rows, pos0, count, merges);
+}
+
+int iskv_window_append_batched(iskv_window* const* ws, int32_t count, const float* rows, int64_t rows_stride,
+                               int32_t pos0, int32_t n, int32_t* merges) {
+  if (merges) *merges = 0;
+  if (!ws || count < 1 || count > ISKV_MAX_BATCH || n < 0 || (n > 0 && !rows)) return ISKV_EINVAL;
+  iskv_window* w0 = ws[0];
+  if (!w0) return ISKV_EINVAL;
+  if (count == 1) return iskv_window_append(w0, rows, pos0, n, merges);
+  if (rows_stride < (int64_t)n * w0->D) return ISKV_EINVAL;
+  std::vector<isvd_handle*> hs(count);
+  const char* r0 = (const char*)w0->rows;
+  const char* p0 = (const char*)w0->pos;
+  for (int z = 0; z < count; ++z)
+    if (!ws[z] || !ws[z]->h) return ISKV_EINVAL;
+  const char* b0 = (const char*)w0->h->ws_base;
+  const ptrdiff_t d1 = (const char*)ws[1]->h->ws_base - b0;
+  for (int z = 0; z < count; ++z) {
+    const iskv_window* w = ws[z];
+    if (w->D != w0->D || w->prot_cap != w0->prot_cap || w->window != w0->window ||
+        w->block != w0->block || w->stream != w0->stream || w->h->stream != w0->stream ||
+        w->n_prot != w0->n_prot || w->appended != w0->appended || w->pending != w0->pending)
+      return ISKV_EINVAL;
+    // window buffers at the same offsets as the handles' buffers, and one
+    // stride from path to path (the pending blocks are passed to the batched
+    // merge as F + z * stride)
+    const ptrdiff_t d = (const char*)w->h->ws_base - b0;
+    if ((const char*)w->rows - r0 != d || (const char*)w->pos - p0 != d) return ISKV_EINVAL;
+    if (d1 <= 0 || d != (ptrdiff_t)z * d1 || d1 / (ptrdiff_t)sizeof(float) < (ptrdiff_t)w0->block * w0->D)
+      return ISKV_EINVAL;
+    for (int y = 0; y < z; ++y)
+      if (ws[y] == w || ws[y]->h == w->h) return ISKV_EINVAL;
+    hs[z] = w->h;
+  }
+  // capacity of every merge this call makes, checked before anything runs
+  {
+    int64_t app = w0->appended;
+    int pend = w0->pending, nm = 0, done = 0;
+    while (done < n) {
+      int c = n - done;
+      if (c > w0->block - pend) c = w0->block - pend;
+      int leave = c;
+      if (w0->window > 0) {
+        if (w0->window < c) c = w0->window;
+        int64_t first_out = app - w0->window, lo = first_out < 0 ? 0 : first_out, hi = first_out + c;
+        leave = hi > lo ? (int)(hi - lo) : 0;
       }
-      int rc = write_to_ring(w, (int)(r % w->window), rows + (size_t)done * D, pos0 + done, c);
-      if (rc) return rc;
-    } else {
-      int rc = iskv_launch_window_move(pend_rows + (size_t)w->pending * D, pend_pos + w->pending,
-                                       rows + (size_t)done * D, nullptr, pos0 + done, c, D, w->stream);
-      if (rc) return rc;
-      w->pending += c;
+      pend += leave;
+      app += c;
+      done += c;
+      if (pend == w0->block) { ++nm; pend = 0; }
     }
-    w->appended += c;
-    done += c;
-    if (w->pending == w->block) {
-      int rc = isvd_merge_block(w->h, pend_rows, pend_pos, w->block);
-      if (rc) return rc;
-      rc = iskv_launch_fill_pos(pend_pos, w->block, -1, 0, w->stream);
-      if (rc) return rc;
-      w->pending = 0;
-      if (merges) (*merges)++;
+    for (int z = 0; z < count; ++z)
+      if ((int64_t)hs[z]->n_host + (int64_t)nm * w0->block > hs[z]->cfg.n_cap) return ISKV_ECAPACITY;
+    if (nm > 0) {
+      // the handles must also form a valid merge batch
+      for (int z = 0; z < count; ++z)
+        if (memcmp(&hs[z]->cfg, &hs[0]->cfg, sizeof(iskv_config)) != 0) return ISKV_EINVAL;
     }
   }
-  return ISKV_OK;
+  int rc = iskv_upload_offsets(hs.data(), count);
+  if (rc) return rc;
+  const win_batch wb = {(const int64_t*)hs[0]->w.btab, count, rows_stride};
+  return window_append(w0, ws, count, hs.data(), wb, rows, pos0, n, merges);
 }
 
 int iskv_window_exact(const iskv_window* w, const float** rows, const int32_t** pos, int32_t* count) {

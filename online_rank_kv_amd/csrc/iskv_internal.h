@@ -155,10 +155,17 @@ int iskv_launch_attend(const uint16_t* q, const uint16_t* K, const uint16_t* V, 
                        int32_t n, int32_t Hq, int32_t Hkv, int32_t dh, float scale, uint16_t* out,
                        void* ws, size_t ws_bytes, hipStream_t s);
 size_t iskv_attend_ws_bytes(int32_t batch, int32_t n, int32_t Hq, int32_t dh);
+// Window row moves and position fills; with bd (count bc) every copy z is
+// rebased by bd[z] bytes (see move_rows_kernel).
 int iskv_launch_window_move(float* dst_rows, int32_t* dst_pos, const float* src_rows,
                             const int32_t* src_pos, int32_t src_pos_base, int32_t count, int32_t D,
-                            hipStream_t s);
-int iskv_launch_fill_pos(int32_t* pos, int32_t count, int32_t value0, int32_t step, hipStream_t s);
+                            hipStream_t s, const int64_t* bd = nullptr, int32_t bc = 1,
+                            int32_t src_rebased = 1, int64_t src_stride = 0);
+int iskv_launch_fill_pos(int32_t* pos, int32_t count, int32_t value0, int32_t step, hipStream_t s,
+                         const int64_t* bd = nullptr, int32_t bc = 1);
+// Upload the byte offsets of handles hs[1..] from hs[0] (workspace bases) to
+// hs[0]'s offset table; no-op when the same set was uploaded last.
+int iskv_upload_offsets(isvd_handle* const* hs, int32_t count);
 int iskv_launch_copy_pos_host(int32_t* pos_dev, const int32_t* pos_host, int32_t count,
                               hipStream_t s);
 

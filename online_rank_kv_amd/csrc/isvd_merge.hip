@@ -1365,9 +1365,7 @@ int iskv_launch_reorth(isvd_handle* h) {
 // corresponding buffer of handle 0; checked by the caller): the launch
 // sequence of one merge runs once with grid.z = count and each copy rebased
 // by its handle's offset. The offsets live in the first handle's workspace.
-namespace {
-
-int upload_offsets(isvd_handle* const* hs, int32_t count) {
+int iskv_upload_offsets(isvd_handle* const* hs, int32_t count) {
   isvd_handle* h0 = hs[0];
   if ((int)h0->g_batch_set.size() == count &&
       std::equal(h0->g_batch_set.begin(), h0->g_batch_set.end(), hs))
@@ -1385,6 +1383,8 @@ int upload_offsets(isvd_handle* const* hs, int32_t count) {
   h0->g_batch_set.assign(hs, hs + count);
   return ISKV_OK;
 }
+
+namespace {
 
 template <class Body>
 int run_batched(isvd_handle* h0, int32_t count, hipGraphExec_t* cache, Body body) {
@@ -1407,7 +1407,7 @@ int run_batched(isvd_handle* h0, int32_t count, hipGraphExec_t* cache, Body body
 int iskv_launch_merge_batched(isvd_handle* const* hs, int32_t count, const float* F, int64_t F_stride,
                               const int32_t* pos_F, int64_t pos_stride, int32_t b) {
   isvd_handle* h0 = hs[0];
-  int rc = upload_offsets(hs, count);
+  int rc = iskv_upload_offsets(hs, count);
   if (rc) return rc;
   if (h0->g_batch_merge && h0->g_batch_b != b) {
     (void)hipGraphExecDestroy(h0->g_batch_merge);
@@ -1425,7 +1425,7 @@ int iskv_launch_merge_batched(isvd_handle* const* hs, int32_t count, const float
 
 int iskv_launch_reorth_batched(isvd_handle* const* hs, int32_t count) {
   isvd_handle* h0 = hs[0];
-  int rc = upload_offsets(hs, count);
+  int rc = iskv_upload_offsets(hs, count);
   if (rc) return rc;
   return run_batched(h0, count, &h0->g_batch_reorth, [&]() { return reorth_body(h0); });
 }

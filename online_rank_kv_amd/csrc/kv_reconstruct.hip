@@ -489,14 +489,30 @@ __global__ __launch_bounds__(256) void exact_rows_kernel(const float* __restrict
 }
 
 // Window bookkeeping: copy `count` rows and their positions.
+// Copy `count` rows and their positions (grid x = row). Copy z of a batched
+// launch (grid z) rebases dst and dpos by bd[z] bytes, and src / spos too when
+// the source lies in the path's own buffers (src_rebased); a caller source is
+// read at src + z * src_stride floats instead.
 __global__ void move_rows_kernel(float* dst, int32_t* dpos, const float* __restrict__ src,
-                                 const int32_t* __restrict__ spos, int32_t pos_base, int D) {
+                                 const int32_t* __restrict__ spos, int32_t pos_base, int D,
+                                 const int64_t* __restrict__ bd, int src_rebased, int64_t src_stride) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  dst = iskv_rb(dst, bdel);
+  dpos = iskv_rb(dpos, bdel);
+  if (src_rebased) {
+    src = iskv_rb(src, bdel);
+    spos = iskv_rb(spos, bdel);
+  } else {
+    src += (size_t)blockIdx.z * src_stride;
+  }
   const int r = blockIdx.x;
   for (int c = threadIdx.x; c < D; c += blockDim.x) dst[(size_t)r * D + c] = src[(size_t)r * D + c];
   if (threadIdx.x == 0 && dpos) dpos[r] = spos ? spos[r] : pos_base + r;
 }
 
-__global__ void fill_pos_kernel(int32_t* pos, int count, int32_t v0, int32_t step) {
+__global__ void fill_pos_kernel(int32_t* pos, int count, int32_t v0, int32_t step,
+                                const int64_t* __restrict__ bd) {
+  pos = iskv_rb(pos, bd ? bd[blockIdx.z] : 0);
   int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < count) pos[i] = v0 + step * i;
 }
@@ -563,18 +579,20 @@ int iskv_launch_exact_rows(const float* X_exact, const int32_t* pos_exact, int32
 
 int iskv_launch_window_move(float* dst_rows, int32_t* dst_pos, const float* src_rows,
                             const int32_t* src_pos, int32_t src_pos_base, int32_t count, int32_t D,
-                            hipStream_t s) {
+                            hipStream_t s, const int64_t* bd, int32_t bc, int32_t src_rebased,
+                            int64_t src_stride) {
   if (count <= 0) return ISKV_OK;
-  hipLaunchKernelGGL(move_rows_kernel, dim3(count), dim3(256), 0, s, dst_rows, dst_pos, src_rows,
-                     src_pos, src_pos_base, D);
+  hipLaunchKernelGGL(move_rows_kernel, bz(dim3(count), bc), dim3(256), 0, s, dst_rows, dst_pos, src_rows,
+                     src_pos, src_pos_base, D, bd, src_rebased, src_stride);
   ISKV_HIP_CHECK(hipGetLastError());
   return ISKV_OK;
 }
 
-int iskv_launch_fill_pos(int32_t* pos, int32_t count, int32_t value0, int32_t step, hipStream_t s) {
+int iskv_launch_fill_pos(int32_t* pos, int32_t count, int32_t value0, int32_t step, hipStream_t s,
+                         const int64_t* bd, int32_t bc) {
   if (count <= 0) return ISKV_OK;
-  hipLaunchKernelGGL(fill_pos_kernel, dim3((count + 255) / 256), dim3(256), 0, s, pos, count, value0,
-                     step);
+  hipLaunchKernelGGL(fill_pos_kernel, bz(dim3((count + 255) / 256), bc), dim3(256), 0, s, pos, count, value0,
+                     step, bd);
   ISKV_HIP_CHECK(hipGetLastError());
   return ISKV_OK;
 }

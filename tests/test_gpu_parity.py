@@ -254,6 +254,52 @@ def test_batched_merges_match_separate(K, graphs):
         p.close()
 
 
+@pytest.mark.parametrize("graphs", [False, True])
+def test_batched_windows_match_separate(K, graphs):
+    """iskv_window_append_batched over 3 paths (windows and factors carved from
+    one allocation) leaves every path's exact window, pending FIFO and factors
+    equal to those of separate iskv_window_append calls, with ragged chunk
+    sizes and a re-orthogonalisation every 4 merges."""
+    cnt, D, r, b, W, T, n = 3, 128, 16, 8, 16, 32, 205
+    Xs = [synth.kv_stream(synth.StreamSpec(D=D, n=n, spectrum="exp4", noise_std=1e-3, seed=20 + z))
+          for z in range(cnt)]
+    Xd = torch.from_numpy(np.stack(Xs)).to(DEV)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream() if graphs else None
+    bat = K.IsvdBatch(cnt, D=D, r_max=r, b_max=b, n_cap=256, reorth_every_rows=T, device=DEV, stream=stream,
+                      graphs=graphs, window=W, block=b)
+    sep_p = [K.IsvdPath(D=D, r_max=r, b_max=b, n_cap=256, reorth_every_rows=T, device=DEV, graphs=False)
+             for _ in range(cnt)]
+    sep_w = [K.ExactWindow(p, window=W, block=b) for p in sep_p]
+    cuts = [0, 5, 8, 24, 27, 60, 61, 100, 140, 141, 180, 205]
+    total_b = total_s = 0
+    for s, e in zip(cuts[:-1], cuts[1:]):
+        total_b += bat.append(Xd[:, s:e], s)
+        for z in range(cnt):
+            total_s += sep_w[z].append(Xd[z, s:e], s)
+    if stream is not None:
+        stream.synchronize()
+    torch.cuda.synchronize()
+    assert total_b * cnt == total_s and total_b == (n - W) // b
+    for z in range(cnt):
+        Cb, Bb, sb, pb, stb = gpu_factors(bat[z])
+        Cs, Bs, ss, ps, sts = gpu_factors(sep_p[z])
+        assert stb == 0 and sts == 0 and np.array_equal(pb, ps)
+        assert rel(Cb @ Bb.T, Cs @ Bs.T) < 1e-6, z
+        assert torch.equal(bat.windows[z].pos, sep_w[z].pos)
+        assert torch.equal(bat.windows[z].rows[bat.windows[z].pos >= 0], sep_w[z].rows[sep_w[z].pos >= 0])
+    # path 1 against the oracle: folded rows are those that left the window
+    C1, B1, _, p1, _ = gpu_factors(bat[1])
+    ref = O.represented(O.run_stream(Xs[1][:C1.shape[0]], b, r, reorth_every_rows=T))
+    assert np.array_equal(p1, np.arange(C1.shape[0]))
+    assert rel(C1 @ B1.T, ref) < 1e-3
+    bat.close()
+    for w in sep_w:
+        w.close()
+    for p in sep_p:
+        p.close()
+
+
 def test_stage_timing_matches_plain_merges(K):
     """Merges with stage events give the same factors as plain merges, report
     five positive stage durations, and refuse to report before a timed merge."""
