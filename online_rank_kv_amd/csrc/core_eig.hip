@@ -14,14 +14,24 @@
 //     on a greedy matching of their strong pairs;          (one workgroup)
 //   every other pair gets the first-order Jacobi angle
 //     K_ij = s_ij / (s_jj - s_ii) (K antisymmetric, clipped),
-//   W <- W R exp(K) with exp(K) = I + K(I + K/2(I + K/3(I + K/4)))
-//                                                  (three GEMMs + one)
-// until every scaled coupling |s_ij| / sqrt(s_ii s_jj) is below 1e-10. This
-// is the first-order eigenvector refinement of the Jacobi family (all
-// rotations of a sweep at once), with near-ties handled exactly. A final
-// Newton-Schulz step restores W^T W = I. Cores that do not converge in
-// PCJ_MAXIT steps (strongly mixed early merges) fall back to the
+//   W <- W R X with X = I + K (I + K/2), the exponential of K to second
+//   order                                           (two GEMMs)
+//   W <- 1.5 W - 0.5 W (W^T W) (Newton-Schulz, two GEMMs) before the next S
+// until every scaled coupling |s_ij| / sqrt(s_ii s_jj) is below the
+// tolerance. This is the first-order eigenvector refinement of the Jacobi
+// family (all rotations of a sweep at once), with near-ties handled exactly.
+// A final Newton-Schulz step restores W^T W = I. Cores that do not converge
+// in PCJ_MAXIT steps (strongly mixed early merges) fall back to the
 // single-workgroup cyclic Jacobi.
+//
+// Tolerance. isvd_sym_eig asks for eigenvectors to 1e-10. A merge only needs
+// the product C B^T: rotations among kept directions leave it unchanged, and
+// a coupling c left between a kept and a dropped direction changes it by
+// about c relative, as does a coupling among kept directions through the
+// stored sigma (the next merge takes C^T C as diagonal). Merges and
+// re-orthogonalisations therefore stop at 1e-8, far below the fp32 rounding
+// the factors carry (on the 16K-row K and V streams this saves one step in
+// most merges and leaves the reconstruction error unchanged).
 #include "iskv_internal.h"
 
 #include <math.h>
@@ -29,7 +39,6 @@
 namespace {
 
 constexpr int PCJ_MAXIT = 7;
-constexpr double PCJ_TOL = 1e-10;
 constexpr double PCJ_OMEGA = 0.1;
 constexpr double PCJ_CLIP = 0.2;
 constexpr int CMAX_S = 6;      // largest cluster diagonalised exactly
@@ -69,9 +78,9 @@ __device__ __forceinline__ double keep_if(double v, bool keep) {
 // (row or column l%16, group g = l/16) takes depths 16 c + 4 g + q for MFMA
 // step q, so that the operands stored along k are contiguous per lane.
 // Matrices have a leading dimension that is a multiple of 16 and at least
-// m_max rounded up to 16, so every index below that lies in the allocation:
-// the loads of the first chunks are issued before m is read, entries with
-// depth >= m are zeroed, rows and columns >= m are computed and dropped.
+// m_max rounded up to 16, so every index of a 16-chunk that starts below m
+// lies in the allocation: entries with depth >= m are zeroed, rows and
+// columns >= m of a tile that starts below m are computed and dropped.
 constexpr int DG_CH = 5;  // chunks per wave kept in flight (m <= 320 in one pass)
 
 template <bool TA, bool TB>
@@ -91,7 +100,7 @@ __global__ __launch_bounds__(256) void dgemm_kernel(const double* __restrict__ A
   const int i0 = blockIdx.y * 16, j0 = blockIdx.x * 16;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int nch_max = (m_max + 15) / 16;
+  (void)m_max;
   double av[DG_CH][4], bv[DG_CH][4];
   // A(i0 + r, k) and B(k, j0 + r) for k = 16 c + 4 g + q
   auto load = [&](int u, int c) {
@@ -102,9 +111,8 @@ __global__ __launch_bounds__(256) void dgemm_kernel(const double* __restrict__ A
       bv[u][q] = TB ? B[(size_t)(j0 + r) * ldb + kb + q] : B[(size_t)(kb + q) * ldb + j0 + r];
     }
   };
-#pragma unroll
-  for (int u = 0; u < DG_CH; ++u)
-    if (wave + 4 * u < nch_max) load(u, wave + 4 * u);
+  // the state is read before any operand load: a launch skipped because
+  // the refinement has converged (or a tile beyond m) moves no data
   const int m = st[ST_JM];
   if (i0 >= m || j0 >= m) return;
   const bool conv = (st[ST_PCJ] & FLAG_CONV) != 0;
@@ -115,6 +123,9 @@ __global__ __launch_bounds__(256) void dgemm_kernel(const double* __restrict__ A
     return;
   }
   const int nch = (m + 15) / 16;
+#pragma unroll
+  for (int u = 0; u < DG_CH; ++u)
+    if (wave + 4 * u < nch) load(u, wave + 4 * u);
   v4d acc = {0.0, 0.0, 0.0, 0.0}, acc2 = {0.0, 0.0, 0.0, 0.0};
   for (int c0 = wave; c0 < nch; c0 += 4 * DG_CH) {
     if (c0 != wave) {
@@ -237,7 +248,7 @@ __device__ void jacobi_serial(double* S, double* V, int c) {
 // pairs are appended to a global list (order fixed later by sorting).
 // aux layout: [0, 256) doubles = block maxima, then EMAX int pairs.
 __global__ __launch_bounds__(256) void pcj_detect_kernel(const double* __restrict__ S, int ld,
-                                                         double* aux, int32_t* st,
+                                                         double* aux, int32_t* st, double tol,
     const int64_t* __restrict__ bd) {
   const int64_t bdel = bd ? bd[blockIdx.z] : 0;
   S = iskv_rb(S, bdel);
@@ -258,7 +269,7 @@ __global__ __launch_bounds__(256) void pcj_detect_kernel(const double* __restric
       double di = S[(size_t)i * ld + i], dj = S[(size_t)j * ld + j];
       double c = coupling(sij, di, dj);
       if (c > cmax) cmax = c;
-      if (c > PCJ_TOL && fabs(sij) > PCJ_OMEGA * fabs(dj - di)) {
+      if (c > tol && fabs(sij) > PCJ_OMEGA * fabs(dj - di)) {
         int slot = atomicAdd(&st[ST_NEDGE], 1);
         if (slot < EMAX) { edges[2 * slot] = i; edges[2 * slot + 1] = j; }
       }
@@ -295,7 +306,7 @@ struct AnalyzeLds {
 // ones: 2x2 rotations on a greedy matching), applied to S and W in place.
 __global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W, int ld,
                                                            const double* __restrict__ aux,
-                                                           int32_t* st, int it,
+                                                           int32_t* st, int it, double tol,
     const int64_t* __restrict__ bd) {
   const int64_t bdel = bd ? bd[blockIdx.z] : 0;
   S = iskv_rb(S, bdel);
@@ -323,7 +334,7 @@ __global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W,
   for (int i = t; i < m; i += nt) L.d[i] = S[(size_t)i * ld + i];
   __syncthreads();
   const double cmax = L.cmax;
-  if (cmax < PCJ_TOL) {  // NaN couplings never pass: they end in the fallback
+  if (cmax < tol) {  // NaN couplings never pass: they end in the fallback
     __syncthreads();
     if (t == 0) { st[ST_PCJ] |= FLAG_CONV; st[ST_PCJIT] = it; st[ST_NEDGE] = 0; }
     return;
@@ -674,7 +685,7 @@ int iskv_core_eig_setup() {
 // Eigen-decompose the m x m matrix in w.A (m = st[ST_JM]): on return the
 // diagonal of w.S holds the eigenvalues and w.V the eigenvectors (columns),
 // unsorted. Fixed launch sequence; no host synchronisation.
-int iskv_launch_core_eig(isvd_handle* h) {
+int iskv_launch_core_eig(isvd_handle* h, double tol) {
   const isvd_ws& w = h->w;
   hipStream_t s = h->stream;
   const int mm = h->m_max, ld = h->ldm;
@@ -694,8 +705,9 @@ int iskv_launch_core_eig(isvd_handle* h) {
       dgemm<false, false>(s, mm, w.A, cur, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 0, h->bd, h->bcount);
       dgemm<true, false>(s, mm, cur, w.T, w.S, nullptr, ld, 1.0, 0.0, 0.0, st, 0, h->bd, h->bcount);
     }
-    hipLaunchKernelGGL(pcj_detect_kernel, bz(dim3(nblk), h->bcount), dim3(256), 0, s, w.S, ld, w.aux, st, h->bd);
-    hipLaunchKernelGGL(pcj_analyze_kernel, bz(dim3(1), h->bcount), dim3(1024), lds, s, w.S, cur, ld, w.aux, st, it, h->bd);
+    hipLaunchKernelGGL(pcj_detect_kernel, bz(dim3(nblk), h->bcount), dim3(256), 0, s, w.S, ld, w.aux, st, tol, h->bd);
+    hipLaunchKernelGGL(pcj_analyze_kernel, bz(dim3(1), h->bcount), dim3(1024), lds, s, w.S, cur, ld, w.aux, st, it, tol,
+                       h->bd);
     if (it == PCJ_MAXIT) break;  // last pass only tests convergence
     hipLaunchKernelGGL(pcj_kmat_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.S, ld, w.Km, w.Pa, st, h->bd);
     // X = I + K (I + K/2); W <- W X

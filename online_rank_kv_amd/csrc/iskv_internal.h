@@ -134,7 +134,10 @@ inline int iskv_core_ld(int m_max) { return (m_max + ISKV_DGEMM_KP - 1) / ISKV_D
 // ---- launch helpers implemented in the kernel translation units ----
 int iskv_kernel_setup();
 int iskv_core_eig_setup();
-int iskv_launch_core_eig(isvd_handle* h);
+// Core eigensolver on w.A; stops when every scaled coupling is below tol.
+int iskv_launch_core_eig(isvd_handle* h, double tol);
+#define ISKV_EIG_TOL_EXACT 1e-10   // isvd_sym_eig
+#define ISKV_EIG_TOL_UPDATE 1e-8   // merges and re-orthogonalisations
 void iskv_dgemm(hipStream_t s, int m_max, const double* A, bool ta, const double* B, bool tb, double* C,
                 const double* Cin, int ld, double alpha, double beta, double gamma, const int32_t* st,
                 int mode, const int64_t* bd, int bc);

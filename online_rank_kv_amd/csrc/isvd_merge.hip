@@ -1098,7 +1098,7 @@ int iskv_launch_sym_eig(isvd_handle* h, const double* A, int32_t m, double* lam,
   const isvd_ws& w = h->w;
   hipStream_t s = h->stream;
   hipLaunchKernelGGL(load_sym_kernel, dim3(128), dim3(256), 0, s, A, m, w.A, h->ldm, w.st);
-  int rc = iskv_launch_core_eig(h);
+  int rc = iskv_launch_core_eig(h, ISKV_EIG_TOL_EXACT);
   if (rc) return rc;
   eig_finish(h, 0);
   hipLaunchKernelGGL(store_sym_kernel, dim3(128), dim3(256), 0, s, w.S, w.V, h->ldm, w.order, m, lam, V);
@@ -1166,7 +1166,7 @@ static int merge_body(isvd_handle* h, const float* F, const int32_t* pos_F, int3
   }
   hipLaunchKernelGGL(set_jm_kernel, bz(dim3(1), h->bcount), dim3(1), 0, s, w.st, (int)ST_M, h->bd);
   {
-    int rc = iskv_launch_core_eig(h);
+    int rc = iskv_launch_core_eig(h, ISKV_EIG_TOL_UPDATE);
     if (rc) return rc;
   }
   eig_finish(h, 1);
@@ -1228,7 +1228,7 @@ static int reorth_body(isvd_handle* h) {
   iskv_dgemm(s, mm, w.MB, false, w.Km, false, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 2, h->bd, h->bcount);
   iskv_dgemm(s, mm, w.T, false, w.MB, true, w.A, nullptr, ld, 1.0, 0.0, 0.0, st, 2, h->bd, h->bcount);
   {
-    int rc = iskv_launch_core_eig(h);
+    int rc = iskv_launch_core_eig(h, ISKV_EIG_TOL_UPDATE);
     if (rc) return rc;
   }
   eig_finish(h, 0);
