@@ -43,7 +43,7 @@ constexpr double PCJ_OMEGA = 0.1;
 constexpr double PCJ_CLIP = 0.2;
 constexpr int CMAX_S = 6;      // largest cluster diagonalised exactly
 constexpr int NCL_MAX = 64;    // clusters handled exactly per step
-constexpr int EMAX = 4096;     // strong pairs recorded per step
+constexpr int EMAX = ISKV_PCJ_EMAX;  // strong pairs recorded per step
 constexpr int NPAIR_MAX = 512; // matched pairs per step
 
 constexpr int FLAG_CONV = 1;
@@ -178,6 +178,223 @@ void dgemm(hipStream_t s, int m_max, const double* A, const double* B, double* C
                      beta, gamma, st, mode, m_max, bd);
 }
 
+__device__ __forceinline__ double coupling(double sij, double di, double dj) {
+  double dd = di * dj;
+  double a = fabs(sij);
+  if (dd > 0.0) return a / sqrt(dd);
+  return a > 0.0 ? INFINITY : 0.0;
+}
+
+// Two products that share the right operand, one 16 x 16 tile of each per
+// workgroup (the right-operand panel is loaded once):
+//   C1 = alpha1 op(A1) B + beta1 Cin1,   C2 = alpha2 op(A2) B + beta2 Cin2
+// over the m x m leading block (m = st[ST_JM]); same depth split, lane
+// layout and skip modes as dgemm_kernel (mode 1 copies Cin1 / Cin2 when the
+// refinement has converged). With Dp, the workgroup also writes, for each
+// column j of its tile, the partial sum over its 16 rows of C1[i][j] C2[i][j]
+// to Dp[blockIdx.y][j]; summed over the row blocks this is the diagonal of
+// C1^T C2.
+template <bool TA1, bool TA2>
+__global__ __launch_bounds__(256) void dgemm2_kernel(const double* __restrict__ A1, const double* __restrict__ A2,
+                                                     const double* __restrict__ B, int ld, double* C1, double* C2,
+                                                     const double* Cin1, const double* Cin2, double alpha1,
+                                                     double beta1, double alpha2, double beta2, double* Dp,
+                                                     const int32_t* __restrict__ st, int mode,
+                                                     const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  A1 = iskv_rb(A1, bdel);
+  A2 = iskv_rb(A2, bdel);
+  B = iskv_rb(B, bdel);
+  C1 = iskv_rb(C1, bdel);
+  C2 = iskv_rb(C2, bdel);
+  Cin1 = iskv_rb(Cin1, bdel);
+  Cin2 = iskv_rb(Cin2, bdel);
+  Dp = iskv_rb(Dp, bdel);
+  st = iskv_rb(st, bdel);
+  const int i0 = blockIdx.y * 16, j0 = blockIdx.x * 16;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int m = st[ST_JM];
+  if (i0 >= m || j0 >= m) return;
+  const bool conv = (st[ST_PCJ] & FLAG_CONV) != 0;
+  if (mode == 0 && conv) return;
+  if (mode == 1 && conv) {
+    const int i = i0 + (t >> 4), j = j0 + (t & 15);
+    if (i < m && j < m) {
+      C1[(size_t)i * ld + j] = Cin1[(size_t)i * ld + j];
+      C2[(size_t)i * ld + j] = Cin2[(size_t)i * ld + j];
+    }
+    return;
+  }
+  const int nch = (m + 15) / 16;
+  double a1v[DG_CH][4], a2v[DG_CH][4], bv[DG_CH][4];
+  auto load = [&](int u, int c) {
+    const int kb = 16 * c + 4 * g;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      a1v[u][q] = TA1 ? A1[(size_t)(kb + q) * ld + i0 + r] : A1[(size_t)(i0 + r) * ld + kb + q];
+      a2v[u][q] = TA2 ? A2[(size_t)(kb + q) * ld + i0 + r] : A2[(size_t)(i0 + r) * ld + kb + q];
+      bv[u][q] = B[(size_t)(kb + q) * ld + j0 + r];
+    }
+  };
+  v4d acc1 = {0.0, 0.0, 0.0, 0.0}, acc1b = acc1, acc2 = acc1, acc2b = acc1;
+  for (int c0 = wave; c0 < nch; c0 += 4 * DG_CH) {
+#pragma unroll
+    for (int u = 0; u < DG_CH; ++u)
+      if (c0 + 4 * u < nch) load(u, c0 + 4 * u);
+#pragma unroll
+    for (int u = 0; u < DG_CH; ++u) {
+      const int c = c0 + 4 * u;
+      if (c < nch) {
+        const int kb = 16 * c + 4 * g;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bool in = kb + q < m;
+          const double bb = keep_if(bv[u][q], in);
+          if (q & 1) {
+            acc1b = __builtin_amdgcn_mfma_f64_16x16x4f64(keep_if(a1v[u][q], in), bb, acc1b, 0, 0, 0);
+            acc2b = __builtin_amdgcn_mfma_f64_16x16x4f64(keep_if(a2v[u][q], in), bb, acc2b, 0, 0, 0);
+          } else {
+            acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(keep_if(a1v[u][q], in), bb, acc1, 0, 0, 0);
+            acc2 = __builtin_amdgcn_mfma_f64_16x16x4f64(keep_if(a2v[u][q], in), bb, acc2, 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+  acc1 += acc1b;
+  acc2 += acc2b;
+  __shared__ double red[3][2][4][64];
+  if (wave > 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      red[wave - 1][0][e][lane] = acc1[e];
+      red[wave - 1][1][e][lane] = acc2[e];
+    }
+  }
+  __syncthreads();
+  if (wave > 0) return;
+  // result lane l, element e is D(l/16 + 4e, l%16)
+  double dsum = 0.0;
+  const int j = j0 + r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = i0 + g + 4 * e;
+    if (i < m && j < m) {
+      double o1 = alpha1 * (acc1[e] + red[0][0][e][lane] + red[1][0][e][lane] + red[2][0][e][lane]);
+      double o2 = alpha2 * (acc2[e] + red[0][1][e][lane] + red[1][1][e][lane] + red[2][1][e][lane]);
+      if (beta1 != 0.0) o1 += beta1 * Cin1[(size_t)i * ld + j];
+      if (beta2 != 0.0) o2 += beta2 * Cin2[(size_t)i * ld + j];
+      C1[(size_t)i * ld + j] = o1;
+      C2[(size_t)i * ld + j] = o2;
+      dsum = fma(o1, o2, dsum);
+    }
+  }
+  if (Dp) {
+    dsum += __shfl_xor(dsum, 16, 64);
+    dsum += __shfl_xor(dsum, 32, 64);
+    if (g == 0) Dp[(size_t)blockIdx.y * ld + j] = dsum;
+  }
+}
+
+// S = W^T T (one 16 x 16 tile per workgroup, as dgemm_kernel<true, false>)
+// with the strong-pair detection of the refinement in its epilogue: the
+// diagonal of S comes from the row-block partial sums Dp of the launch that
+// formed W and T (ceil(m / 16) blocks), every pair i < j of the tile gets its scaled
+// coupling, strong pairs are appended to the edge list and the tile's
+// largest coupling goes to aux[tile] (0 for tiles outside m x m or after
+// convergence, so the maxima never carry values of an earlier step).
+__global__ __launch_bounds__(256) void dgemm_s_kernel(const double* __restrict__ W, const double* __restrict__ T,
+                                                      int ld, double* S, const double* __restrict__ Dp,
+                                                      double* aux, int* edges, int32_t* st, double tol,
+                                                      const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  W = iskv_rb(W, bdel);
+  T = iskv_rb(T, bdel);
+  S = iskv_rb(S, bdel);
+  Dp = iskv_rb(Dp, bdel);
+  aux = iskv_rb(aux, bdel);
+  edges = iskv_rb(edges, bdel);
+  st = iskv_rb(st, bdel);
+  const int i0 = blockIdx.y * 16, j0 = blockIdx.x * 16;
+  const int tile = blockIdx.y * gridDim.x + blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int m = st[ST_JM];
+  const bool conv = (st[ST_PCJ] & FLAG_CONV) != 0;
+  if (i0 >= m || j0 >= m || conv) {
+    if (t == 0) aux[tile] = 0.0;
+    return;
+  }
+  const int nch = (m + 15) / 16, nrb = nch;
+  double av[DG_CH][4], bv[DG_CH][4];
+#pragma unroll
+  for (int u = 0; u < DG_CH; ++u) {
+    const int c = wave + 4 * u;
+    if (c < nch) {
+      const int kb = 16 * c + 4 * g;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        av[u][q] = W[(size_t)(kb + q) * ld + i0 + r];
+        bv[u][q] = T[(size_t)(kb + q) * ld + j0 + r];
+      }
+    }
+  }
+  // diagonal entries of the tile's rows and columns (lane r: row i0 + r and column j0 + r)
+  double di = 0.0, dj = 0.0;
+  if (wave == 0) {
+    for (int b = 0; b < nrb; ++b) {
+      di += Dp[(size_t)b * ld + i0 + r];
+      dj += Dp[(size_t)b * ld + j0 + r];
+    }
+  }
+  v4d acc = {0.0, 0.0, 0.0, 0.0}, acc2 = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int u = 0; u < DG_CH; ++u) {
+    const int c = wave + 4 * u;
+    if (c < nch) {
+      const int kb = 16 * c + 4 * g;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool in = kb + q < m;
+        const double a = keep_if(av[u][q], in), bb = keep_if(bv[u][q], in);
+        if (q & 1) acc2 = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bb, acc2, 0, 0, 0);
+        else acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bb, acc, 0, 0, 0);
+      }
+    }
+  }
+  acc += acc2;
+  __shared__ double red[3][4][64];
+  if (wave > 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[wave - 1][e][lane] = acc[e];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+  double cmax = 0.0;
+  const int j = j0 + r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = i0 + g + 4 * e;
+    const double dii = __shfl(di, g + 4 * e, 64);
+    if (i < m && j < m) {
+      const double o = acc[e] + red[0][e][lane] + red[1][e][lane] + red[2][e][lane];
+      S[(size_t)i * ld + j] = o;
+      if (j > i) {
+        const double c = coupling(o, dii, dj);
+        cmax = fmax(cmax, c);
+        if (c > tol && fabs(o) > PCJ_OMEGA * fabs(dj - dii)) {
+          const int slot = atomicAdd(&st[ST_NEDGE], 1);
+          if (slot < EMAX) { edges[2 * slot] = i; edges[2 * slot + 1] = j; }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) cmax = fmax(cmax, __shfl_xor(cmax, o, 64));
+  if (lane == 0) aux[tile] = cmax;
+}
+
 // S = A, W = I, flags cleared.
 __global__ __launch_bounds__(256) void pcj_init_kernel(const double* __restrict__ A, double* S,
                                                        double* W, int ld, int32_t* st,
@@ -197,12 +414,6 @@ __global__ __launch_bounds__(256) void pcj_init_kernel(const double* __restrict_
   if (blockIdx.x == 0 && threadIdx.x == 0) { st[ST_PCJ] = 0; st[ST_PCJIT] = 0; st[ST_NEDGE] = 0; }
 }
 
-__device__ __forceinline__ double coupling(double sij, double di, double dj) {
-  double dd = di * dj;
-  double a = fabs(sij);
-  if (dd > 0.0) return a / sqrt(dd);
-  return a > 0.0 ? INFINITY : 0.0;
-}
 
 __device__ __forceinline__ void rot2(double app, double aqq, double apq, double* c, double* s) {
   double tau = (aqq - app) / (2.0 * apq);
@@ -243,16 +454,18 @@ __device__ void jacobi_serial(double* S, double* V, int c) {
   }
 }
 
-// Strong pairs and per-block maxima of the scaled coupling, many workgroups.
-// Block b scans rows [16 b, 16 b + 16) against every column j > i. Strong
-// pairs are appended to a global list (order fixed later by sorting).
-// aux layout: [0, 256) doubles = block maxima, then EMAX int pairs.
+// Strong pairs and per-block maxima of the scaled coupling, many workgroups
+// (first refinement step, where S = A; later steps detect in the epilogue of
+// the GEMM that forms S). Block b scans rows [16 b, 16 b + 16) against every
+// column j > i and writes its maximum to aux[b]. Strong pairs are appended to
+// the edge list (order fixed later by sorting).
 __global__ __launch_bounds__(256) void pcj_detect_kernel(const double* __restrict__ S, int ld,
-                                                         double* aux, int32_t* st, double tol,
+                                                         double* aux, int* edges, int32_t* st, double tol,
     const int64_t* __restrict__ bd) {
   const int64_t bdel = bd ? bd[blockIdx.z] : 0;
   S = iskv_rb(S, bdel);
   aux = iskv_rb(aux, bdel);
+  edges = iskv_rb(edges, bdel);
   st = iskv_rb(st, bdel);
   if (st[ST_PCJ] & FLAG_CONV) return;
   const int m = st[ST_JM];
@@ -260,7 +473,6 @@ __global__ __launch_bounds__(256) void pcj_detect_kernel(const double* __restric
   __shared__ double red[4];
   double cmax = 0.0;
   if (r0 < m) {
-    int* edges = (int*)(aux + 256);
     const int rows = min(16, m - r0);
     for (int e = threadIdx.x; e < rows * m; e += 256) {
       int i = r0 + e / m, j = e % m;
@@ -279,8 +491,7 @@ __global__ __launch_bounds__(256) void pcj_detect_kernel(const double* __restric
   for (int o = 32; o > 0; o >>= 1) cmax = fmax(cmax, __shfl_xor(cmax, o, 64));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = cmax;
   __syncthreads();
-  if (threadIdx.x == 0 && blockIdx.x < 256)
-    aux[blockIdx.x] = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+  if (threadIdx.x == 0) aux[blockIdx.x] = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
 }
 
 struct AnalyzeLds {
@@ -305,23 +516,24 @@ struct AnalyzeLds {
 // strong-pair graph), exact rotations (small clusters: cyclic Jacobi; big
 // ones: 2x2 rotations on a greedy matching), applied to S and W in place.
 __global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W, int ld,
-                                                           const double* __restrict__ aux,
+                                                           const double* __restrict__ aux, int nmx,
+                                                           const int* __restrict__ edges,
                                                            int32_t* st, int it, double tol,
     const int64_t* __restrict__ bd) {
   const int64_t bdel = bd ? bd[blockIdx.z] : 0;
   S = iskv_rb(S, bdel);
   W = iskv_rb(W, bdel);
   aux = iskv_rb(aux, bdel);
+  edges = iskv_rb(edges, bdel);
   st = iskv_rb(st, bdel);
   extern __shared__ unsigned char smem_raw[];
   AnalyzeLds& L = *reinterpret_cast<AnalyzeLds*>(smem_raw);
   if (st[ST_PCJ] & FLAG_CONV) return;
   const int m = st[ST_JM];
   const int t = threadIdx.x, nt = blockDim.x;
-  const int nblk = (m + 15) / 16;
   if (t < 64) {
     double c = 0.0;
-    for (int b = t; b < nblk && b < 256; b += 64) c = fmax(c, aux[b]);
+    for (int b = t; b < nmx; b += 64) c = fmax(c, aux[b]);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) c = fmax(c, __shfl_xor(c, o, 64));
     if (t == 0) {
@@ -340,7 +552,6 @@ __global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W,
     return;
   }
   const int ne = L.nedge;
-  const int* edges = (const int*)(aux + 256);
   for (int e = t; e < ne; e += nt) L.key[e] = edges[2 * e] * 1024 + edges[2 * e + 1];
   for (int i = t; i < m; i += nt) { L.lab[i] = i; L.size[i] = 0; L.used[i] = 0; L.cid[i] = -1; }
   __syncthreads();
@@ -691,35 +902,49 @@ int iskv_launch_core_eig(isvd_handle* h, double tol) {
   const int mm = h->m_max, ld = h->ldm;
   int32_t* st = w.st;
   const int nblk = (mm + 15) / 16;
-  hipLaunchKernelGGL(pcj_init_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.A, w.S, w.W0, ld, st, h->bd);
-  double* cur = w.W0;
-  double* nxt = w.W1;
+  const dim3 tiles(nblk, nblk);
   const size_t lds = sizeof(AnalyzeLds);
-  for (int it = 0; it <= PCJ_MAXIT; ++it) {
-    if (it > 0) {
-      // Newton-Schulz: W <- 1.5 W - 0.5 W (W^T W) keeps W orthonormal to
-      // O(defect^2), so S is measured in an orthonormal basis
-      dgemm<true, false>(s, mm, cur, cur, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 0, h->bd, h->bcount);
-      dgemm<false, false>(s, mm, cur, w.T, nxt, cur, ld, -0.5, 1.5, 0.0, st, 1, h->bd, h->bcount);
-      { double* tmp = cur; cur = nxt; nxt = tmp; }
-      dgemm<false, false>(s, mm, w.A, cur, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 0, h->bd, h->bcount);
-      dgemm<true, false>(s, mm, cur, w.T, w.S, nullptr, ld, 1.0, 0.0, 0.0, st, 0, h->bd, h->bcount);
-    }
-    hipLaunchKernelGGL(pcj_detect_kernel, bz(dim3(nblk), h->bcount), dim3(256), 0, s, w.S, ld, w.aux, st, tol, h->bd);
-    hipLaunchKernelGGL(pcj_analyze_kernel, bz(dim3(1), h->bcount), dim3(1024), lds, s, w.S, cur, ld, w.aux, st, it, tol,
-                       h->bd);
+  hipLaunchKernelGGL(pcj_init_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.A, w.S, w.W0, ld, st, h->bd);
+  // step 0 works on S = A with W = I
+  hipLaunchKernelGGL(pcj_detect_kernel, bz(dim3(nblk), h->bcount), dim3(256), 0, s, w.S, ld, w.aux, w.edges, st,
+                     tol, h->bd);
+  hipLaunchKernelGGL(pcj_analyze_kernel, bz(dim3(1), h->bcount), dim3(1024), lds, s, w.S, w.W0, ld, w.aux, nblk,
+                     w.edges, st, 0, tol, h->bd);
+  hipLaunchKernelGGL(pcj_kmat_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.S, ld, w.Km, w.Pa, st, h->bd);
+  // X = I + K (I + K/2); W <- W X
+  dgemm<false, false>(s, mm, w.Km, w.Pa, w.Pb, nullptr, ld, 1.0, 0.0, 1.0, st, 0, h->bd, h->bcount);
+  dgemm<false, false>(s, mm, w.W0, w.Pb, w.W1, w.W0, ld, 1.0, 0.0, 0.0, st, 1, h->bd, h->bcount);
+  // From step 1 on, W sits in `wc` at the start of a step and its
+  // re-orthonormalised form W' in `wo`; after convergence `wo` keeps the final
+  // W (the launches that would change it are skipped).
+  double* wc = w.W1;
+  double* wo = w.W0;
+  for (int it = 1; it <= PCJ_MAXIT; ++it) {
+    // T1 = W^T W and T2 = A W (A symmetric: read as A^T)
+    hipLaunchKernelGGL((dgemm2_kernel<true, true>), bz(tiles, h->bcount), dim3(256), 0, s, wc, w.A, wc, ld, w.T,
+                       w.Km, nullptr, nullptr, 1.0, 0.0, 1.0, 0.0, nullptr, st, 0, h->bd);
+    // Newton-Schulz W' = 1.5 W - 0.5 W T1, and A W' = 1.5 T2 - 0.5 T2 T1 (keeps W
+    // orthonormal to O(defect^2), so S is measured in an orthonormal basis);
+    // partial sums of diag(W'^T A W')
+    hipLaunchKernelGGL((dgemm2_kernel<false, false>), bz(tiles, h->bcount), dim3(256), 0, s, wc, w.Km, w.T, ld, wo,
+                       w.Pa, wc, w.Km, -0.5, 1.5, -0.5, 1.5, w.Dp, st, 0, h->bd);
+    // S = W'^T (A W') with the strong-pair detection
+    hipLaunchKernelGGL(dgemm_s_kernel, bz(tiles, h->bcount), dim3(256), 0, s, wo, w.Pa, ld, w.S, w.Dp, w.aux,
+                       w.edges, st, tol, h->bd);
+    hipLaunchKernelGGL(pcj_analyze_kernel, bz(dim3(1), h->bcount), dim3(1024), lds, s, w.S, wo, ld, w.aux,
+                       nblk * nblk, w.edges, st, it, tol, h->bd);
     if (it == PCJ_MAXIT) break;  // last pass only tests convergence
     hipLaunchKernelGGL(pcj_kmat_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.S, ld, w.Km, w.Pa, st, h->bd);
-    // X = I + K (I + K/2); W <- W X
     dgemm<false, false>(s, mm, w.Km, w.Pa, w.Pb, nullptr, ld, 1.0, 0.0, 1.0, st, 0, h->bd, h->bcount);
-    dgemm<false, false>(s, mm, cur, w.Pb, nxt, cur, ld, 1.0, 0.0, 0.0, st, 1, h->bd, h->bcount);
-    { double* tmp = cur; cur = nxt; nxt = tmp; }
+    dgemm<false, false>(s, mm, wo, w.Pb, wc, wo, ld, 1.0, 0.0, 0.0, st, 1, h->bd, h->bcount);
   }
-  // final Newton-Schulz, then T = A W for the eigenvalues
-  dgemm<true, false>(s, mm, cur, cur, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 2, h->bd, h->bcount);
-  dgemm<false, false>(s, mm, cur, w.T, nxt, cur, ld, -0.5, 1.5, 0.0, st, 2, h->bd, h->bcount);
-  dgemm<false, false>(s, mm, w.A, nxt, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 2, h->bd, h->bcount);
-  hipLaunchKernelGGL(pcj_final_kernel, bz(dim3(mm), h->bcount), dim3(256), 0, s, nxt, w.T, w.A, w.S, w.V, ld, st, h->bd);
+  // final Newton-Schulz of W (in wo) into wc, with A W for the eigenvalues
+  hipLaunchKernelGGL((dgemm2_kernel<true, true>), bz(tiles, h->bcount), dim3(256), 0, s, wo, w.A, wo, ld, w.T, w.Km,
+                     nullptr, nullptr, 1.0, 0.0, 1.0, 0.0, nullptr, st, 2, h->bd);
+  hipLaunchKernelGGL((dgemm2_kernel<false, false>), bz(tiles, h->bcount), dim3(256), 0, s, wo, w.Km, w.T, ld, wc,
+                     w.Pa, wo, w.Km, -0.5, 1.5, -0.5, 1.5, nullptr, st, 2, h->bd);
+  hipLaunchKernelGGL(pcj_final_kernel, bz(dim3(mm), h->bcount), dim3(256), 0, s, wc, w.Pa, w.A, w.S, w.V, ld, st,
+                     h->bd);
   hipLaunchKernelGGL(core_jacobi_kernel, bz(dim3(1), h->bcount), dim3(1024), 0, s, w.S, w.V, ld, st, 1e-13,
                      ISKV_JACOBI_MAX_SWEEPS, h->bd);
   ISKV_HIP_CHECK(hipGetLastError());

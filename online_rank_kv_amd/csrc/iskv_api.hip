@@ -62,7 +62,10 @@ size_t carve(const iskv_config* c, char* base, isvd_ws* w) {
   x.Pb = (double*)take(LM * LM * 8);
   x.MB = (double*)take(LM * LM * 8);
   x.Zb = (double*)take(LM * LM * 8);
-  x.aux = (double*)take(256 * 8 + 4096 * 8);
+  x.naux = (int)((LM / 16) * (LM / 16));
+  x.aux = (double*)take((size_t)x.naux * 8);
+  x.edges = (int32_t*)take((size_t)ISKV_PCJ_EMAX * 2 * 4);
+  x.Dp = (double*)take((LM / 16) * LM * 8);
   x.lam = (double*)take(M * 8);
   x.rot_cap = 0;
   x.rot = nullptr;

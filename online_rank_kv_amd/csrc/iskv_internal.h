@@ -53,7 +53,9 @@ struct isvd_ws {
   double* Pb;         // [ldm x ldm]
   double* MB;         // [ldm x ldm]  reorth: (B^T B)^(1/2)
   double* Zb;         // [ldm x ldm]  reorth: (B^T B)^(-1/2)
-  double* aux;        // [256 doubles + 4096 int pairs] detection results
+  double* aux;        // [naux] per-tile / per-block maxima of the scaled coupling
+  int32_t* edges;     // [ISKV_PCJ_EMAX x 2] strongly coupled pairs of a refinement step
+  double* Dp;         // [ldm / 16 x ldm] partial sums of diag(W^T A W) per 16-row block
   double* lam;        // [m_max]
   double* rot;        // [rot_cap] Jacobi rotation log (c, s) pairs
   float* Hc;          // [m_max x r_max]  kept right singular vectors of the core
@@ -67,6 +69,7 @@ struct isvd_ws {
   int32_t* posFs;     // [b_max]      its positions
   int64_t* btab;      // [ISKV_MAX_BATCH] per-handle byte offsets of a batched launch
   size_t rot_cap;     // doubles in rot
+  int naux;           // doubles in aux
   int gram_splits;
 };
 
@@ -123,6 +126,8 @@ struct iskv_window {
 };
 
 #define ISKV_JACOBI_MAX_SWEEPS 40
+// Strongly coupled pairs recorded per refinement step of the core solver.
+#define ISKV_PCJ_EMAX 4096
 // K-panel depth of the fp64 core GEMM; the leading dimension of every fp64
 // core matrix in the workspace is a multiple of it.
 #define ISKV_DGEMM_KP 288
