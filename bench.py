@@ -52,6 +52,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--batch-paths", type=int, default=64,
+                    help="paths of the many-path leg (0 skips it)")
+    ap.add_argument("--batch-rows", type=int, default=N0, help="rows per path before the many-path leg's timing")
+    ap.add_argument("--batch-steps", type=int, default=16, help="timed batched merges of the many-path leg")
     ap.add_argument("--batched-kv", action="store_true",
                     help="K and V carved from one allocation, merged as one batched launch sequence")
     ap.add_argument("--no-graphs", action="store_true",
@@ -75,6 +79,62 @@ def profiled_traffic(name):
     if hashlib.sha256(src).hexdigest() != d["source_sha256"]:
         return None
     return float(d["traffic_bytes_per_dispatch"])
+
+
+def many_path_leg(args, K, torch, dev):
+    """Many independent paths merged as one batched launch sequence per step
+    (isvd_merge_block_batched through iskv_window_append_batched): half key
+    paths, half value paths, rows drawn on the device (synth.DeviceStreams),
+    each path first filled to --batch-rows rows, then --batch-steps timed
+    steps of one b-row block per path (one merge per path)."""
+    import synth
+    P, n0, steps = args.batch_paths, args.batch_rows, args.batch_steps
+    warm = 2
+    st = torch.cuda.Stream()
+    n_cap = n0 + WIN + (steps + warm + 4) * BLK
+    with torch.cuda.stream(st):
+        ds = synth.DeviceStreams(P, P // 2, D, 1000, dev)
+        bat = K.IsvdBatch(P, D=D, r_max=R, b_max=BLK, n_cap=n_cap, reorth_every_rows=256, device=dev, stream=st,
+                          window=WIN, block=BLK)
+        t0 = time.perf_counter()
+        for s in range(0, n0 + WIN, 512):
+            bat.append(ds.rows(min(512, n0 + WIN - s)), s)
+        st.synchronize()
+        fill_s = time.perf_counter() - t0
+        cursor = n0 + WIN
+        blocks = [ds.rows(BLK) for _ in range(steps + warm)]
+        st.synchronize()
+        for i in range(warm):
+            bat.append(blocks[i], cursor)
+            cursor += BLK
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st.synchronize()
+        t0 = time.perf_counter()
+        e0.record(st)
+        for i in range(warm, warm + steps):
+            bat.append(blocks[i], cursor)
+            cursor += BLK
+        e1.record(st)
+        st.synchronize()
+        wall = time.perf_counter() - t0
+        # stage breakdown of two more batched merges (kernels one by one, events)
+        bat.paths[0].set_timing(True)
+        stage = []
+        for _ in range(2):
+            bat.append(ds.rows(BLK), cursor)
+            cursor += BLK
+            stage.append(bat.paths[0].stage_times())
+        bat.paths[0].set_timing(False)
+    ms = e0.elapsed_time(e1)
+    states = [p.state() for p in bat.paths[:: max(1, P // 4)]]
+    bat.close()
+    return {"paths": P, "rows_per_path": n0, "block": BLK, "rank": R, "steps": steps,
+            "merges_per_s": P * steps / wall, "ms_per_batched_merge": ms / steps,
+            "merges_per_s_events": P * steps / (ms * 1e-3), "fill_s": fill_s,
+            "stage_ms_per_batched_merge": {k: float(np.mean([r[k] for r in stage])) for k in stage[0]},
+            "core_solver_flags_sampled": [c[11] for c in states],
+            "workload": f"{P} independent paths ({P // 2} K, {P // 2} V spectra), n={n0}, D={D}, r={R}, "
+                        f"b={BLK}, w={WIN}, reorth every 256 rows, rows drawn on the device"}
 
 
 def cpu_baseline(Xk, Xv, seconds):
@@ -321,6 +381,8 @@ def main():
         "core_solver_last_merge": [{"flags": c[11], "steps": c[12], "resid_sweeps": c[14], "k": c[1], "n": c[0]}
                                    for c in core],
     }
+    if args.batch_paths > 0:
+        result["many_paths"] = many_path_leg(args, K, torch, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(Xk, Xv, args.cpu_seconds)
     else:

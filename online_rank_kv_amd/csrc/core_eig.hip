@@ -38,7 +38,10 @@
 
 namespace {
 
-constexpr int PCJ_MAXIT = 7;
+#ifndef ISKV_PCJ_MAXIT
+#define ISKV_PCJ_MAXIT 7
+#endif
+constexpr int PCJ_MAXIT = ISKV_PCJ_MAXIT;
 constexpr double PCJ_OMEGA = 0.1;
 constexpr double PCJ_CLIP = 0.2;
 constexpr int CMAX_S = 6;      // largest cluster diagonalised exactly
@@ -48,6 +51,7 @@ constexpr int NPAIR_MAX = 512; // matched pairs per step
 
 constexpr int FLAG_CONV = 1;
 constexpr int FLAG_FALLBACK = 2;
+constexpr int FLAG_COLD = 4;     // the fallback starts from A itself
 
 // ----------------------------------------------------------------------------
 // C = alpha * opA(A) opB(B) + beta * Cin + gamma * I, all m x m (m from
@@ -60,6 +64,7 @@ constexpr int FLAG_FALLBACK = 2;
 // mode 0: skip the launch when (st[ST_PCJ] & FLAG_CONV).
 // mode 1: when converged, copy Cin (the current W) to C instead.
 // mode 2: always run.
+// mode 3: run only when the refinement has not converged.
 typedef double v4d __attribute__((ext_vector_type(4)));
 // Branch-free masking of a loaded value: the bits are ANDed with 0 or
 // all-ones, so the load itself is never placed under a branch and every load
@@ -116,7 +121,7 @@ __global__ __launch_bounds__(256) void dgemm_kernel(const double* __restrict__ A
   const int m = st[ST_JM];
   if (i0 >= m || j0 >= m) return;
   const bool conv = (st[ST_PCJ] & FLAG_CONV) != 0;
-  if (mode == 0 && conv) return;
+  if ((mode == 0 || mode == 3) && conv) return;
   if (mode == 1 && conv) {
     const int i = i0 + (t >> 4), j = j0 + (t & 15);
     if (i < m && j < m) C[(size_t)i * ldc + j] = Cin[(size_t)i * ldcin + j];
@@ -750,15 +755,21 @@ __global__ __launch_bounds__(256) void pcj_kmat_kernel(const double* __restrict_
   }
 }
 
-// Eigenvalues lambda_i = w_i^T (A w_i) from T = A W; V = W when converged,
-// otherwise hand the matrix to the Jacobi fallback (S = A, flag). Grid (m).
+// Eigenvalues lambda_i = w_i^T (A w_i) from T = A W; V = W when converged.
+// Otherwise the Jacobi fallback takes over: when the last step's couplings
+// (aux, nmx maxima) are all finite and below 0.05, it continues from
+// S = Wf^T A Wf (formed by the launch before) and V = Wf, nearly diagonal so
+// that a few sweeps finish it; else it starts from S = A, V = I (FLAG_COLD).
+// Grid (m).
 __global__ __launch_bounds__(256) void pcj_final_kernel(const double* __restrict__ Wf,
                                                         const double* __restrict__ T,
                                                         const double* __restrict__ A, double* S,
-                                                        double* V, int ld, int32_t* st,
+                                                        double* V, int ld, const double* __restrict__ aux,
+                                                        int nmx, int32_t* st,
     const int64_t* __restrict__ bd) {
   const int64_t bdel = bd ? bd[blockIdx.z] : 0;
   Wf = iskv_rb(Wf, bdel);
+  aux = iskv_rb(aux, bdel);
   T = iskv_rb(T, bdel);
   A = iskv_rb(A, bdel);
   S = iskv_rb(S, bdel);
@@ -782,8 +793,19 @@ __global__ __launch_bounds__(256) void pcj_final_kernel(const double* __restrict
     __syncthreads();
     if (threadIdx.x == 0) S[(size_t)j * ld + j] = red[0] + red[1] + red[2] + red[3];
   } else {
-    for (int r = threadIdx.x; r < m; r += 256) S[(size_t)j * ld + r] = A[(size_t)j * ld + r];
-    if (j == 0 && threadIdx.x == 0) st[ST_PCJ] |= FLAG_FALLBACK;
+    double c = 0.0;
+    bool fin = true;
+    for (int b = threadIdx.x; b < nmx; b += 256) {
+      fin = fin && isfinite(aux[b]);
+      c = fmax(c, aux[b]);
+    }
+    const bool warm = __syncthreads_and(fin && c < 0.05) != 0;  // same in every block
+    if (warm) {
+      for (int r = threadIdx.x; r < m; r += 256) V[(size_t)r * ld + j] = Wf[(size_t)r * ld + j];
+    } else {
+      for (int r = threadIdx.x; r < m; r += 256) S[(size_t)j * ld + r] = A[(size_t)j * ld + r];
+    }
+    if (j == 0 && threadIdx.x == 0) st[ST_PCJ] |= FLAG_FALLBACK | (warm ? 0 : FLAG_COLD);
   }
 }
 
@@ -805,7 +827,8 @@ __global__ __launch_bounds__(1024) void core_jacobi_kernel(double* S, double* V,
   __shared__ int active;
   const int n = st[ST_JM];
   const int t = threadIdx.x, nt = blockDim.x;
-  for (int idx = t; idx < n * n; idx += nt) V[(size_t)(idx / n) * ld + idx % n] = (idx / n == idx % n) ? 1.0 : 0.0;
+  if (st[ST_PCJ] & FLAG_COLD)
+    for (int idx = t; idx < n * n; idx += nt) V[(size_t)(idx / n) * ld + idx % n] = (idx / n == idx % n) ? 1.0 : 0.0;
   __syncthreads();
   int sweep = 0;
   if (n >= 2) {
@@ -943,8 +966,10 @@ int iskv_launch_core_eig(isvd_handle* h, double tol) {
                      nullptr, nullptr, 1.0, 0.0, 1.0, 0.0, nullptr, st, 2, h->bd);
   hipLaunchKernelGGL((dgemm2_kernel<false, false>), bz(tiles, h->bcount), dim3(256), 0, s, wo, w.Km, w.T, ld, wc,
                      w.Pa, wo, w.Km, -0.5, 1.5, -0.5, 1.5, nullptr, st, 2, h->bd);
-  hipLaunchKernelGGL(pcj_final_kernel, bz(dim3(mm), h->bcount), dim3(256), 0, s, wc, w.Pa, w.A, w.S, w.V, ld, st,
-                     h->bd);
+  // S = W^T A W of the final W, used only by a fallback that continues from it
+  dgemm<true, false>(s, mm, wc, w.Pa, w.S, nullptr, ld, 1.0, 0.0, 0.0, st, 3, h->bd, h->bcount);
+  hipLaunchKernelGGL(pcj_final_kernel, bz(dim3(mm), h->bcount), dim3(256), 0, s, wc, w.Pa, w.A, w.S, w.V, ld,
+                     w.aux, nblk * nblk, st, h->bd);
   hipLaunchKernelGGL(core_jacobi_kernel, bz(dim3(1), h->bcount), dim3(1024), 0, s, w.S, w.V, ld, st, 1e-13,
                      ISKV_JACOBI_MAX_SWEEPS, h->bd);
   ISKV_HIP_CHECK(hipGetLastError());

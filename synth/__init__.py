@@ -33,6 +33,7 @@ __all__ = [
     "CONFIG_KV_V",
     "protected_prompt_rows",
     "bf16_queries",
+    "DeviceStreams",
 ]
 
 
@@ -138,3 +139,40 @@ def bf16_queries(batch: int, hq: int, dh: int, seed: int) -> np.ndarray:
     lsb = (u >> 16) & 1
     u = (u + 0x7FFF + lsb) >> 16
     return u.astype(np.uint16)
+
+
+class DeviceStreams:
+    """Many independent streams drawn on the GPU (the many-path workload: every
+    (sequence, layer, K/V) path is its own stream).
+
+    Path z < n_k uses the key spectrum (exp(-i/40) + 0.01), the others the
+    value spectrum ((1+i)^-1/2); each kind has one Haar basis drawn on the host
+    as in ``kv_stream`` (seeds ``seed`` and ``seed + 1``), and the coordinates
+    of every path are i.i.d. N(0, 1) from one seeded device generator, drawn
+    block by block in call order. ``rows(c)`` returns the next c rows of every
+    path as a float32 tensor [paths, c, D] on ``device``.
+    """
+
+    def __init__(self, paths: int, n_k: int, D: int, seed: int, device):
+        import torch
+        self.paths, self.n_k, self.D = paths, n_k, D
+        self.device = torch.device(device)
+        bases, sigmas = [], []
+        for kind, sd in (("exp40+0.01", seed), ("invsqrt", seed + 1)):
+            O = haar_orthonormal(np.random.default_rng(sd), D)
+            bases.append(torch.from_numpy(np.ascontiguousarray(O.T)).to(self.device, torch.float32))
+            sigmas.append(torch.from_numpy(spectrum(kind, D)).to(self.device, torch.float32))
+        self.OT, self.sig = bases, sigmas
+        self.gen = torch.Generator(device=self.device)
+        self.gen.manual_seed(seed + 2)
+
+    def rows(self, c: int):
+        import torch
+        z = torch.randn((self.paths, c, self.D), generator=self.gen, device=self.device, dtype=torch.float32)
+        out = torch.empty_like(z)
+        nk = self.n_k
+        if nk > 0:
+            out[:nk] = torch.matmul(z[:nk] * self.sig[0], self.OT[0])
+        if nk < self.paths:
+            out[nk:] = torch.matmul(z[nk:] * self.sig[1], self.OT[1])
+        return out
