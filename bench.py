@@ -95,7 +95,7 @@ def many_path_leg(args, K, torch, dev):
     with torch.cuda.stream(st):
         ds = synth.DeviceStreams(P, P // 2, D, 1000, dev)
         bat = K.IsvdBatch(P, D=D, r_max=R, b_max=BLK, n_cap=n_cap, reorth_every_rows=256, device=dev, stream=st,
-                          window=WIN, block=BLK)
+                          graphs=not args.no_graphs, window=WIN, block=BLK)
         t0 = time.perf_counter()
         for s in range(0, n0 + WIN, 512):
             bat.append(ds.rows(min(512, n0 + WIN - s)), s)

@@ -400,6 +400,343 @@ __global__ __launch_bounds__(256) void dgemm_s_kernel(const double* __restrict__
   if (lane == 0) aux[tile] = cmax;
 }
 
+// ----------------------------------------------------------------------------
+// Large-tile forms of the three fp64 GEMM kernels above, for batched launches
+// over many paths: one workgroup per 96 x 96 output tile (9 per path at
+// m <= 288) instead of one per 16 x 16 tile, so each operand panel is read
+// from L2 six times less often. The depth is staged through LDS in chunks of
+// 16 (double-buffered, one barrier per chunk; the next chunk's global loads
+// are in flight during the current chunk's MFMAs). Wave (wr, wc) of the 2 x 2
+// arrangement owns the 3 x 3 block of 16 x 16 sub-tiles at rows 48 wr and
+// columns 48 wc; its MFMA operands come from LDS laid out k-major (As[k][i],
+// Bs[k][j]) with a row stride of 112 doubles, so the two 16-lane halves of a
+// fragment read fall on opposite halves of the banks. Depth entries >= m are
+// zeroed as they enter LDS. Outputs, skip modes, diagonal partial sums and
+// coupling maxima are those of the 16 x 16 kernels, with the same layouts.
+constexpr int BT = 96;          // output tile edge
+constexpr int BT_LD = 112;      // LDS row stride (doubles)
+constexpr int BT_CH = 16 * BT_LD;  // doubles of one operand chunk in LDS
+
+// Global -> registers for one depth chunk of one operand whose LDS form is
+// X[k][x] = op(M)[x][k] (x in the tile's 96 indices). Transposed in memory
+// (TM: M[k][x] row-major) the 16 rows of 96 are read along x; otherwise
+// M[x][k] rows are read along k (16 values per row).
+template <bool TM>
+__device__ __forceinline__ void bt_load(const double* __restrict__ M, int ld, int x0, int k0, int t, double2 (&r)[3]) {
+#pragma unroll
+  for (int u = 0; u < 3; ++u) {
+    const int e = t + 256 * u;
+    if (TM) {
+      const int kk = e / 48, x2 = e % 48;
+      r[u] = *(const double2*)(M + (size_t)(k0 + kk) * ld + x0 + 2 * x2);
+    } else {
+      const int x = e / 8, kk2 = e % 8;
+      r[u] = *(const double2*)(M + (size_t)(x0 + x) * ld + k0 + 2 * kk2);
+    }
+  }
+}
+
+template <bool TM>
+__device__ __forceinline__ void bt_store(double* X, int k0, int m, int t, const double2 (&r)[3]) {
+#pragma unroll
+  for (int u = 0; u < 3; ++u) {
+    const int e = t + 256 * u;
+    if (TM) {
+      const int kk = e / 48, x2 = e % 48;
+      const bool in = k0 + kk < m;
+      X[kk * BT_LD + 2 * x2] = keep_if(r[u].x, in);
+      X[kk * BT_LD + 2 * x2 + 1] = keep_if(r[u].y, in);
+    } else {
+      const int x = e / 8, kk2 = e % 8;
+      X[(2 * kk2) * BT_LD + x] = keep_if(r[u].x, k0 + 2 * kk2 < m);
+      X[(2 * kk2 + 1) * BT_LD + x] = keep_if(r[u].y, k0 + 2 * kk2 + 1 < m);
+    }
+  }
+}
+
+// 4 k-steps of one chunk: acc[a][b] += As[:, 48 wr + 16 a] Bs[:, 48 wc + 16 b]
+__device__ __forceinline__ void bt_mma(const double* As, const double* Bs, int wr, int wc, int lane,
+                                       v4d (&acc)[3][3]) {
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int k = 4 * q + g;
+    double af[3], bf[3];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) af[a] = As[k * BT_LD + 48 * wr + 16 * a + r];
+#pragma unroll
+    for (int b = 0; b < 3; ++b) bf[b] = Bs[k * BT_LD + 48 * wc + 16 * b + r];
+#pragma unroll
+    for (int a = 0; a < 3; ++a)
+#pragma unroll
+      for (int b = 0; b < 3; ++b) acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[a], bf[b], acc[a][b], 0, 0, 0);
+  }
+}
+
+// Main loop over the depth for one (DUAL: two) left operand(s) and one right
+// operand; lds holds 2 buffers of (1 + DUAL) A chunks and one B chunk.
+template <bool TA1, bool TA2, bool TB, bool DUAL>
+__device__ __forceinline__ void bt_mainloop(const double* A1, const double* A2, const double* B, int ld, int m,
+                                            int i0, int j0, double* lds, v4d (&acc1)[3][3], v4d (&acc2)[3][3]) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  constexpr int NB = DUAL ? 3 : 2;  // chunks per buffer
+  const int nch = (m + 15) / 16;
+  double2 ra1[3], ra2[3], rb[3];
+  bt_load<TA1>(A1, ld, i0, 0, t, ra1);
+  if (DUAL) bt_load<TA2>(A2, ld, i0, 0, t, ra2);
+  bt_load<!TB>(B, ld, j0, 0, t, rb);
+  for (int c = 0; c < nch; ++c) {
+    double* buf = lds + (c & 1) * NB * BT_CH;
+    bt_store<TA1>(buf, 16 * c, m, t, ra1);
+    if (DUAL) bt_store<TA2>(buf + 2 * BT_CH, 16 * c, m, t, ra2);
+    bt_store<!TB>(buf + BT_CH, 16 * c, m, t, rb);
+    __syncthreads();
+    if (c + 1 < nch) {
+      bt_load<TA1>(A1, ld, i0, 16 * (c + 1), t, ra1);
+      if (DUAL) bt_load<TA2>(A2, ld, i0, 16 * (c + 1), t, ra2);
+      bt_load<!TB>(B, ld, j0, 16 * (c + 1), t, rb);
+    }
+    bt_mma(buf, buf + BT_CH, wr, wc, lane, acc1);
+    if (DUAL) bt_mma(buf + 2 * BT_CH, buf + BT_CH, wr, wc, lane, acc2);
+  }
+}
+
+template <bool TA, bool TB>
+__global__ __launch_bounds__(256) void bgemm_kernel(const double* __restrict__ A, const double* __restrict__ B,
+                                                    double* C, const double* Cin, int ld, double alpha, double beta,
+                                                    double gamma, const int32_t* __restrict__ st, int mode,
+                                                    const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  A = iskv_rb(A, bdel);
+  B = iskv_rb(B, bdel);
+  C = iskv_rb(C, bdel);
+  Cin = iskv_rb(Cin, bdel);
+  st = iskv_rb(st, bdel);
+  const int i0 = blockIdx.y * BT, j0 = blockIdx.x * BT;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int m = st[ST_JM];
+  if (i0 >= m || j0 >= m) return;
+  const bool conv = (st[ST_PCJ] & FLAG_CONV) != 0;
+  if ((mode == 0 || mode == 3) && conv) return;
+  if (mode == 1 && conv) {
+    for (int e = t; e < BT * BT; e += 256) {
+      const int i = i0 + e / BT, j = j0 + e % BT;
+      if (i < m && j < m) C[(size_t)i * ld + j] = Cin[(size_t)i * ld + j];
+    }
+    return;
+  }
+  extern __shared__ double bt_lds[];
+  v4d acc[3][3], unused[3][3];
+#pragma unroll
+  for (int a = 0; a < 3; ++a)
+#pragma unroll
+    for (int b = 0; b < 3; ++b) acc[a][b] = v4d{0.0, 0.0, 0.0, 0.0};
+  bt_mainloop<TA, false, TB, false>(A, nullptr, B, ld, m, i0, j0, bt_lds, acc, unused);
+  const int r = lane & 15, g = lane >> 4, wr = wave >> 1, wc = wave & 1;
+#pragma unroll
+  for (int a = 0; a < 3; ++a)
+#pragma unroll
+    for (int b = 0; b < 3; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = i0 + 48 * wr + 16 * a + g + 4 * e, j = j0 + 48 * wc + 16 * b + r;
+        if (i < m && j < m) {
+          double o = alpha * acc[a][b][e];
+          if (beta != 0.0) o += beta * Cin[(size_t)i * ld + j];
+          if (i == j) o += gamma;
+          C[(size_t)i * ld + j] = o;
+        }
+      }
+}
+
+template <bool TA1, bool TA2>
+__global__ __launch_bounds__(256) void bgemm2_kernel(const double* __restrict__ A1, const double* __restrict__ A2,
+                                                     const double* __restrict__ B, int ld, double* C1, double* C2,
+                                                     const double* Cin1, const double* Cin2, double alpha1,
+                                                     double beta1, double alpha2, double beta2, double* Dp,
+                                                     const int32_t* __restrict__ st, int mode,
+                                                     const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  A1 = iskv_rb(A1, bdel);
+  A2 = iskv_rb(A2, bdel);
+  B = iskv_rb(B, bdel);
+  C1 = iskv_rb(C1, bdel);
+  C2 = iskv_rb(C2, bdel);
+  Cin1 = iskv_rb(Cin1, bdel);
+  Cin2 = iskv_rb(Cin2, bdel);
+  Dp = iskv_rb(Dp, bdel);
+  st = iskv_rb(st, bdel);
+  const int i0 = blockIdx.y * BT, j0 = blockIdx.x * BT;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int m = st[ST_JM];
+  if (i0 >= m || j0 >= m) return;
+  const bool conv = (st[ST_PCJ] & FLAG_CONV) != 0;
+  if (mode == 0 && conv) return;
+  if (mode == 1 && conv) {
+    for (int e = t; e < BT * BT; e += 256) {
+      const int i = i0 + e / BT, j = j0 + e % BT;
+      if (i < m && j < m) {
+        C1[(size_t)i * ld + j] = Cin1[(size_t)i * ld + j];
+        C2[(size_t)i * ld + j] = Cin2[(size_t)i * ld + j];
+      }
+    }
+    return;
+  }
+  extern __shared__ double bt_lds[];
+  v4d acc1[3][3], acc2[3][3];
+#pragma unroll
+  for (int a = 0; a < 3; ++a)
+#pragma unroll
+    for (int b = 0; b < 3; ++b) acc1[a][b] = acc2[a][b] = v4d{0.0, 0.0, 0.0, 0.0};
+  bt_mainloop<TA1, TA2, false, true>(A1, A2, B, ld, m, i0, j0, bt_lds, acc1, acc2);
+  const int r = lane & 15, g = lane >> 4, wr = wave >> 1, wc = wave & 1;
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    const int ib = i0 + 48 * wr + 16 * a;  // first row of the sub-tile
+#pragma unroll
+    for (int b = 0; b < 3; ++b) {
+      const int j = j0 + 48 * wc + 16 * b + r;
+      double dsum = 0.0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = ib + g + 4 * e;
+        if (i < m && j < m) {
+          double o1 = alpha1 * acc1[a][b][e], o2 = alpha2 * acc2[a][b][e];
+          if (beta1 != 0.0) o1 += beta1 * Cin1[(size_t)i * ld + j];
+          if (beta2 != 0.0) o2 += beta2 * Cin2[(size_t)i * ld + j];
+          C1[(size_t)i * ld + j] = o1;
+          C2[(size_t)i * ld + j] = o2;
+          dsum = fma(o1, o2, dsum);
+        }
+      }
+      if (Dp) {
+        dsum += __shfl_xor(dsum, 16, 64);
+        dsum += __shfl_xor(dsum, 32, 64);
+        if (g == 0 && ib < m) Dp[(size_t)(ib / 16) * ld + j] = dsum;
+      }
+    }
+  }
+}
+
+// S = W^T T with the strong-pair detection (as dgemm_s_kernel); the coupling
+// maximum of 16 x 16 sub-tile (I, J) goes to aux[I nblk + J].
+__global__ __launch_bounds__(256) void bgemm_s_kernel(const double* __restrict__ W, const double* __restrict__ T,
+                                                      int ld, double* S, const double* __restrict__ Dp,
+                                                      double* aux, int nblk, int* edges, int32_t* st, double tol,
+                                                      const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  W = iskv_rb(W, bdel);
+  T = iskv_rb(T, bdel);
+  S = iskv_rb(S, bdel);
+  Dp = iskv_rb(Dp, bdel);
+  aux = iskv_rb(aux, bdel);
+  edges = iskv_rb(edges, bdel);
+  st = iskv_rb(st, bdel);
+  const int i0 = blockIdx.y * BT, j0 = blockIdx.x * BT;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int r = lane & 15, g = lane >> 4, wr = wave >> 1, wc = wave & 1;
+  const int m = st[ST_JM];
+  const bool conv = (st[ST_PCJ] & FLAG_CONV) != 0;
+  if (i0 >= m || j0 >= m || conv) {
+    // every sub-tile maximum of this tile is 0
+    if (t < 36) {
+      const int I = i0 / 16 + t / 6, J = j0 / 16 + t % 6;
+      if (I < nblk && J < nblk) aux[I * nblk + J] = 0.0;
+    }
+    return;
+  }
+  extern __shared__ double bt_lds[];
+  v4d acc[3][3], unused[3][3];
+#pragma unroll
+  for (int a = 0; a < 3; ++a)
+#pragma unroll
+    for (int b = 0; b < 3; ++b) acc[a][b] = v4d{0.0, 0.0, 0.0, 0.0};
+  bt_mainloop<true, false, false, false>(W, nullptr, T, ld, m, i0, j0, bt_lds, acc, unused);
+  const int nrb = (m + 15) / 16;
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    const int ib = i0 + 48 * wr + 16 * a;
+    double di = 0.0;
+    for (int b2 = 0; b2 < nrb; ++b2) di += Dp[(size_t)b2 * ld + ib + r];
+#pragma unroll
+    for (int b = 0; b < 3; ++b) {
+      const int jb = j0 + 48 * wc + 16 * b, j = jb + r;
+      double dj = 0.0;
+      for (int b2 = 0; b2 < nrb; ++b2) dj += Dp[(size_t)b2 * ld + j];
+      double cmax = 0.0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = ib + g + 4 * e;
+        const double dii = __shfl(di, g + 4 * e, 64);
+        if (i < m && j < m) {
+          const double o = acc[a][b][e];
+          S[(size_t)i * ld + j] = o;
+          if (j > i) {
+            const double c = coupling(o, dii, dj);
+            cmax = fmax(cmax, c);
+            if (c > tol && fabs(o) > PCJ_OMEGA * fabs(dj - dii)) {
+              const int slot = atomicAdd(&st[ST_NEDGE], 1);
+              if (slot < EMAX) { edges[2 * slot] = i; edges[2 * slot + 1] = j; }
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) cmax = fmax(cmax, __shfl_xor(cmax, o, 64));
+      if (lane == 0 && ib / 16 < nblk && jb / 16 < nblk) aux[(ib / 16) * nblk + jb / 16] = cmax;
+    }
+  }
+}
+
+static inline size_t bt_lds_bytes(bool dual) { return (size_t)2 * (dual ? 3 : 2) * BT_CH * sizeof(double); }
+
+// Batched launches over at least this many paths use the 96 x 96 tiles.
+constexpr int BT_MIN_BATCH = 16;
+
+// C = alpha op(A) op(B) + beta Cin + gamma I, tile size chosen by batch size.
+template <bool TA, bool TB>
+void gemm(hipStream_t s, int m_max, const double* A, const double* B, double* C, const double* Cin, int ld,
+          double alpha, double beta, double gamma, const int32_t* st, int mode, const int64_t* bd, int bc) {
+  if (bc >= BT_MIN_BATCH) {
+    const int nt = (m_max + BT - 1) / BT;
+    hipLaunchKernelGGL((bgemm_kernel<TA, TB>), bz(dim3(nt, nt), bc), dim3(256), bt_lds_bytes(false), s, A, B, C,
+                       Cin, ld, alpha, beta, gamma, st, mode, bd);
+  } else {
+    dgemm<TA, TB>(s, m_max, A, B, C, Cin, ld, alpha, beta, gamma, st, mode, bd, bc);
+  }
+}
+
+// C1 = alpha1 op(A1) B + beta1 Cin1, C2 = alpha2 op(A2) B + beta2 Cin2 (+ Dp).
+template <bool TA1, bool TA2>
+void gemm2(hipStream_t s, int m_max, const double* A1, const double* A2, const double* B, int ld, double* C1,
+           double* C2, const double* Cin1, const double* Cin2, double alpha1, double beta1, double alpha2,
+           double beta2, double* Dp, const int32_t* st, int mode, const int64_t* bd, int bc) {
+  if (bc >= BT_MIN_BATCH) {
+    const int nt = (m_max + BT - 1) / BT;
+    hipLaunchKernelGGL((bgemm2_kernel<TA1, TA2>), bz(dim3(nt, nt), bc), dim3(256), bt_lds_bytes(true), s, A1, A2,
+                       B, ld, C1, C2, Cin1, Cin2, alpha1, beta1, alpha2, beta2, Dp, st, mode, bd);
+  } else {
+    const int nb = (m_max + 15) / 16;
+    hipLaunchKernelGGL((dgemm2_kernel<TA1, TA2>), bz(dim3(nb, nb), bc), dim3(256), 0, s, A1, A2, B, ld, C1, C2,
+                       Cin1, Cin2, alpha1, beta1, alpha2, beta2, Dp, st, mode, bd);
+  }
+}
+
+// S = W^T T with strong-pair detection (aux: nblk x nblk maxima).
+void gemm_s(hipStream_t s, int m_max, const double* W, const double* T, int ld, double* S, const double* Dp,
+            double* aux, int* edges, int32_t* st, double tol, const int64_t* bd, int bc) {
+  const int nb = (m_max + 15) / 16;
+  if (bc >= BT_MIN_BATCH) {
+    const int nt = (m_max + BT - 1) / BT;
+    hipLaunchKernelGGL(bgemm_s_kernel, bz(dim3(nt, nt), bc), dim3(256), bt_lds_bytes(false), s, W, T, ld, S, Dp,
+                       aux, nb, edges, st, tol, bd);
+  } else {
+    hipLaunchKernelGGL(dgemm_s_kernel, bz(dim3(nb, nb), bc), dim3(256), 0, s, W, T, ld, S, Dp, aux, edges, st, tol,
+                       bd);
+  }
+}
+
 // S = A, W = I, flags cleared.
 __global__ __launch_bounds__(256) void pcj_init_kernel(const double* __restrict__ A, double* S,
                                                        double* W, int ld, int32_t* st,
@@ -903,13 +1240,17 @@ __global__ __launch_bounds__(1024) void core_jacobi_kernel(double* S, double* V,
 void iskv_dgemm(hipStream_t s, int m_max, const double* A, bool ta, const double* B, bool tb, double* C,
                 const double* Cin, int ld, double alpha, double beta, double gamma, const int32_t* st,
                 int mode, const int64_t* bd, int bc) {
-  if (!ta && !tb) dgemm<false, false>(s, m_max, A, B, C, Cin, ld, alpha, beta, gamma, st, mode, bd, bc);
-  else if (ta && !tb) dgemm<true, false>(s, m_max, A, B, C, Cin, ld, alpha, beta, gamma, st, mode, bd, bc);
-  else if (!ta && tb) dgemm<false, true>(s, m_max, A, B, C, Cin, ld, alpha, beta, gamma, st, mode, bd, bc);
-  else dgemm<true, true>(s, m_max, A, B, C, Cin, ld, alpha, beta, gamma, st, mode, bd, bc);
+  if (!ta && !tb) gemm<false, false>(s, m_max, A, B, C, Cin, ld, alpha, beta, gamma, st, mode, bd, bc);
+  else if (ta && !tb) gemm<true, false>(s, m_max, A, B, C, Cin, ld, alpha, beta, gamma, st, mode, bd, bc);
+  else if (!ta && tb) gemm<false, true>(s, m_max, A, B, C, Cin, ld, alpha, beta, gamma, st, mode, bd, bc);
+  else gemm<true, true>(s, m_max, A, B, C, Cin, ld, alpha, beta, gamma, st, mode, bd, bc);
 }
 
 int iskv_core_eig_setup() {
+  ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)bgemm2_kernel<true, true>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bt_lds_bytes(true)));
+  ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)bgemm2_kernel<false, false>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bt_lds_bytes(true)));
   ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)pcj_analyze_kernel,
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)sizeof(AnalyzeLds)));
@@ -925,7 +1266,6 @@ int iskv_launch_core_eig(isvd_handle* h, double tol) {
   const int mm = h->m_max, ld = h->ldm;
   int32_t* st = w.st;
   const int nblk = (mm + 15) / 16;
-  const dim3 tiles(nblk, nblk);
   const size_t lds = sizeof(AnalyzeLds);
   hipLaunchKernelGGL(pcj_init_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.A, w.S, w.W0, ld, st, h->bd);
   // step 0 works on S = A with W = I
@@ -935,8 +1275,8 @@ int iskv_launch_core_eig(isvd_handle* h, double tol) {
                      w.edges, st, 0, tol, h->bd);
   hipLaunchKernelGGL(pcj_kmat_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.S, ld, w.Km, w.Pa, st, h->bd);
   // X = I + K (I + K/2); W <- W X
-  dgemm<false, false>(s, mm, w.Km, w.Pa, w.Pb, nullptr, ld, 1.0, 0.0, 1.0, st, 0, h->bd, h->bcount);
-  dgemm<false, false>(s, mm, w.W0, w.Pb, w.W1, w.W0, ld, 1.0, 0.0, 0.0, st, 1, h->bd, h->bcount);
+  gemm<false, false>(s, mm, w.Km, w.Pa, w.Pb, nullptr, ld, 1.0, 0.0, 1.0, st, 0, h->bd, h->bcount);
+  gemm<false, false>(s, mm, w.W0, w.Pb, w.W1, w.W0, ld, 1.0, 0.0, 0.0, st, 1, h->bd, h->bcount);
   // From step 1 on, W sits in `wc` at the start of a step and its
   // re-orthonormalised form W' in `wo`; after convergence `wo` keeps the final
   // W (the launches that would change it are skipped).
@@ -944,30 +1284,29 @@ int iskv_launch_core_eig(isvd_handle* h, double tol) {
   double* wo = w.W0;
   for (int it = 1; it <= PCJ_MAXIT; ++it) {
     // T1 = W^T W and T2 = A W (A symmetric: read as A^T)
-    hipLaunchKernelGGL((dgemm2_kernel<true, true>), bz(tiles, h->bcount), dim3(256), 0, s, wc, w.A, wc, ld, w.T,
-                       w.Km, nullptr, nullptr, 1.0, 0.0, 1.0, 0.0, nullptr, st, 0, h->bd);
+    gemm2<true, true>(s, mm, wc, w.A, wc, ld, w.T, w.Km, nullptr, nullptr, 1.0, 0.0, 1.0, 0.0, nullptr, st, 0, h->bd,
+                      h->bcount);
     // Newton-Schulz W' = 1.5 W - 0.5 W T1, and A W' = 1.5 T2 - 0.5 T2 T1 (keeps W
     // orthonormal to O(defect^2), so S is measured in an orthonormal basis);
     // partial sums of diag(W'^T A W')
-    hipLaunchKernelGGL((dgemm2_kernel<false, false>), bz(tiles, h->bcount), dim3(256), 0, s, wc, w.Km, w.T, ld, wo,
-                       w.Pa, wc, w.Km, -0.5, 1.5, -0.5, 1.5, w.Dp, st, 0, h->bd);
+    gemm2<false, false>(s, mm, wc, w.Km, w.T, ld, wo, w.Pa, wc, w.Km, -0.5, 1.5, -0.5, 1.5, w.Dp, st, 0, h->bd,
+                        h->bcount);
     // S = W'^T (A W') with the strong-pair detection
-    hipLaunchKernelGGL(dgemm_s_kernel, bz(tiles, h->bcount), dim3(256), 0, s, wo, w.Pa, ld, w.S, w.Dp, w.aux,
-                       w.edges, st, tol, h->bd);
+    gemm_s(s, mm, wo, w.Pa, ld, w.S, w.Dp, w.aux, w.edges, st, tol, h->bd, h->bcount);
     hipLaunchKernelGGL(pcj_analyze_kernel, bz(dim3(1), h->bcount), dim3(1024), lds, s, w.S, wo, ld, w.aux,
                        nblk * nblk, w.edges, st, it, tol, h->bd);
     if (it == PCJ_MAXIT) break;  // last pass only tests convergence
     hipLaunchKernelGGL(pcj_kmat_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.S, ld, w.Km, w.Pa, st, h->bd);
-    dgemm<false, false>(s, mm, w.Km, w.Pa, w.Pb, nullptr, ld, 1.0, 0.0, 1.0, st, 0, h->bd, h->bcount);
-    dgemm<false, false>(s, mm, wo, w.Pb, wc, wo, ld, 1.0, 0.0, 0.0, st, 1, h->bd, h->bcount);
+    gemm<false, false>(s, mm, w.Km, w.Pa, w.Pb, nullptr, ld, 1.0, 0.0, 1.0, st, 0, h->bd, h->bcount);
+    gemm<false, false>(s, mm, wo, w.Pb, wc, wo, ld, 1.0, 0.0, 0.0, st, 1, h->bd, h->bcount);
   }
   // final Newton-Schulz of W (in wo) into wc, with A W for the eigenvalues
-  hipLaunchKernelGGL((dgemm2_kernel<true, true>), bz(tiles, h->bcount), dim3(256), 0, s, wo, w.A, wo, ld, w.T, w.Km,
-                     nullptr, nullptr, 1.0, 0.0, 1.0, 0.0, nullptr, st, 2, h->bd);
-  hipLaunchKernelGGL((dgemm2_kernel<false, false>), bz(tiles, h->bcount), dim3(256), 0, s, wo, w.Km, w.T, ld, wc,
-                     w.Pa, wo, w.Km, -0.5, 1.5, -0.5, 1.5, nullptr, st, 2, h->bd);
+  gemm2<true, true>(s, mm, wo, w.A, wo, ld, w.T, w.Km, nullptr, nullptr, 1.0, 0.0, 1.0, 0.0, nullptr, st, 2, h->bd,
+                    h->bcount);
+  gemm2<false, false>(s, mm, wo, w.Km, w.T, ld, wc, w.Pa, wo, w.Km, -0.5, 1.5, -0.5, 1.5, nullptr, st, 2, h->bd,
+                      h->bcount);
   // S = W^T A W of the final W, used only by a fallback that continues from it
-  dgemm<true, false>(s, mm, wc, w.Pa, w.S, nullptr, ld, 1.0, 0.0, 0.0, st, 3, h->bd, h->bcount);
+  gemm<true, false>(s, mm, wc, w.Pa, w.S, nullptr, ld, 1.0, 0.0, 0.0, st, 3, h->bd, h->bcount);
   hipLaunchKernelGGL(pcj_final_kernel, bz(dim3(mm), h->bcount), dim3(256), 0, s, wc, w.Pa, w.A, w.S, w.V, ld,
                      w.aux, nblk * nblk, st, h->bd);
   hipLaunchKernelGGL(core_jacobi_kernel, bz(dim3(1), h->bcount), dim3(1024), 0, s, w.S, w.V, ld, st, 1e-13,

@@ -330,6 +330,40 @@ def test_stage_timing_matches_plain_merges(K):
     b.close()
 
 
+def test_large_batch_matches_separate(K):
+    """16 paths batched (the launch form that switches the core eigensolver's
+    GEMMs to 96 x 96 tiles) with a core of 128 = 2 x 2 large tiles, partly
+    filled: every path equals its separate, small-tile merges."""
+    cnt, D, r, b, T, n = 16, 256, 96, 32, 128, 384
+    Xs = [synth.kv_stream(synth.StreamSpec(D=D, n=n, spectrum="exp40+0.01" if z % 2 == 0 else "invsqrt",
+                                           noise_std=0.0, seed=40 + z)) for z in range(cnt)]
+    Xd = torch.from_numpy(np.stack(Xs)).to(DEV)
+    posd = torch.arange(n, dtype=torch.int32, device=DEV).repeat(cnt, 1).contiguous()
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    bat = K.IsvdBatch(cnt, D=D, r_max=r, b_max=b, n_cap=n, reorth_every_rows=T, device=DEV, stream=stream)
+    for s in range(0, n, b):
+        bat.merge(Xd[:, s:s + b], posd[:, s:s + b])
+    stream.synchronize()
+    for z in (0, 5, 10, 15):
+        sep = K.IsvdPath(D=D, r_max=r, b_max=b, n_cap=n, reorth_every_rows=T, device=DEV, graphs=False)
+        for s in range(0, n, b):
+            sep.merge(Xd[z, s:s + b], posd[z, s:s + b])
+        torch.cuda.synchronize()
+        Cb, Bb, sb, _, stb = gpu_factors(bat[z])
+        Cs, Bs, ss, _, sts = gpu_factors(sep)
+        assert stb == 0 and sts == 0 and Cb.shape == Cs.shape
+        err = rel(Cb @ Bb.T, Cs @ Bs.T)
+        assert err < 1e-6, (z, err)
+        assert np.allclose(sb, ss, rtol=1e-6)
+        assert np.abs(Bb.T @ Bb - np.eye(Bb.shape[1])).max() < 1e-4
+        sep.close()
+    ref = O.represented(O.run_stream(Xs[3], b, r, reorth_every_rows=T))
+    C3, B3, _, _, _ = gpu_factors(bat[3])
+    assert rel(C3 @ B3.T, ref) < 1e-3
+    bat.close()
+
+
 def test_batched_merge_rejects_bad_sets(K):
     """Handles of separate allocations (no common offset), repeated handles and
     a capacity overflow are refused before anything runs."""
