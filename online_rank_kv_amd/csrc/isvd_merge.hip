@@ -508,11 +508,22 @@ __global__ __launch_bounds__(256) void core_gram_kernel(const float* __restrict_
   const int i = blockIdx.y * 16 + (threadIdx.x >> 4);
   const int j = blockIdx.x * 16 + (threadIdx.x & 15);
   if (i >= m || j >= m) return;
+  // column i (j) of M = [Q[:, :k], FP[:, :p]]: base and row stride
+  const float* pi = i < k ? Q + i : FP + (i - k);
+  const float* pj = j < k ? Q + j : FP + (j - k);
+  const int si = i < k ? ldq : ldfp, sj = j < k ? ldq : ldfp;
   double acc = 0.0;
-  for (int r = 0; r < b; ++r) {
-    float mi = i < k ? Q[r * ldq + i] : FP[r * ldfp + (i - k)];
-    float mj = j < k ? Q[r * ldq + j] : FP[r * ldfp + (j - k)];
-    acc = fma((double)mi, (double)mj, acc);
+  for (int r0 = 0; r0 < b; r0 += 8) {  // 8 rows' loads in flight before their products
+    float mi[8], mj[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = min(r0 + u, b - 1);
+      mi[u] = pi[(size_t)r * si];
+      mj[u] = pj[(size_t)r * sj];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (r0 + u < b) acc = fma((double)mi[u], (double)mj[u], acc);
   }
   if (i == j && i < k) acc += (double)sigma[i] * (double)sigma[i];
   A[(size_t)i * lda + j] = acc;
@@ -538,6 +549,7 @@ __global__ __launch_bounds__(1024) void eig_order_kernel(const double* __restric
   for (int i = t; i < n; i += blockDim.x) {
     int rnk = 0;
     const double ki = rank_key(lam[i]);
+#pragma unroll 16
     for (int j = 0; j < n; ++j) {
       const double kj = rank_key(lam[j]);
       rnk += (kj > ki) || (kj == ki && j < i);
@@ -1011,18 +1023,21 @@ __global__ __launch_bounds__(256) void store_sym_kernel(const double* __restrict
 // Skinny products on fp32 MFMA (v_mfma_f32_16x16x4f32), one launch each:
 //   out[i, j] = alpha * sum_k X[i, k] Y'(k, j) + beta * Z[i, j],  i < M (<= 64),
 //   Y'(k, j) = TY ? Y[j, k] : Y[k, j].
-// A workgroup owns one 16 x 16 output block; its 4 waves split K in chunks
-// of 16 (wave w takes chunks w, w+4, ...) and the partial blocks are summed
-// through LDS. Inside a chunk, lane l (row or column l%16, group g = l/16)
-// takes depths 16 s + 4 g + q for MFMA step q: the summation order over k is
-// permuted so that each lane's four operands are consecutive in memory.
-// Depths >= K, rows >= M and columns >= N are masked or dropped.
-template <bool TY>
-__global__ __launch_bounds__(256) void skinny_mfma_kernel(const float* __restrict__ X, int ldx,
-                                                          const float* __restrict__ Y, int ldy, int M,
-                                                          int Nmax, Dim Nd, Dim Kd, float alpha,
-                                                          float beta, const float* Z, int ldz,
-                                                          float* out, int ldo,
+// A workgroup of NW waves owns one 16 x 16 output block; wave w takes the
+// depth chunks of 16 at w, w + NW, ... and issues the loads of up to SK_CPW
+// chunks before their MFMAs, so a wave waits for memory about once per
+// NW * SK_CPW chunks (the whole depth at the merge shapes); the partial
+// blocks are summed through LDS. Inside a chunk, lane l (row or column l%16,
+// group g = l/16) takes depths 16 s + 4 g + q for MFMA step q: the summation
+// order over k is permuted so that each lane's four operands are consecutive
+// in memory. Depths >= K, rows >= M and columns >= N are masked or dropped.
+constexpr int SK_CPW = 4;
+template <bool TY, int NW>
+__global__ __launch_bounds__(64 * NW) void skinny_mfma_kernel(const float* __restrict__ X, int ldx,
+                                                               const float* __restrict__ Y, int ldy, int M,
+                                                               int Nmax, Dim Nd, Dim Kd, float alpha,
+                                                               float beta, const float* Z, int ldz,
+                                                               float* out, int ldo,
     const int64_t* __restrict__ bd) {
   const int64_t bdel = bd ? bd[blockIdx.z] : 0;
   X = iskv_rb(X, bdel);
@@ -1040,22 +1055,26 @@ __global__ __launch_bounds__(256) void skinny_mfma_kernel(const float* __restric
   const float* xr = X + (size_t)row * ldx;
   v4f_t acc = {0.f, 0.f, 0.f, 0.f};
   const int nch = (K + 15) / 16;
-#pragma unroll 2
-  for (int c = wave; c < nch; c += 4) {
-    const int kb = c * 16 + 4 * g;
-    float av[4], bv[4];
+  for (int c0 = wave; c0 < nch; c0 += NW * SK_CPW) {
+    float av[SK_CPW][4], bv[SK_CPW][4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int k = kb + q, kc = min(k, K - 1);
-      const float a = xr[kc];
-      const float bb = TY ? Y[(size_t)col * ldy + kc] : Y[(size_t)kc * ldy + col];
-      av[q] = k < K ? a : 0.f;
-      bv[q] = k < K ? bb : 0.f;
+    for (int u = 0; u < SK_CPW; ++u) {
+      const int kb = (c0 + NW * u) * 16 + 4 * g;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int k = kb + q, kc = min(k, K - 1);
+        const float a = xr[kc];
+        const float bb = TY ? Y[(size_t)col * ldy + kc] : Y[(size_t)kc * ldy + col];
+        av[u][q] = k < K ? a : 0.f;
+        bv[u][q] = k < K ? bb : 0.f;
+      }
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], bv[q], acc, 0, 0, 0);
+    for (int u = 0; u < SK_CPW; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u][q], bv[u][q], acc, 0, 0, 0);
   }
-  __shared__ float red[3][4][64];
+  __shared__ float red[NW - 1][4][64];
   if (wave > 0) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) red[wave - 1][e][lane] = acc[e];
@@ -1065,7 +1084,9 @@ __global__ __launch_bounds__(256) void skinny_mfma_kernel(const float* __restric
   // result lane l, element e: row 4(l/16) + e, column l%16
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const float v = acc[e] + red[0][e][lane] + red[1][e][lane] + red[2][e][lane];
+    float v = acc[e];
+#pragma unroll
+    for (int w = 0; w < NW - 1; ++w) v += red[w][e][lane];
     const int i = i0 + 4 * g + e, j = j0 + r;
     if (i < M && j < N) {
       float o = alpha * v;
@@ -1075,14 +1096,20 @@ __global__ __launch_bounds__(256) void skinny_mfma_kernel(const float* __restric
   }
 }
 
+// Waves per workgroup: enough that the whole depth (Kmax) is in flight at once.
 template <bool TY>
 static void skinny(isvd_handle* h, int M, int Nmax, const float* X, int ldx, const float* Y, int ldy,
                    Dim N, int Kmax, float alpha, float beta, const float* Z, int ldz, float* out,
                    int ldo) {
   Dim K = TY ? ddim(h->w.st + ST_K) : hdim(Kmax);
   dim3 grid((Nmax + 15) / 16, (M + 15) / 16);
-  hipLaunchKernelGGL((skinny_mfma_kernel<TY>), bz(grid, h->bcount), dim3(256), 0, h->stream, X, ldx, Y, ldy, M, Nmax, N,
-                     K, alpha, beta, Z, ldz, out, ldo, h->bd);
+  const int nch = (Kmax + 15) / 16;
+  if (nch > 4 * SK_CPW)
+    hipLaunchKernelGGL((skinny_mfma_kernel<TY, 16>), bz(grid, h->bcount), dim3(1024), 0, h->stream, X, ldx, Y, ldy,
+                       M, Nmax, N, K, alpha, beta, Z, ldz, out, ldo, h->bd);
+  else
+    hipLaunchKernelGGL((skinny_mfma_kernel<TY, 4>), bz(grid, h->bcount), dim3(256), 0, h->stream, X, ldx, Y, ldy,
+                       M, Nmax, N, K, alpha, beta, Z, ldz, out, ldo, h->bd);
 }
 
 static void eig_finish(isvd_handle* h, int for_merge) {
