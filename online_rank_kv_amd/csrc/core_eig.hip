@@ -303,11 +303,13 @@ __global__ __launch_bounds__(256) void dgemm2_kernel(const double* __restrict__ 
 }
 
 // S = W^T T (one 16 x 16 tile per workgroup, as dgemm_kernel<true, false>)
-// with the strong-pair detection of the refinement in its epilogue: the
-// diagonal of S comes from the row-block partial sums Dp of the launch that
-// formed W and T (ceil(m / 16) blocks), every pair i < j of the tile gets its scaled
-// coupling, strong pairs are appended to the edge list and the tile's
-// largest coupling goes to aux[tile] (0 for tiles outside m x m or after
+// with the strong-pair detection of the refinement in its epilogue. S is
+// symmetric, so only tiles on or above the diagonal are computed; each value
+// is written to both (i, j) and (j, i). The diagonal of S comes from the
+// row-block partial sums Dp of the launch that formed W and T (ceil(m / 16)
+// blocks), every pair i < j of the tile gets its scaled coupling, strong
+// pairs are appended to the edge list and the tile's largest coupling goes
+// to aux[tile] (0 for tiles below the diagonal or outside m x m, and after
 // convergence, so the maxima never carry values of an earlier step).
 __global__ __launch_bounds__(256) void dgemm_s_kernel(const double* __restrict__ W, const double* __restrict__ T,
                                                       int ld, double* S, const double* __restrict__ Dp,
@@ -327,7 +329,8 @@ __global__ __launch_bounds__(256) void dgemm_s_kernel(const double* __restrict__
   const int r = lane & 15, g = lane >> 4;
   const int m = st[ST_JM];
   const bool conv = (st[ST_PCJ] & FLAG_CONV) != 0;
-  if (i0 >= m || j0 >= m || conv) {
+  // S is symmetric: tiles below the diagonal are written by their mirror
+  if (i0 >= m || j0 >= m || conv || j0 < i0) {
     if (t == 0) aux[tile] = 0.0;
     return;
   }
@@ -382,9 +385,10 @@ __global__ __launch_bounds__(256) void dgemm_s_kernel(const double* __restrict__
   for (int e = 0; e < 4; ++e) {
     const int i = i0 + g + 4 * e;
     const double dii = __shfl(di, g + 4 * e, 64);
-    if (i < m && j < m) {
+    if (i < m && j < m && j >= i) {
       const double o = acc[e] + red[0][e][lane] + red[1][e][lane] + red[2][e][lane];
       S[(size_t)i * ld + j] = o;
+      S[(size_t)j * ld + i] = o;  // the mirror (the same value: S exactly symmetric)
       if (j > i) {
         const double c = coupling(o, dii, dj);
         cmax = fmax(cmax, c);
@@ -638,7 +642,8 @@ __global__ __launch_bounds__(256) void bgemm_s_kernel(const double* __restrict__
   const int r = lane & 15, g = lane >> 4, wr = wave >> 1, wc = wave & 1;
   const int m = st[ST_JM];
   const bool conv = (st[ST_PCJ] & FLAG_CONV) != 0;
-  if (i0 >= m || j0 >= m || conv) {
+  // S is symmetric: tiles below the diagonal are written by their mirror
+  if (i0 >= m || j0 >= m || conv || j0 < i0) {
     // every sub-tile maximum of this tile is 0
     if (t < 36) {
       const int I = i0 / 16 + t / 6, J = j0 / 16 + t % 6;
@@ -669,9 +674,10 @@ __global__ __launch_bounds__(256) void bgemm_s_kernel(const double* __restrict__
       for (int e = 0; e < 4; ++e) {
         const int i = ib + g + 4 * e;
         const double dii = __shfl(di, g + 4 * e, 64);
-        if (i < m && j < m) {
+        if (i < m && j < m && j >= i) {
           const double o = acc[a][b][e];
           S[(size_t)i * ld + j] = o;
+          S[(size_t)j * ld + i] = o;
           if (j > i) {
             const double c = coupling(o, dii, dj);
             cmax = fmax(cmax, c);
@@ -885,7 +891,6 @@ __global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W,
       L.ncl = 0; L.npair = 0; L.anybig = 0;
     }
   }
-  for (int i = t; i < m; i += nt) L.d[i] = S[(size_t)i * ld + i];
   __syncthreads();
   const double cmax = L.cmax;
   if (cmax < tol) {  // NaN couplings never pass: they end in the fallback
@@ -894,6 +899,11 @@ __global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W,
     return;
   }
   const int ne = L.nedge;
+  if (ne == 0) {  // no strongly coupled pair: the first-order angles do everything
+    if (t == 0) { st[ST_NEDGE] = 0; st[ST_PCJIT] = it + 1; }
+    return;
+  }
+  for (int i = t; i < m; i += nt) L.d[i] = S[(size_t)i * ld + i];
   for (int e = t; e < ne; e += nt) L.key[e] = edges[2 * e] * 1024 + edges[2 * e + 1];
   for (int i = t; i < m; i += nt) { L.lab[i] = i; L.size[i] = 0; L.used[i] = 0; L.cid[i] = -1; }
   __syncthreads();
