@@ -86,7 +86,8 @@ __device__ __forceinline__ double keep_if(double v, bool keep) {
 // m_max rounded up to 16, so every index of a 16-chunk that starts below m
 // lies in the allocation: entries with depth >= m are zeroed, rows and
 // columns >= m of a tile that starts below m are computed and dropped.
-constexpr int DG_CH = 5;  // chunks per wave kept in flight (m <= 320 in one pass)
+constexpr int DG_CH = 5;   // chunks per wave kept in flight (m <= 320 in one pass)
+constexpr int DG2_NW = 4;  // waves of the paired GEMM (a depth split 8 ways measured slower)
 
 template <bool TA, bool TB>
 __global__ __launch_bounds__(256) void dgemm_kernel(const double* __restrict__ A, int lda,
@@ -199,8 +200,8 @@ __device__ __forceinline__ double coupling(double sij, double di, double dj) {
 // column j of its tile, the partial sum over its 16 rows of C1[i][j] C2[i][j]
 // to Dp[blockIdx.y][j]; summed over the row blocks this is the diagonal of
 // C1^T C2.
-template <bool TA1, bool TA2>
-__global__ __launch_bounds__(256) void dgemm2_kernel(const double* __restrict__ A1, const double* __restrict__ A2,
+template <bool TA1, bool TA2, int NW>
+__global__ __launch_bounds__(64 * NW) void dgemm2_kernel(const double* __restrict__ A1, const double* __restrict__ A2,
                                                      const double* __restrict__ B, int ld, double* C1, double* C2,
                                                      const double* Cin1, const double* Cin2, double alpha1,
                                                      double beta1, double alpha2, double beta2, double* Dp,
@@ -224,10 +225,12 @@ __global__ __launch_bounds__(256) void dgemm2_kernel(const double* __restrict__ 
   const bool conv = (st[ST_PCJ] & FLAG_CONV) != 0;
   if (mode == 0 && conv) return;
   if (mode == 1 && conv) {
-    const int i = i0 + (t >> 4), j = j0 + (t & 15);
-    if (i < m && j < m) {
-      C1[(size_t)i * ld + j] = Cin1[(size_t)i * ld + j];
-      C2[(size_t)i * ld + j] = Cin2[(size_t)i * ld + j];
+    if (t < 256) {
+      const int i = i0 + (t >> 4), j = j0 + (t & 15);
+      if (i < m && j < m) {
+        C1[(size_t)i * ld + j] = Cin1[(size_t)i * ld + j];
+        C2[(size_t)i * ld + j] = Cin2[(size_t)i * ld + j];
+      }
     }
     return;
   }
@@ -243,13 +246,13 @@ __global__ __launch_bounds__(256) void dgemm2_kernel(const double* __restrict__ 
     }
   };
   v4d acc1 = {0.0, 0.0, 0.0, 0.0}, acc1b = acc1, acc2 = acc1, acc2b = acc1;
-  for (int c0 = wave; c0 < nch; c0 += 4 * DG_CH) {
+  for (int c0 = wave; c0 < nch; c0 += NW * DG_CH) {
 #pragma unroll
     for (int u = 0; u < DG_CH; ++u)
-      if (c0 + 4 * u < nch) load(u, c0 + 4 * u);
+      if (c0 + NW * u < nch) load(u, c0 + NW * u);
 #pragma unroll
     for (int u = 0; u < DG_CH; ++u) {
-      const int c = c0 + 4 * u;
+      const int c = c0 + NW * u;
       if (c < nch) {
         const int kb = 16 * c + 4 * g;
 #pragma unroll
@@ -269,7 +272,7 @@ __global__ __launch_bounds__(256) void dgemm2_kernel(const double* __restrict__ 
   }
   acc1 += acc1b;
   acc2 += acc2b;
-  __shared__ double red[3][2][4][64];
+  __shared__ double red[NW - 1][2][4][64];
   if (wave > 0) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -286,8 +289,13 @@ __global__ __launch_bounds__(256) void dgemm2_kernel(const double* __restrict__ 
   for (int e = 0; e < 4; ++e) {
     const int i = i0 + g + 4 * e;
     if (i < m && j < m) {
-      double o1 = alpha1 * (acc1[e] + red[0][0][e][lane] + red[1][0][e][lane] + red[2][0][e][lane]);
-      double o2 = alpha2 * (acc2[e] + red[0][1][e][lane] + red[1][1][e][lane] + red[2][1][e][lane]);
+      double s1 = acc1[e], s2 = acc2[e];
+#pragma unroll
+      for (int w = 0; w < NW - 1; ++w) {
+        s1 += red[w][0][e][lane];
+        s2 += red[w][1][e][lane];
+      }
+      double o1 = alpha1 * s1, o2 = alpha2 * s2;
       if (beta1 != 0.0) o1 += beta1 * Cin1[(size_t)i * ld + j];
       if (beta2 != 0.0) o2 += beta2 * Cin2[(size_t)i * ld + j];
       C1[(size_t)i * ld + j] = o1;
@@ -724,7 +732,8 @@ void gemm2(hipStream_t s, int m_max, const double* A1, const double* A2, const d
                        B, ld, C1, C2, Cin1, Cin2, alpha1, beta1, alpha2, beta2, Dp, st, mode, bd);
   } else {
     const int nb = (m_max + 15) / 16;
-    hipLaunchKernelGGL((dgemm2_kernel<TA1, TA2>), bz(dim3(nb, nb), bc), dim3(256), 0, s, A1, A2, B, ld, C1, C2,
+    hipLaunchKernelGGL((dgemm2_kernel<TA1, TA2, DG2_NW>), bz(dim3(nb, nb), bc), dim3(64 * DG2_NW), 0, s, A1, A2, B,
+                       ld, C1, C2,
                        Cin1, Cin2, alpha1, beta1, alpha2, beta2, Dp, st, mode, bd);
   }
 }
