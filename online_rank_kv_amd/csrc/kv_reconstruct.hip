@@ -367,14 +367,19 @@ __global__ __launch_bounds__(256) void recon_stream_kernel(const float* __restri
   __shared__ int posS[2][RS_BM];
   float4 creg[2][8];
   int preg[2];
+  // C rows through a buffer descriptor based at the block's first row and
+  // bounded by the last row n - 1: rows past n read as zero, and the per-load
+  // offsets are fixed (row t / 64 + 4 u, column 4 (t % 64)), so no address
+  // arithmetic runs per block.
+  const uint32_t voff0 = (uint32_t)(((t >> 6) * ldc + (t & 63) * 4) * 4);
+  const uint32_t vstep = (uint32_t)(4 * ldc * 4);
   auto load_c = [&](int slot, int blk) {
     const int i0 = blk * RS_BM;
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(C + (size_t)i0 * ldc), (short)0, (int)((n - i0) * ldc * 4), 0x00020000);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = t + 256 * u, r = e >> 6, c4 = (e & 63) * 4;
-      const int row = min(i0 + r, n - 1);
-      creg[slot][u] = *(const float4*)(C + (size_t)row * ldc + min(c4, ldc - 4));
-    }
+    for (int u = 0; u < 8; ++u)
+      creg[slot][u] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rc, voff0 + u * vstep, 0, 0));
     preg[slot] = pos[min(i0 + (t & 31), n - 1)];
   };
   auto store_c = [&](int slot, uint16_t* cs, int* ps, int blk) {
@@ -413,19 +418,24 @@ __global__ __launch_bounds__(256) void recon_stream_kernel(const float* __restri
     for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) acc[a][cb] = v4f{0.f, 0.f, 0.f, 0.f};
+    auto kstep = [&](int sk) {
+      const int ko = 32 * sk + 8 * (lane >> 4);
 #pragma unroll
-    for (int sk = 0; sk < 8; ++sk) {
-      if (sk < ks) {
-        const int ko = 32 * sk + 8 * (lane >> 4);
-#pragma unroll
-        for (int a = 0; a < 2; ++a) {
-          const v8bf av = __builtin_bit_cast(v8bf, *(const uint4*)(cs + (16 * a + (lane & 15)) * RS_CS + ko));
-          acc[a][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(v8bf, breg[0][sk]),
-                                                              acc[a][0], 0, 0, 0);
-          acc[a][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(v8bf, breg[1][sk]),
-                                                              acc[a][1], 0, 0, 0);
-        }
+      for (int a = 0; a < 2; ++a) {
+        const v8bf av = __builtin_bit_cast(v8bf, *(const uint4*)(cs + (16 * a + (lane & 15)) * RS_CS + ko));
+        acc[a][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(v8bf, breg[0][sk]),
+                                                            acc[a][0], 0, 0, 0);
+        acc[a][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(v8bf, breg[1][sk]),
+                                                            acc[a][1], 0, 0, 0);
       }
+    };
+    if (ks == 8) {  // the whole rank: no branch between the steps, reads issued ahead
+#pragma unroll
+      for (int sk = 0; sk < 8; ++sk) kstep(sk);
+    } else {
+#pragma unroll
+      for (int sk = 0; sk < 8; ++sk)
+        if (sk < ks) kstep(sk);
     }
     // epilogue: lane l, element e holds row 4(l/16) + e of each 16-row half a
 #pragma unroll
@@ -531,7 +541,8 @@ int iskv_launch_reconstruct(const isvd_handle* h, const float* X_exact, const in
     dim3 grid(D / W, (n + 31) / 32);
     const bool mfma = bf && D % RM_BN == 0 && head_dim % 32 == 0 && RM_BN % head_dim == 0 &&
                       R % 8 == 0;
-    if (mfma && R % 32 == 0 && R <= 256) {
+    // (the streaming kernel's buffer descriptors bound C in 32-bit bytes)
+    if (mfma && R % 32 == 0 && R <= 256 && (size_t)n * R * 4 < ((size_t)1 << 31)) {
       const int T = D / 128;
       const int G = T >= 64 ? 1 : 64 / T;  // 512 workgroups when T divides 64
       hipLaunchKernelGGL(recon_stream_kernel, dim3(8 * T * G), dim3(256), 0, s, h->C, R, h->w.Bbf, R,
