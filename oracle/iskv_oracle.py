@@ -39,6 +39,7 @@ __all__ = [
     "bf16_round",
     "reconstruct",
     "attend",
+    "attend_factor_v",
     "persistent_bytes",
     "breakeven_rows",
     "dense_kv_bytes",
@@ -319,6 +320,53 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndar
             m = logits.max()
             w = np.exp(logits - m)
             out[bi, h] = (w @ V[bi, :, g, :]) / w.sum()
+    return out
+
+
+def attend_factor_v(q: np.ndarray, K: np.ndarray, fac: Factor, X_exact, pos_exact,
+                    scale: float) -> np.ndarray:
+    """Decode attention with the value history kept factored (the value-side
+    decode the iS-KV notes point to in §5.2 / §6: attend with the factors
+    instead of rebuilding the dense value cache).
+
+    One sequence: q (H_q, d_h); K (n_total, H_kv, d_h) in position order; the
+    value path's factor ``fac`` (compressed rows at fac.pos) and its exact
+    rows X_exact (n_e, D) at pos_exact. For query head h on KV head g,
+    p_h = softmax over every position t of scale * K[t, g] . q_h; then
+      o_h = (p_h[fac.pos]^T U diag(sigma)) B[g d_h : (g + 1) d_h, :]^T
+            + p_h[pos_exact]^T X_exact[:, g d_h : (g + 1) d_h].
+    The compressed and exact positions must partition 0 .. n_total - 1.
+    Float64; returns (H_q, d_h).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    n_total, Hkv, dh = K.shape
+    Hq = q.shape[0]
+    grp = Hq // Hkv
+    pos_c = np.asarray(fac.pos, dtype=np.int64).reshape(-1)
+    pos_e = np.asarray(pos_exact, dtype=np.int64).reshape(-1)
+    X_exact = np.asarray(X_exact, dtype=np.float64).reshape(-1, fac.D)
+    allpos = np.concatenate([pos_c, pos_e])
+    covered = np.zeros(n_total, dtype=np.int64)
+    if allpos.size and (allpos.min() < 0 or allpos.max() >= n_total):
+        raise ValueError("a position lies outside 0..n_total-1")
+    np.add.at(covered, allpos, 1)
+    if not np.all(covered == 1):
+        raise ValueError("compressed and exact positions must partition 0..n_total-1")
+    # stored coordinates of the compressed rows (C = U diag(sigma), or the
+    # stale coordinates of the basis-only ablation)
+    C = (fac.C_stale if fac.C_stale is not None else fac.U * fac.sigma[None, :]) if fac.n > 0 else None
+    out = np.zeros((Hq, dh))
+    for h in range(Hq):
+        g = h // grp
+        logits = (K[:, g, :] @ q[h]) * scale
+        w = np.exp(logits - logits.max())
+        p = w / w.sum()
+        o = p[pos_e] @ X_exact[:, g * dh:(g + 1) * dh] if pos_e.size else np.zeros(dh)
+        if fac.n > 0:
+            y = p[pos_c] @ C
+            o = o + y @ fac.B[g * dh:(g + 1) * dh, :].T
+        out[h] = o
     return out
 
 

@@ -301,6 +301,63 @@ def test_attend_special_cases():
     assert np.allclose(out[:, 4], V[:, 4, 1], atol=1e-10)
 
 
+def _factor_v_case(seed, sync=True):
+    """A small value path (D = 16 = 2 heads x 8, r = 4) folded from 24 rows,
+    plus 6 exact rows, with the 30 positions shuffled between the two."""
+    rng = np.random.default_rng(seed)
+    D, dh, n_c, n_e = 16, 8, 24, 6
+    X = rng.standard_normal((n_c, D)) @ np.diag(np.exp(-np.arange(D) / 3.0))
+    perm = rng.permutation(n_c + n_e)
+    pos_c, pos_e = np.sort(perm[:n_c]), perm[n_c:]
+    fac = O.empty_factor(D, sync=sync)
+    for s in range(0, n_c, 4):
+        fac = O.merge(fac, X[s:s + 4], pos_c[s:s + 4], 4)
+    X_e = rng.standard_normal((n_e, D))
+    return fac, X_e, pos_e, n_c + n_e, dh
+
+
+@pytest.mark.parametrize("sync", [True, False])
+def test_attend_factor_v_equals_dense_on_reconstructed_values(sync):
+    """Value attention on the factors = dense attention over the rebuilt value
+    cache (the identity the factored decode rests on), also with the stale
+    coordinates of the basis-only ablation."""
+    fac, X_e, pos_e, n_total, dh = _factor_v_case(3, sync)
+    rng = np.random.default_rng(4)
+    Hq, Hkv = 4, 2
+    q = rng.standard_normal((Hq, dh))
+    K = rng.standard_normal((n_total, Hkv, dh))
+    Vhat = O.reconstruct(fac, X_e, pos_e, n_total, dh, apply_rope=False)
+    if not sync:  # the ablation keeps stale coordinates: the stored rows differ from U S B^T
+        Vhat[fac.pos] = O.stored_rows(fac)
+    dense = O.attend(q[None], K[None], Vhat.reshape(1, n_total, Hkv, dh), 0.3)[0]
+    got = O.attend_factor_v(q, K, fac, X_e, pos_e, 0.3)
+    assert np.allclose(got, dense, rtol=1e-12, atol=1e-12)
+
+
+def test_attend_factor_v_special_cases():
+    fac, X_e, pos_e, n_total, dh = _factor_v_case(5)
+    Hq, Hkv = 4, 2
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((Hq, dh))
+    C = fac.U * fac.sigma[None, :]
+    # equal keys: every head returns the mean over all positions of its value slice
+    K = np.broadcast_to(rng.standard_normal((1, Hkv, dh)), (n_total, Hkv, dh)).copy()
+    got = O.attend_factor_v(q, K, fac, X_e, pos_e, 1.0)
+    for h in range(Hq):
+        g = h // 2
+        want = (C.sum(axis=0) @ fac.B[g * dh:(g + 1) * dh].T + X_e[:, g * dh:(g + 1) * dh].sum(axis=0)) / n_total
+        assert np.allclose(got[h], want, atol=1e-12)
+    # a planted needle at a compressed position returns that row's rebuilt slice
+    i = 7
+    K = rng.standard_normal((n_total, Hkv, dh)) * 0.01
+    K[fac.pos[i], 0] = 200.0 * q[0]
+    got = O.attend_factor_v(q, K, fac, X_e, pos_e, 1.0)
+    assert np.allclose(got[0], C[i] @ fac.B[:dh].T, atol=1e-9)
+    # positions that do not partition the cache are refused
+    with pytest.raises(ValueError):
+        O.attend_factor_v(q, K[:-1], fac, X_e, pos_e, 1.0)
+
+
 # ---------------------------------------------------------------- storage
 def test_storage_accounting_matches_pages():
     g = json.load(open(os.path.join(GOLDEN, "storage_eq12.json")))
