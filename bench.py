@@ -308,6 +308,47 @@ def main():
     def avg_ms(key):
         return float(np.mean([a.elapsed_time(b) for a, b in ev[key]]))
 
+    # value side of the decode with the value history kept factored
+    # (decode_attend_fv, outside the timed region) against the dense value
+    # side of the timed step (V reconstruction + exact rows + attention over
+    # rebuilt values), on the same caches
+    torch.cuda.synchronize()
+    n_tot = cursor[0]
+    sv = streams[1]
+    wsf = torch.empty(K.decode_attend_fv_workspace_bytes(paths[1].h, wins[1].rows.shape[0], HQ), dtype=torch.uint8,
+                      device=dev)
+    of = torch.empty((HQ, DH), dtype=torch.bfloat16, device=dev)
+    ef = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    reps = 20
+
+    def fv():
+        K.decode_attend_fv(q[0], Kc, paths[1].h, wins[1].rows, wins[1].pos, wins[1].rows.shape[0], n_tot, HQ, HKV,
+                           DH, DH ** -0.5, of, wsf, stream=sv)
+
+    def dense_v():
+        paths[1].reconstruct(Vc, n_tot, head_dim=DH, rope=False, stream=sv)
+        K.kv_scatter_exact(wins[1].rows, wins[1].pos, wins[1].rows.shape[0], D, n_tot, DH, False, THETA, Vc,
+                           K.ISKV_OUT_BF16, sv)
+        K.decode_attend(q, Kc, Vc, 1, n_tot, HQ, HKV, DH, DH ** -0.5, o, ws, stream=sv)
+
+    for _ in range(3):
+        fv()
+        dense_v()
+    ef[0].record(sv)
+    for _ in range(reps):
+        fv()
+    ef[1].record(sv)
+    for _ in range(reps):
+        dense_v()
+    ef[2].record(sv)
+    sv.synchronize()
+    fv_ms = ef[0].elapsed_time(ef[1]) / reps
+    dense_ms = ef[1].elapsed_time(ef[2]) / reps
+    n_c = paths[1].n
+    # algorithmic bytes: keys (n_total x D bf16), coordinates (n_c x k fp32), exact rows, basis
+    fv_bytes = n_tot * D * 2 + n_c * R * 4 + wins[1].rows.shape[0] * D * 4 + D * R * 4
+    fv_dev = float(np.abs(of.float().cpu().numpy() - o[0].float().cpu().numpy()).max())
+
     # stage breakdown of merges (outside the timed region): the handle runs
     # its merges kernel by kernel with HIP events at the stage boundaries; in
     # the batched layout each stage covers both paths (one launch per kernel)
@@ -370,6 +411,10 @@ def main():
                      "kernel": "kv_reconstruct (K, bf16 + RoPE)",
                      "mfma_frac": recon_flops / (ms["recon_k"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
         "merge_stage_ms": stage_k,
+        "factor_v_attention": {"ms": fv_ms, "dense_value_side_ms": dense_ms, "algorithmic_bytes": fv_bytes,
+                               "achieved_GBps": fv_bytes / (fv_ms * 1e-3) / 1e9, "n_total": n_tot,
+                               "max_abs_vs_dense": fv_dev,
+                               "kernel": "decode_attend_fv (value history factored, no V reconstruction)"},
         "merge_stage_paths": cu_paths,
         "coord_update": {"bound": "hbm", "achieved": cu_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": cu_gbps / HBM_PEAK_GBPS, "algorithmic_bytes": cu_bytes, "rows": n_cu,

@@ -249,6 +249,32 @@ int decode_attend(const uint16_t* q, const uint16_t* K, const uint16_t* V, int32
                   int32_t n, int32_t Hq, int32_t Hkv, int32_t dh, float scale, uint16_t* out,
                   void* workspace, size_t ws_bytes, void* stream);
 
+/* Decode attention with the value history kept factored (the value-side
+ * decode the iS-KV notes point to in §5.2 and §6: attend with the factors
+ * rather than rebuilding the dense value cache). One sequence. For query
+ * head h on KV head g = h / (Hq / Hkv), with p_h the softmax over every
+ * position t of scale * K[t, g] . q_h:
+ *   out_h = (p_h[pos]^T C) B[g dh : (g + 1) dh, :k]^T + p_h[pos_exact]^T X_exact[:, g dh : (g + 1) dh]
+ * where C (n x k), B and pos are the value handle hv's coordinates, basis and
+ * row positions, so the value side reads n k coordinates instead of n D values.
+ *   q          device bf16 [Hq x dh], already rotated.
+ *   K          device bf16 [n_total x Hkv x dh]: the key cache in position order.
+ *   hv         the value path (read only); D = Hkv dh, r_max % 4 == 0, r_max <= 448.
+ *   X_exact    device fp32 [n_exact x D] exact value rows at pos_exact (device
+ *              int32 [n_exact]; slots with a position outside 0..n_total-1 are
+ *              skipped, so a window buffer can be passed whole). The compressed and
+ *              valid exact positions must partition 0..n_total-1.
+ *   dh == 128, Hq <= 32, Hq / Hkv in {1, 2, 4}.
+ *   out        device bf16 [Hq x dh].
+ *   workspace  >= decode_attend_fv_workspace_bytes(hv, n_exact, Hq) bytes (sized
+ *              for hv's row capacity); it holds partial results and per-head
+ *              counters, so calls that may overlap must not share one.
+ * Errors: EINVAL, EWORKSPACE, EHIP. */
+size_t decode_attend_fv_workspace_bytes(const isvd_handle* hv, int32_t n_exact, int32_t Hq);
+int decode_attend_fv(const uint16_t* q, const uint16_t* K, const isvd_handle* hv, const float* X_exact,
+                     const int32_t* pos_exact, int32_t n_exact, int32_t n_total, int32_t Hq, int32_t Hkv,
+                     int32_t dh, float scale, uint16_t* out, void* workspace, size_t ws_bytes, void* stream);
+
 /* ---- exact window and pending FIFO --------------------------------------- */
 /* The cache policy of §3.2 and Algorithm 3 (iS-KV notes): every new row is
  * stored exactly in a recent window of `window` rows; an unprotected row

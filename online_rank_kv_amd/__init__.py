@@ -21,7 +21,8 @@ __all__ = [
     "ISKV_OUT_FP32", "ISKV_DEV_NONFINITE", "ISKV_DEV_NOCONV", "EXPORTED_SYMBOLS",
     "isvd_workspace_bytes", "isvd_init", "isvd_merge_block", "isvd_reorth", "isvd_query",
     "isvd_rows", "isvd_destroy", "isvd_query_state", "isvd_sym_eig", "kv_reconstruct", "kv_scatter_exact",
-    "decode_attend_workspace_bytes", "decode_attend", "iskv_window_rows", "iskv_window_init", "iskv_window_protect",
+    "decode_attend_workspace_bytes", "decode_attend", "decode_attend_fv_workspace_bytes", "decode_attend_fv",
+    "iskv_window_rows", "iskv_window_init", "iskv_window_protect",
     "iskv_window_append", "iskv_window_exact", "iskv_window_destroy", "iskv_strerror",
     "iskv_window_append_batched", "isvd_merge_block_batched", "isvd_set_timing", "isvd_stage_times", "MERGE_STAGES", "IsvdPath", "IsvdBatch", "ExactWindow",
 ]
@@ -49,6 +50,7 @@ EXPORTED_SYMBOLS = (
     "iskv_window_append", "iskv_window_exact", "iskv_window_destroy", "iskv_strerror",
     "isvd_query_state", "isvd_sym_eig", "kv_scatter_exact", "isvd_merge_block_batched",
     "isvd_set_timing", "isvd_stage_times", "iskv_window_append_batched",
+    "decode_attend_fv_workspace_bytes", "decode_attend_fv",
 )
 
 
@@ -105,6 +107,11 @@ lib.decode_attend_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
 lib.decode_attend.restype = ctypes.c_int
 lib.decode_attend.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _vp, _vp,
                               ctypes.c_size_t, _vp]
+lib.decode_attend_fv_workspace_bytes.restype = ctypes.c_size_t
+lib.decode_attend_fv_workspace_bytes.argtypes = [_vp, _i32, _i32]
+lib.decode_attend_fv.restype = ctypes.c_int
+lib.decode_attend_fv.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _vp, _vp,
+                                 ctypes.c_size_t, _vp]
 lib.iskv_window_rows.restype = _i32
 lib.iskv_window_rows.argtypes = [_i32, _i32, _i32]
 lib.iskv_window_init.restype = ctypes.c_int
@@ -237,6 +244,18 @@ def decode_attend(q, K, V, batch: int, n: int, Hq: int, Hkv: int, dh: int, scale
                              int(dh), float(scale), _ptr(out), _ptr(workspace),
                              workspace.numel() * workspace.element_size(), _stream_ptr(stream)),
            "decode_attend")
+
+
+def decode_attend_fv_workspace_bytes(hv: int, n_exact: int, Hq: int) -> int:
+    return int(lib.decode_attend_fv_workspace_bytes(hv, int(n_exact), int(Hq)))
+
+
+def decode_attend_fv(q, K, hv: int, X_exact, pos_exact, n_exact: int, n_total: int, Hq: int, Hkv: int, dh: int,
+                     scale: float, out, workspace, stream=None) -> None:
+    _check(lib.decode_attend_fv(_ptr(q), _ptr(K), hv, _ptr(X_exact), _ptr(pos_exact), int(n_exact), int(n_total),
+                                int(Hq), int(Hkv), int(dh), float(scale), _ptr(out), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream_ptr(stream)),
+           "decode_attend_fv")
 
 
 def iskv_window_rows(prot_cap: int, window: int, block: int) -> int:

@@ -307,6 +307,27 @@ int decode_attend(const uint16_t* q, const uint16_t* K, const uint16_t* V, int32
                             (hipStream_t)stream);
 }
 
+size_t decode_attend_fv_workspace_bytes(const isvd_handle* hv, int32_t n_exact, int32_t Hq) {
+  if (!hv || n_exact < 0 || Hq < 1) return 0;
+  return iskv_attend_fv_ws_bytes(hv->cfg.n_cap, n_exact, Hq, hv->cfg.r_max);
+}
+
+int decode_attend_fv(const uint16_t* q, const uint16_t* K, const isvd_handle* hv, const float* X_exact,
+                     const int32_t* pos_exact, int32_t n_exact, int32_t n_total, int32_t Hq, int32_t Hkv,
+                     int32_t dh, float scale, uint16_t* out, void* workspace, size_t ws_bytes, void* stream) {
+  if (!q || !K || !hv || !out || !workspace) return ISKV_EINVAL;
+  if (n_exact < 0 || (n_exact > 0 && (!X_exact || !pos_exact))) return ISKV_EINVAL;
+  if (n_total < 1 || Hq < 1 || Hkv < 1 || dh != 128 || Hq > 32 || Hq % Hkv != 0) return ISKV_EINVAL;
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4) return ISKV_EINVAL;
+  if (hv->cfg.D != Hkv * 128 || hv->cfg.D > 1024) return ISKV_EINVAL;
+  if (hv->cfg.r_max % 4 != 0 || hv->cfg.r_max > 448) return ISKV_EINVAL;  // a chunk of rows fits in LDS
+  if (hv->n_host + n_exact < 1) return ISKV_EINVAL;
+  if (ws_bytes < iskv_attend_fv_ws_bytes(hv->n_host, n_exact, Hq, hv->cfg.r_max)) return ISKV_EWORKSPACE;
+  return iskv_launch_attend_fv(q, K, hv, X_exact, pos_exact, n_exact, n_total, Hq, Hkv, scale, out, workspace,
+                               ws_bytes, (hipStream_t)stream);
+}
+
 // ---- exact window and pending FIFO ----------------------------------------
 int32_t iskv_window_rows(int32_t prot_cap, int32_t window, int32_t block) {
   if (prot_cap < 0 || window < 0 || block < 1) return 0;

@@ -542,6 +542,58 @@ def test_decode_attend_needle(K):
     assert np.abs(out[0, 9].float().cpu().numpy() - v).max() < 2e-2
 
 
+@pytest.mark.parametrize("hq,hkv,r,n", [(32, 8, 256, 3000), (8, 8, 64, 777), (16, 4, 320, 1500), (32, 8, 256, 17000)])
+def test_decode_attend_factor_v_matches_oracle(K, hq, hkv, r, n):
+    """Value attention on the factors of a V path (window w = 128 and pending
+    rows exact, the rest folded) against the oracle evaluated on the GPU's own
+    factors and keys, and against dense attention over the rebuilt values."""
+    D, b, W = hkv * 128, 32, 128
+    X = synth.kv_stream(synth.StreamSpec(D=D, n=n, spectrum="invsqrt", noise_std=0.0, seed=7))
+    Xd = torch.from_numpy(X).to(DEV)
+    torch.cuda.synchronize()
+    st = torch.cuda.Stream()
+    hv = K.IsvdPath(D=D, r_max=r, b_max=b, n_cap=n, reorth_every_rows=256, device=DEV, stream=st)
+    win = K.ExactWindow(hv, window=W, block=b, stream=st)
+    for s in range(0, n, 200):
+        win.append(Xd[s:min(n, s + 200)], s)
+    st.synchronize()
+    rng = np.random.default_rng(8)
+    Kc = (rng.standard_normal((n, hkv, 128)) * 0.3).astype(np.float32)
+    Kc[1234 % n, 1, :] = 0.0
+    qn = rng.standard_normal((hq, 128)).astype(np.float32)
+    Kbf = torch.from_numpy(Kc).to(DEV).bfloat16().contiguous()
+    q = torch.from_numpy(qn).to(DEV).bfloat16()
+    out = torch.empty((hq, 128), dtype=torch.bfloat16, device=DEV)
+    nrows = win.rows.shape[0]
+    ws = torch.empty(K.decode_attend_fv_workspace_bytes(hv.h, nrows, hq), dtype=torch.uint8, device=DEV)
+    scale = 128 ** -0.5 * 2.0
+    K.decode_attend_fv(q, Kbf, hv.h, win.rows, win.pos, nrows, n, hq, hkv, 128, scale, out, ws, stream=st)
+    st.synchronize()
+    got = out.float().cpu().numpy()
+    # oracle on the GPU's own factors (C given as U with unit sigma) and bf16 keys / query
+    Cg, Bg, _, pg, stt = gpu_factors(hv)
+    assert stt == 0
+    fac = O.Factor(U=Cg, sigma=np.ones(Cg.shape[1]), B=Bg, pos=pg)
+    wp = win.pos.cpu().numpy()
+    keep = wp >= 0
+    Xe = win.rows.double().cpu().numpy()[keep]
+    qbf = torch.from_numpy(qn).bfloat16().double().numpy()
+    ref = O.attend_factor_v(qbf, Kbf.double().cpu().numpy(), fac, Xe, wp[keep], scale)
+    assert np.abs(got - ref).max() < 2e-2
+    assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 2e-2
+    # dense attention over the rebuilt bf16 values gives the same output
+    Vc = torch.empty((n, D), dtype=torch.bfloat16, device=DEV)
+    hv.reconstruct(Vc, n, X_exact=win.rows, pos_exact=win.pos, head_dim=128, rope=False, stream=st)
+    dense = torch.empty((1, hq, 128), dtype=torch.bfloat16, device=DEV)
+    wsd = torch.empty(K.decode_attend_workspace_bytes(1, n, hq, 128), dtype=torch.uint8, device=DEV)
+    K.decode_attend(q.view(1, hq, 128), Kbf.view(1, n, hkv, 128), Vc.view(1, n, hkv, 128), 1, n, hq, hkv, 128,
+                    scale, dense, wsd, stream=st)
+    st.synchronize()
+    assert np.abs(got - dense[0].float().cpu().numpy()).max() < 2e-2
+    win.close()
+    hv.close()
+
+
 # --------------------------------------------------------------------------- window
 def test_window_pending_and_merge(K):
     """Exact window (w=128) + pending FIFO: 508 merges for 16,384 rows? here 2,048 rows -> 60 merges."""
