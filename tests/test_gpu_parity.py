@@ -594,6 +594,60 @@ def test_decode_attend_factor_v_matches_oracle(K, hq, hkv, r, n):
     hv.close()
 
 
+@pytest.mark.parametrize("mode", ["no_exact_rows", "only_exact_rows"])
+def test_decode_attend_factor_v_one_side_only(K, mode):
+    """Value attention on the factors when one side is empty: every row folded
+    (n_exact = 0, a ragged 1,000 rows) or none folded yet (n_c = 0, 100 rows in
+    the window), against the oracle on the GPU's own factors."""
+    hq, hkv, r, b = 16, 4, 128, 32
+    D = hkv * 128
+    n = 1000 if mode == "no_exact_rows" else 100
+    X = synth.kv_stream(synth.StreamSpec(D=D, n=n, spectrum="invsqrt", noise_std=0.0, seed=11))
+    Xd = torch.from_numpy(X).to(DEV)
+    hv = K.IsvdPath(D=D, r_max=r, b_max=b, n_cap=n, reorth_every_rows=256, device=DEV)
+    win = None
+    if mode == "no_exact_rows":
+        pos = torch.arange(n, dtype=torch.int32, device=DEV)
+        for s0 in range(0, n, b):
+            e = min(n, s0 + b)
+            hv.merge(Xd[s0:e], pos[s0:e])
+    else:
+        win = K.ExactWindow(hv, window=128, block=b)
+        win.append(Xd, 0)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(12)
+    Kc = (rng.standard_normal((n, hkv, 128)) * 0.3).astype(np.float32)
+    qn = rng.standard_normal((hq, 128)).astype(np.float32)
+    Kbf = torch.from_numpy(Kc).to(DEV).bfloat16().contiguous()
+    q = torch.from_numpy(qn).to(DEV).bfloat16()
+    out = torch.empty((hq, 128), dtype=torch.bfloat16, device=DEV)
+    ne = 0 if win is None else win.rows.shape[0]
+    ws = torch.empty(K.decode_attend_fv_workspace_bytes(hv.h, ne, hq), dtype=torch.uint8, device=DEV)
+    scale = 128 ** -0.5 * 2.0
+    K.decode_attend_fv(q, Kbf, hv.h, None if win is None else win.rows, None if win is None else win.pos, ne, n,
+                       hq, hkv, 128, scale, out, ws)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    Cg, Bg, _, pg, stt = gpu_factors(hv)
+    assert stt == 0
+    assert (Cg.shape[0] == n) if mode == "no_exact_rows" else (Cg.shape[0] == 0)
+    fac = O.Factor(U=Cg, sigma=np.ones(Cg.shape[1]), B=Bg, pos=pg)
+    if win is None:
+        Xe, pe = np.zeros((0, D)), np.zeros(0, dtype=np.int64)
+    else:
+        wp = win.pos.cpu().numpy()
+        keep = wp >= 0
+        Xe, pe = win.rows.double().cpu().numpy()[keep], wp[keep]
+    qbf = torch.from_numpy(qn).bfloat16().double().numpy()
+    ref = O.attend_factor_v(qbf, Kbf.double().cpu().numpy(), fac, Xe, pe, scale)
+    assert np.all(np.isfinite(got))
+    assert np.abs(got - ref).max() < 2e-2
+    assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 2e-2
+    if win is not None:
+        win.close()
+    hv.close()
+
+
 # --------------------------------------------------------------------------- window
 def test_window_pending_and_merge(K):
     """Exact window (w=128) + pending FIFO: 508 merges for 16,384 rows? here 2,048 rows -> 60 merges."""
