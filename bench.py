@@ -414,6 +414,7 @@ def main():
         "factor_v_attention": {"ms": fv_ms, "dense_value_side_ms": dense_ms, "algorithmic_bytes": fv_bytes,
                                "achieved_GBps": fv_bytes / (fv_ms * 1e-3) / 1e9, "n_total": n_tot,
                                "max_abs_vs_dense": fv_dev,
+                               "split_kernel_traffic": profiled_traffic("fv_split_kernel_kv_n16k_traffic.md"),
                                "kernel": "decode_attend_fv (value history factored, no V reconstruction)"},
         "merge_stage_paths": cu_paths,
         "coord_update": {"bound": "hbm", "achieved": cu_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
