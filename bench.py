@@ -43,6 +43,7 @@ CALIB_BYTES = 256 << 20
 BF16_PEAK_TFLOPS = 2500.0
 FP32_PEAK_TFLOPS = 157.3
 TIMED_MERGES = 8  # merges run once more with stage events after the timed region
+MODE_MERGES = 16  # merges timed in each merge mode at the end of the run
 
 
 def parse():
@@ -191,7 +192,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     steps, warm = args.steps, args.warmup
-    n_rows = N0 + (steps + warm + 4 + TIMED_MERGES) * BLK + WIN
+    n_rows = N0 + (steps + warm + 4 + TIMED_MERGES + 3 * (MODE_MERGES + 2)) * BLK + WIN
     t_gen = time.perf_counter()
     Xk = synth.kv_stream(synth.StreamSpec(D, n_rows, "exp40+0.01", 0.0, 0))
     Xv = synth.kv_stream(synth.StreamSpec(D, n_rows, "invsqrt", 0.0, 1))
@@ -374,6 +375,32 @@ def main():
     cu_gbps = cu_bytes / (stage_k["coord_update"] * 1e-3) / 1e9
     cu_tflops = cu_paths * 2.0 * n_cu * R * R / (stage_k["coord_update"] * 1e-3) / 1e12
 
+    # merge modes on the K path, last because they change its factors: the
+    # full merge (with its re-orthogonalisation every 256 rows), the
+    # basis-only ablation (no coordinate rewrite) and the frozen basis (new
+    # rows' coordinates only), MODE_MERGES merges each on the path's stream
+    mode_ms = {}
+    n_mode = paths[0].n
+    pos_all = torch.arange(n_rows, dtype=torch.int32, device=dev)
+    sk = streams[0]
+    em = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def one_merge():
+        s0 = cursor[0]
+        paths[0].merge(Xd[0][s0:s0 + BLK], pos_all[s0:s0 + BLK])
+        cursor[0] += BLK
+
+    for name, mode in (("full", 0), ("basis_only", K.ISKV_NO_COORD_SYNC), ("frozen_basis", K.ISKV_FROZEN_BASIS)):
+        paths[0].set_mode(mode)
+        for _ in range(2):
+            one_merge()
+        em[0].record(sk)
+        for _ in range(MODE_MERGES):
+            one_merge()
+        em[1].record(sk)
+        sk.synchronize()
+        mode_ms[name] = em[0].elapsed_time(em[1]) / MODE_MERGES
+
     ms = {k: avg_ms(k) for k in ev}
     core = [p.state() for p in paths]
     merges = 2 * steps
@@ -417,6 +444,12 @@ def main():
                                "split_kernel_traffic": profiled_traffic("fv_split_kernel_kv_n16k_traffic.md"),
                                "kernel": "decode_attend_fv (value history factored, no V reconstruction)"},
         "merge_stage_paths": cu_paths,
+        "merge_modes": {"full_ms": mode_ms["full"], "basis_only_ms": mode_ms["basis_only"],
+                        "frozen_basis_ms": mode_ms["frozen_basis"], "merges_each": MODE_MERGES,
+                        "rows_at_start": n_mode,
+                        "what": "K path alone on its stream, recorded sequences; full includes its "
+                                "re-orthogonalisation every 256 rows; basis-only skips the coordinate "
+                                "rewrite; frozen basis stores F B only"},
         "coord_update": {"bound": "hbm", "achieved": cu_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": cu_gbps / HBM_PEAK_GBPS, "algorithmic_bytes": cu_bytes, "rows": n_cu,
                          "traffic": profiled_traffic("xh_reg_kernel_coord_update_kv_n16k_traffic.md"),

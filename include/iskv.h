@@ -65,6 +65,11 @@ enum iskv_status {
                                 non-null stream, the fixed launch sequence is
                                 recorded once into a HIP graph (per block size)
                                 and replayed; results are the same. */
+#define ISKV_FROZEN_BASIS 4  /* frozen-basis baseline (iS-KV notes §6.4 ablation,
+                                §8): merges keep B and every stored row as they
+                                are and append only the new rows' coordinates
+                                F B; no residual, core solve, coordinate rewrite,
+                                basis update or re-orthogonalisation */
 
 /* Output dtypes of kv_reconstruct. */
 #define ISKV_OUT_BF16 0
@@ -83,7 +88,8 @@ typedef struct iskv_config {
                                 keep residual direction j when
                                 rho_j > max(delta*s, max(D,b)*2^-23*s),
                                 s = max(sigma_1, rho_1)                                   */
-  int32_t flags;             /* ISKV_NO_COORD_SYNC | ISKV_NO_GRAPH, or 0                  */
+  int32_t flags;             /* ISKV_NO_COORD_SYNC | ISKV_NO_GRAPH | ISKV_FROZEN_BASIS, or 0
+                                (at most one of NO_COORD_SYNC and FROZEN_BASIS)           */
 } iskv_config;
 
 typedef struct isvd_handle isvd_handle;
@@ -144,8 +150,20 @@ int isvd_merge_block_batched(isvd_handle* const* hs, int32_t count, const float*
  * thin QR of U and B and SVD of R_U diag(sigma) R_B^T: the product C B^T is
  * kept, B becomes orthonormal and C's columns orthogonal with norms sigma.
  * Errors: EMODE under ISKV_NO_COORD_SYNC (the stale rows have no consistent
- * factorisation to re-orthogonalise). */
+ * factorisation to re-orthogonalise) or ISKV_FROZEN_BASIS (B is frozen). */
 int isvd_reorth(isvd_handle* h);
+
+/* Switch the merge mode of a handle between calls (the baselines the iS-KV
+ * notes compare the full merge against): `mode` is 0 (full merge, §4),
+ * ISKV_NO_COORD_SYNC (basis-only ablation, §2.3) or ISKV_FROZEN_BASIS (frozen
+ * basis, §6.4 / §8); the handle's other flags are kept. Typical use: fold a
+ * prompt with full merges, then freeze its basis. Leaving the frozen mode for
+ * the full merge enqueues a re-orthogonalisation (§4.4) first, since the
+ * appended coordinates F B are not orthogonal columns with norms sigma; no
+ * other switch changes the factors. Recorded launch sequences are dropped and
+ * recorded again on the next call.
+ * Errors: EINVAL (null handle, another bit in mode, both bits), EHIP. */
+int isvd_set_mode(isvd_handle* h, int32_t mode);
 
 /* Synchronise the handle's stream and read the device counters: rows n,
  * current rank k and the device status word (ISKV_DEV_* bits). Any pointer

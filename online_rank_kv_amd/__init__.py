@@ -17,7 +17,8 @@ import ctypes
 import os
 
 __all__ = [
-    "LIB_PATH", "lib", "IskvError", "IskvConfig", "ISKV_NO_COORD_SYNC", "ISKV_NO_GRAPH", "ISKV_OUT_BF16",
+    "LIB_PATH", "lib", "IskvError", "IskvConfig", "ISKV_NO_COORD_SYNC", "ISKV_NO_GRAPH", "ISKV_FROZEN_BASIS",
+    "ISKV_OUT_BF16", "isvd_set_mode",
     "ISKV_OUT_FP32", "ISKV_DEV_NONFINITE", "ISKV_DEV_NOCONV", "EXPORTED_SYMBOLS",
     "isvd_workspace_bytes", "isvd_init", "isvd_merge_block", "isvd_reorth", "isvd_query",
     "isvd_rows", "isvd_destroy", "isvd_query_state", "isvd_sym_eig", "kv_reconstruct", "kv_scatter_exact",
@@ -38,6 +39,7 @@ lib = ctypes.CDLL(LIB_PATH)
 
 ISKV_NO_COORD_SYNC = 1
 ISKV_NO_GRAPH = 2
+ISKV_FROZEN_BASIS = 4
 ISKV_OUT_BF16 = 0
 ISKV_OUT_FP32 = 1
 ISKV_DEV_NONFINITE = 1
@@ -50,7 +52,7 @@ EXPORTED_SYMBOLS = (
     "iskv_window_append", "iskv_window_exact", "iskv_window_destroy", "iskv_strerror",
     "isvd_query_state", "isvd_sym_eig", "kv_scatter_exact", "isvd_merge_block_batched",
     "isvd_set_timing", "isvd_stage_times", "iskv_window_append_batched",
-    "decode_attend_fv_workspace_bytes", "decode_attend_fv",
+    "decode_attend_fv_workspace_bytes", "decode_attend_fv", "isvd_set_mode",
 )
 
 
@@ -84,6 +86,8 @@ lib.isvd_merge_block_batched.argtypes = [ctypes.POINTER(_vp), _i32, _vp, ctypes.
                                          _i32]
 lib.isvd_reorth.restype = ctypes.c_int
 lib.isvd_reorth.argtypes = [_vp]
+lib.isvd_set_mode.restype = ctypes.c_int
+lib.isvd_set_mode.argtypes = [_vp, _i32]
 lib.isvd_query.restype = ctypes.c_int
 lib.isvd_query.argtypes = [_vp, _pi32, _pi32, _pi32]
 lib.isvd_query_state.restype = ctypes.c_int
@@ -181,6 +185,10 @@ def isvd_merge_block_batched(handles, F, F_stride: int, pos_F, pos_stride: int, 
 
 def isvd_reorth(h: int) -> None:
     _check(lib.isvd_reorth(h), "isvd_reorth")
+
+
+def isvd_set_mode(h: int, mode: int) -> None:
+    _check(lib.isvd_set_mode(h, int(mode)), "isvd_set_mode")
 
 
 def isvd_query(h: int):
@@ -334,6 +342,10 @@ class IsvdPath:
 
     def reorth(self) -> None:
         isvd_reorth(self.h)
+
+    def set_mode(self, mode: int) -> None:
+        """0 (full merge), ISKV_NO_COORD_SYNC (basis-only) or ISKV_FROZEN_BASIS."""
+        isvd_set_mode(self.h, mode)
 
     def query(self):
         return isvd_query(self.h)

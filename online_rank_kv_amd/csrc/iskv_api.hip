@@ -25,7 +25,8 @@ bool cfg_ok(const iskv_config* c) {
   if (c->n_cap < 1) return false;
   if (c->reorth_every_rows < 0) return false;
   if (!(c->resid_rel_tol >= 0.f)) return false;
-  if (c->flags & ~(ISKV_NO_COORD_SYNC | ISKV_NO_GRAPH)) return false;
+  if (c->flags & ~(ISKV_NO_COORD_SYNC | ISKV_NO_GRAPH | ISKV_FROZEN_BASIS)) return false;
+  if ((c->flags & ISKV_NO_COORD_SYNC) && (c->flags & ISKV_FROZEN_BASIS)) return false;
   return true;
 }
 
@@ -159,7 +160,7 @@ int isvd_merge_block(isvd_handle* h, const float* F, const int32_t* pos_F, int32
   h->n_host += b;
   h->folded_host += b;
   const int T = h->cfg.reorth_every_rows;
-  if (T > 0 && !(h->cfg.flags & ISKV_NO_COORD_SYNC) && (h->folded_host / T) > (before / T)) {
+  if (T > 0 && !(h->cfg.flags & (ISKV_NO_COORD_SYNC | ISKV_FROZEN_BASIS)) && (h->folded_host / T) > (before / T)) {
     rc = iskv_launch_reorth(h);
     if (rc) return rc;
   }
@@ -197,7 +198,7 @@ int isvd_merge_block_batched(isvd_handle* const* hs, int32_t count, const float*
     h->n_host += b;
     h->folded_host += b;
     if (h->folded_host != h0->folded_host) lockstep = false;
-    if (T > 0 && !(h->cfg.flags & ISKV_NO_COORD_SYNC) && (h->folded_host / T) > (before / T))
+    if (T > 0 && !(h->cfg.flags & (ISKV_NO_COORD_SYNC | ISKV_FROZEN_BASIS)) && (h->folded_host / T) > (before / T))
       due.push_back(h);
   }
   if (due.empty()) return ISKV_OK;
@@ -211,8 +212,21 @@ int isvd_merge_block_batched(isvd_handle* const* hs, int32_t count, const float*
 
 int isvd_reorth(isvd_handle* h) {
   if (!h) return ISKV_EINVAL;
-  if (h->cfg.flags & ISKV_NO_COORD_SYNC) return ISKV_EMODE;
+  if (h->cfg.flags & (ISKV_NO_COORD_SYNC | ISKV_FROZEN_BASIS)) return ISKV_EMODE;
   return iskv_launch_reorth(h);
+}
+
+int isvd_set_mode(isvd_handle* h, int32_t mode) {
+  const int32_t modes = ISKV_NO_COORD_SYNC | ISKV_FROZEN_BASIS;
+  if (!h || (mode & ~modes) || mode == modes) return ISKV_EINVAL;
+  const int32_t old = h->cfg.flags & modes;
+  if (old == mode) return ISKV_OK;
+  iskv_release_graphs(h);
+  h->cfg.flags = (h->cfg.flags & ~modes) | mode;
+  // the appended coordinates F B are not orthogonal columns with norms sigma:
+  // the full merge's core (eq.(7)) needs them re-orthogonalised first
+  if ((old & ISKV_FROZEN_BASIS) && mode == 0 && h->n_host > 0) return iskv_launch_reorth(h);
+  return ISKV_OK;
 }
 
 int isvd_query(isvd_handle* h, int32_t* n, int32_t* k, int32_t* status) {

@@ -866,6 +866,37 @@ __global__ void merge_commit_kernel(float* sigma, const float* __restrict__ sig_
   }
 }
 
+// Frozen-basis merge (iS-KV notes §6.4 / §8 baseline): append the new rows'
+// coordinates Q = F B (b x k, columns past k zero) and positions at row n,
+// then n += b. One workgroup per path: every thread reads n before thread 0
+// advances it. Non-finite coordinates are latched like the full merge's input.
+__global__ __launch_bounds__(256) void frozen_append_kernel(const float* __restrict__ Q, int ldq,
+                                                            const int32_t* __restrict__ pos_F, int b, float* C,
+                                                            int ldc, int32_t* pos, int32_t* st,
+                                                            const int64_t* __restrict__ bd) {
+  const int64_t d = bd ? bd[blockIdx.z] : 0;
+  Q = iskv_rb(Q, d);
+  pos_F = iskv_rb(pos_F, d);
+  C = iskv_rb(C, d);
+  pos = iskv_rb(pos, d);
+  st = iskv_rb(st, d);
+  const int n = st[ST_N], k = st[ST_K];
+  bool bad = false;
+  for (int e = threadIdx.x; e < b * ldc; e += blockDim.x) {
+    const int i = e / ldc, j = e % ldc;
+    const float v = j < k ? Q[(size_t)i * ldq + j] : 0.f;
+    bad |= !isfinite(v);
+    C[(size_t)(n + i) * ldc + j] = v;
+  }
+  for (int i = threadIdx.x; i < b; i += blockDim.x) pos[n + i] = pos_F[i];
+  if (bad) atomicOr(&st[ST_STATUS], ISKV_DEV_NONFINITE);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    st[ST_N] = n + b;
+    st[ST_FOLDED] += b;
+  }
+}
+
 // Copy k (or another slot) into ST_JM so the eigensolver knows its order.
 __global__ void set_jm_kernel(int32_t* st, int from_slot,
     const int64_t* __restrict__ bd) {
@@ -1166,6 +1197,15 @@ static int merge_body(isvd_handle* h, const float* F, const int32_t* pos_F, int3
   mark(0);
   // 1. Q = F B (b x k)
   skinny<false>(h, b, R, F, D, h->B, R, ddim(dk), D, 1.f, 0.f, nullptr, 0, w.Q, R);
+  if (c.flags & ISKV_FROZEN_BASIS) {
+    // frozen basis: the new rows keep their coordinates in B; nothing else changes
+    hipLaunchKernelGGL(frozen_append_kernel, bz(dim3(1), h->bcount), dim3(256), 0, s, w.Q, R, pos_F, b, h->C, R,
+                       h->pos, w.st, h->bd);
+    for (int i = 1; i <= 5; ++i) mark(i);
+    if (h->timing) h->timed = true;
+    ISKV_HIP_CHECK(hipGetLastError());
+    return ISKV_OK;
+  }
   // 2. E = F - Q B^T (b x D)
   skinny<true>(h, b, D, w.Q, R, h->B, R, hdim(D), R, -1.f, 1.f, F, D, w.E, D);
   // 3. EB = E B; 4. E -= EB B^T (second projection, §4.1)

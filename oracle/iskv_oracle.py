@@ -32,6 +32,7 @@ __all__ = [
     "empty_factor",
     "merge",
     "reorth",
+    "fold_frozen",
     "represented",
     "stored_rows",
     "fresh_truncated_svd",
@@ -214,6 +215,17 @@ def reorth(fac: Factor) -> Factor:
     W, S, Vt = _svd(M)
     return Factor(U=QU @ W, sigma=S, B=QB @ Vt.T, pos=fac.pos.copy(), folded=fac.folded,
                   C_stale=fac.C_stale, dtype=fac.dtype)
+
+
+def fold_frozen(C: np.ndarray, B: np.ndarray, pos, F: np.ndarray, pos_F):
+    """Frozen-basis fold, the baseline of the iS-KV notes' §6.4 ablation and
+    §8: the basis B (D x k) and every stored row keep their values; the b new
+    rows are stored with their coordinates in B, F B. C holds the stored
+    coordinates (n x k). Returns the coordinates and positions after the fold.
+    """
+    C = np.asarray(C)
+    F = np.asarray(F, dtype=np.float64)
+    return np.vstack([C, F @ B]), np.concatenate([np.asarray(pos), np.asarray(pos_F)])
 
 
 def represented(fac: Factor) -> np.ndarray:

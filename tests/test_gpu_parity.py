@@ -436,6 +436,74 @@ def test_basis_only_ablation_matches_oracle(K):
         path.reorth()
 
 
+@pytest.mark.parametrize("graphs", [False, True])
+def test_merge_modes_frozen_basis_and_switches(K, graphs):
+    """Merge modes switched at run time (notes §6.4 / §8 frozen basis, §2.3
+    basis-only): frozen merges keep B and old rows bit for bit and store F B
+    (oracle fold); reorth is refused while frozen; unfreezing re-orthogonalises
+    (product kept, B orthonormal, columns orthogonal with norms sigma) and the
+    next full merge matches the oracle's merge of that state; a basis-only
+    merge keeps the old rows and matches the oracle's stale-coordinate merge."""
+    D, r, b = 256, 64, 16
+    X = synth.kv_stream(synth.StreamSpec(D=D, n=768, spectrum="exp40+0.01", noise_std=0.0, seed=21))
+    Xd = torch.from_numpy(X).to(DEV)
+    posd = torch.arange(768, dtype=torch.int32, device=DEV)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream() if graphs else None
+    path = K.IsvdPath(D=D, r_max=r, b_max=b, n_cap=768, reorth_every_rows=256, device=DEV, stream=stream,
+                      graphs=graphs)
+
+    def fold(s0, e0):
+        for s1 in range(s0, e0, b):
+            path.merge(Xd[s1:s1 + b], posd[s1:s1 + b])
+        if stream is not None:
+            stream.synchronize()
+
+    fold(0, 512)
+    C0, B0, s0, p0, st = gpu_factors(path)
+    assert st == 0 and C0.shape == (512, r)
+    # frozen basis: 8 blocks
+    path.set_mode(K.ISKV_FROZEN_BASIS)
+    fold(512, 640)
+    C1, B1, s1, p1, st = gpu_factors(path)
+    assert st == 0 and C1.shape == (640, r)
+    assert np.array_equal(B1, B0) and np.array_equal(C1[:512], C0) and np.array_equal(s1, s0)
+    Cref, pref = O.fold_frozen(C0, B0, p0, X[512:640].astype(np.float64), np.arange(512, 640))
+    assert np.array_equal(p1, pref)
+    assert rel(C1[512:], Cref[512:]) < 1e-5
+    with pytest.raises(K.IskvError):
+        path.reorth()
+    # back to the full merge: re-orthogonalised first
+    before = C1 @ B1.T
+    path.set_mode(0)
+    C2, B2, s2, _, st = gpu_factors(path)
+    assert st == 0
+    assert rel(C2 @ B2.T, before) < 1e-5
+    assert np.abs(B2.T @ B2 - np.eye(r)).max() < 1e-4
+    G = C2.T @ C2
+    assert np.abs(G - np.diag(np.diag(G))).max() < 1e-4 * G[0, 0]
+    assert np.allclose(np.sqrt(np.diag(G)), s2, rtol=1e-4)
+    fac = O.Factor(U=C2 / s2[None, :], sigma=s2, B=B2, pos=np.arange(640), folded=640)
+    fold(640, 656)
+    C3, B3, s3, _, st = gpu_factors(path)
+    ref = O.merge(fac, X[640:656].astype(np.float64), np.arange(640, 656), r)
+    assert st == 0
+    assert rel(C3 @ B3.T, O.represented(ref)) < 1e-4
+    # basis-only: old rows keep their coordinates, the new basis matches the oracle's
+    path.set_mode(K.ISKV_NO_COORD_SYNC)
+    fold(656, 672)
+    C4, B4, _, _, st = gpu_factors(path)
+    assert st == 0 and np.array_equal(C4[:656], C3)
+    fac3 = O.Factor(U=C3 / s3[None, :], sigma=s3, B=B3, pos=np.arange(656), folded=656, C_stale=C3.copy())
+    ref4 = O.merge(fac3, X[656:672].astype(np.float64), np.arange(656, 672), r)
+    assert rel(C4 @ B4.T, O.stored_rows(ref4)) < 1e-4
+    with pytest.raises(K.IskvError):
+        path.set_mode(K.ISKV_NO_COORD_SYNC | K.ISKV_FROZEN_BASIS)
+    with pytest.raises(K.IskvError):
+        path.set_mode(8)
+    path.close()
+
+
 # --------------------------------------------------------------------------- reconstruction
 def test_reconstruct_rope_and_exact_rows(K):
     """Scatter by position, exact rows, per-position RoPE (fp32 and bf16 outputs)."""

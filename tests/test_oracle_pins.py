@@ -394,3 +394,32 @@ def test_tiny_stream_fp32_tracks_fp64_and_near_fresh_svd():
     drift = O.factor_drift(X, R64, 8)
     assert 0.0 <= drift < 0.5 * rel_fresh
     assert f64.n == 256 and f64.k == 8
+
+
+# --------------------------------------------------------------------------- frozen basis
+def test_fold_frozen_pins():
+    """Frozen-basis fold (notes §6.4 / §8): rows inside span(B) are stored
+    exactly; the new coordinates are the least-squares coordinates of F in B
+    (numpy lstsq); the residual is orthogonal to B; old rows and B untouched."""
+    rng = np.random.default_rng(31)
+    D, k, n, b = 48, 7, 20, 5
+    B, _ = np.linalg.qr(rng.standard_normal((D, k)))
+    C = rng.standard_normal((n, k))
+    pos = np.arange(n)
+    # inside the span: F = Y B^T is stored exactly
+    Y = rng.standard_normal((b, k))
+    C2, pos2 = O.fold_frozen(C, B, pos, Y @ B.T, np.arange(n, n + b))
+    assert np.array_equal(C2[:n], C)
+    assert np.allclose(C2[n:], Y, atol=1e-12)
+    assert np.array_equal(pos2, np.arange(n + b))
+    assert np.allclose(C2[n:] @ B.T, Y @ B.T, atol=1e-12)
+    # a general block: least-squares coordinates, residual orthogonal to B
+    F = rng.standard_normal((b, D))
+    C3, _ = O.fold_frozen(C, B, pos, F, np.arange(100, 100 + b))
+    lsq = np.linalg.lstsq(B, F.T, rcond=None)[0].T
+    assert np.allclose(C3[n:], lsq, atol=1e-12)
+    assert np.abs((F - C3[n:] @ B.T) @ B).max() < 1e-12
+    # a non-orthonormal basis is not what the fold assumes: its F B differs from lstsq
+    B2 = B * np.linspace(1.0, 3.0, k)[None, :]
+    C4, _ = O.fold_frozen(C, B2, pos, F, np.arange(b))
+    assert not np.allclose(C4[n:], np.linalg.lstsq(B2, F.T, rcond=None)[0].T, atol=1e-6)
