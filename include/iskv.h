@@ -70,6 +70,12 @@ enum iskv_status {
                                 are and append only the new rows' coordinates
                                 F B; no residual, core solve, coordinate rewrite,
                                 basis update or re-orthogonalisation */
+#define ISKV_BF16_COORDS 8   /* persistent 2-byte factors (iS-KV notes §4.4, §7.3):
+                                the coordinates C are stored as bf16 ([n_cap x
+                                r_max] uint16, round to nearest even), every
+                                product still computed in fp32; B and sigma
+                                stay fp32. The rounding of the stored rows at
+                                each merge is the factor drift of eq.(14). */
 
 /* Output dtypes of kv_reconstruct. */
 #define ISKV_OUT_BF16 0
@@ -88,8 +94,9 @@ typedef struct iskv_config {
                                 keep residual direction j when
                                 rho_j > max(delta*s, max(D,b)*2^-23*s),
                                 s = max(sigma_1, rho_1)                                   */
-  int32_t flags;             /* ISKV_NO_COORD_SYNC | ISKV_NO_GRAPH | ISKV_FROZEN_BASIS, or 0
-                                (at most one of NO_COORD_SYNC and FROZEN_BASIS)           */
+  int32_t flags;             /* ISKV_NO_COORD_SYNC | ISKV_NO_GRAPH | ISKV_FROZEN_BASIS |
+                                ISKV_BF16_COORDS, or 0 (at most one of NO_COORD_SYNC
+                                and FROZEN_BASIS)                                          */
 } iskv_config;
 
 typedef struct isvd_handle isvd_handle;
@@ -101,7 +108,8 @@ size_t isvd_workspace_bytes(const iskv_config* cfg);
 /* Create a handle over caller-owned device buffers and reset the history to
  * empty (n = k = 0). iS-KV notes §2.2: the history is X^ = C B^T where
  * C = U diag(sigma) holds one row of coordinates per token.
- *   C         device fp32 [n_cap x r_max]: coordinates; zero-filled here.
+ *   C         device fp32 [n_cap x r_max] (bf16 under ISKV_BF16_COORDS):
+ *             coordinates; zero-filled here.
  *   sigma     device fp32 [r_max]: singular values, descending.
  *   B         device fp32 [D x r_max]: shared orthonormal basis, column j is
  *             basis vector j (row d holds feature d's k coefficients).

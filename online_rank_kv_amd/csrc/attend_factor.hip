@@ -81,15 +81,16 @@ __device__ __forceinline__ float fv_max8(float a) {
   return fmaxf(a, fv_dpp<0xb1>(a));
 }
 
-// Floats of a staged block of rows x ld floats in LDS, rounded up to whole
-// rounds of FV_THREADS lanes x 16 bytes.
-__host__ __device__ inline int fv_stage_floats(int rows, int ld) {
-  return (rows * ld + 4 * FV_THREADS - 1) / (4 * FV_THREADS) * (4 * FV_THREADS);
+// Bytes of a staged block of rows x ld elements of esz bytes in LDS, rounded
+// up to whole rounds of FV_THREADS lanes x 16 bytes.
+__host__ __device__ inline int fv_stage_bytes(int rows, int ld, int esz) {
+  return (rows * ld * esz + 16 * FV_THREADS - 1) / (16 * FV_THREADS) * (16 * FV_THREADS);
 }
 
-// Dynamic LDS of the split kernel: one compressed chunk or one exact block.
-__host__ __device__ inline int fv_split_lds_floats(int ldc, int D) {
-  const int a = fv_stage_floats(FV_CH, ldc), b = fv_stage_floats(FV_CHE, D);
+// Dynamic LDS of the split kernel: one compressed chunk (coordinates of esz
+// bytes) or one exact block (fp32).
+__host__ __device__ inline int fv_split_lds_bytes(int ldc, int esz, int D) {
+  const int a = fv_stage_bytes(FV_CH, ldc, esz), b = fv_stage_bytes(FV_CHE, D, 4);
   return a > b ? a : b;
 }
 
@@ -98,9 +99,9 @@ __host__ __device__ inline int fv_split_lds_floats(int ldc, int D) {
 // for the exact ones (acc over the head's slice). Workgroups [0, nwg_c) take
 // an even share of the compressed rows each (chunks of FV_CH), the nwg_e
 // after them an even share of the exact rows (chunks of FV_CHE).
-template <int KJ, int G>
+template <int KJ, int G, typename TC>
 __global__ __launch_bounds__(FV_THREADS) void fv_split_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ K, int n_total, const float* __restrict__ C,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ K, int n_total, const TC* __restrict__ C,
     int ldc, const int32_t* __restrict__ posc, int nc_rows, int nwg_c, const float* __restrict__ X,
     const int32_t* __restrict__ pose, int ne_rows, int nwg_e, int Hq, int Hkv, float scale,
     float* __restrict__ part_c, float* __restrict__ part_e, int* __restrict__ cnt) {
@@ -113,8 +114,9 @@ __global__ __launch_bounds__(FV_THREADS) void fv_split_kernel(
   if (blockIdx.x == 0 && t < Hq) cnt[t] = 0;  // merge arrival counters of this call
   // block geometry: rows R (ld), positions, rows per chunk, and this
   // workgroup's even share [r_begin, r_end) of the rows
-  const float* const R = exact ? X : C;
+  const char* const R = exact ? (const char*)X : (const char*)C;
   const int ld = exact ? D : ldc;
+  const int esz = exact ? 4 : (int)sizeof(TC);  // bytes per staged element
   const int32_t* const pos = exact ? pose : posc;
   const int nrows = exact ? ne_rows : nc_rows;
   const int rpc = exact ? FV_CHE : FV_CH;
@@ -128,8 +130,9 @@ __global__ __launch_bounds__(FV_THREADS) void fv_split_kernel(
   __shared__ float scs[FV_HQ];             // per-head rescale of this chunk
   __shared__ float W2[FV_CH * FV_WP];      // weights [row][head]
   extern __shared__ float4 fv_stage[];
-  float* const buf = (float*)fv_stage;
-  const int sfl = fv_stage_floats(rpc, ld);
+  float* const buf = (float*)fv_stage;  // exact rows (fp32)
+  const TC* const bufc = (const TC*)fv_stage;  // compressed rows (stored coordinates)
+  const int sbytes = fv_stage_bytes(rpc, ld, esz);
 
   // query entries of this lane's 16 features for the G heads of its KV head
   const int gq = lane >> 3, sub = lane & 7;
@@ -164,11 +167,12 @@ __global__ __launch_bounds__(FV_THREADS) void fv_split_kernel(
   auto stage = [&](int c) {
     const int r0 = r_begin + c * rpc;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(R + (size_t)r0 * ld), 0, min(rpc, r_end - r0) * ld * (int)sizeof(float), 0x00020000);
-    const int nd = sfl / (4 * FV_THREADS);
+        (void*)(R + (size_t)r0 * ld * esz), 0, min(rpc, r_end - r0) * ld * esz, 0x00020000);
+    const int nd = sbytes / (16 * FV_THREADS);
     for (int v = 0; v < nd; ++v) {
-      const int base = 256 * (FV_WAVES * v + wv);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (fv_lds_ptr)(buf + base), 16, (base + 4 * lane) * 4, 0, 0, 0);
+      const int base = 1024 * (FV_WAVES * v + wv);  // bytes
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (fv_lds_ptr)((char*)fv_stage + base), 16, base + 16 * lane, 0, 0,
+                                               0);
     }
   };
   // positions of this wave's rows (uniform: scalar loads)
@@ -301,7 +305,7 @@ __global__ __launch_bounds__(FV_THREADS) void fv_split_kernel(
         nok[tt] = n < ld;
         nb[tt] = min(n, ld - 1);
       }
-      const float* const brow0 = buf + 16 * kk * ld;
+      const TC* const brow0 = bufc + 16 * kk * ld;
       if (vr >= 16) {
         // operands of all 16 k-steps first, then the MFMA chain
         float av[16], bv[16][NT];
@@ -309,7 +313,7 @@ __global__ __launch_bounds__(FV_THREADS) void fv_split_kernel(
         for (int st = 0; st < 16; ++st) {
           av[st] = wcol[st * FV_WP];
 #pragma unroll
-          for (int tt = 0; tt < NT; ++tt) bv[st][tt] = brow0[st * ld + nb[tt]];
+          for (int tt = 0; tt < NT; ++tt) bv[st][tt] = iskv_ld(brow0 + st * ld + nb[tt]);
         }
 #pragma unroll
         for (int st = 0; st < 16; ++st)
@@ -321,7 +325,7 @@ __global__ __launch_bounds__(FV_THREADS) void fv_split_kernel(
           const float a = wcol[st * FV_WP];
 #pragma unroll
           for (int tt = 0; tt < NT; ++tt) {
-            const float b = brow0[st * ld + nb[tt]];
+            const float b = iskv_ld(brow0 + st * ld + nb[tt]);
             accm[tt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, nok[tt] ? b : 0.f, accm[tt], 0, 0, 0);
           }
         }
@@ -540,13 +544,21 @@ int iskv_launch_attend_fv(const uint16_t* q, const uint16_t* K, const isvd_handl
   float* opart = pe + (size_t)ne * Hq * (FV_DH + FV_PAD);
   int* cnt = (int*)(opart + (size_t)Hq * NSL * FV_DH);
   const int G = Hq / Hkv;
-  const size_t lds = (size_t)fv_split_lds_floats(R, D) * sizeof(float);
+  const bool c16 = iskv_bf16_coords(hv->cfg);
+  const size_t lds = (size_t)fv_split_lds_bytes(R, c16 ? 2 : 4, D);
   auto launch = [&](auto kj_c, auto g_c) -> hipError_t {
     constexpr int KJ = decltype(kj_c)::value, GG = decltype(g_c)::value;
-    const hipError_t e = fv_lds_limit(fv_split_kernel<KJ, GG>, lds);
+    auto split = [&](auto* Cp) -> hipError_t {
+      using TC = std::remove_pointer_t<decltype(Cp)>;
+      const hipError_t e = fv_lds_limit(fv_split_kernel<KJ, GG, TC>, lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((fv_split_kernel<KJ, GG, TC>), dim3(nc + ne), dim3(FV_THREADS), lds, s, q, K, n_total,
+                         (const TC*)Cp, R, hv->pos, n_c, nc, X_exact, pos_exact, n_exact, ne, Hq, Hkv, scale, pc, pe,
+                         cnt);
+      return hipSuccess;
+    };
+    const hipError_t e = c16 ? split((uint16_t*)hv->C) : split(hv->C);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((fv_split_kernel<KJ, GG>), dim3(nc + ne), dim3(FV_THREADS), lds, s, q, K, n_total, hv->C, R,
-                       hv->pos, n_c, nc, X_exact, pos_exact, n_exact, ne, Hq, Hkv, scale, pc, pe, cnt);
     hipLaunchKernelGGL((fv_merge_kernel<KJ, GG>), dim3(Hq, NSL), dim3(256), (size_t)2 * (nc + ne) * sizeof(float), s,
                        pc, nc, pe, ne, Hq, hv->B, R, hv->w.st, opart, cnt, out);
     return hipGetLastError();

@@ -25,7 +25,7 @@ bool cfg_ok(const iskv_config* c) {
   if (c->n_cap < 1) return false;
   if (c->reorth_every_rows < 0) return false;
   if (!(c->resid_rel_tol >= 0.f)) return false;
-  if (c->flags & ~(ISKV_NO_COORD_SYNC | ISKV_NO_GRAPH | ISKV_FROZEN_BASIS)) return false;
+  if (c->flags & ~(ISKV_NO_COORD_SYNC | ISKV_NO_GRAPH | ISKV_FROZEN_BASIS | ISKV_BF16_COORDS)) return false;
   if ((c->flags & ISKV_NO_COORD_SYNC) && (c->flags & ISKV_FROZEN_BASIS)) return false;
   return true;
 }
@@ -127,7 +127,7 @@ int isvd_init(isvd_handle** out, const iskv_config* cfg, float* C, float* sigma,
   hipStream_t s = h->stream;
   const size_t R = cfg->r_max;
   if (hipMemsetAsync(h->w.st, 0, ST_COUNT * sizeof(int32_t), s) != hipSuccess ||
-      hipMemsetAsync(C, 0, (size_t)cfg->n_cap * R * sizeof(float), s) != hipSuccess ||
+      hipMemsetAsync(C, 0, (size_t)cfg->n_cap * R * (iskv_bf16_coords(*cfg) ? 2 : 4), s) != hipSuccess ||
       hipMemsetAsync(sigma, 0, R * sizeof(float), s) != hipSuccess ||
       hipMemsetAsync(B, 0, (size_t)cfg->D * R * sizeof(float), s) != hipSuccess ||
       hipMemsetAsync(h->w.Bbf, 0, (size_t)cfg->D * R * 2, s) != hipSuccess ||
@@ -336,6 +336,7 @@ int decode_attend_fv(const uint16_t* q, const uint16_t* K, const isvd_handle* hv
   if (G != 1 && G != 2 && G != 4) return ISKV_EINVAL;
   if (hv->cfg.D != Hkv * 128 || hv->cfg.D > 1024) return ISKV_EINVAL;
   if (hv->cfg.r_max % 4 != 0 || hv->cfg.r_max > 448) return ISKV_EINVAL;  // a chunk of rows fits in LDS
+  if (iskv_bf16_coords(hv->cfg) && hv->cfg.r_max % 8 != 0) return ISKV_EINVAL;  // 16-byte aligned 2-byte rows
   if (hv->n_host + n_exact < 1) return ISKV_EINVAL;
   if (ws_bytes < iskv_attend_fv_ws_bytes(hv->n_host, n_exact, Hq, hv->cfg.r_max)) return ISKV_EWORKSPACE;
   return iskv_launch_attend_fv(q, K, hv, X_exact, pos_exact, n_exact, n_total, Hq, Hkv, scale, out, workspace,

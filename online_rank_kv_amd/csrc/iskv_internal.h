@@ -181,6 +181,20 @@ int iskv_upload_offsets(isvd_handle* const* hs, int32_t count);
 int iskv_launch_copy_pos_host(int32_t* pos_dev, const int32_t* pos_host, int32_t count,
                               hipStream_t s);
 
+// Stored coordinates: fp32, or bf16 (uint16 bits) under ISKV_BF16_COORDS.
+// Loads widen to fp32; stores round to nearest even (NaN stays NaN).
+__device__ __forceinline__ float iskv_ld(const float* p) { return *p; }
+__device__ __forceinline__ float iskv_ld(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
+__device__ __forceinline__ uint16_t iskv_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ void iskv_st(float* p, float v) { *p = v; }
+__device__ __forceinline__ void iskv_st(uint16_t* p, float v) { *p = iskv_to_bf16(v); }
+inline bool iskv_bf16_coords(const iskv_config& c) { return (c.flags & ISKV_BF16_COORDS) != 0; }
+
 // Batched launches: z copies of a grid, and the per-copy pointer rebase.
 inline dim3 bz(dim3 g, int count) { return dim3(g.x, g.y, (unsigned)count); }
 template <class T>

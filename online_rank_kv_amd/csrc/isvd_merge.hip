@@ -18,6 +18,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <type_traits>
 
 namespace {
 
@@ -610,11 +611,11 @@ static inline size_t xh_lds_bytes(int bm, int kin_max) {
   return ((size_t)bm * xh_ldx(kin_max) + (size_t)XH_KC * XH_HS) * sizeof(float);
 }
 
-template <int BM>
-__global__ __launch_bounds__(256) void xh_mfma_kernel(const float* X1, int ld1, const float* X2, int ld2,
+template <int BM, typename TX, typename TY>
+__global__ __launch_bounds__(256) void xh_mfma_kernel(const TX* X1, int ld1, const float* X2, int ld2,
                                                       Dim k1_d, Dim kin_d, const float* __restrict__ H,
                                                       int ldh, int hcols, Dim kout_d, Dim rows_d,
-                                                      float* Y, int ldy, uint16_t* Ybf, int ldbf,
+                                                      TY* Y, int ldy, uint16_t* Ybf, int ldbf,
                                                       int ldx, int32_t* pos, const int32_t* pos_src,
                                                       Dim yoff_d,
     const int64_t* __restrict__ bd) {
@@ -651,7 +652,7 @@ __global__ __launch_bounds__(256) void xh_mfma_kernel(const float* X1, int ld1, 
         int rc = min(r, nr - 1);
         float v = 0.f;
         if (e < BM * kin4 && c < kin)
-          v = c < k1 ? X1[(size_t)(i0 + rc) * ld1 + c] : X2[(size_t)(i0 + rc) * ld2 + (c - k1)];
+          v = c < k1 ? iskv_ld(X1 + (size_t)(i0 + rc) * ld1 + c) : X2[(size_t)(i0 + rc) * ld2 + (c - k1)];
         xv[u] = (r < nr) ? v : 0.f;
       }
 #pragma unroll
@@ -714,7 +715,7 @@ __global__ __launch_bounds__(256) void xh_mfma_kernel(const float* X1, int ld1, 
         for (int e = 0; e < 4; ++e) {
           const int r = a * 16 + 4 * (lane >> 4) + e;
           if (r < nr && j < kout) {
-            Y[(size_t)(yo + i0 + r) * ldy + j] = acc[a][b][e];
+            iskv_st(Y + (size_t)(yo + i0 + r) * ldy + j, acc[a][b][e]);
             if (Ybf) Ybf[(size_t)(yo + i0 + r) * ldbf + j] = f2bf(acc[a][b][e]);
           }
         }
@@ -731,10 +732,10 @@ __global__ __launch_bounds__(256) void xh_mfma_kernel(const float* X1, int ld1, 
 // before any of its outputs is written, so in-place use stays safe.
 constexpr int XR_LDX = 292; // LDS row stride (floats) of a staged X block
 
-template <int XR_KS>  // k steps of 4 held per lane: kin <= 4 XR_KS
-__global__ __launch_bounds__(1024) void xh_reg_kernel(const float* X1, int ld1, const float* X2, int ld2,
+template <int XR_KS, typename TX, typename TY>  // k steps of 4 held per lane: kin <= 4 XR_KS
+__global__ __launch_bounds__(1024) void xh_reg_kernel(const TX* X1, int ld1, const float* X2, int ld2,
                                                       Dim k1_d, Dim kin_d, const float* __restrict__ H,
-                                                      int ldh, int hcols, Dim kout_d, Dim rows_d, float* Y,
+                                                      int ldh, int hcols, Dim kout_d, Dim rows_d, TY* Y,
                                                       int ldy, uint16_t* Ybf, int ldbf, int32_t* pos,
                                                       const int32_t* pos_src, Dim yoff_d,
     const int64_t* __restrict__ bd) {
@@ -780,9 +781,13 @@ __global__ __launch_bounds__(1024) void xh_reg_kernel(const float* X1, int ld1, 
     for (int u = 0; u < PER; ++u) {
       const int e = min(t + 1024 * u, 16 * KW - 1), r = e / KW, c = e % KW;
       const int row = min(i0 + r, rows - 1);
-      const float* src = c < k1 ? X1 + (size_t)row * ld1 + c
-                                : (c < kin ? X2 + (size_t)row * ld2 + (c - k1) : X1 + (size_t)row * ld1);
-      xr[u] = *src;
+      if constexpr (std::is_same<TX, float>::value) {
+        const float* src = c < k1 ? X1 + (size_t)row * ld1 + c
+                                  : (c < kin ? X2 + (size_t)row * ld2 + (c - k1) : X1 + (size_t)row * ld1);
+        xr[u] = *src;
+      } else {  // 2-byte rows are only ever the whole input (k1 = kin)
+        xr[u] = iskv_ld(X1 + (size_t)row * ld1 + min(c, k1 - 1));
+      }
     }
   };
   load_x(blockIdx.x);
@@ -807,7 +812,7 @@ __global__ __launch_bounds__(1024) void xh_reg_kernel(const float* X1, int ld1, 
       for (int e = 0; e < 4; ++e) {
         const int row = i0 + 4 * (lane >> 4) + e;
         if (row < rows) {
-          Y[(size_t)(yo + row) * ldy + col] = acc[e];
+          iskv_st(Y + (size_t)(yo + row) * ldy + col, acc[e]);
           if (Ybf) Ybf[(size_t)(yo + row) * ldbf + col] = f2bf(acc[e]);
         }
       }
@@ -819,9 +824,10 @@ __global__ __launch_bounds__(1024) void xh_reg_kernel(const float* X1, int ld1, 
 
 // Launch Y = [X1 | X2] H over `rows_host` rows (an upper bound when rows_d is
 // a device value); kin_max bounds kin for the LDS layout.
-static void xh_launch(hipStream_t s, const int64_t* bd, int bc, int rows_host, const float* X1, int ld1, const float* X2, int ld2,
+template <typename TX, typename TY>
+static void xh_launch(hipStream_t s, const int64_t* bd, int bc, int rows_host, const TX* X1, int ld1, const float* X2, int ld2,
                       Dim k1, Dim kin, int kin_max, const float* H, int ldh, int hcols, Dim kout,
-                      Dim rows, float* Y, int ldy, uint16_t* Ybf, int ldbf, int32_t* pos = nullptr,
+                      Dim rows, TY* Y, int ldy, uint16_t* Ybf, int ldbf, int32_t* pos = nullptr,
                       const int32_t* pos_src = nullptr, bool prefer16 = false, Dim yoff = hdim(0)) {
   const int ldx = xh_ldx(kin_max);
   if (kin_max <= 288 && hcols <= 256) {
@@ -829,20 +835,20 @@ static void xh_launch(hipStream_t s, const int64_t* bd, int bc, int rows_host, c
     const int grid = nblk < 256 ? nblk : 256;
     if (grid > 0) {
       if (kin_max <= 256)
-        hipLaunchKernelGGL(xh_reg_kernel<64>, bz(dim3(grid), bc), dim3(1024), 0, s, X1, ld1, X2, ld2, k1, kin, H,
+        hipLaunchKernelGGL((xh_reg_kernel<64, TX, TY>), bz(dim3(grid), bc), dim3(1024), 0, s, X1, ld1, X2, ld2, k1, kin, H,
                            ldh, hcols, kout, rows, Y, ldy, Ybf, ldbf, pos, pos_src, yoff, bd);
       else
-        hipLaunchKernelGGL(xh_reg_kernel<72>, bz(dim3(grid), bc), dim3(1024), 0, s, X1, ld1, X2, ld2, k1, kin, H,
+        hipLaunchKernelGGL((xh_reg_kernel<72, TX, TY>), bz(dim3(grid), bc), dim3(1024), 0, s, X1, ld1, X2, ld2, k1, kin, H,
                            ldh, hcols, kout, rows, Y, ldy, Ybf, ldbf, pos, pos_src, yoff, bd);
     }
     return;
   }
   if (!prefer16 && xh_lds_bytes(32, kin_max) <= 80 * 1024) {
-    hipLaunchKernelGGL(xh_mfma_kernel<32>, bz(dim3((rows_host + 31) / 32), bc), dim3(256),
+    hipLaunchKernelGGL((xh_mfma_kernel<32, TX, TY>), bz(dim3((rows_host + 31) / 32), bc), dim3(256),
                        xh_lds_bytes(32, kin_max), s, X1, ld1, X2, ld2, k1, kin, H, ldh, hcols, kout,
                        rows, Y, ldy, Ybf, ldbf, ldx, pos, pos_src, yoff, bd);
   } else {
-    hipLaunchKernelGGL(xh_mfma_kernel<16>, bz(dim3((rows_host + 15) / 16), bc), dim3(256),
+    hipLaunchKernelGGL((xh_mfma_kernel<16, TX, TY>), bz(dim3((rows_host + 15) / 16), bc), dim3(256),
                        xh_lds_bytes(16, kin_max), s, X1, ld1, X2, ld2, k1, kin, H, ldh, hcols, kout,
                        rows, Y, ldy, Ybf, ldbf, ldx, pos, pos_src, yoff, bd);
   }
@@ -870,8 +876,9 @@ __global__ void merge_commit_kernel(float* sigma, const float* __restrict__ sig_
 // coordinates Q = F B (b x k, columns past k zero) and positions at row n,
 // then n += b. One workgroup per path: every thread reads n before thread 0
 // advances it. Non-finite coordinates are latched like the full merge's input.
+template <typename TC>
 __global__ __launch_bounds__(256) void frozen_append_kernel(const float* __restrict__ Q, int ldq,
-                                                            const int32_t* __restrict__ pos_F, int b, float* C,
+                                                            const int32_t* __restrict__ pos_F, int b, TC* C,
                                                             int ldc, int32_t* pos, int32_t* st,
                                                             const int64_t* __restrict__ bd) {
   const int64_t d = bd ? bd[blockIdx.z] : 0;
@@ -886,7 +893,7 @@ __global__ __launch_bounds__(256) void frozen_append_kernel(const float* __restr
     const int i = e / ldc, j = e % ldc;
     const float v = j < k ? Q[(size_t)i * ldq + j] : 0.f;
     bad |= !isfinite(v);
-    C[(size_t)(n + i) * ldc + j] = v;
+    iskv_st(C + (size_t)(n + i) * ldc + j, v);
   }
   for (int i = threadIdx.x; i < b; i += blockDim.x) pos[n + i] = pos_F[i];
   if (bad) atomicOr(&st[ST_STATUS], ISKV_DEV_NONFINITE);
@@ -910,7 +917,8 @@ __global__ void set_jm_kernel(int32_t* st, int from_slot,
 // Partial Gram of the columns of X (rows x k, fp32) over a row chunk, fp64:
 // G_part[s][i][j] = sum_{rows in chunk s} X[r, i] X[r, j]. Grid: (tiles of
 // 16x16 over k x k, chunks). 256 threads.
-__global__ __launch_bounds__(256) void gram_partial_kernel(const float* __restrict__ X, int ldx,
+template <typename TX>
+__global__ __launch_bounds__(256) void gram_partial_kernel(const TX* __restrict__ X, int ldx,
                                                            Dim rows_d, const int32_t* st,
                                                            double* Gpart, int ldg,
                                                            int rows_per_chunk,
@@ -934,8 +942,8 @@ __global__ __launch_bounds__(256) void gram_partial_kernel(const float* __restri
       int rr = idx >> 4, cc = idx & 15;
       int row = rb + rr;
       int ci = ti * 16 + cc, cj = tj * 16 + cc;
-      Xi[rr][cc] = (row < r1 && ci < k) ? X[(size_t)row * ldx + ci] : 0.f;
-      Xj[rr][cc] = (row < r1 && cj < k) ? X[(size_t)row * ldx + cj] : 0.f;
+      Xi[rr][cc] = (row < r1 && ci < k) ? iskv_ld(X + (size_t)row * ldx + ci) : 0.f;
+      Xj[rr][cc] = (row < r1 && cj < k) ? iskv_ld(X + (size_t)row * ldx + cj) : 0.f;
     }
     __syncthreads();
     for (int rr = 0; rr < 64; ++rr)
@@ -1172,10 +1180,12 @@ int iskv_kernel_setup() {
   ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)resid_basis_kernel<32>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)resid_lds_bytes(32)));
-  ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)xh_mfma_kernel<32>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds));
-  ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)xh_mfma_kernel<16>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds));
+  const void* xh[] = {(const void*)xh_mfma_kernel<32, float, float>, (const void*)xh_mfma_kernel<16, float, float>,
+                      (const void*)xh_mfma_kernel<32, uint16_t, uint16_t>,
+                      (const void*)xh_mfma_kernel<16, uint16_t, uint16_t>,
+                      (const void*)xh_mfma_kernel<32, float, uint16_t>,
+                      (const void*)xh_mfma_kernel<16, float, uint16_t>};
+  for (const void* f : xh) ISKV_HIP_CHECK(hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds));
   if (iskv_core_eig_setup() != ISKV_OK) return ISKV_EHIP;
   done = 1;
   return ISKV_OK;
@@ -1184,6 +1194,13 @@ int iskv_kernel_setup() {
 // The launch sequence of one merge. It depends on the host only through b
 // and the handle's fixed buffers: the row count n is read on the device, so
 // the sequence can be recorded once and replayed.
+// Run f with the handle's coordinate array typed as stored (fp32 or bf16 bits).
+template <class Fn>
+static void with_coords(isvd_handle* h, Fn f) {
+  if (iskv_bf16_coords(h->cfg)) f((uint16_t*)h->C);
+  else f(h->C);
+}
+
 static int merge_body(isvd_handle* h, const float* F, const int32_t* pos_F, int32_t b) {
   const iskv_config& c = h->cfg;
   const isvd_ws& w = h->w;
@@ -1199,8 +1216,11 @@ static int merge_body(isvd_handle* h, const float* F, const int32_t* pos_F, int3
   skinny<false>(h, b, R, F, D, h->B, R, ddim(dk), D, 1.f, 0.f, nullptr, 0, w.Q, R);
   if (c.flags & ISKV_FROZEN_BASIS) {
     // frozen basis: the new rows keep their coordinates in B; nothing else changes
-    hipLaunchKernelGGL(frozen_append_kernel, bz(dim3(1), h->bcount), dim3(256), 0, s, w.Q, R, pos_F, b, h->C, R,
-                       h->pos, w.st, h->bd);
+    with_coords(h, [&](auto* Cp) {
+      using TC = std::remove_pointer_t<decltype(Cp)>;
+      hipLaunchKernelGGL((frozen_append_kernel<TC>), bz(dim3(1), h->bcount), dim3(256), 0, s, w.Q, R, pos_F, b, Cp,
+                         R, h->pos, w.st, h->bd);
+    });
     for (int i = 1; i <= 5; ++i) mark(i);
     if (h->timing) h->timed = true;
     ISKV_HIP_CHECK(hipGetLastError());
@@ -1242,12 +1262,14 @@ static int merge_body(isvd_handle* h, const float* F, const int32_t* pos_F, int3
   // appended at row n, basis update
   const int M = h->m_max;
   const Dim dn = ddim(w.st + ST_N);
-  if (!(c.flags & ISKV_NO_COORD_SYNC))
-    xh_launch(s, h->bd, h->bcount, c.n_cap, h->C, R, nullptr, 0, ddim(dk), ddim(dk), R, w.Hc, R, R, ddim(w.st + ST_KNEW),
-              dn, h->C, R, nullptr, 0);
-  mark(4);
-  xh_launch(s, h->bd, h->bcount, b, w.Q, R, w.FP, c.b_max, ddim(dk), ddim(w.st + ST_M), M, w.Hc, R, R,
-            ddim(w.st + ST_KNEW), hdim(b), h->C, R, nullptr, 0, h->pos, pos_F, false, dn);
+  with_coords(h, [&](auto* Cp) {
+    if (!(c.flags & ISKV_NO_COORD_SYNC))
+      xh_launch(s, h->bd, h->bcount, c.n_cap, Cp, R, nullptr, 0, ddim(dk), ddim(dk), R, w.Hc, R, R,
+                ddim(w.st + ST_KNEW), dn, Cp, R, nullptr, 0);
+    mark(4);
+    xh_launch(s, h->bd, h->bcount, b, w.Q, R, w.FP, c.b_max, ddim(dk), ddim(w.st + ST_M), M, w.Hc, R, R,
+              ddim(w.st + ST_KNEW), hdim(b), Cp, R, nullptr, 0, h->pos, pos_F, false, dn);
+  });
   xh_launch(s, h->bd, h->bcount, D, h->B, R, w.P, c.b_max, ddim(dk), ddim(w.st + ST_M), M, w.Hc, R, R,
             ddim(w.st + ST_KNEW), hdim(D), h->B, R, w.Bbf, R, nullptr, nullptr, true);
   hipLaunchKernelGGL(merge_commit_kernel, bz(dim3(1), h->bcount), dim3(256), 0, s, h->sigma, w.sig_new, w.st, b, R, h->bd);
@@ -1279,9 +1301,12 @@ static int reorth_body(isvd_handle* h) {
   const int rpc = (ncap + nchunks - 1) / nchunks;
   const Dim dn = ddim(w.st + ST_N);
   hipLaunchKernelGGL(set_jm_kernel, bz(dim3(1), h->bcount), dim3(1), 0, s, w.st, (int)ST_K, h->bd);
-  hipLaunchKernelGGL(gram_partial_kernel, bz(dim3(tiles * tiles, nchunks), h->bcount), dim3(256), 0, s, h->C, R, dn,
-                     w.st, w.GC, R, rpc, h->bd);
-  hipLaunchKernelGGL(gram_partial_kernel, bz(dim3(tiles * tiles, 1), h->bcount), dim3(256), 0, s, h->B, R, hdim(D), w.st,
+  with_coords(h, [&](auto* Cp) {
+    using TC = std::remove_pointer_t<decltype(Cp)>;
+    hipLaunchKernelGGL((gram_partial_kernel<TC>), bz(dim3(tiles * tiles, nchunks), h->bcount), dim3(256), 0, s,
+                       (const TC*)Cp, R, dn, w.st, w.GC, R, rpc, h->bd);
+  });
+  hipLaunchKernelGGL(gram_partial_kernel<float>, bz(dim3(tiles * tiles, 1), h->bcount), dim3(256), 0, s, h->B, R, hdim(D), w.st,
                      w.GC + (size_t)nchunks * R * R, R, D, h->bd);
   hipLaunchKernelGGL(reorth_sum_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.GC, nchunks, R, w.Km, w.Pa, w.Pb,
                      ld, w.st, h->bd);
@@ -1304,8 +1329,10 @@ static int reorth_body(isvd_handle* h) {
   iskv_dgemm(s, mm, w.MB, true, w.W1, false, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 2, h->bd, h->bcount);
   iskv_dgemm(s, mm, w.Zb, false, w.W1, false, w.Pa, nullptr, ld, 1.0, 0.0, 0.0, st, 2, h->bd, h->bcount);
   hipLaunchKernelGGL(to_f32_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.T, w.Pa, ld, w.Hc, w.T2, R, w.st, h->bd);
-  xh_launch(s, h->bd, h->bcount, ncap, h->C, R, nullptr, 0, ddim(w.st + ST_K), ddim(w.st + ST_K), R, w.Hc, R, R,
-            ddim(w.st + ST_K), dn, h->C, R, nullptr, 0);
+  with_coords(h, [&](auto* Cp) {
+    xh_launch(s, h->bd, h->bcount, ncap, Cp, R, nullptr, 0, ddim(w.st + ST_K), ddim(w.st + ST_K), R, w.Hc, R, R,
+              ddim(w.st + ST_K), dn, Cp, R, nullptr, 0);
+  });
   xh_launch(s, h->bd, h->bcount, D, h->B, R, nullptr, 0, ddim(w.st + ST_K), ddim(w.st + ST_K), R, w.T2, R, R,
             ddim(w.st + ST_K), hdim(D), h->B, R, w.Bbf, R, nullptr, nullptr, true);
   hipLaunchKernelGGL(reorth_commit_kernel, bz(dim3(1), h->bcount), dim3(256), 0, s, h->sigma, w.sig_new, w.st, R, h->bd);

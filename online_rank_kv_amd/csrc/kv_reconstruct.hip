@@ -55,6 +55,15 @@ __device__ __forceinline__ float rope_rev(uint32_t p, uint64_t F) {
   return (float)(int32_t)top * 2.3283064365386963e-10f;  // * 2^-32
 }
 
+// Four consecutive stored coordinates as fp32 (fp32 rows, or bf16 rows under
+// 2-byte persistence; the bf16 load needs 8-byte alignment).
+__device__ __forceinline__ float4 ld_c4(const float* p) { return *(const float4*)p; }
+__device__ __forceinline__ float4 ld_c4(const uint16_t* p) {
+  const uint2 v = *(const uint2*)p;
+  return float4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y << 16),
+                __uint_as_float(v.y & 0xffff0000u)};
+}
+
 // Column tile of W (128 or 64) features; rotary pair q (0 .. W/2-1) of the
 // tile is (lo, lo + dh/2) with lo = (q / (dh/2)) * dh + q % (dh/2).
 // Requires W % dh == 0.
@@ -66,8 +75,8 @@ __device__ __forceinline__ int pair_lo(int q, int dh) {
 // Compressed rows: out[pos[i], tile] = RoPE(C[i, :k] B[tile, :k]^T).
 // Grid (D / W, ceil(n / 32)); 256 threads; thread owns 4 rows x 2 pairs
 // (one pair when W == 64).
-template <bool BF16>
-__global__ __launch_bounds__(256) void recon_kernel(const float* __restrict__ C, int ldc,
+template <bool BF16, typename TC>
+__global__ __launch_bounds__(256) void recon_kernel(const TC* __restrict__ C, int ldc,
                                                     const float* __restrict__ B, int ldb,
                                                     const int32_t* __restrict__ pos,
                                                     const int32_t* __restrict__ st, int n, int D,
@@ -90,7 +99,7 @@ __global__ __launch_bounds__(256) void recon_kernel(const float* __restrict__ C,
   for (int k0 = 0; k0 < k; k0 += 32) {
     for (int idx = t; idx < 32 * 32; idx += 256) {
       int r = idx >> 5, c = idx & 31;
-      Cs[r][c] = (i0 + r < n && k0 + c < k) ? C[(size_t)(i0 + r) * ldc + k0 + c] : 0.f;
+      Cs[r][c] = (i0 + r < n && k0 + c < k) ? iskv_ld(C + (size_t)(i0 + r) * ldc + k0 + c) : 0.f;
     }
     for (int idx = t; idx < W * 32; idx += 256) {
       int r = idx >> 5, c = idx & 31;
@@ -158,7 +167,8 @@ constexpr int RM_OS = RM_BN + 8;    // LDS row stride (bf16) of the output tile
 constexpr int RM_LDS = (RM_BM + RM_BN) * RM_RS;  // bf16 elements
 static_assert(RM_BM * RM_OS <= RM_LDS, "output tile must fit in the staging area");
 
-__global__ __launch_bounds__(256) void recon_mfma_kernel(const float* __restrict__ C, int ldc,
+template <typename TC>
+__global__ __launch_bounds__(256) void recon_mfma_kernel(const TC* __restrict__ C, int ldc,
                                                          const uint16_t* __restrict__ Bbf, int ldb,
                                                          const int32_t* __restrict__ pos,
                                                          const int32_t* __restrict__ st, int n,
@@ -203,7 +213,7 @@ __global__ __launch_bounds__(256) void recon_mfma_kernel(const float* __restrict
     for (int u = 0; u < 4; ++u) {
       int e = t + 256 * u, r = e >> 4, col = k0 + (e & 15) * 4;
       int row = min(i0 + r, n - 1), colc = min(col, ldc - 4);
-      cv[u] = *(const float4*)(C + (size_t)row * ldc + colc);
+      cv[u] = ld_c4(C + (size_t)row * ldc + colc);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -311,7 +321,8 @@ constexpr int RS_BM = 32;            // rows per block
 constexpr int RS_CS = 256 + 8;       // LDS row stride (bf16) of a staged C block
 constexpr int RS_OS = 128 + 8;       // LDS row stride (bf16) of the output block
 
-__global__ __launch_bounds__(256) void recon_stream_kernel(const float* __restrict__ C, int ldc,
+template <typename TC>
+__global__ __launch_bounds__(256) void recon_stream_kernel(const TC* __restrict__ C, int ldc,
                                                            const uint16_t* __restrict__ Bbf, int ldb,
                                                            const int32_t* __restrict__ pos,
                                                            const int32_t* __restrict__ st, int n, int D,
@@ -371,15 +382,23 @@ __global__ __launch_bounds__(256) void recon_stream_kernel(const float* __restri
   // bounded by the last row n - 1: rows past n read as zero, and the per-load
   // offsets are fixed (row t / 64 + 4 u, column 4 (t % 64)), so no address
   // arithmetic runs per block.
-  const uint32_t voff0 = (uint32_t)(((t >> 6) * ldc + (t & 63) * 4) * 4);
-  const uint32_t vstep = (uint32_t)(4 * ldc * 4);
+  constexpr int ES = (int)sizeof(TC);  // bytes per stored coordinate
+  const uint32_t voff0 = (uint32_t)(((t >> 6) * ldc + (t & 63) * 4) * ES);
+  const uint32_t vstep = (uint32_t)(4 * ldc * ES);
   auto load_c = [&](int slot, int blk) {
     const int i0 = blk * RS_BM;
     const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(C + (size_t)i0 * ldc), (short)0, (int)((n - i0) * ldc * 4), 0x00020000);
+        (void*)(C + (size_t)i0 * ldc), (short)0, (int)((n - i0) * ldc * ES), 0x00020000);
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      creg[slot][u] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rc, voff0 + u * vstep, 0, 0));
+    for (int u = 0; u < 8; ++u) {
+      if constexpr (ES == 4) {
+        creg[slot][u] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rc, voff0 + u * vstep, 0, 0));
+      } else {
+        const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rc, voff0 + u * vstep, 0, 0));
+        creg[slot][u] = float4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                               __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
+      }
+    }
     preg[slot] = pos[min(i0 + (t & 31), n - 1)];
   };
   auto store_c = [&](int slot, uint16_t* cs, int* ps, int blk) {
@@ -542,24 +561,31 @@ int iskv_launch_reconstruct(const isvd_handle* h, const float* X_exact, const in
     const bool mfma = bf && D % RM_BN == 0 && head_dim % 32 == 0 && RM_BN % head_dim == 0 &&
                       R % 8 == 0;
     // (the streaming kernel's buffer descriptors bound C in 32-bit bytes)
-    if (mfma && R % 32 == 0 && R <= 256 && (size_t)n * R * 4 < ((size_t)1 << 31)) {
-      const int T = D / 128;
-      const int G = T >= 64 ? 1 : 64 / T;  // 512 workgroups when T divides 64
-      hipLaunchKernelGGL(recon_stream_kernel, dim3(8 * T * G), dim3(256), 0, s, h->C, R, h->w.Bbf, R,
-                         h->pos, h->w.st, n, D, head_dim, apply_rope, lt, (uint16_t*)out, n_total, T,
-                         8 * G);
-    } else if (mfma) {
-      const int tiles = D / RM_BN, nrb = (n + RM_BM - 1) / RM_BM;
-      const int nwg = (nrb + 7) / 8 * 8 * tiles;
-      hipLaunchKernelGGL(recon_mfma_kernel, dim3(nwg), dim3(256), 0, s, h->C, R, h->w.Bbf, R,
-                         h->pos, h->w.st, n, D, head_dim, apply_rope, lt, (uint16_t*)out, n_total,
-                         tiles);
-    } else if (bf)
-      hipLaunchKernelGGL(recon_kernel<true>, grid, dim3(256), 0, s, h->C, R, h->B, R, h->pos,
-                         h->w.st, n, D, head_dim, W, apply_rope, lt, out, n_total);
-    else
-      hipLaunchKernelGGL(recon_kernel<false>, grid, dim3(256), 0, s, h->C, R, h->B, R, h->pos,
-                         h->w.st, n, D, head_dim, W, apply_rope, lt, out, n_total);
+    auto go = [&](auto* Cp) {
+      using TC = std::remove_pointer_t<decltype(Cp)>;
+      const TC* Cc = Cp;
+      if (mfma && R % 32 == 0 && R <= 256 && (size_t)n * R * sizeof(TC) < ((size_t)1 << 31)) {
+        const int T = D / 128;
+        const int G = T >= 64 ? 1 : 64 / T;  // 512 workgroups when T divides 64
+        hipLaunchKernelGGL((recon_stream_kernel<TC>), dim3(8 * T * G), dim3(256), 0, s, Cc, R, h->w.Bbf, R,
+                           h->pos, h->w.st, n, D, head_dim, apply_rope, lt, (uint16_t*)out, n_total, T,
+                           8 * G);
+      } else if (mfma) {
+        const int tiles = D / RM_BN, nrb = (n + RM_BM - 1) / RM_BM;
+        const int nwg = (nrb + 7) / 8 * 8 * tiles;
+        hipLaunchKernelGGL((recon_mfma_kernel<TC>), dim3(nwg), dim3(256), 0, s, Cc, R, h->w.Bbf, R,
+                           h->pos, h->w.st, n, D, head_dim, apply_rope, lt, (uint16_t*)out, n_total,
+                           tiles);
+      } else if (bf) {
+        hipLaunchKernelGGL((recon_kernel<true, TC>), grid, dim3(256), 0, s, Cc, R, h->B, R, h->pos,
+                           h->w.st, n, D, head_dim, W, apply_rope, lt, out, n_total);
+      } else {
+        hipLaunchKernelGGL((recon_kernel<false, TC>), grid, dim3(256), 0, s, Cc, R, h->B, R, h->pos,
+                           h->w.st, n, D, head_dim, W, apply_rope, lt, out, n_total);
+      }
+    };
+    if (iskv_bf16_coords(h->cfg)) go((uint16_t*)h->C);
+    else go(h->C);
   }
   if (n_exact > 0) {
     if (bf)

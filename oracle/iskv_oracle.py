@@ -33,6 +33,7 @@ __all__ = [
     "merge",
     "reorth",
     "fold_frozen",
+    "persist_coords_bf16",
     "represented",
     "stored_rows",
     "fresh_truncated_svd",
@@ -214,6 +215,20 @@ def reorth(fac: Factor) -> Factor:
     M = RU @ np.diag(fac.sigma) @ RB.T
     W, S, Vt = _svd(M)
     return Factor(U=QU @ W, sigma=S, B=QB @ Vt.T, pos=fac.pos.copy(), folded=fac.folded,
+                  C_stale=fac.C_stale, dtype=fac.dtype)
+
+
+def persist_coords_bf16(fac: Factor) -> Factor:
+    """Persistent 2-byte factors (iS-KV notes §7.3, with fp32 compute): the
+    stored coordinates C = U diag(sigma) are rounded to bfloat16 whenever they
+    are written; sigma and B keep full precision. Returns the factor whose
+    U diag(sigma) equals the rounded C (columns with sigma = 0 stay zero)."""
+    if fac.k == 0 or fac.n == 0:
+        return fac
+    C = bf16_round(fac.U * fac.sigma[None, :])
+    safe = np.where(fac.sigma > 0, fac.sigma, 1.0)
+    U = np.where(fac.sigma[None, :] > 0, C / safe[None, :], 0.0)
+    return Factor(U=U, sigma=fac.sigma.copy(), B=fac.B.copy(), pos=fac.pos.copy(), folded=fac.folded,
                   C_stale=fac.C_stale, dtype=fac.dtype)
 
 
@@ -442,12 +457,14 @@ def one_step_drift(fac: Factor, F, pos_F, r: int, delta: float = 0.0):
 
 def run_stream(X: np.ndarray, b: int, r: int, reorth_every_rows: int = 0, delta: float = 0.0,
                dtype=np.float64, sync: bool = True, pos0: int = 0, fac: Factor | None = None,
-               callback=None) -> Factor:
+               callback=None, persist_bf16: bool = False) -> Factor:
     """Fold the rows of X block by block (b rows each), in order.
 
     Re-orthogonalises whenever the folded-row counter reaches a multiple of
     ``reorth_every_rows`` (iS-KV notes §4.4; 0 disables it). ``callback`` is
-    called after every merge with (merge index, factor).
+    called after every merge with (merge index, factor). ``persist_bf16``
+    rounds the stored coordinates to bfloat16 after every merge and
+    re-orthogonalisation (persistent 2-byte factors, §7.3).
     """
     X = np.asarray(X)
     n = X.shape[0]
@@ -458,8 +475,12 @@ def run_stream(X: np.ndarray, b: int, r: int, reorth_every_rows: int = 0, delta:
         pos_F = np.arange(pos0 + s, pos0 + s + F.shape[0])
         before = fac.folded
         fac = merge(fac, F, pos_F, r, delta)
+        if persist_bf16:
+            fac = persist_coords_bf16(fac)
         if reorth_every_rows and sync and (fac.folded // reorth_every_rows) > (before // reorth_every_rows):
             fac = reorth(fac)
+            if persist_bf16:
+                fac = persist_coords_bf16(fac)
         if callback is not None:
             callback(t, fac)
     return fac

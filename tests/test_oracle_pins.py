@@ -423,3 +423,30 @@ def test_fold_frozen_pins():
     B2 = B * np.linspace(1.0, 3.0, k)[None, :]
     C4, _ = O.fold_frozen(C, B2, pos, F, np.arange(b))
     assert not np.allclose(C4[n:], np.linalg.lstsq(B2, F.T, rcond=None)[0].T, atol=1e-6)
+
+
+# --------------------------------------------------------------------------- 2-byte persistence
+def test_persist_coords_bf16_pins():
+    """Persistent 2-byte coordinates (notes §7.3): the stored C = U diag(sigma)
+    becomes exactly bf16-representable (rounding again changes nothing), each
+    entry moves by at most the bf16 unit roundoff (8 significant bits: 2^-8
+    relative), sigma and B are untouched, and a column with sigma = 0 stays
+    zero."""
+    rng = np.random.default_rng(41)
+    n, k, D = 30, 6, 20
+    U, _ = np.linalg.qr(rng.standard_normal((n, k)))
+    B, _ = np.linalg.qr(rng.standard_normal((D, k)))
+    sigma = np.array([50.0, 7.0, 3.0, 1.0, 0.25, 0.0])
+    fac = O.Factor(U=U, sigma=sigma, B=B, pos=np.arange(n))
+    p = O.persist_coords_bf16(fac)
+    C = fac.U * fac.sigma[None, :]
+    Cp = p.U * p.sigma[None, :]
+    # (U is held as C / sigma: multiplying back leaves fp64 rounding only)
+    assert np.all(np.abs(O.bf16_round(Cp) - Cp) <= 1e-14 * np.abs(Cp))
+    assert np.all(np.abs(Cp - C) <= 2.0 ** -8 * np.abs(C) + 1e-300)
+    assert np.array_equal(p.sigma, fac.sigma) and np.array_equal(p.B, fac.B)
+    assert np.all(p.U[:, 5] == 0)
+    assert np.linalg.norm(O.represented(p) - O.represented(fac)) <= 2.0 ** -8 * np.linalg.norm(O.represented(fac))
+    # a value half-way between two bf16 numbers rounds to the even one
+    half = O.Factor(U=np.array([[1.0 + 2.0 ** -8]]), sigma=np.array([1.0]), B=np.eye(1), pos=np.arange(1))
+    assert O.persist_coords_bf16(half).U[0, 0] == 1.0
