@@ -82,6 +82,62 @@ def profiled_traffic(name):
     return float(d["traffic_bytes_per_dispatch"])
 
 
+def coords_leg(args, K, torch, dev, Xk, Kc):
+    """fp32 against 2-byte (bf16) stored coordinates on two fresh K paths of
+    N0 rows each, filled by merges and then timed the same way: MODE_MERGES
+    merges (with re-orthogonalisation every 256 rows), 10 reconstructions
+    (bf16 with RoPE) and 10 factor-aware attentions (all rows compressed)."""
+    st = torch.cuda.Stream()
+    n_fill, extra = N0, (MODE_MERGES + 2) * BLK
+    Xd = torch.from_numpy(Xk[:n_fill + extra]).to(dev)
+    pos = torch.arange(n_fill + extra, dtype=torch.int32, device=dev)
+    rng = np.random.default_rng(6)
+    q = torch.from_numpy(rng.standard_normal((HQ, DH)).astype(np.float32)).to(dev).bfloat16()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    res, outs = {}, {}
+    for c16 in (False, True):
+        p = K.IsvdPath(D=D, r_max=R, b_max=BLK, n_cap=n_fill + extra, reorth_every_rows=256, device=dev,
+                       stream=st, graphs=not args.no_graphs, coords_bf16=c16)
+        for s0 in range(0, n_fill, BLK):
+            p.merge(Xd[s0:s0 + BLK], pos[s0:s0 + BLK])
+        st.synchronize()
+        n = p.n
+        out = torch.empty((n, D), dtype=torch.bfloat16, device=dev)
+        of = torch.empty((HQ, DH), dtype=torch.bfloat16, device=dev)
+        wsf = torch.empty(K.decode_attend_fv_workspace_bytes(p.h, 0, HQ), dtype=torch.uint8, device=dev)
+
+        def timed(fn, reps):
+            for _ in range(2):
+                fn()
+            ev[0].record(st)
+            for _ in range(reps):
+                fn()
+            ev[1].record(st)
+            st.synchronize()
+            return ev[0].elapsed_time(ev[1]) / reps
+
+        r_ms = timed(lambda: p.reconstruct(out, n, head_dim=DH, rope=True, theta=THETA, stream=st), 10)
+        f_ms = timed(lambda: K.decode_attend_fv(q, Kc, p.h, None, None, 0, n, HQ, HKV, DH, DH ** -0.5, of, wsf,
+                                                stream=st), 10)
+        outs[c16] = (out.float(), of.float())
+        cur = [n_fill]
+
+        def one_merge():
+            s0 = cur[0]
+            p.merge(Xd[s0:s0 + BLK], pos[s0:s0 + BLK])
+            cur[0] += BLK
+
+        m_ms = timed(one_merge, MODE_MERGES)
+        res["bf16" if c16 else "fp32"] = {"merge_ms": m_ms, "recon_ms": r_ms, "factor_v_ms": f_ms,
+                                          "coordinate_bytes": n * R * (2 if c16 else 4)}
+        p.close()
+    (ra, fa), (rb, fb) = outs[False], outs[True]
+    res["rows"] = n_fill
+    res["recon_rel_diff"] = float(torch.linalg.norm(rb - ra) / torch.linalg.norm(ra))
+    res["factor_v_max_abs_diff"] = float((fb - fa).abs().max())
+    return res
+
+
 def many_path_leg(args, K, torch, dev):
     """Many independent paths merged as one batched launch sequence per step
     (isvd_merge_block_batched through iskv_window_append_batched): half key
@@ -460,6 +516,7 @@ def main():
         "core_solver_last_merge": [{"flags": c[11], "steps": c[12], "resid_sweeps": c[14], "k": c[1], "n": c[0]}
                                    for c in core],
     }
+    result["coords_2byte"] = coords_leg(args, K, torch, dev, Xk, Kc)
     if args.batch_paths > 0:
         result["many_paths"] = many_path_leg(args, K, torch, dev)
     if not args.no_cpu_baseline:

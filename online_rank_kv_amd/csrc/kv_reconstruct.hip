@@ -376,13 +376,15 @@ __global__ __launch_bounds__(256) void recon_stream_kernel(const TC* __restrict_
   // columns 4 ((t + 256 u) % 64) .. +3; thread t < 32 also carries row t's
   // position. Loads run two blocks ahead (a ring of two register sets).
   __shared__ int posS[2][RS_BM];
-  float4 creg[2][8];
+  constexpr int ES = (int)sizeof(TC);  // bytes per stored coordinate
+  // fp32 rows are held as float4, 2-byte rows as their raw bf16 bits
+  using CR = std::conditional_t<ES == 4, float4, uint2>;
+  CR creg[2][8];
   int preg[2];
   // C rows through a buffer descriptor based at the block's first row and
   // bounded by the last row n - 1: rows past n read as zero, and the per-load
   // offsets are fixed (row t / 64 + 4 u, column 4 (t % 64)), so no address
   // arithmetic runs per block.
-  constexpr int ES = (int)sizeof(TC);  // bytes per stored coordinate
   const uint32_t voff0 = (uint32_t)(((t >> 6) * ldc + (t & 63) * 4) * ES);
   const uint32_t vstep = (uint32_t)(4 * ldc * ES);
   auto load_c = [&](int slot, int blk) {
@@ -391,13 +393,10 @@ __global__ __launch_bounds__(256) void recon_stream_kernel(const TC* __restrict_
         (void*)(C + (size_t)i0 * ldc), (short)0, (int)((n - i0) * ldc * ES), 0x00020000);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      if constexpr (ES == 4) {
+      if constexpr (ES == 4)
         creg[slot][u] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rc, voff0 + u * vstep, 0, 0));
-      } else {
-        const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rc, voff0 + u * vstep, 0, 0));
-        creg[slot][u] = float4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
-                               __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
-      }
+      else
+        creg[slot][u] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rc, voff0 + u * vstep, 0, 0));
     }
     preg[slot] = pos[min(i0 + (t & 31), n - 1)];
   };
@@ -407,18 +406,29 @@ __global__ __launch_bounds__(256) void recon_stream_kernel(const TC* __restrict_
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int e = t + 256 * u, r = e >> 6, c4 = (e & 63) * 4;
-        const float4 v = creg[slot][u];
-        *(uint2*)(cs + r * RS_CS + c4) = uint2{pk_bf16(v.x, v.y), pk_bf16(v.z, v.w)};
+        if constexpr (ES == 4) {
+          const float4 v = creg[slot][u];
+          *(uint2*)(cs + r * RS_CS + c4) = uint2{pk_bf16(v.x, v.y), pk_bf16(v.z, v.w)};
+        } else {
+          *(uint2*)(cs + r * RS_CS + c4) = creg[slot][u];
+        }
       }
     } else {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int e = t + 256 * u, r = e >> 6, c4 = (e & 63) * 4;
         const bool rv = i0 + r < n;
-        const float4 v = creg[slot][u];
-        const float x0 = (rv && c4 < kdev) ? v.x : 0.f, x1 = (rv && c4 + 1 < kdev) ? v.y : 0.f;
-        const float x2 = (rv && c4 + 2 < kdev) ? v.z : 0.f, x3 = (rv && c4 + 3 < kdev) ? v.w : 0.f;
-        *(uint2*)(cs + r * RS_CS + c4) = uint2{pk_bf16(x0, x1), pk_bf16(x2, x3)};
+        if constexpr (ES == 4) {
+          const float4 v = creg[slot][u];
+          const float x0 = (rv && c4 < kdev) ? v.x : 0.f, x1 = (rv && c4 + 1 < kdev) ? v.y : 0.f;
+          const float x2 = (rv && c4 + 2 < kdev) ? v.z : 0.f, x3 = (rv && c4 + 3 < kdev) ? v.w : 0.f;
+          *(uint2*)(cs + r * RS_CS + c4) = uint2{pk_bf16(x0, x1), pk_bf16(x2, x3)};
+        } else {  // zero the 16-bit halves at columns >= k (rows past n read as zero)
+          const uint2 v = creg[slot][u];
+          const uint32_t m0 = (c4 < kdev ? 0xffffu : 0u) | (c4 + 1 < kdev ? 0xffff0000u : 0u);
+          const uint32_t m1 = (c4 + 2 < kdev ? 0xffffu : 0u) | (c4 + 3 < kdev ? 0xffff0000u : 0u);
+          *(uint2*)(cs + r * RS_CS + c4) = rv ? uint2{v.x & m0, v.y & m1} : uint2{0u, 0u};
+        }
       }
     }
     if (t < RS_BM) ps[t] = (i0 + t < n) ? preg[slot] : -1;
