@@ -33,6 +33,8 @@ __all__ = [
     "merge",
     "reorth",
     "fold_frozen",
+    "anomaly_block_scores",
+    "prompt_protect",
     "persist_coords_bf16",
     "represented",
     "stored_rows",
@@ -230,6 +232,68 @@ def persist_coords_bf16(fac: Factor) -> Factor:
     U = np.where(fac.sigma[None, :] > 0, C / safe[None, :], 0.0)
     return Factor(U=U, sigma=fac.sigma.copy(), B=fac.B.copy(), pos=fac.pos.copy(), folded=fac.folded,
                   C_stale=fac.C_stale, dtype=fac.dtype)
+
+
+def anomaly_block_scores(K_rot: np.ndarray, Hkv: int, dh: int, block: int = 8, suffix_blocks: int = 4):
+    """Anomaly score of each prompt block (iS-KV notes §3.1, Algorithm 1 step 2).
+
+    The prompt's post-RoPE keys K_rot (L x Hkv*dh) are cut into blocks of
+    `block` tokens; the last `suffix_blocks` whole blocks and the partial tail
+    form the local suffix and are not scored. For KV head g and block j the
+    score is the minimum over the block's tokens of the cosine similarity
+    between the token's key and the mean key of the block. Reading: a cosine
+    with a zero vector counts as 1 (no anomaly signal). Returns the scores
+    (Hkv x nb, float64, nb = scored blocks) and the first suffix position.
+    """
+    K_rot = np.asarray(K_rot, dtype=np.float64)
+    L = K_rot.shape[0]
+    nfull = L // block
+    nb = max(nfull - suffix_blocks, 0)
+    scores = np.zeros((Hkv, nb))
+    for g in range(Hkv):
+        for j in range(nb):
+            X = K_rot[j * block:(j + 1) * block, g * dh:(g + 1) * dh]
+            mu = X.mean(axis=0)
+            nm = np.linalg.norm(mu)
+            cos = []
+            for t in range(block):
+                nt = np.linalg.norm(X[t])
+                cos.append(1.0 if nt == 0.0 or nm == 0.0 else float(X[t] @ mu) / (nt * nm))
+            scores[g, j] = min(cos)
+    return scores, nb * block
+
+
+def prompt_protect(K_rot: np.ndarray, Hkv: int, dh: int, block: int = 8, per_head: int = 128,
+                   suffix_blocks: int = 4, v_radius: int = 32, v_window: int = 128, scores=None):
+    """The exact-row sets of the prompt (iS-KV notes §3.1, Algorithm 1 steps 2-6).
+
+    Each KV head selects its `per_head` lowest-scoring blocks (all of them when
+    there are fewer; equal scores: the lower block index first); the positions
+    of the union of the selected blocks over heads, plus the local suffix, are
+    P_K. P_V is every prompt position within `v_radius` of a P_K position; W_V
+    the last min(v_window, L) positions (W_K is empty). ``scores`` may supply
+    the block scores (for checking a selection made from them). Returns
+    boolean masks (P_K, P_V, W_V) of length L; E_K = P_K, E_V = P_V | W_V.
+    """
+    L = np.asarray(K_rot).shape[0]
+    if scores is None:
+        scores, s0 = anomaly_block_scores(K_rot, Hkv, dh, block, suffix_blocks)
+    else:
+        scores = np.asarray(scores, dtype=np.float64)
+        s0 = scores.shape[1] * block
+    nb = scores.shape[1]
+    pk = np.zeros(L, dtype=bool)
+    pk[s0:] = True
+    for g in range(Hkv):
+        order = sorted(range(nb), key=lambda j: (scores[g, j], j))
+        for j in order[:per_head]:
+            pk[j * block:(j + 1) * block] = True
+    pv = np.zeros(L, dtype=bool)
+    for p in np.nonzero(pk)[0]:
+        pv[max(0, p - v_radius):min(L, p + v_radius + 1)] = True
+    wv = np.zeros(L, dtype=bool)
+    wv[max(0, L - v_window):] = True
+    return pk, pv, wv
 
 
 def fold_frozen(C: np.ndarray, B: np.ndarray, pos, F: np.ndarray, pos_F):

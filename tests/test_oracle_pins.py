@@ -450,3 +450,47 @@ def test_persist_coords_bf16_pins():
     # a value half-way between two bf16 numbers rounds to the even one
     half = O.Factor(U=np.array([[1.0 + 2.0 ** -8]]), sigma=np.array([1.0]), B=np.eye(1), pos=np.arange(1))
     assert O.persist_coords_bf16(half).U[0, 0] == 1.0
+
+
+# --------------------------------------------------------------------------- prompt protection
+def test_anomaly_scores_and_protect_pins():
+    """Algorithm 1 steps 2-6 (notes §3.1): a block of equal keys scores 1, one
+    key opposite to the rest gives that key's cosine with the mean (closed
+    form), the suffix (last 4 blocks + tail) is never scored and always kept,
+    a head keeps its lowest blocks (ties: lower index), P_V dilates P_K by 32
+    positions (brute force) and W_V is the last 128 positions."""
+    Hkv, dh, blk = 2, 4, 8
+    L = 8 * 9 + 3                       # 9 whole blocks + a tail of 3: 5 scored blocks
+    rng = np.random.default_rng(51)
+    K = np.tile(rng.standard_normal((1, Hkv * dh)), (L, 1))   # every key equal: every score 1
+    sc, s0 = O.anomaly_block_scores(K, Hkv, dh)
+    assert sc.shape == (2, 5) and s0 == 40 and np.allclose(sc, 1.0)
+    # block 2, head 1: seven keys e and one key -e -> mean 6e/8, cosine of the odd key = -1
+    e = np.array([1.0, 0.0, 0.0, 0.0])
+    K[16:24, dh:2 * dh] = e
+    K[19, dh:2 * dh] = -e
+    # block 4, head 0: keys e and one key orthogonal: mean (7e + f)/8, min cosine = 1/sqrt(50)
+    f = np.array([0.0, 1.0, 0.0, 0.0])
+    K[32:40, :dh] = e
+    K[35, :dh] = f
+    sc, _ = O.anomaly_block_scores(K, Hkv, dh)
+    assert abs(sc[1, 2] + 1.0) < 1e-12
+    assert abs(sc[0, 4] - 1.0 / np.sqrt(50.0)) < 1e-12
+    pk, pv, wv = O.prompt_protect(K, Hkv, dh, per_head=1)
+    expect = np.zeros(L, dtype=bool)
+    expect[16:24] = True                # head 1's lowest block
+    expect[32:40] = True                # head 0's lowest block
+    expect[40:] = True                  # suffix
+    assert np.array_equal(pk, expect)
+    brute = np.array([any(pk[q] for q in range(max(0, p - 32), min(L, p + 33))) for p in range(L)])
+    assert np.array_equal(pv, brute)
+    assert np.array_equal(wv, np.arange(L) >= L - 128)
+    # ties: all scores equal -> the lowest block indices; fewer blocks than per_head -> all
+    pk2, _, _ = O.prompt_protect(np.tile(K[:1], (L, 1)), Hkv, dh, per_head=2)
+    assert np.array_equal(np.nonzero(pk2[:40])[0], np.arange(16))
+    pk3, _, _ = O.prompt_protect(K, Hkv, dh, per_head=128)
+    assert pk3.all()
+    # a prompt shorter than the suffix: nothing scored, everything protected
+    sc4, s4 = O.anomaly_block_scores(K[:30], Hkv, dh)
+    assert sc4.shape == (2, 0) and s4 == 0
+    assert O.prompt_protect(K[:30], Hkv, dh)[0].all()
