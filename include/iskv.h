@@ -301,6 +301,31 @@ int decode_attend_fv(const uint16_t* q, const uint16_t* K, const isvd_handle* hv
                      const int32_t* pos_exact, int32_t n_exact, int32_t n_total, int32_t Hq, int32_t Hkv,
                      int32_t dh, float scale, uint16_t* out, void* workspace, size_t ws_bytes, void* stream);
 
+/* ---- prompt initialisation ----------------------------------------------- */
+/* Exact-row sets of a prompt (iS-KV notes §3.1, Algorithm 1 steps 2-6), from
+ * its post-RoPE keys. The prompt is cut into blocks of `block` tokens; the last
+ * `suffix_blocks` whole blocks and the partial tail are the local suffix. For
+ * each KV head and every other block, the anomaly score is the minimum over the
+ * block's tokens of the cosine between the token's key and the block's mean key
+ * (fp32; a cosine with a zero vector counts as 1). Each head keeps its
+ * `per_head` lowest-scoring blocks (equal scores: lower block index first; NaN
+ * scores last); P_K = union of the kept blocks over heads plus the suffix;
+ * P_V = every position within v_radius of P_K; W_V = the last v_window
+ * positions (W_K is empty). The notes use block 8, per_head 128, suffix 4,
+ * v_radius 32, v_window 128.
+ *   K_rot      device bf16 [L x Hkv x dh], the prompt's post-RoPE keys.
+ *   flags      device uint8 [L]: bit 0 P_K, bit 1 P_V, bit 2 W_V. The exact
+ *              sets are E_K = P_K and E_V = P_V | W_V.
+ *   scores     device fp32 [Hkv x nb] or NULL: the block scores, nb =
+ *              max(L / block - suffix_blocks, 0) scored blocks per head.
+ *   workspace  >= iskv_prompt_protect_workspace_bytes(L, Hkv, block, suffix_blocks).
+ * 1 <= block <= 64, 1 <= dh <= 256, per_head, suffix_blocks, v_radius,
+ * v_window >= 0. Errors: EINVAL, EWORKSPACE, EHIP. */
+size_t iskv_prompt_protect_workspace_bytes(int32_t L, int32_t Hkv, int32_t block, int32_t suffix_blocks);
+int iskv_prompt_protect(const uint16_t* K_rot, int32_t L, int32_t Hkv, int32_t dh, int32_t block,
+                        int32_t per_head, int32_t suffix_blocks, int32_t v_radius, int32_t v_window,
+                        uint8_t* flags, float* scores, void* workspace, size_t ws_bytes, void* stream);
+
 /* ---- exact window and pending FIFO --------------------------------------- */
 /* The cache policy of §3.2 and Algorithm 3 (iS-KV notes): every new row is
  * stored exactly in a recent window of `window` rows; an unprotected row

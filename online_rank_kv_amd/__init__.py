@@ -18,7 +18,7 @@ import os
 
 __all__ = [
     "LIB_PATH", "lib", "IskvError", "IskvConfig", "ISKV_NO_COORD_SYNC", "ISKV_NO_GRAPH", "ISKV_FROZEN_BASIS",
-    "ISKV_BF16_COORDS",
+    "ISKV_BF16_COORDS", "iskv_prompt_protect_workspace_bytes", "iskv_prompt_protect", "prompt_protect",
     "ISKV_OUT_BF16", "isvd_set_mode",
     "ISKV_OUT_FP32", "ISKV_DEV_NONFINITE", "ISKV_DEV_NOCONV", "EXPORTED_SYMBOLS",
     "isvd_workspace_bytes", "isvd_init", "isvd_merge_block", "isvd_reorth", "isvd_query",
@@ -55,6 +55,7 @@ EXPORTED_SYMBOLS = (
     "isvd_query_state", "isvd_sym_eig", "kv_scatter_exact", "isvd_merge_block_batched",
     "isvd_set_timing", "isvd_stage_times", "iskv_window_append_batched",
     "decode_attend_fv_workspace_bytes", "decode_attend_fv", "isvd_set_mode",
+    "iskv_prompt_protect_workspace_bytes", "iskv_prompt_protect",
 )
 
 
@@ -90,6 +91,11 @@ lib.isvd_reorth.restype = ctypes.c_int
 lib.isvd_reorth.argtypes = [_vp]
 lib.isvd_set_mode.restype = ctypes.c_int
 lib.isvd_set_mode.argtypes = [_vp, _i32]
+lib.iskv_prompt_protect_workspace_bytes.restype = ctypes.c_size_t
+lib.iskv_prompt_protect_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
+lib.iskv_prompt_protect.restype = ctypes.c_int
+lib.iskv_prompt_protect.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
+                                    ctypes.c_size_t, _vp]
 lib.isvd_query.restype = ctypes.c_int
 lib.isvd_query.argtypes = [_vp, _pi32, _pi32, _pi32]
 lib.isvd_query_state.restype = ctypes.c_int
@@ -191,6 +197,36 @@ def isvd_reorth(h: int) -> None:
 
 def isvd_set_mode(h: int, mode: int) -> None:
     _check(lib.isvd_set_mode(h, int(mode)), "isvd_set_mode")
+
+
+def iskv_prompt_protect_workspace_bytes(L: int, Hkv: int, block: int = 8, suffix_blocks: int = 4) -> int:
+    return int(lib.iskv_prompt_protect_workspace_bytes(L, Hkv, block, suffix_blocks))
+
+
+def iskv_prompt_protect(K_rot, L: int, Hkv: int, dh: int, block: int, per_head: int, suffix_blocks: int,
+                        v_radius: int, v_window: int, flags, scores, workspace, stream=None) -> None:
+    _check(lib.iskv_prompt_protect(_ptr(K_rot), int(L), int(Hkv), int(dh), int(block), int(per_head),
+                                   int(suffix_blocks), int(v_radius), int(v_window), _ptr(flags), _ptr(scores),
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream_ptr(stream)), "iskv_prompt_protect")
+
+
+def prompt_protect(K_rot, Hkv: int, dh: int, block: int = 8, per_head: int = 128, suffix_blocks: int = 4,
+                   v_radius: int = 32, v_window: int = 128, with_scores: bool = False, stream=None):
+    """Exact-row masks (P_K, P_V, W_V) of a prompt from its post-RoPE keys
+    (bf16 [L, Hkv * dh] on the device); optionally the block scores too."""
+    import torch
+    L = int(K_rot.shape[0])
+    dev = K_rot.device
+    flags = torch.empty((L,), dtype=torch.uint8, device=dev)
+    nb = max(L // block - suffix_blocks, 0)
+    scores = torch.empty((Hkv, nb), dtype=torch.float32, device=dev) if with_scores and nb > 0 else None
+    ws = torch.empty((iskv_prompt_protect_workspace_bytes(L, Hkv, block, suffix_blocks),), dtype=torch.uint8,
+                     device=dev)
+    iskv_prompt_protect(K_rot, L, Hkv, dh, block, per_head, suffix_blocks, v_radius, v_window, flags, scores, ws,
+                        stream)
+    pk, pv, wv = (flags & 1) != 0, (flags & 2) != 0, (flags & 4) != 0
+    return (pk, pv, wv, scores) if with_scores else (pk, pv, wv)
 
 
 def isvd_query(h: int):

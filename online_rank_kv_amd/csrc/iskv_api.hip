@@ -343,6 +343,22 @@ int decode_attend_fv(const uint16_t* q, const uint16_t* K, const isvd_handle* hv
                                ws_bytes, (hipStream_t)stream);
 }
 
+// ---- prompt initialisation ---------------------------------------------------
+size_t iskv_prompt_protect_workspace_bytes(int32_t L, int32_t Hkv, int32_t block, int32_t suffix_blocks) {
+  return iskv_prompt_protect_ws_bytes(L, Hkv, block, suffix_blocks);
+}
+
+int iskv_prompt_protect(const uint16_t* K_rot, int32_t L, int32_t Hkv, int32_t dh, int32_t block,
+                        int32_t per_head, int32_t suffix_blocks, int32_t v_radius, int32_t v_window,
+                        uint8_t* flags, float* scores, void* workspace, size_t ws_bytes, void* stream) {
+  if (!K_rot || !flags || !workspace) return ISKV_EINVAL;
+  if (L < 1 || Hkv < 1 || dh < 1 || dh > 256 || block < 1 || block > 64) return ISKV_EINVAL;
+  if (per_head < 0 || suffix_blocks < 0 || v_radius < 0 || v_window < 0) return ISKV_EINVAL;
+  if ((int64_t)L * Hkv * dh > ((int64_t)1 << 31)) return ISKV_EINVAL;
+  return iskv_launch_prompt_protect(K_rot, L, Hkv, dh, block, per_head, suffix_blocks, v_radius, v_window, flags,
+                                    scores, workspace, ws_bytes, (hipStream_t)stream);
+}
+
 // ---- exact window and pending FIFO ----------------------------------------
 int32_t iskv_window_rows(int32_t prot_cap, int32_t window, int32_t block) {
   if (prot_cap < 0 || window < 0 || block < 1) return 0;

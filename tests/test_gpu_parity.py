@@ -816,3 +816,43 @@ def test_error_paths(K):
     bad.merge(Fn, p)
     _, _, st = bad.query()
     assert st & K.ISKV_DEV_NONFINITE
+
+
+# --------------------------------------------------------------------------- prompt protection
+@pytest.mark.parametrize("L,hkv,dh,per_head", [(3003, 8, 128, 128), (1000, 4, 64, 16), (30, 2, 128, 128),
+                                               (8 * 9 + 3, 2, 128, 1)])
+def test_prompt_protect_matches_oracle(K, L, hkv, dh, per_head):
+    """Algorithm 1 steps 2-6 (notes §3.1) on the GPU: block anomaly scores equal
+    the oracle's (fp64 on the same bf16 keys) to 1e-5; the kept blocks, P_K, P_V
+    and W_V equal the oracle's sets computed from the GPU's own scores exactly,
+    and from the oracle's scores except at a near tie on the per-head cut."""
+    rng = np.random.default_rng(61 + L)
+    Kr = rng.standard_normal((L, hkv * dh)).astype(np.float32)
+    for j in range(0, L // 8, 7):        # planted anomalies: one token turned against its block
+        Kr[8 * j + 3] = -Kr[8 * j + 3] * 2.0
+    Kb = torch.from_numpy(Kr).bfloat16()
+    Kd = Kb.to(DEV).contiguous()
+    pk, pv, wv, sc = K.prompt_protect(Kd, hkv, dh, per_head=per_head, with_scores=True)
+    torch.cuda.synchronize()
+    pk, pv, wv = pk.cpu().numpy(), pv.cpu().numpy(), wv.cpu().numpy()
+    Kh = Kb.double().numpy()
+    ref_sc, s0 = O.anomaly_block_scores(Kh, hkv, dh)
+    if sc is None:
+        assert ref_sc.shape[1] == 0
+        gsc = ref_sc
+    else:
+        gsc = sc.double().cpu().numpy()
+        assert np.abs(gsc - ref_sc).max() < 1e-5
+    # exact given the GPU's scores
+    pk_g, pv_g, wv_g = O.prompt_protect(Kh, hkv, dh, per_head=per_head, scores=gsc)
+    assert np.array_equal(pk, pk_g) and np.array_equal(pv, pv_g) and np.array_equal(wv, wv_g)
+    # against the oracle's own scores: any difference is a near tie at a head's cut
+    pk_o, pv_o, _ = O.prompt_protect(Kh, hkv, dh, per_head=per_head)
+    diff = np.nonzero(pk != pk_o)[0]
+    for p in diff:
+        j = p // 8
+        assert any(abs(ref_sc[g, j] - np.sort(ref_sc[g])[min(per_head, ref_sc.shape[1]) - 1]) < 1e-5
+                   for g in range(hkv)), (p, j)
+    assert pk[s0:].all() and wv.sum() == min(128, L)
+    if L == 3003:
+        assert 0 < pk.sum() < L and pv.sum() >= pk.sum()
