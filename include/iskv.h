@@ -302,6 +302,30 @@ int decode_attend_fv(const uint16_t* q, const uint16_t* K, const isvd_handle* hv
                      int32_t dh, float scale, uint16_t* out, void* workspace, size_t ws_bytes, void* stream);
 
 /* ---- prompt initialisation ----------------------------------------------- */
+/* Replace the history by a fresh rank-k truncated SVD of the rows X (iS-KV
+ * notes Algorithm 1 step 7: the non-exact prompt rows; §3.2: the value first
+ * refit over the rebuilt prompt values plus the first rows to leave the
+ * window). The handle is reset to empty, the rows are folded by merges
+ * (Algorithm 2, with the re-orthogonalisation schedule), and `iters` subspace
+ * iterations with a Rayleigh-Ritz step follow, each C <- X B and
+ * re-orthogonalise (§4.4: the Ritz vectors of X^T X in span(B)); Z <- X^T C;
+ * B <- Z with unit columns, re-orthogonalised; a last Ritz step gives
+ * C = X B. They converge
+ * to the top-k right singular subspace of X, so the factors approach the
+ * fresh truncated SVD the notes specify (k = the rank the fold reached).
+ *   X     device fp32 [n x D], rows in the order of pos.
+ *   pos   device int32 [n], their original positions.
+ *   work  device buffer of >= isvd_refit_workspace_bytes(h) bytes (not read
+ *         when iters = 0).
+ * The iterations stage 16 rows of X in LDS, so they need D <= 1984.
+ * Errors: EINVAL (also D > 1984 with iters > 0), ECAPACITY (n > n_cap),
+ * EMODE (basis-only or frozen mode),
+ * EWORKSPACE, EHIP. */
+size_t isvd_refit_workspace_bytes(const isvd_handle* h);
+int isvd_refit(isvd_handle* h, const float* X, const int32_t* pos, int32_t n, int32_t iters, void* work,
+               size_t work_bytes);
+
+
 /* Exact-row sets of a prompt (iS-KV notes §3.1, Algorithm 1 steps 2-6), from
  * its post-RoPE keys. The prompt is cut into blocks of `block` tokens; the last
  * `suffix_blocks` whole blocks and the partial tail are the local suffix. For

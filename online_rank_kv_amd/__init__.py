@@ -18,7 +18,7 @@ import os
 
 __all__ = [
     "LIB_PATH", "lib", "IskvError", "IskvConfig", "ISKV_NO_COORD_SYNC", "ISKV_NO_GRAPH", "ISKV_FROZEN_BASIS",
-    "ISKV_BF16_COORDS", "iskv_prompt_protect_workspace_bytes", "iskv_prompt_protect", "prompt_protect",
+    "ISKV_BF16_COORDS", "isvd_refit_workspace_bytes", "isvd_refit", "iskv_prompt_protect_workspace_bytes", "iskv_prompt_protect", "prompt_protect",
     "ISKV_OUT_BF16", "isvd_set_mode",
     "ISKV_OUT_FP32", "ISKV_DEV_NONFINITE", "ISKV_DEV_NOCONV", "EXPORTED_SYMBOLS",
     "isvd_workspace_bytes", "isvd_init", "isvd_merge_block", "isvd_reorth", "isvd_query",
@@ -55,7 +55,7 @@ EXPORTED_SYMBOLS = (
     "isvd_query_state", "isvd_sym_eig", "kv_scatter_exact", "isvd_merge_block_batched",
     "isvd_set_timing", "isvd_stage_times", "iskv_window_append_batched",
     "decode_attend_fv_workspace_bytes", "decode_attend_fv", "isvd_set_mode",
-    "iskv_prompt_protect_workspace_bytes", "iskv_prompt_protect",
+    "iskv_prompt_protect_workspace_bytes", "iskv_prompt_protect", "isvd_refit_workspace_bytes", "isvd_refit",
 )
 
 
@@ -91,6 +91,10 @@ lib.isvd_reorth.restype = ctypes.c_int
 lib.isvd_reorth.argtypes = [_vp]
 lib.isvd_set_mode.restype = ctypes.c_int
 lib.isvd_set_mode.argtypes = [_vp, _i32]
+lib.isvd_refit_workspace_bytes.restype = ctypes.c_size_t
+lib.isvd_refit_workspace_bytes.argtypes = [_vp]
+lib.isvd_refit.restype = ctypes.c_int
+lib.isvd_refit.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp, ctypes.c_size_t]
 lib.iskv_prompt_protect_workspace_bytes.restype = ctypes.c_size_t
 lib.iskv_prompt_protect_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
 lib.iskv_prompt_protect.restype = ctypes.c_int
@@ -197,6 +201,15 @@ def isvd_reorth(h: int) -> None:
 
 def isvd_set_mode(h: int, mode: int) -> None:
     _check(lib.isvd_set_mode(h, int(mode)), "isvd_set_mode")
+
+
+def isvd_refit_workspace_bytes(h: int) -> int:
+    return int(lib.isvd_refit_workspace_bytes(h))
+
+
+def isvd_refit(h: int, X, pos, n: int, iters: int, work) -> None:
+    nbytes = 0 if work is None else work.numel() * work.element_size()
+    _check(lib.isvd_refit(h, _ptr(X), _ptr(pos), int(n), int(iters), _ptr(work), nbytes), "isvd_refit")
 
 
 def iskv_prompt_protect_workspace_bytes(L: int, Hkv: int, block: int = 8, suffix_blocks: int = 4) -> int:
@@ -382,6 +395,15 @@ class IsvdPath:
 
     def reorth(self) -> None:
         isvd_reorth(self.h)
+
+    def refit(self, X, pos, iters: int = 8) -> None:
+        """Fresh rank-r truncated SVD of the rows X (fp32 [n, D]) at positions pos."""
+        import torch
+        work = None
+        if iters > 0:
+            work = torch.empty((isvd_refit_workspace_bytes(self.h),), dtype=torch.uint8, device=self.C.device)
+        isvd_refit(self.h, X, pos, int(X.shape[0]), iters, work)
+        self._refit_work = work  # kept until the stream has used it
 
     def set_mode(self, mode: int) -> None:
         """0 (full merge), ISKV_NO_COORD_SYNC (basis-only) or ISKV_FROZEN_BASIS."""

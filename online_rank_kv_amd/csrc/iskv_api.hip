@@ -107,6 +107,22 @@ size_t isvd_workspace_bytes(const iskv_config* cfg) {
   return carve(cfg, nullptr, nullptr) + kAlign;
 }
 
+// Empty history: n = k = 0, zero factors, no positions (enqueued on the stream).
+static int reset_history(isvd_handle* h) {
+  const iskv_config& c = h->cfg;
+  hipStream_t s = h->stream;
+  const size_t R = c.r_max;
+  h->n_host = 0;
+  h->folded_host = 0;
+  ISKV_HIP_CHECK(hipMemsetAsync(h->w.st, 0, ST_COUNT * sizeof(int32_t), s));
+  ISKV_HIP_CHECK(hipMemsetAsync(h->C, 0, (size_t)c.n_cap * R * (iskv_bf16_coords(c) ? 2 : 4), s));
+  ISKV_HIP_CHECK(hipMemsetAsync(h->sigma, 0, R * sizeof(float), s));
+  ISKV_HIP_CHECK(hipMemsetAsync(h->B, 0, (size_t)c.D * R * sizeof(float), s));
+  ISKV_HIP_CHECK(hipMemsetAsync(h->w.Bbf, 0, (size_t)c.D * R * 2, s));
+  ISKV_HIP_CHECK(hipMemsetAsync(h->pos, 0xff, (size_t)c.n_cap * sizeof(int32_t), s));
+  return ISKV_OK;
+}
+
 int isvd_init(isvd_handle** out, const iskv_config* cfg, float* C, float* sigma, float* B,
               int32_t* pos, void* workspace, size_t ws_bytes, void* stream) {
   if (!out || !cfg_ok(cfg) || !C || !sigma || !B || !pos || !workspace) return ISKV_EINVAL;
@@ -122,21 +138,33 @@ int isvd_init(isvd_handle** out, const iskv_config* cfg, float* C, float* sigma,
   h->m_max = cfg->r_max + cfg->b_max;
   h->ldm = iskv_core_ld(h->m_max);
   carve(cfg, (char*)workspace, &h->w);
-  h->n_host = 0;
-  h->folded_host = 0;
-  hipStream_t s = h->stream;
-  const size_t R = cfg->r_max;
-  if (hipMemsetAsync(h->w.st, 0, ST_COUNT * sizeof(int32_t), s) != hipSuccess ||
-      hipMemsetAsync(C, 0, (size_t)cfg->n_cap * R * (iskv_bf16_coords(*cfg) ? 2 : 4), s) != hipSuccess ||
-      hipMemsetAsync(sigma, 0, R * sizeof(float), s) != hipSuccess ||
-      hipMemsetAsync(B, 0, (size_t)cfg->D * R * sizeof(float), s) != hipSuccess ||
-      hipMemsetAsync(h->w.Bbf, 0, (size_t)cfg->D * R * 2, s) != hipSuccess ||
-      hipMemsetAsync(pos, 0xff, (size_t)cfg->n_cap * sizeof(int32_t), s) != hipSuccess) {
+  if (reset_history(h) != ISKV_OK) {
     delete h;
     return ISKV_EHIP;
   }
   *out = h;
   return ISKV_OK;
+}
+
+size_t isvd_refit_workspace_bytes(const isvd_handle* h) { return h ? iskv_refit_ws_bytes(h) : 0; }
+
+int isvd_refit(isvd_handle* h, const float* X, const int32_t* pos, int32_t n, int32_t iters, void* work,
+               size_t work_bytes) {
+  if (!h || !X || !pos || n < 1 || iters < 0 || iters > 64) return ISKV_EINVAL;
+  if (n > h->cfg.n_cap) return ISKV_ECAPACITY;
+  if (h->cfg.flags & (ISKV_NO_COORD_SYNC | ISKV_FROZEN_BASIS)) return ISKV_EMODE;
+  if (iters > 0 && !iskv_refit_supported(h->cfg)) return ISKV_EINVAL;
+  if (iters > 0 && (!work || work_bytes < iskv_refit_ws_bytes(h))) return ISKV_EWORKSPACE;
+  int rc = reset_history(h);
+  if (rc) return rc;
+  // fold the rows (Algorithm 2, with the re-orthogonalisation schedule) ...
+  for (int32_t s0 = 0; s0 < n; s0 += h->cfg.b_max) {
+    const int32_t b = n - s0 < h->cfg.b_max ? n - s0 : h->cfg.b_max;
+    rc = isvd_merge_block(h, X + (size_t)s0 * h->cfg.D, pos + s0, b);
+    if (rc) return rc;
+  }
+  // ... then refine to the top-k singular subspace of the rows
+  return iskv_launch_refit_iterations(h, X, n, iters, work);
 }
 
 int32_t isvd_rows(const isvd_handle* h) { return h ? h->n_host : 0; }

@@ -167,6 +167,9 @@ size_t iskv_attend_fv_ws_bytes(int32_t n_c, int32_t n_exact, int32_t Hq, int32_t
 int iskv_launch_attend_fv(const uint16_t* q, const uint16_t* K, const isvd_handle* hv, const float* X_exact,
                           const int32_t* pos_exact, int32_t n_exact, int32_t n_total, int32_t Hq, int32_t Hkv,
                           float scale, uint16_t* out, void* ws, size_t ws_bytes, hipStream_t s);
+bool iskv_refit_supported(const iskv_config& c);
+size_t iskv_refit_ws_bytes(const isvd_handle* h);
+int iskv_launch_refit_iterations(isvd_handle* h, const float* X, int32_t n, int32_t iters, void* work);
 size_t iskv_prompt_protect_ws_bytes(int32_t L, int32_t Hkv, int32_t block, int32_t suffix_blocks);
 int iskv_launch_prompt_protect(const uint16_t* K_rot, int32_t L, int32_t Hkv, int32_t dh, int32_t block,
                                int32_t per_head, int32_t suffix_blocks, int32_t v_radius, int32_t v_window,

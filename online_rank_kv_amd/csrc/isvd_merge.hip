@@ -1454,6 +1454,141 @@ int iskv_launch_reorth(isvd_handle* h) {
 }
 
 // ---------------------------------------------------------------------------
+// Fresh truncated SVD of given rows (Algorithm 1 step 7, the value first
+// refit of §3.2): after the rows are folded by merges, subspace iterations
+// with a Rayleigh-Ritz step converge to the top-k right singular subspace of X.
+// Each iteration:
+//   C <- X B and re-orthogonalise (§4.4): with B orthonormal, C B^T = X B B^T
+//     becomes its exact SVD, whose right singular vectors are the Ritz
+//     vectors of X^T X in span(B) and whose coordinates are X B;
+//   Z <- X^T C (= X^T X B);  B <- Z diag(1 / |z_j|);
+//   re-orthogonalise again: an orthonormal basis of span(Z).
+// A last Ritz step gives the factors C = X B.
+namespace {
+
+// Zpart[s][d][j] = sum over rows i of chunk s of X[i][d] C[i][j], for
+// d < D, j < k (64 x 64 output tile per workgroup, 4 x 4 per thread).
+template <typename TC>
+__global__ __launch_bounds__(256) void xtc_partial_kernel(const float* __restrict__ X, int ldx,
+                                                          const TC* __restrict__ C, int ldc, int n, int D,
+                                                          const int32_t* __restrict__ st, int rows_per_chunk,
+                                                          float* __restrict__ Zpart, int ldz) {
+  const int k = st[ST_K];
+  const int d0 = blockIdx.x * 64, j0 = blockIdx.y * 64;
+  if (j0 >= k) return;
+  const int r0 = blockIdx.z * rows_per_chunk, r1 = min(n, r0 + rows_per_chunk);
+  __shared__ float Xs[32][64 + 4], Cs[32][64 + 4];
+  const int t = threadIdx.x, td = t >> 4, tj = t & 15;
+  float acc[4][4] = {};
+  for (int rb = r0; rb < r1; rb += 32) {
+    for (int e = t; e < 32 * 64; e += 256) {
+      const int rr = e >> 6, cc = e & 63, row = rb + rr;
+      Xs[rr][cc] = (row < r1 && d0 + cc < D) ? X[(size_t)row * ldx + d0 + cc] : 0.f;
+      Cs[rr][cc] = (row < r1 && j0 + cc < k) ? iskv_ld(C + (size_t)row * ldc + j0 + cc) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int rr = 0; rr < 32; ++rr) {
+      float xv[4], cv[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        xv[a] = Xs[rr][td + 16 * a];
+        cv[a] = Cs[rr][tj + 16 * a];
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[a][c] = fmaf(xv[a], cv[c], acc[a][c]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int d = d0 + td + 16 * a, j = j0 + tj + 16 * c;
+      if (d < D && j < k) Zpart[((size_t)blockIdx.z * D + d) * ldz + j] = acc[a][c];
+    }
+}
+
+// B[:, j] = Z[:, j] / |Z[:, j]| for j < k (Z = the sum of the chunk
+// partials), columns j >= k zero. One workgroup per column.
+__global__ __launch_bounds__(256) void refit_basis_kernel(const float* __restrict__ Zpart, int nchunks, int D,
+                                                          int ldz, const int32_t* __restrict__ st, float* B,
+                                                          int ldb) {
+  const int j = blockIdx.x, k = st[ST_K];
+  const int t = threadIdx.x;
+  __shared__ float red[4];
+  float ss = 0.f;
+  for (int d = t; d < D; d += 256) {
+    float z = 0.f;
+    for (int c = 0; c < nchunks; ++c) z += Zpart[((size_t)c * D + d) * ldz + j];
+    ss = fmaf(z, z, ss);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  if ((t & 63) == 0) red[t >> 6] = ss;
+  __syncthreads();
+  const float nrm = sqrtf(red[0] + red[1] + red[2] + red[3]);
+  const float inv = (j < k && nrm > 0.f) ? 1.f / nrm : 0.f;
+  for (int d = t; d < D; d += 256) {
+    float z = 0.f;
+    if (j < k)
+      for (int c = 0; c < nchunks; ++c) z += Zpart[((size_t)c * D + d) * ldz + j];
+    B[(size_t)d * ldb + j] = z * inv;
+  }
+}
+
+constexpr int RF_CHUNKS = 16;  // row chunks of X^T C
+
+}  // namespace
+
+// C <- X B stages 16 rows of X (D wide) in LDS: D up to 1984.
+bool iskv_refit_supported(const iskv_config& c) { return xh_lds_bytes(16, c.D) <= 160 * 1024; }
+
+size_t iskv_refit_ws_bytes(const isvd_handle* h) {
+  return (size_t)RF_CHUNKS * h->cfg.D * h->cfg.r_max * sizeof(float);
+}
+
+int iskv_launch_refit_iterations(isvd_handle* h, const float* X, int32_t n, int32_t iters, void* work) {
+  const iskv_config& c = h->cfg;
+  hipStream_t s = h->stream;
+  const int D = c.D, R = c.r_max;
+  float* Zp = (float*)work;
+  if (iters > 0 && !iskv_refit_supported(c)) return ISKV_EINVAL;
+  const int rpc = (n + RF_CHUNKS - 1) / RF_CHUNKS;
+  auto c_from_x = [&]() {  // C <- X B (rows 0 .. n-1, k columns)
+    with_coords(h, [&](auto* Cp) {
+      xh_launch(s, nullptr, 1, n, X, D, nullptr, 0, hdim(D), hdim(D), D, h->B, R, R, ddim(h->w.st + ST_K), hdim(n),
+                Cp, R, nullptr, 0, nullptr, nullptr, true);
+    });
+  };
+  auto ritz = [&]() -> int {  // C <- X B, then the exact SVD of C B^T
+    c_from_x();
+    ISKV_HIP_CHECK(hipGetLastError());
+    return iskv_launch_reorth(h);
+  };
+  for (int it = 0; it < iters; ++it) {
+    // Ritz vectors of X^T X in span(B) (B orthonormal here): z_i = X^T X b_i
+    // then equals theta_i b_i plus a residual orthogonal to span(B), so the
+    // normalised columns of Z are orthonormal up to the residuals' products
+    int rc = ritz();
+    if (rc) return rc;
+    with_coords(h, [&](auto* Cp) {
+      using TC = std::remove_pointer_t<decltype(Cp)>;
+      hipLaunchKernelGGL((xtc_partial_kernel<TC>), dim3((D + 63) / 64, (R + 63) / 64, RF_CHUNKS), dim3(256), 0, s, X,
+                         D, (const TC*)Cp, R, n, D, h->w.st, rpc, Zp, R);
+    });
+    hipLaunchKernelGGL(refit_basis_kernel, dim3(R), dim3(256), 0, s, Zp, RF_CHUNKS, D, R, h->w.st, h->B, R);
+    ISKV_HIP_CHECK(hipGetLastError());
+    // orthonormal basis of span(Z) (the coordinates are recomputed next)
+    rc = iskv_launch_reorth(h);
+    if (rc) return rc;
+  }
+  return iters > 0 ? ritz() : ISKV_OK;
+}
+
+// ---------------------------------------------------------------------------
 // Batched merges / reorths over handles with one configuration and one buffer
 // layout (every buffer of handle z lies at the same byte offset from the
 // corresponding buffer of handle 0; checked by the caller): the launch

@@ -856,3 +856,53 @@ def test_prompt_protect_matches_oracle(K, L, hkv, dh, per_head):
     assert pk[s0:].all() and wv.sum() == min(128, L)
     if L == 3003:
         assert 0 < pk.sum() < L and pv.sum() >= pk.sum()
+
+
+# --------------------------------------------------------------------------- fresh truncated SVD (refit)
+@pytest.mark.parametrize("D,r,b,n,spec,iters,c16", [
+    (128, 16, 32, 600, "exp4", 12, False),
+    (256, 40, 64, 1000, "exp40+0.01", 8, False),
+    (1024, 192, 64, 3000, "exp40+0.01", 6, False),
+    (1024, 320, 64, 3000, "invsqrt", 6, True),
+])
+def test_refit_reaches_fresh_truncated_svd(K, D, r, b, n, spec, iters, c16):
+    """isvd_refit (Algorithm 1 step 7, the value first refit of §3.2): the
+    handle's old history is dropped; with iters = 0 the factors are the
+    oracle's fold of the rows; the iterations bring the error down towards the
+    Eckart-Young optimum of the oracle's fresh truncated SVD and never below
+    it, with orthonormal B and the rows' positions kept."""
+    X = synth.kv_stream(synth.StreamSpec(D=D, n=n, spectrum=spec, noise_std=0.0, seed=70 + D + r))
+    Xd = torch.from_numpy(X).to(DEV)
+    pos = (1000 + 3 * torch.arange(n, dtype=torch.int32)).to(DEV)
+    path = K.IsvdPath(D=D, r_max=r, b_max=b, n_cap=n + 64, device=DEV, coords_bf16=c16)
+    old = torch.randn((b, D), device=DEV)
+    path.merge(old, torch.arange(b, dtype=torch.int32, device=DEV))   # history the refit replaces
+    Xr, disc = O.fresh_truncated_svd(X, r)
+    nx = np.linalg.norm(X)
+    opt = math.sqrt(float(np.sum(disc ** 2))) / nx
+    errs = {}
+    for it in (0, iters):
+        path.refit(Xd, pos, iters=it)
+        torch.cuda.synchronize()
+        C, B, s, p, st = gpu_factors(path)
+        assert st == 0 and C.shape[0] == n
+        assert np.array_equal(p, pos.cpu().numpy())
+        errs[it] = np.linalg.norm(X - C @ B.T) / nx
+        assert np.abs(B.T @ B - np.eye(B.shape[1])).max() < 1e-4
+        if it == 0 and not c16:
+            ref = O.represented(O.run_stream(X, b, r))
+            assert rel(C @ B.T, ref) < 1e-3
+    sv = np.linalg.svd(X.astype(np.float64), compute_uv=False)[:r]
+    print(f"D={D} r={r} {spec}: optimum {opt:.6e}, fold {errs[0]:.6e}, {iters} iterations {errs[iters]:.6e}; "
+          f"sigma rel {np.abs(s - sv).max() / sv[0]:.2e}; to X_r {rel(C @ B.T, Xr):.2e}")
+    floor = 4e-3 if c16 else 2e-5   # coordinate rounding (bf16: 2^-8 relative) and fp32 products
+    assert errs[iters] >= opt * (1 - 1e-6) - floor
+    assert errs[iters] <= errs[0] + floor
+    assert errs[iters] - opt <= 0.25 * (errs[0] - opt) + floor
+    # Ritz values approach the singular values from below (Poincare
+    # interlacing for C = X B with B orthonormal); the leading half, far from
+    # the cut, have converged
+    tol = 5e-3 if c16 else 1e-5
+    assert np.all(s <= sv * (1 + tol) + tol * sv[0])
+    h = r // 2
+    assert np.abs(s[:h] - sv[:h]).max() < (5e-3 if c16 else 1e-4) * sv[0]
