@@ -33,6 +33,9 @@ __all__ = [
     "merge",
     "reorth",
     "fold_frozen",
+    "truncated_factor",
+    "prefill_init",
+    "value_first_refit",
     "anomaly_block_scores",
     "prompt_protect",
     "persist_coords_bf16",
@@ -294,6 +297,51 @@ def prompt_protect(K_rot: np.ndarray, Hkv: int, dh: int, block: int = 8, per_hea
     wv = np.zeros(L, dtype=bool)
     wv[max(0, L - v_window):] = True
     return pk, pv, wv
+
+
+def truncated_factor(X: np.ndarray, pos, r: int) -> Factor:
+    """A path's factor from the fresh rank-r truncated SVD of its rows
+    (iS-KV notes §2.2; Algorithm 1 step 7). Reading: k = the number of the
+    first min(r, n, D) singular values that are not zero."""
+    X = np.asarray(X, dtype=np.float64)
+    n, D = X.shape
+    if n == 0:
+        return empty_factor(D)
+    u, sv, vt = _svd(X)
+    k = int(np.count_nonzero(sv[:min(r, sv.shape[0])] > 0.0))
+    return Factor(U=u[:, :k].copy(), sigma=sv[:k].copy(), B=vt[:k].T.copy(),
+                  pos=np.asarray(pos, dtype=np.int64).copy(), folded=0)
+
+
+def prefill_init(K_pre: np.ndarray, K_rot: np.ndarray, V: np.ndarray, Hkv: int, dh: int, r_K: int, r_V: int,
+                 block: int = 8, per_head: int = 128, suffix_blocks: int = 4, v_radius: int = 32,
+                 v_window: int = 128):
+    """Prompt initialisation (iS-KV notes §3.1, Algorithm 1 steps 2-9).
+
+    The exact sets come from the post-RoPE keys: E_K = P_K and
+    E_V = P_V | W_V (W_K is empty). Each path keeps its exact rows as they are
+    and replaces the rest by the fresh truncated SVD of those rows in position
+    order (rank r_K for the pre-RoPE keys, r_V for the values), with their
+    positions saved. Returns (factor_K, factor_V, E_K, E_V), E as boolean
+    masks of length L. The pending queue starts empty and the value first
+    refit is still to come (value_first_refit).
+    """
+    pk, pv, wv = prompt_protect(K_rot, Hkv, dh, block, per_head, suffix_blocks, v_radius, v_window)
+    E_K, E_V = pk, pv | wv
+    idx = np.arange(np.asarray(K_pre).shape[0])
+    fac_K = truncated_factor(np.asarray(K_pre)[~E_K], idx[~E_K], r_K)
+    fac_V = truncated_factor(np.asarray(V)[~E_V], idx[~E_V], r_V)
+    return fac_K, fac_V, E_K, E_V
+
+
+def value_first_refit(fac_V: Factor, rows: np.ndarray, pos_rows, r_V: int) -> Factor:
+    """The value first refit (iS-KV notes §3.2): once r_V value rows have
+    left the recent window, the value path is rebuilt as the fresh rank-r_V
+    truncated SVD of its reconstructed history followed by those rows, and
+    block folds take over afterwards."""
+    X = np.concatenate([represented(fac_V), np.asarray(rows, dtype=np.float64)], axis=0)
+    pos = np.concatenate([fac_V.pos, np.asarray(pos_rows, dtype=np.int64)])
+    return truncated_factor(X, pos, r_V)
 
 
 def fold_frozen(C: np.ndarray, B: np.ndarray, pos, F: np.ndarray, pos_F):

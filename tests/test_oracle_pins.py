@@ -494,3 +494,62 @@ def test_anomaly_scores_and_protect_pins():
     sc4, s4 = O.anomaly_block_scores(K[:30], Hkv, dh)
     assert sc4.shape == (2, 0) and s4 == 0
     assert O.prompt_protect(K[:30], Hkv, dh)[0].all()
+
+
+def _orthonormal(rng, n, k):
+    q, _ = np.linalg.qr(rng.standard_normal((n, k)))
+    return q
+
+
+def test_truncated_factor_and_prefill_init_pins():
+    """Algorithm 1 steps 7-9 (notes §3.1): each path's factor covers exactly its
+    non-exact rows (positions saved in order; the exact rows, here planted
+    with huge values, never reach it), a non-exact part of rank <= r is
+    reproduced exactly, and truncation keeps the r largest of known singular
+    values with error^2 = the sum of the rest (Eckart-Young, closed form)."""
+    rng = np.random.default_rng(81)
+    Hkv, dh = 2, 8
+    D, L = Hkv * dh, 8 * 40
+    K_rot = rng.standard_normal((L, D))
+    pk, pv, wv = O.prompt_protect(K_rot, Hkv, dh, per_head=3)
+    E_K, E_V = pk, pv | wv
+    assert 0 < (~E_K).sum() and 0 < (~E_V).sum() < (~E_K).sum()
+    K_pre = 1e6 * rng.standard_normal((L, D))
+    V = 1e6 * rng.standard_normal((L, D))
+    K_pre[~E_K] = rng.standard_normal(((~E_K).sum(), 3)) @ rng.standard_normal((3, D))
+    V[~E_V] = rng.standard_normal(((~E_V).sum(), 4)) @ rng.standard_normal((4, D))
+    fK, fV, eK, eV = O.prefill_init(K_pre, K_rot, V, Hkv, dh, r_K=5, r_V=4, per_head=3)
+    assert np.array_equal(eK, E_K) and np.array_equal(eV, E_V)
+    assert np.array_equal(fK.pos, np.nonzero(~E_K)[0]) and np.array_equal(fV.pos, np.nonzero(~E_V)[0])
+    for f, X in ((fK, K_pre[~E_K]), (fV, V[~E_V])):
+        assert np.abs(O.represented(f) - X).max() < 1e-10 * np.abs(X).max()
+        assert np.abs(f.B.T @ f.B - np.eye(f.k)).max() < 1e-12
+    # known singular values 5, 4, 3, 2, 1: rank 2 keeps 5 and 4, error^2 = 9 + 4 + 1
+    sv = np.array([5.0, 4.0, 3.0, 2.0, 1.0])
+    Q1, Q2 = _orthonormal(rng, 40, 5), _orthonormal(rng, D, 5)
+    X = (Q1 * sv) @ Q2.T
+    f = O.truncated_factor(X, np.arange(100, 140), 2)
+    assert np.allclose(f.sigma, [5.0, 4.0], atol=1e-12)
+    assert abs(np.linalg.norm(X - O.represented(f)) ** 2 - 14.0) < 1e-10
+    assert np.allclose(np.abs(f.B.T @ Q2[:, :2]), np.eye(2), atol=1e-12)
+    assert np.array_equal(f.pos, np.arange(100, 140))
+    assert O.truncated_factor(np.zeros((0, D)), [], 4).n == 0
+
+
+def test_value_first_refit_pins():
+    """§3.2 value first refit: the fresh SVD of [reconstructed history; rows].
+    History rows 5 e1 and 4 e2, a new row 3 e3, rank 2: keeps 5 and 4 and
+    loses the new row (error^2 = 9); with the new row 6 e3 the refit keeps
+    6 and 5 and drops an old direction (error^2 = 16); positions: the
+    history's, then the new rows'. Rank <= r: exact."""
+    D = 6
+    e = np.eye(D)
+    hist = O.truncated_factor(np.stack([5 * e[0], 4 * e[1]]), [7, 9], 2)
+    for new, keep, err2 in ((3.0, [5.0, 4.0], 9.0), (6.0, [6.0, 5.0], 16.0)):
+        f = O.value_first_refit(hist, (new * e[2])[None, :], [30], 2)
+        assert np.allclose(f.sigma, keep, atol=1e-12)
+        stacked = np.stack([5 * e[0], 4 * e[1], new * e[2]])
+        assert abs(np.linalg.norm(stacked - O.represented(f)) ** 2 - err2) < 1e-10
+        assert list(f.pos) == [7, 9, 30]
+    f = O.value_first_refit(hist, np.stack([e[0] + e[1], 2 * e[1]]), [30, 31], 3)
+    assert np.abs(O.represented(f) - np.stack([5 * e[0], 4 * e[1], e[0] + e[1], 2 * e[1]])).max() < 1e-12
