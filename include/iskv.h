@@ -325,6 +325,37 @@ size_t isvd_refit_workspace_bytes(const isvd_handle* h);
 int isvd_refit(isvd_handle* h, const float* X, const int32_t* pos, int32_t n, int32_t iters, void* work,
                size_t work_bytes);
 
+/* The value first refit (iS-KV notes §3.2): once r_V value rows have left the
+ * recent window, the value path is rebuilt from its reconstructed history
+ * (C B^T in the handle's row order, positions kept) followed by those rows,
+ * by isvd_refit over the stacked rows; block folds take over afterwards.
+ *   F      device fp32 [count x D], the rows that left the window (count >= 0).
+ *   pos_F  device int32 [count], their positions.
+ *   work   device buffer of >= isvd_value_first_refit_workspace_bytes(h)
+ *          bytes (holds the stacked rows: about n_cap x D x 4 bytes).
+ * Errors: as isvd_refit; ECAPACITY when history + count > n_cap. */
+size_t isvd_value_first_refit_workspace_bytes(const isvd_handle* h);
+int isvd_value_first_refit(isvd_handle* h, const float* F, const int32_t* pos_F, int32_t count, int32_t iters,
+                           void* work, size_t work_bytes);
+
+/* Split the prompt's rows by their flags (iS-KV notes Algorithm 1 steps 7-8):
+ * row p (position pos0 + p) is kept exact when flags[p] & mask, otherwise it
+ * belongs to the rows the path's factor is built from; both lists keep
+ * position order. For the keys mask = 1 (E_K = P_K), for the values
+ * mask = 6 (E_V = P_V | W_V), with the flags of iskv_prompt_protect.
+ *   X        device fp32 [L x D], 16-byte aligned, D a multiple of 4.
+ *   X_keep, pos_keep   device [L x D] fp32 / [L] int32 (either may be NULL
+ *            to drop the exact rows or their positions); X_rest, pos_rest
+ *            likewise for the other rows.
+ *   counts   device int32 [2]: the exact and the other row counts (L = 0:
+ *            both zero; X, flags and workspace are then not read).
+ *   workspace  >= iskv_prompt_split_workspace_bytes(L) bytes.
+ * Errors: EINVAL, EWORKSPACE, EHIP. */
+size_t iskv_prompt_split_workspace_bytes(int32_t L);
+int iskv_prompt_split(const float* X, const uint8_t* flags, int32_t L, int32_t D, uint32_t mask, int32_t pos0,
+                      float* X_keep, int32_t* pos_keep, float* X_rest, int32_t* pos_rest, int32_t* counts,
+                      void* workspace, size_t ws_bytes, void* stream);
+
 
 /* Exact-row sets of a prompt (iS-KV notes §3.1, Algorithm 1 steps 2-6), from
  * its post-RoPE keys. The prompt is cut into blocks of `block` tokens; the last

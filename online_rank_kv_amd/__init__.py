@@ -18,7 +18,9 @@ import os
 
 __all__ = [
     "LIB_PATH", "lib", "IskvError", "IskvConfig", "ISKV_NO_COORD_SYNC", "ISKV_NO_GRAPH", "ISKV_FROZEN_BASIS",
-    "ISKV_BF16_COORDS", "isvd_refit_workspace_bytes", "isvd_refit", "iskv_prompt_protect_workspace_bytes", "iskv_prompt_protect", "prompt_protect",
+    "ISKV_BF16_COORDS", "isvd_refit_workspace_bytes", "isvd_refit", "isvd_value_first_refit_workspace_bytes",
+    "isvd_value_first_refit", "iskv_prompt_split_workspace_bytes", "iskv_prompt_split", "prompt_split",
+    "prefill_init", "iskv_prompt_protect_workspace_bytes", "iskv_prompt_protect", "prompt_protect",
     "ISKV_OUT_BF16", "isvd_set_mode",
     "ISKV_OUT_FP32", "ISKV_DEV_NONFINITE", "ISKV_DEV_NOCONV", "EXPORTED_SYMBOLS",
     "isvd_workspace_bytes", "isvd_init", "isvd_merge_block", "isvd_reorth", "isvd_query",
@@ -56,6 +58,8 @@ EXPORTED_SYMBOLS = (
     "isvd_set_timing", "isvd_stage_times", "iskv_window_append_batched",
     "decode_attend_fv_workspace_bytes", "decode_attend_fv", "isvd_set_mode",
     "iskv_prompt_protect_workspace_bytes", "iskv_prompt_protect", "isvd_refit_workspace_bytes", "isvd_refit",
+    "isvd_value_first_refit_workspace_bytes", "isvd_value_first_refit", "iskv_prompt_split_workspace_bytes",
+    "iskv_prompt_split",
 )
 
 
@@ -95,6 +99,15 @@ lib.isvd_refit_workspace_bytes.restype = ctypes.c_size_t
 lib.isvd_refit_workspace_bytes.argtypes = [_vp]
 lib.isvd_refit.restype = ctypes.c_int
 lib.isvd_refit.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp, ctypes.c_size_t]
+lib.isvd_value_first_refit_workspace_bytes.restype = ctypes.c_size_t
+lib.isvd_value_first_refit_workspace_bytes.argtypes = [_vp]
+lib.isvd_value_first_refit.restype = ctypes.c_int
+lib.isvd_value_first_refit.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp, ctypes.c_size_t]
+lib.iskv_prompt_split_workspace_bytes.restype = ctypes.c_size_t
+lib.iskv_prompt_split_workspace_bytes.argtypes = [_i32]
+lib.iskv_prompt_split.restype = ctypes.c_int
+lib.iskv_prompt_split.argtypes = [_vp, _vp, _i32, _i32, ctypes.c_uint32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                  ctypes.c_size_t, _vp]
 lib.iskv_prompt_protect_workspace_bytes.restype = ctypes.c_size_t
 lib.iskv_prompt_protect_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
 lib.iskv_prompt_protect.restype = ctypes.c_int
@@ -210,6 +223,71 @@ def isvd_refit_workspace_bytes(h: int) -> int:
 def isvd_refit(h: int, X, pos, n: int, iters: int, work) -> None:
     nbytes = 0 if work is None else work.numel() * work.element_size()
     _check(lib.isvd_refit(h, _ptr(X), _ptr(pos), int(n), int(iters), _ptr(work), nbytes), "isvd_refit")
+
+
+def isvd_value_first_refit_workspace_bytes(h: int) -> int:
+    return int(lib.isvd_value_first_refit_workspace_bytes(h))
+
+
+def isvd_value_first_refit(h: int, F, pos_F, count: int, iters: int, work) -> None:
+    nbytes = 0 if work is None else work.numel() * work.element_size()
+    _check(lib.isvd_value_first_refit(h, _ptr(F), _ptr(pos_F), int(count), int(iters), _ptr(work), nbytes),
+           "isvd_value_first_refit")
+
+
+def iskv_prompt_split_workspace_bytes(L: int) -> int:
+    return int(lib.iskv_prompt_split_workspace_bytes(int(L)))
+
+
+def iskv_prompt_split(X, flags, L: int, D: int, mask: int, pos0: int, X_keep, pos_keep, X_rest, pos_rest, counts,
+                      workspace, stream=None) -> None:
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.iskv_prompt_split(_ptr(X), _ptr(flags), int(L), int(D), int(mask), int(pos0), _ptr(X_keep),
+                                 _ptr(pos_keep), _ptr(X_rest), _ptr(pos_rest), _ptr(counts), _ptr(workspace),
+                                 nbytes, _stream_ptr(stream)), "iskv_prompt_split")
+
+
+def prompt_split(X, flags, mask: int, pos0: int = 0, stream=None):
+    """Rows of X (fp32 [L, D] on the device) kept exact (flags & mask) and the
+    others, each in position order with their positions; the two counts are
+    read back. Returns (X_keep, pos_keep, X_rest, pos_rest) trimmed to them."""
+    import torch
+    L, D = int(X.shape[0]), int(X.shape[1])
+    dev = X.device
+    X_keep = torch.empty((max(L, 1), D), dtype=torch.float32, device=dev)
+    X_rest = torch.empty((max(L, 1), D), dtype=torch.float32, device=dev)
+    pos_keep = torch.empty((max(L, 1),), dtype=torch.int32, device=dev)
+    pos_rest = torch.empty((max(L, 1),), dtype=torch.int32, device=dev)
+    counts = torch.empty((2,), dtype=torch.int32, device=dev)
+    ws = torch.empty((max(iskv_prompt_split_workspace_bytes(L), 1),), dtype=torch.uint8, device=dev)
+    iskv_prompt_split(X, flags, L, D, mask, pos0, X_keep, pos_keep, X_rest, pos_rest, counts, ws, stream)
+    nk, nr = (int(v) for v in counts.cpu().tolist())
+    return X_keep[:nk], pos_keep[:nk], X_rest[:nr], pos_rest[:nr]
+
+
+def prefill_init(kpath, vpath, K_pre, K_rot, V, Hkv: int, dh: int, block: int = 8, per_head: int = 128,
+                 suffix_blocks: int = 4, v_radius: int = 32, v_window: int = 128, iters: int = 6):
+    """Prompt initialisation (iS-KV notes §3.1, Algorithm 1 steps 2-9) of one
+    layer's key and value paths (fresh handles, fp32 rows on the device):
+    exact sets from the post-RoPE keys K_rot (bf16 [L, Hkv * dh]), E_K = P_K
+    and E_V = P_V | W_V; each path's other rows (pre-RoPE keys K_pre, values
+    V) replaced by their fresh truncated SVD (isvd_refit) with positions
+    saved. Returns ((K_exact, pos_K), (V_exact, pos_V), flags): the exact rows
+    each path keeps, in position order, and the flags of every position."""
+    import torch
+    L = int(K_pre.shape[0])
+    dev = K_pre.device
+    flags = torch.empty((L,), dtype=torch.uint8, device=dev)
+    ws = torch.empty((iskv_prompt_protect_workspace_bytes(L, Hkv, block, suffix_blocks),), dtype=torch.uint8,
+                     device=dev)
+    iskv_prompt_protect(K_rot, L, Hkv, dh, block, per_head, suffix_blocks, v_radius, v_window, flags, None, ws)
+    out = []
+    for path, X, mask in ((kpath, K_pre, 1), (vpath, V, 6)):
+        Xk, pk, Xr, pr = prompt_split(X, flags, mask)
+        if Xr.shape[0] > 0:
+            path.refit(Xr, pr, iters=iters)
+        out.append((Xk, pk))
+    return out[0], out[1], flags
 
 
 def iskv_prompt_protect_workspace_bytes(L: int, Hkv: int, block: int = 8, suffix_blocks: int = 4) -> int:
@@ -403,6 +481,14 @@ class IsvdPath:
         if iters > 0:
             work = torch.empty((isvd_refit_workspace_bytes(self.h),), dtype=torch.uint8, device=self.C.device)
         isvd_refit(self.h, X, pos, int(X.shape[0]), iters, work)
+        self._refit_work = work  # kept until the stream has used it
+
+    def value_first_refit(self, F, pos_F, iters: int = 6) -> None:
+        """The value first refit: fresh truncated SVD of [history; F]."""
+        import torch
+        work = torch.empty((isvd_value_first_refit_workspace_bytes(self.h),), dtype=torch.uint8,
+                           device=self.C.device)
+        isvd_value_first_refit(self.h, F, pos_F, int(F.shape[0]), iters, work)
         self._refit_work = work  # kept until the stream has used it
 
     def set_mode(self, mode: int) -> None:

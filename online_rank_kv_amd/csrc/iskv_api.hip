@@ -167,6 +167,68 @@ int isvd_refit(isvd_handle* h, const float* X, const int32_t* pos, int32_t n, in
   return iskv_launch_refit_iterations(h, X, n, iters, work);
 }
 
+// Workspace of the value first refit: the refit's, then B^T (r_max x D), the
+// stacked rows (n_cap x D) and their positions (n_cap), 256-byte aligned.
+static size_t vfr_offsets(const isvd_handle* h, size_t* o_bt, size_t* o_x, size_t* o_pos) {
+  const iskv_config& c = h->cfg;
+  auto al = [](size_t b) { return (b + 255) / 256 * 256; };
+  *o_bt = al(iskv_refit_ws_bytes(h));
+  *o_x = *o_bt + al((size_t)c.r_max * c.D * sizeof(float));
+  *o_pos = *o_x + al((size_t)c.n_cap * c.D * sizeof(float));
+  return *o_pos + al((size_t)c.n_cap * sizeof(int32_t));
+}
+
+size_t isvd_value_first_refit_workspace_bytes(const isvd_handle* h) {
+  if (!h) return 0;
+  size_t a, b, c;
+  return vfr_offsets(h, &a, &b, &c);
+}
+
+int isvd_value_first_refit(isvd_handle* h, const float* F, const int32_t* pos_F, int32_t count, int32_t iters,
+                           void* work, size_t work_bytes) {
+  if (!h || count < 0 || (count > 0 && (!F || !pos_F)) || iters < 0 || iters > 64) return ISKV_EINVAL;
+  if (h->cfg.flags & (ISKV_NO_COORD_SYNC | ISKV_FROZEN_BASIS)) return ISKV_EMODE;
+  const int64_t n = (int64_t)h->n_host + count;
+  if (n > h->cfg.n_cap) return ISKV_ECAPACITY;
+  if (n == 0) return ISKV_OK;
+  if (iters > 0 && !iskv_refit_supported(h->cfg)) return ISKV_EINVAL;
+  size_t o_bt, o_x, o_pos;
+  const size_t need = vfr_offsets(h, &o_bt, &o_x, &o_pos);
+  if (!work || work_bytes < need) return ISKV_EWORKSPACE;
+  char* wb = (char*)work;
+  float* Xs = (float*)(wb + o_x);
+  int32_t* Ps = (int32_t*)(wb + o_pos);
+  const size_t D = h->cfg.D;
+  const int32_t n_old = h->n_host;
+  hipStream_t s = h->stream;
+  // [reconstructed history; F] with positions [history's; pos_F]
+  int rc = iskv_launch_materialize(h, Xs, (float*)(wb + o_bt));
+  if (rc) return rc;
+  if (n_old > 0)
+    ISKV_HIP_CHECK(hipMemcpyAsync(Ps, h->pos, (size_t)n_old * sizeof(int32_t), hipMemcpyDeviceToDevice, s));
+  if (count > 0) {
+    ISKV_HIP_CHECK(hipMemcpyAsync(Xs + (size_t)n_old * D, F, (size_t)count * D * sizeof(float),
+                                  hipMemcpyDeviceToDevice, s));
+    ISKV_HIP_CHECK(hipMemcpyAsync(Ps + n_old, pos_F, (size_t)count * sizeof(int32_t), hipMemcpyDeviceToDevice, s));
+  }
+  return isvd_refit(h, Xs, Ps, (int32_t)n, iters, work, work_bytes);
+}
+
+// ---- prompt split ------------------------------------------------------------
+size_t iskv_prompt_split_workspace_bytes(int32_t L) { return iskv_prompt_split_ws_bytes(L); }
+
+int iskv_prompt_split(const float* X, const uint8_t* flags, int32_t L, int32_t D, uint32_t mask, int32_t pos0,
+                      float* X_keep, int32_t* pos_keep, float* X_rest, int32_t* pos_rest, int32_t* counts,
+                      void* workspace, size_t ws_bytes, void* stream) {
+  if (!counts || L < 0 || D < 4 || D % 4 != 0 || pos0 < 0) return ISKV_EINVAL;
+  if ((int64_t)pos0 + L > INT32_MAX) return ISKV_EINVAL;
+  if (L > 0 && (!X || !flags || !workspace)) return ISKV_EINVAL;
+  if ((uintptr_t)X % 16 || (uintptr_t)X_keep % 16 || (uintptr_t)X_rest % 16) return ISKV_EINVAL;
+  if (ws_bytes < iskv_prompt_split_ws_bytes(L)) return ISKV_EWORKSPACE;
+  return iskv_launch_prompt_split(X, flags, L, D, mask, pos0, X_keep, pos_keep, X_rest, pos_rest, counts, workspace,
+                                  (hipStream_t)stream);
+}
+
 int32_t isvd_rows(const isvd_handle* h) { return h ? h->n_host : 0; }
 
 int isvd_query_state(isvd_handle* h, int32_t* state, int32_t count) {

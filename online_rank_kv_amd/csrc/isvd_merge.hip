@@ -1541,7 +1541,36 @@ __global__ __launch_bounds__(256) void refit_basis_kernel(const float* __restric
 
 constexpr int RF_CHUNKS = 16;  // row chunks of X^T C
 
+// Bt[j][d] = B[d][j] (32 x 32 tiles through LDS).
+__global__ __launch_bounds__(256) void transpose_b_kernel(const float* __restrict__ B, int D, int R,
+                                                          float* __restrict__ Bt) {
+  __shared__ float tile[32][33];
+  const int d0 = blockIdx.x * 32, j0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int yy = ty; yy < 32; yy += 8)
+    tile[yy][tx] = (d0 + yy < D && j0 + tx < R) ? B[(size_t)(d0 + yy) * R + j0 + tx] : 0.f;
+  __syncthreads();
+  for (int yy = ty; yy < 32; yy += 8)
+    if (j0 + yy < R && d0 + tx < D) Bt[(size_t)(j0 + yy) * D + d0 + tx] = tile[tx][yy];
+}
+
 }  // namespace
+
+// Y (n x D, fp32, path order) = C B^T: the rows the history represents.
+int iskv_launch_materialize(isvd_handle* h, float* Y, float* Bt) {
+  const iskv_config& c = h->cfg;
+  hipStream_t s = h->stream;
+  const int D = c.D, R = c.r_max, n = h->n_host;
+  if (n == 0) return ISKV_OK;
+  if (xh_lds_bytes(16, R) > 160 * 1024) return ISKV_EINVAL;
+  hipLaunchKernelGGL(transpose_b_kernel, dim3((D + 31) / 32, (R + 31) / 32), dim3(256), 0, s, h->B, D, R, Bt);
+  with_coords(h, [&](auto* Cp) {
+    xh_launch(s, nullptr, 1, n, Cp, R, nullptr, 0, ddim(h->w.st + ST_K), ddim(h->w.st + ST_K), R, Bt, D, D, hdim(D),
+              hdim(n), Y, D, nullptr, 0, nullptr, nullptr, true);
+  });
+  ISKV_HIP_CHECK(hipGetLastError());
+  return ISKV_OK;
+}
 
 // C <- X B stages 16 rows of X (D wide) in LDS: D up to 1984.
 bool iskv_refit_supported(const iskv_config& c) { return xh_lds_bytes(16, c.D) <= 160 * 1024; }

@@ -126,6 +126,59 @@ __global__ __launch_bounds__(256) void flags_kernel(const uint8_t* __restrict__ 
   flags[p] = (uint8_t)((pk ? 1 : 0) | (pv ? 2 : 0) | (wv ? 4 : 0));
 }
 
+// Split of the prompt rows by their flags (Algorithm 1 steps 7-8): row p is
+// kept exact when flags[p] & mask, else it goes to the rows the factor is
+// built from; both lists stay in position order. One workgroup ranks all
+// positions: thread t owns a contiguous run of them, the runs' keep counts
+// are scanned over the workgroup, and dest[p] receives the row's slot
+// (>= 0 in the exact list, -1 - slot in the other).
+__global__ __launch_bounds__(1024) void split_scan_kernel(const uint8_t* __restrict__ flags, int L, unsigned mask,
+                                                          int32_t* __restrict__ dest, int32_t* __restrict__ counts) {
+  __shared__ int wsum[16];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int run = (L + 1023) / 1024;
+  const int p0 = min(L, t * run), p1 = min(L, p0 + run);
+  int keep = 0;
+  for (int p = p0; p < p1; ++p) keep += (flags[p] & mask) ? 1 : 0;
+  int incl = keep;  // inclusive scan over the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+  for (int w = 0; w < 16; ++w) {
+    before += w < wv ? wsum[w] : 0;
+    total += wsum[w];
+  }
+  int k = before + incl - keep;  // exact rows before this run
+  int rr = p0 - k;               // other rows before this run
+  for (int p = p0; p < p1; ++p) dest[p] = (flags[p] & mask) ? k++ : -1 - rr++;
+  if (t == 0) {
+    counts[0] = total;
+    counts[1] = L - total;
+  }
+}
+
+// Row p moves to its slot (float4 copies) with its position pos0 + p.
+__global__ __launch_bounds__(256) void split_gather_kernel(const float* __restrict__ X, int D,
+                                                           const int32_t* __restrict__ dest, int pos0,
+                                                           float* __restrict__ X_keep, int32_t* __restrict__ pos_keep,
+                                                           float* __restrict__ X_rest, int32_t* __restrict__ pos_rest) {
+  const int p = blockIdx.x;
+  const int d = dest[p];
+  float* out = d >= 0 ? X_keep : X_rest;
+  int32_t* po = d >= 0 ? pos_keep : pos_rest;
+  const int slot = d >= 0 ? d : -1 - d;
+  if (!out) return;
+  const float4* src = reinterpret_cast<const float4*>(X + (size_t)p * D);
+  float4* dst = reinterpret_cast<float4*>(out + (size_t)slot * D);
+  for (int i = threadIdx.x; i < D / 4; i += 256) dst[i] = src[i];
+  if (threadIdx.x == 0 && po) po[slot] = pos0 + p;
+}
+
 inline int pp_scored_blocks(int L, int block, int suffix_blocks) {
   const int nb = L / block - suffix_blocks;
   return nb > 0 ? nb : 0;
@@ -154,6 +207,20 @@ int iskv_launch_prompt_protect(const uint16_t* K_rot, int32_t L, int32_t Hkv, in
   }
   hipLaunchKernelGGL(flags_kernel, dim3((L + 255) / 256), dim3(256), 0, s, sel, Hkv, nb, L, block, v_radius,
                      v_window, flags);
+  ISKV_HIP_CHECK(hipGetLastError());
+  return ISKV_OK;
+}
+
+size_t iskv_prompt_split_ws_bytes(int32_t L) { return L < 0 ? 0 : ((size_t)L * sizeof(int32_t) + 255) / 256 * 256; }
+
+int iskv_launch_prompt_split(const float* X, const uint8_t* flags, int32_t L, int32_t D, uint32_t mask, int32_t pos0,
+                             float* X_keep, int32_t* pos_keep, float* X_rest, int32_t* pos_rest, int32_t* counts,
+                             void* ws, hipStream_t s) {
+  int32_t* dest = (int32_t*)ws;
+  hipLaunchKernelGGL(split_scan_kernel, dim3(1), dim3(1024), 0, s, flags, L, mask, dest, counts);
+  if (L > 0)
+    hipLaunchKernelGGL(split_gather_kernel, dim3(L), dim3(256), 0, s, X, D, dest, pos0, X_keep, pos_keep, X_rest,
+                       pos_rest);
   ISKV_HIP_CHECK(hipGetLastError());
   return ISKV_OK;
 }

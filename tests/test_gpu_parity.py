@@ -906,3 +906,82 @@ def test_refit_reaches_fresh_truncated_svd(K, D, r, b, n, spec, iters, c16):
     assert np.all(s <= sv * (1 + tol) + tol * sv[0])
     h = r // 2
     assert np.abs(s[:h] - sv[:h]).max() < (5e-3 if c16 else 1e-4) * sv[0]
+
+
+# --------------------------------------------------------------------------- prompt initialisation
+@pytest.mark.parametrize("L,D,mask", [(0, 64, 1), (1, 64, 1), (1000, 64, 6), (4097, 1024, 1), (8192, 1024, 6)])
+def test_prompt_split_exact(K, L, D, mask):
+    """Algorithm 1 steps 7-8: rows split by flags & mask, both lists in
+    position order, rows and positions bit-exact."""
+    rng = np.random.default_rng(90 + L)
+    X = rng.standard_normal((L, D)).astype(np.float32)
+    fl = rng.integers(0, 8, size=L).astype(np.uint8)
+    Xk, pk, Xr, pr = K.prompt_split(torch.from_numpy(X).to(DEV), torch.from_numpy(fl).to(DEV), mask, pos0=5)
+    keep = (fl & mask) != 0
+    assert np.array_equal(pk.cpu().numpy(), 5 + np.nonzero(keep)[0])
+    assert np.array_equal(pr.cpu().numpy(), 5 + np.nonzero(~keep)[0])
+    assert np.array_equal(Xk.cpu().numpy(), X[keep]) and np.array_equal(Xr.cpu().numpy(), X[~keep])
+
+
+def _prompt_inputs(L, Hkv, dh, seed):
+    """Post-RoPE keys with planted anomalies (bf16), pre-RoPE keys and values
+    from the key and value spectra (fp32)."""
+    rng = np.random.default_rng(seed)
+    Kr = rng.standard_normal((L, Hkv * dh)).astype(np.float32)
+    for j in range(0, L // 8, 5):
+        Kr[8 * j + 2] = -2.0 * Kr[8 * j + 2]
+    Kb = torch.from_numpy(Kr).bfloat16()
+    D = Hkv * dh
+    K_pre = synth.kv_stream(synth.StreamSpec(D=D, n=L, spectrum="exp40+0.01", noise_std=0.0, seed=seed))
+    V = synth.kv_stream(synth.StreamSpec(D=D, n=L + 512, spectrum="invsqrt", noise_std=0.0, seed=seed + 1))
+    return Kb, K_pre, V
+
+
+@pytest.mark.parametrize("L,per_head,r_K,r_V", [(3000, 16, 192, 320), (8192, 12, 192, 320)])
+def test_prefill_init_and_value_first_refit(K, L, per_head, r_K, r_V):
+    """Algorithm 1 (notes §3.1) through the C ABI: the GPU's exact sets and
+    positions equal the oracle's, the exact rows are the prompt's rows
+    bit-exact, each factor's error is within 1% of the oracle's fresh
+    truncated SVD optimum (Eckart-Young) on the same non-exact rows; then the
+    §3.2 value first refit with the first r_V rows after the prompt: positions
+    [history; new], error within 1% of the optimum of the stacked rows."""
+    Hkv, dh = 8, 128
+    D = Hkv * dh
+    Kb, K_pre, Vall = _prompt_inputs(L, Hkv, dh, 300 + L)
+    V = Vall[:L]
+    fK, fV, E_K, E_V = O.prefill_init(K_pre, Kb.double().numpy(), V, Hkv, dh, r_K, r_V, per_head=per_head)
+    kp = K.IsvdPath(D=D, r_max=r_K, b_max=64, n_cap=L + 512, device=DEV)
+    vp = K.IsvdPath(D=D, r_max=r_V, b_max=64, n_cap=L + 512, device=DEV)
+    (Kx, pKx), (Vx, pVx), flags = K.prefill_init(kp, vp, torch.from_numpy(K_pre).to(DEV),
+                                                 Kb.to(DEV).contiguous(), torch.from_numpy(V).to(DEV), Hkv, dh,
+                                                 per_head=per_head)
+    torch.cuda.synchronize()
+    fl = flags.cpu().numpy()
+    assert np.array_equal((fl & 1) != 0, E_K) and np.array_equal((fl & 6) != 0, E_V)
+    assert np.array_equal(pKx.cpu().numpy(), np.nonzero(E_K)[0])
+    assert np.array_equal(pVx.cpu().numpy(), np.nonzero(E_V)[0])
+    assert np.array_equal(Kx.cpu().numpy(), K_pre[E_K]) and np.array_equal(Vx.cpu().numpy(), V[E_V])
+    print(f"L={L}: exact K rows {E_K.sum()}, exact V rows {E_V.sum()}")
+    for path, fac, X, E in ((kp, fK, K_pre, E_K), (vp, fV, V, E_V)):
+        C, B, s, p, st = gpu_factors(path)
+        assert st == 0
+        assert np.array_equal(p, fac.pos)
+        Xr = X[~E].astype(np.float64)
+        err = np.linalg.norm(Xr - C @ B.T) / np.linalg.norm(Xr)
+        opt = np.linalg.norm(Xr - O.represented(fac)) / np.linalg.norm(Xr)
+        print(f"  path r={B.shape[1]}: error {err:.6e}, optimum {opt:.6e}")
+        assert opt * (1 - 1e-6) - 2e-5 <= err <= opt * 1.01 + 2e-5
+        assert np.abs(B.T @ B - np.eye(B.shape[1])).max() < 1e-4
+    # value first refit with the next r_V rows
+    C, B, _, p0, _ = gpu_factors(vp)
+    new = Vall[L:L + r_V]
+    stacked = np.concatenate([C @ B.T, new.astype(np.float64)])
+    ref = O.truncated_factor(stacked, np.concatenate([p0, np.arange(L, L + r_V)]), r_V)
+    vp.value_first_refit(torch.from_numpy(new).to(DEV), torch.arange(L, L + r_V, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    C2, B2, _, p2, st = gpu_factors(vp)
+    assert st == 0 and np.array_equal(p2, ref.pos)
+    err = np.linalg.norm(stacked - C2 @ B2.T) / np.linalg.norm(stacked)
+    opt = np.linalg.norm(stacked - O.represented(ref)) / np.linalg.norm(stacked)
+    print(f"  value first refit: error {err:.6e}, optimum {opt:.6e}")
+    assert opt * (1 - 1e-6) - 2e-5 <= err <= opt * 1.01 + 2e-5
