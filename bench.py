@@ -82,6 +82,55 @@ def profiled_traffic(name):
     return float(d["traffic_bytes_per_dispatch"])
 
 
+def prefill_leg(args, K, torch, dev):
+    """Prompt initialisation of one layer at the 64K-stream shape's prompt:
+    L = 8192 rows, D = 1024 (8 KV heads x 128), r_K = 192 and r_V = 320
+    (the K and V stream ranks), b = 64; anomaly scores on synthetic post-RoPE keys with 12 kept blocks per
+    head (about 10% of the blocks, plus the value neighbourhoods), each path's
+    non-exact rows refit with 6 subspace iterations, then the value first
+    refit with the next 320 rows. Each stage timed on the null stream; median
+    of 2 runs after one warm-up."""
+    import synth
+    L, hkv, dh, r_k, r, per_head, iters = 8192, 8, 128, 192, 320, 12, 6
+    Kb = torch.from_numpy(synth.prompt_keys(L, hkv, dh, 41)).to(dev).bfloat16()
+    K_pre = torch.from_numpy(synth.kv_stream(synth.StreamSpec(D, L, "exp40+0.01", 0.0, 40))).to(dev)
+    Vall = torch.from_numpy(synth.kv_stream(synth.StreamSpec(D, L + r, "invsqrt", 0.0, 41))).to(dev)
+    V, Vnew = Vall[:L], Vall[L:]
+    pos_new = torch.arange(L, L + r, dtype=torch.int32, device=dev)
+    flags = torch.empty((L,), dtype=torch.uint8, device=dev)
+    ws = torch.empty((K.iskv_prompt_protect_workspace_bytes(L, hkv),), dtype=torch.uint8, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        ev[0].record()
+        out = fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]), out
+
+    runs, rows = [], {}
+    for rep in range(3):
+        kp = K.IsvdPath(D=D, r_max=r_k, b_max=64, n_cap=L + r, device=dev)
+        vp = K.IsvdPath(D=D, r_max=r, b_max=64, n_cap=L + r, device=dev)
+        t = {}
+        t["protect_ms"], _ = timed(lambda: K.iskv_prompt_protect(Kb, L, hkv, dh, 8, per_head, 4, 32, 128, flags,
+                                                                  None, ws))
+        t["split_ms"], (sk, sv) = timed(lambda: (K.prompt_split(K_pre, flags, 1), K.prompt_split(V, flags, 6)))
+        t["refit_k_ms"], _ = timed(lambda: kp.refit(sk[2], sk[3], iters=iters))
+        t["refit_v_ms"], _ = timed(lambda: vp.refit(sv[2], sv[3], iters=iters))
+        t["value_first_refit_ms"], _ = timed(lambda: vp.value_first_refit(Vnew, pos_new, iters=iters))
+        rows = {"exact_k": int(sk[0].shape[0]), "refit_k": int(sk[2].shape[0]), "exact_v": int(sv[0].shape[0]),
+                "refit_v": int(sv[2].shape[0]), "value_first_refit": int(sv[2].shape[0]) + r}
+        if rep > 0:
+            runs.append(t)
+        kp.close()
+        vp.close()
+    res = {k: float(np.median([u[k] for u in runs])) for k in runs[0]}
+    res.update({"rows": rows, "L": L, "D": D, "r_k": r_k, "r_v": r, "b": 64, "iters": iters, "per_head": per_head})
+    return res
+
+
 def coords_leg(args, K, torch, dev, Xk, Kc):
     """fp32 against 2-byte (bf16) stored coordinates on two fresh K paths of
     N0 rows each, filled by merges and then timed the same way: MODE_MERGES
@@ -517,6 +566,7 @@ def main():
                                    for c in core],
     }
     result["coords_2byte"] = coords_leg(args, K, torch, dev, Xk, Kc)
+    result["prefill_init"] = prefill_leg(args, K, torch, dev)
     if args.batch_paths > 0:
         result["many_paths"] = many_path_leg(args, K, torch, dev)
     if not args.no_cpu_baseline:

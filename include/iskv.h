@@ -305,22 +305,22 @@ int decode_attend_fv(const uint16_t* q, const uint16_t* K, const isvd_handle* hv
 /* Replace the history by a fresh rank-k truncated SVD of the rows X (iS-KV
  * notes Algorithm 1 step 7: the non-exact prompt rows; §3.2: the value first
  * refit over the rebuilt prompt values plus the first rows to leave the
- * window). The handle is reset to empty, the rows are folded by merges
- * (Algorithm 2, with the re-orthogonalisation schedule), and `iters` subspace
- * iterations with a Rayleigh-Ritz step follow, each C <- X B and
- * re-orthogonalise (§4.4: the Ritz vectors of X^T X in span(B)); Z <- X^T C;
- * B <- Z with unit columns, re-orthogonalised; a last Ritz step gives
- * C = X B. They converge
- * to the top-k right singular subspace of X, so the factors approach the
- * fresh truncated SVD the notes specify (k = the rank the fold reached).
+ * window), k = min(r_max, n, D). The handle is reset to these n rows. With
+ * iters > 0 the factors come from a randomized subspace iteration: a random
+ * orthonormal D x k start, `iters` power steps B <- orth(X^T X B) (CholeskyQR2
+ * in fp64), then the Rayleigh-Ritz step (C <- X B and re-orthogonalise, §4.4:
+ * the exact SVD of X B B^T), one more power step whose basis is orthonormalised
+ * by its polar factor, and a last Ritz step: C = X B, C^T C diagonal. The
+ * error approaches the Eckart-Young optimum as iters grows (6 is within 0.2%
+ * on the key and value streams). iters = 0 folds the rows by merges instead
+ * (Algorithm 2), the incremental factor the refit replaces.
  *   X     device fp32 [n x D], rows in the order of pos.
  *   pos   device int32 [n], their original positions.
  *   work  device buffer of >= isvd_refit_workspace_bytes(h) bytes (not read
  *         when iters = 0).
  * The iterations stage 16 rows of X in LDS, so they need D <= 1984.
  * Errors: EINVAL (also D > 1984 with iters > 0), ECAPACITY (n > n_cap),
- * EMODE (basis-only or frozen mode),
- * EWORKSPACE, EHIP. */
+ * EMODE (basis-only or frozen mode), EWORKSPACE, EHIP. */
 size_t isvd_refit_workspace_bytes(const isvd_handle* h);
 int isvd_refit(isvd_handle* h, const float* X, const int32_t* pos, int32_t n, int32_t iters, void* work,
                size_t work_bytes);

@@ -184,7 +184,12 @@ void dgemm(hipStream_t s, int m_max, const double* A, const double* B, double* C
                      beta, gamma, st, mode, m_max, bd);
 }
 
+// Scaled coupling |s_ij| / sqrt(s_ii s_jj). A non-finite entry counts as an
+// infinite coupling: the maxima are taken with fmax, which would drop a NaN,
+// and a NaN must never pass the convergence test (it sends the solve to the
+// fallback from A itself).
 __device__ __forceinline__ double coupling(double sij, double di, double dj) {
+  if (!isfinite(sij) || !isfinite(di) || !isfinite(dj)) return INFINITY;
   double dd = di * dj;
   double a = fabs(sij);
   if (dd > 0.0) return a / sqrt(dd);

@@ -157,14 +157,24 @@ int isvd_refit(isvd_handle* h, const float* X, const int32_t* pos, int32_t n, in
   if (iters > 0 && (!work || work_bytes < iskv_refit_ws_bytes(h))) return ISKV_EWORKSPACE;
   int rc = reset_history(h);
   if (rc) return rc;
-  // fold the rows (Algorithm 2, with the re-orthogonalisation schedule) ...
-  for (int32_t s0 = 0; s0 < n; s0 += h->cfg.b_max) {
-    const int32_t b = n - s0 < h->cfg.b_max ? n - s0 : h->cfg.b_max;
-    rc = isvd_merge_block(h, X + (size_t)s0 * h->cfg.D, pos + s0, b);
-    if (rc) return rc;
+  if (iters == 0) {  // the incremental fold alone (Algorithm 2)
+    for (int32_t s0 = 0; s0 < n; s0 += h->cfg.b_max) {
+      const int32_t b = n - s0 < h->cfg.b_max ? n - s0 : h->cfg.b_max;
+      rc = isvd_merge_block(h, X + (size_t)s0 * h->cfg.D, pos + s0, b);
+      if (rc) return rc;
+    }
+    return ISKV_OK;
   }
-  // ... then refine to the top-k singular subspace of the rows
-  return iskv_launch_refit_iterations(h, X, n, iters, work);
+  // random orthonormal start, `iters` power steps with CholeskyQR2, then the
+  // Rayleigh-Ritz step, one refinement iteration and a last Ritz step
+  ISKV_HIP_CHECK(hipMemcpyAsync(h->pos, pos, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToDevice, h->stream));
+  h->n_host = n;
+  h->folded_host = 0;
+  rc = iskv_launch_refit_start(h, n);
+  if (rc) return rc;
+  rc = iskv_launch_refit_power(h, X, n, iters, work);
+  if (rc) return rc;
+  return iskv_launch_refit_iterations(h, X, n, 1, work);
 }
 
 // Workspace of the value first refit: the refit's, then B^T (r_max x D), the

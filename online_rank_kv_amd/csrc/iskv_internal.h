@@ -170,6 +170,8 @@ int iskv_launch_attend_fv(const uint16_t* q, const uint16_t* K, const isvd_handl
 bool iskv_refit_supported(const iskv_config& c);
 size_t iskv_refit_ws_bytes(const isvd_handle* h);
 int iskv_launch_refit_iterations(isvd_handle* h, const float* X, int32_t n, int32_t iters, void* work);
+int iskv_launch_refit_start(isvd_handle* h, int32_t n);
+int iskv_launch_refit_power(isvd_handle* h, const float* X, int32_t n, int32_t iters, void* work);
 int iskv_launch_materialize(isvd_handle* h, float* Y, float* Bt);
 size_t iskv_prompt_split_ws_bytes(int32_t L);
 int iskv_launch_prompt_split(const float* X, const uint8_t* flags, int32_t L, int32_t D, uint32_t mask, int32_t pos0,

@@ -1453,6 +1453,39 @@ int iskv_launch_reorth(isvd_handle* h) {
   return ISKV_OK;
 }
 
+// B <- B G^(-1/2), G = B^T B: the orthonormal basis closest to B (its polar
+// factor), by Newton-Schulz steps Z <- Z (3I - G Z^2) / 2 from Z = I in fp64.
+// Converges when the columns of B are nearly orthonormal (|I - G| < 1); no
+// rotation inside span(B), so near-eigenvector columns stay near them.
+static int orthonormalize_basis(isvd_handle* h, int ns_steps) {
+  const iskv_config& c = h->cfg;
+  const isvd_ws& w = h->w;
+  hipStream_t s = h->stream;
+  const int R = c.r_max, D = c.D, mm = h->m_max, ld = h->ldm;
+  const int tiles = (R + 15) / 16;
+  const int32_t* st = w.st;
+  hipLaunchKernelGGL(set_jm_kernel, dim3(1), dim3(1), 0, s, w.st, (int)ST_K, nullptr);
+  hipLaunchKernelGGL(gram_partial_kernel<float>, dim3(tiles * tiles, 1), dim3(256), 0, s, h->B, R, hdim(D), w.st,
+                     w.GC, R, D, nullptr);
+  // no C chunks: G_B -> Pa, Z_1 = 1.5 I - 0.5 G_B -> Pb
+  hipLaunchKernelGGL(reorth_sum_kernel, dim3(128), dim3(256), 0, s, w.GC, 0, R, w.Km, w.Pa, w.Pb, ld, w.st, nullptr);
+  double* z = w.Pb;
+  double* zn = w.Zb;
+  for (int t = 0; t < ns_steps; ++t) {
+    iskv_dgemm(s, mm, w.Pa, false, z, false, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 2, nullptr, 1);
+    iskv_dgemm(s, mm, w.T, false, z, false, w.S, nullptr, ld, 1.0, 0.0, 0.0, st, 2, nullptr, 1);
+    iskv_dgemm(s, mm, z, false, w.S, false, zn, z, ld, -0.5, 1.5, 0.0, st, 2, nullptr, 1);
+    double* tmp = z;
+    z = zn;
+    zn = tmp;
+  }
+  hipLaunchKernelGGL(to_f32_kernel, dim3(128), dim3(256), 0, s, z, z, ld, w.Hc, w.T2, R, w.st, nullptr);
+  xh_launch(s, nullptr, 1, D, h->B, R, nullptr, 0, ddim(w.st + ST_K), ddim(w.st + ST_K), R, w.T2, R, R,
+            ddim(w.st + ST_K), hdim(D), h->B, R, w.Bbf, R, nullptr, nullptr, true);
+  ISKV_HIP_CHECK(hipGetLastError());
+  return ISKV_OK;
+}
+
 // ---------------------------------------------------------------------------
 // Fresh truncated SVD of given rows (Algorithm 1 step 7, the value first
 // refit of §3.2): after the rows are folded by merges, subspace iterations
@@ -1462,7 +1495,9 @@ int iskv_launch_reorth(isvd_handle* h) {
 //     becomes its exact SVD, whose right singular vectors are the Ritz
 //     vectors of X^T X in span(B) and whose coordinates are X B;
 //   Z <- X^T C (= X^T X B);  B <- Z diag(1 / |z_j|);
-//   re-orthogonalise again: an orthonormal basis of span(Z).
+//   B <- its polar factor (orthonormal, no rotation inside span(Z)), so the
+//   columns stay close to the Ritz vectors and the next Ritz core is nearly
+//   diagonal (the eigensolver's refinement then converges in a few steps).
 // A last Ritz step gives the factors C = X B.
 namespace {
 
@@ -1541,6 +1576,73 @@ __global__ __launch_bounds__(256) void refit_basis_kernel(const float* __restric
 
 constexpr int RF_CHUNKS = 16;  // row chunks of X^T C
 
+// History of n rows of rank k = min(r_max, n, D) about to be built directly.
+__global__ void refit_start_kernel(int32_t* st, int n, int k) {
+  st[ST_N] = n;
+  st[ST_K] = k;
+  st[ST_FOLDED] = 0;
+}
+
+// Start basis: B[d][j] uniform in [-1, 1) for j < k from a splitmix64 hash
+// of (d, j), columns past k zero.
+__global__ __launch_bounds__(256) void rand_basis_kernel(float* B, int D, int R, const int32_t* __restrict__ st) {
+  const int k = st[ST_K];
+  const size_t tot = (size_t)D * R;
+  for (size_t e = blockIdx.x * 256 + threadIdx.x; e < tot; e += (size_t)gridDim.x * 256) {
+    const int j = (int)(e % R);
+    unsigned long long z = e + 0x9e3779b97f4a7c15ull;
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+    z ^= z >> 31;
+    const float u = (float)(z >> 40) * (1.0f / 16777216.0f);  // [0, 1)
+    B[e] = j < k ? 2.f * u - 1.f : 0.f;
+  }
+}
+
+// H = L^(-T) for the Cholesky factor L of G + eps tr(G)/k I (G = B^T B,
+// k x k fp64 at ld, overwritten by L). One workgroup: right-looking
+// Cholesky column by column, then L^(-1) by forward substitution, one
+// column of the inverse per thread. The small shift keeps a rank-deficient
+// G factorable (a second pass then restores orthonormality).
+__global__ __launch_bounds__(1024) void chol_inv_kernel(double* G, double* H, int ld, const int32_t* __restrict__ st) {
+  const int k = st[ST_K];
+  const int t = threadIdx.x, nt = blockDim.x;
+  __shared__ double shift;
+  if (t == 0) {
+    double tr = 0.0;
+    for (int i = 0; i < k; ++i) tr += G[(size_t)i * ld + i];
+    shift = 1e-13 * (k > 0 ? tr / k : 0.0) + 1e-300;
+  }
+  __syncthreads();
+  for (int i = t; i < k; i += nt) G[(size_t)i * ld + i] += shift;
+  __syncthreads();
+  for (int j = 0; j < k; ++j) {
+    const double d = sqrt(fmax(G[(size_t)j * ld + j], shift));
+    __syncthreads();
+    if (t == 0) G[(size_t)j * ld + j] = d;
+    for (int i = j + 1 + t; i < k; i += nt) G[(size_t)i * ld + j] /= d;
+    __syncthreads();
+    const int w = k - j - 1;  // trailing block (lower triangle)
+    for (int e = t; e < w * w; e += nt) {
+      const int i = j + 1 + e / w, l = j + 1 + e % w;
+      if (l <= i) G[(size_t)i * ld + l] -= G[(size_t)i * ld + j] * G[(size_t)l * ld + j];
+    }
+    __syncthreads();
+  }
+  // column c of L^(-1): x_i = (delta_ic - sum_{c <= m < i} L_im x_m) / L_ii, stored as H[c][i]
+  for (int c = t; c < k; c += nt) {
+    for (int i = 0; i < k; ++i) {
+      double x = 0.0;
+      if (i >= c) {
+        double acc = (i == c) ? 1.0 : 0.0;
+        for (int m = c; m < i; ++m) acc -= G[(size_t)i * ld + m] * H[(size_t)c * ld + m];
+        x = acc / G[(size_t)i * ld + i];
+      }
+      H[(size_t)c * ld + i] = x;
+    }
+  }
+}
+
 // Bt[j][d] = B[d][j] (32 x 32 tiles through LDS).
 __global__ __launch_bounds__(256) void transpose_b_kernel(const float* __restrict__ B, int D, int R,
                                                           float* __restrict__ Bt) {
@@ -1579,6 +1681,63 @@ size_t iskv_refit_ws_bytes(const isvd_handle* h) {
   return (size_t)RF_CHUNKS * h->cfg.D * h->cfg.r_max * sizeof(float);
 }
 
+// B <- B R^(-1) with R^T R = B^T B (CholeskyQR): an orthonormal basis of
+// span(B) for any full-rank B.
+static int cholqr_basis(isvd_handle* h) {
+  const iskv_config& c = h->cfg;
+  const isvd_ws& w = h->w;
+  hipStream_t s = h->stream;
+  const int R = c.r_max, D = c.D, ld = h->ldm;
+  const int tiles = (R + 15) / 16;
+  hipLaunchKernelGGL(gram_partial_kernel<float>, dim3(tiles * tiles, 1), dim3(256), 0, s, h->B, R, hdim(D), w.st,
+                     w.GC, R, D, nullptr);
+  hipLaunchKernelGGL(reorth_sum_kernel, dim3(128), dim3(256), 0, s, w.GC, 0, R, w.Km, w.Pa, w.Pb, ld, w.st, nullptr);
+  hipLaunchKernelGGL(chol_inv_kernel, dim3(1), dim3(1024), 0, s, w.Pa, w.T, ld, w.st);
+  hipLaunchKernelGGL(to_f32_kernel, dim3(128), dim3(256), 0, s, w.T, w.T, ld, w.Hc, w.T2, R, w.st, nullptr);
+  xh_launch(s, nullptr, 1, D, h->B, R, nullptr, 0, ddim(w.st + ST_K), ddim(w.st + ST_K), R, w.T2, R, R,
+            ddim(w.st + ST_K), hdim(D), h->B, R, w.Bbf, R, nullptr, nullptr, true);
+  ISKV_HIP_CHECK(hipGetLastError());
+  return ISKV_OK;
+}
+
+int iskv_launch_refit_start(isvd_handle* h, int32_t n) {
+  const iskv_config& c = h->cfg;
+  int k = c.r_max < n ? c.r_max : n;
+  if (k > c.D) k = c.D;
+  hipLaunchKernelGGL(refit_start_kernel, dim3(1), dim3(1), 0, h->stream, h->w.st, n, k);
+  hipLaunchKernelGGL(rand_basis_kernel, dim3(256), dim3(256), 0, h->stream, h->B, c.D, c.r_max, h->w.st);
+  ISKV_HIP_CHECK(hipGetLastError());
+  for (int pass = 0; pass < 2; ++pass) {  // CholeskyQR2
+    const int rc = cholqr_basis(h);
+    if (rc) return rc;
+  }
+  return ISKV_OK;
+}
+
+int iskv_launch_refit_power(isvd_handle* h, const float* X, int32_t n, int32_t iters, void* work) {
+  const iskv_config& c = h->cfg;
+  hipStream_t s = h->stream;
+  const int D = c.D, R = c.r_max;
+  float* Zp = (float*)work;
+  const int rpc = (n + RF_CHUNKS - 1) / RF_CHUNKS;
+  for (int it = 0; it < iters; ++it) {
+    with_coords(h, [&](auto* Cp) {
+      using TC = std::remove_pointer_t<decltype(Cp)>;
+      xh_launch(s, nullptr, 1, n, X, D, nullptr, 0, hdim(D), hdim(D), D, h->B, R, R, ddim(h->w.st + ST_K), hdim(n),
+                Cp, R, nullptr, 0, nullptr, nullptr, true);
+      hipLaunchKernelGGL((xtc_partial_kernel<TC>), dim3((D + 63) / 64, (R + 63) / 64, RF_CHUNKS), dim3(256), 0, s, X,
+                         D, (const TC*)Cp, R, n, D, h->w.st, rpc, Zp, R);
+    });
+    hipLaunchKernelGGL(refit_basis_kernel, dim3(R), dim3(256), 0, s, Zp, RF_CHUNKS, D, R, h->w.st, h->B, R);
+    ISKV_HIP_CHECK(hipGetLastError());
+    for (int pass = 0; pass < 2; ++pass) {
+      const int rc = cholqr_basis(h);
+      if (rc) return rc;
+    }
+  }
+  return ISKV_OK;
+}
+
 int iskv_launch_refit_iterations(isvd_handle* h, const float* X, int32_t n, int32_t iters, void* work) {
   const iskv_config& c = h->cfg;
   hipStream_t s = h->stream;
@@ -1611,7 +1770,7 @@ int iskv_launch_refit_iterations(isvd_handle* h, const float* X, int32_t n, int3
     hipLaunchKernelGGL(refit_basis_kernel, dim3(R), dim3(256), 0, s, Zp, RF_CHUNKS, D, R, h->w.st, h->B, R);
     ISKV_HIP_CHECK(hipGetLastError());
     // orthonormal basis of span(Z) (the coordinates are recomputed next)
-    rc = iskv_launch_reorth(h);
+    rc = orthonormalize_basis(h, 6);
     if (rc) return rc;
   }
   return iters > 0 ? ritz() : ISKV_OK;

@@ -176,3 +176,14 @@ class DeviceStreams:
         if nk < self.paths:
             out[nk:] = torch.matmul(z[nk:] * self.sig[1], self.OT[1])
         return out
+
+
+def prompt_keys(L: int, Hkv: int, dh: int, seed: int) -> np.ndarray:
+    """Post-RoPE prompt keys (fp32 [L, Hkv * dh]) for the anomaly-score rule:
+    N(0, 1) entries, and in every fifth 8-token block the token at offset 2
+    turned against its block and doubled (a planted anomaly)."""
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((L, Hkv * dh)).astype(np.float32)
+    for j in range(0, L // 8, 5):
+        k[8 * j + 2] = -2.0 * k[8 * j + 2]
+    return k

@@ -926,11 +926,7 @@ def test_prompt_split_exact(K, L, D, mask):
 def _prompt_inputs(L, Hkv, dh, seed):
     """Post-RoPE keys with planted anomalies (bf16), pre-RoPE keys and values
     from the key and value spectra (fp32)."""
-    rng = np.random.default_rng(seed)
-    Kr = rng.standard_normal((L, Hkv * dh)).astype(np.float32)
-    for j in range(0, L // 8, 5):
-        Kr[8 * j + 2] = -2.0 * Kr[8 * j + 2]
-    Kb = torch.from_numpy(Kr).bfloat16()
+    Kb = torch.from_numpy(synth.prompt_keys(L, Hkv, dh, seed)).bfloat16()
     D = Hkv * dh
     K_pre = synth.kv_stream(synth.StreamSpec(D=D, n=L, spectrum="exp40+0.01", noise_std=0.0, seed=seed))
     V = synth.kv_stream(synth.StreamSpec(D=D, n=L + 512, spectrum="invsqrt", noise_std=0.0, seed=seed + 1))
