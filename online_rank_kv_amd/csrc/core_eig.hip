@@ -1259,6 +1259,255 @@ __global__ __launch_bounds__(1024) void core_jacobi_kernel(double* S, double* V,
   }
 }
 
+// ----------------------------------------------------------------------------
+// Block Jacobi fallback for large cores (m_max > BJ_MIN_M). The indices are cut
+// into blocks of 32; a round pairs the blocks (round-robin), and every pair of
+// blocks is a 64 x 64 symmetric subproblem that one workgroup sweeps once with
+// cyclic Jacobi in LDS, accumulating its rotation Q. The pairs' rotations are
+// disjoint, so S <- Q^T S Q and V <- V Q for the whole round are a row pass
+// and a column pass over many workgroups. A sweep is NB - 1 rounds (NB blocks,
+// even); the largest scaled coupling met in a sweep decides convergence.
+constexpr int BJ_B = 32;          // block size
+constexpr int BJ_P = 2 * BJ_B;    // pair size
+constexpr int BJ_LD = BJ_P + 1;   // LDS row stride (doubles)
+// Cores up to BJ_MIN_M keep the one-workgroup Jacobi: there the refinement
+// converges except in early merges, and a merge's recorded sequence would
+// otherwise carry the block Jacobi's ~1000 (mostly idle) launches.
+constexpr int BJ_MIN_M = 384;
+constexpr int BJ_SWEEPS = 32;
+constexpr int FLAG_BJDONE = 8;
+
+__device__ __forceinline__ bool bj_active(const int32_t* st) {
+  const int f = st[ST_PCJ];
+  return (f & FLAG_FALLBACK) && !(f & FLAG_BJDONE);
+}
+
+// Blocks of pair p in round r of a round-robin over NB blocks (NB even).
+__device__ __forceinline__ void bj_pair(int r, int p, int NB, int* a, int* b) {
+  const int x = p == 0 ? NB - 1 : (r + p) % (NB - 1);
+  const int y = (r - p + NB - 1) % (NB - 1);
+  *a = x < y ? x : y;
+  *b = x < y ? y : x;
+}
+
+// Global index of local index l of the pair (blocks a, b).
+__device__ __forceinline__ int bj_gidx(int l, int a, int b) { return l < BJ_B ? a * BJ_B + l : b * BJ_B + l - BJ_B; }
+
+// Cold start (S = A set by the caller): V = I. smax[1] = max |s_ii|, the
+// scale of the absolute part of the convergence test.
+__global__ __launch_bounds__(256) void bj_init_kernel(const double* __restrict__ S, double* V, int ld, int32_t* st,
+                                                      double* smax, const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  S = iskv_rb(S, bdel);
+  V = iskv_rb(V, bdel);
+  st = iskv_rb(st, bdel);
+  smax = iskv_rb(smax, bdel);
+  if (!(st[ST_PCJ] & FLAG_FALLBACK)) return;
+  const int m = st[ST_JM];
+  if (blockIdx.x == 0) {
+    __shared__ double red[4];
+    double d = 0.0;
+    for (int i = threadIdx.x; i < m; i += 256) d = fmax(d, fabs(S[(size_t)i * ld + i]));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) d = fmax(d, __shfl_xor(d, o, 64));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = d;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      smax[0] = 0.0;
+      smax[1] = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+      st[ST_SWEEPS] = 0;
+    }
+  }
+  if (!(st[ST_PCJ] & FLAG_COLD)) return;
+  const size_t tot = (size_t)m * m;
+  for (size_t e = blockIdx.x * 256 + threadIdx.x; e < tot; e += (size_t)gridDim.x * 256)
+    V[(e / m) * ld + e % m] = (e / m == e % m) ? 1.0 : 0.0;
+}
+
+// One cyclic sweep on the 64 x 64 subproblem of pair p (grid.x) in round r;
+// Q (64 x 64, row-major) to Qbuf[p]. The largest scaled coupling found,
+// |s_ij| / max(sqrt(|s_ii s_jj|), 0.01 max_i |s_ii|) (relative, with an
+// absolute floor at the rounding level of the largest entries), goes to
+// smax[0] (atomic max on the bits of a non-negative double).
+__global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict__ S, int ld, double* Qbuf,
+                                                       int32_t* st, double* smax, int r, int NB, double tol,
+                                                       const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  S = iskv_rb(S, bdel);
+  Qbuf = iskv_rb(Qbuf, bdel);
+  st = iskv_rb(st, bdel);
+  smax = iskv_rb(smax, bdel);
+  if (!bj_active(st)) return;
+  const int m = st[ST_JM];
+  int a, b;
+  bj_pair(r, blockIdx.x, NB, &a, &b);
+  extern __shared__ double bj_lds[];
+  double* A = bj_lds;               // [64][65]
+  double* Q = bj_lds + BJ_P * BJ_LD;  // [64][65]
+  __shared__ double cs[BJ_B], sn[BJ_B], red[4];
+  __shared__ int pp[BJ_B], qq[BJ_B];
+  const int t = threadIdx.x;
+  double cmax = 0.0;
+  const double floor_d = 0.01 * smax[1];
+  for (int e = t; e < BJ_P * BJ_P; e += 256) {
+    const int i = e / BJ_P, j = e % BJ_P;
+    const int gi = bj_gidx(i, a, b), gj = bj_gidx(j, a, b);
+    const double v = (gi < m && gj < m) ? S[(size_t)gi * ld + gj] : 0.0;
+    A[i * BJ_LD + j] = v;
+    Q[i * BJ_LD + j] = i == j ? 1.0 : 0.0;
+  }
+  __syncthreads();
+  for (int e = t; e < BJ_P * BJ_P; e += 256) {
+    const int i = e / BJ_P, j = e % BJ_P;
+    if (j > i) {
+      const double den = fmax(sqrt(fabs(A[i * BJ_LD + i] * A[j * BJ_LD + j])), floor_d);
+      const double x = fabs(A[i * BJ_LD + j]);
+      const double c = !isfinite(x) ? INFINITY : (den > 0.0 ? x / den : (x > 0.0 ? INFINITY : 0.0));
+      cmax = fmax(cmax, c);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) cmax = fmax(cmax, __shfl_xor(cmax, o, 64));
+  if ((t & 63) == 0) red[t >> 6] = cmax;
+  __syncthreads();
+  if (t == 0) {
+    const double c = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+    atomicMax((unsigned long long*)smax, (unsigned long long)__double_as_longlong(c));
+  }
+  // one cyclic sweep: 63 rounds of 32 disjoint rotations
+  for (int rr = 0; rr < BJ_P - 1; ++rr) {
+    if (t < BJ_B) {
+      const int x = t == 0 ? BJ_P - 1 : (rr + t) % (BJ_P - 1);
+      const int y = (rr - t + BJ_P - 1) % (BJ_P - 1);
+      const int p = x < y ? x : y, q = x < y ? y : x;
+      const double app = A[p * BJ_LD + p], aqq = A[q * BJ_LD + q], apq = A[p * BJ_LD + q];
+      double c = 1.0, sv = 0.0;
+      if (apq != 0.0 && isfinite(apq) && fabs(apq) > tol * sqrt(fabs(app * aqq))) rot2(app, aqq, apq, &c, &sv);
+      cs[t] = c;
+      sn[t] = sv;
+      pp[t] = p;
+      qq[t] = q;
+    }
+    __syncthreads();
+    for (int e = t; e < BJ_B * BJ_P; e += 256) {  // rows p, q of A
+      const int i = e / BJ_P, j = e % BJ_P;
+      const int p = pp[i], q = qq[i];
+      const double c = cs[i], sv = sn[i];
+      const double xp = A[p * BJ_LD + j], xq = A[q * BJ_LD + j];
+      A[p * BJ_LD + j] = c * xp - sv * xq;
+      A[q * BJ_LD + j] = sv * xp + c * xq;
+    }
+    __syncthreads();
+    for (int e = t; e < BJ_B * BJ_P; e += 256) {  // columns p, q of A and Q
+      const int i = e / BJ_P, j = e % BJ_P;
+      const int p = pp[i], q = qq[i];
+      const double c = cs[i], sv = sn[i];
+      const double xp = A[j * BJ_LD + p], xq = A[j * BJ_LD + q];
+      A[j * BJ_LD + p] = c * xp - sv * xq;
+      A[j * BJ_LD + q] = sv * xp + c * xq;
+      const double vp = Q[j * BJ_LD + p], vq = Q[j * BJ_LD + q];
+      Q[j * BJ_LD + p] = c * vp - sv * vq;
+      Q[j * BJ_LD + q] = sv * vp + c * vq;
+    }
+    __syncthreads();
+  }
+  double* Qo = Qbuf + (size_t)blockIdx.x * BJ_P * BJ_P;
+  for (int e = t; e < BJ_P * BJ_P; e += 256) Qo[e] = Q[(e / BJ_P) * BJ_LD + e % BJ_P];
+}
+
+// Row pass: S[I, j0 .. j0+63] <- Q^T S[I, j0 .. j0+63] for the pair's 64
+// indices I. Grid (pairs, column tiles).
+__global__ __launch_bounds__(256) void bj_rows_kernel(double* S, int ld, const double* __restrict__ Qbuf,
+                                                      const int32_t* st, int r, int NB,
+                                                      const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  S = iskv_rb(S, bdel);
+  Qbuf = iskv_rb(Qbuf, bdel);
+  st = iskv_rb(st, bdel);
+  if (!bj_active(st)) return;
+  const int m = st[ST_JM];
+  const int j0 = blockIdx.y * BJ_P;
+  if (j0 >= m) return;
+  int a, b;
+  bj_pair(r, blockIdx.x, NB, &a, &b);
+  __shared__ double Qs[BJ_P][BJ_LD], X[BJ_P][BJ_LD];
+  const double* Qp = Qbuf + (size_t)blockIdx.x * BJ_P * BJ_P;
+  const int t = threadIdx.x;
+  for (int e = t; e < BJ_P * BJ_P; e += 256) {
+    const int i = e / BJ_P, j = e % BJ_P;
+    Qs[i][j] = Qp[e];
+    const int gi = bj_gidx(i, a, b), gj = j0 + j;
+    X[i][j] = (gi < m && gj < m) ? S[(size_t)gi * ld + gj] : 0.0;
+  }
+  __syncthreads();
+  for (int e = t; e < BJ_P * BJ_P; e += 256) {
+    const int i = e / BJ_P, j = e % BJ_P;  // output row i (local), column j
+    const int gi = bj_gidx(i, a, b), gj = j0 + j;
+    if (gi >= m || gj >= m) continue;
+    double acc = 0.0;
+#pragma unroll 8
+    for (int l = 0; l < BJ_P; ++l) acc = fma(Qs[l][i], X[l][j], acc);
+    S[(size_t)gi * ld + gj] = acc;
+  }
+}
+
+// Column pass: S[i, I] <- S[i, I] Q and V[i, I] <- V[i, I] Q for rows
+// i0 .. i0+63. Grid (pairs, row tiles).
+__global__ __launch_bounds__(256) void bj_cols_kernel(double* S, double* V, int ld, const double* __restrict__ Qbuf,
+                                                      const int32_t* st, int r, int NB,
+                                                      const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  S = iskv_rb(S, bdel);
+  V = iskv_rb(V, bdel);
+  Qbuf = iskv_rb(Qbuf, bdel);
+  st = iskv_rb(st, bdel);
+  if (!bj_active(st)) return;
+  const int m = st[ST_JM];
+  const int i0 = blockIdx.y * BJ_P;
+  if (i0 >= m) return;
+  int a, b;
+  bj_pair(r, blockIdx.x, NB, &a, &b);
+  __shared__ double Qs[BJ_P][BJ_LD], X[BJ_P][BJ_LD];
+  const double* Qp = Qbuf + (size_t)blockIdx.x * BJ_P * BJ_P;
+  const int t = threadIdx.x;
+  for (int e = t; e < BJ_P * BJ_P; e += 256) Qs[e / BJ_P][e % BJ_P] = Qp[e];
+  for (int pass = 0; pass < 2; ++pass) {
+    double* M = pass == 0 ? S : V;
+    __syncthreads();
+    for (int e = t; e < BJ_P * BJ_P; e += 256) {
+      const int i = e / BJ_P, j = e % BJ_P;
+      const int gi = i0 + i, gj = bj_gidx(j, a, b);
+      X[i][j] = (gi < m && gj < m) ? M[(size_t)gi * ld + gj] : 0.0;
+    }
+    __syncthreads();
+    for (int e = t; e < BJ_P * BJ_P; e += 256) {
+      const int i = e / BJ_P, j = e % BJ_P;
+      const int gi = i0 + i, gj = bj_gidx(j, a, b);
+      if (gi >= m || gj >= m) continue;
+      double acc = 0.0;
+#pragma unroll 8
+      for (int l = 0; l < BJ_P; ++l) acc = fma(X[i][l], Qs[l][j], acc);
+      M[(size_t)gi * ld + gj] = acc;
+    }
+  }
+}
+
+// End of a sweep: converged when the sweep's largest scaled coupling is below
+// tol; after the last sweep, no convergence is reported in the status.
+__global__ void bj_check_kernel(int32_t* st, double* smax, double tol, int last,
+                                const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  st = iskv_rb(st, bdel);
+  smax = iskv_rb(smax, bdel);
+  if (!bj_active(st)) return;
+  st[ST_SWEEPS] += 1;
+  if (smax[0] < tol) st[ST_PCJ] |= FLAG_BJDONE;
+  else if (last) atomicOr(&st[ST_STATUS], ISKV_DEV_NOCONV);
+  smax[0] = 0.0;
+}
+
+inline size_t bj_lds_bytes() { return (size_t)2 * BJ_P * BJ_LD * sizeof(double); }
+
 }  // namespace
 
 void iskv_dgemm(hipStream_t s, int m_max, const double* A, bool ta, const double* B, bool tb, double* C,
@@ -1278,6 +1527,8 @@ int iskv_core_eig_setup() {
   ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)pcj_analyze_kernel,
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)sizeof(AnalyzeLds)));
+  ISKV_HIP_CHECK(hipFuncSetAttribute((const void*)bj_solve_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)bj_lds_bytes()));
   return ISKV_OK;
 }
 
@@ -1333,8 +1584,32 @@ int iskv_launch_core_eig(isvd_handle* h, double tol) {
   gemm<true, false>(s, mm, wc, w.Pa, w.S, nullptr, ld, 1.0, 0.0, 0.0, st, 3, h->bd, h->bcount);
   hipLaunchKernelGGL(pcj_final_kernel, bz(dim3(mm), h->bcount), dim3(256), 0, s, wc, w.Pa, w.A, w.S, w.V, ld,
                      w.aux, nblk * nblk, st, h->bd);
-  hipLaunchKernelGGL(core_jacobi_kernel, bz(dim3(1), h->bcount), dim3(1024), 0, s, w.S, w.V, ld, st, 1e-13,
-                     ISKV_JACOBI_MAX_SWEEPS, h->bd);
+  const int NB = ((mm + BJ_B - 1) / BJ_B + 1) & ~1;
+  // the pairs' rotations live in Km (ld x ld doubles), the sweep maxima in aux
+  const bool bj_fits = (size_t)(NB / 2) * BJ_P * BJ_P <= (size_t)ld * ld && w.naux >= 2;
+  if (!bj_fits || (mm <= BJ_MIN_M && !h->force_block_jacobi)) {
+    hipLaunchKernelGGL(core_jacobi_kernel, bz(dim3(1), h->bcount), dim3(1024), 0, s, w.S, w.V, ld, st, 1e-13,
+                       ISKV_JACOBI_MAX_SWEEPS, h->bd);
+  } else {
+    // block Jacobi; Km (free once the refinement has ended) holds the pairs'
+    // rotations, aux[0] the sweep's largest coupling
+    const int tiles = (mm + BJ_P - 1) / BJ_P;
+    hipLaunchKernelGGL(bj_init_kernel, bz(dim3(64), h->bcount), dim3(256), 0, s, w.S, w.V, ld, st, w.aux, h->bd);
+    for (int sw = 0; sw < BJ_SWEEPS; ++sw) {
+      for (int r = 0; r < NB - 1; ++r) {
+        hipLaunchKernelGGL(bj_solve_kernel, bz(dim3(NB / 2), h->bcount), dim3(256), bj_lds_bytes(), s, w.S, ld, w.Km,
+                           st, w.aux, r, NB, 1e-13, h->bd);
+        hipLaunchKernelGGL(bj_rows_kernel, bz(dim3(NB / 2, tiles), h->bcount), dim3(256), 0, s, w.S, ld, w.Km, st, r,
+                           NB, h->bd);
+        hipLaunchKernelGGL(bj_cols_kernel, bz(dim3(NB / 2, tiles), h->bcount), dim3(256), 0, s, w.S, w.V, ld, w.Km, st,
+                           r, NB, h->bd);
+      }
+      // the two 64-term passes leave ~1e-14 max|s_ii| of rounding in the
+      // entries, i.e. scaled couplings near 1e-12 at the absolute floor
+      hipLaunchKernelGGL(bj_check_kernel, bz(dim3(1), h->bcount), dim3(1), 0, s, st, w.aux, 1e-10,
+                         sw == BJ_SWEEPS - 1 ? 1 : 0, h->bd);
+    }
+  }
   ISKV_HIP_CHECK(hipGetLastError());
   return ISKV_OK;
 }

@@ -111,6 +111,9 @@ struct isvd_handle {
   bool timing = false;
   bool timed = false;  // a merge has been timed since timing was switched on
   hipEvent_t tev[ISKV_STAGES + 1] = {};
+  // the core eigensolver's fallback is the block Jacobi whatever the core
+  // size (set around eager solves of dense cores, never while recording)
+  bool force_block_jacobi = false;
 };
 
 struct iskv_window {

@@ -1754,7 +1754,11 @@ int iskv_launch_refit_iterations(isvd_handle* h, const float* X, int32_t n, int3
   auto ritz = [&]() -> int {  // C <- X B, then the exact SVD of C B^T
     c_from_x();
     ISKV_HIP_CHECK(hipGetLastError());
-    return iskv_launch_reorth(h);
+    // eager, with the block Jacobi: the first Ritz core of a refit is dense
+    h->force_block_jacobi = true;
+    const int rc = reorth_body(h);
+    h->force_block_jacobi = false;
+    return rc;
   };
   for (int it = 0; it < iters; ++it) {
     // Ritz vectors of X^T X in span(B) (B orthonormal here): z_i = X^T X b_i
