@@ -309,8 +309,8 @@ int decode_attend_fv(const uint16_t* q, const uint16_t* K, const isvd_handle* hv
  * iters > 0 the factors come from a randomized subspace iteration: a random
  * orthonormal D x k start, `iters` power steps B <- orth(X^T X B) (CholeskyQR2
  * in fp64), then the Rayleigh-Ritz step (C <- X B and re-orthogonalise, §4.4:
- * the exact SVD of X B B^T), one more power step whose basis is orthonormalised
- * by its polar factor, and a last Ritz step: C = X B, C^T C diagonal. The
+ * the exact SVD of X B B^T), one more power step, and a last Ritz step:
+ * C = X B, C^T C diagonal. The
  * error approaches the Eckart-Young optimum as iters grows (6 is within 0.2%
  * on the key and value streams). iters = 0 folds the rows by merges instead
  * (Algorithm 2), the incremental factor the refit replaces.

@@ -1262,8 +1262,8 @@ __global__ __launch_bounds__(1024) void core_jacobi_kernel(double* S, double* V,
 // ----------------------------------------------------------------------------
 // Block Jacobi fallback for large cores (m_max > BJ_MIN_M). The indices are cut
 // into blocks of 32; a round pairs the blocks (round-robin), and every pair of
-// blocks is a 64 x 64 symmetric subproblem that one workgroup sweeps once with
-// cyclic Jacobi in LDS, accumulating its rotation Q. The pairs' rotations are
+// blocks is a 64 x 64 symmetric subproblem that one workgroup diagonalises by
+// cyclic Jacobi in LDS (up to BJ_INNER sweeps), accumulating its rotation Q. The pairs' rotations are
 // disjoint, so S <- Q^T S Q and V <- V Q for the whole round are a row pass
 // and a column pass over many workgroups. A sweep is NB - 1 rounds (NB blocks,
 // even); the largest scaled coupling met in a sweep decides convergence.
@@ -1275,6 +1275,7 @@ constexpr int BJ_LD = BJ_P + 1;   // LDS row stride (doubles)
 // otherwise carry the block Jacobi's ~1000 (mostly idle) launches.
 constexpr int BJ_MIN_M = 384;
 constexpr int BJ_SWEEPS = 32;
+constexpr int BJ_INNER = 8;       // inner sweeps at most per pair subproblem
 constexpr int FLAG_BJDONE = 8;
 
 __device__ __forceinline__ bool bj_active(const int32_t* st) {
@@ -1293,11 +1294,13 @@ __device__ __forceinline__ void bj_pair(int r, int p, int NB, int* a, int* b) {
 // Global index of local index l of the pair (blocks a, b).
 __device__ __forceinline__ int bj_gidx(int l, int a, int b) { return l < BJ_B ? a * BJ_B + l : b * BJ_B + l - BJ_B; }
 
-// Cold start (S = A set by the caller): V = I. smax[1] = max |s_ii|, the
-// scale of the absolute part of the convergence test.
-__global__ __launch_bounds__(256) void bj_init_kernel(const double* __restrict__ S, double* V, int ld, int32_t* st,
-                                                      double* smax, const int64_t* __restrict__ bd) {
+// The block Jacobi always starts cold: S = A, V = I (a warm start would
+// inherit whatever orthogonality defect the refinement's W has). smax[1] =
+// max |a_ii|, the scale of the absolute part of the convergence test.
+__global__ __launch_bounds__(256) void bj_init_kernel(const double* __restrict__ A, double* S, double* V, int ld,
+                                                      int32_t* st, double* smax, const int64_t* __restrict__ bd) {
   const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  A = iskv_rb(A, bdel);
   S = iskv_rb(S, bdel);
   V = iskv_rb(V, bdel);
   st = iskv_rb(st, bdel);
@@ -1307,7 +1310,7 @@ __global__ __launch_bounds__(256) void bj_init_kernel(const double* __restrict__
   if (blockIdx.x == 0) {
     __shared__ double red[4];
     double d = 0.0;
-    for (int i = threadIdx.x; i < m; i += 256) d = fmax(d, fabs(S[(size_t)i * ld + i]));
+    for (int i = threadIdx.x; i < m; i += 256) d = fmax(d, fabs(A[(size_t)i * ld + i]));
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) d = fmax(d, __shfl_xor(d, o, 64));
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = d;
@@ -1318,10 +1321,12 @@ __global__ __launch_bounds__(256) void bj_init_kernel(const double* __restrict__
       st[ST_SWEEPS] = 0;
     }
   }
-  if (!(st[ST_PCJ] & FLAG_COLD)) return;
   const size_t tot = (size_t)m * m;
-  for (size_t e = blockIdx.x * 256 + threadIdx.x; e < tot; e += (size_t)gridDim.x * 256)
-    V[(e / m) * ld + e % m] = (e / m == e % m) ? 1.0 : 0.0;
+  for (size_t e = blockIdx.x * 256 + threadIdx.x; e < tot; e += (size_t)gridDim.x * 256) {
+    const size_t i = e / m, j = e % m;
+    S[i * ld + j] = A[i * ld + j];
+    V[i * ld + j] = i == j ? 1.0 : 0.0;
+  }
 }
 
 // One cyclic sweep on the 64 x 64 subproblem of pair p (grid.x) in round r;
@@ -1374,7 +1379,13 @@ __global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict_
     const double c = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
     atomicMax((unsigned long long*)smax, (unsigned long long)__double_as_longlong(c));
   }
-  // one cyclic sweep: 63 rounds of 32 disjoint rotations
+  // cyclic sweeps of 63 rounds of 32 disjoint rotations until a sweep
+  // rotates nothing (the subproblem diagonalised; a single sweep can stall
+  // the outer iteration on clusters of nearly equal eigenvalues)
+  __shared__ int rotated;
+  for (int inner = 0; inner < BJ_INNER; ++inner) {
+  if (t == 0) rotated = 0;
+  __syncthreads();
   for (int rr = 0; rr < BJ_P - 1; ++rr) {
     if (t < BJ_B) {
       const int x = t == 0 ? BJ_P - 1 : (rr + t) % (BJ_P - 1);
@@ -1382,7 +1393,10 @@ __global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict_
       const int p = x < y ? x : y, q = x < y ? y : x;
       const double app = A[p * BJ_LD + p], aqq = A[q * BJ_LD + q], apq = A[p * BJ_LD + q];
       double c = 1.0, sv = 0.0;
-      if (apq != 0.0 && isfinite(apq) && fabs(apq) > tol * sqrt(fabs(app * aqq))) rot2(app, aqq, apq, &c, &sv);
+      if (apq != 0.0 && isfinite(apq) && fabs(apq) > tol * sqrt(fabs(app * aqq))) {
+        rot2(app, aqq, apq, &c, &sv);
+        rotated = 1;
+      }
       cs[t] = c;
       sn[t] = sv;
       pp[t] = p;
@@ -1410,6 +1424,12 @@ __global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict_
       Q[j * BJ_LD + q] = sv * vp + c * vq;
     }
     __syncthreads();
+  }
+  // every thread reads the flag before thread 0 may clear it for the next
+  // sweep, so the exit is uniform across the workgroup
+  const int any = rotated;
+  __syncthreads();
+  if (!any) break;
   }
   double* Qo = Qbuf + (size_t)blockIdx.x * BJ_P * BJ_P;
   for (int e = t; e < BJ_P * BJ_P; e += 256) Qo[e] = Q[(e / BJ_P) * BJ_LD + e % BJ_P];
@@ -1594,7 +1614,8 @@ int iskv_launch_core_eig(isvd_handle* h, double tol) {
     // block Jacobi; Km (free once the refinement has ended) holds the pairs'
     // rotations, aux[0] the sweep's largest coupling
     const int tiles = (mm + BJ_P - 1) / BJ_P;
-    hipLaunchKernelGGL(bj_init_kernel, bz(dim3(64), h->bcount), dim3(256), 0, s, w.S, w.V, ld, st, w.aux, h->bd);
+    hipLaunchKernelGGL(bj_init_kernel, bz(dim3(64), h->bcount), dim3(256), 0, s, w.A, w.S, w.V, ld, st, w.aux,
+                       h->bd);
     for (int sw = 0; sw < BJ_SWEEPS; ++sw) {
       for (int r = 0; r < NB - 1; ++r) {
         hipLaunchKernelGGL(bj_solve_kernel, bz(dim3(NB / 2), h->bcount), dim3(256), bj_lds_bytes(), s, w.S, ld, w.Km,
@@ -1604,9 +1625,10 @@ int iskv_launch_core_eig(isvd_handle* h, double tol) {
         hipLaunchKernelGGL(bj_cols_kernel, bz(dim3(NB / 2, tiles), h->bcount), dim3(256), 0, s, w.S, w.V, ld, w.Km, st,
                            r, NB, h->bd);
       }
-      // the two 64-term passes leave ~1e-14 max|s_ii| of rounding in the
-      // entries, i.e. scaled couplings near 1e-12 at the absolute floor
-      hipLaunchKernelGGL(bj_check_kernel, bz(dim3(1), h->bcount), dim3(1), 0, s, st, w.aux, 1e-10,
+      // converged at the solve's tolerance (at least 1e-10: the two 64-term
+      // passes leave ~1e-14 max|s_ii| of rounding in the entries, scaled
+      // couplings near 1e-12 at the absolute floor)
+      hipLaunchKernelGGL(bj_check_kernel, bz(dim3(1), h->bcount), dim3(1), 0, s, st, w.aux, fmax(tol, 1e-10),
                          sw == BJ_SWEEPS - 1 ? 1 : 0, h->bd);
     }
   }

@@ -1453,39 +1453,6 @@ int iskv_launch_reorth(isvd_handle* h) {
   return ISKV_OK;
 }
 
-// B <- B G^(-1/2), G = B^T B: the orthonormal basis closest to B (its polar
-// factor), by Newton-Schulz steps Z <- Z (3I - G Z^2) / 2 from Z = I in fp64.
-// Converges when the columns of B are nearly orthonormal (|I - G| < 1); no
-// rotation inside span(B), so near-eigenvector columns stay near them.
-static int orthonormalize_basis(isvd_handle* h, int ns_steps) {
-  const iskv_config& c = h->cfg;
-  const isvd_ws& w = h->w;
-  hipStream_t s = h->stream;
-  const int R = c.r_max, D = c.D, mm = h->m_max, ld = h->ldm;
-  const int tiles = (R + 15) / 16;
-  const int32_t* st = w.st;
-  hipLaunchKernelGGL(set_jm_kernel, dim3(1), dim3(1), 0, s, w.st, (int)ST_K, nullptr);
-  hipLaunchKernelGGL(gram_partial_kernel<float>, dim3(tiles * tiles, 1), dim3(256), 0, s, h->B, R, hdim(D), w.st,
-                     w.GC, R, D, nullptr);
-  // no C chunks: G_B -> Pa, Z_1 = 1.5 I - 0.5 G_B -> Pb
-  hipLaunchKernelGGL(reorth_sum_kernel, dim3(128), dim3(256), 0, s, w.GC, 0, R, w.Km, w.Pa, w.Pb, ld, w.st, nullptr);
-  double* z = w.Pb;
-  double* zn = w.Zb;
-  for (int t = 0; t < ns_steps; ++t) {
-    iskv_dgemm(s, mm, w.Pa, false, z, false, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 2, nullptr, 1);
-    iskv_dgemm(s, mm, w.T, false, z, false, w.S, nullptr, ld, 1.0, 0.0, 0.0, st, 2, nullptr, 1);
-    iskv_dgemm(s, mm, z, false, w.S, false, zn, z, ld, -0.5, 1.5, 0.0, st, 2, nullptr, 1);
-    double* tmp = z;
-    z = zn;
-    zn = tmp;
-  }
-  hipLaunchKernelGGL(to_f32_kernel, dim3(128), dim3(256), 0, s, z, z, ld, w.Hc, w.T2, R, w.st, nullptr);
-  xh_launch(s, nullptr, 1, D, h->B, R, nullptr, 0, ddim(w.st + ST_K), ddim(w.st + ST_K), R, w.T2, R, R,
-            ddim(w.st + ST_K), hdim(D), h->B, R, w.Bbf, R, nullptr, nullptr, true);
-  ISKV_HIP_CHECK(hipGetLastError());
-  return ISKV_OK;
-}
-
 // ---------------------------------------------------------------------------
 // Fresh truncated SVD of given rows (Algorithm 1 step 7, the value first
 // refit of §3.2): after the rows are folded by merges, subspace iterations
@@ -1494,11 +1461,11 @@ static int orthonormalize_basis(isvd_handle* h, int ns_steps) {
 //   C <- X B and re-orthogonalise (§4.4): with B orthonormal, C B^T = X B B^T
 //     becomes its exact SVD, whose right singular vectors are the Ritz
 //     vectors of X^T X in span(B) and whose coordinates are X B;
-//   Z <- X^T C (= X^T X B);  B <- Z diag(1 / |z_j|);
-//   B <- its polar factor (orthonormal, no rotation inside span(Z)), so the
-//   columns stay close to the Ritz vectors and the next Ritz core is nearly
-//   diagonal (the eigensolver's refinement then converges in a few steps).
-// A last Ritz step gives the factors C = X B.
+//   Z <- X^T C (= X^T X B);  B <- Z diag(1 / |z_j|), orthonormalised by
+//   shifted CholeskyQR3 (the first pass shifted, so that a numerically
+//   rank-deficient Z in fp32 stays factorable with bounded growth).
+// A last Ritz step gives the factors C = X B. The Ritz cores can be dense;
+// their eigensolves take the block Jacobi fallback.
 namespace {
 
 // Zpart[s][d][j] = sum over rows i of chunk s of X[i][d] C[i][j], for
@@ -1599,19 +1566,21 @@ __global__ __launch_bounds__(256) void rand_basis_kernel(float* B, int D, int R,
   }
 }
 
-// H = L^(-T) for the Cholesky factor L of G + eps tr(G)/k I (G = B^T B,
+// H = L^(-T) for the Cholesky factor L of G + rel_shift tr(G)/k I (G = B^T B,
 // k x k fp64 at ld, overwritten by L). One workgroup: right-looking
 // Cholesky column by column, then L^(-1) by forward substitution, one
-// column of the inverse per thread. The small shift keeps a rank-deficient
-// G factorable (a second pass then restores orthonormality).
-__global__ __launch_bounds__(1024) void chol_inv_kernel(double* G, double* H, int ld, const int32_t* __restrict__ st) {
+// column of the inverse per thread. The shift keeps a numerically
+// rank-deficient G factorable with bounded growth (shifted CholeskyQR); the
+// passes after it restore orthonormality.
+__global__ __launch_bounds__(1024) void chol_inv_kernel(double* G, double* H, int ld, const int32_t* __restrict__ st,
+                                                        double rel_shift) {
   const int k = st[ST_K];
   const int t = threadIdx.x, nt = blockDim.x;
   __shared__ double shift;
   if (t == 0) {
     double tr = 0.0;
     for (int i = 0; i < k; ++i) tr += G[(size_t)i * ld + i];
-    shift = 1e-13 * (k > 0 ? tr / k : 0.0) + 1e-300;
+    shift = rel_shift * (k > 0 ? tr / k : 0.0) + 1e-300;
   }
   __syncthreads();
   for (int i = t; i < k; i += nt) G[(size_t)i * ld + i] += shift;
@@ -1681,9 +1650,10 @@ size_t iskv_refit_ws_bytes(const isvd_handle* h) {
   return (size_t)RF_CHUNKS * h->cfg.D * h->cfg.r_max * sizeof(float);
 }
 
-// B <- B R^(-1) with R^T R = B^T B (CholeskyQR): an orthonormal basis of
-// span(B) for any full-rank B.
-static int cholqr_basis(isvd_handle* h) {
+// B <- B R^(-1) with R^T R = B^T B + shift (CholeskyQR): an orthonormal
+// basis of span(B) for a well-conditioned B (shift 1e-13 relative); with the
+// shift 1e-6 relative, a basis of condition at most ~1e3 for any B.
+static int cholqr_basis(isvd_handle* h, double rel_shift = 1e-13) {
   const iskv_config& c = h->cfg;
   const isvd_ws& w = h->w;
   hipStream_t s = h->stream;
@@ -1692,7 +1662,7 @@ static int cholqr_basis(isvd_handle* h) {
   hipLaunchKernelGGL(gram_partial_kernel<float>, dim3(tiles * tiles, 1), dim3(256), 0, s, h->B, R, hdim(D), w.st,
                      w.GC, R, D, nullptr);
   hipLaunchKernelGGL(reorth_sum_kernel, dim3(128), dim3(256), 0, s, w.GC, 0, R, w.Km, w.Pa, w.Pb, ld, w.st, nullptr);
-  hipLaunchKernelGGL(chol_inv_kernel, dim3(1), dim3(1024), 0, s, w.Pa, w.T, ld, w.st);
+  hipLaunchKernelGGL(chol_inv_kernel, dim3(1), dim3(1024), 0, s, w.Pa, w.T, ld, w.st, rel_shift);
   hipLaunchKernelGGL(to_f32_kernel, dim3(128), dim3(256), 0, s, w.T, w.T, ld, w.Hc, w.T2, R, w.st, nullptr);
   xh_launch(s, nullptr, 1, D, h->B, R, nullptr, 0, ddim(w.st + ST_K), ddim(w.st + ST_K), R, w.T2, R, R,
             ddim(w.st + ST_K), hdim(D), h->B, R, w.Bbf, R, nullptr, nullptr, true);
@@ -1730,8 +1700,9 @@ int iskv_launch_refit_power(isvd_handle* h, const float* X, int32_t n, int32_t i
     });
     hipLaunchKernelGGL(refit_basis_kernel, dim3(R), dim3(256), 0, s, Zp, RF_CHUNKS, D, R, h->w.st, h->B, R);
     ISKV_HIP_CHECK(hipGetLastError());
-    for (int pass = 0; pass < 2; ++pass) {
-      const int rc = cholqr_basis(h);
+    // X^T X B is ill-conditioned in fp32: shifted CholeskyQR3
+    for (int pass = 0; pass < 3; ++pass) {
+      const int rc = cholqr_basis(h, pass == 0 ? 1e-6 : 1e-13);
       if (rc) return rc;
     }
   }
@@ -1774,8 +1745,10 @@ int iskv_launch_refit_iterations(isvd_handle* h, const float* X, int32_t n, int3
     hipLaunchKernelGGL(refit_basis_kernel, dim3(R), dim3(256), 0, s, Zp, RF_CHUNKS, D, R, h->w.st, h->B, R);
     ISKV_HIP_CHECK(hipGetLastError());
     // orthonormal basis of span(Z) (the coordinates are recomputed next)
-    rc = orthonormalize_basis(h, 6);
-    if (rc) return rc;
+    for (int pass = 0; pass < 3; ++pass) {
+      rc = cholqr_basis(h, pass == 0 ? 1e-6 : 1e-13);
+      if (rc) return rc;
+    }
   }
   return iters > 0 ? ritz() : ISKV_OK;
 }
