@@ -773,7 +773,7 @@ __global__ __launch_bounds__(256) void pcj_init_kernel(const double* __restrict_
     S[(size_t)i * ld + j] = A[(size_t)i * ld + j];
     W[(size_t)i * ld + j] = (i == j) ? 1.0 : 0.0;
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) { st[ST_PCJ] = 0; st[ST_PCJIT] = 0; st[ST_NEDGE] = 0; }
+  if (blockIdx.x == 0 && threadIdx.x == 0) { st[ST_PCJ] = 0; st[ST_PCJIT] = 0; st[ST_NEDGE] = 0; st[ST_ROUNDS] = 0; }
 }
 
 
@@ -1116,6 +1116,31 @@ __global__ __launch_bounds__(256) void pcj_kmat_kernel(const double* __restrict_
   }
 }
 
+// A converged refinement also needs an orthonormal W: W^T A W diagonal does
+// not imply it (inside a cluster of nearly equal eigenvalues the columns can
+// drift towards each other while the couplings stay small). T = W^T W of the
+// W before its final Newton-Schulz step: any |T - I| above thr withdraws the
+// convergence and marks the fallback cold (ST_ROUNDS = 1). Grid-stride.
+__global__ __launch_bounds__(256) void pcj_orth_check_kernel(const double* __restrict__ T, int ld, int32_t* st,
+                                                             double thr, const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  T = iskv_rb(T, bdel);
+  st = iskv_rb(st, bdel);
+  if (!(st[ST_PCJ] & FLAG_CONV)) return;
+  const int m = st[ST_JM];
+  const size_t tot = (size_t)m * m;
+  bool bad = false;
+  for (size_t e = blockIdx.x * 256 + threadIdx.x; e < tot; e += (size_t)gridDim.x * 256) {
+    const size_t i = e / m, j = e % m;
+    const double v = T[i * ld + j] - (i == j ? 1.0 : 0.0);
+    bad |= !(fabs(v) <= thr);
+  }
+  if (bad) {
+    atomicAnd(&st[ST_PCJ], ~FLAG_CONV);
+    st[ST_ROUNDS] = 1;
+  }
+}
+
 // Eigenvalues lambda_i = w_i^T (A w_i) from T = A W; V = W when converged.
 // Otherwise the Jacobi fallback takes over: when the last step's couplings
 // (aux, nmx maxima) are all finite and below 0.05, it continues from
@@ -1160,7 +1185,8 @@ __global__ __launch_bounds__(256) void pcj_final_kernel(const double* __restrict
       fin = fin && isfinite(aux[b]);
       c = fmax(c, aux[b]);
     }
-    const bool warm = __syncthreads_and(fin && c < 0.05) != 0;  // same in every block
+    // same in every block; never warm after a failed orthogonality check
+    const bool warm = __syncthreads_and(fin && c < 0.05 && st[ST_ROUNDS] == 0) != 0;
     if (warm) {
       for (int r = threadIdx.x; r < m; r += 256) V[(size_t)r * ld + j] = Wf[(size_t)r * ld + j];
     } else {
@@ -1600,6 +1626,7 @@ int iskv_launch_core_eig(isvd_handle* h, double tol) {
                     h->bcount);
   gemm2<false, false>(s, mm, wo, w.Km, w.T, ld, wc, w.Pa, wo, w.Km, -0.5, 1.5, -0.5, 1.5, nullptr, st, 2, h->bd,
                       h->bcount);
+  hipLaunchKernelGGL(pcj_orth_check_kernel, bz(dim3(64), h->bcount), dim3(256), 0, s, w.T, ld, st, 1e-4, h->bd);
   // S = W^T A W of the final W, used only by a fallback that continues from it
   gemm<true, false>(s, mm, wc, w.Pa, w.S, nullptr, ld, 1.0, 0.0, 0.0, st, 3, h->bd, h->bcount);
   hipLaunchKernelGGL(pcj_final_kernel, bz(dim3(mm), h->bcount), dim3(256), 0, s, wc, w.Pa, w.A, w.S, w.V, ld,

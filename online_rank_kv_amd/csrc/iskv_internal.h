@@ -22,7 +22,7 @@ enum {
   ST_SWEEPS = 7,   // Jacobi sweeps used by the last eigensolve
   ST_EZERO = 8,    // 1 when the residual of the merge in flight is exactly zero
   ST_JM = 9,       // order of the matrix handed to the Jacobi eigensolver
-  ST_ROUNDS = 10,  // reserved
+  ST_ROUNDS = 10,  // 1 when the refinement's W failed its orthogonality check (cold fallback)
   ST_PCJ = 11,     // core eigensolver flags: 1 converged, 2 Jacobi fallback used
   ST_PCJIT = 12,   // refinement steps used by the last core eigensolve
   ST_NEDGE = 13,   // strong pairs found by the current detection pass

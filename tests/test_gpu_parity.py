@@ -984,12 +984,7 @@ def test_prefill_init_and_value_first_refit(K, L, per_head, r_K, r_V):
 
 
 # --------------------------------------------------------------------------- 64K-row prompt + decode stream
-R512_SKIP = ("r = 512: the stream's factors turn non-finite after about 2,800 folded rows, at a "
-             "re-orthogonalisation whose block-Jacobi solve does not converge (the status reports both); "
-             "the cause is not found yet. r = 384 runs the same workload.")
-
-
-@pytest.mark.parametrize("r", [384, pytest.param(512, marks=pytest.mark.skip(reason=R512_SKIP))])
+@pytest.mark.parametrize("r", [384, 512])
 def test_prompt_decode_stream_64k(K, r):
     """One 64K-row stream at D = 1024, rank r, b = 64 (the prompt + decode
     workload, specified at r = 512): an 8K-row prompt whose exact rows come from the anomaly rule
