@@ -1029,3 +1029,29 @@ def test_prompt_decode_stream_64k(K, r):
     print(f"64K stream: compressed rows {int((~exact).sum())}, error {err:.6e}, optimum {opt:.6e}, "
           f"drift {err / opt - 1:.4f}", flush=True)
     assert opt * (1 - 1e-6) <= err <= 1.05 * opt
+
+
+def test_prompt_init_error_paths(K):
+    """Refits and the prompt split refuse what they cannot do, before any work."""
+    D = 128
+    path = K.IsvdPath(D=D, r_max=8, b_max=8, n_cap=32, device=DEV)
+    X = torch.randn((40, D), device=DEV)
+    pos = torch.arange(40, dtype=torch.int32, device=DEV)
+    with pytest.raises(K.IskvError):          # n > n_cap
+        path.refit(X, pos, iters=2)
+    with pytest.raises(K.IskvError):          # iters out of range
+        path.refit(X[:16], pos[:16], iters=65)
+    path.refit(X[:16], pos[:16], iters=2)
+    with pytest.raises(K.IskvError):          # history 16 + 20 rows > n_cap
+        path.value_first_refit(X[:20], pos[:20])
+    path.value_first_refit(X[16:16], pos[16:16])   # no new rows: a refit of the history
+    torch.cuda.synchronize()
+    n, k, st = path.query()
+    assert n == 16 and k == 8 and st == 0
+    frozen = K.IsvdPath(D=D, r_max=8, b_max=8, n_cap=32, device=DEV)
+    frozen.set_mode(K.ISKV_FROZEN_BASIS)
+    with pytest.raises(K.IskvError):          # the frozen basis cannot be refit
+        frozen.refit(X[:16], pos[:16], iters=2)
+    fl = torch.zeros((6,), dtype=torch.uint8, device=DEV)
+    with pytest.raises(K.IskvError):          # D not a multiple of 4
+        K.prompt_split(torch.zeros((6, 6), device=DEV), fl, 1)
