@@ -131,6 +131,41 @@ def prefill_leg(args, K, torch, dev):
     return res
 
 
+def high_rank_leg(args, K, torch, dev):
+    """Merges at the prompt + decode stream's rank: one K-spectrum path at
+    D = 1024, r = 512, b = 64, started by a refit of 4,096 rows, then 16
+    merges timed with HIP events on its stream (recorded sequences). The core
+    (576) is above the size where the parallel refinement converges on this
+    spectrum's flat floor, so most merges finish in the block Jacobi."""
+    import synth
+    r, b, n0, merges = 512, 64, 4096, 16
+    X = torch.from_numpy(synth.kv_stream(synth.StreamSpec(D, n0 + (merges + 2) * b, "exp40+0.01", 0.0, 77))).to(dev)
+    pos = torch.arange(X.shape[0], dtype=torch.int32, device=dev)
+    st = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    p = K.IsvdPath(D=D, r_max=r, b_max=b, n_cap=X.shape[0], reorth_every_rows=256, device=dev, stream=st,
+                   graphs=not args.no_graphs)
+    p.refit(X[:n0], pos[:n0], iters=6)
+    for j in range(2):  # warm-up (records the sequences)
+        s0 = n0 + j * b
+        p.merge(X[s0:s0 + b], pos[s0:s0 + b])
+    st.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(st)
+    for j in range(2, merges + 2):
+        s0 = n0 + j * b
+        p.merge(X[s0:s0 + b], pos[s0:s0 + b])
+    ev[1].record(st)
+    st.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / merges
+    n, k, status = p.query()
+    state = p.state()
+    p.close()
+    return {"merge_ms": ms, "r": r, "b": b, "rows_at_start": n0, "merges": merges, "status": status,
+            "last_core_solve": {"flags": state[11], "steps": state[12], "sweeps": state[7]},
+            "what": "K-spectrum path at r=512, b=64 (core 576): refinement, then the block-Jacobi fallback"}
+
+
 def coords_leg(args, K, torch, dev, Xk, Kc):
     """fp32 against 2-byte (bf16) stored coordinates on two fresh K paths of
     N0 rows each, filled by merges and then timed the same way: MODE_MERGES
@@ -567,6 +602,7 @@ def main():
     }
     result["coords_2byte"] = coords_leg(args, K, torch, dev, Xk, Kc)
     result["prefill_init"] = prefill_leg(args, K, torch, dev)
+    result["high_rank_merges"] = high_rank_leg(args, K, torch, dev)
     if args.batch_paths > 0:
         result["many_paths"] = many_path_leg(args, K, torch, dev)
     if not args.no_cpu_baseline:

@@ -1288,8 +1288,8 @@ __global__ __launch_bounds__(1024) void core_jacobi_kernel(double* S, double* V,
 // ----------------------------------------------------------------------------
 // Block Jacobi fallback for large cores (m_max > BJ_MIN_M). The indices are cut
 // into blocks of 32; a round pairs the blocks (round-robin), and every pair of
-// blocks is a 64 x 64 symmetric subproblem that one workgroup diagonalises by
-// cyclic Jacobi in LDS (up to BJ_INNER sweeps), accumulating its rotation Q. The pairs' rotations are
+// blocks is a 64 x 64 symmetric subproblem that one workgroup sweeps with
+// cyclic Jacobi in LDS (BJ_INNER sweeps at most), accumulating its rotation Q. The pairs' rotations are
 // disjoint, so S <- Q^T S Q and V <- V Q for the whole round are a row pass
 // and a column pass over many workgroups. A sweep is NB - 1 rounds (NB blocks,
 // even); the largest scaled coupling met in a sweep decides convergence.
@@ -1301,7 +1301,13 @@ constexpr int BJ_LD = BJ_P + 1;   // LDS row stride (doubles)
 // otherwise carry the block Jacobi's ~1000 (mostly idle) launches.
 constexpr int BJ_MIN_M = 384;
 constexpr int BJ_SWEEPS = 32;
-constexpr int BJ_INNER = 8;       // inner sweeps at most per pair subproblem
+#ifndef ISKV_BJ_INNER
+#define ISKV_BJ_INNER 1
+#endif
+// Inner sweeps at most per pair subproblem. More than one measured no fewer
+// outer sweeps on dense and clustered spectra (333-576), only slower merges
+// (r = 512: 32 ms with one, 57 ms with up to eight).
+constexpr int BJ_INNER = ISKV_BJ_INNER;
 constexpr int FLAG_BJDONE = 8;
 
 __device__ __forceinline__ bool bj_active(const int32_t* st) {
@@ -1405,9 +1411,8 @@ __global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict_
     const double c = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
     atomicMax((unsigned long long*)smax, (unsigned long long)__double_as_longlong(c));
   }
-  // cyclic sweeps of 63 rounds of 32 disjoint rotations until a sweep
-  // rotates nothing (the subproblem diagonalised; a single sweep can stall
-  // the outer iteration on clusters of nearly equal eigenvalues)
+  // cyclic sweeps of 63 rounds of 32 disjoint rotations, until a sweep
+  // rotates nothing or BJ_INNER sweeps are done
   __shared__ int rotated;
   for (int inner = 0; inner < BJ_INNER; ++inner) {
   if (t == 0) rotated = 0;
