@@ -1566,17 +1566,18 @@ __global__ __launch_bounds__(256) void rand_basis_kernel(float* B, int D, int R,
   }
 }
 
-// H = L^(-T) for the Cholesky factor L of G + rel_shift tr(G)/k I (G = B^T B,
-// k x k fp64 at ld, overwritten by L). One workgroup: right-looking
-// Cholesky column by column, then L^(-1) by forward substitution, one
-// column of the inverse per thread. The shift keeps a numerically
-// rank-deficient G factorable with bounded growth (shifted CholeskyQR); the
-// passes after it restore orthonormality.
-__global__ __launch_bounds__(1024) void chol_inv_kernel(double* G, double* H, int ld, const int32_t* __restrict__ st,
-                                                        double rel_shift) {
+// Cholesky factor L of G + rel_shift tr(G)/k I (G = B^T B, k x k fp64 at ld,
+// overwritten by L in its lower triangle). One workgroup, right-looking,
+// column by column; the scaled column is cached in LDS for the trailing
+// update. The shift keeps a numerically rank-deficient G factorable with
+// bounded growth (shifted CholeskyQR); the passes after it restore
+// orthonormality.
+__global__ __launch_bounds__(1024) void chol_kernel(double* G, int ld, const int32_t* __restrict__ st,
+                                                    double rel_shift) {
   const int k = st[ST_K];
   const int t = threadIdx.x, nt = blockDim.x;
   __shared__ double shift;
+  __shared__ double col[1024];
   if (t == 0) {
     double tr = 0.0;
     for (int i = 0; i < k; ++i) tr += G[(size_t)i * ld + i];
@@ -1589,27 +1590,58 @@ __global__ __launch_bounds__(1024) void chol_inv_kernel(double* G, double* H, in
     const double d = sqrt(fmax(G[(size_t)j * ld + j], shift));
     __syncthreads();
     if (t == 0) G[(size_t)j * ld + j] = d;
-    for (int i = j + 1 + t; i < k; i += nt) G[(size_t)i * ld + j] /= d;
+    for (int i = j + 1 + t; i < k; i += nt) {
+      const double v = G[(size_t)i * ld + j] / d;
+      G[(size_t)i * ld + j] = v;
+      col[i] = v;
+    }
     __syncthreads();
     const int w = k - j - 1;  // trailing block (lower triangle)
     for (int e = t; e < w * w; e += nt) {
       const int i = j + 1 + e / w, l = j + 1 + e % w;
-      if (l <= i) G[(size_t)i * ld + l] -= G[(size_t)i * ld + j] * G[(size_t)l * ld + j];
+      if (l <= i) G[(size_t)i * ld + l] -= col[i] * col[l];
     }
     __syncthreads();
   }
-  // column c of L^(-1): x_i = (delta_ic - sum_{c <= m < i} L_im x_m) / L_ii, stored as H[c][i]
-  for (int c = t; c < k; c += nt) {
-    for (int i = 0; i < k; ++i) {
-      double x = 0.0;
-      if (i >= c) {
-        double acc = (i == c) ? 1.0 : 0.0;
-        for (int m = c; m < i; ++m) acc -= G[(size_t)i * ld + m] * H[(size_t)c * ld + m];
-        x = acc / G[(size_t)i * ld + i];
-      }
-      H[(size_t)c * ld + i] = x;
+}
+
+// H = L^(-T) (H[c][i] = (L^(-1))[i][c]), one wave per column c of L^(-1):
+// forward substitution x_i = (delta_ic - sum_{c <= m < i} L_im x_m) / L_ii,
+// the sum split over the 64 lanes (lane l holds x_m for m = c + l + 64q in
+// registers) and reduced across the wave. k <= 1024.
+__global__ __launch_bounds__(256) void tri_inv_kernel(const double* __restrict__ L, double* H, int ld,
+                                                      const int32_t* __restrict__ st) {
+  const int k = st[ST_K];
+  const int lane = threadIdx.x & 63;
+  const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (c >= k) return;  // whole waves; no workgroup barrier below
+  constexpr int NQ = 16;
+  double xr[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) xr[q] = 0.0;
+  for (int i = c; i < k; ++i) {
+    const double* Li = L + (size_t)i * ld;
+    double part = 0.0;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int m = c + lane + 64 * q;
+      if (m < i) part = fma(Li[m], xr[q], part);
     }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+    const double x = ((i == c ? 1.0 : 0.0) - part) / Li[i];
+    const int q0 = (i - c) >> 6, owner = (i - c) & 63;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+      if (q == q0 && lane == owner) xr[q] = x;
   }
+  double* Hc = H + (size_t)c * ld;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int i = c + lane + 64 * q;
+    if (i < k) Hc[i] = xr[q];
+  }
+  for (int i = lane; i < c; i += 64) Hc[i] = 0.0;
 }
 
 // Bt[j][d] = B[d][j] (32 x 32 tiles through LDS).
@@ -1662,7 +1694,8 @@ static int cholqr_basis(isvd_handle* h, double rel_shift = 1e-13) {
   hipLaunchKernelGGL(gram_partial_kernel<float>, dim3(tiles * tiles, 1), dim3(256), 0, s, h->B, R, hdim(D), w.st,
                      w.GC, R, D, nullptr);
   hipLaunchKernelGGL(reorth_sum_kernel, dim3(128), dim3(256), 0, s, w.GC, 0, R, w.Km, w.Pa, w.Pb, ld, w.st, nullptr);
-  hipLaunchKernelGGL(chol_inv_kernel, dim3(1), dim3(1024), 0, s, w.Pa, w.T, ld, w.st, rel_shift);
+  hipLaunchKernelGGL(chol_kernel, dim3(1), dim3(1024), 0, s, w.Pa, ld, w.st, rel_shift);
+  hipLaunchKernelGGL(tri_inv_kernel, dim3((R + 3) / 4), dim3(256), 0, s, w.Pa, w.T, ld, w.st);
   hipLaunchKernelGGL(to_f32_kernel, dim3(128), dim3(256), 0, s, w.T, w.T, ld, w.Hc, w.T2, R, w.st, nullptr);
   xh_launch(s, nullptr, 1, D, h->B, R, nullptr, 0, ddim(w.st + ST_K), ddim(w.st + ST_K), R, w.T2, R, R,
             ddim(w.st + ST_K), hdim(D), h->B, R, w.Bbf, R, nullptr, nullptr, true);
