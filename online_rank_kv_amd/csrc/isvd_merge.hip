@@ -1596,10 +1596,11 @@ __global__ __launch_bounds__(1024) void chol_kernel(double* G, int ld, const int
       col[i] = v;
     }
     __syncthreads();
-    const int w = k - j - 1;  // trailing block (lower triangle)
-    for (int e = t; e < w * w; e += nt) {
-      const int i = j + 1 + e / w, l = j + 1 + e % w;
-      if (l <= i) G[(size_t)i * ld + l] -= col[i] * col[l];
+    // trailing update of the lower triangle: wave per row, lanes along it
+    for (int i = j + 1 + (t >> 6); i < k; i += nt >> 6) {
+      const double ci = col[i];
+      double* Gi = G + (size_t)i * ld;
+      for (int l = j + 1 + (t & 63); l <= i; l += 64) Gi[l] -= ci * col[l];
     }
     __syncthreads();
   }
