@@ -1309,6 +1309,10 @@ constexpr int BJ_SWEEPS = 32;
 // (r = 512: 32 ms with one, 57 ms with up to eight).
 constexpr int BJ_INNER = ISKV_BJ_INNER;
 constexpr int FLAG_BJDONE = 8;
+#ifndef ISKV_PCJ_MAXIT_LARGE
+#define ISKV_PCJ_MAXIT_LARGE 3
+#endif
+constexpr int PCJ_MAXIT_LARGE = ISKV_PCJ_MAXIT_LARGE;
 
 __device__ __forceinline__ bool bj_active(const int32_t* st) {
   const int f = st[ST_PCJ];
@@ -1608,7 +1612,10 @@ int iskv_launch_core_eig(isvd_handle* h, double tol) {
   // W (the launches that would change it are skipped).
   double* wc = w.W1;
   double* wo = w.W0;
-  for (int it = 1; it <= PCJ_MAXIT; ++it) {
+  // cores above BJ_MIN_M rarely converge in the refinement (flat spectral
+  // floors) and have the block Jacobi behind them: fewer steps there
+  const int maxit = mm > BJ_MIN_M ? PCJ_MAXIT_LARGE : PCJ_MAXIT;
+  for (int it = 1; it <= maxit; ++it) {
     // T1 = W^T W and T2 = A W (A symmetric: read as A^T)
     gemm2<true, true>(s, mm, wc, w.A, wc, ld, w.T, w.Km, nullptr, nullptr, 1.0, 0.0, 1.0, 0.0, nullptr, st, 0, h->bd,
                       h->bcount);
@@ -1621,7 +1628,7 @@ int iskv_launch_core_eig(isvd_handle* h, double tol) {
     gemm_s(s, mm, wo, w.Pa, ld, w.S, w.Dp, w.aux, w.edges, st, tol, h->bd, h->bcount);
     hipLaunchKernelGGL(pcj_analyze_kernel, bz(dim3(1), h->bcount), dim3(1024), lds, s, w.S, wo, ld, w.aux,
                        nblk * nblk, w.edges, st, it, tol, h->bd);
-    if (it == PCJ_MAXIT) break;  // last pass only tests convergence
+    if (it == maxit) break;  // last pass only tests convergence
     hipLaunchKernelGGL(pcj_kmat_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.S, ld, w.Km, w.Pa, st, h->bd);
     gemm<false, false>(s, mm, w.Km, w.Pa, w.Pb, nullptr, ld, 1.0, 0.0, 1.0, st, 0, h->bd, h->bcount);
     gemm<false, false>(s, mm, wo, w.Pb, wc, wo, ld, 1.0, 0.0, 0.0, st, 1, h->bd, h->bcount);
