@@ -303,7 +303,7 @@ int decode_attend_fv(const uint16_t* q, const uint16_t* K, const isvd_handle* hv
 
 /* ---- prompt initialisation ----------------------------------------------- */
 /* Replace the history by a fresh rank-k truncated SVD of the rows X (iS-KV
- * notes Algorithm 1 step 7: the non-exact prompt rows; §3.2: the value first
+ * notes Algorithm 1: the non-exact prompt rows; §3.2: the value first
  * refit over the rebuilt prompt values plus the first rows to leave the
  * window), k = min(r_max, n, D). The handle is reset to these n rows. With
  * iters > 0 the factors come from a randomized subspace iteration: a random
@@ -338,7 +338,7 @@ size_t isvd_value_first_refit_workspace_bytes(const isvd_handle* h);
 int isvd_value_first_refit(isvd_handle* h, const float* F, const int32_t* pos_F, int32_t count, int32_t iters,
                            void* work, size_t work_bytes);
 
-/* Split the prompt's rows by their flags (iS-KV notes Algorithm 1 steps 7-8):
+/* Split the prompt's rows by their flags (iS-KV notes Algorithm 1):
  * row p (position pos0 + p) is kept exact when flags[p] & mask, otherwise it
  * belongs to the rows the path's factor is built from; both lists keep
  * position order. For the keys mask = 1 (E_K = P_K), for the values
@@ -357,7 +357,7 @@ int iskv_prompt_split(const float* X, const uint8_t* flags, int32_t L, int32_t D
                       void* workspace, size_t ws_bytes, void* stream);
 
 
-/* Exact-row sets of a prompt (iS-KV notes §3.1, Algorithm 1 steps 2-6), from
+/* Exact-row sets of a prompt (iS-KV notes §3.1, Algorithm 1), from
  * its post-RoPE keys. The prompt is cut into blocks of `block` tokens; the last
  * `suffix_blocks` whole blocks and the partial tail are the local suffix. For
  * each KV head and every other block, the anomaly score is the minimum over the

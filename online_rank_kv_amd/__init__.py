@@ -267,7 +267,7 @@ def prompt_split(X, flags, mask: int, pos0: int = 0, stream=None):
 
 def prefill_init(kpath, vpath, K_pre, K_rot, V, Hkv: int, dh: int, block: int = 8, per_head: int = 128,
                  suffix_blocks: int = 4, v_radius: int = 32, v_window: int = 128, iters: int = 6):
-    """Prompt initialisation (iS-KV notes §3.1, Algorithm 1 steps 2-9) of one
+    """Prompt initialisation (iS-KV notes §3.1, Algorithm 1) of one
     layer's key and value paths (fresh handles, fp32 rows on the device):
     exact sets from the post-RoPE keys K_rot (bf16 [L, Hkv * dh]), E_K = P_K
     and E_V = P_V | W_V; each path's other rows (pre-RoPE keys K_pre, values

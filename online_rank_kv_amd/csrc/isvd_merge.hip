@@ -1454,7 +1454,7 @@ int iskv_launch_reorth(isvd_handle* h) {
 }
 
 // ---------------------------------------------------------------------------
-// Fresh truncated SVD of given rows (Algorithm 1 step 7, the value first
+// Fresh truncated SVD of given rows (Algorithm 1, the value first
 // refit of §3.2): after the rows are folded by merges, subspace iterations
 // with a Rayleigh-Ritz step converge to the top-k right singular subspace of X.
 // Each iteration:

@@ -1,4 +1,4 @@
-// Exact-row sets of the prompt (iS-KV notes §3.1, Algorithm 1 steps 2-6):
+// Exact-row sets of the prompt (iS-KV notes §3.1, Algorithm 1):
 // the post-RoPE keys are cut into blocks of `block` tokens; the last
 // `suffix_blocks` whole blocks and the partial tail are the local suffix.
 // For every KV head and every other block, the anomaly score is the minimum
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256) void flags_kernel(const uint8_t* __restrict__ 
   flags[p] = (uint8_t)((pk ? 1 : 0) | (pv ? 2 : 0) | (wv ? 4 : 0));
 }
 
-// Split of the prompt rows by their flags (Algorithm 1 steps 7-8): row p is
+// Split of the prompt rows by their flags (Algorithm 1): row p is
 // kept exact when flags[p] & mask, else it goes to the rows the factor is
 // built from; both lists stay in position order. One workgroup ranks all
 // positions: thread t owns a contiguous run of them, the runs' keep counts

@@ -238,7 +238,7 @@ def persist_coords_bf16(fac: Factor) -> Factor:
 
 
 def anomaly_block_scores(K_rot: np.ndarray, Hkv: int, dh: int, block: int = 8, suffix_blocks: int = 4):
-    """Anomaly score of each prompt block (iS-KV notes §3.1, Algorithm 1 step 2).
+    """Anomaly score of each prompt block (iS-KV notes §3.1, Algorithm 1).
 
     The prompt's post-RoPE keys K_rot (L x Hkv*dh) are cut into blocks of
     `block` tokens; the last `suffix_blocks` whole blocks and the partial tail
@@ -268,7 +268,7 @@ def anomaly_block_scores(K_rot: np.ndarray, Hkv: int, dh: int, block: int = 8, s
 
 def prompt_protect(K_rot: np.ndarray, Hkv: int, dh: int, block: int = 8, per_head: int = 128,
                    suffix_blocks: int = 4, v_radius: int = 32, v_window: int = 128, scores=None):
-    """The exact-row sets of the prompt (iS-KV notes §3.1, Algorithm 1 steps 2-6).
+    """The exact-row sets of the prompt (iS-KV notes §3.1, Algorithm 1).
 
     Each KV head selects its `per_head` lowest-scoring blocks (all of them when
     there are fewer; equal scores: the lower block index first); the positions
@@ -301,7 +301,7 @@ def prompt_protect(K_rot: np.ndarray, Hkv: int, dh: int, block: int = 8, per_hea
 
 def truncated_factor(X: np.ndarray, pos, r: int) -> Factor:
     """A path's factor from the fresh rank-r truncated SVD of its rows
-    (iS-KV notes §2.2; Algorithm 1 step 7). Reading: k = the number of the
+    (iS-KV notes §2.2; Algorithm 1). Reading: k = the number of the
     first min(r, n, D) singular values that are not zero."""
     X = np.asarray(X, dtype=np.float64)
     n, D = X.shape
@@ -316,7 +316,7 @@ def truncated_factor(X: np.ndarray, pos, r: int) -> Factor:
 def prefill_init(K_pre: np.ndarray, K_rot: np.ndarray, V: np.ndarray, Hkv: int, dh: int, r_K: int, r_V: int,
                  block: int = 8, per_head: int = 128, suffix_blocks: int = 4, v_radius: int = 32,
                  v_window: int = 128):
-    """Prompt initialisation (iS-KV notes §3.1, Algorithm 1 steps 2-9).
+    """Prompt initialisation (iS-KV notes §3.1, Algorithm 1).
 
     The exact sets come from the post-RoPE keys: E_K = P_K and
     E_V = P_V | W_V (W_K is empty). Each path keeps its exact rows as they are

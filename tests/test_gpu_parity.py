@@ -822,7 +822,7 @@ def test_error_paths(K):
 @pytest.mark.parametrize("L,hkv,dh,per_head", [(3003, 8, 128, 128), (1000, 4, 64, 16), (30, 2, 128, 128),
                                                (8 * 9 + 3, 2, 128, 1)])
 def test_prompt_protect_matches_oracle(K, L, hkv, dh, per_head):
-    """Algorithm 1 steps 2-6 (notes §3.1) on the GPU: block anomaly scores equal
+    """Algorithm 1 (notes §3.1) on the GPU: block anomaly scores equal
     the oracle's (fp64 on the same bf16 keys) to 1e-5; the kept blocks, P_K, P_V
     and W_V equal the oracle's sets computed from the GPU's own scores exactly,
     and from the oracle's scores except at a near tie on the per-head cut."""
@@ -866,7 +866,7 @@ def test_prompt_protect_matches_oracle(K, L, hkv, dh, per_head):
     (1024, 320, 64, 3000, "invsqrt", 6, True),
 ])
 def test_refit_reaches_fresh_truncated_svd(K, D, r, b, n, spec, iters, c16):
-    """isvd_refit (Algorithm 1 step 7, the value first refit of §3.2): the
+    """isvd_refit (Algorithm 1, the value first refit of §3.2): the
     handle's old history is dropped; with iters = 0 the factors are the
     oracle's fold of the rows; the iterations bring the error down towards the
     Eckart-Young optimum of the oracle's fresh truncated SVD and never below
@@ -911,7 +911,7 @@ def test_refit_reaches_fresh_truncated_svd(K, D, r, b, n, spec, iters, c16):
 # --------------------------------------------------------------------------- prompt initialisation
 @pytest.mark.parametrize("L,D,mask", [(0, 64, 1), (1, 64, 1), (1000, 64, 6), (4097, 1024, 1), (8192, 1024, 6)])
 def test_prompt_split_exact(K, L, D, mask):
-    """Algorithm 1 steps 7-8: rows split by flags & mask, both lists in
+    """Algorithm 1: rows split by flags & mask, both lists in
     position order, rows and positions bit-exact."""
     rng = np.random.default_rng(90 + L)
     X = rng.standard_normal((L, D)).astype(np.float32)
@@ -989,7 +989,7 @@ def test_prompt_decode_stream_64k(K, r):
     """One 64K-row stream at D = 1024, rank r, b = 64 (the prompt + decode
     workload, specified at r = 512): an 8K-row prompt whose exact rows come from the anomaly rule
     (12 blocks per head, about 10%, with the +-32 value neighbourhoods and the
-    last 128), the rest refit (Algorithm 1 step 7); then 57,344 decode rows
+    last 128), the rest refit (Algorithm 1); then 57,344 decode rows
     through the exact window (w = 128) and block merges. At the end the whole
     64K rows are reconstructed: exact rows bit-exact, and the compressed rows'
     error lies between the Eckart-Young optimum of those rows and 1.05 times it

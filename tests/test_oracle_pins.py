@@ -454,7 +454,7 @@ def test_persist_coords_bf16_pins():
 
 # --------------------------------------------------------------------------- prompt protection
 def test_anomaly_scores_and_protect_pins():
-    """Algorithm 1 steps 2-6 (notes §3.1): a block of equal keys scores 1, one
+    """Algorithm 1 (notes §3.1): a block of equal keys scores 1, one
     key opposite to the rest gives that key's cosine with the mean (closed
     form), the suffix (last 4 blocks + tail) is never scored and always kept,
     a head keeps its lowest blocks (ties: lower index), P_V dilates P_K by 32
@@ -502,7 +502,7 @@ def _orthonormal(rng, n, k):
 
 
 def test_truncated_factor_and_prefill_init_pins():
-    """Algorithm 1 steps 7-9 (notes §3.1): each path's factor covers exactly its
+    """Algorithm 1 (notes §3.1): each path's factor covers exactly its
     non-exact rows (positions saved in order; the exact rows, here planted
     with huge values, never reach it), a non-exact part of rank <= r is
     reproduced exactly, and truncation keeps the r largest of known singular
