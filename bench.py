@@ -19,7 +19,7 @@ timed step is one pass of the whole hot path at n ~ 16K:
 The headline value is iSVD merges per second (two per step). Inputs are
 synthetic and resident in HBM before the timed region.
 
-Prints ONE JSON line (rank 0). `--gpus N` with N > 1 exits: this build runs on
+Prints ONE JSON line (rank 0). `--gpus N` with N > 1 exits: the benchmark runs on
 one GPU.
 """
 from __future__ import annotations
@@ -322,8 +322,8 @@ def cpu_baseline(Xk, Xv, seconds):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(every (sequence, layer, K/V) stream is independent; see DESIGN.md).", file=sys.stderr)
+        print("bench.py runs on one GPU only: there is no multi-GPU path "
+              "(every (sequence, layer, K/V) stream is independent of the others).", file=sys.stderr)
         sys.exit(2)
     import torch
     import synth
