@@ -279,19 +279,30 @@ def many_path_leg(args, K, torch, dev):
 
 
 def cpu_baseline(Xk, Xv, seconds):
-    """The oracle (float64 NumPy/LAPACK) timed on the host on a bounded sample.
+    """The oracle (float64 NumPy/LAPACK) timed on the host on a bounded sample,
+    with the BLAS on all the host's threads and again on one thread.
 
     Sample: both paths start from a factorisation of their first 16,384 rows
     (the oracle's fresh truncated SVD, not timed); then whole steps (merge K,
     merge V, reconstruct K with RoPE and V, attention) are timed until
-    `seconds` elapse. Reported in merges/s like the GPU value.
+    `seconds` elapse (half of that on one thread). Reported in merges/s like
+    the GPU value.
     """
+    from threadpoolctl import threadpool_info, threadpool_limits
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    res = _cpu_steps(Xk, Xv, seconds)
+    res["cores"] = int(threads)
+    with threadpool_limits(limits=1):
+        one = _cpu_steps(Xk, Xv, seconds / 2)
+    one["cores"] = 1
+    res["one_thread"] = one
+    res["host"] = {"sched_getaffinity": len(os.sched_getaffinity(0)), "cpu_count": os.cpu_count(),
+                   "blas": sorted({p.get("internal_api", "?") for p in threadpool_info()})}
+    return res
+
+
+def _cpu_steps(Xk, Xv, seconds):
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
     facs = []
     for X in (Xk, Xv):
         u, s, vt = np.linalg.svd(X[:N0].astype(np.float64), full_matrices=False)
@@ -313,7 +324,7 @@ def cpu_baseline(Xk, Xv, seconds):
         el = time.perf_counter() - t0
         if el >= seconds or s0 + 2 * BLK > Xk.shape[0]:
             break
-    return {"value": merges / el, "unit": "merges/s", "cores": int(threads), "kind": "oracle",
+    return {"value": merges / el, "unit": "merges/s", "kind": "oracle",
             "sample": f"{steps} whole steps (2 merges at n={N0}..{N0 + steps * BLK}, K+V reconstruction "
                       f"incl. RoPE, attention) from a fresh factorisation of 16,384 rows, float64, "
                       f"{el:.1f} s"}
@@ -394,6 +405,10 @@ def main():
     cursor = [N0 + WIN]
     ev = {k: [] for k in ("merge_k", "merge_v", "recon_k", "recon_v", "attend")}
     attend_done = [None]
+    # rows of every timed step: n_total (compressed + window) and the
+    # compressed rows the K reconstruction kernel reads and writes (all rows
+    # but the w-row exact window: every step folds the b rows that left it)
+    timed_rows = []
 
     def step(record):
         s0 = cursor[0]
@@ -429,6 +444,7 @@ def main():
         e[6].record(sk)
         attend_done[0] = e[6]
         if record:
+            timed_rows.append((n_total, n_total - WIN))
             ev["merge_k"].append((e[0], e[1]))   # batched: the K + V merge sequence
             ev["merge_v"].append((e[3], e[4]) if not batched else (e[0], e[1]))
             ev["recon_k"].append((e[1], e[2]))
@@ -445,6 +461,11 @@ def main():
     t_issue = time.perf_counter() - t0
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    # the bookkeeping behind timed_rows: after the last timed step the K
+    # path holds every row but the window
+    n_after = paths[0].n
+    if n_after != timed_rows[-1][1]:
+        raise RuntimeError(f"K path holds {n_after} compressed rows, expected {timed_rows[-1][1]}")
 
     def avg_ms(key):
         return float(np.mean([a.elapsed_time(b) for a, b in ev[key]]))
@@ -544,11 +565,12 @@ def main():
     ms = {k: avg_ms(k) for k in ev}
     core = [p.state() for p in paths]
     merges = 2 * steps
-    n_mid = cursor[0] - BLK * steps // 2
-    # algorithmic bytes of one K reconstruction: read C (n x r fp32) and B^T
-    # (its bf16 copy, D x r), write n_total x D bf16; flops 2 n r D
-    recon_bytes = n_mid * R * 4 + R * D * 2 + n_mid * D * 2
-    recon_flops = 2.0 * n_mid * R * D
+    # algorithmic bytes of one K reconstruction launch, averaged over the
+    # timed steps: read the n_c compressed rows' coordinates (n_c x r fp32)
+    # and B^T (its bf16 copy, r x D), write n_c x D bf16; flops 2 n_c r D
+    n_c = float(np.mean([c for _, c in timed_rows]))
+    recon_bytes = n_c * R * 4 + R * D * 2 + n_c * D * 2
+    recon_flops = 2.0 * n_c * R * D
     recon_gbps = recon_bytes / (ms["recon_k"] * 1e-3) / 1e9
     result = {
         "metric": "iSVD merges/s + reconstructed KV GB/s at n=16K, D=1024, r=256; % HBM/MFMA peak",
@@ -568,7 +590,9 @@ def main():
                                "GQA 32q/8kv decode", "n_rows_start": N0, "rank": R, "block": BLK,
                    "window": WIN, "reorth_every_rows": 256, "hip_graphs": not args.no_graphs,
                    "kv_merges": "batched" if batched else "two streams"},
-        "reconstructed_GBps": n_mid * D * 2 / (ms["recon_k"] * 1e-3) / 1e9,
+        "reconstructed_GBps": n_c * D * 2 / (ms["recon_k"] * 1e-3) / 1e9,
+        "timed_rows": {"n_total_first": timed_rows[0][0], "n_total_last": timed_rows[-1][0],
+                       "compressed_mean": n_c},
         "stage_ms": ms,
         "host_issue_ms_per_step": t_issue * 1e3 / steps,
         "roofline": {"bound": "hbm", "achieved": recon_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -632,6 +632,54 @@ def test_reconstruct_high_positions_rope(K):
         assert rel(gb, refb) < 5e-3, (base, rel(gb, refb))
 
 
+@pytest.mark.parametrize("c16", [False, True])
+def test_reconstruct_full_size_elementwise(K, c16):
+    """Algorithm 3 steps 7-8 at the full workload size (n = 16,384
+    compressed rows, D = 1024, r = 256, 512 exact rows): compressed and exact
+    positions are a shuffled partition of 0 .. n_total-1, and the compressed
+    rows arrive in shuffled position order. The bf16 output (the streaming
+    matrix-core kernel, which at this size takes several 32-row blocks per
+    workgroup through its two-block load ring) is compared element by element
+    with the oracle's rebuild of the GPU's own factors, with and without RoPE;
+    the fp32 output to 2e-6 relative. Repeated with 2-byte stored coordinates."""
+    D, hd, theta, n, ne = 1024, 128, 500000.0, 16384, 512
+    n_total = n + ne
+    X = synth.kv_stream(synth.CONFIG_KSTREAM, n)
+    rng = np.random.default_rng(17)
+    perm = rng.permutation(n_total).astype(np.int32)
+    comp_pos, ex_pos = perm[:n], perm[n:]
+    path = K.IsvdPath(D=D, r_max=256, b_max=32, n_cap=n, reorth_every_rows=256, device=DEV, coords_bf16=c16)
+    Xd = torch.from_numpy(X).to(DEV)
+    pd = torch.from_numpy(comp_pos).to(DEV)
+    for s in range(0, n, 32):
+        path.merge(Xd[s:s + 32], pd[s:s + 32])
+    C, B, _, pos, st = gpu_factors(path)
+    assert st == 0 and C.shape[0] == n and np.array_equal(pos, comp_pos)
+    fac = O.Factor(U=C, sigma=np.ones(C.shape[1]), B=B, pos=pos)
+    Xe = rng.standard_normal((ne, D)).astype(np.float32)
+    Xed = torch.from_numpy(Xe).to(DEV)
+    ped = torch.from_numpy(ex_pos.copy()).to(DEV)
+    for rope in (True, False):
+        ref = O.reconstruct(fac, Xe, ex_pos, n_total, hd, rope, theta)
+        out = torch.full((n_total, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+        path.reconstruct(out, n_total, X_exact=Xed, pos_exact=ped, head_dim=hd, rope=rope, theta=theta)
+        torch.cuda.synchronize()
+        gb = out.double().cpu().numpy()
+        assert np.isfinite(gb).all()
+        # element by element: bf16 rounding of the output (2^-9 relative) plus
+        # the bf16 rounding of C and B^T inside the products, bounded by the
+        # row's scale
+        rms = np.sqrt(np.mean(ref ** 2, axis=1, keepdims=True))
+        bad = np.abs(gb - ref) > 5e-3 * np.abs(ref) + 5e-3 * rms
+        assert not bad.any(), (rope, np.argwhere(bad)[:5])
+        assert rel(gb, ref) < 5e-3
+        got = gpu_recon_fp32(path, n_total, head_dim=hd, rope=rope, X_exact=Xed, pos_exact=ped)
+        assert rel(got, ref) < 2e-6, (rope, rel(got, ref))
+        print(f"c16={c16} rope={rope}: bf16 rel {rel(gb, ref):.3e}, max elt {np.abs(gb - ref).max():.3e}, "
+              f"fp32 rel {rel(got, ref):.3e}")
+    path.close()
+
+
 # --------------------------------------------------------------------------- attention
 @pytest.mark.parametrize("batch,n,hq,hkv", [(1, 1000, 32, 8), (2, 4096, 32, 8), (1, 63, 8, 8)])
 def test_decode_attend_matches_oracle(K, batch, n, hq, hkv):

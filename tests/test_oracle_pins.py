@@ -269,6 +269,97 @@ def test_rope_closed_forms():
     assert abs(d1 - d2).max() < 1e-12
 
 
+def test_reconstruct_turns_each_row_at_its_original_position():
+    """Algorithm 3 / §3.2: keys are rotated at their original token position
+    after the scatter, not at their compressed index. Planted unit rows on
+    feature 0 of a head (whose pair angle is pos * theta**0 = pos radians for
+    every theta) sit at shuffled positions; each must come out as
+    (cos pos, sin pos) on features (0, d_h/2) of that head, a row at position 0
+    must come out unturned, and two equal rows at positions a, b must have the
+    dot product cos(b - a)."""
+    rng = np.random.default_rng(31)
+    hd, Hkv, theta = 8, 2, 500000.0
+    D = Hkv * hd
+    n_total = 40
+    perm = rng.permutation(n_total)
+    z = int(np.nonzero(perm == 0)[0][0])
+    perm[z], perm[7] = perm[7], perm[z]          # position 0 sits at compressed index 7
+    pos_c, pos_e = perm[:25], perm[25:]
+    heads = rng.integers(0, Hkv, size=25)
+    rows = np.zeros((25, D))
+    rows[np.arange(25), heads * hd] = 1.0
+    # a factor whose represented rows are exactly those unit rows
+    U, s, Vt = np.linalg.svd(rows, full_matrices=False)
+    k = int(np.count_nonzero(s > 1e-12))
+    fac = O.Factor(U=U[:, :k], sigma=s[:k], B=Vt[:k].T, pos=pos_c.copy())
+    X_e = rng.standard_normal((15, D))
+    out = O.reconstruct(fac, X_e, pos_e, n_total, hd, apply_rope=True, theta=theta)
+    for i, p in enumerate(pos_c):
+        exp = np.zeros(D)
+        exp[heads[i] * hd] = math.cos(p)
+        exp[heads[i] * hd + hd // 2] = math.sin(p)
+        assert np.allclose(out[p], exp, atol=1e-12), (i, p)
+    i0 = int(np.nonzero(pos_c == 0)[0][0])
+    assert np.allclose(out[0], rows[i0], atol=1e-12)
+    same = [i for i in range(25) if heads[i] == heads[0]]
+    a, b = pos_c[same[0]], pos_c[same[1]]
+    assert abs(out[a] @ out[b] - math.cos(b - a)) < 1e-12
+    # exact rows: norms of every (j, j + d_h/2) pair are kept at their positions
+    for h in range(Hkv):
+        for j in range(hd // 2):
+            c0, c1 = h * hd + j, h * hd + j + hd // 2
+            assert np.allclose(out[pos_e, c0] ** 2 + out[pos_e, c1] ** 2, X_e[:, c0] ** 2 + X_e[:, c1] ** 2)
+    # turning at the compressed index instead would have been detected
+    wrong = np.cos(np.arange(25)[pos_c != np.arange(25)])
+    assert not np.allclose(out[pos_c[pos_c != np.arange(25)], heads[pos_c != np.arange(25)] * hd], wrong)
+
+
+@pytest.mark.parametrize("T,b,n", [(256, 32, 1024), (1024, 64, 4096)])
+def test_run_stream_reorth_schedule(monkeypatch, T, b, n):
+    """§4.4: re-orthogonalisation runs each time the folded-row counter
+    crosses a multiple of T (every T / b merges), and each call leaves the
+    represented product unchanged while making B and U orthonormal."""
+    calls = []
+    real = O.iskv_oracle.reorth
+
+    def counting(fac):
+        new = real(fac)
+        before, after = O.represented(fac), O.represented(new)
+        calls.append((fac.folded, float(np.linalg.norm(after - before) / np.linalg.norm(before)),
+                      float(np.abs(new.B.T @ new.B - np.eye(new.k)).max())))
+        return new
+
+    monkeypatch.setattr(O.iskv_oracle, "reorth", counting)
+    merges = []
+    X = synth.kv_stream(synth.StreamSpec(D=48, n=n, spectrum="exp4", noise_std=1e-3, seed=41))
+    O.run_stream(X, b, 6, reorth_every_rows=T, callback=lambda t, f: merges.append(f.folded))
+    assert [c[0] for c in calls] == list(range(T, n + 1, T))
+    assert len(calls) == n // T and len(merges) == n // b
+    for folded, drel, orth in calls:
+        assert drel < 1e-12 and orth < 1e-12
+    # T = 0 never re-orthogonalises; neither does the basis-only ablation
+    calls.clear()
+    O.run_stream(X[:4 * b], b, 6, reorth_every_rows=0)
+    O.run_stream(X[:4 * b], b, 6, reorth_every_rows=b, sync=False)
+    assert calls == []
+
+
+def test_value_first_refit_resets_the_reorth_counter(monkeypatch):
+    """§3.2 and §4.4: the value first refit is not a regular fold, so the
+    folded-row counter restarts at zero after it, and the next
+    re-orthogonalisation comes after T more folded rows."""
+    X = synth.kv_stream(synth.StreamSpec(D=32, n=400, spectrum="invsqrt", noise_std=0.0, seed=42))
+    fac = O.run_stream(X[:96], 16, 8, reorth_every_rows=64)
+    assert fac.folded == 96
+    fac = O.value_first_refit(fac, X[96:104], np.arange(96, 104), 8)
+    assert fac.folded == 0
+    calls = []
+    real = O.iskv_oracle.reorth
+    monkeypatch.setattr(O.iskv_oracle, "reorth", lambda f: (calls.append(f.folded), real(f))[1])
+    O.run_stream(X[104:232], 16, 8, reorth_every_rows=64, fac=fac, pos0=104)
+    assert calls == [64, 128]
+
+
 def test_bf16_round_known_values():
     vals = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, -2.5, 3.0e38, 1e-40])
     got = O.bf16_round(vals)
