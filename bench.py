@@ -87,11 +87,14 @@ def prefill_leg(args, K, torch, dev):
     L = 8192 rows, D = 1024 (8 KV heads x 128), r_K = 192 and r_V = 320
     (the K and V stream ranks), b = 64; anomaly scores on synthetic post-RoPE keys with 12 kept blocks per
     head (about 10% of the blocks, plus the value neighbourhoods), each path's
-    non-exact rows refit with 6 subspace iterations, then the value first
-    refit with the next 320 rows. Each stage timed on the null stream; median
+    non-exact rows refit (the fresh truncated SVD: 24 subspace iterations on
+    the key path, 40 on the value path), then the value first refit with the
+    next 320 rows. Each stage timed on the null stream; median
     of 2 runs after one warm-up."""
     import synth
-    L, hkv, dh, r_k, r, per_head, iters = 8192, 8, 128, 192, 320, 12, 6
+    # subspace iterations of the refits: the key spectrum converges in about
+    # 15 (24 kept), the value spectrum's flatter tail needs about 40
+    L, hkv, dh, r_k, r, per_head, iters_k, iters = 8192, 8, 128, 192, 320, 12, 24, 40
     Kb = torch.from_numpy(synth.prompt_keys(L, hkv, dh, 41)).to(dev).bfloat16()
     K_pre = torch.from_numpy(synth.kv_stream(synth.StreamSpec(D, L, "exp40+0.01", 0.0, 40))).to(dev)
     Vall = torch.from_numpy(synth.kv_stream(synth.StreamSpec(D, L + r, "invsqrt", 0.0, 41))).to(dev)
@@ -117,7 +120,7 @@ def prefill_leg(args, K, torch, dev):
         t["protect_ms"], _ = timed(lambda: K.iskv_prompt_protect(Kb, L, hkv, dh, 8, per_head, 4, 32, 128, flags,
                                                                   None, ws))
         t["split_ms"], (sk, sv) = timed(lambda: (K.prompt_split(K_pre, flags, 1), K.prompt_split(V, flags, 6)))
-        t["refit_k_ms"], _ = timed(lambda: kp.refit(sk[2], sk[3], iters=iters))
+        t["refit_k_ms"], _ = timed(lambda: kp.refit(sk[2], sk[3], iters=iters_k))
         t["refit_v_ms"], _ = timed(lambda: vp.refit(sv[2], sv[3], iters=iters))
         t["value_first_refit_ms"], _ = timed(lambda: vp.value_first_refit(Vnew, pos_new, iters=iters))
         rows = {"exact_k": int(sk[0].shape[0]), "refit_k": int(sk[2].shape[0]), "exact_v": int(sv[0].shape[0]),
@@ -127,7 +130,8 @@ def prefill_leg(args, K, torch, dev):
         kp.close()
         vp.close()
     res = {k: float(np.median([u[k] for u in runs])) for k in runs[0]}
-    res.update({"rows": rows, "L": L, "D": D, "r_k": r_k, "r_v": r, "b": 64, "iters": iters, "per_head": per_head})
+    res.update({"rows": rows, "L": L, "D": D, "r_k": r_k, "r_v": r, "b": 64, "iters_k": iters_k, "iters_v": iters,
+                "per_head": per_head})
     return res
 
 
@@ -145,7 +149,7 @@ def high_rank_leg(args, K, torch, dev):
     torch.cuda.synchronize()
     p = K.IsvdPath(D=D, r_max=r, b_max=b, n_cap=X.shape[0], reorth_every_rows=256, device=dev, stream=st,
                    graphs=not args.no_graphs)
-    p.refit(X[:n0], pos[:n0], iters=6)
+    p.refit(X[:n0], pos[:n0])
     for j in range(2):  # warm-up (records the sequences)
         s0 = n0 + j * b
         p.merge(X[s0:s0 + b], pos[s0:s0 + b])

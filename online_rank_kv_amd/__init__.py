@@ -266,7 +266,7 @@ def prompt_split(X, flags, mask: int, pos0: int = 0, stream=None):
 
 
 def prefill_init(kpath, vpath, K_pre, K_rot, V, Hkv: int, dh: int, block: int = 8, per_head: int = 128,
-                 suffix_blocks: int = 4, v_radius: int = 32, v_window: int = 128, iters: int = 6):
+                 suffix_blocks: int = 4, v_radius: int = 32, v_window: int = 128, iters: int = 40):
     """Prompt initialisation (iS-KV notes §3.1, Algorithm 1) of one
     layer's key and value paths (fresh handles, fp32 rows on the device):
     exact sets from the post-RoPE keys K_rot (bf16 [L, Hkv * dh]), E_K = P_K
@@ -474,7 +474,7 @@ class IsvdPath:
     def reorth(self) -> None:
         isvd_reorth(self.h)
 
-    def refit(self, X, pos, iters: int = 8) -> None:
+    def refit(self, X, pos, iters: int = 40) -> None:
         """Fresh rank-r truncated SVD of the rows X (fp32 [n, D]) at positions pos."""
         import torch
         work = None
@@ -483,7 +483,7 @@ class IsvdPath:
         isvd_refit(self.h, X, pos, int(X.shape[0]), iters, work)
         self._refit_work = work  # kept until the stream has used it
 
-    def value_first_refit(self, F, pos_F, iters: int = 6) -> None:
+    def value_first_refit(self, F, pos_F, iters: int = 40) -> None:
         """The value first refit: fresh truncated SVD of [history; F]."""
         import torch
         work = torch.empty((isvd_value_first_refit_workspace_bytes(self.h),), dtype=torch.uint8,

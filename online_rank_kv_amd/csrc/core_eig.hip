@@ -1563,6 +1563,16 @@ __global__ void bj_check_kernel(int32_t* st, double* smax, double tol, int last,
 
 inline size_t bj_lds_bytes() { return (size_t)2 * BJ_P * BJ_LD * sizeof(double); }
 
+// A dense matrix goes straight to the block Jacobi (cold: S = A, V = I).
+__global__ void bj_force_kernel(int32_t* st) {
+  st[ST_PCJ] = FLAG_FALLBACK | FLAG_COLD;
+  st[ST_PCJIT] = 0;
+  st[ST_ROUNDS] = 0;
+}
+// Sweep budget of a dense solve (enqueued up front; sweeps after convergence
+// return at once).
+constexpr int BJ_SWEEPS_DENSE = 16;
+
 }  // namespace
 
 void iskv_dgemm(hipStream_t s, int m_max, const double* A, bool ta, const double* B, bool tb, double* C,
@@ -1597,6 +1607,37 @@ int iskv_launch_core_eig(isvd_handle* h, double tol) {
   int32_t* st = w.st;
   const int nblk = (mm + 15) / 16;
   const size_t lds = sizeof(AnalyzeLds);
+  const int NB = ((mm + BJ_B - 1) / BJ_B + 1) & ~1;
+  const int tiles = (mm + BJ_P - 1) / BJ_P;
+  // block Jacobi: Km (free once the refinement has ended) holds the pairs'
+  // rotations, aux[0] the sweep's largest coupling
+  auto block_jacobi = [&](int sweeps) {
+    hipLaunchKernelGGL(bj_init_kernel, bz(dim3(64), h->bcount), dim3(256), 0, s, w.A, w.S, w.V, ld, st, w.aux,
+                       h->bd);
+    for (int sw = 0; sw < sweeps; ++sw) {
+      for (int r = 0; r < NB - 1; ++r) {
+        hipLaunchKernelGGL(bj_solve_kernel, bz(dim3(NB / 2), h->bcount), dim3(256), bj_lds_bytes(), s, w.S, ld, w.Km,
+                           st, w.aux, r, NB, 1e-13, h->bd);
+        hipLaunchKernelGGL(bj_rows_kernel, bz(dim3(NB / 2, tiles), h->bcount), dim3(256), 0, s, w.S, ld, w.Km, st, r,
+                           NB, h->bd);
+        hipLaunchKernelGGL(bj_cols_kernel, bz(dim3(NB / 2, tiles), h->bcount), dim3(256), 0, s, w.S, w.V, ld, w.Km, st,
+                           r, NB, h->bd);
+      }
+      // converged at the solve's tolerance (at least 1e-10: the two 64-term
+      // passes leave ~1e-14 max|s_ii| of rounding in the entries, scaled
+      // couplings near 1e-12 at the absolute floor)
+      hipLaunchKernelGGL(bj_check_kernel, bz(dim3(1), h->bcount), dim3(1), 0, s, st, w.aux, fmax(tol, 1e-10),
+                         sw == sweeps - 1 ? 1 : 0, h->bd);
+    }
+  };
+  const bool bj_fits = (size_t)(NB / 2) * BJ_P * BJ_P <= (size_t)ld * ld && w.naux >= 2;
+  if (h->force_block_jacobi && bj_fits && h->bcount == 1) {
+    // a dense matrix (the refit's Rayleigh-Ritz core): no refinement
+    hipLaunchKernelGGL(bj_force_kernel, dim3(1), dim3(1), 0, s, st);
+    block_jacobi(BJ_SWEEPS_DENSE);
+    ISKV_HIP_CHECK(hipGetLastError());
+    return ISKV_OK;
+  }
   hipLaunchKernelGGL(pcj_init_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.A, w.S, w.W0, ld, st, h->bd);
   // step 0 works on S = A with W = I
   hipLaunchKernelGGL(pcj_detect_kernel, bz(dim3(nblk), h->bcount), dim3(256), 0, s, w.S, ld, w.aux, w.edges, st,
@@ -1643,33 +1684,11 @@ int iskv_launch_core_eig(isvd_handle* h, double tol) {
   gemm<true, false>(s, mm, wc, w.Pa, w.S, nullptr, ld, 1.0, 0.0, 0.0, st, 3, h->bd, h->bcount);
   hipLaunchKernelGGL(pcj_final_kernel, bz(dim3(mm), h->bcount), dim3(256), 0, s, wc, w.Pa, w.A, w.S, w.V, ld,
                      w.aux, nblk * nblk, st, h->bd);
-  const int NB = ((mm + BJ_B - 1) / BJ_B + 1) & ~1;
-  // the pairs' rotations live in Km (ld x ld doubles), the sweep maxima in aux
-  const bool bj_fits = (size_t)(NB / 2) * BJ_P * BJ_P <= (size_t)ld * ld && w.naux >= 2;
-  if (!bj_fits || (mm <= BJ_MIN_M && !h->force_block_jacobi)) {
+  if (!bj_fits || mm <= BJ_MIN_M) {
     hipLaunchKernelGGL(core_jacobi_kernel, bz(dim3(1), h->bcount), dim3(1024), 0, s, w.S, w.V, ld, st, 1e-13,
                        ISKV_JACOBI_MAX_SWEEPS, h->bd);
   } else {
-    // block Jacobi; Km (free once the refinement has ended) holds the pairs'
-    // rotations, aux[0] the sweep's largest coupling
-    const int tiles = (mm + BJ_P - 1) / BJ_P;
-    hipLaunchKernelGGL(bj_init_kernel, bz(dim3(64), h->bcount), dim3(256), 0, s, w.A, w.S, w.V, ld, st, w.aux,
-                       h->bd);
-    for (int sw = 0; sw < BJ_SWEEPS; ++sw) {
-      for (int r = 0; r < NB - 1; ++r) {
-        hipLaunchKernelGGL(bj_solve_kernel, bz(dim3(NB / 2), h->bcount), dim3(256), bj_lds_bytes(), s, w.S, ld, w.Km,
-                           st, w.aux, r, NB, 1e-13, h->bd);
-        hipLaunchKernelGGL(bj_rows_kernel, bz(dim3(NB / 2, tiles), h->bcount), dim3(256), 0, s, w.S, ld, w.Km, st, r,
-                           NB, h->bd);
-        hipLaunchKernelGGL(bj_cols_kernel, bz(dim3(NB / 2, tiles), h->bcount), dim3(256), 0, s, w.S, w.V, ld, w.Km, st,
-                           r, NB, h->bd);
-      }
-      // converged at the solve's tolerance (at least 1e-10: the two 64-term
-      // passes leave ~1e-14 max|s_ii| of rounding in the entries, scaled
-      // couplings near 1e-12 at the absolute floor)
-      hipLaunchKernelGGL(bj_check_kernel, bz(dim3(1), h->bcount), dim3(1), 0, s, st, w.aux, fmax(tol, 1e-10),
-                         sw == BJ_SWEEPS - 1 ? 1 : 0, h->bd);
-    }
+    block_jacobi(BJ_SWEEPS);
   }
   ISKV_HIP_CHECK(hipGetLastError());
   return ISKV_OK;

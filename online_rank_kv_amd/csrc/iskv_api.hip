@@ -153,7 +153,7 @@ int isvd_refit(isvd_handle* h, const float* X, const int32_t* pos, int32_t n, in
   if (!h || !X || !pos || n < 1 || iters < 0 || iters > 64) return ISKV_EINVAL;
   if (n > h->cfg.n_cap) return ISKV_ECAPACITY;
   if (h->cfg.flags & (ISKV_NO_COORD_SYNC | ISKV_FROZEN_BASIS)) return ISKV_EMODE;
-  if (iters > 0 && !iskv_refit_supported(h->cfg)) return ISKV_EINVAL;
+  if (iters > 0 && (!iskv_refit_supported(h->cfg) || iskv_refit_block(h) > 1024)) return ISKV_EINVAL;
   if (iters > 0 && (!work || work_bytes < iskv_refit_ws_bytes(h))) return ISKV_EWORKSPACE;
   int rc = reset_history(h);
   if (rc) return rc;
@@ -165,16 +165,12 @@ int isvd_refit(isvd_handle* h, const float* X, const int32_t* pos, int32_t n, in
     }
     return ISKV_OK;
   }
-  // random orthonormal start, `iters` power steps with CholeskyQR2, then the
-  // Rayleigh-Ritz step, one refinement iteration and a last Ritz step
+  // the fp64 Gram, `iters` subspace iterations on an oversampled block, the
+  // Rayleigh-Ritz step and C = X B (refit_gram.hip)
   ISKV_HIP_CHECK(hipMemcpyAsync(h->pos, pos, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToDevice, h->stream));
   h->n_host = n;
   h->folded_host = 0;
-  rc = iskv_launch_refit_start(h, n);
-  if (rc) return rc;
-  rc = iskv_launch_refit_power(h, X, n, iters, work);
-  if (rc) return rc;
-  return iskv_launch_refit_iterations(h, X, n, 1, work);
+  return iskv_launch_refit_gram(h, X, n, iters, work);
 }
 
 // Workspace of the value first refit: the refit's, then B^T (r_max x D), the

@@ -111,8 +111,9 @@ struct isvd_handle {
   bool timing = false;
   bool timed = false;  // a merge has been timed since timing was switched on
   hipEvent_t tev[ISKV_STAGES + 1] = {};
-  // the core eigensolver's fallback is the block Jacobi whatever the core
-  // size (set around eager solves of dense cores, never while recording)
+  // the next core eigensolve is of a dense matrix: straight to the block
+  // Jacobi, no refinement (set around eager solves of the refit's
+  // Rayleigh-Ritz core, never while recording)
   bool force_block_jacobi = false;
 };
 
@@ -172,9 +173,13 @@ int iskv_launch_attend_fv(const uint16_t* q, const uint16_t* K, const isvd_handl
                           float scale, uint16_t* out, void* ws, size_t ws_bytes, hipStream_t s);
 bool iskv_refit_supported(const iskv_config& c);
 size_t iskv_refit_ws_bytes(const isvd_handle* h);
-int iskv_launch_refit_iterations(isvd_handle* h, const float* X, int32_t n, int32_t iters, void* work);
-int iskv_launch_refit_start(isvd_handle* h, int32_t n);
-int iskv_launch_refit_power(isvd_handle* h, const float* X, int32_t n, int32_t iters, void* work);
+// Fresh truncated SVD of n rows (refit_gram.hip): subspace block width, its
+// workspace, and the launch sequence (iters subspace iterations, >= 1).
+int iskv_refit_block(const isvd_handle* h);
+size_t iskv_refit_gram_ws_bytes(const isvd_handle* h);
+int iskv_launch_refit_gram(isvd_handle* h, const float* X, int32_t n, int32_t iters, void* work);
+// C <- X B for the n rows X (n x D fp32), k = st[ST_K] columns.
+int iskv_launch_coords_from_rows(isvd_handle* h, const float* X, int32_t n);
 int iskv_launch_materialize(isvd_handle* h, float* Y, float* Bt);
 size_t iskv_prompt_split_ws_bytes(int32_t L);
 int iskv_launch_prompt_split(const float* X, const uint8_t* flags, int32_t L, int32_t D, uint32_t mask, int32_t pos0,

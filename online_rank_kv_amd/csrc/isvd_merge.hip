@@ -1468,183 +1468,6 @@ int iskv_launch_reorth(isvd_handle* h) {
 // their eigensolves take the block Jacobi fallback.
 namespace {
 
-// Zpart[s][d][j] = sum over rows i of chunk s of X[i][d] C[i][j], for
-// d < D, j < k (64 x 64 output tile per workgroup, 4 x 4 per thread).
-template <typename TC>
-__global__ __launch_bounds__(256) void xtc_partial_kernel(const float* __restrict__ X, int ldx,
-                                                          const TC* __restrict__ C, int ldc, int n, int D,
-                                                          const int32_t* __restrict__ st, int rows_per_chunk,
-                                                          float* __restrict__ Zpart, int ldz) {
-  const int k = st[ST_K];
-  const int d0 = blockIdx.x * 64, j0 = blockIdx.y * 64;
-  if (j0 >= k) return;
-  const int r0 = blockIdx.z * rows_per_chunk, r1 = min(n, r0 + rows_per_chunk);
-  __shared__ float Xs[32][64 + 4], Cs[32][64 + 4];
-  const int t = threadIdx.x, td = t >> 4, tj = t & 15;
-  float acc[4][4] = {};
-  for (int rb = r0; rb < r1; rb += 32) {
-    for (int e = t; e < 32 * 64; e += 256) {
-      const int rr = e >> 6, cc = e & 63, row = rb + rr;
-      Xs[rr][cc] = (row < r1 && d0 + cc < D) ? X[(size_t)row * ldx + d0 + cc] : 0.f;
-      Cs[rr][cc] = (row < r1 && j0 + cc < k) ? iskv_ld(C + (size_t)row * ldc + j0 + cc) : 0.f;
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int rr = 0; rr < 32; ++rr) {
-      float xv[4], cv[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        xv[a] = Xs[rr][td + 16 * a];
-        cv[a] = Cs[rr][tj + 16 * a];
-      }
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[a][c] = fmaf(xv[a], cv[c], acc[a][c]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int d = d0 + td + 16 * a, j = j0 + tj + 16 * c;
-      if (d < D && j < k) Zpart[((size_t)blockIdx.z * D + d) * ldz + j] = acc[a][c];
-    }
-}
-
-// B[:, j] = Z[:, j] / |Z[:, j]| for j < k (Z = the sum of the chunk
-// partials), columns j >= k zero. One workgroup per column.
-__global__ __launch_bounds__(256) void refit_basis_kernel(const float* __restrict__ Zpart, int nchunks, int D,
-                                                          int ldz, const int32_t* __restrict__ st, float* B,
-                                                          int ldb) {
-  const int j = blockIdx.x, k = st[ST_K];
-  const int t = threadIdx.x;
-  __shared__ float red[4];
-  float ss = 0.f;
-  for (int d = t; d < D; d += 256) {
-    float z = 0.f;
-    for (int c = 0; c < nchunks; ++c) z += Zpart[((size_t)c * D + d) * ldz + j];
-    ss = fmaf(z, z, ss);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
-  if ((t & 63) == 0) red[t >> 6] = ss;
-  __syncthreads();
-  const float nrm = sqrtf(red[0] + red[1] + red[2] + red[3]);
-  const float inv = (j < k && nrm > 0.f) ? 1.f / nrm : 0.f;
-  for (int d = t; d < D; d += 256) {
-    float z = 0.f;
-    if (j < k)
-      for (int c = 0; c < nchunks; ++c) z += Zpart[((size_t)c * D + d) * ldz + j];
-    B[(size_t)d * ldb + j] = z * inv;
-  }
-}
-
-constexpr int RF_CHUNKS = 16;  // row chunks of X^T C
-
-// History of n rows of rank k = min(r_max, n, D) about to be built directly.
-__global__ void refit_start_kernel(int32_t* st, int n, int k) {
-  st[ST_N] = n;
-  st[ST_K] = k;
-  st[ST_FOLDED] = 0;
-}
-
-// Start basis: B[d][j] uniform in [-1, 1) for j < k from a splitmix64 hash
-// of (d, j), columns past k zero.
-__global__ __launch_bounds__(256) void rand_basis_kernel(float* B, int D, int R, const int32_t* __restrict__ st) {
-  const int k = st[ST_K];
-  const size_t tot = (size_t)D * R;
-  for (size_t e = blockIdx.x * 256 + threadIdx.x; e < tot; e += (size_t)gridDim.x * 256) {
-    const int j = (int)(e % R);
-    unsigned long long z = e + 0x9e3779b97f4a7c15ull;
-    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
-    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
-    z ^= z >> 31;
-    const float u = (float)(z >> 40) * (1.0f / 16777216.0f);  // [0, 1)
-    B[e] = j < k ? 2.f * u - 1.f : 0.f;
-  }
-}
-
-// Cholesky factor L of G + rel_shift tr(G)/k I (G = B^T B, k x k fp64 at ld,
-// overwritten by L in its lower triangle). One workgroup, right-looking,
-// column by column; the scaled column is cached in LDS for the trailing
-// update. The shift keeps a numerically rank-deficient G factorable with
-// bounded growth (shifted CholeskyQR); the passes after it restore
-// orthonormality.
-__global__ __launch_bounds__(1024) void chol_kernel(double* G, int ld, const int32_t* __restrict__ st,
-                                                    double rel_shift) {
-  const int k = st[ST_K];
-  const int t = threadIdx.x, nt = blockDim.x;
-  __shared__ double shift;
-  __shared__ double col[1024];
-  if (t == 0) {
-    double tr = 0.0;
-    for (int i = 0; i < k; ++i) tr += G[(size_t)i * ld + i];
-    shift = rel_shift * (k > 0 ? tr / k : 0.0) + 1e-300;
-  }
-  __syncthreads();
-  for (int i = t; i < k; i += nt) G[(size_t)i * ld + i] += shift;
-  __syncthreads();
-  for (int j = 0; j < k; ++j) {
-    const double d = sqrt(fmax(G[(size_t)j * ld + j], shift));
-    __syncthreads();
-    if (t == 0) G[(size_t)j * ld + j] = d;
-    for (int i = j + 1 + t; i < k; i += nt) {
-      const double v = G[(size_t)i * ld + j] / d;
-      G[(size_t)i * ld + j] = v;
-      col[i] = v;
-    }
-    __syncthreads();
-    // trailing update of the lower triangle: wave per row, lanes along it
-    for (int i = j + 1 + (t >> 6); i < k; i += nt >> 6) {
-      const double ci = col[i];
-      double* Gi = G + (size_t)i * ld;
-      for (int l = j + 1 + (t & 63); l <= i; l += 64) Gi[l] -= ci * col[l];
-    }
-    __syncthreads();
-  }
-}
-
-// H = L^(-T) (H[c][i] = (L^(-1))[i][c]), one wave per column c of L^(-1):
-// forward substitution x_i = (delta_ic - sum_{c <= m < i} L_im x_m) / L_ii,
-// the sum split over the 64 lanes (lane l holds x_m for m = c + l + 64q in
-// registers) and reduced across the wave. k <= 1024.
-__global__ __launch_bounds__(256) void tri_inv_kernel(const double* __restrict__ L, double* H, int ld,
-                                                      const int32_t* __restrict__ st) {
-  const int k = st[ST_K];
-  const int lane = threadIdx.x & 63;
-  const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (c >= k) return;  // whole waves; no workgroup barrier below
-  constexpr int NQ = 16;
-  double xr[NQ];
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) xr[q] = 0.0;
-  for (int i = c; i < k; ++i) {
-    const double* Li = L + (size_t)i * ld;
-    double part = 0.0;
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int m = c + lane + 64 * q;
-      if (m < i) part = fma(Li[m], xr[q], part);
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
-    const double x = ((i == c ? 1.0 : 0.0) - part) / Li[i];
-    const int q0 = (i - c) >> 6, owner = (i - c) & 63;
-#pragma unroll
-    for (int q = 0; q < NQ; ++q)
-      if (q == q0 && lane == owner) xr[q] = x;
-  }
-  double* Hc = H + (size_t)c * ld;
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const int i = c + lane + 64 * q;
-    if (i < k) Hc[i] = xr[q];
-  }
-  for (int i = lane; i < c; i += 64) Hc[i] = 0.0;
-}
-
 // Bt[j][d] = B[d][j] (32 x 32 tiles through LDS).
 __global__ __launch_bounds__(256) void transpose_b_kernel(const float* __restrict__ B, int D, int R,
                                                           float* __restrict__ Bt) {
@@ -1679,112 +1502,19 @@ int iskv_launch_materialize(isvd_handle* h, float* Y, float* Bt) {
 // C <- X B stages 16 rows of X (D wide) in LDS: D up to 1984.
 bool iskv_refit_supported(const iskv_config& c) { return xh_lds_bytes(16, c.D) <= 160 * 1024; }
 
-size_t iskv_refit_ws_bytes(const isvd_handle* h) {
-  return (size_t)RF_CHUNKS * h->cfg.D * h->cfg.r_max * sizeof(float);
-}
+size_t iskv_refit_ws_bytes(const isvd_handle* h) { return iskv_refit_gram_ws_bytes(h); }
 
-// B <- B R^(-1) with R^T R = B^T B + shift (CholeskyQR): an orthonormal
-// basis of span(B) for a well-conditioned B (shift 1e-13 relative); with the
-// shift 1e-6 relative, a basis of condition at most ~1e3 for any B.
-static int cholqr_basis(isvd_handle* h, double rel_shift = 1e-13) {
+// C <- X B over the n rows X (n x D fp32), k = st[ST_K] columns; stored as
+// the handle keeps its coordinates (fp32 or bf16).
+int iskv_launch_coords_from_rows(isvd_handle* h, const float* X, int32_t n) {
   const iskv_config& c = h->cfg;
-  const isvd_ws& w = h->w;
-  hipStream_t s = h->stream;
-  const int R = c.r_max, D = c.D, ld = h->ldm;
-  const int tiles = (R + 15) / 16;
-  hipLaunchKernelGGL(gram_partial_kernel<float>, dim3(tiles * tiles, 1), dim3(256), 0, s, h->B, R, hdim(D), w.st,
-                     w.GC, R, D, nullptr);
-  hipLaunchKernelGGL(reorth_sum_kernel, dim3(128), dim3(256), 0, s, w.GC, 0, R, w.Km, w.Pa, w.Pb, ld, w.st, nullptr);
-  hipLaunchKernelGGL(chol_kernel, dim3(1), dim3(1024), 0, s, w.Pa, ld, w.st, rel_shift);
-  hipLaunchKernelGGL(tri_inv_kernel, dim3((R + 3) / 4), dim3(256), 0, s, w.Pa, w.T, ld, w.st);
-  hipLaunchKernelGGL(to_f32_kernel, dim3(128), dim3(256), 0, s, w.T, w.T, ld, w.Hc, w.T2, R, w.st, nullptr);
-  xh_launch(s, nullptr, 1, D, h->B, R, nullptr, 0, ddim(w.st + ST_K), ddim(w.st + ST_K), R, w.T2, R, R,
-            ddim(w.st + ST_K), hdim(D), h->B, R, w.Bbf, R, nullptr, nullptr, true);
+  const int D = c.D, R = c.r_max;
+  with_coords(h, [&](auto* Cp) {
+    xh_launch(h->stream, nullptr, 1, n, X, D, nullptr, 0, hdim(D), hdim(D), D, h->B, R, R, ddim(h->w.st + ST_K),
+              hdim(n), Cp, R, nullptr, 0, nullptr, nullptr, true);
+  });
   ISKV_HIP_CHECK(hipGetLastError());
   return ISKV_OK;
-}
-
-int iskv_launch_refit_start(isvd_handle* h, int32_t n) {
-  const iskv_config& c = h->cfg;
-  int k = c.r_max < n ? c.r_max : n;
-  if (k > c.D) k = c.D;
-  hipLaunchKernelGGL(refit_start_kernel, dim3(1), dim3(1), 0, h->stream, h->w.st, n, k);
-  hipLaunchKernelGGL(rand_basis_kernel, dim3(256), dim3(256), 0, h->stream, h->B, c.D, c.r_max, h->w.st);
-  ISKV_HIP_CHECK(hipGetLastError());
-  for (int pass = 0; pass < 2; ++pass) {  // CholeskyQR2
-    const int rc = cholqr_basis(h);
-    if (rc) return rc;
-  }
-  return ISKV_OK;
-}
-
-int iskv_launch_refit_power(isvd_handle* h, const float* X, int32_t n, int32_t iters, void* work) {
-  const iskv_config& c = h->cfg;
-  hipStream_t s = h->stream;
-  const int D = c.D, R = c.r_max;
-  float* Zp = (float*)work;
-  const int rpc = (n + RF_CHUNKS - 1) / RF_CHUNKS;
-  for (int it = 0; it < iters; ++it) {
-    with_coords(h, [&](auto* Cp) {
-      using TC = std::remove_pointer_t<decltype(Cp)>;
-      xh_launch(s, nullptr, 1, n, X, D, nullptr, 0, hdim(D), hdim(D), D, h->B, R, R, ddim(h->w.st + ST_K), hdim(n),
-                Cp, R, nullptr, 0, nullptr, nullptr, true);
-      hipLaunchKernelGGL((xtc_partial_kernel<TC>), dim3((D + 63) / 64, (R + 63) / 64, RF_CHUNKS), dim3(256), 0, s, X,
-                         D, (const TC*)Cp, R, n, D, h->w.st, rpc, Zp, R);
-    });
-    hipLaunchKernelGGL(refit_basis_kernel, dim3(R), dim3(256), 0, s, Zp, RF_CHUNKS, D, R, h->w.st, h->B, R);
-    ISKV_HIP_CHECK(hipGetLastError());
-    // X^T X B is ill-conditioned in fp32: shifted CholeskyQR3
-    for (int pass = 0; pass < 3; ++pass) {
-      const int rc = cholqr_basis(h, pass == 0 ? 1e-6 : 1e-13);
-      if (rc) return rc;
-    }
-  }
-  return ISKV_OK;
-}
-
-int iskv_launch_refit_iterations(isvd_handle* h, const float* X, int32_t n, int32_t iters, void* work) {
-  const iskv_config& c = h->cfg;
-  hipStream_t s = h->stream;
-  const int D = c.D, R = c.r_max;
-  float* Zp = (float*)work;
-  if (iters > 0 && !iskv_refit_supported(c)) return ISKV_EINVAL;
-  const int rpc = (n + RF_CHUNKS - 1) / RF_CHUNKS;
-  auto c_from_x = [&]() {  // C <- X B (rows 0 .. n-1, k columns)
-    with_coords(h, [&](auto* Cp) {
-      xh_launch(s, nullptr, 1, n, X, D, nullptr, 0, hdim(D), hdim(D), D, h->B, R, R, ddim(h->w.st + ST_K), hdim(n),
-                Cp, R, nullptr, 0, nullptr, nullptr, true);
-    });
-  };
-  auto ritz = [&]() -> int {  // C <- X B, then the exact SVD of C B^T
-    c_from_x();
-    ISKV_HIP_CHECK(hipGetLastError());
-    // eager, with the block Jacobi: the first Ritz core of a refit is dense
-    h->force_block_jacobi = true;
-    const int rc = reorth_body(h);
-    h->force_block_jacobi = false;
-    return rc;
-  };
-  for (int it = 0; it < iters; ++it) {
-    // Ritz vectors of X^T X in span(B) (B orthonormal here): z_i = X^T X b_i
-    // then equals theta_i b_i plus a residual orthogonal to span(B), so the
-    // normalised columns of Z are orthonormal up to the residuals' products
-    int rc = ritz();
-    if (rc) return rc;
-    with_coords(h, [&](auto* Cp) {
-      using TC = std::remove_pointer_t<decltype(Cp)>;
-      hipLaunchKernelGGL((xtc_partial_kernel<TC>), dim3((D + 63) / 64, (R + 63) / 64, RF_CHUNKS), dim3(256), 0, s, X,
-                         D, (const TC*)Cp, R, n, D, h->w.st, rpc, Zp, R);
-    });
-    hipLaunchKernelGGL(refit_basis_kernel, dim3(R), dim3(256), 0, s, Zp, RF_CHUNKS, D, R, h->w.st, h->B, R);
-    ISKV_HIP_CHECK(hipGetLastError());
-    // orthonormal basis of span(Z) (the coordinates are recomputed next)
-    for (int pass = 0; pass < 3; ++pass) {
-      rc = cholqr_basis(h, pass == 0 ? 1e-6 : 1e-13);
-      if (rc) return rc;
-    }
-  }
-  return iters > 0 ? ritz() : ISKV_OK;
 }
 
 // ---------------------------------------------------------------------------

@@ -666,16 +666,27 @@ def test_reconstruct_full_size_elementwise(K, c16):
         torch.cuda.synchronize()
         gb = out.double().cpu().numpy()
         assert np.isfinite(gb).all()
-        # element by element: bf16 rounding of the output (2^-9 relative) plus
-        # the bf16 rounding of C and B^T inside the products, bounded by the
-        # row's scale
-        rms = np.sqrt(np.mean(ref ** 2, axis=1, keepdims=True))
-        bad = np.abs(gb - ref) > 5e-3 * np.abs(ref) + 5e-3 * rms
-        assert not bad.any(), (rope, np.argwhere(bad)[:5])
+        # element by element, a worst-case bound of the bf16 arithmetic (8
+        # significant bits: rounding moves a value by at most 2^-8 of it):
+        # the output's rounding, plus the rounding of every product term
+        # c_k B[d, k] (C and B^T each stored in bf16: at most 2^-7 of
+        # |c_k B[d, k]|), summed as |C| |B|^T and over both members of the
+        # rotated pair when RoPE mixes them; fp32 accumulation and the fp32
+        # rotation add far less than the 2^-10 slack
+        A = np.abs(C) @ np.abs(B).T
+        if rope:
+            hv = hd // 2
+            Ap = A.reshape(n, D // hd, 2, hv)
+            A = (Ap + Ap[:, :, ::-1, :]).reshape(n, D)
+        err = np.abs(gb - ref)
+        ratio_c = err[comp_pos] / (2.0 ** -8 * (1 + 2.0 ** -10) * (np.abs(ref[comp_pos]) + 2 * A))
+        ratio_e = err[ex_pos] / (2.0 ** -8 * (1 + 2.0 ** -10) * np.abs(ref[ex_pos]) + 1e-6 * np.abs(Xe).max())
+        assert ratio_c.max() <= 1.0, (rope, np.argwhere(ratio_c > 1.0)[:5], ratio_c.max())
+        assert ratio_e.max() <= 1.0, (rope, np.argwhere(ratio_e > 1.0)[:5], ratio_e.max())
         assert rel(gb, ref) < 5e-3
         got = gpu_recon_fp32(path, n_total, head_dim=hd, rope=rope, X_exact=Xed, pos_exact=ped)
         assert rel(got, ref) < 2e-6, (rope, rel(got, ref))
-        print(f"c16={c16} rope={rope}: bf16 rel {rel(gb, ref):.3e}, max elt {np.abs(gb - ref).max():.3e}, "
+        print(f"c16={c16} rope={rope}: bf16 rel {rel(gb, ref):.3e}, largest error / bound {ratio_c.max():.3f} (compressed), {ratio_e.max():.3f} (exact), "
               f"fp32 rel {rel(got, ref):.3e}")
     path.close()
 
@@ -907,18 +918,21 @@ def test_prompt_protect_matches_oracle(K, L, hkv, dh, per_head):
 
 
 # --------------------------------------------------------------------------- fresh truncated SVD (refit)
-@pytest.mark.parametrize("D,r,b,n,spec,iters,c16", [
-    (128, 16, 32, 600, "exp4", 12, False),
-    (256, 40, 64, 1000, "exp40+0.01", 8, False),
-    (1024, 192, 64, 3000, "exp40+0.01", 6, False),
-    (1024, 320, 64, 3000, "invsqrt", 6, True),
+@pytest.mark.parametrize("D,r,b,n,spec,c16", [
+    (128, 16, 32, 600, "exp4", False),
+    (256, 40, 64, 1000, "exp40+0.01", False),
+    (1024, 192, 64, 3000, "exp40+0.01", False),
+    (1024, 320, 64, 3000, "invsqrt", False),
+    (1024, 320, 64, 3000, "invsqrt", True),
 ])
-def test_refit_reaches_fresh_truncated_svd(K, D, r, b, n, spec, iters, c16):
+def test_refit_reaches_fresh_truncated_svd(K, D, r, b, n, spec, c16):
     """isvd_refit (Algorithm 1, the value first refit of §3.2): the
-    handle's old history is dropped; with iters = 0 the factors are the
-    oracle's fold of the rows; the iterations bring the error down towards the
-    Eckart-Young optimum of the oracle's fresh truncated SVD and never below
-    it, with orthonormal B and the rows' positions kept."""
+    handle's old history is dropped and the factor is the oracle's fresh
+    rank-r truncated SVD X_r of the rows: rel |C B^T - X_r| <= 1e-3 (fp32
+    coordinates; 2-byte coordinates carry their own rounding, 2^-8 relative,
+    so their floor is 5e-3). With iters = 0 the factors are the oracle's fold
+    of the rows instead. Also: the error equals the Eckart-Young optimum,
+    singular values interlace from below, B is orthonormal, positions kept."""
     X = synth.kv_stream(synth.StreamSpec(D=D, n=n, spectrum=spec, noise_std=0.0, seed=70 + D + r))
     Xd = torch.from_numpy(X).to(DEV)
     pos = (1000 + 3 * torch.arange(n, dtype=torch.int32)).to(DEV)
@@ -926,34 +940,37 @@ def test_refit_reaches_fresh_truncated_svd(K, D, r, b, n, spec, iters, c16):
     old = torch.randn((b, D), device=DEV)
     path.merge(old, torch.arange(b, dtype=torch.int32, device=DEV))   # history the refit replaces
     Xr, disc = O.fresh_truncated_svd(X, r)
+    sv_all = np.linalg.svd(X.astype(np.float64), compute_uv=False)
+    gap = (sv_all[r - 1] - sv_all[r]) / sv_all[r - 1]
+    assert gap > 1e-5, f"X_r is ill-conditioned at this cut (relative gap {gap:.1e}): no unique target"
     nx = np.linalg.norm(X)
     opt = math.sqrt(float(np.sum(disc ** 2))) / nx
-    errs = {}
-    for it in (0, iters):
-        path.refit(Xd, pos, iters=it)
-        torch.cuda.synchronize()
-        C, B, s, p, st = gpu_factors(path)
-        assert st == 0 and C.shape[0] == n
-        assert np.array_equal(p, pos.cpu().numpy())
-        errs[it] = np.linalg.norm(X - C @ B.T) / nx
-        assert np.abs(B.T @ B - np.eye(B.shape[1])).max() < 1e-4
-        if it == 0 and not c16:
-            ref = O.represented(O.run_stream(X, b, r))
-            assert rel(C @ B.T, ref) < 1e-3
-    sv = np.linalg.svd(X.astype(np.float64), compute_uv=False)[:r]
-    print(f"D={D} r={r} {spec}: optimum {opt:.6e}, fold {errs[0]:.6e}, {iters} iterations {errs[iters]:.6e}; "
-          f"sigma rel {np.abs(s - sv).max() / sv[0]:.2e}; to X_r {rel(C @ B.T, Xr):.2e}")
+    path.refit(Xd, pos, iters=0)
+    torch.cuda.synchronize()
+    C, B, s, p, st = gpu_factors(path)
+    assert st == 0 and C.shape[0] == n and np.array_equal(p, pos.cpu().numpy())
+    if not c16:
+        assert rel(C @ B.T, O.represented(O.run_stream(X, b, r))) < 1e-3
+    err_fold = np.linalg.norm(X - C @ B.T) / nx
+    path.refit(Xd, pos)
+    torch.cuda.synchronize()
+    C, B, s, p, st = gpu_factors(path)
+    assert st == 0 and C.shape[0] == n
+    assert np.array_equal(p, pos.cpu().numpy())
+    assert np.abs(B.T @ B - np.eye(B.shape[1])).max() < 1e-4
+    to_xr = rel(C @ B.T, Xr)
+    err = np.linalg.norm(X - C @ B.T) / nx
+    sv = sv_all[:r]
+    print(f"D={D} r={r} {spec} c16={c16}: to X_r {to_xr:.2e}; optimum {opt:.6e}, refit {err:.6e}, "
+          f"fold {err_fold:.6e}; sigma rel {np.abs(s - sv).max() / sv[0]:.2e}; gap at r {gap:.1e}")
+    assert to_xr <= (5e-3 if c16 else 1e-3), to_xr
     floor = 4e-3 if c16 else 2e-5   # coordinate rounding (bf16: 2^-8 relative) and fp32 products
-    assert errs[iters] >= opt * (1 - 1e-6) - floor
-    assert errs[iters] <= errs[0] + floor
-    assert errs[iters] - opt <= 0.25 * (errs[0] - opt) + floor
-    # Ritz values approach the singular values from below (Poincare
-    # interlacing for C = X B with B orthonormal); the leading half, far from
-    # the cut, have converged
+    assert opt * (1 - 1e-6) - floor <= err <= opt * (1 + 1e-5) + floor
+    # singular values interlace from below (C = X B with B orthonormal) and
+    # equal the oracle's to the coordinates' precision
     tol = 5e-3 if c16 else 1e-5
     assert np.all(s <= sv * (1 + tol) + tol * sv[0])
-    h = r // 2
-    assert np.abs(s[:h] - sv[:h]).max() < (5e-3 if c16 else 1e-4) * sv[0]
+    assert np.abs(s - sv).max() < (5e-3 if c16 else 1e-5) * sv[0]
 
 
 # --------------------------------------------------------------------------- prompt initialisation
@@ -1013,22 +1030,28 @@ def test_prefill_init_and_value_first_refit(K, L, per_head, r_K, r_V):
         Xr = X[~E].astype(np.float64)
         err = np.linalg.norm(Xr - C @ B.T) / np.linalg.norm(Xr)
         opt = np.linalg.norm(Xr - O.represented(fac)) / np.linalg.norm(Xr)
-        print(f"  path r={B.shape[1]}: error {err:.6e}, optimum {opt:.6e}")
-        assert opt * (1 - 1e-6) - 2e-5 <= err <= opt * 1.01 + 2e-5
+        to_xr = rel(C @ B.T, O.represented(fac))
+        print(f"  path r={B.shape[1]}: to the oracle's factor {to_xr:.2e}; error {err:.6e}, optimum {opt:.6e}")
+        assert to_xr <= 1e-3
+        assert opt * (1 - 1e-6) - 2e-5 <= err <= opt * (1 + 1e-5) + 2e-5
         assert np.abs(B.T @ B - np.eye(B.shape[1])).max() < 1e-4
-    # value first refit with the next r_V rows
-    C, B, _, p0, _ = gpu_factors(vp)
+    # value first refit with the next r_V rows: the oracle's value_first_refit
+    # on the GPU's own value factor (rebuilt history C B^T, then the new rows)
+    C, B, s0, p0, _ = gpu_factors(vp)
+    fV_gpu = O.Factor(U=C / np.where(s0 > 0, s0, 1.0)[None, :], sigma=s0, B=B, pos=p0)
     new = Vall[L:L + r_V]
-    stacked = np.concatenate([C @ B.T, new.astype(np.float64)])
-    ref = O.truncated_factor(stacked, np.concatenate([p0, np.arange(L, L + r_V)]), r_V)
+    ref = O.value_first_refit(fV_gpu, new, np.arange(L, L + r_V), r_V)
+    stacked = np.concatenate([O.represented(fV_gpu), new.astype(np.float64)])
     vp.value_first_refit(torch.from_numpy(new).to(DEV), torch.arange(L, L + r_V, dtype=torch.int32, device=DEV))
     torch.cuda.synchronize()
     C2, B2, _, p2, st = gpu_factors(vp)
     assert st == 0 and np.array_equal(p2, ref.pos)
     err = np.linalg.norm(stacked - C2 @ B2.T) / np.linalg.norm(stacked)
     opt = np.linalg.norm(stacked - O.represented(ref)) / np.linalg.norm(stacked)
-    print(f"  value first refit: error {err:.6e}, optimum {opt:.6e}")
-    assert opt * (1 - 1e-6) - 2e-5 <= err <= opt * 1.01 + 2e-5
+    to_xr = rel(C2 @ B2.T, O.represented(ref))
+    print(f"  value first refit: to the oracle's factor {to_xr:.2e}; error {err:.6e}, optimum {opt:.6e}")
+    assert to_xr <= 1e-3
+    assert opt * (1 - 1e-6) - 2e-5 <= err <= opt * (1 + 1e-5) + 2e-5
 
 
 # --------------------------------------------------------------------------- 64K-row prompt + decode stream
@@ -1053,7 +1076,7 @@ def test_prompt_decode_stream_64k(K, r):
     ne = int(Xe.shape[0])
     print(f"prompt: {ne} exact rows, {int(Xr.shape[0])} refit", flush=True)
     path = K.IsvdPath(D=D, r_max=r, b_max=b, n_cap=N, reorth_every_rows=256, device=DEV)
-    path.refit(Xr, pr, iters=6)
+    path.refit(Xr, pr)
     win = K.ExactWindow(path, window=w, block=b, prot_cap=ne)
     win.protect(Xe, [int(v) for v in pe.cpu().numpy()])
     for s in range(L, N, 512):
