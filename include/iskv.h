@@ -275,6 +275,24 @@ int decode_attend(const uint16_t* q, const uint16_t* K, const uint16_t* V, int32
                   int32_t n, int32_t Hq, int32_t Hkv, int32_t dh, float scale, uint16_t* out,
                   void* workspace, size_t ws_bytes, void* stream);
 
+/* decode_attend for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and kernels as decode_attend, with the partial
+ * results in a fixed 8 MiB device array inside the library instead of a
+ * caller workspace. Nothing is allocated, here or in the library.
+ *   Limit: batch * Hq * ceil(n / 128) * 520 bytes <= 8 MiB (for example
+ *   Hq = 32 with batch * n <= 64,512 rows); larger calls return
+ *   ISKV_EWORKSPACE before anything is enqueued.
+ *   stream must belong to the current device (EINVAL otherwise). The first
+ *   call on a device looks up that device's copy of the array.
+ *   Every call on one device shares its array: calls that may overlap on one
+ *   device (concurrent streams, or host threads) race and must be
+ *   serialised by the caller. Each call writes every partial it reads, so
+ *   nothing carries over from the previous call.
+ * Arguments, limits and other errors as decode_attend. */
+int decode_attend_noalloc(const uint16_t* q, const uint16_t* K, const uint16_t* V, int32_t batch, int32_t n,
+                          int32_t Hq, int32_t Hkv, int32_t dh, float scale, uint16_t* out, void* stream);
+
 /* Decode attention with the value history kept factored (the value-side
  * decode the iS-KV notes point to in §5.2 and §6: attend with the factors
  * rather than rebuilding the dense value cache). One sequence. For query

@@ -25,8 +25,8 @@ __all__ = [
     "ISKV_OUT_FP32", "ISKV_DEV_NONFINITE", "ISKV_DEV_NOCONV", "EXPORTED_SYMBOLS",
     "isvd_workspace_bytes", "isvd_init", "isvd_merge_block", "isvd_reorth", "isvd_query",
     "isvd_rows", "isvd_destroy", "isvd_query_state", "isvd_sym_eig", "kv_reconstruct", "kv_scatter_exact",
-    "decode_attend_workspace_bytes", "decode_attend", "decode_attend_fv_workspace_bytes", "decode_attend_fv",
-    "iskv_window_rows", "iskv_window_init", "iskv_window_protect",
+    "decode_attend_workspace_bytes", "decode_attend", "decode_attend_noalloc", "decode_attend_fv_workspace_bytes",
+    "decode_attend_fv", "iskv_window_rows", "iskv_window_init", "iskv_window_protect",
     "iskv_window_append", "iskv_window_exact", "iskv_window_destroy", "iskv_strerror",
     "iskv_window_append_batched", "isvd_merge_block_batched", "isvd_set_timing", "isvd_stage_times", "MERGE_STAGES", "IsvdPath", "IsvdBatch", "ExactWindow",
 ]
@@ -59,7 +59,7 @@ EXPORTED_SYMBOLS = (
     "decode_attend_fv_workspace_bytes", "decode_attend_fv", "isvd_set_mode",
     "iskv_prompt_protect_workspace_bytes", "iskv_prompt_protect", "isvd_refit_workspace_bytes", "isvd_refit",
     "isvd_value_first_refit_workspace_bytes", "isvd_value_first_refit", "iskv_prompt_split_workspace_bytes",
-    "iskv_prompt_split",
+    "iskv_prompt_split", "decode_attend_noalloc",
 )
 
 
@@ -136,6 +136,7 @@ lib.decode_attend_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
 lib.decode_attend.restype = ctypes.c_int
 lib.decode_attend.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _vp, _vp,
                               ctypes.c_size_t, _vp]
+lib.decode_attend_noalloc.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _vp, _vp]
 lib.decode_attend_fv_workspace_bytes.restype = ctypes.c_size_t
 lib.decode_attend_fv_workspace_bytes.argtypes = [_vp, _i32, _i32]
 lib.decode_attend_fv.restype = ctypes.c_int
@@ -381,6 +382,14 @@ def decode_attend(q, K, V, batch: int, n: int, Hq: int, Hkv: int, dh: int, scale
                              int(dh), float(scale), _ptr(out), _ptr(workspace),
                              workspace.numel() * workspace.element_size(), _stream_ptr(stream)),
            "decode_attend")
+
+
+def decode_attend_noalloc(q, K, V, batch: int, n: int, Hq: int, Hkv: int, dh: int, scale: float, out,
+                          stream=None) -> None:
+    """decode_attend with its partials in the library's fixed device scratch
+    (no workspace, nothing allocated); see include/iskv.h for the size limit."""
+    _check(lib.decode_attend_noalloc(_ptr(q), _ptr(K), _ptr(V), int(batch), int(n), int(Hq), int(Hkv), int(dh),
+                                     float(scale), _ptr(out), _stream_ptr(stream)), "decode_attend_noalloc")
 
 
 def decode_attend_fv_workspace_bytes(hv: int, n_exact: int, Hq: int) -> int:

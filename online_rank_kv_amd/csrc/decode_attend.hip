@@ -7,6 +7,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 namespace {
 
 constexpr int DH = 128;
@@ -214,7 +216,49 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(const float* __rest
 
 static int num_splits(int n) { return (n + ROWS - 1) / ROWS; }
 
+// Scratch of decode_attend_noalloc: the split kernel's (max, sum, output)
+// partials live in this fixed array instead of a caller workspace. Every
+// device holds its own copy until the process ends. Host code uses only the
+// per-device address from hipGetSymbolAddress, never the array's name.
+constexpr size_t ATTEND_SCRATCH_BYTES = (size_t)8 << 20;
+__device__ __align__(256) float scratch[ATTEND_SCRATCH_BYTES / sizeof(float)];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[MAX_DEVICES] = {};
+
+// Device address of this device's scratch, looked up once per device with
+// that device current.
+int scratch_for(int dev, float** out) {
+  if (dev < 0 || dev >= MAX_DEVICES) return ISKV_EINVAL;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    ISKV_HIP_CHECK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return ISKV_EHIP;
+    g_scratch_ptr[dev] = (float*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ISKV_OK;
+}
+
 }  // namespace
+
+int iskv_launch_attend_noalloc(const uint16_t* q, const uint16_t* K, const uint16_t* V, int32_t batch, int32_t n,
+                               int32_t Hq, int32_t Hkv, int32_t dh, float scale, uint16_t* out, hipStream_t s) {
+  if (iskv_attend_ws_bytes(batch, n, Hq, dh) > ATTEND_SCRATCH_BYTES) return ISKV_EWORKSPACE;
+  int dev = 0;
+  ISKV_HIP_CHECK(hipGetDevice(&dev));
+  if (s) {  // the stream must belong to the current device
+    int sdev = -1;
+    ISKV_HIP_CHECK(hipStreamGetDevice(s, &sdev));
+    if (sdev != dev) return ISKV_EINVAL;
+  }
+  float* ws = nullptr;
+  const int rc = scratch_for(dev, &ws);
+  if (rc) return rc;
+  return iskv_launch_attend(q, K, V, batch, n, Hq, Hkv, dh, scale, out, ws, ATTEND_SCRATCH_BYTES, s);
+}
 
 size_t iskv_attend_ws_bytes(int32_t batch, int32_t n, int32_t Hq, int32_t dh) {
   (void)dh;

@@ -417,6 +417,14 @@ int decode_attend(const uint16_t* q, const uint16_t* K, const uint16_t* V, int32
                             (hipStream_t)stream);
 }
 
+int decode_attend_noalloc(const uint16_t* q, const uint16_t* K, const uint16_t* V, int32_t batch, int32_t n,
+                          int32_t Hq, int32_t Hkv, int32_t dh, float scale, uint16_t* out, void* stream) {
+  if (!q || !K || !V || !out) return ISKV_EINVAL;
+  if (batch < 1 || n < 1 || Hq < 1 || Hkv < 1 || dh != 128) return ISKV_EINVAL;
+  if (Hq % Hkv != 0 || Hq / Hkv > 16) return ISKV_EINVAL;
+  return iskv_launch_attend_noalloc(q, K, V, batch, n, Hq, Hkv, dh, scale, out, (hipStream_t)stream);
+}
+
 size_t decode_attend_fv_workspace_bytes(const isvd_handle* hv, int32_t n_exact, int32_t Hq) {
   if (!hv || n_exact < 0 || Hq < 1) return 0;
   return iskv_attend_fv_ws_bytes(hv->cfg.n_cap, n_exact, Hq, hv->cfg.r_max);

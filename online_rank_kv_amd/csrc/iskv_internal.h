@@ -167,6 +167,9 @@ int iskv_launch_attend(const uint16_t* q, const uint16_t* K, const uint16_t* V, 
                        int32_t n, int32_t Hq, int32_t Hkv, int32_t dh, float scale, uint16_t* out,
                        void* ws, size_t ws_bytes, hipStream_t s);
 size_t iskv_attend_ws_bytes(int32_t batch, int32_t n, int32_t Hq, int32_t dh);
+// decode attention with its partials in the library's fixed device scratch
+int iskv_launch_attend_noalloc(const uint16_t* q, const uint16_t* K, const uint16_t* V, int32_t batch, int32_t n,
+                               int32_t Hq, int32_t Hkv, int32_t dh, float scale, uint16_t* out, hipStream_t s);
 size_t iskv_attend_fv_ws_bytes(int32_t n_c, int32_t n_exact, int32_t Hq, int32_t r_max);
 int iskv_launch_attend_fv(const uint16_t* q, const uint16_t* K, const isvd_handle* hv, const float* X_exact,
                           const int32_t* pos_exact, int32_t n_exact, int32_t n_total, int32_t Hq, int32_t Hkv,
