@@ -161,6 +161,8 @@ __global__ __launch_bounds__(256) void recon_kernel(const TC* __restrict__ C, in
 // dispatched to the same XCD and share its L2 copy of the C rows.
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 constexpr int RM_BM = 64, RM_BN = 128, RM_KC = 64;
 constexpr int RM_RS = RM_KC + 8;    // LDS row stride (bf16) of the staged operands
 constexpr int RM_OS = RM_BN + 8;    // LDS row stride (bf16) of the output tile
@@ -311,31 +313,44 @@ __global__ __launch_bounds__(256) void recon_mfma_kernel(const TC* __restrict__ 
 // multiple of 32, at most 256): each workgroup keeps one 128-feature tile of
 // B^T in registers for the whole launch (wave w holds the MFMA B operands of
 // its two 16-feature blocks, the "lo" block and the one half a head further,
-// for every k step) and streams 32-row blocks of C through LDS: the next
-// block's loads are in flight while the current block is multiplied, rotated
-// (RoPE in registers, as above) and written through an LDS tile with 16-byte
-// stores. Workgroup w serves feature tile (w / 8) % T and row blocks
+// for every k step) and streams 32-row blocks of C through LDS: the loads of
+// the block two ahead are in flight while the current block is multiplied.
+// The product is taken transposed, out^T = B C^T (B as the MFMA's left
+// operand), so that lane l holds four consecutive features of token l % 16
+// for both members of each rotary pair: it rotates them in registers and
+// stores 8 bytes per member straight into the token's row (neighbouring
+// lanes and waves fill the rest of the row's 256 bytes). One barrier per
+// block: the two staging buffers alternate. Workgroup w serves feature tile (w / 8) % T and row blocks
 // rs, rs + S, ... with rs = w % 8 + 8 (w / 8T): the T tiles of a row block run
 // on the same XCD and share its L2 copy of the C rows.
-constexpr int RS_BM = 32;            // rows per block
+// Memory operations are issued so that the hardware's in-order counter can
+// wait for exactly the block in use: every block issues the same eight C
+// loads (a block past the end reads through an empty buffer descriptor:
+// zeros, no memory traffic) and the same two stores (rows without a valid
+// position are sent past the end of the output descriptor, which drops
+// them), and the row positions of 16 blocks at a time are staged in LDS
+// beforehand, so no per-block load waits behind the prefetches and stores.
+constexpr int RS_BM32 = 32;          // rows per block of the 4-wave form
 constexpr int RS_CS = 256 + 8;       // LDS row stride (bf16) of a staged C block
-constexpr int RS_OS = 128 + 8;       // LDS row stride (bf16) of the output block
+constexpr int RS_PCH = 16;           // blocks whose positions are staged at once
 
-template <typename TC>
-__global__ __launch_bounds__(256) void recon_stream_kernel(const TC* __restrict__ C, int ldc,
+template <typename TC, int NW, int RS_BM>  // NW waves: a tile of 32 NW features; RS_BM rows per block
+__global__ __launch_bounds__(64 * NW, 2) void recon_stream_kernel(const TC* __restrict__ C, int ldc,
                                                            const uint16_t* __restrict__ Bbf, int ldb,
                                                            const int32_t* __restrict__ pos,
                                                            const int32_t* __restrict__ st, int n, int D,
                                                            int dh, int apply_rope, double log_theta,
                                                            uint16_t* out, int n_total, int T, int S) {
+  constexpr int NT = 64 * NW;          // threads
+  constexpr int PER = RS_BM * 64 / NT; // float4 (or 4-coordinate) loads per thread per block
   const int kdev = st[ST_K];
   const int wg = blockIdx.x;
   const int ct = (wg / 8) % T, rs = wg % 8 + 8 * (wg / (8 * T));
-  const int c0 = ct * 128;
+  const int c0 = ct * 32 * NW;
   const int nblk = (n + RS_BM - 1) / RS_BM;
   if (rs >= nblk) return;
   __shared__ __attribute__((aligned(16))) uint16_t Cs[2][RS_BM * RS_CS];
-  __shared__ __attribute__((aligned(16))) uint16_t Os[RS_BM * RS_OS];
+  __shared__ int posC[RS_PCH * RS_BM];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int half = dh >> 1;
   const int ks = (kdev + 31) / 32;
@@ -343,14 +358,14 @@ __global__ __launch_bounds__(256) void recon_stream_kernel(const TC* __restrict_
   int lob = 0;
   {
     int cnt = 0;
-    for (int b = 0; b < 8; ++b)
+    for (int b = 0; b < 2 * NW; ++b)
       if ((b * 16) % dh < half) {
         if (cnt == wave) lob = b;
         ++cnt;
       }
   }
   const int blk0 = lob, blk1 = lob + half / 16;
-  // B operands: lane holds B(feature 16 blk + l%16, k 32 s + 8 (l/16) .. +7)
+  // left MFMA operands: lane holds B(feature 16 blk + l%16, k 32 s + 8 (l/16) .. +7)
   uint4 breg[2][8];
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
@@ -369,43 +384,48 @@ __global__ __launch_bounds__(256) void recon_stream_kernel(const TC* __restrict_
       breg[cb][sk] = v;
     }
   }
-  const int flo = 16 * blk0 + (lane & 15);  // tile-local feature of the lo member
-  const uint64_t rope_F =
-      rope_fraction(exp(-(2.0 * (flo % dh) / dh) * log_theta) * 0.15915494309189533577);
-  // C block staging: element u of this thread is row (t + 256 u) / 64,
-  // columns 4 ((t + 256 u) % 64) .. +3; thread t < 32 also carries row t's
-  // position. Loads run two blocks ahead (a ring of two register sets).
-  __shared__ int posS[2][RS_BM];
+  // tile-local features of this lane's lo members: 16 blk0 + 4 (l / 16) + e
+  const int flo = 16 * blk0 + 4 * (lane >> 4);
+  uint64_t rope_F[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    rope_F[e] = rope_fraction(exp(-(2.0 * ((flo + e) % dh) / dh) * log_theta) * 0.15915494309189533577);
+  // C block staging: element u of this thread is row (t + NT u) / 64,
+  // columns 4 ((t + NT u) % 64) .. +3. Loads run two blocks ahead (a ring
+  // of two register sets).
   constexpr int ES = (int)sizeof(TC);  // bytes per stored coordinate
   // fp32 rows are held as float4, 2-byte rows as their raw bf16 bits
   using CR = std::conditional_t<ES == 4, float4, uint2>;
-  CR creg[2][8];
-  int preg[2];
+  CR creg[2][PER];
   // C rows through a buffer descriptor based at the block's first row and
-  // bounded by the last row n - 1: rows past n read as zero, and the per-load
-  // offsets are fixed (row t / 64 + 4 u, column 4 (t % 64)), so no address
-  // arithmetic runs per block.
+  // bounded by the last row n - 1 (rows past n read as zero; a block past the
+  // end gets an empty descriptor); per-load offsets are fixed (row t / 64 +
+  // NW u, column 4 (t % 64)), so no address arithmetic runs per block.
   const uint32_t voff0 = (uint32_t)(((t >> 6) * ldc + (t & 63) * 4) * ES);
-  const uint32_t vstep = (uint32_t)(4 * ldc * ES);
+  const uint32_t vstep = (uint32_t)(NW * ldc * ES);
   auto load_c = [&](int slot, int blk) {
-    const int i0 = blk * RS_BM;
+    const bool live = blk < nblk;
+    const int i0 = (live ? blk : 0) * RS_BM;
     const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(C + (size_t)i0 * ldc), (short)0, (int)((n - i0) * ldc * ES), 0x00020000);
+        (void*)(C + (size_t)i0 * ldc), (short)0, live ? (int)((n - i0) * ldc * ES) : 0, 0x00020000);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < PER; ++u) {
       if constexpr (ES == 4)
         creg[slot][u] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rc, voff0 + u * vstep, 0, 0));
       else
         creg[slot][u] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rc, voff0 + u * vstep, 0, 0));
     }
-    preg[slot] = pos[min(i0 + (t & 31), n - 1)];
   };
-  auto store_c = [&](int slot, uint16_t* cs, int* ps, int blk) {
+  // output through one descriptor over the whole cache (n_total x D bf16);
+  // an invalid row's offset lies past its end
+  const __amdgpu_buffer_rsrc_t ro =
+      __builtin_amdgcn_make_buffer_rsrc((void*)out, (short)0, (int)((size_t)n_total * D * 2), 0x00020000);
+  auto store_c = [&](int slot, uint16_t* cs, int blk) {
     const int i0 = blk * RS_BM;
     if (i0 + RS_BM <= n && kdev >= ldc) {  // full block: nothing to mask
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = t + 256 * u, r = e >> 6, c4 = (e & 63) * 4;
+      for (int u = 0; u < PER; ++u) {
+        const int e = t + NT * u, r = e >> 6, c4 = (e & 63) * 4;
         if constexpr (ES == 4) {
           const float4 v = creg[slot][u];
           *(uint2*)(cs + r * RS_CS + c4) = uint2{pk_bf16(v.x, v.y), pk_bf16(v.z, v.w)};
@@ -415,8 +435,8 @@ __global__ __launch_bounds__(256) void recon_stream_kernel(const TC* __restrict_
       }
     } else {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = t + 256 * u, r = e >> 6, c4 = (e & 63) * 4;
+      for (int u = 0; u < PER; ++u) {
+        const int e = t + NT * u, r = e >> 6, c4 = (e & 63) * 4;
         const bool rv = i0 + r < n;
         if constexpr (ES == 4) {
           const float4 v = creg[slot][u];
@@ -431,30 +451,31 @@ __global__ __launch_bounds__(256) void recon_stream_kernel(const TC* __restrict_
         }
       }
     }
-    if (t < RS_BM) ps[t] = (i0 + t < n) ? preg[slot] : -1;
   };
   // one block through the pipeline; `slot` is a compile-time constant at each
-  // call, so the register ring is never indexed at run time
-  auto process = [&](auto slot_c, int blk) {
+  // call, so the register ring is never indexed at run time. jl: the block's
+  // index in the staged position chunk.
+  auto process = [&](auto slot_c, int blk, int jl) {
     constexpr int slot = decltype(slot_c)::value;
     uint16_t* cs = Cs[slot];
-    int* ps = posS[slot];
-    store_c(slot, cs, ps, blk);
+    const int* ps = posC + jl * RS_BM;
+    store_c(slot, cs, blk);
     __syncthreads();
-    if (blk + 2 * S < nblk) load_c(slot, blk + 2 * S);
-    v4f acc[2][2];
+    load_c(slot, blk + 2 * S);
+    constexpr int RT = RS_BM / 16;  // 16-token tiles per block
+    v4f acc[RT][2];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < RT; ++a)
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) acc[a][cb] = v4f{0.f, 0.f, 0.f, 0.f};
     auto kstep = [&](int sk) {
       const int ko = 32 * sk + 8 * (lane >> 4);
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
+      for (int a = 0; a < RT; ++a) {
         const v8bf av = __builtin_bit_cast(v8bf, *(const uint4*)(cs + (16 * a + (lane & 15)) * RS_CS + ko));
-        acc[a][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(v8bf, breg[0][sk]),
+        acc[a][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, breg[0][sk]), av,
                                                             acc[a][0], 0, 0, 0);
-        acc[a][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(v8bf, breg[1][sk]),
+        acc[a][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, breg[1][sk]), av,
                                                             acc[a][1], 0, 0, 0);
       }
     };
@@ -466,38 +487,53 @@ __global__ __launch_bounds__(256) void recon_stream_kernel(const TC* __restrict_
       for (int sk = 0; sk < 8; ++sk)
         if (sk < ks) kstep(sk);
     }
-    // epilogue: lane l, element e holds row 4(l/16) + e of each 16-row half a
+    // epilogue: lane l, element e of acc[a][cb] holds feature 4 (l/16) + e of
+    // block cb for token 16 a + l % 16
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
+    for (int a = 0; a < RT; ++a) {
+      const int p = ps[16 * a + (lane & 15)];
+      float x[4], y[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int rl = 16 * a + 4 * (lane >> 4) + e;
-        float x = acc[a][0][e], y = acc[a][1][e];
+        x[e] = acc[a][0][e];
+        y[e] = acc[a][1][e];
         if (apply_rope) {
-          const float rr = rope_rev((uint32_t)ps[rl], rope_F);
+          const float rr = rope_rev((uint32_t)p, rope_F[e]);
           const float c = __builtin_amdgcn_cosf(rr), sn = __builtin_amdgcn_sinf(rr);
-          const float xr = x * c - y * sn, yr = y * c + x * sn;
-          x = xr; y = yr;
+          const float xr = x[e] * c - y[e] * sn, yr = y[e] * c + x[e] * sn;
+          x[e] = xr; y[e] = yr;
         }
-        const uint32_t xy = pk_bf16(x, y);
-        Os[rl * RS_OS + flo] = (uint16_t)xy;
-        Os[rl * RS_OS + flo + half] = (uint16_t)(xy >> 16);
       }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int e = t + 256 * u, r = e >> 4, cc = (e & 15) * 8;
-      const int p = ps[r];
-      if (p >= 0 && p < n_total)  // rows past n and positions outside the output: dropped
-        *(uint4*)(out + (size_t)p * D + c0 + cc) = *(const uint4*)(Os + r * RS_OS + cc);
+      // rows past n (position -1) and positions outside the output: dropped
+      const uint32_t off = (p >= 0 && p < n_total) ? (uint32_t)(((size_t)p * D + c0 + flo) * 2) : 0x80000000u;
+      const uint32_t offh = (p >= 0 && p < n_total) ? off + (uint32_t)(half * 2) : 0x80000000u;
+      __builtin_amdgcn_raw_buffer_store_b64(v2u{pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3])}, ro, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(v2u{pk_bf16(y[0], y[1]), pk_bf16(y[2], y[3])}, ro, offh, 0, 0);
     }
   };
+  // positions of this workgroup's blocks j0 .. j0 + RS_PCH - 1 (past n: -1)
+  auto stage_pos = [&](int j0) {
+    __syncthreads();  // the previous chunk's last stores have read it
+    for (int e = t; e < RS_PCH * RS_BM; e += NT) {
+      const int i = (rs + (j0 + e / RS_BM) * S) * RS_BM + e % RS_BM;
+      posC[e] = i < n ? pos[min(i, n - 1)] : -1;
+    }
+    __syncthreads();
+  };
+  // this workgroup's blocks in chunks of RS_PCH, each chunk as pairs of
+  // blocks with straight-line bodies (an odd last block runs empty: zeros in,
+  // nothing stored)
+  const int nbw = (nblk - rs + S - 1) / S;
   load_c(0, rs);
-  if (rs + S < nblk) load_c(1, rs + S);
-  for (int blk = rs; blk < nblk; blk += 2 * S) {
-    process(std::integral_constant<int, 0>{}, blk);
-    if (blk + S < nblk) process(std::integral_constant<int, 1>{}, blk + S);
+  load_c(1, rs + S);
+  for (int j0 = 0; j0 < nbw; j0 += RS_PCH) {
+    stage_pos(j0);
+    const int npair = (min(RS_PCH, nbw - j0) + 1) / 2;
+    for (int jp = 0; jp < npair; ++jp) {
+      const int b0 = rs + (j0 + 2 * jp) * S;
+      process(std::integral_constant<int, 0>{}, b0, 2 * jp);
+      process(std::integral_constant<int, 1>{}, b0 + S, 2 * jp + 1);
+    }
   }
 }
 
@@ -570,16 +606,25 @@ int iskv_launch_reconstruct(const isvd_handle* h, const float* X_exact, const in
     dim3 grid(D / W, (n + 31) / 32);
     const bool mfma = bf && D % RM_BN == 0 && head_dim % 32 == 0 && RM_BN % head_dim == 0 &&
                       R % 8 == 0;
-    // (the streaming kernel's buffer descriptors bound C in 32-bit bytes)
+    // (the streaming kernel's buffer descriptors bound C and the output in
+    // 32-bit bytes)
     auto go = [&](auto* Cp) {
       using TC = std::remove_pointer_t<decltype(Cp)>;
       const TC* Cc = Cp;
-      if (mfma && R % 32 == 0 && R <= 256 && (size_t)n * R * sizeof(TC) < ((size_t)1 << 31)) {
-        const int T = D / 128;
-        const int G = T >= 64 ? 1 : 64 / T;  // 512 workgroups when T divides 64
-        hipLaunchKernelGGL((recon_stream_kernel<TC>), dim3(8 * T * G), dim3(256), 0, s, Cc, R, h->w.Bbf, R,
-                           h->pos, h->w.st, n, D, head_dim, apply_rope, lt, (uint16_t*)out, n_total, T,
-                           8 * G);
+      if (mfma && R % 32 == 0 && R <= 256 && (size_t)n * R * sizeof(TC) < ((size_t)1 << 31) &&
+          (size_t)n_total * D * 2 < ((size_t)1 << 31)) {
+        if (D % 256 == 0 && 256 % head_dim == 0) {
+          // 256-feature tiles (8 waves), one workgroup per CU
+          const int T = D / 256;
+          const int G = T >= 32 ? 1 : 32 / T;  // 256 workgroups when T divides 32
+          hipLaunchKernelGGL((recon_stream_kernel<TC, 8, RS_BM32>), dim3(8 * T * G), dim3(512), 0, s, Cc, R, h->w.Bbf, R,
+                             h->pos, h->w.st, n, D, head_dim, apply_rope, lt, (uint16_t*)out, n_total, T, 8 * G);
+        } else {
+          const int T = D / 128;
+          const int G = T >= 64 ? 1 : 64 / T;  // 512 workgroups when T divides 64
+          hipLaunchKernelGGL((recon_stream_kernel<TC, 4, RS_BM32>), dim3(8 * T * G), dim3(256), 0, s, Cc, R, h->w.Bbf, R,
+                             h->pos, h->w.st, n, D, head_dim, apply_rope, lt, (uint16_t*)out, n_total, T, 8 * G);
+        }
       } else if (mfma) {
         const int tiles = D / RM_BN, nrb = (n + RM_BM - 1) / RM_BM;
         const int nwg = (nrb + 7) / 8 * 8 * tiles;
