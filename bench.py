@@ -539,6 +539,8 @@ def main():
     cu_bytes = cu_paths * 2.0 * n_cu * R * 4
     cu_gbps = cu_bytes / (stage_k["coord_update"] * 1e-3) / 1e9
     cu_tflops = cu_paths * 2.0 * n_cu * R * R / (stage_k["coord_update"] * 1e-3) / 1e12
+    # the split-bf16 product runs three bf16 matrix-core products per output
+    cu_bf16_frac = 3.0 * cu_tflops / BF16_PEAK_TFLOPS
 
     # merge modes on the K path, last because they change its factors: the
     # full merge (with its re-orthogonalisation every 256 rows), the
@@ -620,9 +622,10 @@ def main():
                                 "rewrite; frozen basis stores F B only"},
         "coord_update": {"bound": "hbm", "achieved": cu_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": cu_gbps / HBM_PEAK_GBPS, "algorithmic_bytes": cu_bytes, "rows": n_cu,
-                         "traffic": profiled_traffic("xh_reg_kernel_coord_update_kv_n16k_traffic.md"),
-                         "fp32_tflops": cu_tflops, "fp32_frac": cu_tflops / FP32_PEAK_TFLOPS,
-                         "kernel": "xh_reg_kernel (old rows C <- C H[:k], fp32 MFMA)",
+                         "traffic": profiled_traffic("xh_bf3_kernel_coord_update_kv_n16k_traffic.md"),
+                         "effective_tflops": cu_tflops, "bf16_mfma_frac": cu_bf16_frac,
+                         "kernel": "xh_bf3_kernel (old rows C <- C H[:k], split-bf16 MFMA: 3 bf16 products, "
+                                   "fp32 accumulation)",
                          "paths_per_launch": cu_paths, "merges_timed": TIMED_MERGES},
         "setup_s": {"generate": gen_s, "fill_16k_rows": fill_s},
         "core_solver_last_merge": [{"flags": c[11], "steps": c[12], "resid_sweeps": c[14], "k": c[1], "n": c[0]}

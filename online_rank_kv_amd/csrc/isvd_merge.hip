@@ -49,6 +49,14 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Two fp32 values to packed bf16 (round to nearest even), one v_cvt_pk_bf16_f32.
+typedef float f2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{a, b}, bf2_t));
+}
+
 // ----------------------------------------------------------------------------
 // Residual Gram E E^T in fp64 (b x b): workgroup (i, jb) forms row i against
 // rows 8 jb .. 8 jb + 7, each thread over 4 consecutive features (D % 4 == 0),
@@ -822,6 +830,155 @@ __global__ __launch_bounds__(1024) void xh_reg_kernel(const TX* X1, int ld1, con
   }
 }
 
+// The coordinate update C <- C H over all n rows (C n x kin, in place; H
+// kin x kout, kin, kout <= 256) on the bf16 matrix cores with split operands:
+// x = x_h + x_l and h = h_h + h_l, each part a bf16 (x_h = bf16(x),
+// x_l = bf16(x - x_h)), and
+//   x . h ~ x_h . h_h + x_h . h_l + x_l . h_h
+// in fp32 accumulation (v_mfma_f32_16x16x32_bf16). The dropped x_l . h_l and
+// the parts' own rounding leave about 2^-16 of |x| |h| per product, against
+// 2^-24 for fp32 products; three bf16 products cost a fifth of the fp32
+// matrix-core time at r = 256, which puts the update under its HBM time.
+// A 1024-thread workgroup: wave w owns output columns 16 w .. 16 w + 15 and
+// keeps their split H as the B operands (lane l: column l % 16, k 32 s +
+// 8 (l / 16) .. +7, for s < 8), read as prepared by split_h_kernel (once per
+// merge, in operand order: every lane loads 16 contiguous 16-byte pieces
+// instead of gathering 64 strided values). Rows go in 16-row
+// blocks (block, block + grid, ...), loaded a chunk of blocks at a time,
+// each split into two bf16 images in LDS (two staging buffers alternate, one
+// barrier per block) and multiplied; a block's rows are all read before any
+// of its outputs is written, so the update is in place.
+// 2-byte stored coordinates (TX = uint16_t) are exact in bf16: x_l = 0 and
+// the x_l . h_h product is skipped.
+constexpr int XB_LD = 256 + 8;  // LDS row stride (bf16) of a staged block image
+constexpr int XB_CH = 8;        // blocks whose rows are loaded together
+
+// Split fragments of H for xh_bf3_kernel: fragment (w, s) of lane l holds
+// the 8 bf16 of column 16 w + l % 16, rows 32 s + 8 (l / 16) .. +7 (zero past
+// kin and kout), hi parts at Hs[(w NS + s) 64 + l], lo parts NW NS 64 uint4
+// further (NW = r_max / 16 column blocks, NS = r_max / 32 depth steps).
+__global__ __launch_bounds__(256) void split_h_kernel(const float* __restrict__ H, int ldh, Dim kin_d, Dim kout_d,
+                                                      int NW, int NS, uint4* Hs, const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  H = iskv_rb(H, bdel);
+  Hs = iskv_rb(Hs, bdel);
+  iskv_rb_dim(kin_d, bdel);
+  iskv_rb_dim(kout_d, bdel);
+  const int kin = dval(kin_d), kout = dval(kout_d);
+  const int g = blockIdx.x * 256 + threadIdx.x;
+  if (g >= NW * NS * 64) return;
+  const int lane = g & 63, sk = (g >> 6) % NS, w = (g >> 6) / NS;
+  const int col = 16 * w + (lane & 15);
+  float hv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int k = 32 * sk + 8 * (lane >> 4) + j;
+    hv[j] = (k < kin && col < kout) ? H[(size_t)k * ldh + col] : 0.f;
+  }
+  uint32_t ph[4], pl[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    ph[j] = pk_bf16(hv[2 * j], hv[2 * j + 1]);
+    const float h0 = __uint_as_float(ph[j] << 16), h1 = __uint_as_float(ph[j] & 0xffff0000u);
+    pl[j] = pk_bf16(hv[2 * j] - h0, hv[2 * j + 1] - h1);
+  }
+  Hs[g] = uint4{ph[0], ph[1], ph[2], ph[3]};
+  Hs[NW * NS * 64 + g] = uint4{pl[0], pl[1], pl[2], pl[3]};
+}
+
+template <typename TX>
+__global__ __launch_bounds__(1024) void xh_bf3_kernel(TX* X, int ldx, Dim kin_d, const uint4* __restrict__ Hs, int NW,
+                                                      int NS, Dim kout_d, Dim rows_d, const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  X = iskv_rb(X, bdel);
+  Hs = iskv_rb(Hs, bdel);
+  iskv_rb_dim(kin_d, bdel);
+  iskv_rb_dim(kout_d, bdel);
+  iskv_rb_dim(rows_d, bdel);
+  constexpr bool SPLIT_X = std::is_same<TX, float>::value;
+  const int kin = dval(kin_d), kout = dval(kout_d), rows = dval(rows_d);
+  const int nblk = (rows + 15) / 16;
+  if ((int)blockIdx.x >= nblk || kout <= 0 || kin <= 0) return;
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[2][2][16 * XB_LD];  // [buffer][hi, lo]
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int col = wave * 16 + (lane & 15);
+  // split H operands: hh[s], hl[s] = 8 bf16 of column col, k 32 s + 8 (l / 16) ..
+  // (depth steps past NS and waves past NW are zero; those waves only stage rows)
+  v8bf hh[8], hl[8];
+#pragma unroll
+  for (int sk = 0; sk < 8; ++sk) {
+    const bool in = sk < NS && wave < NW;
+    const uint4 a = in ? Hs[(wave * NS + sk) * 64 + lane] : uint4{0u, 0u, 0u, 0u};
+    const uint4 b = in ? Hs[(NW * NS + wave * NS + sk) * 64 + lane] : uint4{0u, 0u, 0u, 0u};
+    hh[sk] = __builtin_bit_cast(v8bf, a);
+    hl[sk] = __builtin_bit_cast(v8bf, b);
+  }
+  // block staging: thread t holds row t / 64, columns 4 (t % 64) .. +3 of
+  // each 16-row block (rows past `rows` and columns past kin read as zero).
+  // A workgroup's blocks go in chunks of XB_CH: the rows of the whole chunk
+  // are loaded first, so the memory latency is paid once per chunk.
+  const int sr = t >> 6, sc = (t & 63) * 4;
+  float4 xr[XB_CH];
+  auto load_x = [&](int u, int blk) {
+    const int row = min(blk * 16 + sr, rows - 1);
+    if constexpr (SPLIT_X) {
+      xr[u] = *(const float4*)(X + (size_t)row * ldx + sc);
+    } else {
+      const uint2 v = *(const uint2*)(X + (size_t)row * ldx + sc);
+      xr[u] = float4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y << 16),
+                     __uint_as_float(v.y & 0xffff0000u)};
+    }
+  };
+  int buf = 0;
+  for (int c0 = blockIdx.x; c0 < nblk; c0 += XB_CH * gridDim.x) {
+#pragma unroll
+  for (int u = 0; u < XB_CH; ++u)
+    if (c0 + u * (int)gridDim.x < nblk) load_x(u, c0 + u * gridDim.x);
+#pragma unroll
+  for (int u = 0; u < XB_CH; ++u) {
+    const int blk = c0 + u * gridDim.x;
+    if (blk >= nblk) break;
+    const int i0 = blk * 16;
+    {
+      const bool rv = i0 + sr < rows;
+      const float4 xv = xr[u];
+      const float x0 = (rv && sc < kin) ? xv.x : 0.f, x1 = (rv && sc + 1 < kin) ? xv.y : 0.f;
+      const float x2 = (rv && sc + 2 < kin) ? xv.z : 0.f, x3 = (rv && sc + 3 < kin) ? xv.w : 0.f;
+      const uint32_t h01 = pk_bf16(x0, x1), h23 = pk_bf16(x2, x3);
+      *(uint2*)(&Xs[buf][0][sr * XB_LD + sc]) = uint2{h01, h23};
+      if constexpr (SPLIT_X) {
+        const uint32_t l01 = pk_bf16(x0 - __uint_as_float(h01 << 16), x1 - __uint_as_float(h01 & 0xffff0000u));
+        const uint32_t l23 = pk_bf16(x2 - __uint_as_float(h23 << 16), x3 - __uint_as_float(h23 & 0xffff0000u));
+        *(uint2*)(&Xs[buf][1][sr * XB_LD + sc]) = uint2{l01, l23};
+      }
+    }
+    __syncthreads();
+    v4f_t acc = {0.f, 0.f, 0.f, 0.f};
+    const uint16_t* xh = &Xs[buf][0][(lane & 15) * XB_LD + 8 * (lane >> 4)];
+    const uint16_t* xl = &Xs[buf][1][(lane & 15) * XB_LD + 8 * (lane >> 4)];
+#pragma unroll
+    for (int sk = 0; sk < 8; ++sk) {
+      const v8bf ah = __builtin_bit_cast(v8bf, *(const uint4*)(xh + 32 * sk));
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, hh[sk], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, hl[sk], acc, 0, 0, 0);
+      if constexpr (SPLIT_X) {
+        const v8bf al = __builtin_bit_cast(v8bf, *(const uint4*)(xl + 32 * sk));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, hh[sk], acc, 0, 0, 0);
+      }
+    }
+    // result lane l, element e: row 4 (l / 16) + e, column l % 16 of the wave's block
+    if (col < kout) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = i0 + 4 * (lane >> 4) + e;
+        if (row < rows) iskv_st(X + (size_t)row * ldx + col, acc[e]);
+      }
+    }
+    buf ^= 1;
+  }
+  }
+}
+
 // Launch Y = [X1 | X2] H over `rows_host` rows (an upper bound when rows_d is
 // a device value); kin_max bounds kin for the LDS layout.
 template <typename TX, typename TY>
@@ -1257,15 +1414,30 @@ static int merge_body(isvd_handle* h, const float* F, const int32_t* pos_F, int3
     if (rc) return rc;
   }
   eig_finish(h, 1);
+  const bool bf3 = c.r_max <= 256 && c.r_max % 32 == 0;  // split-bf16 coordinate update
+  const int NW3 = c.r_max / 16, NS3 = c.r_max / 32;
+  if (bf3 && !(c.flags & ISKV_NO_COORD_SYNC))
+    // H split once into the update's operand fragments (in T2, free during a
+    // merge: R / 16 x R / 32 x 64 x 2 uint4 = R^2 floats)
+    hipLaunchKernelGGL(split_h_kernel, bz(dim3((NW3 * NS3 * 64 + 255) / 256), h->bcount), dim3(256), 0, s, w.Hc,
+                       c.r_max, ddim(dk), ddim(w.st + ST_KNEW), NW3, NS3, (uint4*)w.T2, h->bd);
   mark(3);
   // 8. coordinate sync of old rows (n of them, read on the device), new rows
   // appended at row n, basis update
   const int M = h->m_max;
   const Dim dn = ddim(w.st + ST_N);
   with_coords(h, [&](auto* Cp) {
-    if (!(c.flags & ISKV_NO_COORD_SYNC))
-      xh_launch(s, h->bd, h->bcount, c.n_cap, Cp, R, nullptr, 0, ddim(dk), ddim(dk), R, w.Hc, R, R,
-                ddim(w.st + ST_KNEW), dn, Cp, R, nullptr, 0);
+    using TC = std::remove_pointer_t<decltype(Cp)>;
+    if (!(c.flags & ISKV_NO_COORD_SYNC)) {
+      if (bf3) {  // split-bf16 matrix cores, one 1024-thread workgroup per CU at most
+        const int nblk = (c.n_cap + 15) / 16;
+        hipLaunchKernelGGL((xh_bf3_kernel<TC>), bz(dim3(nblk < 256 ? nblk : 256), h->bcount), dim3(1024), 0, s, Cp,
+                           R, ddim(dk), (const uint4*)w.T2, NW3, NS3, ddim(w.st + ST_KNEW), dn, h->bd);
+      } else {
+        xh_launch(s, h->bd, h->bcount, c.n_cap, Cp, R, nullptr, 0, ddim(dk), ddim(dk), R, w.Hc, R, R,
+                  ddim(w.st + ST_KNEW), dn, Cp, R, nullptr, 0);
+      }
+    }
     mark(4);
     xh_launch(s, h->bd, h->bcount, b, w.Q, R, w.FP, c.b_max, ddim(dk), ddim(w.st + ST_M), M, w.Hc, R, R,
               ddim(w.st + ST_KNEW), hdim(b), Cp, R, nullptr, 0, h->pos, pos_F, false, dn);
