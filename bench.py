@@ -53,10 +53,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--batch-paths", type=int, default=64,
-                    help="paths of the many-path leg (0 skips it)")
-    ap.add_argument("--batch-rows", type=int, default=N0, help="rows per path before the many-path leg's timing")
-    ap.add_argument("--batch-steps", type=int, default=16, help="timed batched merges of the many-path leg")
+    ap.add_argument("--batch-paths", type=int, default=1024,
+                    help="paths of the batch leg (16 sequences x 32 layers x K/V; 0 skips it)")
+    ap.add_argument("--batch-rows", type=int, default=32768, help="rows per path before the batch leg's timing")
+    ap.add_argument("--batch-steps", type=int, default=16, help="timed batched merges of the batch leg")
     ap.add_argument("--batched-kv", action="store_true",
                     help="K and V carved from one allocation, merged as one batched launch sequence")
     ap.add_argument("--no-graphs", action="store_true",
@@ -135,39 +135,149 @@ def prefill_leg(args, K, torch, dev):
     return res
 
 
-def high_rank_leg(args, K, torch, dev):
-    """Merges at the prompt + decode stream's rank: one K-spectrum path at
-    D = 1024, r = 512, b = 64, started by a refit of 4,096 rows, then 16
-    merges timed with HIP events on its stream (recorded sequences). The core
-    (576) is above the size where the parallel refinement converges on this
-    spectrum's flat floor, so most merges finish in the block Jacobi."""
+def prompt_decode_leg(args, K, torch, dev):
+    """The 64K-row prompt + decode stream at its full size: D = 1024, r = 512,
+    b = 64, key spectrum, rows drawn on the device. The factor of its first
+    65,536 - 18 x 64 rows comes from the fresh truncated SVD (isvd_refit:
+    the prompt's factor step of Algorithm 1, here over every row), then 16
+    merges are timed at n ~ 64K (re-orthogonalisation every 256 rows,
+    recorded sequences, HIP events on the path's stream). The workload
+    reconstructs all rows every 64 decode steps: that reconstruction (bf16 +
+    RoPE, all n rows) is timed 10 times, with its bytes, MFMA fraction and
+    cost per decode step (one 64th)."""
     import synth
-    r, b, n0, merges = 512, 64, 4096, 16
-    X = torch.from_numpy(synth.kv_stream(synth.StreamSpec(D, n0 + (merges + 2) * b, "exp40+0.01", 0.0, 77))).to(dev)
-    pos = torch.arange(X.shape[0], dtype=torch.int32, device=dev)
+    r, b, N, merges = 512, 64, 65536, 16
+    n0 = N - (merges + 2) * b
     st = torch.cuda.Stream()
-    torch.cuda.synchronize()
-    p = K.IsvdPath(D=D, r_max=r, b_max=b, n_cap=X.shape[0], reorth_every_rows=256, device=dev, stream=st,
+    with torch.cuda.stream(st):
+        X = synth.DeviceStreams(1, 1, D, 64, dev).rows(N)[0].contiguous()
+        pos = torch.arange(N, dtype=torch.int32, device=dev)
+    st.synchronize()
+    p = K.IsvdPath(D=D, r_max=r, b_max=b, n_cap=N, reorth_every_rows=256, device=dev, stream=st,
                    graphs=not args.no_graphs)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(st)
     p.refit(X[:n0], pos[:n0])
+    ev[1].record(st)
+    st.synchronize()
+    refit_ms = ev[0].elapsed_time(ev[1])
     for j in range(2):  # warm-up (records the sequences)
         s0 = n0 + j * b
         p.merge(X[s0:s0 + b], pos[s0:s0 + b])
     st.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev[0].record(st)
     for j in range(2, merges + 2):
         s0 = n0 + j * b
         p.merge(X[s0:s0 + b], pos[s0:s0 + b])
     ev[1].record(st)
     st.synchronize()
-    ms = ev[0].elapsed_time(ev[1]) / merges
+    merge_ms = ev[0].elapsed_time(ev[1]) / merges
     n, k, status = p.query()
     state = p.state()
+    out = torch.empty((N, D), dtype=torch.bfloat16, device=dev)
+    for _ in range(2):
+        p.reconstruct(out, N, head_dim=DH, rope=True, theta=THETA, stream=st)
+    ev[0].record(st)
+    reps = 10
+    for _ in range(reps):
+        p.reconstruct(out, N, head_dim=DH, rope=True, theta=THETA, stream=st)
+    ev[1].record(st)
+    st.synchronize()
+    rec_ms = ev[0].elapsed_time(ev[1]) / reps
+    rec_bytes = n * r * 4 + r * D * 2 + n * D * 2
+    rec_flops = 2.0 * n * r * D
     p.close()
-    return {"merge_ms": ms, "r": r, "b": b, "rows_at_start": n0, "merges": merges, "status": status,
+    return {"rows": n, "rank": k, "r": r, "b": b, "status": status, "refit_rows": n0, "refit_ms": refit_ms,
+            "merge_ms": merge_ms, "merges": merges,
             "last_core_solve": {"flags": state[11], "steps": state[12], "sweeps": state[7]},
-            "what": "K-spectrum path at r=512, b=64 (core 576): refinement, then the block-Jacobi fallback"}
+            "reconstruct_ms": rec_ms, "reconstruct_bytes": rec_bytes,
+            "reconstruct_GBps": rec_bytes / (rec_ms * 1e-3) / 1e9,
+            "reconstruct_hbm_frac": rec_bytes / (rec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "reconstruct_mfma_frac": rec_flops / (rec_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "reconstruct_ms_per_step": rec_ms / 64,
+            "what": "64K-row key stream at r=512, b=64 (core 576): factor of the first rows by the fresh "
+                    "truncated SVD, merges timed at n~64K, full reconstruction every 64 steps"}
+
+
+def batch_leg(args, K, torch, dev):
+    """The batch workload: 16 sequences x 32 layers x {K, V} = 1024
+    independent paths of 32,768 rows (D = 1024, r = 256, b = 32), carved from
+    one allocation. A key-spectrum and a value-spectrum path are factored
+    from 32,768 rows each (isvd_refit, the fresh truncated SVD), every path
+    of the batch starts as a copy of the one of its kind (isvd_copy), and
+    from then on each path takes its own rows (synth.DeviceStreams, one draw
+    per path per block). Timed: --batch-steps batched merges, one b-row block
+    per path each (isvd_merge_block_batched, re-orthogonalisation every 256
+    rows), then two more with stage events."""
+    import synth
+    P, n0, steps = args.batch_paths, args.batch_rows, args.batch_steps
+    warm = 2
+    st = torch.cuda.Stream()
+    n_cap = n0 + (steps + warm + 2) * BLK
+    with torch.cuda.stream(st):
+        ds = synth.DeviceStreams(P, P // 2, D, 1000, dev)
+        bat = K.IsvdBatch(P, D=D, r_max=R, b_max=BLK, n_cap=n_cap, reorth_every_rows=256, device=dev, stream=st,
+                          graphs=not args.no_graphs)
+        t0 = time.perf_counter()
+        seeds = []
+        for kind, spec in ((0, "exp40+0.01"), (1, "invsqrt")):
+            Xs = torch.from_numpy(synth.kv_stream(synth.StreamSpec(D, n0, spec, 0.0, 1000 + kind))).to(dev)
+            ps = torch.arange(n0, dtype=torch.int32, device=dev)
+            src = K.IsvdPath(D=D, r_max=R, b_max=BLK, n_cap=n0, reorth_every_rows=256, device=dev, stream=st,
+                             graphs=False)
+            src.refit(Xs, ps, iters=24 if kind == 0 else 40)
+            seeds.append(src)
+        st.synchronize()
+        for z in range(P):
+            bat.paths[z].copy_from(seeds[0 if z < P // 2 else 1])
+        st.synchronize()
+        init_s = time.perf_counter() - t0
+        for sp in seeds:
+            sp.close()
+        cursor = n0
+        pos = torch.empty((P, BLK), dtype=torch.int32, device=dev)
+
+        def one_step():
+            nonlocal cursor
+            rows = ds.rows(BLK).contiguous()
+            pos.copy_(torch.arange(cursor, cursor + BLK, dtype=torch.int32, device=dev).expand(P, BLK))
+            bat.merge(rows, pos)
+            cursor += BLK
+
+        for _ in range(warm):
+            one_step()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st.synchronize()
+        t0 = time.perf_counter()
+        e0.record(st)
+        for _ in range(steps):
+            one_step()
+        e1.record(st)
+        st.synchronize()
+        wall = time.perf_counter() - t0
+        bat.paths[0].set_timing(True)
+        stage = []
+        for _ in range(2):
+            one_step()
+            stage.append(bat.paths[0].stage_times())
+        bat.paths[0].set_timing(False)
+        st.synchronize()
+    ms = e0.elapsed_time(e1)
+    states = [p.state() for p in bat.paths[:: max(1, P // 4)]]
+    n_end = bat.paths[0].n
+    bat.close()
+    stage_ms = {k: float(np.mean([r[k] for r in stage])) for k in stage[0]}
+    cu_bytes = P * 2.0 * (n_end - BLK) * R * 4
+    return {"paths": P, "rows_per_path": n0, "block": BLK, "rank": R, "steps": steps,
+            "merges_per_s": P * steps / wall, "ms_per_batched_merge": ms / steps,
+            "merges_per_s_events": P * steps / (ms * 1e-3), "init_s": init_s,
+            "stage_ms_per_batched_merge": stage_ms,
+            "coord_update_GBps": cu_bytes / (stage_ms["coord_update"] * 1e-3) / 1e9,
+            "core_solver_flags_sampled": [c[11] for c in states], "rows_at_end": n_end,
+            "workload": f"{P} independent paths ({P // 2} K, {P // 2} V spectra: 16 sequences x 32 layers x K/V "
+                        f"when P = 1024), n={n0}, D={D}, r={R}, b={BLK}, reorth every 256 rows; paths start as "
+                        f"copies of a K and a V factor of {n0} rows (fresh truncated SVD) and take their own "
+                        f"rows, drawn on the device"}
 
 
 def coords_leg(args, K, torch, dev, Xk, Kc):
@@ -224,62 +334,6 @@ def coords_leg(args, K, torch, dev, Xk, Kc):
     res["recon_rel_diff"] = float(torch.linalg.norm(rb - ra) / torch.linalg.norm(ra))
     res["factor_v_max_abs_diff"] = float((fb - fa).abs().max())
     return res
-
-
-def many_path_leg(args, K, torch, dev):
-    """Many independent paths merged as one batched launch sequence per step
-    (isvd_merge_block_batched through iskv_window_append_batched): half key
-    paths, half value paths, rows drawn on the device (synth.DeviceStreams),
-    each path first filled to --batch-rows rows, then --batch-steps timed
-    steps of one b-row block per path (one merge per path)."""
-    import synth
-    P, n0, steps = args.batch_paths, args.batch_rows, args.batch_steps
-    warm = 2
-    st = torch.cuda.Stream()
-    n_cap = n0 + WIN + (steps + warm + 4) * BLK
-    with torch.cuda.stream(st):
-        ds = synth.DeviceStreams(P, P // 2, D, 1000, dev)
-        bat = K.IsvdBatch(P, D=D, r_max=R, b_max=BLK, n_cap=n_cap, reorth_every_rows=256, device=dev, stream=st,
-                          graphs=not args.no_graphs, window=WIN, block=BLK)
-        t0 = time.perf_counter()
-        for s in range(0, n0 + WIN, 512):
-            bat.append(ds.rows(min(512, n0 + WIN - s)), s)
-        st.synchronize()
-        fill_s = time.perf_counter() - t0
-        cursor = n0 + WIN
-        blocks = [ds.rows(BLK) for _ in range(steps + warm)]
-        st.synchronize()
-        for i in range(warm):
-            bat.append(blocks[i], cursor)
-            cursor += BLK
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        st.synchronize()
-        t0 = time.perf_counter()
-        e0.record(st)
-        for i in range(warm, warm + steps):
-            bat.append(blocks[i], cursor)
-            cursor += BLK
-        e1.record(st)
-        st.synchronize()
-        wall = time.perf_counter() - t0
-        # stage breakdown of two more batched merges (kernels one by one, events)
-        bat.paths[0].set_timing(True)
-        stage = []
-        for _ in range(2):
-            bat.append(ds.rows(BLK), cursor)
-            cursor += BLK
-            stage.append(bat.paths[0].stage_times())
-        bat.paths[0].set_timing(False)
-    ms = e0.elapsed_time(e1)
-    states = [p.state() for p in bat.paths[:: max(1, P // 4)]]
-    bat.close()
-    return {"paths": P, "rows_per_path": n0, "block": BLK, "rank": R, "steps": steps,
-            "merges_per_s": P * steps / wall, "ms_per_batched_merge": ms / steps,
-            "merges_per_s_events": P * steps / (ms * 1e-3), "fill_s": fill_s,
-            "stage_ms_per_batched_merge": {k: float(np.mean([r[k] for r in stage])) for k in stage[0]},
-            "core_solver_flags_sampled": [c[11] for c in states],
-            "workload": f"{P} independent paths ({P // 2} K, {P // 2} V spectra), n={n0}, D={D}, r={R}, "
-                        f"b={BLK}, w={WIN}, reorth every 256 rows, rows drawn on the device"}
 
 
 def cpu_baseline(Xk, Xv, seconds):
@@ -633,9 +687,9 @@ def main():
     }
     result["coords_2byte"] = coords_leg(args, K, torch, dev, Xk, Kc)
     result["prefill_init"] = prefill_leg(args, K, torch, dev)
-    result["high_rank_merges"] = high_rank_leg(args, K, torch, dev)
+    result["prompt_decode_64k"] = prompt_decode_leg(args, K, torch, dev)
     if args.batch_paths > 0:
-        result["many_paths"] = many_path_leg(args, K, torch, dev)
+        result["batch_1024x32k"] = batch_leg(args, K, torch, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(Xk, Xv, args.cpu_seconds)
     else:

@@ -216,6 +216,20 @@ int isvd_stage_times(isvd_handle* h, float* ms, int32_t count);
 /* Rows folded so far (host-side, no sync). */
 int32_t isvd_rows(const isvd_handle* h);
 
+/* Copy one path's compressed history into another handle: C (rows 0..n-1),
+ * sigma, B and its bf16 copy, the positions and the device state words (n, k,
+ * the folded-row counter), i.e. the factor U diag(sigma) B^T of one
+ * (sequence, layer, K/V) path of iS-KV notes §2.2 with its row positions
+ * (Algorithm 3). The two paths are independent afterwards: this forks a
+ * sequence whose continuations are compressed separately.
+ *   dst, src  handles with the same D, r_max, b_max, coordinate storage and
+ *             merge mode; dst's n_cap >= src's row count.
+ * Enqueued on dst's stream as device-to-device copies; src's pending work on
+ * another stream must be complete (the caller synchronises). dst's own
+ * history is replaced. Errors: EINVAL (mismatched handles, dst == src),
+ * ECAPACITY, EHIP. */
+int isvd_copy(isvd_handle* dst, const isvd_handle* src);
+
 /* Release the host handle (device buffers stay the caller's). NULL is a no-op. */
 void isvd_destroy(isvd_handle* h);
 

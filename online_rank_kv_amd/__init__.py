@@ -23,7 +23,7 @@ __all__ = [
     "prefill_init", "iskv_prompt_protect_workspace_bytes", "iskv_prompt_protect", "prompt_protect",
     "ISKV_OUT_BF16", "isvd_set_mode",
     "ISKV_OUT_FP32", "ISKV_DEV_NONFINITE", "ISKV_DEV_NOCONV", "EXPORTED_SYMBOLS",
-    "isvd_workspace_bytes", "isvd_init", "isvd_merge_block", "isvd_reorth", "isvd_query",
+    "isvd_workspace_bytes", "isvd_init", "isvd_merge_block", "isvd_reorth", "isvd_query", "isvd_copy",
     "isvd_rows", "isvd_destroy", "isvd_query_state", "isvd_sym_eig", "kv_reconstruct", "kv_scatter_exact",
     "decode_attend_workspace_bytes", "decode_attend", "decode_attend_noalloc", "decode_attend_fv_workspace_bytes",
     "decode_attend_fv", "iskv_window_rows", "iskv_window_init", "iskv_window_protect",
@@ -59,7 +59,7 @@ EXPORTED_SYMBOLS = (
     "decode_attend_fv_workspace_bytes", "decode_attend_fv", "isvd_set_mode",
     "iskv_prompt_protect_workspace_bytes", "iskv_prompt_protect", "isvd_refit_workspace_bytes", "isvd_refit",
     "isvd_value_first_refit_workspace_bytes", "isvd_value_first_refit", "iskv_prompt_split_workspace_bytes",
-    "iskv_prompt_split", "decode_attend_noalloc",
+    "iskv_prompt_split", "decode_attend_noalloc", "isvd_copy",
 )
 
 
@@ -93,6 +93,7 @@ lib.isvd_merge_block_batched.argtypes = [ctypes.POINTER(_vp), _i32, _vp, ctypes.
                                          _i32]
 lib.isvd_reorth.restype = ctypes.c_int
 lib.isvd_reorth.argtypes = [_vp]
+lib.isvd_copy.argtypes = [_vp, _vp]
 lib.isvd_set_mode.restype = ctypes.c_int
 lib.isvd_set_mode.argtypes = [_vp, _i32]
 lib.isvd_refit_workspace_bytes.restype = ctypes.c_size_t
@@ -211,6 +212,10 @@ def isvd_merge_block_batched(handles, F, F_stride: int, pos_F, pos_stride: int, 
 
 def isvd_reorth(h: int) -> None:
     _check(lib.isvd_reorth(h), "isvd_reorth")
+
+
+def isvd_copy(dst: int, src: int) -> None:
+    _check(lib.isvd_copy(dst, src), "isvd_copy")
 
 
 def isvd_set_mode(h: int, mode: int) -> None:
@@ -499,6 +504,10 @@ class IsvdPath:
                            device=self.C.device)
         isvd_value_first_refit(self.h, F, pos_F, int(F.shape[0]), iters, work)
         self._refit_work = work  # kept until the stream has used it
+
+    def copy_from(self, other: "IsvdPath") -> None:
+        """Replace this path's history by a copy of other's (isvd_copy)."""
+        isvd_copy(self.h, other.h)
 
     def set_mode(self, mode: int) -> None:
         """0 (full merge), ISKV_NO_COORD_SYNC (basis-only) or ISKV_FROZEN_BASIS."""

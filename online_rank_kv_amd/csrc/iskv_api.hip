@@ -336,6 +336,30 @@ int isvd_query(isvd_handle* h, int32_t* n, int32_t* k, int32_t* status) {
   return ISKV_OK;
 }
 
+int isvd_copy(isvd_handle* dst, const isvd_handle* src) {
+  if (!dst || !src || dst == src) return ISKV_EINVAL;
+  const iskv_config& a = dst->cfg;
+  const iskv_config& b = src->cfg;
+  const int32_t same = ISKV_BF16_COORDS | ISKV_NO_COORD_SYNC | ISKV_FROZEN_BASIS;
+  if (a.D != b.D || a.r_max != b.r_max || a.b_max != b.b_max || (a.flags & same) != (b.flags & same))
+    return ISKV_EINVAL;
+  const int32_t n = src->n_host;
+  if (n > a.n_cap) return ISKV_ECAPACITY;
+  hipStream_t s = dst->stream;
+  const size_t R = a.r_max, D = a.D, es = iskv_bf16_coords(a) ? 2 : 4;
+  if (n > 0) {
+    ISKV_HIP_CHECK(hipMemcpyAsync(dst->C, src->C, (size_t)n * R * es, hipMemcpyDeviceToDevice, s));
+    ISKV_HIP_CHECK(hipMemcpyAsync(dst->pos, src->pos, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToDevice, s));
+  }
+  ISKV_HIP_CHECK(hipMemcpyAsync(dst->sigma, src->sigma, R * sizeof(float), hipMemcpyDeviceToDevice, s));
+  ISKV_HIP_CHECK(hipMemcpyAsync(dst->B, src->B, D * R * sizeof(float), hipMemcpyDeviceToDevice, s));
+  ISKV_HIP_CHECK(hipMemcpyAsync(dst->w.Bbf, src->w.Bbf, D * R * 2, hipMemcpyDeviceToDevice, s));
+  ISKV_HIP_CHECK(hipMemcpyAsync(dst->w.st, src->w.st, ST_COUNT * sizeof(int32_t), hipMemcpyDeviceToDevice, s));
+  dst->n_host = n;
+  dst->folded_host = src->folded_host;
+  return ISKV_OK;
+}
+
 void isvd_destroy(isvd_handle* h) {
   if (!h) return;
   iskv_release_graphs(h);

@@ -365,6 +365,52 @@ def test_large_batch_matches_separate(K):
     bat.close()
 
 
+def test_copy_forks_a_path(K):
+    """isvd_copy: a path's history (§2.2 factor, Algorithm 3 positions) copied
+    into a fresh handle continues exactly like the original - the same next
+    blocks give bit-identical factors - and the two paths are independent
+    afterwards; mismatched handles and a too small capacity are refused."""
+    D, r, b = 256, 32, 16
+    X = synth.kv_stream(synth.StreamSpec(D=D, n=640, spectrum="exp40+0.01", noise_std=0.0, seed=81))
+    Xd = torch.from_numpy(X).to(DEV)
+    pos = torch.arange(640, dtype=torch.int32, device=DEV)
+    a = K.IsvdPath(D=D, r_max=r, b_max=b, n_cap=640, reorth_every_rows=64, device=DEV)
+    for s0 in range(0, 512, b):
+        a.merge(Xd[s0:s0 + b], pos[s0:s0 + b])
+    c = K.IsvdPath(D=D, r_max=r, b_max=b, n_cap=1024, reorth_every_rows=64, device=DEV)
+    c.merge(torch.randn((b, D), device=DEV), pos[:b])     # history the copy replaces
+    c.copy_from(a)
+    torch.cuda.synchronize()
+    assert c.query() == a.query()
+    before = gpu_factors(a)
+    for s0 in range(512, 576, b):
+        a.merge(Xd[s0:s0 + b], pos[s0:s0 + b])
+        c.merge(Xd[s0:s0 + b], pos[s0:s0 + b])
+    torch.cuda.synchronize()
+    fa, fc = gpu_factors(a), gpu_factors(c)
+    for u, v in zip(fa[:4], fc[:4]):
+        assert np.array_equal(u, v)
+    # independence: more rows into the copy leave the original as it was
+    for s0 in range(576, 640, b):
+        c.merge(Xd[s0:s0 + b], pos[s0:s0 + b])
+    torch.cuda.synchronize()
+    fa2 = gpu_factors(a)
+    for u, v in zip(fa[:4], fa2[:4]):
+        assert np.array_equal(u, v)
+    assert c.query()[0] == 640 and a.query()[0] == 576
+    assert before[0].shape[0] == 512
+    small = K.IsvdPath(D=D, r_max=r, b_max=b, n_cap=256, device=DEV)
+    with pytest.raises(K.IskvError):
+        small.copy_from(a)                                   # 576 rows > n_cap 256
+    other = K.IsvdPath(D=D, r_max=2 * r, b_max=b, n_cap=1024, device=DEV)
+    with pytest.raises(K.IskvError):
+        other.copy_from(a)                                   # different r_max
+    with pytest.raises(K.IskvError):
+        a.copy_from(a)
+    for p in (a, c, small, other):
+        p.close()
+
+
 def test_batched_merge_rejects_bad_sets(K):
     """Handles of separate allocations (no common offset), repeated handles and
     a capacity overflow are refused before anything runs."""
