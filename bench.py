@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--batch-steps", type=int, default=16, help="timed batched merges of the batch leg")
     ap.add_argument("--batched-kv", action="store_true",
                     help="K and V carved from one allocation, merged as one batched launch sequence")
+    ap.add_argument("--main-only", action="store_true",
+                    help="only the timed K/V steps and their stage breakdown (for counter passes)")
     ap.add_argument("--no-graphs", action="store_true",
                     help="enqueue every kernel directly instead of replaying recorded HIP graphs "
                          "(same kernels; for kernel-trace profilers)")
@@ -685,11 +687,12 @@ def main():
         "core_solver_last_merge": [{"flags": c[11], "steps": c[12], "resid_sweeps": c[14], "k": c[1], "n": c[0]}
                                    for c in core],
     }
-    result["coords_2byte"] = coords_leg(args, K, torch, dev, Xk, Kc)
-    result["prefill_init"] = prefill_leg(args, K, torch, dev)
-    result["prompt_decode_64k"] = prompt_decode_leg(args, K, torch, dev)
-    if args.batch_paths > 0:
-        result["batch_1024x32k"] = batch_leg(args, K, torch, dev)
+    if not args.main_only:
+        result["coords_2byte"] = coords_leg(args, K, torch, dev, Xk, Kc)
+        result["prefill_init"] = prefill_leg(args, K, torch, dev)
+        result["prompt_decode_64k"] = prompt_decode_leg(args, K, torch, dev)
+        if args.batch_paths > 0:
+            result["batch_1024x32k"] = batch_leg(args, K, torch, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(Xk, Xv, args.cpu_seconds)
     else:
