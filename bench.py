@@ -283,10 +283,14 @@ def batch_leg(args, K, torch, dev):
 
 
 def coords_leg(args, K, torch, dev, Xk, Kc):
-    """fp32 against 2-byte (bf16) stored coordinates on two fresh K paths of
-    N0 rows each, filled by merges and then timed the same way: MODE_MERGES
-    merges (with re-orthogonalisation every 256 rows), 10 reconstructions
-    (bf16 with RoPE) and 10 factor-aware attentions (all rows compressed)."""
+    """fp32 against 2-byte (bf16, fp16) stored coordinates on three fresh K
+    paths of N0 rows each, filled by merges and then timed the same way:
+    MODE_MERGES merges (with re-orthogonalisation every 256 rows), 10
+    reconstructions (bf16 with RoPE) and 10 factor-aware attentions (all rows
+    compressed). After the fill, each path's factor drift of eq.(14) (relative
+    error of C B^T against the N0 rows, minus that of their fresh rank-R
+    truncated SVD; the latter from the eigenvalues of X^T X in float64) and
+    its device status word (fp16 overflow guard) are recorded."""
     st = torch.cuda.Stream()
     n_fill, extra = N0, (MODE_MERGES + 2) * BLK
     Xd = torch.from_numpy(Xk[:n_fill + extra]).to(dev)
@@ -294,14 +298,24 @@ def coords_leg(args, K, torch, dev, Xk, Kc):
     rng = np.random.default_rng(6)
     q = torch.from_numpy(rng.standard_normal((HQ, DH)).astype(np.float32)).to(dev).bfloat16()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    # the fresh truncated SVD's error of the filled rows: sum of the trailing
+    # eigenvalues of X^T X
+    X64 = Xd[:n_fill].double()
+    lam = torch.linalg.eigvalsh(X64.T @ X64).flip(0).clamp_min(0)
+    nx = float(torch.sqrt(lam.sum()))
+    fresh_rel = float(torch.sqrt(lam[R:].sum())) / nx
     res, outs = {}, {}
-    for c16 in (False, True):
+    for fmt in ("fp32", "bf16", "fp16"):
         p = K.IsvdPath(D=D, r_max=R, b_max=BLK, n_cap=n_fill + extra, reorth_every_rows=256, device=dev,
-                       stream=st, graphs=not args.no_graphs, coords_bf16=c16)
+                       stream=st, graphs=not args.no_graphs, coords_bf16=fmt == "bf16", coords_fp16=fmt == "fp16")
         for s0 in range(0, n_fill, BLK):
             p.merge(Xd[s0:s0 + BLK], pos[s0:s0 + BLK])
         st.synchronize()
         n = p.n
+        nq, kq, status = p.query()
+        inc = p.C[:n, :kq].double() @ p.B[:, :kq].double().T  # rows in position order (pos = 0 .. n-1)
+        inc_rel = float(torch.linalg.norm(X64 - inc)) / nx
+        del inc
         out = torch.empty((n, D), dtype=torch.bfloat16, device=dev)
         of = torch.empty((HQ, DH), dtype=torch.bfloat16, device=dev)
         wsf = torch.empty(K.decode_attend_fv_workspace_bytes(p.h, 0, HQ), dtype=torch.uint8, device=dev)
@@ -319,7 +333,7 @@ def coords_leg(args, K, torch, dev, Xk, Kc):
         r_ms = timed(lambda: p.reconstruct(out, n, head_dim=DH, rope=True, theta=THETA, stream=st), 10)
         f_ms = timed(lambda: K.decode_attend_fv(q, Kc, p.h, None, None, 0, n, HQ, HKV, DH, DH ** -0.5, of, wsf,
                                                 stream=st), 10)
-        outs[c16] = (out.float(), of.float())
+        outs[fmt] = (out.float(), of.float())
         cur = [n_fill]
 
         def one_merge():
@@ -328,13 +342,19 @@ def coords_leg(args, K, torch, dev, Xk, Kc):
             cur[0] += BLK
 
         m_ms = timed(one_merge, MODE_MERGES)
-        res["bf16" if c16 else "fp32"] = {"merge_ms": m_ms, "recon_ms": r_ms, "factor_v_ms": f_ms,
-                                          "coordinate_bytes": n * R * (2 if c16 else 4)}
+        res[fmt] = {"merge_ms": m_ms, "recon_ms": r_ms, "factor_v_ms": f_ms,
+                    "coordinate_bytes": n * R * (4 if fmt == "fp32" else 2),
+                    "drift_eq14": inc_rel - fresh_rel, "status": int(status)}
         p.close()
-    (ra, fa), (rb, fb) = outs[False], outs[True]
+    del X64
     res["rows"] = n_fill
-    res["recon_rel_diff"] = float(torch.linalg.norm(rb - ra) / torch.linalg.norm(ra))
-    res["factor_v_max_abs_diff"] = float((fb - fa).abs().max())
+    res["fresh_svd_rel_err"] = fresh_rel
+    ra, fa = outs["fp32"]
+    for fmt in ("bf16", "fp16"):
+        rb, fb = outs[fmt]
+        res[fmt]["drift_minus_fp32"] = res[fmt]["drift_eq14"] - res["fp32"]["drift_eq14"]
+        res[fmt]["recon_rel_diff"] = float(torch.linalg.norm(rb - ra) / torch.linalg.norm(ra))
+        res[fmt]["factor_v_max_abs_diff"] = float((fb - fa).abs().max())
     return res
 
 

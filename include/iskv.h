@@ -55,6 +55,14 @@ enum iskv_status {
 /* Device status word bits (isvd_query's *status). */
 #define ISKV_DEV_NONFINITE 1
 #define ISKV_DEV_NOCONV 2
+#define ISKV_DEV_FP16_OVERFLOW 4 /* under ISKV_FP16_COORDS: a coordinate written
+                                    to the fp16 store had magnitude above 65504,
+                                    the largest finite fp16 (iS-KV notes §7.3:
+                                    derived factors, whose scale carries the
+                                    singular values, can pass it while the K/V
+                                    inputs do not). It was stored as +-65504,
+                                    never as an infinity; the bit stays set
+                                    until isvd_init. */
 
 /* Config flags. */
 #define ISKV_NO_COORD_SYNC 1 /* basis-only ablation (iS-KV notes §2.3): merges
@@ -76,6 +84,13 @@ enum iskv_status {
                                 product still computed in fp32; B and sigma
                                 stay fp32. The rounding of the stored rows at
                                 each merge is the factor drift of eq.(14). */
+#define ISKV_FP16_COORDS 16  /* persistent fp16 factors (iS-KV notes §7.3): C is
+                                stored as IEEE half ([n_cap x r_max] uint16 bits,
+                                round to nearest even), products in fp32 as
+                                above. Overflow guard: a value above 65504 in
+                                magnitude is stored as +-65504 (saturated) and
+                                latches ISKV_DEV_FP16_OVERFLOW. Exclusive with
+                                ISKV_BF16_COORDS. */
 
 /* Output dtypes of kv_reconstruct. */
 #define ISKV_OUT_BF16 0
@@ -95,8 +110,9 @@ typedef struct iskv_config {
                                 rho_j > max(delta*s, max(D,b)*2^-23*s),
                                 s = max(sigma_1, rho_1)                                   */
   int32_t flags;             /* ISKV_NO_COORD_SYNC | ISKV_NO_GRAPH | ISKV_FROZEN_BASIS |
-                                ISKV_BF16_COORDS, or 0 (at most one of NO_COORD_SYNC
-                                and FROZEN_BASIS)                                          */
+                                ISKV_BF16_COORDS | ISKV_FP16_COORDS, or 0 (at most
+                                one of NO_COORD_SYNC and FROZEN_BASIS, at most one
+                                of BF16_COORDS and FP16_COORDS)                                          */
 } iskv_config;
 
 typedef struct isvd_handle isvd_handle;
@@ -108,7 +124,8 @@ size_t isvd_workspace_bytes(const iskv_config* cfg);
 /* Create a handle over caller-owned device buffers and reset the history to
  * empty (n = k = 0). iS-KV notes §2.2: the history is X^ = C B^T where
  * C = U diag(sigma) holds one row of coordinates per token.
- *   C         device fp32 [n_cap x r_max] (bf16 under ISKV_BF16_COORDS):
+ *   C         device fp32 [n_cap x r_max] (bf16 under ISKV_BF16_COORDS, fp16
+ *             under ISKV_FP16_COORDS):
  *             coordinates; zero-filled here.
  *   sigma     device fp32 [r_max]: singular values, descending.
  *   B         device fp32 [D x r_max]: shared orthonormal basis, column j is
@@ -135,7 +152,8 @@ int isvd_init(isvd_handle** out, const iskv_config* cfg, float* C, float* sigma,
  *   b      1..b_max.
  * Errors: EINVAL (null pointer, b out of range), ECAPACITY (n + b > n_cap).
  * Non-finite input and a non-converged core are latched on the device
- * (ISKV_DEV_NONFINITE / ISKV_DEV_NOCONV, read by isvd_query). */
+ * (ISKV_DEV_NONFINITE / ISKV_DEV_NOCONV, read by isvd_query), and so is a
+ * saturated fp16 coordinate (ISKV_DEV_FP16_OVERFLOW). */
 int isvd_merge_block(isvd_handle* h, const float* F, const int32_t* pos_F, int32_t b);
 
 /* One merge on each of `count` paths in a single launch sequence (the

@@ -18,7 +18,7 @@ import os
 
 __all__ = [
     "LIB_PATH", "lib", "IskvError", "IskvConfig", "ISKV_NO_COORD_SYNC", "ISKV_NO_GRAPH", "ISKV_FROZEN_BASIS",
-    "ISKV_BF16_COORDS", "isvd_refit_workspace_bytes", "isvd_refit", "isvd_value_first_refit_workspace_bytes",
+    "ISKV_BF16_COORDS", "ISKV_FP16_COORDS", "ISKV_DEV_FP16_OVERFLOW", "isvd_refit_workspace_bytes", "isvd_refit", "isvd_value_first_refit_workspace_bytes",
     "isvd_value_first_refit", "iskv_prompt_split_workspace_bytes", "iskv_prompt_split", "prompt_split",
     "prefill_init", "iskv_prompt_protect_workspace_bytes", "iskv_prompt_protect", "prompt_protect",
     "ISKV_OUT_BF16", "isvd_set_mode",
@@ -44,10 +44,12 @@ ISKV_NO_COORD_SYNC = 1
 ISKV_NO_GRAPH = 2
 ISKV_FROZEN_BASIS = 4
 ISKV_BF16_COORDS = 8
+ISKV_FP16_COORDS = 16
 ISKV_OUT_BF16 = 0
 ISKV_OUT_FP32 = 1
 ISKV_DEV_NONFINITE = 1
 ISKV_DEV_NOCONV = 2
+ISKV_DEV_FP16_OVERFLOW = 4
 
 EXPORTED_SYMBOLS = (
     "isvd_workspace_bytes", "isvd_init", "isvd_merge_block", "isvd_reorth", "isvd_query",
@@ -452,15 +454,21 @@ def iskv_window_destroy(w: int) -> None:
 
 
 # ---- owners of the device buffers behind one handle --------------------------
+def _coord_dtype(torch, bf16: bool, fp16: bool):
+    return torch.bfloat16 if bf16 else (torch.float16 if fp16 else torch.float32)
+
+
 class IsvdPath:
     """One compressed (layer, K-or-V) path: torch tensors + the C handle."""
 
     def __init__(self, D: int, r_max: int, b_max: int, n_cap: int, reorth_every_rows: int = 0,
                  resid_rel_tol: float = 0.0, sync: bool = True, device="cuda", stream=None,
-                 graphs: bool = True, _buffers=None, coords_bf16: bool = False):
+                 graphs: bool = True, _buffers=None, coords_bf16: bool = False, coords_fp16: bool = False):
         import torch
+        if coords_bf16 and coords_fp16:
+            raise ValueError("coords_bf16 and coords_fp16 are exclusive")
         flags = ((0 if sync else ISKV_NO_COORD_SYNC) | (0 if graphs else ISKV_NO_GRAPH) |
-                 (ISKV_BF16_COORDS if coords_bf16 else 0))
+                 (ISKV_BF16_COORDS if coords_bf16 else 0) | (ISKV_FP16_COORDS if coords_fp16 else 0))
         self.cfg = IskvConfig(D, r_max, b_max, n_cap, reorth_every_rows, resid_rel_tol, flags)
         ws = isvd_workspace_bytes(self.cfg)
         if ws == 0:
@@ -471,8 +479,8 @@ class IsvdPath:
             self.workspace = None
         else:
             dev = torch.device(device)
-            # stored coordinates: fp32, or bf16 (2-byte persistent factors)
-            self.C = torch.empty((n_cap, r_max), dtype=torch.bfloat16 if coords_bf16 else torch.float32, device=dev)
+            # stored coordinates: fp32, or bf16 / fp16 (2-byte persistent factors)
+            self.C = torch.empty((n_cap, r_max), dtype=_coord_dtype(torch, coords_bf16, coords_fp16), device=dev)
             self.sigma = torch.empty((r_max,), dtype=torch.float32, device=dev)
             self.B = torch.empty((D, r_max), dtype=torch.float32, device=dev)
             self.pos = torch.empty((n_cap,), dtype=torch.int32, device=dev)
@@ -573,7 +581,7 @@ class IsvdBatch:
     def __init__(self, count: int, D: int, r_max: int, b_max: int, n_cap: int, reorth_every_rows: int = 0,
                  resid_rel_tol: float = 0.0, sync: bool = True, device="cuda", stream=None,
                  graphs: bool = True, window: int | None = None, block: int | None = None, prot_cap: int = 0,
-                 coords_bf16: bool = False):
+                 coords_bf16: bool = False, coords_fp16: bool = False):
         import torch
         if count < 1:
             raise ValueError("count must be >= 1")
@@ -581,7 +589,7 @@ class IsvdBatch:
         ws = isvd_workspace_bytes(cfg)
         if ws == 0:
             raise ValueError("invalid iskv configuration")
-        csz = 2 if coords_bf16 else 4
+        csz = 2 if (coords_bf16 or coords_fp16) else 4
         sizes = [n_cap * r_max * csz, r_max * 4, D * r_max * 4, n_cap * 4, ws]
         wrows = 0
         if window is not None:  # exact window + pending FIFO of every path in the same slot
@@ -606,12 +614,13 @@ class IsvdBatch:
             def view(i, dtype, shape):
                 return self.blob[z0 + offs[i]:z0 + offs[i] + sizes[i]].view(dtype).view(shape)
 
-            bufs = (view(0, torch.bfloat16 if coords_bf16 else torch.float32, (n_cap, r_max)),
+            bufs = (view(0, _coord_dtype(torch, coords_bf16, coords_fp16), (n_cap, r_max)),
                     view(1, torch.float32, (r_max,)),
                     view(2, torch.float32, (D, r_max)), view(3, torch.int32, (n_cap,)),
                     self.blob[z0 + offs[4]:z0 + offs[4] + ws])
             self.paths.append(IsvdPath(D, r_max, b_max, n_cap, reorth_every_rows, resid_rel_tol, sync,
-                                       device, stream, graphs, _buffers=bufs, coords_bf16=coords_bf16))
+                                       device, stream, graphs, _buffers=bufs, coords_bf16=coords_bf16,
+                                       coords_fp16=coords_fp16))
             if wrows:
                 self.windows.append(ExactWindow(self.paths[-1], window, block if block is not None else b_max,
                                                 prot_cap, stream,

@@ -544,8 +544,7 @@ int iskv_launch_attend_fv(const uint16_t* q, const uint16_t* K, const isvd_handl
   float* opart = pe + (size_t)ne * Hq * (FV_DH + FV_PAD);
   int* cnt = (int*)(opart + (size_t)Hq * NSL * FV_DH);
   const int G = Hq / Hkv;
-  const bool c16 = iskv_bf16_coords(hv->cfg);
-  const size_t lds = (size_t)fv_split_lds_bytes(R, c16 ? 2 : 4, D);
+  const size_t lds = (size_t)fv_split_lds_bytes(R, iskv_coord_bytes(hv->cfg), D);
   auto launch = [&](auto kj_c, auto g_c) -> hipError_t {
     constexpr int KJ = decltype(kj_c)::value, GG = decltype(g_c)::value;
     auto split = [&](auto* Cp) -> hipError_t {
@@ -557,7 +556,9 @@ int iskv_launch_attend_fv(const uint16_t* q, const uint16_t* K, const isvd_handl
                          cnt);
       return hipSuccess;
     };
-    const hipError_t e = c16 ? split((uint16_t*)hv->C) : split(hv->C);
+    const hipError_t e = iskv_bf16_coords(hv->cfg)   ? split((uint16_t*)hv->C)
+                         : iskv_fp16_coords(hv->cfg) ? split((_Float16*)hv->C)
+                                                     : split(hv->C);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((fv_merge_kernel<KJ, GG>), dim3(Hq, NSL), dim3(256), (size_t)2 * (nc + ne) * sizeof(float), s,
                        pc, nc, pe, ne, Hq, hv->B, R, hv->w.st, opart, cnt, out);

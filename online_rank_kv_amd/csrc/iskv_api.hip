@@ -25,7 +25,9 @@ bool cfg_ok(const iskv_config* c) {
   if (c->n_cap < 1) return false;
   if (c->reorth_every_rows < 0) return false;
   if (!(c->resid_rel_tol >= 0.f)) return false;
-  if (c->flags & ~(ISKV_NO_COORD_SYNC | ISKV_NO_GRAPH | ISKV_FROZEN_BASIS | ISKV_BF16_COORDS)) return false;
+  if (c->flags & ~(ISKV_NO_COORD_SYNC | ISKV_NO_GRAPH | ISKV_FROZEN_BASIS | ISKV_BF16_COORDS | ISKV_FP16_COORDS))
+    return false;
+  if ((c->flags & ISKV_BF16_COORDS) && (c->flags & ISKV_FP16_COORDS)) return false;
   if ((c->flags & ISKV_NO_COORD_SYNC) && (c->flags & ISKV_FROZEN_BASIS)) return false;
   return true;
 }
@@ -115,7 +117,7 @@ static int reset_history(isvd_handle* h) {
   h->n_host = 0;
   h->folded_host = 0;
   ISKV_HIP_CHECK(hipMemsetAsync(h->w.st, 0, ST_COUNT * sizeof(int32_t), s));
-  ISKV_HIP_CHECK(hipMemsetAsync(h->C, 0, (size_t)c.n_cap * R * (iskv_bf16_coords(c) ? 2 : 4), s));
+  ISKV_HIP_CHECK(hipMemsetAsync(h->C, 0, (size_t)c.n_cap * R * iskv_coord_bytes(c), s));
   ISKV_HIP_CHECK(hipMemsetAsync(h->sigma, 0, R * sizeof(float), s));
   ISKV_HIP_CHECK(hipMemsetAsync(h->B, 0, (size_t)c.D * R * sizeof(float), s));
   ISKV_HIP_CHECK(hipMemsetAsync(h->w.Bbf, 0, (size_t)c.D * R * 2, s));
@@ -340,13 +342,13 @@ int isvd_copy(isvd_handle* dst, const isvd_handle* src) {
   if (!dst || !src || dst == src) return ISKV_EINVAL;
   const iskv_config& a = dst->cfg;
   const iskv_config& b = src->cfg;
-  const int32_t same = ISKV_BF16_COORDS | ISKV_NO_COORD_SYNC | ISKV_FROZEN_BASIS;
+  const int32_t same = ISKV_BF16_COORDS | ISKV_FP16_COORDS | ISKV_NO_COORD_SYNC | ISKV_FROZEN_BASIS;
   if (a.D != b.D || a.r_max != b.r_max || a.b_max != b.b_max || (a.flags & same) != (b.flags & same))
     return ISKV_EINVAL;
   const int32_t n = src->n_host;
   if (n > a.n_cap) return ISKV_ECAPACITY;
   hipStream_t s = dst->stream;
-  const size_t R = a.r_max, D = a.D, es = iskv_bf16_coords(a) ? 2 : 4;
+  const size_t R = a.r_max, D = a.D, es = iskv_coord_bytes(a);
   if (n > 0) {
     ISKV_HIP_CHECK(hipMemcpyAsync(dst->C, src->C, (size_t)n * R * es, hipMemcpyDeviceToDevice, s));
     ISKV_HIP_CHECK(hipMemcpyAsync(dst->pos, src->pos, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToDevice, s));
@@ -464,7 +466,7 @@ int decode_attend_fv(const uint16_t* q, const uint16_t* K, const isvd_handle* hv
   if (G != 1 && G != 2 && G != 4) return ISKV_EINVAL;
   if (hv->cfg.D != Hkv * 128 || hv->cfg.D > 1024) return ISKV_EINVAL;
   if (hv->cfg.r_max % 4 != 0 || hv->cfg.r_max > 448) return ISKV_EINVAL;  // a chunk of rows fits in LDS
-  if (iskv_bf16_coords(hv->cfg) && hv->cfg.r_max % 8 != 0) return ISKV_EINVAL;  // 16-byte aligned 2-byte rows
+  if (iskv_coord_bytes(hv->cfg) == 2 && hv->cfg.r_max % 8 != 0) return ISKV_EINVAL;  // 16-byte aligned 2-byte rows
   if (hv->n_host + n_exact < 1) return ISKV_EINVAL;
   if (ws_bytes < iskv_attend_fv_ws_bytes(hv->n_host, n_exact, Hq, hv->cfg.r_max)) return ISKV_EWORKSPACE;
   return iskv_launch_attend_fv(q, K, hv, X_exact, pos_exact, n_exact, n_total, Hq, Hkv, scale, out, workspace,

@@ -8,6 +8,7 @@
 
 #include "../../include/iskv.h"
 
+#include <type_traits>
 #include <vector>
 
 // ---- device state word slots (int32 array at the head of the workspace) ----
@@ -206,19 +207,41 @@ int iskv_upload_offsets(isvd_handle* const* hs, int32_t count);
 int iskv_launch_copy_pos_host(int32_t* pos_dev, const int32_t* pos_host, int32_t count,
                               hipStream_t s);
 
-// Stored coordinates: fp32, or bf16 (uint16 bits) under ISKV_BF16_COORDS.
-// Loads widen to fp32; stores round to nearest even (NaN stays NaN).
+// Stored coordinates: fp32, bf16 (uint16 bits) under ISKV_BF16_COORDS, or
+// IEEE half (_Float16) under ISKV_FP16_COORDS. Loads widen to fp32; stores
+// round to nearest even (NaN stays NaN) and return whether the value had to
+// be saturated: only the half store can, at magnitudes above 65504 (its
+// largest finite value), where it writes +-65504 instead of an infinity.
+// Kernels OR the returned flags and latch ISKV_DEV_FP16_OVERFLOW once.
 __device__ __forceinline__ float iskv_ld(const float* p) { return *p; }
 __device__ __forceinline__ float iskv_ld(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
+__device__ __forceinline__ float iskv_ld(const _Float16* p) { return (float)*p; }
 __device__ __forceinline__ uint16_t iskv_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
   u += 0x7fffu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
 }
-__device__ __forceinline__ void iskv_st(float* p, float v) { *p = v; }
-__device__ __forceinline__ void iskv_st(uint16_t* p, float v) { *p = iskv_to_bf16(v); }
+constexpr float ISKV_F16_MAX = 65504.f;
+__device__ __forceinline__ bool iskv_f16_over(float v) { return fabsf(v) > ISKV_F16_MAX; }  // NaN: false
+__device__ __forceinline__ _Float16 iskv_to_f16(float v) {
+  return (_Float16)(iskv_f16_over(v) ? copysignf(ISKV_F16_MAX, v) : v);
+}
+__device__ __forceinline__ bool iskv_st(float* p, float v) { *p = v; return false; }
+__device__ __forceinline__ bool iskv_st(uint16_t* p, float v) { *p = iskv_to_bf16(v); return false; }
+__device__ __forceinline__ bool iskv_st(_Float16* p, float v) {
+  *p = iskv_to_f16(v);
+  return iskv_f16_over(v);
+}
+template <class TC>
+__device__ __forceinline__ void iskv_latch_overflow(int32_t* st, bool over) {
+  if constexpr (sizeof(TC) == 2 && !std::is_same<TC, uint16_t>::value)
+    if (over) atomicOr(&st[ST_STATUS], ISKV_DEV_FP16_OVERFLOW);
+}
 inline bool iskv_bf16_coords(const iskv_config& c) { return (c.flags & ISKV_BF16_COORDS) != 0; }
+inline bool iskv_fp16_coords(const iskv_config& c) { return (c.flags & ISKV_FP16_COORDS) != 0; }
+// bytes per stored coordinate
+inline int iskv_coord_bytes(const iskv_config& c) { return (c.flags & (ISKV_BF16_COORDS | ISKV_FP16_COORDS)) ? 2 : 4; }
 
 // Batched launches: z copies of a grid, and the per-copy pointer rebase.
 inline dim3 bz(dim3 g, int count) { return dim3(g.x, g.y, (unsigned)count); }

@@ -625,7 +625,7 @@ __global__ __launch_bounds__(256) void xh_mfma_kernel(const TX* X1, int ld1, con
                                                       int ldh, int hcols, Dim kout_d, Dim rows_d,
                                                       TY* Y, int ldy, uint16_t* Ybf, int ldbf,
                                                       int ldx, int32_t* pos, const int32_t* pos_src,
-                                                      Dim yoff_d,
+                                                      Dim yoff_d, int32_t* st,
     const int64_t* __restrict__ bd) {
   const int64_t bdel = bd ? bd[blockIdx.z] : 0;
   X1 = iskv_rb(X1, bdel);
@@ -639,6 +639,7 @@ __global__ __launch_bounds__(256) void xh_mfma_kernel(const TX* X1, int ld1, con
   Ybf = iskv_rb(Ybf, bdel);
   pos = iskv_rb(pos, bdel);
   pos_src = iskv_rb(pos_src, bdel);
+  st = iskv_rb(st, bdel);
   iskv_rb_dim(yoff_d, bdel);
   const int k1 = dval(k1_d), kin = dval(kin_d), kout = dval(kout_d), rows = dval(rows_d);
   const int yo = dval(yoff_d);
@@ -649,6 +650,7 @@ __global__ __launch_bounds__(256) void xh_mfma_kernel(const TX* X1, int ld1, con
   float* Hs = sm + BM * ldx;    // [XH_KC][XH_HS]
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int nr = min(BM, rows - i0);
+  bool over = false;  // a saturated half store (fp16 coordinates only)
   // X tile: all loads issued, then stored; zero beyond kin and nr
   {
     const int kin4 = (kin + 3) & ~3;
@@ -723,12 +725,13 @@ __global__ __launch_bounds__(256) void xh_mfma_kernel(const TX* X1, int ld1, con
         for (int e = 0; e < 4; ++e) {
           const int r = a * 16 + 4 * (lane >> 4) + e;
           if (r < nr && j < kout) {
-            iskv_st(Y + (size_t)(yo + i0 + r) * ldy + j, acc[a][b][e]);
+            over |= iskv_st(Y + (size_t)(yo + i0 + r) * ldy + j, acc[a][b][e]);
             if (Ybf) Ybf[(size_t)(yo + i0 + r) * ldbf + j] = f2bf(acc[a][b][e]);
           }
         }
       }
   }
+  iskv_latch_overflow<TY>(st, over);
 }
 
 // Same product with H held in registers (kin <= 288, kout <= 256): a
@@ -745,7 +748,7 @@ __global__ __launch_bounds__(1024) void xh_reg_kernel(const TX* X1, int ld1, con
                                                       Dim k1_d, Dim kin_d, const float* __restrict__ H,
                                                       int ldh, int hcols, Dim kout_d, Dim rows_d, TY* Y,
                                                       int ldy, uint16_t* Ybf, int ldbf, int32_t* pos,
-                                                      const int32_t* pos_src, Dim yoff_d,
+                                                      const int32_t* pos_src, Dim yoff_d, int32_t* st,
     const int64_t* __restrict__ bd) {
   const int64_t bdel = bd ? bd[blockIdx.z] : 0;
   X1 = iskv_rb(X1, bdel);
@@ -759,6 +762,7 @@ __global__ __launch_bounds__(1024) void xh_reg_kernel(const TX* X1, int ld1, con
   Ybf = iskv_rb(Ybf, bdel);
   pos = iskv_rb(pos, bdel);
   pos_src = iskv_rb(pos_src, bdel);
+  st = iskv_rb(st, bdel);
   iskv_rb_dim(yoff_d, bdel);
   constexpr int KW = 4 * XR_KS;                // staged columns (zero beyond kin)
   constexpr int PER = (16 * KW + 1023) / 1024;  // staged elements per thread
@@ -769,6 +773,7 @@ __global__ __launch_bounds__(1024) void xh_reg_kernel(const TX* X1, int ld1, con
   __shared__ float Xs[2][16 * XR_LDX];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int col = wave * 16 + (lane & 15);
+  bool over = false;  // a saturated half store (fp16 coordinates only)
   float hreg[XR_KS];
   {
     const int cc = min(col, hcols - 1);
@@ -820,7 +825,7 @@ __global__ __launch_bounds__(1024) void xh_reg_kernel(const TX* X1, int ld1, con
       for (int e = 0; e < 4; ++e) {
         const int row = i0 + 4 * (lane >> 4) + e;
         if (row < rows) {
-          iskv_st(Y + (size_t)(yo + row) * ldy + col, acc[e]);
+          over |= iskv_st(Y + (size_t)(yo + row) * ldy + col, acc[e]);
           if (Ybf) Ybf[(size_t)(yo + row) * ldbf + col] = f2bf(acc[e]);
         }
       }
@@ -828,6 +833,7 @@ __global__ __launch_bounds__(1024) void xh_reg_kernel(const TX* X1, int ld1, con
     if (pos && t < 16 && i0 + t < rows) pos[yo + i0 + t] = pos_src[i0 + t];
     buf ^= 1;
   }
+  iskv_latch_overflow<TY>(st, over);
 }
 
 // The coordinate update C <- C H over all n rows (C n x kin, in place; H
@@ -888,14 +894,19 @@ __global__ __launch_bounds__(256) void split_h_kernel(const float* __restrict__ 
 
 template <typename TX>
 __global__ __launch_bounds__(1024) void xh_bf3_kernel(TX* X, int ldx, Dim kin_d, const uint4* __restrict__ Hs, int NW,
-                                                      int NS, Dim kout_d, Dim rows_d, const int64_t* __restrict__ bd) {
+                                                      int NS, Dim kout_d, Dim rows_d, int32_t* st,
+                                                      const int64_t* __restrict__ bd) {
   const int64_t bdel = bd ? bd[blockIdx.z] : 0;
   X = iskv_rb(X, bdel);
+  st = iskv_rb(st, bdel);
   Hs = iskv_rb(Hs, bdel);
   iskv_rb_dim(kin_d, bdel);
   iskv_rb_dim(kout_d, bdel);
   iskv_rb_dim(rows_d, bdel);
-  constexpr bool SPLIT_X = std::is_same<TX, float>::value;
+  // fp32 and fp16 rows need the low bf16 part (fp16 carries 11 significant
+  // bits); bf16 rows are exact in the high part
+  constexpr bool SPLIT_X = !std::is_same<TX, uint16_t>::value;
+  bool over = false;  // a saturated half store (fp16 coordinates only)
   const int kin = dval(kin_d), kout = dval(kout_d), rows = dval(rows_d);
   const int nblk = (rows + 15) / 16;
   if ((int)blockIdx.x >= nblk || kout <= 0 || kin <= 0) return;
@@ -921,8 +932,12 @@ __global__ __launch_bounds__(1024) void xh_bf3_kernel(TX* X, int ldx, Dim kin_d,
   float4 xr[XB_CH];
   auto load_x = [&](int u, int blk) {
     const int row = min(blk * 16 + sr, rows - 1);
-    if constexpr (SPLIT_X) {
+    if constexpr (std::is_same<TX, float>::value) {
       xr[u] = *(const float4*)(X + (size_t)row * ldx + sc);
+    } else if constexpr (std::is_same<TX, _Float16>::value) {
+      typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+      const h4_t v = *(const h4_t*)(X + (size_t)row * ldx + sc);
+      xr[u] = float4{(float)v.x, (float)v.y, (float)v.z, (float)v.w};
     } else {
       const uint2 v = *(const uint2*)(X + (size_t)row * ldx + sc);
       xr[u] = float4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y << 16),
@@ -971,12 +986,13 @@ __global__ __launch_bounds__(1024) void xh_bf3_kernel(TX* X, int ldx, Dim kin_d,
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = i0 + 4 * (lane >> 4) + e;
-        if (row < rows) iskv_st(X + (size_t)row * ldx + col, acc[e]);
+        if (row < rows) over |= iskv_st(X + (size_t)row * ldx + col, acc[e]);
       }
     }
     buf ^= 1;
   }
   }
+  iskv_latch_overflow<TX>(st, over);
 }
 
 // Launch Y = [X1 | X2] H over `rows_host` rows (an upper bound when rows_d is
@@ -985,7 +1001,8 @@ template <typename TX, typename TY>
 static void xh_launch(hipStream_t s, const int64_t* bd, int bc, int rows_host, const TX* X1, int ld1, const float* X2, int ld2,
                       Dim k1, Dim kin, int kin_max, const float* H, int ldh, int hcols, Dim kout,
                       Dim rows, TY* Y, int ldy, uint16_t* Ybf, int ldbf, int32_t* pos = nullptr,
-                      const int32_t* pos_src = nullptr, bool prefer16 = false, Dim yoff = hdim(0)) {
+                      const int32_t* pos_src = nullptr, bool prefer16 = false, Dim yoff = hdim(0),
+                      int32_t* st = nullptr) {
   const int ldx = xh_ldx(kin_max);
   if (kin_max <= 288 && hcols <= 256) {
     const int nblk = (rows_host + 15) / 16;
@@ -993,21 +1010,21 @@ static void xh_launch(hipStream_t s, const int64_t* bd, int bc, int rows_host, c
     if (grid > 0) {
       if (kin_max <= 256)
         hipLaunchKernelGGL((xh_reg_kernel<64, TX, TY>), bz(dim3(grid), bc), dim3(1024), 0, s, X1, ld1, X2, ld2, k1, kin, H,
-                           ldh, hcols, kout, rows, Y, ldy, Ybf, ldbf, pos, pos_src, yoff, bd);
+                           ldh, hcols, kout, rows, Y, ldy, Ybf, ldbf, pos, pos_src, yoff, st, bd);
       else
         hipLaunchKernelGGL((xh_reg_kernel<72, TX, TY>), bz(dim3(grid), bc), dim3(1024), 0, s, X1, ld1, X2, ld2, k1, kin, H,
-                           ldh, hcols, kout, rows, Y, ldy, Ybf, ldbf, pos, pos_src, yoff, bd);
+                           ldh, hcols, kout, rows, Y, ldy, Ybf, ldbf, pos, pos_src, yoff, st, bd);
     }
     return;
   }
   if (!prefer16 && xh_lds_bytes(32, kin_max) <= 80 * 1024) {
     hipLaunchKernelGGL((xh_mfma_kernel<32, TX, TY>), bz(dim3((rows_host + 31) / 32), bc), dim3(256),
                        xh_lds_bytes(32, kin_max), s, X1, ld1, X2, ld2, k1, kin, H, ldh, hcols, kout,
-                       rows, Y, ldy, Ybf, ldbf, ldx, pos, pos_src, yoff, bd);
+                       rows, Y, ldy, Ybf, ldbf, ldx, pos, pos_src, yoff, st, bd);
   } else {
     hipLaunchKernelGGL((xh_mfma_kernel<16, TX, TY>), bz(dim3((rows_host + 15) / 16), bc), dim3(256),
                        xh_lds_bytes(16, kin_max), s, X1, ld1, X2, ld2, k1, kin, H, ldh, hcols, kout,
-                       rows, Y, ldy, Ybf, ldbf, ldx, pos, pos_src, yoff, bd);
+                       rows, Y, ldy, Ybf, ldbf, ldx, pos, pos_src, yoff, st, bd);
   }
 }
 
@@ -1045,15 +1062,16 @@ __global__ __launch_bounds__(256) void frozen_append_kernel(const float* __restr
   pos = iskv_rb(pos, d);
   st = iskv_rb(st, d);
   const int n = st[ST_N], k = st[ST_K];
-  bool bad = false;
+  bool bad = false, over = false;
   for (int e = threadIdx.x; e < b * ldc; e += blockDim.x) {
     const int i = e / ldc, j = e % ldc;
     const float v = j < k ? Q[(size_t)i * ldq + j] : 0.f;
     bad |= !isfinite(v);
-    iskv_st(C + (size_t)(n + i) * ldc + j, v);
+    over |= iskv_st(C + (size_t)(n + i) * ldc + j, v);
   }
   for (int i = threadIdx.x; i < b; i += blockDim.x) pos[n + i] = pos_F[i];
   if (bad) atomicOr(&st[ST_STATUS], ISKV_DEV_NONFINITE);
+  iskv_latch_overflow<TC>(st, over);
   __syncthreads();
   if (threadIdx.x == 0) {
     st[ST_N] = n + b;
@@ -1341,7 +1359,13 @@ int iskv_kernel_setup() {
                       (const void*)xh_mfma_kernel<32, uint16_t, uint16_t>,
                       (const void*)xh_mfma_kernel<16, uint16_t, uint16_t>,
                       (const void*)xh_mfma_kernel<32, float, uint16_t>,
-                      (const void*)xh_mfma_kernel<16, float, uint16_t>};
+                      (const void*)xh_mfma_kernel<16, float, uint16_t>,
+                      (const void*)xh_mfma_kernel<32, _Float16, _Float16>,
+                      (const void*)xh_mfma_kernel<16, _Float16, _Float16>,
+                      (const void*)xh_mfma_kernel<32, float, _Float16>,
+                      (const void*)xh_mfma_kernel<16, float, _Float16>,
+                      (const void*)xh_mfma_kernel<16, uint16_t, float>,
+                      (const void*)xh_mfma_kernel<16, _Float16, float>};
   for (const void* f : xh) ISKV_HIP_CHECK(hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds));
   if (iskv_core_eig_setup() != ISKV_OK) return ISKV_EHIP;
   done = 1;
@@ -1351,10 +1375,12 @@ int iskv_kernel_setup() {
 // The launch sequence of one merge. It depends on the host only through b
 // and the handle's fixed buffers: the row count n is read on the device, so
 // the sequence can be recorded once and replayed.
-// Run f with the handle's coordinate array typed as stored (fp32 or bf16 bits).
+// Run f with the handle's coordinate array typed as stored (fp32, bf16 bits or
+// IEEE half).
 template <class Fn>
 static void with_coords(isvd_handle* h, Fn f) {
   if (iskv_bf16_coords(h->cfg)) f((uint16_t*)h->C);
+  else if (iskv_fp16_coords(h->cfg)) f((_Float16*)h->C);
   else f(h->C);
 }
 
@@ -1432,15 +1458,15 @@ static int merge_body(isvd_handle* h, const float* F, const int32_t* pos_F, int3
       if (bf3) {  // split-bf16 matrix cores, one 1024-thread workgroup per CU at most
         const int nblk = (c.n_cap + 15) / 16;
         hipLaunchKernelGGL((xh_bf3_kernel<TC>), bz(dim3(nblk < 256 ? nblk : 256), h->bcount), dim3(1024), 0, s, Cp,
-                           R, ddim(dk), (const uint4*)w.T2, NW3, NS3, ddim(w.st + ST_KNEW), dn, h->bd);
+                           R, ddim(dk), (const uint4*)w.T2, NW3, NS3, ddim(w.st + ST_KNEW), dn, w.st, h->bd);
       } else {
         xh_launch(s, h->bd, h->bcount, c.n_cap, Cp, R, nullptr, 0, ddim(dk), ddim(dk), R, w.Hc, R, R,
-                  ddim(w.st + ST_KNEW), dn, Cp, R, nullptr, 0);
+                  ddim(w.st + ST_KNEW), dn, Cp, R, nullptr, 0, nullptr, nullptr, false, hdim(0), w.st);
       }
     }
     mark(4);
     xh_launch(s, h->bd, h->bcount, b, w.Q, R, w.FP, c.b_max, ddim(dk), ddim(w.st + ST_M), M, w.Hc, R, R,
-              ddim(w.st + ST_KNEW), hdim(b), Cp, R, nullptr, 0, h->pos, pos_F, false, dn);
+              ddim(w.st + ST_KNEW), hdim(b), Cp, R, nullptr, 0, h->pos, pos_F, false, dn, w.st);
   });
   xh_launch(s, h->bd, h->bcount, D, h->B, R, w.P, c.b_max, ddim(dk), ddim(w.st + ST_M), M, w.Hc, R, R,
             ddim(w.st + ST_KNEW), hdim(D), h->B, R, w.Bbf, R, nullptr, nullptr, true);
@@ -1503,7 +1529,7 @@ static int reorth_body(isvd_handle* h) {
   hipLaunchKernelGGL(to_f32_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.T, w.Pa, ld, w.Hc, w.T2, R, w.st, h->bd);
   with_coords(h, [&](auto* Cp) {
     xh_launch(s, h->bd, h->bcount, ncap, Cp, R, nullptr, 0, ddim(w.st + ST_K), ddim(w.st + ST_K), R, w.Hc, R, R,
-              ddim(w.st + ST_K), dn, Cp, R, nullptr, 0);
+              ddim(w.st + ST_K), dn, Cp, R, nullptr, 0, nullptr, nullptr, false, hdim(0), w.st);
   });
   xh_launch(s, h->bd, h->bcount, D, h->B, R, nullptr, 0, ddim(w.st + ST_K), ddim(w.st + ST_K), R, w.T2, R, R,
             ddim(w.st + ST_K), hdim(D), h->B, R, w.Bbf, R, nullptr, nullptr, true);
@@ -1677,13 +1703,13 @@ bool iskv_refit_supported(const iskv_config& c) { return xh_lds_bytes(16, c.D) <
 size_t iskv_refit_ws_bytes(const isvd_handle* h) { return iskv_refit_gram_ws_bytes(h); }
 
 // C <- X B over the n rows X (n x D fp32), k = st[ST_K] columns; stored as
-// the handle keeps its coordinates (fp32 or bf16).
+// the handle keeps its coordinates (fp32, bf16 or fp16).
 int iskv_launch_coords_from_rows(isvd_handle* h, const float* X, int32_t n) {
   const iskv_config& c = h->cfg;
   const int D = c.D, R = c.r_max;
   with_coords(h, [&](auto* Cp) {
     xh_launch(h->stream, nullptr, 1, n, X, D, nullptr, 0, hdim(D), hdim(D), D, h->B, R, R, ddim(h->w.st + ST_K),
-              hdim(n), Cp, R, nullptr, 0, nullptr, nullptr, true);
+              hdim(n), Cp, R, nullptr, 0, nullptr, nullptr, true, hdim(0), h->w.st);
   });
   ISKV_HIP_CHECK(hipGetLastError());
   return ISKV_OK;

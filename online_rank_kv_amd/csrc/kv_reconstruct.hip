@@ -55,13 +55,19 @@ __device__ __forceinline__ float rope_rev(uint32_t p, uint64_t F) {
   return (float)(int32_t)top * 2.3283064365386963e-10f;  // * 2^-32
 }
 
-// Four consecutive stored coordinates as fp32 (fp32 rows, or bf16 rows under
-// 2-byte persistence; the bf16 load needs 8-byte alignment).
+// Four consecutive stored coordinates as fp32 (fp32 rows, or bf16 / fp16 rows
+// under 2-byte persistence; the 2-byte loads need 8-byte alignment).
 __device__ __forceinline__ float4 ld_c4(const float* p) { return *(const float4*)p; }
 __device__ __forceinline__ float4 ld_c4(const uint16_t* p) {
   const uint2 v = *(const uint2*)p;
   return float4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y << 16),
                 __uint_as_float(v.y & 0xffff0000u)};
+}
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float4 ld_c4(const _Float16* p) {
+  const uint2 v = *(const uint2*)p;
+  const h2_t a = __builtin_bit_cast(h2_t, v.x), b = __builtin_bit_cast(h2_t, v.y);
+  return float4{(float)a.x, (float)a.y, (float)b.x, (float)b.y};
 }
 
 // Column tile of W (128 or 64) features; rotary pair q (0 .. W/2-1) of the
@@ -397,6 +403,15 @@ __global__ __launch_bounds__(64 * NW, 2) void recon_stream_kernel(const TC* __re
   // fp32 rows are held as float4, 2-byte rows as their raw bf16 bits
   using CR = std::conditional_t<ES == 4, float4, uint2>;
   CR creg[2][PER];
+  // four 2-byte coordinates as bf16 bits (fp16 rows are rounded to bf16)
+  auto to_bf4 = [](uint2 v) -> uint2 {
+    if constexpr (std::is_same<TC, _Float16>::value) {
+      const h2_t a = __builtin_bit_cast(h2_t, v.x), b = __builtin_bit_cast(h2_t, v.y);
+      return uint2{pk_bf16((float)a.x, (float)a.y), pk_bf16((float)b.x, (float)b.y)};
+    } else {
+      return v;
+    }
+  };
   // C rows through a buffer descriptor based at the block's first row and
   // bounded by the last row n - 1 (rows past n read as zero; a block past the
   // end gets an empty descriptor); per-load offsets are fixed (row t / 64 +
@@ -430,7 +445,7 @@ __global__ __launch_bounds__(64 * NW, 2) void recon_stream_kernel(const TC* __re
           const float4 v = creg[slot][u];
           *(uint2*)(cs + r * RS_CS + c4) = uint2{pk_bf16(v.x, v.y), pk_bf16(v.z, v.w)};
         } else {
-          *(uint2*)(cs + r * RS_CS + c4) = creg[slot][u];
+          *(uint2*)(cs + r * RS_CS + c4) = to_bf4(creg[slot][u]);
         }
       }
     } else {
@@ -444,7 +459,7 @@ __global__ __launch_bounds__(64 * NW, 2) void recon_stream_kernel(const TC* __re
           const float x2 = (rv && c4 + 2 < kdev) ? v.z : 0.f, x3 = (rv && c4 + 3 < kdev) ? v.w : 0.f;
           *(uint2*)(cs + r * RS_CS + c4) = uint2{pk_bf16(x0, x1), pk_bf16(x2, x3)};
         } else {  // zero the 16-bit halves at columns >= k (rows past n read as zero)
-          const uint2 v = creg[slot][u];
+          const uint2 v = to_bf4(creg[slot][u]);
           const uint32_t m0 = (c4 < kdev ? 0xffffu : 0u) | (c4 + 1 < kdev ? 0xffff0000u : 0u);
           const uint32_t m1 = (c4 + 2 < kdev ? 0xffffu : 0u) | (c4 + 3 < kdev ? 0xffff0000u : 0u);
           *(uint2*)(cs + r * RS_CS + c4) = rv ? uint2{v.x & m0, v.y & m1} : uint2{0u, 0u};
@@ -640,6 +655,7 @@ int iskv_launch_reconstruct(const isvd_handle* h, const float* X_exact, const in
       }
     };
     if (iskv_bf16_coords(h->cfg)) go((uint16_t*)h->C);
+    else if (iskv_fp16_coords(h->cfg)) go((_Float16*)h->C);
     else go(h->C);
   }
   if (n_exact > 0) {

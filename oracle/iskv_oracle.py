@@ -39,6 +39,9 @@ __all__ = [
     "anomaly_block_scores",
     "prompt_protect",
     "persist_coords_bf16",
+    "persist_coords_fp16",
+    "fp16_round",
+    "FP16_MAX",
     "represented",
     "stored_rows",
     "fresh_truncated_svd",
@@ -78,6 +81,7 @@ class Factor:
     folded: int = 0
     C_stale: np.ndarray | None = None
     dtype: type = np.float64
+    fp16_overflow: bool = False  # a stored fp16 coordinate was saturated (§7.3 guard)
 
     @property
     def n(self) -> int:
@@ -140,7 +144,8 @@ def merge(fac: Factor, F: np.ndarray, pos_F, r: int, delta: float = 0.0,
             diag.update(dict(p=None, empty=True, s_plus=s, r_prime=rp))
         C_stale = None if sync else (U_new * sig_new[None, :])
         return Factor(U=U_new.astype(dt), sigma=sig_new.astype(dt), B=B_new.astype(dt),
-                      pos=pos_F.copy(), folded=fac.folded + b, C_stale=C_stale, dtype=dt)
+                      pos=pos_F.copy(), folded=fac.folded + b, C_stale=C_stale, dtype=dt,
+                      fp16_overflow=fac.fp16_overflow)
 
     B = fac.B
     # Projection and residual, with the second subtraction of the leftover
@@ -203,7 +208,7 @@ def merge(fac: Factor, F: np.ndarray, pos_F, r: int, delta: float = 0.0,
                          s_plus=s_plus, Hc=Hc, r_prime=rp, FP=FP))
     return Factor(U=U_new, sigma=sig_new, B=B_new,
                   pos=np.concatenate([fac.pos, pos_F]), folded=fac.folded + b,
-                  C_stale=C_stale, dtype=dt)
+                  C_stale=C_stale, dtype=dt, fp16_overflow=fac.fp16_overflow)
 
 
 def reorth(fac: Factor) -> Factor:
@@ -220,7 +225,7 @@ def reorth(fac: Factor) -> Factor:
     M = RU @ np.diag(fac.sigma) @ RB.T
     W, S, Vt = _svd(M)
     return Factor(U=QU @ W, sigma=S, B=QB @ Vt.T, pos=fac.pos.copy(), folded=fac.folded,
-                  C_stale=fac.C_stale, dtype=fac.dtype)
+                  C_stale=fac.C_stale, dtype=fac.dtype, fp16_overflow=fac.fp16_overflow)
 
 
 def persist_coords_bf16(fac: Factor) -> Factor:
@@ -235,6 +240,23 @@ def persist_coords_bf16(fac: Factor) -> Factor:
     U = np.where(fac.sigma[None, :] > 0, C / safe[None, :], 0.0)
     return Factor(U=U, sigma=fac.sigma.copy(), B=fac.B.copy(), pos=fac.pos.copy(), folded=fac.folded,
                   C_stale=fac.C_stale, dtype=fac.dtype)
+
+
+def persist_coords_fp16(fac: Factor) -> Factor:
+    """Persistent fp16 factors with the overflow guard (iS-KV notes §7.3: with
+    FP16 factors some coordinates passed the largest finite half, 65504,
+    became infinite and led to NaN logits; the scale of the derived factor
+    carries the singular values, so finite inputs do not keep it finite).
+    The stored C = U diag(sigma) is rounded to half whenever it is written;
+    a magnitude above 65504 is stored as +-65504 and the returned factor's
+    ``fp16_overflow`` is set (it stays set). sigma and B keep full precision."""
+    if fac.k == 0 or fac.n == 0:
+        return fac
+    C, over = fp16_round(fac.U * fac.sigma[None, :])
+    safe = np.where(fac.sigma > 0, fac.sigma, 1.0)
+    U = np.where(fac.sigma[None, :] > 0, C / safe[None, :], 0.0)
+    return Factor(U=U, sigma=fac.sigma.copy(), B=fac.B.copy(), pos=fac.pos.copy(), folded=fac.folded,
+                  C_stale=fac.C_stale, dtype=fac.dtype, fp16_overflow=fac.fp16_overflow or over)
 
 
 def anomaly_block_scores(K_rot: np.ndarray, Hkv: int, dh: int, block: int = 8, suffix_blocks: int = 4):
@@ -411,6 +433,22 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     return u.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
+# Largest finite IEEE half-precision value, (2 - 2^-10) * 2^15.
+FP16_MAX = 65504.0
+
+
+def fp16_round(x: np.ndarray):
+    """Round to IEEE half precision (via float32, the compute precision, then
+    round-to-nearest-even) with the overflow guard of the persistent fp16
+    factors: a magnitude above FP16_MAX is stored as +-FP16_MAX instead of an
+    infinity. NaN stays NaN. Returns (values as float64, whether any
+    magnitude was above FP16_MAX)."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    over = np.abs(f) > FP16_MAX  # NaN compares false
+    h = np.where(over, np.copysign(np.float32(FP16_MAX), f), f).astype(np.float16)
+    return h.astype(np.float64), bool(over.any())
+
+
 def reconstruct(fac: Factor, X_exact, pos_exact, n_total: int, head_dim: int,
                 apply_rope: bool, theta: float = 500000.0) -> np.ndarray:
     """Dense cache in original position order (iS-KV notes §3.2, §5, Algorithm 3).
@@ -569,15 +607,19 @@ def one_step_drift(fac: Factor, F, pos_F, r: int, delta: float = 0.0):
 
 def run_stream(X: np.ndarray, b: int, r: int, reorth_every_rows: int = 0, delta: float = 0.0,
                dtype=np.float64, sync: bool = True, pos0: int = 0, fac: Factor | None = None,
-               callback=None, persist_bf16: bool = False) -> Factor:
+               callback=None, persist_bf16: bool = False, persist_fp16: bool = False) -> Factor:
     """Fold the rows of X block by block (b rows each), in order.
 
     Re-orthogonalises whenever the folded-row counter reaches a multiple of
     ``reorth_every_rows`` (iS-KV notes §4.4; 0 disables it). ``callback`` is
     called after every merge with (merge index, factor). ``persist_bf16``
-    rounds the stored coordinates to bfloat16 after every merge and
-    re-orthogonalisation (persistent 2-byte factors, §7.3).
+    (``persist_fp16``) rounds the stored coordinates to bfloat16 (to half,
+    with the overflow guard) after every merge and re-orthogonalisation
+    (persistent 2-byte factors, §7.3).
     """
+    if persist_bf16 and persist_fp16:
+        raise ValueError("one 2-byte format at a time")
+    persist = persist_coords_bf16 if persist_bf16 else (persist_coords_fp16 if persist_fp16 else None)
     X = np.asarray(X)
     n = X.shape[0]
     if fac is None:
@@ -587,12 +629,12 @@ def run_stream(X: np.ndarray, b: int, r: int, reorth_every_rows: int = 0, delta:
         pos_F = np.arange(pos0 + s, pos0 + s + F.shape[0])
         before = fac.folded
         fac = merge(fac, F, pos_F, r, delta)
-        if persist_bf16:
-            fac = persist_coords_bf16(fac)
+        if persist is not None:
+            fac = persist(fac)
         if reorth_every_rows and sync and (fac.folded // reorth_every_rows) > (before // reorth_every_rows):
             fac = reorth(fac)
-            if persist_bf16:
-                fac = persist_coords_bf16(fac)
+            if persist is not None:
+                fac = persist(fac)
         if callback is not None:
             callback(t, fac)
     return fac

@@ -551,36 +551,42 @@ def test_merge_modes_frozen_basis_and_switches(K, graphs):
     path.close()
 
 
-def test_bf16_coords_persistence(K):
-    """Persistent 2-byte coordinates (notes §7.3, ISKV_BF16_COORDS): rows stored
-    as bf16, products in fp32. The stored history deviates from the fp32 path as
-    much as the oracle's rounding-after-every-write model deviates from fp64, the
-    factor drift of eq.(14) matches that model's, B stays orthonormal, and the
-    reconstruction and factor-aware attention read the 2-byte rows exactly."""
+@pytest.mark.parametrize("fmt", ["bf16", "fp16"])
+def test_2byte_coords_persistence(K, fmt):
+    """Persistent 2-byte coordinates (notes §7.3, ISKV_BF16_COORDS and
+    ISKV_FP16_COORDS): rows stored as bf16 or IEEE half, products in fp32. The
+    stored history deviates from the fp32 path as much as the oracle's
+    rounding-after-every-write model deviates from fp64, the factor drift of
+    eq.(14) matches that model's, B stays orthonormal, no value reaches the
+    fp16 guard, and the reconstruction and factor-aware attention read the
+    2-byte rows exactly."""
     D, r, b, n, hq, hkv = 512, 64, 16, 1024, 16, 4
     X = synth.kv_stream(synth.StreamSpec(D=D, n=n, spectrum="exp40+0.01", noise_std=0.0, seed=23))
     Xd = torch.from_numpy(X).to(DEV)
     posd = torch.arange(n, dtype=torch.int32, device=DEV)
     paths = {}
     for c16 in (False, True):
-        p = K.IsvdPath(D=D, r_max=r, b_max=b, n_cap=n, reorth_every_rows=256, device=DEV, coords_bf16=c16)
+        p = K.IsvdPath(D=D, r_max=r, b_max=b, n_cap=n, reorth_every_rows=256, device=DEV,
+                       coords_bf16=c16 and fmt == "bf16", coords_fp16=c16 and fmt == "fp16")
         for s0 in range(0, n, b):
             p.merge(Xd[s0:s0 + b], posd[s0:s0 + b])
         paths[c16] = p
     torch.cuda.synchronize()
-    assert paths[True].C.dtype == torch.bfloat16
+    assert paths[True].C.dtype == (torch.bfloat16 if fmt == "bf16" else torch.float16)
     Cf, Bf, _, _, st_f = gpu_factors(paths[False])
     Cb, Bb, sb, pb, st_b = gpu_factors(paths[True])
     assert st_f == 0 and st_b == 0
     of = O.represented(O.run_stream(X, b, r, 256))
-    ob = O.represented(O.run_stream(X, b, r, 256, persist_bf16=True))
+    fo = O.run_stream(X, b, r, 256, persist_bf16=fmt == "bf16", persist_fp16=fmt == "fp16")
+    assert not fo.fp16_overflow
+    ob = O.represented(fo)
     dev_gpu, dev_orc = rel(Cb @ Bb.T, Cf @ Bf.T), rel(ob, of)
     dr = {name: O.factor_drift(X, Xh, r) for name, Xh in
-          (("gpu_bf16", Cb @ Bb.T), ("gpu_fp32", Cf @ Bf.T), ("oracle_bf16", ob), ("oracle_fp64", of))}
-    print(f"bf16 coords: deviation from fp32 gpu {dev_gpu:.3e} oracle {dev_orc:.3e}; drift eq.(14) {dr}")
+          (("gpu_2byte", Cb @ Bb.T), ("gpu_fp32", Cf @ Bf.T), ("oracle_2byte", ob), ("oracle_fp64", of))}
+    print(f"{fmt} coords: deviation from fp32 gpu {dev_gpu:.3e} oracle {dev_orc:.3e}; drift eq.(14) {dr}")
     assert 0.5 * dev_orc < dev_gpu < 2.0 * dev_orc
-    assert abs(dr["gpu_bf16"] - dr["oracle_bf16"]) < 0.05 * dr["oracle_bf16"]
-    assert dr["gpu_bf16"] > dr["gpu_fp32"] - 1e-5
+    assert abs(dr["gpu_2byte"] - dr["oracle_2byte"]) < 0.05 * dr["oracle_2byte"]
+    assert dr["gpu_2byte"] > dr["gpu_fp32"] - 1e-5
     assert np.abs(Bb.T @ Bb - np.eye(r)).max() < 1e-4
     # consumers read the stored 2-byte rows exactly
     rec = gpu_recon_fp32(paths[True], n, head_dim=128)
@@ -605,6 +611,65 @@ def test_bf16_coords_persistence(K):
     assert np.abs(o.float().cpu().numpy() - refo).max() < 2e-2
     for p in paths.values():
         p.close()
+
+
+def test_fp16_overflow_guard(K):
+    """The fp16 overflow guard (notes §7.3: half-precision factors passed 65504,
+    became infinite and ended in NaN logits). Rows scaled by 3e4 give
+    coordinates (which carry the singular values) above 65504: every merge,
+    re-orthogonalisation and refit that writes the fp16 store saturates them
+    to +-65504 and latches ISKV_DEV_FP16_OVERFLOW, as the oracle's guarded
+    model reports; nothing stored or reconstructed is infinite. The same rows
+    in bf16 or fp32 storage, and unscaled rows in fp16, raise nothing. In a
+    batch only the path that overflowed reports it."""
+    D, r, b, n = 64, 8, 16, 96
+    X = synth.kv_stream(synth.StreamSpec(D=D, n=n, spectrum="exp4", noise_std=1e-3, seed=44))
+    big = X * 3e4
+    assert O.run_stream(big, b, r, reorth_every_rows=32, persist_fp16=True).fp16_overflow
+    assert not O.run_stream(X, b, r, reorth_every_rows=32, persist_fp16=True).fp16_overflow
+    posd = torch.arange(n, dtype=torch.int32, device=DEV)
+
+    def stream(rows, **kw):
+        p = K.IsvdPath(D=D, r_max=r, b_max=b, n_cap=n, reorth_every_rows=32, device=DEV, **kw)
+        Xd = torch.from_numpy(np.ascontiguousarray(rows)).to(DEV)
+        for s0 in range(0, n, b):
+            p.merge(Xd[s0:s0 + b], posd[s0:s0 + b])
+        torch.cuda.synchronize()
+        return p
+
+    p16 = stream(big, coords_fp16=True)
+    nn, k, st = p16.query()
+    C = p16.C[:nn, :k].float().cpu().numpy()
+    assert st & K.ISKV_DEV_FP16_OVERFLOW and not st & K.ISKV_DEV_NONFINITE, st
+    assert np.all(np.isfinite(C)) and np.abs(C).max() <= 65504.0
+    out = torch.empty((n, D), dtype=torch.bfloat16, device=DEV)
+    p16.reconstruct(out, n, head_dim=64, rope=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    for kw in ({"coords_bf16": True}, {}):
+        p = stream(big, **kw)
+        assert p.query()[2] == 0
+        p.close()
+    p = stream(X, coords_fp16=True)
+    assert p.query()[2] == 0
+    p.close()
+    # the refit writes the store too
+    pr = K.IsvdPath(D=D, r_max=r, b_max=b, n_cap=n, device=DEV, coords_fp16=True)
+    pr.refit(torch.from_numpy(np.ascontiguousarray(big)).to(DEV), posd)
+    torch.cuda.synchronize()
+    assert pr.query()[2] & K.ISKV_DEV_FP16_OVERFLOW
+    pr.close()
+    # batched merges latch per path
+    bat = K.IsvdBatch(2, D=D, r_max=r, b_max=b, n_cap=n, reorth_every_rows=32, device=DEV, coords_fp16=True)
+    Xs = torch.from_numpy(np.stack([X, big])).to(DEV)
+    pz = posd.repeat(2, 1).contiguous()
+    for s0 in range(0, n, b):
+        bat.merge(Xs[:, s0:s0 + b], pz[:, s0:s0 + b])
+    torch.cuda.synchronize()
+    assert bat[0].query()[2] == 0
+    assert bat[1].query()[2] & K.ISKV_DEV_FP16_OVERFLOW
+    bat.close()
+    p16.close()
 
 
 # --------------------------------------------------------------------------- reconstruction

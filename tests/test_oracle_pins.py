@@ -543,6 +543,78 @@ def test_persist_coords_bf16_pins():
     assert O.persist_coords_bf16(half).U[0, 0] == 1.0
 
 
+def test_fp16_round_known_values():
+    """IEEE binary16 (1 sign, 5 exponent, 10 fraction bits): ties go to the even
+    fraction, 2^-24 is the smallest subnormal, 65504 = (2 - 2^-10) 2^15 the
+    largest finite value; the guard stores larger magnitudes as +-65504 and
+    reports them."""
+    vals = np.array([1.0, 1.0 + 2 ** -11, 1.0 + 3 * 2 ** -11, 1.0 + 2 ** -12, -2.5,
+                     2.0 ** -24, 2.0 ** -26, 3 * 2.0 ** -25])
+    got, over = O.fp16_round(vals)
+    assert not over
+    assert got[0] == 1.0 and got[1] == 1.0        # tie between 1 and 1 + 2^-10 -> even
+    assert got[2] == 1.0 + 2 ** -9                # tie between 1 + 2^-10 and 1 + 2^-9 -> even
+    assert got[3] == 1.0 and got[4] == -2.5
+    assert got[5] == 2.0 ** -24 and got[6] == 0.0
+    assert got[7] == 2.0 ** -23                   # subnormal tie -> even
+    g, over = O.fp16_round(np.array([65504.0, -65504.0, 65500.0]))
+    assert not over and g[0] == 65504.0 and g[1] == -65504.0 and g[2] == 65504.0
+    for big in (65505.0, 65519.0, 65520.0, 1e6, 3e38):
+        g, over = O.fp16_round(np.array([1.0, big, -big]))
+        assert over and g[1] == 65504.0 and g[2] == -65504.0 and g[0] == 1.0
+    g, over = O.fp16_round(np.array([np.nan, 2.0]))
+    assert not over and np.isnan(g[0]) and g[1] == 2.0
+    # without the guard a value past 65520 would round to an infinity
+    with np.errstate(over="ignore"):
+        assert np.isinf(np.float32(65520.0).astype(np.float16))
+
+
+def test_persist_coords_fp16_pins():
+    """Persistent fp16 coordinates (notes §7.3): the stored C = U diag(sigma) is
+    exactly half-representable, entries move by at most 2^-11 relative (11
+    significant bits) above the subnormal range, sigma and B are untouched; a
+    coordinate above 65504 in magnitude is saturated, the factor stays finite
+    and flagged, and the flag is sticky through later merges and
+    re-orthogonalisations of a stream."""
+    rng = np.random.default_rng(43)
+    n, k, D = 30, 6, 20
+    U, _ = np.linalg.qr(rng.standard_normal((n, k)))
+    B, _ = np.linalg.qr(rng.standard_normal((D, k)))
+    sigma = np.array([900.0, 70.0, 3.0, 1.0, 0.25, 0.0])
+    fac = O.Factor(U=U, sigma=sigma, B=B, pos=np.arange(n))
+    p = O.persist_coords_fp16(fac)
+    C = fac.U * fac.sigma[None, :]
+    Cp = p.U * p.sigma[None, :]
+    assert not p.fp16_overflow
+    assert np.all(np.abs(O.fp16_round(Cp)[0] - Cp) <= 1e-14 * np.abs(Cp))
+    normal = np.abs(C) >= 2.0 ** -14
+    assert np.all(np.abs(Cp - C)[normal] <= 2.0 ** -11 * np.abs(C)[normal])
+    assert np.all(np.abs(Cp - C)[~normal] <= 2.0 ** -25)
+    assert np.array_equal(p.sigma, fac.sigma) and np.array_equal(p.B, fac.B)
+    assert np.all(p.U[:, 5] == 0)
+    # sigma_1 = 2e5 on a column whose largest entry is ~0.6: C passes 65504
+    big = O.Factor(U=U, sigma=np.array([2e5, 70.0, 3.0, 1.0, 0.25, 0.0]), B=B, pos=np.arange(n))
+    pb = O.persist_coords_fp16(big)
+    Cb = pb.U * pb.sigma[None, :]
+    assert pb.fp16_overflow and np.all(np.isfinite(Cb))
+    hit = np.abs(U[:, 0] * 2e5) > 65504.0
+    # (U is held as C / sigma: multiplying back leaves fp64 rounding only)
+    assert hit.any() and np.allclose(np.abs(Cb[hit, 0]), 65504.0, rtol=1e-14, atol=0)
+    assert np.all(np.sign(Cb[hit, 0]) == np.sign(U[hit, 0]))
+    # a stream of large rows: the fp16 path saturates and reports, stays finite
+    # and keeps reporting; bf16 (8 exponent bits) holds the same values
+    X = synth.kv_stream(synth.StreamSpec(D=64, n=96, spectrum="exp4", noise_std=1e-3, seed=44)) * 3e4
+    f16 = O.run_stream(X, 16, 8, reorth_every_rows=32, persist_fp16=True)
+    assert f16.fp16_overflow and np.all(np.isfinite(f16.U * f16.sigma[None, :]))
+    assert np.abs(f16.U * f16.sigma[None, :]).max() <= 65504.0 * (1 + 1e-12)
+    f16b = O.run_stream(X, 16, 8, reorth_every_rows=32, persist_bf16=True)
+    assert not f16b.fp16_overflow and np.abs(f16b.U * f16b.sigma[None, :]).max() > 65504.0
+    small = O.run_stream(X / 3e4, 16, 8, reorth_every_rows=32, persist_fp16=True)
+    assert not small.fp16_overflow
+    with pytest.raises(ValueError):
+        O.run_stream(X, 16, 8, persist_bf16=True, persist_fp16=True)
+
+
 # --------------------------------------------------------------------------- prompt protection
 def test_anomaly_scores_and_protect_pins():
     """Algorithm 1 (notes §3.1): a block of equal keys scores 1, one
