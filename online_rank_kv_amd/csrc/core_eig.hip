@@ -24,14 +24,19 @@
 // in PCJ_MAXIT steps (strongly mixed early merges) fall back to the
 // single-workgroup cyclic Jacobi.
 //
-// Tolerance. isvd_sym_eig asks for eigenvectors to 1e-10. A merge only needs
-// the product C B^T: rotations among kept directions leave it unchanged, and
-// a coupling c left between a kept and a dropped direction changes it by
-// about c relative, as does a coupling among kept directions through the
-// stored sigma (the next merge takes C^T C as diagonal). Merges and
-// re-orthogonalisations therefore stop at 1e-8, far below the fp32 rounding
-// the factors carry (on the 16K-row K and V streams this saves one step in
-// most merges and leaves the reconstruction error unchanged).
+// Tolerance. isvd_sym_eig asks for eigenvectors to 1e-10 in the scaled
+// coupling |s_ij| / sqrt(s_ii s_jj), which holds the smallest eigenvectors to
+// the same relative accuracy as the largest. A merge only needs the product
+// C B^T: rotations among kept directions leave it unchanged, and a rotation
+// left between a kept and a dropped direction, or among kept directions
+// through the stored sigma (the next merge takes C^T C as diagonal), moves
+// it by about |s_ij| / sqrt(max(s_ii, s_jj) s_max) relative to its largest
+// singular value (coupling_at). Merges and re-orthogonalisations stop when
+// that measure is below 1e-8, far below the fp32 rounding the factors carry.
+// On the 16K-row K and V streams the scaled measure is held up for two more
+// steps by pairs between a large direction and one of the smallest ones
+// (scaled coupling ~3e-3 after the first step where the product measure is
+// ~1e-5), which do not change the product.
 #include "iskv_internal.h"
 
 #include <math.h>
@@ -65,6 +70,9 @@ constexpr int FLAG_COLD = 4;     // the fallback starts from A itself
 // mode 1: when converged, copy Cin (the current W) to C instead.
 // mode 2: always run.
 // mode 3: run only when the refinement has not converged.
+// mode 4 (paired products): skip when it converged at a step >= 1, whose W
+//   and A W are already orthonormalised and formed (run after step 0 or
+//   without convergence).
 typedef double v4d __attribute__((ext_vector_type(4)));
 // Branch-free masking of a loaded value: the bits are ANDed with 0 or
 // all-ones, so the load itself is never placed under a branch and every load
@@ -196,6 +204,42 @@ __device__ __forceinline__ double coupling(double sij, double di, double dj) {
   return a > 0.0 ? INFINITY : 0.0;
 }
 
+// The coupling a step measures. With sref = 0: the scaled coupling above,
+// which asks every eigenvector, the smallest included, for the tolerance
+// (isvd_sym_eig, the refit). With sref > 0 (the largest diagonal entry of the
+// matrix being solved; merges and re-orthogonalisations) it measures how far
+// the pair's remaining rotation moves the represented product, relative to
+// its largest singular value sigma_1 = sqrt(sref):
+//   * directions on the same side of the truncation (both kept or both
+//     dropped): a rotation between them leaves the product unchanged, and
+//     the coupling itself, dropped from the stored sigma (the next merge
+//     takes C^T C as diagonal), moves it by
+//       |s_ij| / sqrt(max(|s_ii|, |s_jj|) sref);
+//   * a kept and a dropped direction (diagonal values on both sides of dcut,
+//     or both within a factor 2 of it, where the final order is not yet
+//     settled): the rotation angle min(1, |s_ij| / |s_jj - s_ii|) weighted by
+//     sqrt(max(|s_ii|, |s_jj|) / sref), the larger of the two.
+// dcut < 0: nothing is dropped. A pair of one large and one of the smallest
+// directions then counts by sigma_j / sigma_1 less than its scaled coupling,
+// so such pairs no longer hold a merge's core for extra steps, while a
+// near-tie across the truncation still has to be resolved.
+__device__ __forceinline__ double coupling_at(double sij, double di, double dj, double sref, double dcut) {
+  if (!(sref > 0.0)) return coupling(sij, di, dj);
+  if (!isfinite(sij) || !isfinite(di) || !isfinite(dj)) return INFINITY;
+  const double a = fabs(sij);
+  if (a == 0.0) return 0.0;
+  const double dm = fmax(fabs(di), fabs(dj));
+  double c = a / sqrt(dm * sref);
+  if (dcut >= 0.0) {
+    const bool across = (di > dcut) != (dj > dcut) ||
+                        (di > 0.5 * dcut && di < 2.0 * dcut && dj > 0.5 * dcut && dj < 2.0 * dcut);
+    if (across) c = fmax(c, fmin(1.0, a / fabs(dj - di)) * sqrt(dm / sref));
+  }
+  return c;
+}
+__device__ __forceinline__ double coupling_ref(const int32_t* st) { return (double)__int_as_float(st[ST_SREF]); }
+__device__ __forceinline__ double coupling_cut(const int32_t* st) { return (double)__int_as_float(st[ST_DCUT]); }
+
 // Two products that share the right operand, one 16 x 16 tile of each per
 // workgroup (the right-operand panel is loaded once):
 //   C1 = alpha1 op(A1) B + beta1 Cin1,   C2 = alpha2 op(A2) B + beta2 Cin2
@@ -229,6 +273,7 @@ __global__ __launch_bounds__(64 * NW) void dgemm2_kernel(const double* __restric
   if (i0 >= m || j0 >= m) return;
   const bool conv = (st[ST_PCJ] & FLAG_CONV) != 0;
   if (mode == 0 && conv) return;
+  if (mode == 4 && conv && st[ST_PCJIT] > 0) return;
   if (mode == 1 && conv) {
     if (t < 256) {
       const int i = i0 + (t >> 4), j = j0 + (t & 15);
@@ -342,6 +387,7 @@ __global__ __launch_bounds__(256) void dgemm_s_kernel(const double* __restrict__
   const int r = lane & 15, g = lane >> 4;
   const int m = st[ST_JM];
   const bool conv = (st[ST_PCJ] & FLAG_CONV) != 0;
+  const double sref = coupling_ref(st), dcut = coupling_cut(st);
   // S is symmetric: tiles below the diagonal are written by their mirror
   if (i0 >= m || j0 >= m || conv || j0 < i0) {
     if (t == 0) aux[tile] = 0.0;
@@ -403,7 +449,7 @@ __global__ __launch_bounds__(256) void dgemm_s_kernel(const double* __restrict__
       S[(size_t)i * ld + j] = o;
       S[(size_t)j * ld + i] = o;  // the mirror (the same value: S exactly symmetric)
       if (j > i) {
-        const double c = coupling(o, dii, dj);
+        const double c = coupling_at(o, dii, dj, sref, dcut);
         cmax = fmax(cmax, c);
         if (c > tol && fabs(o) > PCJ_OMEGA * fabs(dj - dii)) {
           const int slot = atomicAdd(&st[ST_NEDGE], 1);
@@ -590,6 +636,7 @@ __global__ __launch_bounds__(256) void bgemm2_kernel(const double* __restrict__ 
   if (i0 >= m || j0 >= m) return;
   const bool conv = (st[ST_PCJ] & FLAG_CONV) != 0;
   if (mode == 0 && conv) return;
+  if (mode == 4 && conv && st[ST_PCJIT] > 0) return;
   if (mode == 1 && conv) {
     for (int e = t; e < BT * BT; e += 256) {
       const int i = i0 + e / BT, j = j0 + e % BT;
@@ -655,6 +702,7 @@ __global__ __launch_bounds__(256) void bgemm_s_kernel(const double* __restrict__
   const int r = lane & 15, g = lane >> 4, wr = wave >> 1, wc = wave & 1;
   const int m = st[ST_JM];
   const bool conv = (st[ST_PCJ] & FLAG_CONV) != 0;
+  const double sref = coupling_ref(st), dcut = coupling_cut(st);
   // S is symmetric: tiles below the diagonal are written by their mirror
   if (i0 >= m || j0 >= m || conv || j0 < i0) {
     // every sub-tile maximum of this tile is 0
@@ -692,7 +740,7 @@ __global__ __launch_bounds__(256) void bgemm_s_kernel(const double* __restrict__
           S[(size_t)i * ld + j] = o;
           S[(size_t)j * ld + i] = o;
           if (j > i) {
-            const double c = coupling(o, dii, dj);
+            const double c = coupling_at(o, dii, dj, sref, dcut);
             cmax = fmax(cmax, c);
             if (c > tol && fabs(o) > PCJ_OMEGA * fabs(dj - dii)) {
               const int slot = atomicAdd(&st[ST_NEDGE], 1);
@@ -759,7 +807,7 @@ void gemm_s(hipStream_t s, int m_max, const double* W, const double* T, int ld, 
 
 // S = A, W = I, flags cleared.
 __global__ __launch_bounds__(256) void pcj_init_kernel(const double* __restrict__ A, double* S,
-                                                       double* W, int ld, int32_t* st,
+                                                       double* W, int ld, int32_t* st, int keep,
     const int64_t* __restrict__ bd) {
   const int64_t bdel = bd ? bd[blockIdx.z] : 0;
   A = iskv_rb(A, bdel);
@@ -767,6 +815,59 @@ __global__ __launch_bounds__(256) void pcj_init_kernel(const double* __restrict_
   W = iskv_rb(W, bdel);
   st = iskv_rb(st, bdel);
   const int m = st[ST_JM];
+  if (blockIdx.x == 0) {
+    // coupling scale (the largest diagonal entry) and cut (between the
+    // keep-th and (keep+1)-th largest diagonal entries, geometric mean),
+    // rounded to fp32; read by later launches only. keep < 0: scaled
+    // couplings; keep >= m: nothing dropped.
+    __shared__ double dl[1024];
+    __shared__ double red[3][4];
+    double dmax = 0.0;
+    for (int i = threadIdx.x; i < m; i += 256) {
+      dl[i] = fabs(A[(size_t)i * ld + i]);
+      dmax = fmax(dmax, dl[i]);
+    }
+    __syncthreads();
+    // the keep-th largest value (hi) and the next one down (lo), by counting
+    double hi = INFINITY, lo = 0.0;
+    if (keep >= 0 && keep < m) {
+      for (int i = threadIdx.x; i < m; i += 256) {
+        const double v = dl[i];
+        int above = 0;
+        for (int j = 0; j < m; ++j) above += dl[j] > v;
+        if (above < keep) hi = fmin(hi, v);
+        else lo = fmax(lo, v);
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      dmax = fmax(dmax, __shfl_xor(dmax, o, 64));
+      hi = fmin(hi, __shfl_xor(hi, o, 64));
+      lo = fmax(lo, __shfl_xor(lo, o, 64));
+    }
+    if ((threadIdx.x & 63) == 0) {
+      red[0][threadIdx.x >> 6] = dmax;
+      red[1][threadIdx.x >> 6] = hi;
+      red[2][threadIdx.x >> 6] = lo;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      dmax = fmax(fmax(red[0][0], red[0][1]), fmax(red[0][2], red[0][3]));
+      hi = fmin(fmin(red[1][0], red[1][1]), fmin(red[1][2], red[1][3]));
+      lo = fmax(fmax(red[2][0], red[2][1]), fmax(red[2][2], red[2][3]));
+      auto up = [](double x) {
+        const float f = (float)x;
+        return (double)f < x ? __int_as_float(__float_as_int(f) + 1) : f;
+      };
+      const float fu = up(dmax);
+      const bool prod = keep >= 0 && isfinite(fu) && fu > 0.f;
+      st[ST_SREF] = prod ? __float_as_int(fu) : 0;
+      // equal values on both sides of the cut (hi == lo) leave it at that
+      // value: the pair then counts as across (both within a factor 2)
+      const double cut = (keep >= 0 && keep < m && isfinite(hi)) ? sqrt(hi * lo) : -1.0;
+      st[ST_DCUT] = __float_as_int(prod && cut >= 0.0 ? (float)cut : -1.f);
+    }
+  }
   const size_t total = (size_t)m * m;
   for (size_t e = blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
     int i = (int)(e / m), j = (int)(e % m);
@@ -831,6 +932,7 @@ __global__ __launch_bounds__(256) void pcj_detect_kernel(const double* __restric
   st = iskv_rb(st, bdel);
   if (st[ST_PCJ] & FLAG_CONV) return;
   const int m = st[ST_JM];
+  const double sref = coupling_ref(st), dcut = coupling_cut(st);
   const int r0 = blockIdx.x * 16;
   __shared__ double red[4];
   double cmax = 0.0;
@@ -841,7 +943,7 @@ __global__ __launch_bounds__(256) void pcj_detect_kernel(const double* __restric
       if (j <= i) continue;
       double sij = S[(size_t)i * ld + j];
       double di = S[(size_t)i * ld + i], dj = S[(size_t)j * ld + j];
-      double c = coupling(sij, di, dj);
+      double c = coupling_at(sij, di, dj, sref, dcut);
       if (c > cmax) cmax = c;
       if (c > tol && fabs(sij) > PCJ_OMEGA * fabs(dj - di)) {
         int slot = atomicAdd(&st[ST_NEDGE], 1);
@@ -1120,13 +1222,15 @@ __global__ __launch_bounds__(256) void pcj_kmat_kernel(const double* __restrict_
 // not imply it (inside a cluster of nearly equal eigenvalues the columns can
 // drift towards each other while the couplings stay small). T = W^T W of the
 // W before its final Newton-Schulz step: any |T - I| above thr withdraws the
-// convergence and marks the fallback cold (ST_ROUNDS = 1). Grid-stride.
+// convergence and marks the fallback cold (ST_ROUNDS = 1). Without
+// convergence the same test keeps the fallback from continuing from a W that
+// is not orthonormal (cold instead of warm). Grid-stride.
 __global__ __launch_bounds__(256) void pcj_orth_check_kernel(const double* __restrict__ T, int ld, int32_t* st,
                                                              double thr, const int64_t* __restrict__ bd) {
   const int64_t bdel = bd ? bd[blockIdx.z] : 0;
   T = iskv_rb(T, bdel);
   st = iskv_rb(st, bdel);
-  if (!(st[ST_PCJ] & FLAG_CONV)) return;
+  const bool conv = (st[ST_PCJ] & FLAG_CONV) != 0;
   const int m = st[ST_JM];
   const size_t tot = (size_t)m * m;
   bool bad = false;
@@ -1136,24 +1240,29 @@ __global__ __launch_bounds__(256) void pcj_orth_check_kernel(const double* __res
     bad |= !(fabs(v) <= thr);
   }
   if (bad) {
-    atomicAnd(&st[ST_PCJ], ~FLAG_CONV);
+    if (conv) atomicAnd(&st[ST_PCJ], ~FLAG_CONV);
     st[ST_ROUNDS] = 1;
   }
 }
 
 // Eigenvalues lambda_i = w_i^T (A w_i) from T = A W; V = W when converged.
+// W is Wo, the last step's orthonormalised iterate, when the refinement
+// converged at a step >= 1 (the final paired products were skipped), else Wf
+// from the final Newton-Schulz step.
 // Otherwise the Jacobi fallback takes over: when the last step's couplings
 // (aux, nmx maxima) are all finite and below 0.05, it continues from
 // S = Wf^T A Wf (formed by the launch before) and V = Wf, nearly diagonal so
 // that a few sweeps finish it; else it starts from S = A, V = I (FLAG_COLD).
 // Grid (m).
-__global__ __launch_bounds__(256) void pcj_final_kernel(const double* __restrict__ Wf,
+__global__ __launch_bounds__(256) void pcj_final_kernel(const double* __restrict__ Wo,
+                                                        const double* __restrict__ Wf,
                                                         const double* __restrict__ T,
                                                         const double* __restrict__ A, double* S,
                                                         double* V, int ld, const double* __restrict__ aux,
                                                         int nmx, int32_t* st,
     const int64_t* __restrict__ bd) {
   const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  Wo = iskv_rb(Wo, bdel);
   Wf = iskv_rb(Wf, bdel);
   aux = iskv_rb(aux, bdel);
   T = iskv_rb(T, bdel);
@@ -1167,9 +1276,10 @@ __global__ __launch_bounds__(256) void pcj_final_kernel(const double* __restrict
   const bool conv = (st[ST_PCJ] & FLAG_CONV) != 0;
   __shared__ double red[4];
   if (conv) {
+    const double* Wv = st[ST_PCJIT] > 0 ? Wo : Wf;
     double acc = 0.0;
     for (int r = threadIdx.x; r < m; r += 256) {
-      double w = Wf[(size_t)r * ld + j];
+      double w = Wv[(size_t)r * ld + j];
       acc = fma(w, T[(size_t)r * ld + j], acc);
       V[(size_t)r * ld + j] = w;
     }
@@ -1600,7 +1710,7 @@ int iskv_core_eig_setup() {
 // Eigen-decompose the m x m matrix in w.A (m = st[ST_JM]): on return the
 // diagonal of w.S holds the eigenvalues and w.V the eigenvectors (columns),
 // unsorted. Fixed launch sequence; no host synchronisation.
-int iskv_launch_core_eig(isvd_handle* h, double tol) {
+int iskv_launch_core_eig(isvd_handle* h, double tol, int keep) {
   const isvd_ws& w = h->w;
   hipStream_t s = h->stream;
   const int mm = h->m_max, ld = h->ldm;
@@ -1638,7 +1748,8 @@ int iskv_launch_core_eig(isvd_handle* h, double tol) {
     ISKV_HIP_CHECK(hipGetLastError());
     return ISKV_OK;
   }
-  hipLaunchKernelGGL(pcj_init_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.A, w.S, w.W0, ld, st, h->bd);
+  hipLaunchKernelGGL(pcj_init_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.A, w.S, w.W0, ld, st, keep,
+                     h->bd);
   // step 0 works on S = A with W = I
   hipLaunchKernelGGL(pcj_detect_kernel, bz(dim3(nblk), h->bcount), dim3(256), 0, s, w.S, ld, w.aux, w.edges, st,
                      tol, h->bd);
@@ -1674,15 +1785,17 @@ int iskv_launch_core_eig(isvd_handle* h, double tol) {
     gemm<false, false>(s, mm, w.Km, w.Pa, w.Pb, nullptr, ld, 1.0, 0.0, 1.0, st, 0, h->bd, h->bcount);
     gemm<false, false>(s, mm, wo, w.Pb, wc, wo, ld, 1.0, 0.0, 0.0, st, 1, h->bd, h->bcount);
   }
-  // final Newton-Schulz of W (in wo) into wc, with A W for the eigenvalues
-  gemm2<true, true>(s, mm, wo, w.A, wo, ld, w.T, w.Km, nullptr, nullptr, 1.0, 0.0, 1.0, 0.0, nullptr, st, 2, h->bd,
+  // final Newton-Schulz of W (in wo) into wc, with A W for the eigenvalues;
+  // skipped after convergence at a step >= 1, where wo is already
+  // orthonormalised and Pa = A wo (T keeps W^T W of the W before it)
+  gemm2<true, true>(s, mm, wo, w.A, wo, ld, w.T, w.Km, nullptr, nullptr, 1.0, 0.0, 1.0, 0.0, nullptr, st, 4, h->bd,
                     h->bcount);
-  gemm2<false, false>(s, mm, wo, w.Km, w.T, ld, wc, w.Pa, wo, w.Km, -0.5, 1.5, -0.5, 1.5, nullptr, st, 2, h->bd,
+  gemm2<false, false>(s, mm, wo, w.Km, w.T, ld, wc, w.Pa, wo, w.Km, -0.5, 1.5, -0.5, 1.5, nullptr, st, 4, h->bd,
                       h->bcount);
   hipLaunchKernelGGL(pcj_orth_check_kernel, bz(dim3(64), h->bcount), dim3(256), 0, s, w.T, ld, st, 1e-4, h->bd);
   // S = W^T A W of the final W, used only by a fallback that continues from it
   gemm<true, false>(s, mm, wc, w.Pa, w.S, nullptr, ld, 1.0, 0.0, 0.0, st, 3, h->bd, h->bcount);
-  hipLaunchKernelGGL(pcj_final_kernel, bz(dim3(mm), h->bcount), dim3(256), 0, s, wc, w.Pa, w.A, w.S, w.V, ld,
+  hipLaunchKernelGGL(pcj_final_kernel, bz(dim3(mm), h->bcount), dim3(256), 0, s, wo, wc, w.Pa, w.A, w.S, w.V, ld,
                      w.aux, nblk * nblk, st, h->bd);
   if (!bj_fits || mm <= BJ_MIN_M) {
     hipLaunchKernelGGL(core_jacobi_kernel, bz(dim3(1), h->bcount), dim3(1024), 0, s, w.S, w.V, ld, st, 1e-13,

@@ -28,7 +28,9 @@ enum {
   ST_PCJIT = 12,   // refinement steps used by the last core eigensolve
   ST_NEDGE = 13,   // strong pairs found by the current detection pass
   ST_RSWEEPS = 14, // Jacobi sweeps of the last residual eigensolve
-  ST_COUNT = 16
+  ST_SREF = 15,    // core eigensolver: fp32 bits of max_i A_ii (coupling scale), 0 = scaled couplings
+  ST_DCUT = 16,    // core eigensolver: fp32 bits of the diagonal value between kept and dropped, < 0 = none
+  ST_COUNT = 20
 };
 
 // Sub-buffers carved out of the caller's workspace (all 256-byte aligned).
@@ -144,8 +146,13 @@ inline int iskv_core_ld(int m_max) { return (m_max + ISKV_DGEMM_KP - 1) / ISKV_D
 // ---- launch helpers implemented in the kernel translation units ----
 int iskv_kernel_setup();
 int iskv_core_eig_setup();
-// Core eigensolver on w.A; stops when every scaled coupling is below tol.
-int iskv_launch_core_eig(isvd_handle* h, double tol);
+// Core eigensolver on w.A; stops when every coupling is below tol: the
+// scaled coupling (every eigenvector to tol) when keep < 0, else the
+// coupling's effect on the represented product (merges keep = r_max, the
+// re-orthogonalisation keeps everything: ISKV_EIG_KEEP_ALL).
+constexpr int ISKV_EIG_SCALED = -1;
+constexpr int ISKV_EIG_KEEP_ALL = 0x7fffffff;
+int iskv_launch_core_eig(isvd_handle* h, double tol, int keep = ISKV_EIG_SCALED);
 #define ISKV_EIG_TOL_EXACT 1e-10   // isvd_sym_eig
 #define ISKV_EIG_TOL_UPDATE 1e-8   // merges and re-orthogonalisations
 void iskv_dgemm(hipStream_t s, int m_max, const double* A, bool ta, const double* B, bool tb, double* C,

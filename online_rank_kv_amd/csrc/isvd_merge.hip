@@ -1436,7 +1436,7 @@ static int merge_body(isvd_handle* h, const float* F, const int32_t* pos_F, int3
   }
   hipLaunchKernelGGL(set_jm_kernel, bz(dim3(1), h->bcount), dim3(1), 0, s, w.st, (int)ST_M, h->bd);
   {
-    int rc = iskv_launch_core_eig(h, ISKV_EIG_TOL_UPDATE);
+    int rc = iskv_launch_core_eig(h, ISKV_EIG_TOL_UPDATE, c.r_max);
     if (rc) return rc;
   }
   eig_finish(h, 1);
@@ -1518,7 +1518,7 @@ static int reorth_body(isvd_handle* h) {
   iskv_dgemm(s, mm, w.MB, false, w.Km, false, w.T, nullptr, ld, 1.0, 0.0, 0.0, st, 2, h->bd, h->bcount);
   iskv_dgemm(s, mm, w.T, false, w.MB, true, w.A, nullptr, ld, 1.0, 0.0, 0.0, st, 2, h->bd, h->bcount);
   {
-    int rc = iskv_launch_core_eig(h, ISKV_EIG_TOL_UPDATE);
+    int rc = iskv_launch_core_eig(h, ISKV_EIG_TOL_UPDATE, ISKV_EIG_KEEP_ALL);
     if (rc) return rc;
   }
   eig_finish(h, 0);
