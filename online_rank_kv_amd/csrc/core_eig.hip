@@ -44,7 +44,7 @@
 namespace {
 
 #ifndef ISKV_PCJ_MAXIT
-#define ISKV_PCJ_MAXIT 7
+#define ISKV_PCJ_MAXIT 6
 #endif
 constexpr int PCJ_MAXIT = ISKV_PCJ_MAXIT;
 constexpr double PCJ_OMEGA = 0.1;
@@ -57,6 +57,7 @@ constexpr int NPAIR_MAX = 512; // matched pairs per step
 constexpr int FLAG_CONV = 1;
 constexpr int FLAG_FALLBACK = 2;
 constexpr int FLAG_COLD = 4;     // the fallback starts from A itself
+constexpr int FLAG_NS = 16;      // converged, but W needs the final Newton-Schulz step
 
 // ----------------------------------------------------------------------------
 // C = alpha * opA(A) opB(B) + beta * Cin + gamma * I, all m x m (m from
@@ -70,9 +71,10 @@ constexpr int FLAG_COLD = 4;     // the fallback starts from A itself
 // mode 1: when converged, copy Cin (the current W) to C instead.
 // mode 2: always run.
 // mode 3: run only when the refinement has not converged.
-// mode 4 (paired products): skip when it converged at a step >= 1, whose W
-//   and A W are already orthonormalised and formed (run after step 0 or
-//   without convergence).
+// mode 4 (paired products): skip when it converged at a step >= 1 whose W,
+//   already orthonormalised with A W formed, came from an iterate within
+//   1e-4 of orthonormal (FLAG_NS clear); run after step 0, without
+//   convergence, or with FLAG_NS.
 typedef double v4d __attribute__((ext_vector_type(4)));
 // Branch-free masking of a loaded value: the bits are ANDed with 0 or
 // all-ones, so the load itself is never placed under a branch and every load
@@ -216,8 +218,8 @@ __device__ __forceinline__ double coupling(double sij, double di, double dj) {
 //     takes C^T C as diagonal), moves it by
 //       |s_ij| / sqrt(max(|s_ii|, |s_jj|) sref);
 //   * a kept and a dropped direction (diagonal values on both sides of dcut,
-//     or both within a factor 2 of it, where the final order is not yet
-//     settled): the rotation angle min(1, |s_ij| / |s_jj - s_ii|) weighted by
+//     between the keep-th and (keep+1)-th largest diagonal entries of the
+//     matrix): the rotation angle min(1, |s_ij| / |s_jj - s_ii|) weighted by
 //     sqrt(max(|s_ii|, |s_jj|) / sref), the larger of the two.
 // dcut < 0: nothing is dropped. A pair of one large and one of the smallest
 // directions then counts by sigma_j / sigma_1 less than its scaled coupling,
@@ -230,11 +232,7 @@ __device__ __forceinline__ double coupling_at(double sij, double di, double dj, 
   if (a == 0.0) return 0.0;
   const double dm = fmax(fabs(di), fabs(dj));
   double c = a / sqrt(dm * sref);
-  if (dcut >= 0.0) {
-    const bool across = (di > dcut) != (dj > dcut) ||
-                        (di > 0.5 * dcut && di < 2.0 * dcut && dj > 0.5 * dcut && dj < 2.0 * dcut);
-    if (across) c = fmax(c, fmin(1.0, a / fabs(dj - di)) * sqrt(dm / sref));
-  }
+  if (dcut >= 0.0 && (di > dcut) != (dj > dcut)) c = fmax(c, fmin(1.0, a / fabs(dj - di)) * sqrt(dm / sref));
   return c;
 }
 __device__ __forceinline__ double coupling_ref(const int32_t* st) { return (double)__int_as_float(st[ST_SREF]); }
@@ -273,7 +271,7 @@ __global__ __launch_bounds__(64 * NW) void dgemm2_kernel(const double* __restric
   if (i0 >= m || j0 >= m) return;
   const bool conv = (st[ST_PCJ] & FLAG_CONV) != 0;
   if (mode == 0 && conv) return;
-  if (mode == 4 && conv && st[ST_PCJIT] > 0) return;
+  if (mode == 4 && conv && st[ST_PCJIT] > 0 && !(st[ST_PCJ] & FLAG_NS)) return;
   if (mode == 1 && conv) {
     if (t < 256) {
       const int i = i0 + (t >> 4), j = j0 + (t & 15);
@@ -636,7 +634,7 @@ __global__ __launch_bounds__(256) void bgemm2_kernel(const double* __restrict__ 
   if (i0 >= m || j0 >= m) return;
   const bool conv = (st[ST_PCJ] & FLAG_CONV) != 0;
   if (mode == 0 && conv) return;
-  if (mode == 4 && conv && st[ST_PCJIT] > 0) return;
+  if (mode == 4 && conv && st[ST_PCJIT] > 0 && !(st[ST_PCJ] & FLAG_NS)) return;
   if (mode == 1 && conv) {
     for (int e = t; e < BT * BT; e += 256) {
       const int i = i0 + e / BT, j = j0 + e % BT;
@@ -863,7 +861,7 @@ __global__ __launch_bounds__(256) void pcj_init_kernel(const double* __restrict_
       const bool prod = keep >= 0 && isfinite(fu) && fu > 0.f;
       st[ST_SREF] = prod ? __float_as_int(fu) : 0;
       // equal values on both sides of the cut (hi == lo) leave it at that
-      // value: the pair then counts as across (both within a factor 2)
+      // value, and neither counts as above it
       const double cut = (keep >= 0 && keep < m && isfinite(hi)) ? sqrt(hi * lo) : -1.0;
       st[ST_DCUT] = __float_as_int(prod && cut >= 0.0 ? (float)cut : -1.f);
     }
@@ -979,14 +977,15 @@ struct AnalyzeLds {
 // convergence test, clusters of strongly coupled indices (components of the
 // strong-pair graph), exact rotations (small clusters: cyclic Jacobi; big
 // ones: 2x2 rotations on a greedy matching), applied to S and W in place.
-__global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W, int ld,
-                                                           const double* __restrict__ aux, int nmx,
+__global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W, const double* __restrict__ T,
+                                                           int ld, const double* __restrict__ aux, int nmx,
                                                            const int* __restrict__ edges,
                                                            int32_t* st, int it, double tol,
     const int64_t* __restrict__ bd) {
   const int64_t bdel = bd ? bd[blockIdx.z] : 0;
   S = iskv_rb(S, bdel);
   W = iskv_rb(W, bdel);
+  T = iskv_rb(T, bdel);
   aux = iskv_rb(aux, bdel);
   edges = iskv_rb(edges, bdel);
   st = iskv_rb(st, bdel);
@@ -1010,16 +1009,25 @@ __global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W,
   __syncthreads();
   const double cmax = L.cmax;
   if (cmax < tol) {  // NaN couplings never pass: they end in the fallback
-    __syncthreads();
-    if (t == 0) { st[ST_PCJ] |= FLAG_CONV; st[ST_PCJIT] = it; st[ST_NEDGE] = 0; }
+    // from step 1 on, T = W^T W of the iterate behind this step's
+    // orthonormalised W: a defect above 1e-4 asks for the final
+    // Newton-Schulz step (FLAG_NS) before W is used
+    bool bad = false;
+    if (it > 0)
+      for (int e = t; e < m * m; e += nt) {
+        const int i = e / m, j = e % m;
+        bad |= !(fabs(T[(size_t)i * ld + j] - (i == j ? 1.0 : 0.0)) <= 1e-4);
+      }
+    bad = __syncthreads_or(bad);
+    if (t == 0) { st[ST_PCJ] |= FLAG_CONV | (bad ? FLAG_NS : 0); st[ST_PCJIT] = it; st[ST_NEDGE] = 0; }
     return;
   }
   const int ne = L.nedge;
+  for (int i = t; i < m; i += nt) L.d[i] = S[(size_t)i * ld + i];
   if (ne == 0) {  // no strongly coupled pair: the first-order angles do everything
     if (t == 0) { st[ST_NEDGE] = 0; st[ST_PCJIT] = it + 1; }
     return;
   }
-  for (int i = t; i < m; i += nt) L.d[i] = S[(size_t)i * ld + i];
   for (int e = t; e < ne; e += nt) L.key[e] = edges[2 * e] * 1024 + edges[2 * e + 1];
   for (int i = t; i < m; i += nt) { L.lab[i] = i; L.size[i] = 0; L.used[i] = 0; L.cid[i] = -1; }
   __syncthreads();
@@ -1276,7 +1284,7 @@ __global__ __launch_bounds__(256) void pcj_final_kernel(const double* __restrict
   const bool conv = (st[ST_PCJ] & FLAG_CONV) != 0;
   __shared__ double red[4];
   if (conv) {
-    const double* Wv = st[ST_PCJIT] > 0 ? Wo : Wf;
+    const double* Wv = (st[ST_PCJIT] > 0 && !(st[ST_PCJ] & FLAG_NS)) ? Wo : Wf;
     double acc = 0.0;
     for (int r = threadIdx.x; r < m; r += 256) {
       double w = Wv[(size_t)r * ld + j];
@@ -1411,6 +1419,12 @@ constexpr int BJ_LD = BJ_P + 1;   // LDS row stride (doubles)
 // otherwise carry the block Jacobi's ~1000 (mostly idle) launches.
 constexpr int BJ_MIN_M = 384;
 constexpr int BJ_SWEEPS = 32;
+// Merges and re-orthogonalisations: the block Jacobi behind the refinement
+// starts from the refinement's W when that is orthonormal and nearly
+// converged, and needs at most 4 sweeps (cold) on the 64K-row r = 384 / 512
+// streams; a recorded merge carries every sweep's launches, idle or not, so
+// the budget is 12 rather than the dense solve's 32.
+constexpr int BJ_SWEEPS_MERGE = 12;
 #ifndef ISKV_BJ_INNER
 #define ISKV_BJ_INNER 1
 #endif
@@ -1440,9 +1454,11 @@ __device__ __forceinline__ void bj_pair(int r, int p, int NB, int* a, int* b) {
 // Global index of local index l of the pair (blocks a, b).
 __device__ __forceinline__ int bj_gidx(int l, int a, int b) { return l < BJ_B ? a * BJ_B + l : b * BJ_B + l - BJ_B; }
 
-// The block Jacobi always starts cold: S = A, V = I (a warm start would
-// inherit whatever orthogonality defect the refinement's W has). smax[1] =
-// max |a_ii|, the scale of the absolute part of the convergence test.
+// The block Jacobi starts cold (FLAG_COLD: S = A, V = I) or from the
+// refinement's last W (S = W^T A W and V = W, set by pcj_final only when W
+// passed the orthonormality check and every coupling was below 0.05).
+// smax[1] = max |a_ii|, the scale of the absolute part of the convergence
+// test.
 __global__ __launch_bounds__(256) void bj_init_kernel(const double* __restrict__ A, double* S, double* V, int ld,
                                                       int32_t* st, double* smax, const int64_t* __restrict__ bd) {
   const int64_t bdel = bd ? bd[blockIdx.z] : 0;
@@ -1467,6 +1483,7 @@ __global__ __launch_bounds__(256) void bj_init_kernel(const double* __restrict__
       st[ST_SWEEPS] = 0;
     }
   }
+  if (!(st[ST_PCJ] & FLAG_COLD)) return;
   const size_t tot = (size_t)m * m;
   for (size_t e = blockIdx.x * 256 + threadIdx.x; e < tot; e += (size_t)gridDim.x * 256) {
     const size_t i = e / m, j = e % m;
@@ -1753,7 +1770,7 @@ int iskv_launch_core_eig(isvd_handle* h, double tol, int keep) {
   // step 0 works on S = A with W = I
   hipLaunchKernelGGL(pcj_detect_kernel, bz(dim3(nblk), h->bcount), dim3(256), 0, s, w.S, ld, w.aux, w.edges, st,
                      tol, h->bd);
-  hipLaunchKernelGGL(pcj_analyze_kernel, bz(dim3(1), h->bcount), dim3(1024), lds, s, w.S, w.W0, ld, w.aux, nblk,
+  hipLaunchKernelGGL(pcj_analyze_kernel, bz(dim3(1), h->bcount), dim3(1024), lds, s, w.S, w.W0, w.T, ld, w.aux, nblk,
                      w.edges, st, 0, tol, h->bd);
   hipLaunchKernelGGL(pcj_kmat_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.S, ld, w.Km, w.Pa, st, h->bd);
   // X = I + K (I + K/2); W <- W X
@@ -1778,7 +1795,7 @@ int iskv_launch_core_eig(isvd_handle* h, double tol, int keep) {
                         h->bcount);
     // S = W'^T (A W') with the strong-pair detection
     gemm_s(s, mm, wo, w.Pa, ld, w.S, w.Dp, w.aux, w.edges, st, tol, h->bd, h->bcount);
-    hipLaunchKernelGGL(pcj_analyze_kernel, bz(dim3(1), h->bcount), dim3(1024), lds, s, w.S, wo, ld, w.aux,
+    hipLaunchKernelGGL(pcj_analyze_kernel, bz(dim3(1), h->bcount), dim3(1024), lds, s, w.S, wo, w.T, ld, w.aux,
                        nblk * nblk, w.edges, st, it, tol, h->bd);
     if (it == maxit) break;  // last pass only tests convergence
     hipLaunchKernelGGL(pcj_kmat_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.S, ld, w.Km, w.Pa, st, h->bd);
@@ -1786,8 +1803,9 @@ int iskv_launch_core_eig(isvd_handle* h, double tol, int keep) {
     gemm<false, false>(s, mm, wo, w.Pb, wc, wo, ld, 1.0, 0.0, 0.0, st, 1, h->bd, h->bcount);
   }
   // final Newton-Schulz of W (in wo) into wc, with A W for the eigenvalues;
-  // skipped after convergence at a step >= 1, where wo is already
-  // orthonormalised and Pa = A wo (T keeps W^T W of the W before it)
+  // skipped after convergence at a step >= 1 when the iterate behind wo was
+  // within 1e-4 of orthonormal (checked by the converging analysis: wo then
+  // within ~1e-8, Pa = A wo, and T keeps W^T W of that iterate)
   gemm2<true, true>(s, mm, wo, w.A, wo, ld, w.T, w.Km, nullptr, nullptr, 1.0, 0.0, 1.0, 0.0, nullptr, st, 4, h->bd,
                     h->bcount);
   gemm2<false, false>(s, mm, wo, w.Km, w.T, ld, wc, w.Pa, wo, w.Km, -0.5, 1.5, -0.5, 1.5, nullptr, st, 4, h->bd,
@@ -1801,7 +1819,7 @@ int iskv_launch_core_eig(isvd_handle* h, double tol, int keep) {
     hipLaunchKernelGGL(core_jacobi_kernel, bz(dim3(1), h->bcount), dim3(1024), 0, s, w.S, w.V, ld, st, 1e-13,
                        ISKV_JACOBI_MAX_SWEEPS, h->bd);
   } else {
-    block_jacobi(BJ_SWEEPS);
+    block_jacobi(keep >= 0 ? BJ_SWEEPS_MERGE : BJ_SWEEPS);
   }
   ISKV_HIP_CHECK(hipGetLastError());
   return ISKV_OK;

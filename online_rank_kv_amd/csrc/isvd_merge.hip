@@ -550,21 +550,31 @@ __global__ __launch_bounds__(1024) void eig_order_kernel(const double* __restric
   sig_new = iskv_rb(sig_new, bdel);
   order = iskv_rb(order, bdel);
   st = iskv_rb(st, bdel);
-  __shared__ double lam[1024];
+  __shared__ double lam[1024], key[1024];
+  __shared__ int rnk[1024];
   const int n = st[ST_JM];
   const int t = threadIdx.x;
-  for (int i = t; i < n; i += blockDim.x) lam[i] = S[(size_t)i * ld + i];
-  __syncthreads();
   for (int i = t; i < n; i += blockDim.x) {
-    int rnk = 0;
-    const double ki = rank_key(lam[i]);
-#pragma unroll 16
-    for (int j = 0; j < n; ++j) {
-      const double kj = rank_key(lam[j]);
-      rnk += (kj > ki) || (kj == ki && j < i);
-    }
-    order[rnk] = i;
+    lam[i] = S[(size_t)i * ld + i];
+    key[i] = rank_key(lam[i]);
+    rnk[i] = 0;
   }
+  __syncthreads();
+  // rank of i = entries ahead of it (larger, or equal at a lower index); the
+  // n x n comparisons are split over the workgroup in quarters of j
+  const int qn = (n + 3) / 4;
+  for (int e = t; e < 4 * n; e += blockDim.x) {
+    const int i = e >> 2, j0 = (e & 3) * qn, j1 = min(j0 + qn, n);
+    const double ki = key[i];
+    int c = 0;
+    for (int j = j0; j < j1; ++j) {
+      const double kj = key[j];
+      c += (kj > ki) || (kj == ki && j < i);
+    }
+    atomicAdd(&rnk[i], c);
+  }
+  __syncthreads();
+  for (int i = t; i < n; i += blockDim.x) order[rnk[i]] = i;
   __syncthreads();
   const int keep = for_merge ? (n < r_max ? n : r_max) : n;
   for (int c = t; c < keep; c += blockDim.x) sig_new[c] = (float)sqrt(fmax(lam[min(max(order[c], 0), n - 1)], 0.0));
