@@ -124,15 +124,17 @@ __global__ __launch_bounds__(256) void resid_gram_kernel(const float* __restrict
 //
 // Phase 1 (when every residual direction can be kept, b <= D - k): sweeps in
 // fp32 on S / trace until every scaled coupling |s_ij| / sqrt(s_ii s_jj) is
-// below 3e-5, then S = V^T (E E^T) V is formed in fp64 from the fp32 V. If
-// its couplings are below 1e-4 and Gershgorin's lower bound of its spectrum
+// below 3e-3, then S = V^T (E E^T) V is formed in fp64 from the fp32 V. If
+// its couplings are below 1e-2 and Gershgorin's lower bound of its spectrum
 // lies above tau^2 (tau from the upper bound of rho_1), then p = b and P only
 // has to be an orthonormal basis of span(E^T), whose choice does not change
 // the merge (the core changes by a rotation of its last b columns).
 // P = E^T V S^-1/2 is one for any nonsingular V; S^-1/2 is taken as
 // D^-1/2 (I - O/2 + 3 O^2 / 8) with D = diag(S), O = D^-1/2 S D^-1/2 - I
-// (error 5/16 |O|^3), so rho = 1, and the core block (F P)^T (F P) stays
-// nearly diagonal for the core eigensolver.
+// (error 5/16 |O|^3 <= 3e-7, the fp32 rounding of P), so rho = 1, and the
+// core block (F P)^T (F P) = S is diagonal up to couplings of 1e-2, which the
+// core eigensolver resolves with the rest (rotations of that size among the
+// new directions do not add a refinement step).
 // Phase 2 (otherwise: a rank decision is needed, the residual is nearly
 // degenerate, or phase 1 did not certify): fp64 sweeps from the Gram until
 // none rotates; an off-diagonal is rotated away when it exceeds 1e-13 of the
@@ -293,14 +295,14 @@ __global__ __launch_bounds__(HB * HB) void resid_basis_kernel(const double* __re
         __syncthreads();
       }
       if (!__syncthreads_or(rotated)) break;
-      if (sweep >= 2) {  // largest scaled coupling left
+      if (sweep >= 1) {  // largest scaled coupling left
         const float* S = Sf + cur * N * LF;
         auto cpl = [&](int i, int j) {
           return (i != j && i < b && j < b)
                      ? fabsf(S[i * LF + j]) / sqrtf(fabsf(S[i * LF + i] * S[j * LF + j]) + 1e-37f) : 0.0f;
         };
         float om = fmaxf(fmaxf(cpl(r0, c0), cpl(r0, c1)), fmaxf(cpl(r1, c0), cpl(r1, c1)));
-        if (__syncthreads_and(!(om >= 3e-5f))) break;  // NaN stays in the loop, fails below
+        if (__syncthreads_and(!(om >= 3e-3f))) break;  // NaN stays in the loop, fails below
       }
     }
     const float* Vc = Vf + cur * N * LF;
@@ -360,7 +362,7 @@ __global__ __launch_bounds__(HB * HB) void resid_basis_kernel(const double* __re
       hm = fmax(hm, wred[2][w]);
     }
     const double tau_hi = tfac * fmax(s1, sqrt(hm));
-    if (om < 1e-4 && lm > tau_hi * tau_hi) {  // same decision in every thread
+    if (om < 1e-2 && lm > tau_hi * tau_hi) {  // same decision in every thread
       // O = D^-1/2 S D^-1/2 - I over the real indices (into G64's place),
       // Z = D^-1/2 (I - O/2 + 3 O^2 / 8) (into T64's place), V_E = V Z.
       double* Ob = G64;
