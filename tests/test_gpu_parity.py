@@ -1213,6 +1213,45 @@ def test_prompt_decode_stream_64k(K, r):
     assert opt * (1 - 1e-6) <= err <= 1.05 * opt
 
 
+@pytest.mark.parametrize("spec", ["exp40+0.01", "invsqrt"])
+def test_high_rank_segment_matches_oracle(K, spec):
+    """The prompt + decode stream's shape (D = 1024, r = 512, b = 64, a
+    576-wide core, re-orthogonalisation every 256 folded rows) against the
+    oracle's own stream from a common start: the GPU's refit of 8,192 rows,
+    then 8 merges of 64 rows (two re-orthogonalisations) on the GPU, and the
+    same merges in the oracle started from the GPU's factor. C B^T within
+    1e-3 of the oracle's product, and the new rows' reconstruction error
+    within 1e-4 (absolute, relative to the rows) of the oracle's."""
+    D, r, b, N0, M = 1024, 512, 64, 8192, 8
+    n = N0 + M * b
+    X = synth.kv_stream(synth.StreamSpec(D=D, n=n, spectrum=spec, noise_std=0.0, seed=71))
+    Xd = torch.from_numpy(X).to(DEV)
+    posd = torch.arange(n, dtype=torch.int32, device=DEV)
+    path = K.IsvdPath(D=D, r_max=r, b_max=b, n_cap=n, reorth_every_rows=256, device=DEV)
+    path.refit(Xd[:N0], posd[:N0])
+    torch.cuda.synchronize()
+    C0, B0, s0, p0, st0 = gpu_factors(path)
+    folded = path.state()[3]
+    assert st0 == 0 and C0.shape == (N0, r) and np.array_equal(p0, np.arange(N0))
+    start = O.Factor(U=C0 / s0[None, :], sigma=s0, B=B0, pos=p0.astype(np.int64), folded=int(folded))
+    for s in range(N0, n, b):
+        path.merge(Xd[s:s + b], posd[s:s + b])
+    torch.cuda.synchronize()
+    C1, B1, _, p1, st1 = gpu_factors(path)
+    assert st1 == 0 and np.array_equal(p1, np.arange(n))
+    ref = O.run_stream(X[N0:], b, r, reorth_every_rows=256, fac=start, pos0=N0)
+    assert np.array_equal(ref.pos, np.arange(n))
+    got, want = C1 @ B1.T, O.represented(ref)
+    err = rel(got, want)
+    new = slice(N0, n)
+    e_gpu = rel(got[new], X[new])
+    e_orc = rel(want[new], X[new])
+    print(f"{spec} r={r}: C B^T vs oracle {err:.3e}; new rows' error gpu {e_gpu:.6e} oracle {e_orc:.6e}", flush=True)
+    assert err < 1e-3
+    assert abs(e_gpu - e_orc) < 1e-4
+    path.close()
+
+
 def test_prompt_init_error_paths(K):
     """Refits and the prompt split refuse what they cannot do, before any work."""
     D = 128
