@@ -883,35 +883,58 @@ __device__ __forceinline__ void rot2(double app, double aqq, double apq, double*
   *s = tt * (*c);
 }
 
-// Serial cyclic Jacobi on a c x c block (c <= CMAX_S) held in LDS by one thread.
-__device__ void jacobi_serial(double* S, double* V, int c) {
-  for (int i = 0; i < c * c; ++i) V[i] = (i / c == i % c) ? 1.0 : 0.0;
+// Cyclic Jacobi on a c x c cluster block (c <= CMAX_S) by a group of 8 lanes
+// of one wave: lane x < c holds row x of the block (srow) and of the
+// eigenvector matrix (vrow) in registers. Every lane of the group forms the
+// same rotation from values shuffled out of lanes p and q; the column update
+// is local, the row update exchanges rows p and q. `base` is the group's
+// first lane in the wave. Sweeps end when one rotates nothing (the decision
+// is the same in every lane of the group).
+// One rotation (p, q) of jacobi_group, with compile-time indices so the
+// row arrays stay in registers.
+template <int P, int Q>
+__device__ __forceinline__ void jacobi_pair(double (&srow)[CMAX_S], double (&vrow)[CMAX_S], int c, int x, int base,
+                                            bool& rotated) {
+  if (Q >= c) return;
+  const double app = __shfl(srow[P], base + P, 64);
+  const double aqq = __shfl(srow[Q], base + Q, 64);
+  const double apq = __shfl(srow[Q], base + P, 64);
+  if (apq == 0.0 || !(fabs(apq) > 1e-14 * sqrt(fabs(app * aqq)))) return;
+  double cs, sn;
+  rot2(app, aqq, apq, &cs, &sn);
+  rotated = true;
+  {  // columns P, Q of the block and of V
+    const double sp = srow[P], sq = srow[Q];
+    srow[P] = cs * sp - sn * sq;
+    srow[Q] = sn * sp + cs * sq;
+    const double vp = vrow[P], vq = vrow[Q];
+    vrow[P] = cs * vp - sn * vq;
+    vrow[Q] = sn * vp + cs * vq;
+  }
+  const int partner = base + (x == P ? Q : P);
+#pragma unroll
+  for (int y = 0; y < CMAX_S; ++y) {  // rows P, Q
+    const double o = __shfl(srow[y], partner, 64);
+    if (x == P) srow[y] = cs * srow[y] - sn * o;
+    else if (x == Q) srow[y] = sn * o + cs * srow[y];
+  }
+}
+
+template <int P, int Q>
+__device__ __forceinline__ void jacobi_sweep(double (&srow)[CMAX_S], double (&vrow)[CMAX_S], int c, int x, int base,
+                                             bool& rotated) {
+  if constexpr (P < CMAX_S - 1) {
+    jacobi_pair<P, Q>(srow, vrow, c, x, base, rotated);
+    if constexpr (Q + 1 < CMAX_S) jacobi_sweep<P, Q + 1>(srow, vrow, c, x, base, rotated);
+    else jacobi_sweep<P + 1, P + 2>(srow, vrow, c, x, base, rotated);
+  }
+}
+
+__device__ void jacobi_group(double (&srow)[CMAX_S], double (&vrow)[CMAX_S], int c, int x, int base) {
   for (int sweep = 0; sweep < 20; ++sweep) {
-    int rot = 0;
-    for (int p = 0; p < c - 1; ++p)
-      for (int q = p + 1; q < c; ++q) {
-        double apq = S[p * c + q];
-        if (apq == 0.0 || !(fabs(apq) > 1e-14 * sqrt(fabs(S[p * c + p] * S[q * c + q])))) continue;
-        double cs, sn;
-        rot2(S[p * c + p], S[q * c + q], apq, &cs, &sn);
-        ++rot;
-        for (int x = 0; x < c; ++x) {  // columns p, q
-          double sp = S[x * c + p], sq = S[x * c + q];
-          S[x * c + p] = cs * sp - sn * sq;
-          S[x * c + q] = sn * sp + cs * sq;
-        }
-        for (int x = 0; x < c; ++x) {  // rows p, q
-          double sp = S[p * c + x], sq = S[q * c + x];
-          S[p * c + x] = cs * sp - sn * sq;
-          S[q * c + x] = sn * sp + cs * sq;
-        }
-        for (int x = 0; x < c; ++x) {
-          double vp = V[x * c + p], vq = V[x * c + q];
-          V[x * c + p] = cs * vp - sn * vq;
-          V[x * c + q] = sn * vp + cs * vq;
-        }
-      }
-    if (!rot) break;
+    bool rotated = false;
+    jacobi_sweep<0, 1>(srow, vrow, c, x, base, rotated);
+    if (!rotated) break;
   }
 }
 
@@ -958,7 +981,6 @@ __global__ __launch_bounds__(256) void pcj_detect_kernel(const double* __restric
 
 struct AnalyzeLds {
   double d[1024];
-  double cmat[NCL_MAX][CMAX_S * CMAX_S];
   double vmat[NCL_MAX][CMAX_S * CMAX_S];
   double pc[NPAIR_MAX], ps[NPAIR_MAX];
   int key[EMAX];
@@ -1125,12 +1147,19 @@ __global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W,
   if (t == 0) st[ST_NEDGE] = 0;  // the next detect pass starts a new list
   __syncthreads();
   const int ncl = L.ncl, npair = L.npair;
-  if (t < ncl) {
-    const int c = L.ccount[t];
-    double* Sc = L.cmat[t];
-    for (int a = 0; a < c; ++a)
-      for (int b = 0; b < c; ++b) Sc[a * c + b] = S[(size_t)L.members[t][a] * ld + L.members[t][b]];
-    jacobi_serial(Sc, L.vmat[t], c);
+  if ((t >> 3) < ncl) {  // cluster t / 8 on lanes 8 (t / 8) .. +7
+    const int g = t >> 3, x = t & 7, c = L.ccount[g];
+    double srow[CMAX_S], vrow[CMAX_S];
+#pragma unroll
+    for (int b = 0; b < CMAX_S; ++b) {
+      srow[b] = (x < c && b < c) ? S[(size_t)L.members[g][x] * ld + L.members[g][b]] : 0.0;
+      vrow[b] = (x == b) ? 1.0 : 0.0;
+    }
+    jacobi_group(srow, vrow, c, x, (t & 63) & ~7);
+    if (x < c)
+#pragma unroll
+      for (int b = 0; b < CMAX_S; ++b)
+        if (b < c) L.vmat[g][x * c + b] = vrow[b];
   }
   for (int q = t; q < npair; q += nt) {
     int a = L.pi[q], b = L.pj[q];
@@ -1145,13 +1174,19 @@ __global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W,
     int g = e / m, j = e % m;
     int c = L.ccount[g];
     double x[CMAX_S], y[CMAX_S];
-    for (int a = 0; a < c; ++a) x[a] = S[(size_t)L.members[g][a] * ld + j];
-    for (int b = 0; b < c; ++b) {
+#pragma unroll
+    for (int a = 0; a < CMAX_S; ++a) x[a] = a < c ? S[(size_t)L.members[g][a] * ld + j] : 0.0;
+#pragma unroll
+    for (int b = 0; b < CMAX_S; ++b) {
       double acc = 0.0;
-      for (int a = 0; a < c; ++a) acc = fma(L.vmat[g][a * c + b], x[a], acc);
+#pragma unroll
+      for (int a = 0; a < CMAX_S; ++a)
+        if (a < c && b < c) acc = fma(L.vmat[g][a * c + b], x[a], acc);
       y[b] = acc;
     }
-    for (int b = 0; b < c; ++b) S[(size_t)L.members[g][b] * ld + j] = y[b];
+#pragma unroll
+    for (int b = 0; b < CMAX_S; ++b)
+      if (b < c) S[(size_t)L.members[g][b] * ld + j] = y[b];
   }
   for (int e = t; e < npair * m; e += nt) {
     int q = e / m, j = e % m;
@@ -1167,16 +1202,21 @@ __global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W,
     int g = e / m, i = e % m;
     int c = L.ccount[g];
     double x[CMAX_S], w[CMAX_S];
-    for (int a = 0; a < c; ++a) {
-      x[a] = S[(size_t)i * ld + L.members[g][a]];
-      w[a] = W[(size_t)i * ld + L.members[g][a]];
+#pragma unroll
+    for (int a = 0; a < CMAX_S; ++a) {
+      x[a] = a < c ? S[(size_t)i * ld + L.members[g][a]] : 0.0;
+      w[a] = a < c ? W[(size_t)i * ld + L.members[g][a]] : 0.0;
     }
-    for (int b = 0; b < c; ++b) {
+#pragma unroll
+    for (int b = 0; b < CMAX_S; ++b) {
+      if (b >= c) continue;
       double s1 = 0.0, s2 = 0.0;
-      for (int a = 0; a < c; ++a) {
-        s1 = fma(x[a], L.vmat[g][a * c + b], s1);
-        s2 = fma(w[a], L.vmat[g][a * c + b], s2);
-      }
+#pragma unroll
+      for (int a = 0; a < CMAX_S; ++a)
+        if (a < c) {
+          s1 = fma(x[a], L.vmat[g][a * c + b], s1);
+          s2 = fma(w[a], L.vmat[g][a * c + b], s2);
+        }
       S[(size_t)i * ld + L.members[g][b]] = s1;
       W[(size_t)i * ld + L.members[g][b]] = s2;
     }
