@@ -805,7 +805,7 @@ void gemm_s(hipStream_t s, int m_max, const double* W, const double* T, int ld, 
 
 // S = A, W = I, flags cleared.
 __global__ __launch_bounds__(256) void pcj_init_kernel(const double* __restrict__ A, double* S,
-                                                       double* W, int ld, int32_t* st, int keep,
+                                                       double* W, int ld, int32_t* st,
     const int64_t* __restrict__ bd) {
   const int64_t bdel = bd ? bd[blockIdx.z] : 0;
   A = iskv_rb(A, bdel);
@@ -813,59 +813,6 @@ __global__ __launch_bounds__(256) void pcj_init_kernel(const double* __restrict_
   W = iskv_rb(W, bdel);
   st = iskv_rb(st, bdel);
   const int m = st[ST_JM];
-  if (blockIdx.x == 0) {
-    // coupling scale (the largest diagonal entry) and cut (between the
-    // keep-th and (keep+1)-th largest diagonal entries, geometric mean),
-    // rounded to fp32; read by later launches only. keep < 0: scaled
-    // couplings; keep >= m: nothing dropped.
-    __shared__ double dl[1024];
-    __shared__ double red[3][4];
-    double dmax = 0.0;
-    for (int i = threadIdx.x; i < m; i += 256) {
-      dl[i] = fabs(A[(size_t)i * ld + i]);
-      dmax = fmax(dmax, dl[i]);
-    }
-    __syncthreads();
-    // the keep-th largest value (hi) and the next one down (lo), by counting
-    double hi = INFINITY, lo = 0.0;
-    if (keep >= 0 && keep < m) {
-      for (int i = threadIdx.x; i < m; i += 256) {
-        const double v = dl[i];
-        int above = 0;
-        for (int j = 0; j < m; ++j) above += dl[j] > v;
-        if (above < keep) hi = fmin(hi, v);
-        else lo = fmax(lo, v);
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      dmax = fmax(dmax, __shfl_xor(dmax, o, 64));
-      hi = fmin(hi, __shfl_xor(hi, o, 64));
-      lo = fmax(lo, __shfl_xor(lo, o, 64));
-    }
-    if ((threadIdx.x & 63) == 0) {
-      red[0][threadIdx.x >> 6] = dmax;
-      red[1][threadIdx.x >> 6] = hi;
-      red[2][threadIdx.x >> 6] = lo;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      dmax = fmax(fmax(red[0][0], red[0][1]), fmax(red[0][2], red[0][3]));
-      hi = fmin(fmin(red[1][0], red[1][1]), fmin(red[1][2], red[1][3]));
-      lo = fmax(fmax(red[2][0], red[2][1]), fmax(red[2][2], red[2][3]));
-      auto up = [](double x) {
-        const float f = (float)x;
-        return (double)f < x ? __int_as_float(__float_as_int(f) + 1) : f;
-      };
-      const float fu = up(dmax);
-      const bool prod = keep >= 0 && isfinite(fu) && fu > 0.f;
-      st[ST_SREF] = prod ? __float_as_int(fu) : 0;
-      // equal values on both sides of the cut (hi == lo) leave it at that
-      // value, and neither counts as above it
-      const double cut = (keep >= 0 && keep < m && isfinite(hi)) ? sqrt(hi * lo) : -1.0;
-      st[ST_DCUT] = __float_as_int(prod && cut >= 0.0 ? (float)cut : -1.f);
-    }
-  }
   const size_t total = (size_t)m * m;
   for (size_t e = blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
     int i = (int)(e / m), j = (int)(e % m);
@@ -944,7 +891,7 @@ __device__ void jacobi_group(double (&srow)[CMAX_S], double (&vrow)[CMAX_S], int
 // column j > i and writes its maximum to aux[b]. Strong pairs are appended to
 // the edge list (order fixed later by sorting).
 __global__ __launch_bounds__(256) void pcj_detect_kernel(const double* __restrict__ S, int ld,
-                                                         double* aux, int* edges, int32_t* st, double tol,
+                                                         double* aux, int* edges, int32_t* st, double tol, int keep,
     const int64_t* __restrict__ bd) {
   const int64_t bdel = bd ? bd[blockIdx.z] : 0;
   S = iskv_rb(S, bdel);
@@ -953,9 +900,57 @@ __global__ __launch_bounds__(256) void pcj_detect_kernel(const double* __restric
   st = iskv_rb(st, bdel);
   if (st[ST_PCJ] & FLAG_CONV) return;
   const int m = st[ST_JM];
-  const double sref = coupling_ref(st), dcut = coupling_cut(st);
   const int r0 = blockIdx.x * 16;
   __shared__ double red[4];
+  // coupling scale (the largest diagonal entry) and cut (between the keep-th
+  // and (keep+1)-th largest diagonal entries, geometric mean), rounded to
+  // fp32 so that the later steps (reading them from st) use the same values;
+  // every workgroup forms them from S = A, block 0 publishes them. keep < 0:
+  // scaled couplings; keep >= m: nothing dropped.
+  __shared__ double dl[1024];
+  __shared__ double cred[3][4];
+  double dmax = 0.0, hi = INFINITY, lo = 0.0;
+  for (int i = threadIdx.x; i < m; i += 256) {
+    dl[i] = fabs(S[(size_t)i * ld + i]);
+    dmax = fmax(dmax, dl[i]);
+  }
+  __syncthreads();
+  if (keep >= 0 && keep < m)
+    for (int i = threadIdx.x; i < m; i += 256) {
+      const double v = dl[i];
+      int above = 0;
+      for (int j = 0; j < m; ++j) above += dl[j] > v;
+      if (above < keep) hi = fmin(hi, v);
+      else lo = fmax(lo, v);
+    }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    dmax = fmax(dmax, __shfl_xor(dmax, o, 64));
+    hi = fmin(hi, __shfl_xor(hi, o, 64));
+    lo = fmax(lo, __shfl_xor(lo, o, 64));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    cred[0][threadIdx.x >> 6] = dmax;
+    cred[1][threadIdx.x >> 6] = hi;
+    cred[2][threadIdx.x >> 6] = lo;
+  }
+  __syncthreads();
+  dmax = fmax(fmax(cred[0][0], cred[0][1]), fmax(cred[0][2], cred[0][3]));
+  hi = fmin(fmin(cred[1][0], cred[1][1]), fmin(cred[1][2], cred[1][3]));
+  lo = fmax(fmax(cred[2][0], cred[2][1]), fmax(cred[2][2], cred[2][3]));
+  auto up = [](double x) {
+    const float f = (float)x;
+    return (double)f < x ? __int_as_float(__float_as_int(f) + 1) : f;
+  };
+  const float fu = up(dmax);
+  const bool prod = keep >= 0 && isfinite(fu) && fu > 0.f;
+  const double cut = (keep >= 0 && keep < m && isfinite(hi)) ? sqrt(hi * lo) : -1.0;
+  const float fcut = prod && cut >= 0.0 ? (float)cut : -1.f;
+  const double sref = prod ? (double)fu : 0.0, dcut = (double)fcut;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    st[ST_SREF] = prod ? __float_as_int(fu) : 0;
+    st[ST_DCUT] = __float_as_int(fcut);
+  }
   double cmax = 0.0;
   if (r0 < m) {
     const int rows = min(16, m - r0);
@@ -999,15 +994,14 @@ struct AnalyzeLds {
 // convergence test, clusters of strongly coupled indices (components of the
 // strong-pair graph), exact rotations (small clusters: cyclic Jacobi; big
 // ones: 2x2 rotations on a greedy matching), applied to S and W in place.
-__global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W, const double* __restrict__ T,
-                                                           int ld, const double* __restrict__ aux, int nmx,
+__global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W, int ld,
+                                                           const double* __restrict__ aux, int nmx,
                                                            const int* __restrict__ edges,
                                                            int32_t* st, int it, double tol,
     const int64_t* __restrict__ bd) {
   const int64_t bdel = bd ? bd[blockIdx.z] : 0;
   S = iskv_rb(S, bdel);
   W = iskv_rb(W, bdel);
-  T = iskv_rb(T, bdel);
   aux = iskv_rb(aux, bdel);
   edges = iskv_rb(edges, bdel);
   st = iskv_rb(st, bdel);
@@ -1031,17 +1025,8 @@ __global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W,
   __syncthreads();
   const double cmax = L.cmax;
   if (cmax < tol) {  // NaN couplings never pass: they end in the fallback
-    // from step 1 on, T = W^T W of the iterate behind this step's
-    // orthonormalised W: a defect above 1e-4 asks for the final
-    // Newton-Schulz step (FLAG_NS) before W is used
-    bool bad = false;
-    if (it > 0)
-      for (int e = t; e < m * m; e += nt) {
-        const int i = e / m, j = e % m;
-        bad |= !(fabs(T[(size_t)i * ld + j] - (i == j ? 1.0 : 0.0)) <= 1e-4);
-      }
-    bad = __syncthreads_or(bad);
-    if (t == 0) { st[ST_PCJ] |= FLAG_CONV | (bad ? FLAG_NS : 0); st[ST_PCJIT] = it; st[ST_NEDGE] = 0; }
+    __syncthreads();
+    if (t == 0) { st[ST_PCJ] |= FLAG_CONV; st[ST_PCJIT] = it; st[ST_NEDGE] = 0; }
     return;
   }
   const int ne = L.nedge;
@@ -1274,11 +1259,14 @@ __global__ __launch_bounds__(256) void pcj_kmat_kernel(const double* __restrict_
 // convergence the same test keeps the fallback from continuing from a W that
 // is not orthonormal (cold instead of warm). Grid-stride.
 __global__ __launch_bounds__(256) void pcj_orth_check_kernel(const double* __restrict__ T, int ld, int32_t* st,
-                                                             double thr, const int64_t* __restrict__ bd) {
+                                                             double thr, int pre, const int64_t* __restrict__ bd) {
   const int64_t bdel = bd ? bd[blockIdx.z] : 0;
   T = iskv_rb(T, bdel);
   st = iskv_rb(st, bdel);
   const bool conv = (st[ST_PCJ] & FLAG_CONV) != 0;
+  // pre: after convergence at a step >= 1, T = W^T W of the iterate behind
+  // the orthonormalised W; a defect above thr asks for the final step
+  if (pre && !(conv && st[ST_PCJIT] > 0)) return;
   const int m = st[ST_JM];
   const size_t tot = (size_t)m * m;
   bool bad = false;
@@ -1287,7 +1275,9 @@ __global__ __launch_bounds__(256) void pcj_orth_check_kernel(const double* __res
     const double v = T[i * ld + j] - (i == j ? 1.0 : 0.0);
     bad |= !(fabs(v) <= thr);
   }
-  if (bad) {
+  if (bad && pre) {
+    atomicOr(&st[ST_PCJ], FLAG_NS);
+  } else if (bad) {
     if (conv) atomicAnd(&st[ST_PCJ], ~FLAG_CONV);
     st[ST_ROUNDS] = 1;
   }
@@ -1805,12 +1795,11 @@ int iskv_launch_core_eig(isvd_handle* h, double tol, int keep) {
     ISKV_HIP_CHECK(hipGetLastError());
     return ISKV_OK;
   }
-  hipLaunchKernelGGL(pcj_init_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.A, w.S, w.W0, ld, st, keep,
-                     h->bd);
+  hipLaunchKernelGGL(pcj_init_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.A, w.S, w.W0, ld, st, h->bd);
   // step 0 works on S = A with W = I
   hipLaunchKernelGGL(pcj_detect_kernel, bz(dim3(nblk), h->bcount), dim3(256), 0, s, w.S, ld, w.aux, w.edges, st,
-                     tol, h->bd);
-  hipLaunchKernelGGL(pcj_analyze_kernel, bz(dim3(1), h->bcount), dim3(1024), lds, s, w.S, w.W0, w.T, ld, w.aux, nblk,
+                     tol, keep, h->bd);
+  hipLaunchKernelGGL(pcj_analyze_kernel, bz(dim3(1), h->bcount), dim3(1024), lds, s, w.S, w.W0, ld, w.aux, nblk,
                      w.edges, st, 0, tol, h->bd);
   hipLaunchKernelGGL(pcj_kmat_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.S, ld, w.Km, w.Pa, st, h->bd);
   // X = I + K (I + K/2); W <- W X
@@ -1835,7 +1824,7 @@ int iskv_launch_core_eig(isvd_handle* h, double tol, int keep) {
                         h->bcount);
     // S = W'^T (A W') with the strong-pair detection
     gemm_s(s, mm, wo, w.Pa, ld, w.S, w.Dp, w.aux, w.edges, st, tol, h->bd, h->bcount);
-    hipLaunchKernelGGL(pcj_analyze_kernel, bz(dim3(1), h->bcount), dim3(1024), lds, s, w.S, wo, w.T, ld, w.aux,
+    hipLaunchKernelGGL(pcj_analyze_kernel, bz(dim3(1), h->bcount), dim3(1024), lds, s, w.S, wo, ld, w.aux,
                        nblk * nblk, w.edges, st, it, tol, h->bd);
     if (it == maxit) break;  // last pass only tests convergence
     hipLaunchKernelGGL(pcj_kmat_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.S, ld, w.Km, w.Pa, st, h->bd);
@@ -1844,13 +1833,14 @@ int iskv_launch_core_eig(isvd_handle* h, double tol, int keep) {
   }
   // final Newton-Schulz of W (in wo) into wc, with A W for the eigenvalues;
   // skipped after convergence at a step >= 1 when the iterate behind wo was
-  // within 1e-4 of orthonormal (checked by the converging analysis: wo then
-  // within ~1e-8, Pa = A wo, and T keeps W^T W of that iterate)
+  // within 1e-4 of orthonormal (wo then within ~1e-8, Pa = A wo, and T keeps
+  // W^T W of that iterate)
+  hipLaunchKernelGGL(pcj_orth_check_kernel, bz(dim3(64), h->bcount), dim3(256), 0, s, w.T, ld, st, 1e-4, 1, h->bd);
   gemm2<true, true>(s, mm, wo, w.A, wo, ld, w.T, w.Km, nullptr, nullptr, 1.0, 0.0, 1.0, 0.0, nullptr, st, 4, h->bd,
                     h->bcount);
   gemm2<false, false>(s, mm, wo, w.Km, w.T, ld, wc, w.Pa, wo, w.Km, -0.5, 1.5, -0.5, 1.5, nullptr, st, 4, h->bd,
                       h->bcount);
-  hipLaunchKernelGGL(pcj_orth_check_kernel, bz(dim3(64), h->bcount), dim3(256), 0, s, w.T, ld, st, 1e-4, h->bd);
+  hipLaunchKernelGGL(pcj_orth_check_kernel, bz(dim3(64), h->bcount), dim3(256), 0, s, w.T, ld, st, 1e-4, 0, h->bd);
   // S = W^T A W of the final W, used only by a fallback that continues from it
   gemm<true, false>(s, mm, wc, w.Pa, w.S, nullptr, ld, 1.0, 0.0, 0.0, st, 3, h->bd, h->bcount);
   hipLaunchKernelGGL(pcj_final_kernel, bz(dim3(mm), h->bcount), dim3(256), 0, s, wo, wc, w.Pa, w.A, w.S, w.V, ld,
