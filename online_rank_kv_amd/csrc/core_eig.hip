@@ -49,7 +49,7 @@ namespace {
 constexpr int PCJ_MAXIT = ISKV_PCJ_MAXIT;
 constexpr double PCJ_OMEGA = 0.1;
 constexpr double PCJ_CLIP = 0.2;
-constexpr int CMAX_S = 6;      // largest cluster diagonalised exactly
+constexpr int CMAX_S = ISKV_PCJ_CMAX;  // largest cluster diagonalised exactly
 constexpr int NCL_MAX = 64;    // clusters handled exactly per step
 constexpr int EMAX = ISKV_PCJ_EMAX;  // strong pairs recorded per step
 constexpr int NPAIR_MAX = 512; // matched pairs per step
@@ -976,8 +976,6 @@ __global__ __launch_bounds__(256) void pcj_detect_kernel(const double* __restric
 
 struct AnalyzeLds {
   double d[1024];
-  double vmat[NCL_MAX][CMAX_S * CMAX_S];
-  double pc[NPAIR_MAX], ps[NPAIR_MAX];
   int key[EMAX];
   int lab[1024];
   int size[1024];
@@ -993,17 +991,19 @@ struct AnalyzeLds {
 // The serial part of one refinement step, one workgroup of 1024 threads:
 // convergence test, clusters of strongly coupled indices (components of the
 // strong-pair graph), exact rotations (small clusters: cyclic Jacobi; big
-// ones: 2x2 rotations on a greedy matching), applied to S and W in place.
-__global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W, int ld,
+// ones: 2x2 rotations on a greedy matching), published as rotation tables
+// that the angle kernel applies to S (on the fly) and W.
+__global__ __launch_bounds__(1024) void pcj_analyze_kernel(const double* __restrict__ S, int ld,
                                                            const double* __restrict__ aux, int nmx,
-                                                           const int* __restrict__ edges,
-                                                           int32_t* st, int it, double tol,
+                                                           const int* __restrict__ edges, int32_t* itab,
+                                                           double* rtab, int mmax, int32_t* st, int it, double tol,
     const int64_t* __restrict__ bd) {
   const int64_t bdel = bd ? bd[blockIdx.z] : 0;
   S = iskv_rb(S, bdel);
-  W = iskv_rb(W, bdel);
   aux = iskv_rb(aux, bdel);
   edges = iskv_rb(edges, bdel);
+  itab = iskv_rb(itab, bdel);
+  rtab = iskv_rb(rtab, bdel);
   st = iskv_rb(st, bdel);
   extern __shared__ unsigned char smem_raw[];
   AnalyzeLds& L = *reinterpret_cast<AnalyzeLds*>(smem_raw);
@@ -1032,7 +1032,7 @@ __global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W,
   const int ne = L.nedge;
   for (int i = t; i < m; i += nt) L.d[i] = S[(size_t)i * ld + i];
   if (ne == 0) {  // no strongly coupled pair: the first-order angles do everything
-    if (t == 0) { st[ST_NEDGE] = 0; st[ST_PCJIT] = it + 1; }
+    if (t == 0) { st[ST_NEDGE] = 0; st[ST_PCJIT] = it + 1; st[ST_NROT] = 0; }
     return;
   }
   for (int e = t; e < ne; e += nt) L.key[e] = edges[2 * e] * 1024 + edges[2 * e + 1];
@@ -1132,6 +1132,18 @@ __global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W,
   if (t == 0) st[ST_NEDGE] = 0;  // the next detect pass starts a new list
   __syncthreads();
   const int ncl = L.ncl, npair = L.npair;
+  // the step's exact rotations go to the tables that the angle kernel
+  // applies: group of each index (or -1) and its place, group sizes and
+  // members, the rotated diagonal of the members, each group's rotation R
+  // (columns = the rotated directions, W <- W R)
+  int32_t* gid = itab;
+  int32_t* gpos = itab + mmax;
+  int32_t* gcnt = itab + 2 * mmax;
+  int32_t* gmem = gcnt + (mmax / 2 + 1);
+  double* drot = rtab;
+  double* Rg = rtab + mmax;
+  for (int i = t; i < m; i += nt) gid[i] = -1;
+  __syncthreads();
   if ((t >> 3) < ncl) {  // cluster t / 8 on lanes 8 (t / 8) .. +7
     const int g = t >> 3, x = t & 7, c = L.ccount[g];
     double srow[CMAX_S], vrow[CMAX_S];
@@ -1141,113 +1153,126 @@ __global__ __launch_bounds__(1024) void pcj_analyze_kernel(double* S, double* W,
       vrow[b] = (x == b) ? 1.0 : 0.0;
     }
     jacobi_group(srow, vrow, c, x, (t & 63) & ~7);
-    if (x < c)
+    if (x < c) {
+      const int mx = L.members[g][x];
+      gid[mx] = g;
+      gpos[mx] = x;
+      gmem[g * CMAX_S + x] = mx;
 #pragma unroll
-      for (int b = 0; b < CMAX_S; ++b)
-        if (b < c) L.vmat[g][x * c + b] = vrow[b];
+      for (int b = 0; b < CMAX_S; ++b) {
+        if (b < c) Rg[(size_t)g * CMAX_S * CMAX_S + x * CMAX_S + b] = vrow[b];
+        if (b == x) drot[mx] = srow[b];
+      }
+      if (x == 0) gcnt[g] = c;
+    }
   }
   for (int q = t; q < npair; q += nt) {
-    int a = L.pi[q], b = L.pj[q];
+    const int a = L.pi[q], b = L.pj[q], g = ncl + q;
     double cs = 1.0, sn = 0.0;
-    double apq = S[(size_t)a * ld + b];
-    if (apq != 0.0) rot2(L.d[a], L.d[b], apq, &cs, &sn);
-    L.pc[q] = cs; L.ps[q] = sn;
+    const double apq = S[(size_t)a * ld + b], da = L.d[a], db = L.d[b];
+    if (apq != 0.0) rot2(da, db, apq, &cs, &sn);
+    gid[a] = g; gpos[a] = 0; gid[b] = g; gpos[b] = 1;
+    gcnt[g] = 2;
+    gmem[g * CMAX_S] = a;
+    gmem[g * CMAX_S + 1] = b;
+    double* R = Rg + (size_t)g * CMAX_S * CMAX_S;  // [[c, s], [-s, c]]
+    R[0] = cs; R[1] = sn; R[CMAX_S] = -sn; R[CMAX_S + 1] = cs;
+    drot[a] = cs * cs * da - 2.0 * cs * sn * apq + sn * sn * db;
+    drot[b] = sn * sn * da + 2.0 * cs * sn * apq + cs * cs * db;
   }
-  __syncthreads();
-  // rows of S: S[C, :] <- R_C^T S[C, :]
-  for (int e = t; e < ncl * m; e += nt) {
-    int g = e / m, j = e % m;
-    int c = L.ccount[g];
-    double x[CMAX_S], y[CMAX_S];
-#pragma unroll
-    for (int a = 0; a < CMAX_S; ++a) x[a] = a < c ? S[(size_t)L.members[g][a] * ld + j] : 0.0;
-#pragma unroll
-    for (int b = 0; b < CMAX_S; ++b) {
-      double acc = 0.0;
-#pragma unroll
-      for (int a = 0; a < CMAX_S; ++a)
-        if (a < c && b < c) acc = fma(L.vmat[g][a * c + b], x[a], acc);
-      y[b] = acc;
-    }
-#pragma unroll
-    for (int b = 0; b < CMAX_S; ++b)
-      if (b < c) S[(size_t)L.members[g][b] * ld + j] = y[b];
-  }
-  for (int e = t; e < npair * m; e += nt) {
-    int q = e / m, j = e % m;
-    int a = L.pi[q], b = L.pj[q];
-    double cs = L.pc[q], sn = L.ps[q];
-    double xa = S[(size_t)a * ld + j], xb = S[(size_t)b * ld + j];
-    S[(size_t)a * ld + j] = cs * xa - sn * xb;
-    S[(size_t)b * ld + j] = sn * xa + cs * xb;
-  }
-  __syncthreads();
-  // columns of S and of W: X[:, C] <- X[:, C] R_C
-  for (int e = t; e < ncl * m; e += nt) {
-    int g = e / m, i = e % m;
-    int c = L.ccount[g];
-    double x[CMAX_S], w[CMAX_S];
-#pragma unroll
-    for (int a = 0; a < CMAX_S; ++a) {
-      x[a] = a < c ? S[(size_t)i * ld + L.members[g][a]] : 0.0;
-      w[a] = a < c ? W[(size_t)i * ld + L.members[g][a]] : 0.0;
-    }
-#pragma unroll
-    for (int b = 0; b < CMAX_S; ++b) {
-      if (b >= c) continue;
-      double s1 = 0.0, s2 = 0.0;
-#pragma unroll
-      for (int a = 0; a < CMAX_S; ++a)
-        if (a < c) {
-          s1 = fma(x[a], L.vmat[g][a * c + b], s1);
-          s2 = fma(w[a], L.vmat[g][a * c + b], s2);
-        }
-      S[(size_t)i * ld + L.members[g][b]] = s1;
-      W[(size_t)i * ld + L.members[g][b]] = s2;
-    }
-  }
-  for (int e = t; e < npair * m; e += nt) {
-    int q = e / m, i = e % m;
-    int a = L.pi[q], b = L.pj[q];
-    double cs = L.pc[q], sn = L.ps[q];
-    double xa = S[(size_t)i * ld + a], xb = S[(size_t)i * ld + b];
-    S[(size_t)i * ld + a] = cs * xa - sn * xb;
-    S[(size_t)i * ld + b] = sn * xa + cs * xb;
-    double wa = W[(size_t)i * ld + a], wb = W[(size_t)i * ld + b];
-    W[(size_t)i * ld + a] = cs * wa - sn * wb;
-    W[(size_t)i * ld + b] = sn * wa + cs * wb;
-  }
-  if (t == 0) st[ST_PCJIT] = it + 1;
+  if (t == 0) { st[ST_PCJIT] = it + 1; st[ST_NROT] = ncl + npair; }
 }
 
-// First-order angles for every pair that is not strongly coupled, from the
-// rotated S: K_ij = s_ij / (s_jj - s_ii), K antisymmetric, clipped; writes
-// Km = K and Pa = I + K/2 (X = I + K (I + K/2) is formed by one GEMM).
-// Grid-stride over m x m, many workgroups.
+// First-order angles for every pair that is not strongly coupled, from
+// S' = R^T S R, S rotated by the step's exact rotations R (block diagonal
+// over the analysis' rotation groups, identity elsewhere): K_ij =
+// s'_ij / (s'_jj - s'_ii), K antisymmetric, clipped; writes Km = K and
+// Pa = I + K/2 (X = I + K (I + K/2) is formed by one GEMM). An entry of S'
+// is formed from the groups of its row and column (pairs inside one group
+// are diagonalised: zero). The same launch applies R to W: W[:, g] <- W[:, g] R_g
+// for every group g (rows and groups disjoint, in place). Grid-stride, many
+// workgroups.
 __global__ __launch_bounds__(256) void pcj_kmat_kernel(const double* __restrict__ S, int ld, double* Km,
-                                                       double* Pa, const int32_t* __restrict__ st,
+                                                       double* Pa, double* W, const int32_t* __restrict__ itab,
+                                                       const double* __restrict__ rtab, int mmax,
+                                                       const int32_t* __restrict__ st,
     const int64_t* __restrict__ bd) {
   const int64_t bdel = bd ? bd[blockIdx.z] : 0;
   S = iskv_rb(S, bdel);
   Km = iskv_rb(Km, bdel);
   Pa = iskv_rb(Pa, bdel);
+  W = iskv_rb(W, bdel);
+  itab = iskv_rb(itab, bdel);
+  rtab = iskv_rb(rtab, bdel);
   st = iskv_rb(st, bdel);
   if (st[ST_PCJ] & FLAG_CONV) return;
   const int m = st[ST_JM];
+  const int nrot = st[ST_NROT];
+  const int32_t* gid = itab;
+  const int32_t* gpos = itab + mmax;
+  const int32_t* gcnt = itab + 2 * mmax;
+  const int32_t* gmem = gcnt + (mmax / 2 + 1);
+  const double* drot = rtab;
+  const double* Rg = rtab + mmax;
   const size_t tot = (size_t)m * m;
-  for (size_t e = blockIdx.x * 256 + threadIdx.x; e < tot; e += (size_t)gridDim.x * 256) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (size_t e = blockIdx.x * 256 + threadIdx.x; e < tot; e += stride) {
     int i = (int)(e / m), j = (int)(e % m);
     double k = 0.0;
     if (i != j) {
       int lo = i < j ? i : j, hi = i < j ? j : i;
-      double slh = S[(size_t)lo * ld + hi];
-      double den = S[(size_t)hi * ld + hi] - S[(size_t)lo * ld + lo];
+      const int gl = nrot > 0 ? gid[lo] : -1, gh = nrot > 0 ? gid[hi] : -1;
+      double slh, dl, dh;
+      if (gl < 0 && gh < 0) {
+        slh = S[(size_t)lo * ld + hi];
+        dl = S[(size_t)lo * ld + lo];
+        dh = S[(size_t)hi * ld + hi];
+      } else {
+        dl = gl >= 0 ? drot[lo] : S[(size_t)lo * ld + lo];
+        dh = gh >= 0 ? drot[hi] : S[(size_t)hi * ld + hi];
+        slh = 0.0;
+        if (gl != gh) {
+          const int cl = gl >= 0 ? gcnt[gl] : 1, ch = gh >= 0 ? gcnt[gh] : 1;
+          const int pl = gl >= 0 ? gpos[lo] : 0, ph = gh >= 0 ? gpos[hi] : 0;
+          for (int a = 0; a < cl; ++a) {
+            const int ma = gl >= 0 ? gmem[gl * CMAX_S + a] : lo;
+            const double ra = gl >= 0 ? Rg[(size_t)gl * CMAX_S * CMAX_S + a * CMAX_S + pl] : 1.0;
+            double row = 0.0;
+            for (int b = 0; b < ch; ++b) {
+              const int mb = gh >= 0 ? gmem[gh * CMAX_S + b] : hi;
+              const double rb = gh >= 0 ? Rg[(size_t)gh * CMAX_S * CMAX_S + b * CMAX_S + ph] : 1.0;
+              row = fma(S[(size_t)ma * ld + mb], rb, row);
+            }
+            slh = fma(ra, row, slh);
+          }
+        }
+      }
+      const double den = dh - dl;
       if (den != 0.0 && fabs(slh) <= PCJ_OMEGA * fabs(den)) k = fmin(fmax(slh / den, -PCJ_CLIP), PCJ_CLIP);
       if (!isfinite(k)) k = 0.0;
       if (i > j) k = -k;
     }
     Km[(size_t)i * ld + j] = k;
     Pa[(size_t)i * ld + j] = (i == j ? 1.0 : 0.0) + 0.5 * k;
+  }
+  // W[i, members of g] <- W[i, members of g] R_g
+  const size_t wtot = (size_t)m * nrot;
+  for (size_t e = blockIdx.x * 256 + threadIdx.x; e < wtot; e += stride) {
+    const int i = (int)(e / nrot), g = (int)(e % nrot);
+    const int c = gcnt[g];
+    double w[CMAX_S];
+#pragma unroll
+    for (int a = 0; a < CMAX_S; ++a) w[a] = a < c ? W[(size_t)i * ld + gmem[g * CMAX_S + a]] : 0.0;
+    const double* R = Rg + (size_t)g * CMAX_S * CMAX_S;
+#pragma unroll
+    for (int b = 0; b < CMAX_S; ++b) {
+      if (b >= c) continue;
+      double acc = 0.0;
+#pragma unroll
+      for (int a = 0; a < CMAX_S; ++a)
+        if (a < c) acc = fma(w[a], R[a * CMAX_S + b], acc);
+      W[(size_t)i * ld + gmem[g * CMAX_S + b]] = acc;
+    }
   }
 }
 
@@ -1799,9 +1824,10 @@ int iskv_launch_core_eig(isvd_handle* h, double tol, int keep) {
   // step 0 works on S = A with W = I
   hipLaunchKernelGGL(pcj_detect_kernel, bz(dim3(nblk), h->bcount), dim3(256), 0, s, w.S, ld, w.aux, w.edges, st,
                      tol, keep, h->bd);
-  hipLaunchKernelGGL(pcj_analyze_kernel, bz(dim3(1), h->bcount), dim3(1024), lds, s, w.S, w.W0, ld, w.aux, nblk,
-                     w.edges, st, 0, tol, h->bd);
-  hipLaunchKernelGGL(pcj_kmat_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.S, ld, w.Km, w.Pa, st, h->bd);
+  hipLaunchKernelGGL(pcj_analyze_kernel, bz(dim3(1), h->bcount), dim3(1024), lds, s, w.S, ld, w.aux, nblk,
+                     w.edges, w.itab, w.rtab, h->m_max, st, 0, tol, h->bd);
+  hipLaunchKernelGGL(pcj_kmat_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.S, ld, w.Km, w.Pa, w.W0, w.itab,
+                     w.rtab, h->m_max, st, h->bd);
   // X = I + K (I + K/2); W <- W X
   gemm<false, false>(s, mm, w.Km, w.Pa, w.Pb, nullptr, ld, 1.0, 0.0, 1.0, st, 0, h->bd, h->bcount);
   gemm<false, false>(s, mm, w.W0, w.Pb, w.W1, w.W0, ld, 1.0, 0.0, 0.0, st, 1, h->bd, h->bcount);
@@ -1824,10 +1850,11 @@ int iskv_launch_core_eig(isvd_handle* h, double tol, int keep) {
                         h->bcount);
     // S = W'^T (A W') with the strong-pair detection
     gemm_s(s, mm, wo, w.Pa, ld, w.S, w.Dp, w.aux, w.edges, st, tol, h->bd, h->bcount);
-    hipLaunchKernelGGL(pcj_analyze_kernel, bz(dim3(1), h->bcount), dim3(1024), lds, s, w.S, wo, ld, w.aux,
-                       nblk * nblk, w.edges, st, it, tol, h->bd);
+    hipLaunchKernelGGL(pcj_analyze_kernel, bz(dim3(1), h->bcount), dim3(1024), lds, s, w.S, ld, w.aux,
+                       nblk * nblk, w.edges, w.itab, w.rtab, h->m_max, st, it, tol, h->bd);
     if (it == maxit) break;  // last pass only tests convergence
-    hipLaunchKernelGGL(pcj_kmat_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.S, ld, w.Km, w.Pa, st, h->bd);
+    hipLaunchKernelGGL(pcj_kmat_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.S, ld, w.Km, w.Pa, wo, w.itab,
+                       w.rtab, h->m_max, st, h->bd);
     gemm<false, false>(s, mm, w.Km, w.Pa, w.Pb, nullptr, ld, 1.0, 0.0, 1.0, st, 0, h->bd, h->bcount);
     gemm<false, false>(s, mm, wo, w.Pb, wc, wo, ld, 1.0, 0.0, 0.0, st, 1, h->bd, h->bcount);
   }

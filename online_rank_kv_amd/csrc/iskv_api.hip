@@ -68,6 +68,11 @@ size_t carve(const iskv_config* c, char* base, isvd_ws* w) {
   x.naux = (int)((LM / 16) * (LM / 16));
   x.aux = (double*)take((size_t)x.naux * 8);
   x.edges = (int32_t*)take((size_t)ISKV_PCJ_EMAX * 2 * 4);
+  {
+    const size_t G = M / 2 + 1;  // rotation groups have at least two members
+    x.itab = (int32_t*)take((2 * M + G * (1 + ISKV_PCJ_CMAX)) * 4);
+    x.rtab = (double*)take((M + G * ISKV_PCJ_CMAX * ISKV_PCJ_CMAX) * 8);
+  }
   x.Dp = (double*)take((LM / 16) * LM * 8);
   x.lam = (double*)take(M * 8);
   x.rot_cap = 0;

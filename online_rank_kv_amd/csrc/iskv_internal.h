@@ -30,6 +30,7 @@ enum {
   ST_RSWEEPS = 14, // Jacobi sweeps of the last residual eigensolve
   ST_SREF = 15,    // core eigensolver: fp32 bits of max_i A_ii (coupling scale), 0 = scaled couplings
   ST_DCUT = 16,    // core eigensolver: fp32 bits of the diagonal value between kept and dropped, < 0 = none
+  ST_NROT = 17,    // core eigensolver: exact rotation groups of the refinement step in flight
   ST_COUNT = 20
 };
 
@@ -58,6 +59,8 @@ struct isvd_ws {
   double* Zb;         // [ldm x ldm]  reorth: (B^T B)^(-1/2)
   double* aux;        // [naux] per-tile / per-block maxima of the scaled coupling
   int32_t* edges;     // [ISKV_PCJ_EMAX x 2] strongly coupled pairs of a refinement step
+  int32_t* itab;      // refinement step's exact rotations: group of each index, its place, group sizes, members
+  double* rtab;       // their rotated diagonal [m_max] and rotation matrices [groups x ISKV_PCJ_CMAX^2]
   double* Dp;         // [ldm / 16 x ldm] partial sums of diag(W^T A W) per 16-row block
   double* lam;        // [m_max]
   double* rot;        // [rot_cap] Jacobi rotation log (c, s) pairs
@@ -135,6 +138,7 @@ struct iskv_window {
 #define ISKV_JACOBI_MAX_SWEEPS 40
 // Strongly coupled pairs recorded per refinement step of the core solver.
 #define ISKV_PCJ_EMAX 4096
+#define ISKV_PCJ_CMAX 6   // largest cluster the refinement diagonalises exactly
 // K-panel depth of the fp64 core GEMM; the leading dimension of every fp64
 // core matrix in the workspace is a multiple of it.
 #define ISKV_DGEMM_KP 288
