@@ -8,6 +8,7 @@
 #include <math.h>
 
 #include <mutex>
+#include <type_traits>
 
 namespace {
 
@@ -167,6 +168,181 @@ __global__ __launch_bounds__(256) void attend_split_kernel(const uint16_t* __res
   }
 }
 
+// Streaming form for GQA groups of up to HG query heads: workgroup
+// (split, g, b) folds NCH chunks of 128 rows with an online softmax (running
+// max and sum per head, the output rescaled when the max moves) and writes
+// one partial per head. Per chunk, lane l
+// of wave w holds 8 features (l % 16) of rows w * 32 + 4 i + l / 16 of K and
+// of V; the next chunk's K loads are issued once the logits have consumed
+// the current K, its V loads once P V has consumed the current V. The 32
+// partial dot products of a lane (4 heads x 8 rows) are reduced over the 16
+// lanes of a row by recursive halving (30 exchanges instead of 128): lane
+// c % 16 ends with the logits of head c / 4 for its rows 2 (c % 4) and
+// 2 (c % 4) + 1.
+constexpr int CROWS = 128;
+template <int NCH>
+__global__ __launch_bounds__(256) void attend_stream_kernel(const uint16_t* __restrict__ q,
+                                                            const uint16_t* __restrict__ K,
+                                                            const uint16_t* __restrict__ V, int n,
+                                                            int Hq, int Hkv, float scale, float* part) {
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int nsplit = gridDim.x;
+  const int G = Hq / Hkv;  // 1 .. HG
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int c = lane & 15, sr = lane >> 4;
+  const int r0 = split * CROWS * NCH;
+  __shared__ float logit[HG][CROWS];
+  __shared__ float red[4][HG][DH];
+  __shared__ float mrun[HG], lrun[HG], alpha[HG];
+  const size_t rstride = (size_t)Hkv * DH;
+  const uint16_t* Kb = K + ((size_t)b * n) * rstride + (size_t)g * DH + c * 8;
+  const uint16_t* Vb = V + ((size_t)b * n) * rstride + (size_t)g * DH + c * 8;
+  uint4 kr[8], vr[8];
+  auto load_k = [&](int ch) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = min(r0 + ch * CROWS + wave * 32 + 4 * i + sr, n - 1);
+      kr[i] = *(const uint4*)(Kb + (size_t)row * rstride);
+    }
+  };
+  auto load_v = [&](int ch) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = min(r0 + ch * CROWS + wave * 32 + 4 * i + sr, n - 1);
+      vr[i] = *(const uint4*)(Vb + (size_t)row * rstride);
+    }
+  };
+  load_k(0);
+  load_v(0);
+  float qf[HG][8];
+#pragma unroll
+  for (int hh = 0; hh < HG; ++hh) {
+    const int h = g * G + min(hh, G - 1);
+    bf8(*(const uint4*)(q + ((size_t)b * Hq + h) * DH + c * 8), qf[hh]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[hh][e] *= scale;
+  }
+  if (t < HG) { mrun[t] = -INFINITY; lrun[t] = 0.f; }
+  float acc[HG][8];
+#pragma unroll
+  for (int hh = 0; hh < HG; ++hh)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
+  const int nch = min(NCH, (n - r0 + CROWS - 1) / CROWS);
+  for (int ch = 0; ch < nch; ++ch) {
+    // partial logits: v[8 hh + i] = q_hh . k_i over this lane's 8 features
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float kf[8];
+      bf8(kr[i], kf);
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh) {
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a = fmaf(qf[hh][e], kf[e], a);
+        v[8 * hh + i] = a;
+      }
+    }
+    if (ch + 1 < nch) load_k(ch + 1);
+    // recursive halving over the 16 lanes of the row group
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const bool up = (c & 8) != 0;
+      const float send = up ? v[j] : v[16 + j];
+      v[j] = (up ? v[16 + j] : v[j]) + __shfl_xor(send, 8, 64);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool up = (c & 4) != 0;
+      const float send = up ? v[j] : v[8 + j];
+      v[j] = (up ? v[8 + j] : v[j]) + __shfl_xor(send, 4, 64);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool up = (c & 2) != 0;
+      const float send = up ? v[j] : v[4 + j];
+      v[j] = (up ? v[4 + j] : v[j]) + __shfl_xor(send, 2, 64);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bool up = (c & 1) != 0;
+      const float send = up ? v[j] : v[2 + j];
+      v[j] = (up ? v[2 + j] : v[j]) + __shfl_xor(send, 1, 64);
+    }
+    {  // v[0], v[1]: head c / 4, rows i = 2 (c % 4) and i + 1
+      const int hh = c >> 2, i = 2 * (c & 3);
+      const int rl = wave * 32 + 4 * i + sr, rb = r0 + ch * CROWS;
+      logit[hh][rl] = (rb + rl < n) ? v[0] : -INFINITY;
+      logit[hh][rl + 4] = (rb + rl + 4 < n) ? v[1] : -INFINITY;
+    }
+    __syncthreads();
+    // chunk statistics: wave w updates head w's running max and sum
+    if (wave < G && wave < HG) {
+      const float a = logit[wave][lane], bq = logit[wave][lane + 64];
+      const float mo = mrun[wave];
+      const float mn = fmaxf(mo, wave_max(fmaxf(a, bq)));
+      const float pa = (a == -INFINITY) ? 0.f : __expf(a - mn);
+      const float pb = (bq == -INFINITY) ? 0.f : __expf(bq - mn);
+      const float ls = wave_sum(pa + pb);
+      logit[wave][lane] = pa;
+      logit[wave][lane + 64] = pb;
+      if (lane == 0) {
+        const float al = (mo == -INFINITY) ? 0.f : __expf(mo - mn);
+        alpha[wave] = al;
+        mrun[wave] = mn;
+        lrun[wave] = lrun[wave] * al + ls;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+      const float al = alpha[hh];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[hh][e] *= al;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float vf[8];
+      bf8(vr[i], vf);
+      const int rl = wave * 32 + 4 * i + sr;
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh) {
+        const float pr = logit[hh][rl];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(pr, vf[e], acc[hh][e]);
+      }
+    }
+    if (ch + 1 < nch) load_v(ch + 1);
+    __syncthreads();  // logit and alpha are rewritten by the next chunk
+  }
+  // reduce over the 4 row lanes of each chunk, then over waves
+#pragma unroll
+  for (int hh = 0; hh < HG; ++hh)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = acc[hh][e];
+      x += __shfl_xor(x, 16, 64);
+      x += __shfl_xor(x, 32, 64);
+      acc[hh][e] = x;
+    }
+  if (sr == 0) {
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[wave][hh][c * 8 + e] = acc[hh][e];
+  }
+  __syncthreads();
+  for (int idx = t; idx < G * DH; idx += 256) {
+    const int hh = idx / DH, d = idx % DH;
+    const float o = red[0][hh][d] + red[1][hh][d] + red[2][hh][d] + red[3][hh][d];
+    const int h = g * G + hh;
+    float* dst = part + (((size_t)b * Hq + h) * nsplit + split) * (DH + 2);
+    dst[2 + d] = o;
+    if (d == 0) { dst[0] = mrun[hh]; dst[1] = lrun[hh]; }
+  }
+}
+
 // Combine: one workgroup per (batch, query head). Split weights
 // w_s = exp(m_s - M) and L = sum w_s l_s are formed in parallel; each wave
 // then sums a quarter of the splits for all 128 features and the quarters are
@@ -269,10 +445,27 @@ int iskv_launch_attend(const uint16_t* q, const uint16_t* K, const uint16_t* V, 
                        int32_t n, int32_t Hq, int32_t Hkv, int32_t dh, float scale, uint16_t* out,
                        void* ws, size_t ws_bytes, hipStream_t s) {
   (void)dh;
-  const int ns = num_splits(n);
   if (ws_bytes < iskv_attend_ws_bytes(batch, n, Hq, dh)) return ISKV_EWORKSPACE;
-  hipLaunchKernelGGL(attend_split_kernel, dim3(ns, Hkv, batch), dim3(256), 0, s, q, K, V, n, Hq, Hkv,
-                     scale, (float*)ws);
+  int ns = num_splits(n);
+  if (Hq / Hkv <= HG) {
+    // streaming form; chunks of 128 rows per workgroup by length (measured at
+    // 8 KV heads: one chunk is fastest up to ~32K rows, where the grid
+    // already holds a thousand workgroups; longer caches fold 4 or 8 chunks
+    // per workgroup and keep the combine's partials few)
+    const int chunks = (n + CROWS - 1) / CROWS;
+    auto go = [&](auto nch_c) {
+      constexpr int NCH = decltype(nch_c)::value;
+      const int nsp = (chunks + NCH - 1) / NCH;
+      hipLaunchKernelGGL((attend_stream_kernel<NCH>), dim3(nsp, Hkv, batch), dim3(256), 0, s, q, K, V, n, Hq, Hkv,
+                         scale, (float*)ws);
+      return nsp;
+    };
+    ns = chunks <= 256 ? go(std::integral_constant<int, 1>{})
+                       : (chunks <= 1024 ? go(std::integral_constant<int, 4>{}) : go(std::integral_constant<int, 8>{}));
+  } else {
+    hipLaunchKernelGGL(attend_split_kernel, dim3(ns, Hkv, batch), dim3(256), 0, s, q, K, V, n, Hq, Hkv,
+                       scale, (float*)ws);
+  }
   hipLaunchKernelGGL(attend_combine_kernel, dim3(batch * Hq), dim3(256), (size_t)ns * sizeof(float), s,
                      (const float*)ws, ns, out);
   ISKV_HIP_CHECK(hipGetLastError());

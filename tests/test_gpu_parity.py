@@ -803,8 +803,13 @@ def test_reconstruct_full_size_elementwise(K, c16):
 
 
 # --------------------------------------------------------------------------- attention
-@pytest.mark.parametrize("batch,n,hq,hkv", [(1, 1000, 32, 8), (2, 4096, 32, 8), (1, 63, 8, 8)])
+@pytest.mark.parametrize("batch,n,hq,hkv", [(1, 1000, 32, 8), (2, 4096, 32, 8), (1, 63, 8, 8),
+                                            (2, 33000, 16, 4), (1, 140000, 32, 8), (1, 3000, 32, 4)])
 def test_decode_attend_matches_oracle(K, batch, n, hq, hkv):
+    """Dense GQA decode attention against the oracle: one 128-row chunk per
+    workgroup (up to 32K rows), 4 chunks (33,000 rows, two sequences), 8
+    chunks (140,000 rows), the ragged tail of each, MHA (one query head per
+    KV head) and 8 query heads per KV head (the split form)."""
     rng = np.random.default_rng(n)
     Kc = torch.from_numpy(rng.standard_normal((batch, n, hkv, 128)).astype(np.float32)).to(DEV).bfloat16()
     Vc = torch.from_numpy(rng.standard_normal((batch, n, hkv, 128)).astype(np.float32)).to(DEV).bfloat16()
