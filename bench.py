@@ -698,10 +698,10 @@ def main():
                                 "rewrite; frozen basis stores F B only"},
         "coord_update": {"bound": "hbm", "achieved": cu_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": cu_gbps / HBM_PEAK_GBPS, "algorithmic_bytes": cu_bytes, "rows": n_cu,
-                         "traffic": profiled_traffic("xh_bf3_kernel_coord_update_kv_n16k_traffic.md"),
+                         "traffic": profiled_traffic("xh_bf3s_kernel_coord_update_kv_n16k_traffic.md"),
                          "effective_tflops": cu_tflops, "bf16_mfma_frac": cu_bf16_frac,
-                         "kernel": "xh_bf3_kernel (old rows C <- C H[:k], split-bf16 MFMA: 3 bf16 products, "
-                                   "fp32 accumulation)",
+                         "kernel": "xh_bf3s_kernel (old rows C <- C H[:k], streaming split-bf16 MFMA: 3 bf16 "
+                                   "products, fp32 accumulation)",
                          "paths_per_launch": cu_paths, "merges_timed": TIMED_MERGES},
         "setup_s": {"generate": gen_s, "fill_16k_rows": fill_s},
         "core_solver_last_merge": [{"flags": c[11], "steps": c[12], "resid_sweeps": c[14], "k": c[1], "n": c[0]}

@@ -53,6 +53,9 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 typedef float f2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{a, b}, bf2_t));
 }
@@ -1007,6 +1010,187 @@ __global__ __launch_bounds__(1024) void xh_bf3_kernel(TX* X, int ldx, Dim kin_d,
   iskv_latch_overflow<TX>(st, over);
 }
 
+// Streaming form of the same update for r_max = 256 (ldx = 256): a
+// 512-thread workgroup per CU, wave w owning output columns 32 w .. 32 w + 31
+// (two 16-column blocks of split H as A operands, so each lane's result is
+// four consecutive columns of one row: one 16- or 8-byte store per block and
+// column block). The workgroup's 16-row blocks b0, b0 + G, ... pass through a
+// three-stage pipeline: the rows of block j + 2 are requested while block
+// j + 1 is split into the idle LDS image and block j is multiplied, with one
+// barrier per block. Every block issues the same memory operations (loads of
+// a block past the workgroup's last re-read that block and are discarded;
+// stores of rows past the end are dropped by the descriptor, and a block
+// always has at least one row in range), and the prologue issues, after the
+// rows of the first two blocks, the stores of one block into a scratch line
+// that nothing reads, so the wait counts at the head of the loop equal the
+// steady state's: the in-order counter waits for exactly the block in use.
+// Columns in [kout, r_max) receive zeros (H is zero there).
+constexpr int XS_NT = 512;  // threads of the streaming update
+
+template <typename TX>
+__global__ __launch_bounds__(XS_NT) void xh_bf3s_kernel(TX* X, int ldx, Dim kin_d, const uint4* __restrict__ Hs,
+                                                        int NW, int NS, Dim kout_d, Dim rows_d, int32_t* st,
+                                                        float* scratch, int scratch_lines,
+                                                        const int64_t* __restrict__ bd) {
+  const int64_t bdel = bd ? bd[blockIdx.z] : 0;
+  X = iskv_rb(X, bdel);
+  st = iskv_rb(st, bdel);
+  Hs = iskv_rb(Hs, bdel);
+  scratch = iskv_rb(scratch, bdel);
+  iskv_rb_dim(kin_d, bdel);
+  iskv_rb_dim(kout_d, bdel);
+  iskv_rb_dim(rows_d, bdel);
+  constexpr bool SPLIT_X = !std::is_same<TX, uint16_t>::value;
+  constexpr int ES = (int)sizeof(TX);
+  const int kin = dval(kin_d), kout = dval(kout_d), rows = dval(rows_d);
+  const int nblk = (rows + 15) / 16;
+  const int G = gridDim.x, b0 = blockIdx.x;
+  if (b0 >= nblk || kout <= 0 || kin <= 0) return;
+  const int nb = (nblk - b0 + G - 1) / G;  // blocks b0 + j G, j < nb
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[2][SPLIT_X ? 2 : 1][16 * XB_LD];  // [buffer][hi, lo]
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  bool over = false;  // a saturated half store (fp16 coordinates only)
+  // staging: thread t holds row t / 32, columns 8 (t % 32) .. +7 of a block
+  const int sr = t >> 5, sc = (t & 31) * 8;
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, (int)((size_t)rows * ldx * ES), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)scratch, (short)0,
+                                                                      scratch_lines * 128, 0x00020000);
+  const uint32_t soff = (uint32_t)((b0 % scratch_lines) * 128);
+  // rows in flight: fp32 rows as two float4, 2-byte rows as one uint4 of raw bits
+  uint4 ring[2][ES == 4 ? 2 : 1];
+  auto load = [&](auto slot_c, int j) {
+    constexpr int slot = decltype(slot_c)::value;
+    const int row = min((b0 + min(j, nb - 1) * G) * 16 + sr, rows - 1);
+    const uint32_t o = (uint32_t)(((size_t)row * ldx + sc) * ES);
+    ring[slot][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, 0));
+    if constexpr (ES == 4)
+      ring[slot][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, o + 16, 0, 0));
+  };
+  // split H operands of column blocks 2 w and 2 w + 1 (past NW: zero)
+  const __amdgpu_buffer_rsrc_t rh =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Hs, (short)0, NW * NS * 64 * 16 * 2, 0x00020000);
+  v8bf hh[2][8], hl[2][8];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int sk = 0; sk < 8; ++sk) {
+      const int w = 2 * wave + q;
+      const bool in = sk < NS && w < NW;
+      const uint32_t oa = in ? (uint32_t)(((w * NS + sk) * 64 + lane) * 16) : 0x80000000u;
+      const uint32_t ob = in ? (uint32_t)(((NW * NS + w * NS + sk) * 64 + lane) * 16) : 0x80000000u;
+      hh[q][sk] = __builtin_bit_cast(v8bf, __builtin_amdgcn_raw_buffer_load_b128(rh, oa, 0, 0));
+      hl[q][sk] = __builtin_bit_cast(v8bf, __builtin_amdgcn_raw_buffer_load_b128(rh, ob, 0, 0));
+    }
+  __builtin_amdgcn_sched_barrier(0);  // H is requested first, so it has arrived once block 0 has
+  load(std::integral_constant<int, 0>{}, 0);
+  load(std::integral_constant<int, 1>{}, 1);
+  __builtin_amdgcn_raw_buffer_store_b128(v4u{0u, 0u, 0u, 0u}, rs, soff, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(v4u{0u, 0u, 0u, 0u}, rs, soff + 64, 0, 0);
+  // split the rows of a slot into the LDS images (rows past the end and
+  // columns >= kin as zero)
+  auto stage = [&](auto slot_c, int j, int buf) {
+    constexpr int slot = decltype(slot_c)::value;
+    const bool rv = (b0 + j * G) * 16 + sr < rows;
+    float x[8];
+    if constexpr (ES == 4) {
+      const uint4 a = ring[slot][0], b = ring[slot][1];
+      const uint32_t u[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = __uint_as_float(u[e]);
+    } else if constexpr (std::is_same<TX, _Float16>::value) {
+      const uint4 a = ring[slot][0];
+      const uint32_t u[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const h2_t hv = __builtin_bit_cast(h2_t, u[e]);
+        x[2 * e] = (float)hv.x;
+        x[2 * e + 1] = (float)hv.y;
+      }
+    } else {
+      const uint4 a = ring[slot][0];
+      const uint32_t u[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = __uint_as_float(u[e] << 16);
+        x[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+      }
+    }
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = (rv && sc + 2 * e < kin) ? x[2 * e] : 0.f;
+      const float b = (rv && sc + 2 * e + 1 < kin) ? x[2 * e + 1] : 0.f;
+      hi[e] = pk_bf16(a, b);
+      lo[e] = pk_bf16(a - __uint_as_float(hi[e] << 16), b - __uint_as_float(hi[e] & 0xffff0000u));
+    }
+    *(uint4*)(&Xs[buf][0][sr * XB_LD + sc]) = uint4{hi[0], hi[1], hi[2], hi[3]};
+    if constexpr (SPLIT_X) *(uint4*)(&Xs[buf][SPLIT_X ? 1 : 0][sr * XB_LD + sc]) = uint4{lo[0], lo[1], lo[2], lo[3]};
+  };
+  stage(std::integral_constant<int, 0>{}, 0, 0);
+  __syncthreads();
+  const int cw = 32 * wave + 4 * (lane >> 4);  // this lane's first output column (column block 0)
+
+  auto process = [&](auto slot_c, int j) {
+    constexpr int slot = decltype(slot_c)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    const int buf = j & 1;
+    v8bf ah[8], al[8];
+    const uint16_t* xh = &Xs[buf][0][(lane & 15) * XB_LD + 8 * (lane >> 4)];
+#pragma unroll
+    for (int sk = 0; sk < 8; ++sk) {
+      ah[sk] = __builtin_bit_cast(v8bf, *(const uint4*)(xh + 32 * sk));
+      if constexpr (SPLIT_X) {
+        const uint16_t* xl = &Xs[buf][SPLIT_X ? 1 : 0][(lane & 15) * XB_LD + 8 * (lane >> 4)];
+        al[sk] = __builtin_bit_cast(v8bf, *(const uint4*)(xl + 32 * sk));
+      }
+    }
+    stage(std::integral_constant<int, slot ^ 1>{}, j + 1, buf ^ 1);
+    load(slot_c, j + 2);
+    v4f_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int sk = 0; sk < 8; ++sk) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hh[q][sk], ah[sk], acc[q], 0, 0, 0);
+        acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hl[q][sk], ah[sk], acc[q], 0, 0, 0);
+        if constexpr (SPLIT_X) acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hh[q][sk], al[sk], acc[q], 0, 0, 0);
+      }
+    }
+    // result lane l, element e: row i0 + l % 16, column cw + 16 q + e
+    const int row = (b0 + j * G) * 16 + (lane & 15);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t o = row < rows ? (uint32_t)(((size_t)row * ldx + cw + 16 * q) * ES) : 0x80000000u;
+      if constexpr (ES == 4) {
+        const v4u v = __builtin_bit_cast(v4u, acc[q]);
+        __builtin_amdgcn_raw_buffer_store_b128(v, rx, o, 0, 0);
+      } else {
+        uint32_t p0, p1;
+        if constexpr (std::is_same<TX, _Float16>::value) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) over |= row < rows && iskv_f16_over(acc[q][e]);
+          p0 = __builtin_bit_cast(uint32_t, h2_t{iskv_to_f16(acc[q][0]), iskv_to_f16(acc[q][1])});
+          p1 = __builtin_bit_cast(uint32_t, h2_t{iskv_to_f16(acc[q][2]), iskv_to_f16(acc[q][3])});
+        } else {
+          p0 = pk_bf16(acc[q][0], acc[q][1]);
+          p1 = pk_bf16(acc[q][2], acc[q][3]);
+        }
+        __builtin_amdgcn_raw_buffer_store_b64(v2u{p0, p1}, rx, o, 0, 0);
+      }
+    }
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int jb = 0;
+  for (; jb + 2 <= nb; jb += 2) {
+    process(std::integral_constant<int, 0>{}, jb);
+    process(std::integral_constant<int, 1>{}, jb + 1);
+  }
+  if (jb < nb) process(std::integral_constant<int, 0>{}, jb);
+  iskv_latch_overflow<TX>(st, over);
+}
+
 // Launch Y = [X1 | X2] H over `rows_host` rows (an upper bound when rows_d is
 // a device value); kin_max bounds kin for the LDS layout.
 template <typename TX, typename TY>
@@ -1467,9 +1651,16 @@ static int merge_body(isvd_handle* h, const float* F, const int32_t* pos_F, int3
   with_coords(h, [&](auto* Cp) {
     using TC = std::remove_pointer_t<decltype(Cp)>;
     if (!(c.flags & ISKV_NO_COORD_SYNC)) {
-      if (bf3) {  // split-bf16 matrix cores, one 1024-thread workgroup per CU at most
-        const int nblk = (c.n_cap + 15) / 16;
-        hipLaunchKernelGGL((xh_bf3_kernel<TC>), bz(dim3(nblk < 256 ? nblk : 256), h->bcount), dim3(1024), 0, s, Cp,
+      const int nblk = (c.n_cap + 15) / 16;
+      const int grid = nblk < 256 ? nblk : 256;  // one workgroup per CU at most
+      if (R == 256 && (size_t)c.n_cap * R * sizeof(TC) < ((size_t)1 << 31) - 4096) {
+        // streaming split-bf16 update; the core scratch Pb (idle here) takes
+        // the stores that nothing reads
+        const int lines = (int)std::min<size_t>((size_t)h->ldm * h->ldm * 8 / 128, 256);
+        hipLaunchKernelGGL((xh_bf3s_kernel<TC>), bz(dim3(grid), h->bcount), dim3(XS_NT), 0, s, Cp, R, ddim(dk),
+                           (const uint4*)w.T2, NW3, NS3, ddim(w.st + ST_KNEW), dn, w.st, (float*)w.Pb, lines, h->bd);
+      } else if (bf3) {  // split-bf16 matrix cores, one 1024-thread workgroup per CU at most
+        hipLaunchKernelGGL((xh_bf3_kernel<TC>), bz(dim3(grid), h->bcount), dim3(1024), 0, s, Cp,
                            R, ddim(dk), (const uint4*)w.T2, NW3, NS3, ddim(w.st + ST_KNEW), dn, w.st, h->bd);
       } else {
         xh_launch(s, h->bd, h->bcount, c.n_cap, Cp, R, nullptr, 0, ddim(dk), ddim(dk), R, w.Hc, R, R,
