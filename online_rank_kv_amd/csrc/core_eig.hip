@@ -885,11 +885,13 @@ __device__ void jacobi_group(double (&srow)[CMAX_S], double (&vrow)[CMAX_S], int
   }
 }
 
-// Strong pairs and per-block maxima of the scaled coupling, many workgroups
-// (first refinement step, where S = A; later steps detect in the epilogue of
-// the GEMM that forms S). Block b scans rows [16 b, 16 b + 16) against every
-// column j > i and writes its maximum to aux[b]. Strong pairs are appended to
-// the edge list (order fixed later by sorting).
+// Strong pairs and per-tile maxima of the scaled coupling, one 16 x 16 tile
+// of S per workgroup (first refinement step, where S = A; later steps detect
+// in the epilogue of the GEMM that forms S). Tile (bi, bj) with bj >= bi
+// checks its pairs i < j and writes its largest coupling to aux[bi nb + bj]
+// (tiles below the diagonal write 0). Strong pairs are appended to the edge
+// list (order fixed later by sorting). Each entry's load is issued before the
+// coupling scale and cut are formed, so the two latencies overlap.
 __global__ __launch_bounds__(256) void pcj_detect_kernel(const double* __restrict__ S, int ld,
                                                          double* aux, int* edges, int32_t* st, double tol, int keep,
     const int64_t* __restrict__ bd) {
@@ -900,26 +902,36 @@ __global__ __launch_bounds__(256) void pcj_detect_kernel(const double* __restric
   st = iskv_rb(st, bdel);
   if (st[ST_PCJ] & FLAG_CONV) return;
   const int m = st[ST_JM];
-  const int r0 = blockIdx.x * 16;
+  const int bi = blockIdx.y, bj = blockIdx.x, tile = bi * gridDim.x + bj;
+  const int i = 16 * bi + (threadIdx.x >> 4), j = 16 * bj + (threadIdx.x & 15);
+  if (bj < bi || 16 * bi >= m || 16 * bj >= m) {
+    if (threadIdx.x == 0) aux[tile] = 0.0;
+    return;
+  }
+  const bool pair = i < m && j < m && j > i;
+  const double sij = pair ? S[(size_t)i * ld + j] : 0.0;
   __shared__ double red[4];
   // coupling scale (the largest diagonal entry) and cut (between the keep-th
   // and (keep+1)-th largest diagonal entries, geometric mean), rounded to
   // fp32 so that the later steps (reading them from st) use the same values;
-  // every workgroup forms them from S = A, block 0 publishes them. keep < 0:
-  // scaled couplings; keep >= m: nothing dropped.
-  __shared__ double dl[1024];
+  // every workgroup forms them from S = A, tile (0, 0) publishes them.
+  // keep < 0: scaled couplings; keep >= m: nothing dropped.
+  __shared__ double dg[1024], dl[1024];
   __shared__ double cred[3][4];
   double dmax = 0.0, hi = INFINITY, lo = 0.0;
-  for (int i = threadIdx.x; i < m; i += 256) {
-    dl[i] = fabs(S[(size_t)i * ld + i]);
-    dmax = fmax(dmax, dl[i]);
+  for (int e = threadIdx.x; e < m; e += 256) {
+    const double d = S[(size_t)e * ld + e];
+    dg[e] = d;
+    dl[e] = fabs(d);
+    dmax = fmax(dmax, fabs(d));
   }
   __syncthreads();
   if (keep >= 0 && keep < m)
-    for (int i = threadIdx.x; i < m; i += 256) {
-      const double v = dl[i];
+    for (int e = threadIdx.x; e < m; e += 256) {
+      const double v = dl[e];
       int above = 0;
-      for (int j = 0; j < m; ++j) above += dl[j] > v;
+#pragma unroll 8
+      for (int q = 0; q < m; ++q) above += dl[q] > v;
       if (above < keep) hi = fmin(hi, v);
       else lo = fmax(lo, v);
     }
@@ -947,31 +959,25 @@ __global__ __launch_bounds__(256) void pcj_detect_kernel(const double* __restric
   const double cut = (keep >= 0 && keep < m && isfinite(hi)) ? sqrt(hi * lo) : -1.0;
   const float fcut = prod && cut >= 0.0 ? (float)cut : -1.f;
   const double sref = prod ? (double)fu : 0.0, dcut = (double)fcut;
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
+  if (tile == 0 && threadIdx.x == 0) {
     st[ST_SREF] = prod ? __float_as_int(fu) : 0;
     st[ST_DCUT] = __float_as_int(fcut);
   }
   double cmax = 0.0;
-  if (r0 < m) {
-    const int rows = min(16, m - r0);
-    for (int e = threadIdx.x; e < rows * m; e += 256) {
-      int i = r0 + e / m, j = e % m;
-      if (j <= i) continue;
-      double sij = S[(size_t)i * ld + j];
-      double di = S[(size_t)i * ld + i], dj = S[(size_t)j * ld + j];
-      double c = coupling_at(sij, di, dj, sref, dcut);
-      if (c > cmax) cmax = c;
-      if (c > tol && fabs(sij) > PCJ_OMEGA * fabs(dj - di)) {
-        int slot = atomicAdd(&st[ST_NEDGE], 1);
-        if (slot < EMAX) { edges[2 * slot] = i; edges[2 * slot + 1] = j; }
-      }
+  if (pair) {
+    const double di = dg[i], dj = dg[j];
+    const double c = coupling_at(sij, di, dj, sref, dcut);
+    cmax = c;
+    if (c > tol && fabs(sij) > PCJ_OMEGA * fabs(dj - di)) {
+      int slot = atomicAdd(&st[ST_NEDGE], 1);
+      if (slot < EMAX) { edges[2 * slot] = i; edges[2 * slot + 1] = j; }
     }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) cmax = fmax(cmax, __shfl_xor(cmax, o, 64));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = cmax;
   __syncthreads();
-  if (threadIdx.x == 0) aux[blockIdx.x] = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+  if (threadIdx.x == 0) aux[tile] = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
 }
 
 struct AnalyzeLds {
@@ -1822,9 +1828,9 @@ int iskv_launch_core_eig(isvd_handle* h, double tol, int keep) {
   }
   hipLaunchKernelGGL(pcj_init_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.A, w.S, w.W0, ld, st, h->bd);
   // step 0 works on S = A with W = I
-  hipLaunchKernelGGL(pcj_detect_kernel, bz(dim3(nblk), h->bcount), dim3(256), 0, s, w.S, ld, w.aux, w.edges, st,
-                     tol, keep, h->bd);
-  hipLaunchKernelGGL(pcj_analyze_kernel, bz(dim3(1), h->bcount), dim3(1024), lds, s, w.S, ld, w.aux, nblk,
+  hipLaunchKernelGGL(pcj_detect_kernel, bz(dim3(nblk, nblk), h->bcount), dim3(256), 0, s, w.S, ld, w.aux, w.edges,
+                     st, tol, keep, h->bd);
+  hipLaunchKernelGGL(pcj_analyze_kernel, bz(dim3(1), h->bcount), dim3(1024), lds, s, w.S, ld, w.aux, nblk * nblk,
                      w.edges, w.itab, w.rtab, h->m_max, st, 0, tol, h->bd);
   hipLaunchKernelGGL(pcj_kmat_kernel, bz(dim3(128), h->bcount), dim3(256), 0, s, w.S, ld, w.Km, w.Pa, w.W0, w.itab,
                      w.rtab, h->m_max, st, h->bd);
