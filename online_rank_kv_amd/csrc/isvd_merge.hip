@@ -484,12 +484,16 @@ __global__ __launch_bounds__(HB * HB) void resid_basis_kernel(const double* __re
   }
 }
 
-// P[:, j] = E^T V_E[:, j] / rho_j for j < p (D x b_max, fp64 accumulation);
-// one thread per (d, j).
-__global__ __launch_bounds__(256) void make_p_kernel(const float* __restrict__ E, int D, int b,
-                                                     const double* __restrict__ VE,
-                                                     const double* __restrict__ rho, float* P,
-                                                     int ldp, const int32_t* st,
+// P[:, j] = E^T V_E[:, j] / rho_j for j < p (D x b_max, fp64 accumulation).
+// Workgroup: 64 features d and all columns; thread (d, g) forms columns
+// 8 g .. 8 g + 7 of row d from V_E staged in LDS (the rows of E are read
+// coalesced along d, all b of them in flight at once) and writes them as
+// 32 contiguous bytes.
+constexpr int MP_BMAX = 64;  // largest block (b_max <= 64: at most 512 threads, 33 KiB of LDS)
+__global__ __launch_bounds__(8 * MP_BMAX) void make_p_kernel(const float* __restrict__ E, int D, int b,
+                                                      const double* __restrict__ VE,
+                                                      const double* __restrict__ rho, float* P,
+                                                      int ldp, const int32_t* st,
     const int64_t* __restrict__ bd) {
   const int64_t bdel = bd ? bd[blockIdx.z] : 0;
   E = iskv_rb(E, bdel);
@@ -497,13 +501,41 @@ __global__ __launch_bounds__(256) void make_p_kernel(const float* __restrict__ E
   rho = iskv_rb(rho, bdel);
   P = iskv_rb(P, bdel);
   st = iskv_rb(st, bdel);
+  extern __shared__ double mp_lds[];  // V_E (b x b), then 1 / rho (b)
   const int p = st[ST_P];
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  const int d = e / ldp, j = e % ldp;
-  if (d >= D || j >= p) return;
-  double acc = 0.0;
-  for (int i = 0; i < b; ++i) acc = fma((double)E[(size_t)i * D + d], VE[i * b + j], acc);
-  P[(size_t)d * ldp + j] = (float)(acc / rho[j]);
+  const int t = threadIdx.x, d = blockIdx.x * 64 + (t & 63), g = t >> 6;
+  for (int e = t; e < b * b; e += blockDim.x) mp_lds[e] = VE[e];
+  for (int e = t; e < b; e += blockDim.x) mp_lds[b * b + e] = e < p ? 1.0 / rho[e] : 0.0;
+  __syncthreads();
+  if (d >= D || 8 * g >= p) return;
+  double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+  for (int i0 = 0; i0 < b; i0 += 16) {
+    float ev[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) ev[u] = E[(size_t)min(i0 + u, b - 1) * D + d];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      if (i0 + u < b) {
+        const double x = (double)ev[u];
+        const double* v = mp_lds + (i0 + u) * b;
+        // columns past b are never stored: their index is only kept in range
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = fma(x, v[min(8 * g + q, b - 1)], acc[q]);
+      }
+    }
+  }
+  float o[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) o[q] = (float)(acc[q] * mp_lds[b * b + min(8 * g + q, b - 1)]);
+  float* dst = P + (size_t)d * ldp + 8 * g;
+  if (8 * g + 8 <= p && (ldp & 3) == 0) {
+    *(float4*)dst = float4{o[0], o[1], o[2], o[3]};
+    *(float4*)(dst + 4) = float4{o[4], o[5], o[6], o[7]};
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (8 * g + q < p) dst[q] = o[q];
+  }
 }
 
 // Core Gram A = diag(sigma^2, 0_p) + M^T M in fp64, M = [Q[:, :k], FP[:, :p]] (b x m).
@@ -556,7 +588,7 @@ __global__ __launch_bounds__(1024) void eig_order_kernel(const double* __restric
   order = iskv_rb(order, bdel);
   st = iskv_rb(st, bdel);
   __shared__ double lam[1024], key[1024];
-  __shared__ int rnk[1024];
+  __shared__ int rnk[1024], ord[1024];
   const int n = st[ST_JM];
   const int t = threadIdx.x;
   for (int i = t; i < n; i += blockDim.x) {
@@ -566,23 +598,33 @@ __global__ __launch_bounds__(1024) void eig_order_kernel(const double* __restric
   }
   __syncthreads();
   // rank of i = entries ahead of it (larger, or equal at a lower index); the
-  // n x n comparisons are split over the workgroup in quarters of j
+  // n x n comparisons are split over the workgroup in quarters of j, read
+  // eight keys at a time
   const int qn = (n + 3) / 4;
   for (int e = t; e < 4 * n; e += blockDim.x) {
     const int i = e >> 2, j0 = (e & 3) * qn, j1 = min(j0 + qn, n);
     const double ki = key[i];
     int c = 0;
-    for (int j = j0; j < j1; ++j) {
+    int j = j0;
+    for (; j + 8 <= j1; j += 8) {
+      double kj[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) kj[u] = key[j + u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c += (kj[u] > ki) || (kj[u] == ki && j + u < i);
+    }
+    for (; j < j1; ++j) {
       const double kj = key[j];
       c += (kj > ki) || (kj == ki && j < i);
     }
     atomicAdd(&rnk[i], c);
   }
   __syncthreads();
-  for (int i = t; i < n; i += blockDim.x) order[rnk[i]] = i;
+  for (int i = t; i < n; i += blockDim.x) ord[rnk[i]] = i;
   __syncthreads();
+  for (int i = t; i < n; i += blockDim.x) order[i] = ord[i];
   const int keep = for_merge ? (n < r_max ? n : r_max) : n;
-  for (int c = t; c < keep; c += blockDim.x) sig_new[c] = (float)sqrt(fmax(lam[min(max(order[c], 0), n - 1)], 0.0));
+  for (int c = t; c < keep; c += blockDim.x) sig_new[c] = (float)sqrt(fmax(lam[min(max(ord[c], 0), n - 1)], 0.0));
   if (t == 0 && for_merge) st[ST_KNEW] = keep;
 }
 
@@ -1619,8 +1661,9 @@ static int merge_body(isvd_handle* h, const float* F, const int32_t* pos_F, int3
   else
     hipLaunchKernelGGL(resid_basis_kernel<32>, bz(dim3(1), h->bcount), dim3(1024), resid_lds_bytes(32), s, w.GE, b,
                        D, h->sigma, c.resid_rel_tol, w.VE, w.rho, w.st, ISKV_RESID_MAX_SWEEPS, h->bd);
-  hipLaunchKernelGGL(make_p_kernel, bz(dim3((D * c.b_max + 255) / 256), h->bcount), dim3(256), 0, s, w.E, D, b, w.VE,
-                     w.rho, w.P, c.b_max, w.st, h->bd);
+  hipLaunchKernelGGL(make_p_kernel, bz(dim3((D + 63) / 64), h->bcount), dim3(64 * ((c.b_max + 7) / 8)),
+                     (size_t)(c.b_max * c.b_max + c.b_max) * sizeof(double), s, w.E, D, b, w.VE, w.rho, w.P, c.b_max,
+                     w.st, h->bd);
   // 6. FP = F P (b x p)
   skinny<false>(h, b, c.b_max, F, D, w.P, c.b_max, ddim(dp), D, 1.f, 0.f, nullptr, 0, w.FP, c.b_max);
   mark(2);
