@@ -1483,8 +1483,10 @@ __global__ __launch_bounds__(256) void store_sym_kernel(const double* __restrict
 // group g = l/16) takes depths 16 s + 4 g + q for MFMA step q: the summation
 // order over k is permuted so that each lane's four operands are consecutive
 // in memory. Depths >= K, rows >= M and columns >= N are masked or dropped.
+// VEC (X rows, and Y rows when TY, 16-byte aligned with a leading dimension
+// divisible by 4): a lane's four consecutive depths come in one 16-byte load.
 constexpr int SK_CPW = 4;
-template <bool TY, int NW>
+template <bool TY, int NW, bool VEC>
 __global__ __launch_bounds__(64 * NW) void skinny_mfma_kernel(const float* __restrict__ X, int ldx,
                                                                const float* __restrict__ Y, int ldy, int M,
                                                                int Nmax, Dim Nd, Dim Kd, float alpha,
@@ -1512,13 +1514,25 @@ __global__ __launch_bounds__(64 * NW) void skinny_mfma_kernel(const float* __res
 #pragma unroll
     for (int u = 0; u < SK_CPW; ++u) {
       const int kb = (c0 + NW * u) * 16 + 4 * g;
+      if (VEC && kb + 4 <= K) {
+        const float4 a = *(const float4*)(xr + kb);
+        av[u][0] = a.x; av[u][1] = a.y; av[u][2] = a.z; av[u][3] = a.w;
+        if constexpr (TY) {
+          const float4 y = *(const float4*)(Y + (size_t)col * ldy + kb);
+          bv[u][0] = y.x; bv[u][1] = y.y; bv[u][2] = y.z; bv[u][3] = y.w;
+        } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int k = kb + q, kc = min(k, K - 1);
-        const float a = xr[kc];
-        const float bb = TY ? Y[(size_t)col * ldy + kc] : Y[(size_t)kc * ldy + col];
-        av[u][q] = k < K ? a : 0.f;
-        bv[u][q] = k < K ? bb : 0.f;
+          for (int q = 0; q < 4; ++q) bv[u][q] = Y[(size_t)(kb + q) * ldy + col];
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int k = kb + q, kc = min(k, K - 1);
+          const float a = xr[kc];
+          const float bb = TY ? Y[(size_t)col * ldy + kc] : Y[(size_t)kc * ldy + col];
+          av[u][q] = k < K ? a : 0.f;
+          bv[u][q] = k < K ? bb : 0.f;
+        }
       }
     }
 #pragma unroll
@@ -1556,12 +1570,25 @@ static void skinny(isvd_handle* h, int M, int Nmax, const float* X, int ldx, con
   Dim K = TY ? ddim(h->w.st + ST_K) : hdim(Kmax);
   dim3 grid((Nmax + 15) / 16, (M + 15) / 16);
   const int nch = (Kmax + 15) / 16;
-  if (nch > 4 * SK_CPW)
-    hipLaunchKernelGGL((skinny_mfma_kernel<TY, 16>), bz(grid, h->bcount), dim3(1024), 0, h->stream, X, ldx, Y, ldy,
-                       M, Nmax, N, K, alpha, beta, Z, ldz, out, ldo, h->bd);
-  else
-    hipLaunchKernelGGL((skinny_mfma_kernel<TY, 4>), bz(grid, h->bcount), dim3(256), 0, h->stream, X, ldx, Y, ldy,
-                       M, Nmax, N, K, alpha, beta, Z, ldz, out, ldo, h->bd);
+  // one path: its pointers are checked here (batched paths are rebased on the
+  // device by offsets the host does not inspect, so they keep scalar loads)
+  const bool vec = h->bcount == 1 && ldx % 4 == 0 && ((uintptr_t)X & 15) == 0 &&
+                   (!TY || (ldy % 4 == 0 && ((uintptr_t)Y & 15) == 0));
+  if (nch > 4 * SK_CPW) {
+    if (vec)
+      hipLaunchKernelGGL((skinny_mfma_kernel<TY, 16, true>), bz(grid, h->bcount), dim3(1024), 0, h->stream, X, ldx,
+                         Y, ldy, M, Nmax, N, K, alpha, beta, Z, ldz, out, ldo, h->bd);
+    else
+      hipLaunchKernelGGL((skinny_mfma_kernel<TY, 16, false>), bz(grid, h->bcount), dim3(1024), 0, h->stream, X, ldx,
+                         Y, ldy, M, Nmax, N, K, alpha, beta, Z, ldz, out, ldo, h->bd);
+  } else {
+    if (vec)
+      hipLaunchKernelGGL((skinny_mfma_kernel<TY, 4, true>), bz(grid, h->bcount), dim3(256), 0, h->stream, X, ldx, Y,
+                         ldy, M, Nmax, N, K, alpha, beta, Z, ldz, out, ldo, h->bd);
+    else
+      hipLaunchKernelGGL((skinny_mfma_kernel<TY, 4, false>), bz(grid, h->bcount), dim3(256), 0, h->stream, X, ldx, Y,
+                         ldy, M, Nmax, N, K, alpha, beta, Z, ldz, out, ldo, h->bd);
+  }
 }
 
 static void eig_finish(isvd_handle* h, int for_merge) {
