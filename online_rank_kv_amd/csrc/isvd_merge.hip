@@ -632,17 +632,23 @@ __global__ __launch_bounds__(1024) void eig_order_kernel(const double* __restric
 // column whose index is an old direction (t < k) is signed so that
 // H[t, t] >= 0, i.e. the basis moves continuously; the synced product does
 // not depend on it, the basis-only ablation does. Grid-stride, many blocks.
+// With Hf, also writes H in the operand order of xh_reg_kernel (XF_KQ groups
+// of four k steps per wave): element j of float4 ((w XF_KQ + q) 64 + l) is
+// H[4 (4 q + j) + l / 16, 16 w + l % 16] (zero outside n x keep), so each lane
+// of the right-multiplication loads its H operands as 16-byte pieces.
+constexpr int XF_KQ = 18;  // 72 k steps of 4: rows up to 288
 __global__ __launch_bounds__(256) void eig_gather_kernel(const double* __restrict__ V, int ld,
                                                          float* Hc, int ldh,
                                                          const int32_t* __restrict__ order,
                                                          const int32_t* __restrict__ st, int r_max,
-                                                         int for_merge,
+                                                         int for_merge, float* Hf,
     const int64_t* __restrict__ bd) {
   const int64_t bdel = bd ? bd[blockIdx.z] : 0;
   V = iskv_rb(V, bdel);
   Hc = iskv_rb(Hc, bdel);
   order = iskv_rb(order, bdel);
   st = iskv_rb(st, bdel);
+  Hf = iskv_rb(Hf, bdel);
   const int n = st[ST_JM];
   const int keep = for_merge ? (n < r_max ? n : r_max) : n;
   const int kold = for_merge ? st[ST_K] : 0;
@@ -653,6 +659,20 @@ __global__ __launch_bounds__(256) void eig_gather_kernel(const double* __restric
     double v = V[(size_t)row * ld + oc];
     if (col < kold && V[(size_t)col * ld + oc] < 0.0) v = -v;
     Hc[(size_t)row * ldh + col] = (float)v;
+  }
+  if (Hf) {
+    constexpr int NF = 16 * XF_KQ * 64 * 4;
+    for (int e = blockIdx.x * 256 + threadIdx.x; e < NF; e += gridDim.x * 256) {
+      const int j = e & 3, l = (e >> 2) & 63, q = (e >> 8) % XF_KQ, w = (e >> 8) / XF_KQ;
+      const int row = 4 * (4 * q + j) + (l >> 4), col = 16 * w + (l & 15);
+      double v = 0.0;
+      if (row < n && col < keep) {
+        const int oc = min(max(order[col], 0), n - 1);
+        v = V[(size_t)row * ld + oc];
+        if (col < kold && V[(size_t)col * ld + oc] < 0.0) v = -v;
+      }
+      Hf[e] = (float)v;
+    }
   }
 }
 
@@ -806,6 +826,7 @@ __global__ __launch_bounds__(1024) void xh_reg_kernel(const TX* X1, int ld1, con
                                                       int ldh, int hcols, Dim kout_d, Dim rows_d, TY* Y,
                                                       int ldy, uint16_t* Ybf, int ldbf, int32_t* pos,
                                                       const int32_t* pos_src, Dim yoff_d, int32_t* st,
+                                                      const float4* __restrict__ Hf,
     const int64_t* __restrict__ bd) {
   const int64_t bdel = bd ? bd[blockIdx.z] : 0;
   X1 = iskv_rb(X1, bdel);
@@ -813,6 +834,7 @@ __global__ __launch_bounds__(1024) void xh_reg_kernel(const TX* X1, int ld1, con
   iskv_rb_dim(k1_d, bdel);
   iskv_rb_dim(kin_d, bdel);
   H = iskv_rb(H, bdel);
+  Hf = iskv_rb(Hf, bdel);
   iskv_rb_dim(kout_d, bdel);
   iskv_rb_dim(rows_d, bdel);
   Y = iskv_rb(Y, bdel);
@@ -832,7 +854,16 @@ __global__ __launch_bounds__(1024) void xh_reg_kernel(const TX* X1, int ld1, con
   const int col = wave * 16 + (lane & 15);
   bool over = false;  // a saturated half store (fp16 coordinates only)
   float hreg[XR_KS];
-  {
+  if (Hf) {  // H in operand order (eig_gather_kernel): 16-byte pieces
+    static_assert(XR_KS % 4 == 0 && XR_KS / 4 <= XF_KQ, "operand-order H holds 72 k steps");
+#pragma unroll
+    for (int q = 0; q < XR_KS / 4; ++q) {
+      const float4 f = Hf[(wave * XF_KQ + q) * 64 + lane];
+      const float fv[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) hreg[4 * q + j] = 4 * (4 * q + j) + (lane >> 4) < kin ? fv[j] : 0.f;
+    }
+  } else {
     const int cc = min(col, hcols - 1);
     const char* hb = (const char*)H;
 #pragma unroll
@@ -1240,7 +1271,7 @@ static void xh_launch(hipStream_t s, const int64_t* bd, int bc, int rows_host, c
                       Dim k1, Dim kin, int kin_max, const float* H, int ldh, int hcols, Dim kout,
                       Dim rows, TY* Y, int ldy, uint16_t* Ybf, int ldbf, int32_t* pos = nullptr,
                       const int32_t* pos_src = nullptr, bool prefer16 = false, Dim yoff = hdim(0),
-                      int32_t* st = nullptr) {
+                      int32_t* st = nullptr, const float4* Hf = nullptr) {
   const int ldx = xh_ldx(kin_max);
   if (kin_max <= 288 && hcols <= 256) {
     const int nblk = (rows_host + 15) / 16;
@@ -1248,10 +1279,10 @@ static void xh_launch(hipStream_t s, const int64_t* bd, int bc, int rows_host, c
     if (grid > 0) {
       if (kin_max <= 256)
         hipLaunchKernelGGL((xh_reg_kernel<64, TX, TY>), bz(dim3(grid), bc), dim3(1024), 0, s, X1, ld1, X2, ld2, k1, kin, H,
-                           ldh, hcols, kout, rows, Y, ldy, Ybf, ldbf, pos, pos_src, yoff, st, bd);
+                           ldh, hcols, kout, rows, Y, ldy, Ybf, ldbf, pos, pos_src, yoff, st, Hf, bd);
       else
         hipLaunchKernelGGL((xh_reg_kernel<72, TX, TY>), bz(dim3(grid), bc), dim3(1024), 0, s, X1, ld1, X2, ld2, k1, kin, H,
-                           ldh, hcols, kout, rows, Y, ldy, Ybf, ldbf, pos, pos_src, yoff, st, bd);
+                           ldh, hcols, kout, rows, Y, ldy, Ybf, ldbf, pos, pos_src, yoff, st, Hf, bd);
     }
     return;
   }
@@ -1591,13 +1622,22 @@ static void skinny(isvd_handle* h, int M, int Nmax, const float* X, int ldx, con
   }
 }
 
+// Operand-order copy of a merge's H for the new-row and basis products: in
+// the core scratch Pb (idle after the solve), past the coordinate update's
+// scratch lines; none when Pb is too small or r_max > 256.
+static float* merge_hf(isvd_handle* h) {
+  const size_t off = 65536, need = (size_t)16 * XF_KQ * 64 * 4 * sizeof(float);
+  if (h->cfg.r_max > 256 || (size_t)h->ldm * h->ldm * sizeof(double) < off + need) return nullptr;
+  return (float*)((char*)h->w.Pb + off);
+}
+
 static void eig_finish(isvd_handle* h, int for_merge) {
   const isvd_ws& w = h->w;
   const int R = h->cfg.r_max;
   hipLaunchKernelGGL(eig_order_kernel, bz(dim3(1), h->bcount), dim3(1024), 0, h->stream, w.S, h->ldm, w.sig_new,
                      w.order, w.st, R, for_merge, h->bd);
   hipLaunchKernelGGL(eig_gather_kernel, bz(dim3(128), h->bcount), dim3(256), 0, h->stream, w.V, h->ldm, w.Hc, R,
-                     w.order, w.st, R, for_merge, h->bd);
+                     w.order, w.st, R, for_merge, for_merge ? merge_hf(h) : nullptr, h->bd);
 }
 
 int iskv_launch_sym_eig(isvd_handle* h, const double* A, int32_t m, double* lam, double* V) {
@@ -1739,10 +1779,12 @@ static int merge_body(isvd_handle* h, const float* F, const int32_t* pos_F, int3
     }
     mark(4);
     xh_launch(s, h->bd, h->bcount, b, w.Q, R, w.FP, c.b_max, ddim(dk), ddim(w.st + ST_M), M, w.Hc, R, R,
-              ddim(w.st + ST_KNEW), hdim(b), Cp, R, nullptr, 0, h->pos, pos_F, false, dn, w.st);
+              ddim(w.st + ST_KNEW), hdim(b), Cp, R, nullptr, 0, h->pos, pos_F, false, dn, w.st,
+              (const float4*)merge_hf(h));
   });
   xh_launch(s, h->bd, h->bcount, D, h->B, R, w.P, c.b_max, ddim(dk), ddim(w.st + ST_M), M, w.Hc, R, R,
-            ddim(w.st + ST_KNEW), hdim(D), h->B, R, w.Bbf, R, nullptr, nullptr, true);
+            ddim(w.st + ST_KNEW), hdim(D), h->B, R, w.Bbf, R, nullptr, nullptr, true, hdim(0), nullptr,
+            (const float4*)merge_hf(h));
   hipLaunchKernelGGL(merge_commit_kernel, bz(dim3(1), h->bcount), dim3(256), 0, s, h->sigma, w.sig_new, w.st, b, R, h->bd);
   mark(5);
   if (h->timing) h->timed = true;
