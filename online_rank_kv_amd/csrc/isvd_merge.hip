@@ -538,11 +538,12 @@ __global__ __launch_bounds__(8 * MP_BMAX) void make_p_kernel(const float* __rest
   }
 }
 
-// Core Gram A = diag(sigma^2, 0_p) + M^T M in fp64, M = [Q[:, :k], FP[:, :p]] (b x m).
+// Core Gram A = diag(sigma^2, 0_p) + M^T M in fp64, M = [Q[:, :k], FP[:, :p]] (b x m);
+// also sets ST_JM = m for the eigensolver.
 __global__ __launch_bounds__(256) void core_gram_kernel(const float* __restrict__ Q, int ldq,
                                                         const float* __restrict__ FP, int ldfp,
                                                         const float* __restrict__ sigma, int b,
-                                                        double* A, int lda, const int32_t* st,
+                                                        double* A, int lda, int32_t* st,
     const int64_t* __restrict__ bd) {
   const int64_t bdel = bd ? bd[blockIdx.z] : 0;
   Q = iskv_rb(Q, bdel);
@@ -551,6 +552,8 @@ __global__ __launch_bounds__(256) void core_gram_kernel(const float* __restrict_
   A = iskv_rb(A, bdel);
   st = iskv_rb(st, bdel);
   const int k = st[ST_K], m = st[ST_M];
+  // the eigensolver's order (no other workgroup of this launch reads it)
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) st[ST_JM] = m;
   const int i = blockIdx.y * 16 + (threadIdx.x >> 4);
   const int j = blockIdx.x * 16 + (threadIdx.x & 15);
   if (i >= m || j >= m) return;
@@ -1740,7 +1743,6 @@ static int merge_body(isvd_handle* h, const float* F, const int32_t* pos_F, int3
     hipLaunchKernelGGL(core_gram_kernel, bz(grid, h->bcount), dim3(256), 0, s, w.Q, R, w.FP, c.b_max, h->sigma, b,
                        w.A, h->ldm, w.st, h->bd);
   }
-  hipLaunchKernelGGL(set_jm_kernel, bz(dim3(1), h->bcount), dim3(1), 0, s, w.st, (int)ST_M, h->bd);
   {
     int rc = iskv_launch_core_eig(h, ISKV_EIG_TOL_UPDATE, c.r_max);
     if (rc) return rc;
