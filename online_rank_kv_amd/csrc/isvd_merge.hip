@@ -823,14 +823,25 @@ __global__ __launch_bounds__(256) void xh_mfma_kernel(const TX* X1, int ld1, con
 // before any of its outputs is written, so in-place use stays safe.
 constexpr int XR_LDX = 292; // LDS row stride (floats) of a staged X block
 
+// One product's arguments (the paired launch takes two).
+template <typename TX, typename TY>
+struct XhJob {
+  const TX* X1; int ld1; const float* X2; int ld2;
+  Dim k1_d, kin_d; const float* H; int ldh, hcols; Dim kout_d, rows_d;
+  TY* Y; int ldy; uint16_t* Ybf; int ldbf; int32_t* pos; const int32_t* pos_src; Dim yoff_d;
+  const float4* Hf;
+  int grid;  // workgroups of this product
+};
+
+// bx, gx: this workgroup's index among the product's gx workgroups.
 template <int XR_KS, typename TX, typename TY>  // k steps of 4 held per lane: kin <= 4 XR_KS
-__global__ __launch_bounds__(1024) void xh_reg_kernel(const TX* X1, int ld1, const float* X2, int ld2,
-                                                      Dim k1_d, Dim kin_d, const float* __restrict__ H,
-                                                      int ldh, int hcols, Dim kout_d, Dim rows_d, TY* Y,
-                                                      int ldy, uint16_t* Ybf, int ldbf, int32_t* pos,
-                                                      const int32_t* pos_src, Dim yoff_d, int32_t* st,
-                                                      const float4* __restrict__ Hf,
-    const int64_t* __restrict__ bd) {
+__device__ __forceinline__ void xh_reg_body(const XhJob<TX, TY>& J, int bx, int gx, int32_t* st,
+                                            float (*Xs)[16 * XR_LDX], const int64_t* __restrict__ bd) {
+  const TX* X1 = J.X1; const int ld1 = J.ld1; const float* X2 = J.X2; const int ld2 = J.ld2;
+  Dim k1_d = J.k1_d, kin_d = J.kin_d; const float* H = J.H; const int ldh = J.ldh, hcols = J.hcols;
+  Dim kout_d = J.kout_d, rows_d = J.rows_d; TY* Y = J.Y; const int ldy = J.ldy; uint16_t* Ybf = J.Ybf;
+  const int ldbf = J.ldbf; int32_t* pos = J.pos; const int32_t* pos_src = J.pos_src; Dim yoff_d = J.yoff_d;
+  const float4* Hf = J.Hf;
   const int64_t bdel = bd ? bd[blockIdx.z] : 0;
   X1 = iskv_rb(X1, bdel);
   X2 = iskv_rb(X2, bdel);
@@ -851,8 +862,7 @@ __global__ __launch_bounds__(1024) void xh_reg_kernel(const TX* X1, int ld1, con
   const int k1 = dval(k1_d), kin = dval(kin_d), kout = dval(kout_d), rows = dval(rows_d);
   const int yo = dval(yoff_d);
   const int nblk = (rows + 15) / 16;
-  if ((int)blockIdx.x >= nblk || kout <= 0 || kin <= 0) return;
-  __shared__ float Xs[2][16 * XR_LDX];
+  if (bx >= nblk || kout <= 0 || kin <= 0) return;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int col = wave * 16 + (lane & 15);
   bool over = false;  // a saturated half store (fp16 coordinates only)
@@ -894,9 +904,9 @@ __global__ __launch_bounds__(1024) void xh_reg_kernel(const TX* X1, int ld1, con
       }
     }
   };
-  load_x(blockIdx.x);
+  load_x(bx);
   int buf = 0;
-  for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+  for (int blk = bx; blk < nblk; blk += gx) {
     float* xs = Xs[buf];
     const int i0 = blk * 16;
 #pragma unroll
@@ -905,7 +915,7 @@ __global__ __launch_bounds__(1024) void xh_reg_kernel(const TX* X1, int ld1, con
       if (e < 16 * KW) xs[r * XR_LDX + c] = (c < kin && i0 + r < rows) ? xr[u] : 0.f;
     }
     __syncthreads();
-    if (blk + (int)gridDim.x < nblk) load_x(blk + gridDim.x);
+    if (blk + gx < nblk) load_x(blk + gx);
     v4f_t acc = {0.f, 0.f, 0.f, 0.f};
     const float* xa = xs + (lane & 15) * XR_LDX + (lane >> 4);
 #pragma unroll
@@ -925,6 +935,22 @@ __global__ __launch_bounds__(1024) void xh_reg_kernel(const TX* X1, int ld1, con
     buf ^= 1;
   }
   iskv_latch_overflow<TY>(st, over);
+}
+
+template <int XR_KS, typename TX, typename TY>
+__global__ __launch_bounds__(1024) void xh_reg_kernel(XhJob<TX, TY> J, int32_t* st, const int64_t* __restrict__ bd) {
+  __shared__ float Xs[2][16 * XR_LDX];
+  xh_reg_body<XR_KS>(J, blockIdx.x, gridDim.x, st, Xs, bd);
+}
+
+// Two independent products in one launch: workgroups [0, A.grid) run A, the
+// rest run B (the merge's new rows and basis update, which share H).
+template <int XR_KS, typename TX, typename TY>
+__global__ __launch_bounds__(1024) void xh_reg2_kernel(XhJob<TX, TY> A, XhJob<TX, TY> B, int32_t* st,
+                                                       const int64_t* __restrict__ bd) {
+  __shared__ float Xs[2][16 * XR_LDX];
+  if ((int)blockIdx.x < A.grid) xh_reg_body<XR_KS>(A, blockIdx.x, A.grid, st, Xs, bd);
+  else xh_reg_body<XR_KS>(B, blockIdx.x - A.grid, B.grid, st, Xs, bd);
 }
 
 // The coordinate update C <- C H over all n rows (C n x kin, in place; H
@@ -1280,12 +1306,12 @@ static void xh_launch(hipStream_t s, const int64_t* bd, int bc, int rows_host, c
     const int nblk = (rows_host + 15) / 16;
     const int grid = nblk < 256 ? nblk : 256;
     if (grid > 0) {
+      const XhJob<TX, TY> J = {X1, ld1, X2, ld2, k1, kin, H, ldh, hcols, kout, rows, Y, ldy, Ybf, ldbf, pos, pos_src,
+                               yoff, Hf, grid};
       if (kin_max <= 256)
-        hipLaunchKernelGGL((xh_reg_kernel<64, TX, TY>), bz(dim3(grid), bc), dim3(1024), 0, s, X1, ld1, X2, ld2, k1, kin, H,
-                           ldh, hcols, kout, rows, Y, ldy, Ybf, ldbf, pos, pos_src, yoff, st, Hf, bd);
+        hipLaunchKernelGGL((xh_reg_kernel<64, TX, TY>), bz(dim3(grid), bc), dim3(1024), 0, s, J, st, bd);
       else
-        hipLaunchKernelGGL((xh_reg_kernel<72, TX, TY>), bz(dim3(grid), bc), dim3(1024), 0, s, X1, ld1, X2, ld2, k1, kin, H,
-                           ldh, hcols, kout, rows, Y, ldy, Ybf, ldbf, pos, pos_src, yoff, st, Hf, bd);
+        hipLaunchKernelGGL((xh_reg_kernel<72, TX, TY>), bz(dim3(grid), bc), dim3(1024), 0, s, J, st, bd);
     }
     return;
   }
@@ -1780,13 +1806,29 @@ static int merge_body(isvd_handle* h, const float* F, const int32_t* pos_F, int3
       }
     }
     mark(4);
-    xh_launch(s, h->bd, h->bcount, b, w.Q, R, w.FP, c.b_max, ddim(dk), ddim(w.st + ST_M), M, w.Hc, R, R,
-              ddim(w.st + ST_KNEW), hdim(b), Cp, R, nullptr, 0, h->pos, pos_F, false, dn, w.st,
-              (const float4*)merge_hf(h));
+    const float4* Hf = (const float4*)merge_hf(h);
+    if (std::is_same<TC, float>::value && M <= 288 && R <= 256) {
+      // new rows and basis update in one launch (both read H in operand order)
+      const int gn = (b + 15) / 16, gd = std::min((D + 15) / 16, 256);
+      const XhJob<float, float> A = {w.Q, R, w.FP, c.b_max, ddim(dk), ddim(w.st + ST_M), w.Hc, R, R,
+                                     ddim(w.st + ST_KNEW), hdim(b), (float*)Cp, R, nullptr, 0, h->pos, pos_F, dn,
+                                     Hf, gn};
+      const XhJob<float, float> Bj = {h->B, R, w.P, c.b_max, ddim(dk), ddim(w.st + ST_M), w.Hc, R, R,
+                                      ddim(w.st + ST_KNEW), hdim(D), h->B, R, w.Bbf, R, nullptr, nullptr, hdim(0),
+                                      Hf, gd};
+      if (M <= 256)
+        hipLaunchKernelGGL((xh_reg2_kernel<64, float, float>), bz(dim3(gn + gd), h->bcount), dim3(1024), 0, s, A, Bj,
+                           w.st, h->bd);
+      else
+        hipLaunchKernelGGL((xh_reg2_kernel<72, float, float>), bz(dim3(gn + gd), h->bcount), dim3(1024), 0, s, A, Bj,
+                           w.st, h->bd);
+    } else {
+      xh_launch(s, h->bd, h->bcount, b, w.Q, R, w.FP, c.b_max, ddim(dk), ddim(w.st + ST_M), M, w.Hc, R, R,
+                ddim(w.st + ST_KNEW), hdim(b), Cp, R, nullptr, 0, h->pos, pos_F, false, dn, w.st, Hf);
+      xh_launch(s, h->bd, h->bcount, D, h->B, R, w.P, c.b_max, ddim(dk), ddim(w.st + ST_M), M, w.Hc, R, R,
+                ddim(w.st + ST_KNEW), hdim(D), h->B, R, w.Bbf, R, nullptr, nullptr, true, hdim(0), nullptr, Hf);
+    }
   });
-  xh_launch(s, h->bd, h->bcount, D, h->B, R, w.P, c.b_max, ddim(dk), ddim(w.st + ST_M), M, w.Hc, R, R,
-            ddim(w.st + ST_KNEW), hdim(D), h->B, R, w.Bbf, R, nullptr, nullptr, true, hdim(0), nullptr,
-            (const float4*)merge_hf(h));
   hipLaunchKernelGGL(merge_commit_kernel, bz(dim3(1), h->bcount), dim3(256), 0, s, h->sigma, w.sig_new, w.st, b, R, h->bd);
   mark(5);
   if (h->timing) h->timed = true;
