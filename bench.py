@@ -44,6 +44,7 @@ BF16_PEAK_TFLOPS = 2500.0
 FP32_PEAK_TFLOPS = 157.3
 TIMED_MERGES = 8  # merges run once more with stage events after the timed region
 MODE_MERGES = 16  # merges timed in each merge mode at the end of the run
+SINGLE_REPS = 20  # one-path reconstruction launches timed after the timed region
 
 
 def parse():
@@ -483,7 +484,7 @@ def main():
     del calib_src, calib_dst
     torch.cuda.synchronize()
     cursor = [N0 + WIN]
-    ev = {k: [] for k in ("merge_k", "merge_v", "recon_k", "recon_v", "attend")}
+    ev = {k: [] for k in ("merge_k", "merge_v", "recon_kv", "attend")}
     attend_done = [None]
     # rows of every timed step: n_total (compressed + window) and the
     # compressed rows the K reconstruction kernel reads and writes (all rows
@@ -496,29 +497,34 @@ def main():
         sk, sv = streams
         e = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
         if attend_done[0] is not None:
-            sv.wait_event(attend_done[0])  # V cache is rewritten only after the last attention read it
+            sv.wait_event(attend_done[0])  # the V factors and cache are rewritten only after the last step read them
         e[0].record(sk)
         if batched:
             ingest(s0, s0 + BLK)                 # K and V merges, one batched sequence (stream K)
             e[1].record(sk)
             sv.wait_event(e[1])
             e[3].record(sv)
-            e[4].record(sv)
+            ev_vm = e[1]
         else:
             e[3].record(sv)
             wins[0].append(Xd[0][s0:s0 + BLK], s0)   # K merge (stream K)
             wins[1].append(Xd[1][s0:s0 + BLK], s0)   # V merge (stream V)
             e[1].record(sk)
-            e[4].record(sv)
-        # compressed rows (one kernel, bracketed by the events), then the exact window rows
-        paths[0].reconstruct(Kc, n_total, head_dim=DH, rope=True, theta=THETA, stream=sk)
-        paths[1].reconstruct(Vc, n_total, head_dim=DH, rope=False, stream=sv)
-        e[2].record(sk)
-        e[5].record(sv)
+            ev_vm = torch.cuda.Event(enable_timing=True)
+            ev_vm.record(sv)
+        # each path's exact window rows on its own stream (their positions are
+        # disjoint from the compressed rows'), then the compressed rows of both
+        # caches in one launch on stream K once both merges are done
+        # (bracketed by e[5], e[2])
         for w_, C_, rope_, st_ in ((wins[0], Kc, True, sk), (wins[1], Vc, False, sv)):
             K.kv_scatter_exact(w_.rows, w_.pos, w_.rows.shape[0], D, n_total, DH, rope_, THETA, C_,
                                K.ISKV_OUT_BF16, st_)
-        sk.wait_event(e[5])
+        e[4].record(sv)
+        sk.wait_event(e[4])
+        e[5].record(sk)
+        K.kv_reconstruct_batched([paths[0].h, paths[1].h], [Kc, Vc], [n_total, n_total], [True, False], DH, THETA,
+                                 stream=sk)
+        e[2].record(sk)
         e[7].record(sk)
         K.decode_attend(q, Kc, Vc, 1, n_total, HQ, HKV, DH, DH ** -0.5, o, ws, stream=sk)
         e[6].record(sk)
@@ -526,9 +532,8 @@ def main():
         if record:
             timed_rows.append((n_total, n_total - WIN))
             ev["merge_k"].append((e[0], e[1]))   # batched: the K + V merge sequence
-            ev["merge_v"].append((e[3], e[4]) if not batched else (e[0], e[1]))
-            ev["recon_k"].append((e[1], e[2]))
-            ev["recon_v"].append((e[4], e[5]))
+            ev["merge_v"].append((e[3], ev_vm) if not batched else (e[0], e[1]))
+            ev["recon_kv"].append((e[5], e[2]))
             ev["attend"].append((e[7], e[6]))
         cursor[0] += BLK
 
@@ -549,6 +554,26 @@ def main():
 
     def avg_ms(key):
         return float(np.mean([a.elapsed_time(b) for a, b in ev[key]]))
+
+    # one history per launch: kv_reconstruct of the K path alone on its
+    # stream, nothing else running (HIP events around each launch), beside
+    # the step's two-path launch
+    sk = streams[0]
+    torch.cuda.synchronize()
+    n_tot1, n_c1 = cursor[0], paths[0].n
+    for _ in range(3):
+        paths[0].reconstruct(Kc, n_tot1, head_dim=DH, rope=True, theta=THETA, stream=sk)
+    es = [torch.cuda.Event(enable_timing=True) for _ in range(2 * SINGLE_REPS)]
+    for i in range(SINGLE_REPS):
+        es[2 * i].record(sk)
+        paths[0].reconstruct(Kc, n_tot1, head_dim=DH, rope=True, theta=THETA, stream=sk)
+        es[2 * i + 1].record(sk)
+    sk.synchronize()
+    s_ms = float(np.mean([es[2 * i].elapsed_time(es[2 * i + 1]) for i in range(SINGLE_REPS)]))
+    s_bytes = n_c1 * R * 4 + R * D * 2 + n_c1 * D * 2
+    single = {"ms": s_ms, "rows": n_c1, "algorithmic_bytes": s_bytes,
+              "achieved_GBps": s_bytes / (s_ms * 1e-3) / 1e9, "frac": s_bytes / (s_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+              "launches": SINGLE_REPS, "kernel": "kv_reconstruct (K path alone, bf16 + RoPE)"}
 
     # value side of the decode with the value history kept factored
     # (decode_attend_fv, outside the timed region) against the dense value
@@ -647,13 +672,14 @@ def main():
     ms = {k: avg_ms(k) for k in ev}
     core = [p.state() for p in paths]
     merges = 2 * steps
-    # algorithmic bytes of one K reconstruction launch, averaged over the
-    # timed steps: read the n_c compressed rows' coordinates (n_c x r fp32)
-    # and B^T (its bf16 copy, r x D), write n_c x D bf16; flops 2 n_c r D
+    # algorithmic bytes of the step's reconstruction launch (the K and the V
+    # path), averaged over the timed steps: per path, read the n_c compressed
+    # rows' coordinates (n_c x r fp32) and B^T (its bf16 copy, r x D), write
+    # n_c x D bf16; flops 2 n_c r D per path. Both paths hold the same rows.
     n_c = float(np.mean([c for _, c in timed_rows]))
-    recon_bytes = n_c * R * 4 + R * D * 2 + n_c * D * 2
-    recon_flops = 2.0 * n_c * R * D
-    recon_gbps = recon_bytes / (ms["recon_k"] * 1e-3) / 1e9
+    recon_bytes = 2 * (n_c * R * 4 + R * D * 2 + n_c * D * 2)
+    recon_flops = 2 * 2.0 * n_c * R * D
+    recon_gbps = recon_bytes / (ms["recon_kv"] * 1e-3) / 1e9
     result = {
         "metric": "iSVD merges/s + reconstructed KV GB/s at n=16K, D=1024, r=256; % HBM/MFMA peak",
         "value": merges / dt,
@@ -672,7 +698,7 @@ def main():
                                "GQA 32q/8kv decode", "n_rows_start": N0, "rank": R, "block": BLK,
                    "window": WIN, "reorth_every_rows": 256, "hip_graphs": not args.no_graphs,
                    "kv_merges": "batched" if batched else "two streams"},
-        "reconstructed_GBps": n_c * D * 2 / (ms["recon_k"] * 1e-3) / 1e9,
+        "reconstructed_GBps": 2 * n_c * D * 2 / (ms["recon_kv"] * 1e-3) / 1e9,
         "timed_rows": {"n_total_first": timed_rows[0][0], "n_total_last": timed_rows[-1][0],
                        "compressed_mean": n_c},
         "stage_ms": ms,
@@ -681,8 +707,10 @@ def main():
                      "frac": recon_gbps / HBM_PEAK_GBPS,
                      "traffic": profiled_traffic("recon_stream_kernel_kv_n16k_traffic.md"),
                      "algorithmic_bytes": recon_bytes,
-                     "kernel": "kv_reconstruct (K, bf16 + RoPE)",
-                     "mfma_frac": recon_flops / (ms["recon_k"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+                     "kernel": "kv_reconstruct_batched (K with RoPE and V, both paths in one launch, bf16)",
+                     "paths_per_launch": 2,
+                     "mfma_frac": recon_flops / (ms["recon_kv"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+        "recon_single_path": single,
         "merge_stage_ms": stage_k,
         "factor_v_attention": {"ms": fv_ms, "dense_value_side_ms": dense_ms, "algorithmic_bytes": fv_bytes,
                                "achieved_GBps": fv_bytes / (fv_ms * 1e-3) / 1e9, "n_total": n_tot,

@@ -278,6 +278,32 @@ int kv_reconstruct(const isvd_handle* h, const float* X_exact, const int32_t* po
                    int32_t n_exact, int32_t n_total, int32_t head_dim, int32_t apply_rope,
                    float rope_theta, void* out, int32_t out_dtype, void* stream);
 
+/* The compressed rows of several histories rebuilt by one launch (Algorithm 3
+ * and §3.2 / §5 of the iS-KV notes, as kv_reconstruct without exact rows):
+ * for every path i, row pos_i[j] of outs[i] gets C_i[j] B_i^T (j < n_i),
+ * turned per head at that position when apply_rope[i] (keys on, values off).
+ * One launch serves all paths, so its fixed cost (the launch, each
+ * workgroup's basis operands, the pipeline's fill and drain) is paid once;
+ * the bytes of every path are the same as with kv_reconstruct, and each
+ * output equals kv_reconstruct(hs[i], NULL, NULL, 0, n_totals[i], head_dim,
+ * apply_rope[i], rope_theta, outs[i], ISKV_OUT_BF16, stream) bit for bit.
+ * The exact rows of each path go through kv_scatter_exact afterwards.
+ *   hs          host array of count handles (1 <= count <=
+ *               ISKV_RECON_MAX_PATHS), sharing D, r_max and the coordinate
+ *               storage (ISKV_BF16_COORDS / ISKV_FP16_COORDS); not modified.
+ *   outs        host array of count device pointers, bf16 [n_totals[i] x D].
+ *   n_totals    host array: rows of each output, at least that handle's n.
+ *   apply_rope  host array of count flags.
+ *   head_dim    32, 64 or 128 (dividing 128); D a multiple of 128; r_max a
+ *               multiple of 32, at most 256 (the bf16 matrix-core kernel's
+ *               shapes: any other shape is EINVAL, use kv_reconstruct).
+ *   stream      hipStream_t as void* (NULL = hs[0]'s stream); the caller
+ *               orders the call after every handle's pending merges.
+ * Errors: EINVAL. */
+#define ISKV_RECON_MAX_PATHS 32
+int kv_reconstruct_batched(isvd_handle* const* hs, int32_t count, void* const* outs, const int32_t* n_totals,
+                           const int32_t* apply_rope, int32_t head_dim, float rope_theta, void* stream);
+
 /* The exact-row half of kv_reconstruct on its own (Algorithm 3 and §3.2 of
  * the iS-KV notes): row pos_exact[e] of `out` gets X_exact[e], turned per
  * head at that position when apply_rope (same convention as kv_reconstruct);

@@ -24,7 +24,8 @@ __all__ = [
     "ISKV_OUT_BF16", "isvd_set_mode",
     "ISKV_OUT_FP32", "ISKV_DEV_NONFINITE", "ISKV_DEV_NOCONV", "EXPORTED_SYMBOLS",
     "isvd_workspace_bytes", "isvd_init", "isvd_merge_block", "isvd_reorth", "isvd_query", "isvd_copy",
-    "isvd_rows", "isvd_destroy", "isvd_query_state", "isvd_sym_eig", "kv_reconstruct", "kv_scatter_exact",
+    "isvd_rows", "isvd_destroy", "isvd_query_state", "isvd_sym_eig", "kv_reconstruct", "kv_reconstruct_batched",
+    "kv_scatter_exact",
     "decode_attend_workspace_bytes", "decode_attend", "decode_attend_noalloc", "decode_attend_fv_workspace_bytes",
     "decode_attend_fv", "iskv_window_rows", "iskv_window_init", "iskv_window_protect",
     "iskv_window_append", "iskv_window_exact", "iskv_window_destroy", "iskv_strerror",
@@ -53,7 +54,7 @@ ISKV_DEV_FP16_OVERFLOW = 4
 
 EXPORTED_SYMBOLS = (
     "isvd_workspace_bytes", "isvd_init", "isvd_merge_block", "isvd_reorth", "isvd_query",
-    "isvd_rows", "isvd_destroy", "kv_reconstruct", "decode_attend_workspace_bytes",
+    "isvd_rows", "isvd_destroy", "kv_reconstruct", "kv_reconstruct_batched", "decode_attend_workspace_bytes",
     "decode_attend", "iskv_window_rows", "iskv_window_init", "iskv_window_protect",
     "iskv_window_append", "iskv_window_exact", "iskv_window_destroy", "iskv_strerror",
     "isvd_query_state", "isvd_sym_eig", "kv_scatter_exact", "isvd_merge_block_batched",
@@ -132,6 +133,9 @@ lib.isvd_destroy.restype = None
 lib.isvd_destroy.argtypes = [_vp]
 lib.kv_reconstruct.restype = ctypes.c_int
 lib.kv_reconstruct.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, ctypes.c_float, _vp, _i32, _vp]
+lib.kv_reconstruct_batched.restype = ctypes.c_int
+lib.kv_reconstruct_batched.argtypes = [ctypes.POINTER(_vp), _i32, ctypes.POINTER(_vp), ctypes.POINTER(_i32),
+                                       ctypes.POINTER(_i32), _i32, ctypes.c_float, _vp]
 lib.kv_scatter_exact.restype = ctypes.c_int
 lib.kv_scatter_exact.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _vp, _i32, _vp]
 lib.decode_attend_workspace_bytes.restype = ctypes.c_size_t
@@ -370,6 +374,20 @@ def kv_reconstruct(h: int, X_exact, pos_exact, n_exact: int, n_total: int, head_
     _check(lib.kv_reconstruct(h, _ptr(X_exact), _ptr(pos_exact), int(n_exact), int(n_total),
                               int(head_dim), int(bool(apply_rope)), float(rope_theta), _ptr(out),
                               int(out_dtype), _stream_ptr(stream)), "kv_reconstruct")
+
+
+def kv_reconstruct_batched(handles, outs, n_totals, apply_rope, head_dim: int, rope_theta: float,
+                           stream=None) -> None:
+    """Compressed rows of several histories (bf16 outputs) in one launch."""
+    k = len(handles)
+    if not (len(outs) == len(n_totals) == len(apply_rope) == k):
+        raise ValueError("kv_reconstruct_batched: one output, row count and RoPE flag per handle")
+    hs = (_vp * k)(*handles)
+    os_ = (_vp * k)(*[_ptr(o) for o in outs])
+    nt = (ctypes.c_int32 * k)(*[int(x) for x in n_totals])
+    rp = (ctypes.c_int32 * k)(*[int(bool(x)) for x in apply_rope])
+    _check(lib.kv_reconstruct_batched(hs, k, os_, nt, rp, int(head_dim), float(rope_theta), _stream_ptr(stream)),
+           "kv_reconstruct_batched")
 
 
 def kv_scatter_exact(X_exact, pos_exact, n_exact: int, D: int, n_total: int, head_dim: int,

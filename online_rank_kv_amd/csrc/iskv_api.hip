@@ -420,6 +420,26 @@ int kv_reconstruct(const isvd_handle* h, const float* X_exact, const int32_t* po
                                  rope_theta, out, out_dtype, s);
 }
 
+int kv_reconstruct_batched(isvd_handle* const* hs, int32_t count, void* const* outs, const int32_t* n_totals,
+                           const int32_t* apply_rope, int32_t head_dim, float rope_theta, void* stream) {
+  if (!hs || !outs || !n_totals || !apply_rope) return ISKV_EINVAL;
+  if (count < 1 || count > ISKV_RECON_MAX_PATHS) return ISKV_EINVAL;
+  const uint32_t smask = ISKV_BF16_COORDS | ISKV_FP16_COORDS;
+  for (int i = 0; i < count; ++i) {
+    const isvd_handle* h = hs[i];
+    if (!h || !outs[i]) return ISKV_EINVAL;
+    if (h->cfg.D != hs[0]->cfg.D || h->cfg.r_max != hs[0]->cfg.r_max ||
+        (h->cfg.flags & smask) != (hs[0]->cfg.flags & smask))
+      return ISKV_EINVAL;
+    if (n_totals[i] < h->n_host || n_totals[i] < 0) return ISKV_EINVAL;
+    if (apply_rope[i] && !(rope_theta > 1.f)) return ISKV_EINVAL;
+    if (!iskv_recon_stream_ok(h, n_totals[i], head_dim)) return ISKV_EINVAL;
+  }
+  hipStream_t s = stream ? (hipStream_t)stream : hs[0]->stream;
+  return iskv_launch_reconstruct_batched(hs, count, (uint16_t* const*)outs, n_totals, apply_rope, head_dim,
+                                         rope_theta, s, nullptr, nullptr, 0);
+}
+
 int kv_scatter_exact(const float* X_exact, const int32_t* pos_exact, int32_t n_exact, int32_t D,
                      int32_t n_total, int32_t head_dim, int32_t apply_rope, float rope_theta,
                      void* out, int32_t out_dtype, void* stream) {

@@ -169,6 +169,11 @@ int iskv_launch_reorth_batched(isvd_handle* const* hs, int32_t count);
 int iskv_launch_reorth(isvd_handle* h);
 void iskv_release_graphs(isvd_handle* h);
 int iskv_launch_sym_eig(isvd_handle* h, const double* A, int32_t m, double* lam, double* V);
+bool iskv_recon_stream_ok(const isvd_handle* h, int32_t n_total, int32_t head_dim);
+int iskv_launch_reconstruct_batched(const isvd_handle* const* hs, int32_t count, uint16_t* const* outs,
+                                    const int32_t* n_totals, const int32_t* ropes, int32_t head_dim,
+                                    float rope_theta, hipStream_t s, const float* X_exact,
+                                    const int32_t* pos_exact, int32_t n_exact);
 int iskv_launch_exact_rows(const float* X_exact, const int32_t* pos_exact, int32_t n_exact, int32_t D,
                            int32_t n_total, int32_t head_dim, int32_t apply_rope, float rope_theta,
                            void* out, int32_t out_dtype, hipStream_t s);

@@ -337,21 +337,41 @@ __global__ __launch_bounds__(256) void recon_mfma_kernel(const TC* __restrict__ 
 // them), and the row positions of 16 blocks at a time are staged in LDS
 // beforehand, so no per-block load waits behind the prefetches and stores.
 constexpr int RS_BM32 = 32;          // rows per block of the 4-wave form
+// One history's compressed rows for the streaming kernel: coordinates (TC,
+// leading dimension r_max), its bf16 basis copy, row positions, state words
+// (k), bf16 output cache [n_total x D], row count and RoPE switch. Several
+// histories of one configuration go in one launch.
+struct RsPath {
+  const void* C;
+  const uint16_t* Bbf;
+  const int32_t* pos;
+  const int32_t* st;
+  uint16_t* out;
+  int32_t n, n_total, rope, pad;
+};
+struct RsPaths {
+  RsPath p[ISKV_RECON_MAX_PATHS];
+};
 constexpr int RS_CS = 256 + 8;       // LDS row stride (bf16) of a staged C block
 constexpr int RS_PCH = 16;           // blocks whose positions are staged at once
 
 template <typename TC, int NW, int RS_BM>  // NW waves: a tile of 32 NW features; RS_BM rows per block
-__global__ __launch_bounds__(64 * NW, 2) void recon_stream_kernel(const TC* __restrict__ C, int ldc,
-                                                           const uint16_t* __restrict__ Bbf, int ldb,
-                                                           const int32_t* __restrict__ pos,
-                                                           const int32_t* __restrict__ st, int n, int D,
-                                                           int dh, int apply_rope, double log_theta,
-                                                           uint16_t* out, int n_total, int T, int S) {
+__global__ __launch_bounds__(64 * NW, 2) void recon_stream_kernel(const RsPaths paths, int np,
+                                                           int ldc, int ldb, int D, int dh, double log_theta,
+                                                           int T, int S_all) {
   constexpr int NT = 64 * NW;          // threads
   constexpr int PER = RS_BM * 64 / NT; // float4 (or 4-coordinate) loads per thread per block
-  const int kdev = st[ST_K];
   const int wg = blockIdx.x;
-  const int ct = (wg / 8) % T, rs = wg % 8 + 8 * (wg / (8 * T));
+  const int ct = (wg / 8) % T, rs_all = wg % 8 + 8 * (wg / (8 * T));
+  // row group rs_all serves path rs_all % np as its (rs_all / np)-th of S
+  // row groups (consecutive row groups alternate paths)
+  const int path = rs_all % np, rs = rs_all / np, S = (S_all - path + np - 1) / np;
+  const TC* __restrict__ C = (const TC*)paths.p[path].C;
+  const uint16_t* __restrict__ Bbf = paths.p[path].Bbf;
+  const int32_t* __restrict__ pos = paths.p[path].pos;
+  uint16_t* out = paths.p[path].out;
+  const int n = paths.p[path].n, n_total = paths.p[path].n_total, apply_rope = paths.p[path].rope;
+  const int kdev = paths.p[path].st[ST_K];
   const int c0 = ct * 32 * NW;
   const int nblk = (n + RS_BM - 1) / RS_BM;
   if (rs >= nblk) return;
@@ -609,6 +629,62 @@ __global__ void fill_pos_kernel(int32_t* pos, int count, int32_t v0, int32_t ste
 
 }  // namespace
 
+// Shapes the streaming kernel serves (bf16 output): r_max a multiple of 32
+// up to 256, D a multiple of 128 with whole heads in a 128-feature tile
+// (head_dim 32, 64 or 128), and byte offsets of C and of the output within
+// the 32-bit range of a buffer descriptor.
+bool iskv_recon_stream_ok(const isvd_handle* h, int32_t n_total, int32_t head_dim) {
+  const int D = h->cfg.D, R = h->cfg.r_max;
+  const size_t cb = (size_t)iskv_coord_bytes(h->cfg);
+  return D % RM_BN == 0 && head_dim % 32 == 0 && RM_BN % head_dim == 0 && R % 32 == 0 && R <= 256 &&
+         (size_t)h->n_host * R * cb < ((size_t)1 << 31) && (size_t)n_total * D * 2 < ((size_t)1 << 31);
+}
+
+int iskv_launch_reconstruct_batched(const isvd_handle* const* hs, int32_t count, uint16_t* const* outs,
+                                    const int32_t* n_totals, const int32_t* ropes, int32_t head_dim,
+                                    float rope_theta, hipStream_t s, const float* X_exact,
+                                    const int32_t* pos_exact, int32_t n_exact) {
+  const isvd_handle* h0 = hs[0];
+  const int D = h0->cfg.D, R = h0->cfg.r_max;
+  const double lt = log((double)rope_theta);
+  RsPaths tab = {};
+  int np = 0;
+  for (int i = 0; i < count; ++i) {
+    if (hs[i]->n_host <= 0) continue;  // nothing compressed: nothing to write
+    const isvd_handle* h = hs[i];
+    tab.p[np] = RsPath{(const void*)h->C, h->w.Bbf, h->pos, h->w.st, outs[i], h->n_host, n_totals[i],
+                       ropes[i] ? 1 : 0, 0};
+    ++np;
+  }
+  if (np > 0) {
+    auto go = [&](auto* tag) {
+      using TC = std::remove_pointer_t<decltype(tag)>;
+      if (D % 256 == 0 && 256 % head_dim == 0) {
+        // 256-feature tiles (8 waves), one workgroup per CU
+        const int T = D / 256;
+        const int G = T >= 32 ? 1 : 32 / T;  // 256 workgroups when T divides 32
+        const int S = std::max(8 * G, (np + 7) / 8 * 8);  // at least one row group per path
+        hipLaunchKernelGGL((recon_stream_kernel<TC, 8, RS_BM32>), dim3(T * S), dim3(512), 0, s, tab, np, R, R, D,
+                           head_dim, lt, T, S);
+      } else {
+        const int T = D / 128;
+        const int G = T >= 64 ? 1 : 64 / T;  // 512 workgroups when T divides 64
+        const int S = std::max(8 * G, (np + 7) / 8 * 8);
+        hipLaunchKernelGGL((recon_stream_kernel<TC, 4, RS_BM32>), dim3(T * S), dim3(256), 0, s, tab, np, R, R, D,
+                           head_dim, lt, T, S);
+      }
+    };
+    if (iskv_bf16_coords(h0->cfg)) go((uint16_t*)nullptr);
+    else if (iskv_fp16_coords(h0->cfg)) go((_Float16*)nullptr);
+    else go((float*)nullptr);
+  }
+  if (n_exact > 0)
+    hipLaunchKernelGGL(exact_rows_kernel<true>, dim3(n_exact), dim3(256), 0, s, X_exact, pos_exact, D, head_dim,
+                       ropes[0], lt, (void*)outs[0], n_totals[0]);
+  ISKV_HIP_CHECK(hipGetLastError());
+  return ISKV_OK;
+}
+
 int iskv_launch_reconstruct(const isvd_handle* h, const float* X_exact, const int32_t* pos_exact,
                             int32_t n_exact, int32_t n_total, int32_t head_dim, int32_t apply_rope,
                             float rope_theta, void* out, int32_t out_dtype, hipStream_t s) {
@@ -621,26 +697,16 @@ int iskv_launch_reconstruct(const isvd_handle* h, const float* X_exact, const in
     dim3 grid(D / W, (n + 31) / 32);
     const bool mfma = bf && D % RM_BN == 0 && head_dim % 32 == 0 && RM_BN % head_dim == 0 &&
                       R % 8 == 0;
-    // (the streaming kernel's buffer descriptors bound C and the output in
-    // 32-bit bytes)
+    if (bf && iskv_recon_stream_ok(h, n_total, head_dim)) {
+      const int rope = apply_rope ? 1 : 0;
+      uint16_t* o = (uint16_t*)out;
+      return iskv_launch_reconstruct_batched(&h, 1, &o, &n_total, &rope, head_dim, rope_theta, s, X_exact,
+                                             pos_exact, n_exact);
+    }
     auto go = [&](auto* Cp) {
       using TC = std::remove_pointer_t<decltype(Cp)>;
       const TC* Cc = Cp;
-      if (mfma && R % 32 == 0 && R <= 256 && (size_t)n * R * sizeof(TC) < ((size_t)1 << 31) &&
-          (size_t)n_total * D * 2 < ((size_t)1 << 31)) {
-        if (D % 256 == 0 && 256 % head_dim == 0) {
-          // 256-feature tiles (8 waves), one workgroup per CU
-          const int T = D / 256;
-          const int G = T >= 32 ? 1 : 32 / T;  // 256 workgroups when T divides 32
-          hipLaunchKernelGGL((recon_stream_kernel<TC, 8, RS_BM32>), dim3(8 * T * G), dim3(512), 0, s, Cc, R, h->w.Bbf, R,
-                             h->pos, h->w.st, n, D, head_dim, apply_rope, lt, (uint16_t*)out, n_total, T, 8 * G);
-        } else {
-          const int T = D / 128;
-          const int G = T >= 64 ? 1 : 64 / T;  // 512 workgroups when T divides 64
-          hipLaunchKernelGGL((recon_stream_kernel<TC, 4, RS_BM32>), dim3(8 * T * G), dim3(256), 0, s, Cc, R, h->w.Bbf, R,
-                             h->pos, h->w.st, n, D, head_dim, apply_rope, lt, (uint16_t*)out, n_total, T, 8 * G);
-        }
-      } else if (mfma) {
+      if (mfma) {
         const int tiles = D / RM_BN, nrb = (n + RM_BM - 1) / RM_BM;
         const int nwg = (nrb + 7) / 8 * 8 * tiles;
         hipLaunchKernelGGL((recon_mfma_kernel<TC>), dim3(nwg), dim3(256), 0, s, Cc, R, h->w.Bbf, R,

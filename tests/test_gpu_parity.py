@@ -802,6 +802,74 @@ def test_reconstruct_full_size_elementwise(K, c16):
     path.close()
 
 
+@pytest.mark.parametrize("c16", [False, True])
+def test_reconstruct_batched_matches_separate(K, c16):
+    """kv_reconstruct_batched (one launch over several histories, Algorithm 3
+    steps 7-8 per history) writes exactly what kv_reconstruct writes for each
+    history alone: a key path (RoPE) and a value path (no RoPE) at the full
+    workload size (16,384 and 16,416 compressed rows, D = 1024, r = 256, the
+    rows in shuffled position order, so every workgroup takes several blocks
+    of its path), then three paths of ragged sizes (one of them empty) with
+    mixed RoPE. Bit for bit against the separate calls, and the key path
+    against the oracle's rebuild of the GPU's own factors."""
+    D, hd, theta = 1024, 128, 500000.0
+    rng = np.random.default_rng(23)
+
+    def make(spec, n, n_total, seed):
+        X = synth.kv_stream(spec, max(n, 1))
+        pos = rng.permutation(n_total)[:n].astype(np.int32)
+        p = K.IsvdPath(D=D, r_max=256, b_max=32, n_cap=max(n, 32), reorth_every_rows=256, device=DEV,
+                       coords_bf16=c16)
+        Xd = torch.from_numpy(X).to(DEV)
+        pd = torch.from_numpy(pos).to(DEV)
+        for s0 in range(0, n, 32):
+            p.merge(Xd[s0:min(s0 + 32, n)], pd[s0:min(s0 + 32, n)])
+        return p, pos
+
+    cases = [[(synth.CONFIG_KV_K, 16384, 16512, True), (synth.CONFIG_KV_V, 16352, 16480, False)],
+             [(synth.CONFIG_KV_K, 3001, 3100, False), (synth.CONFIG_KV_V, 0, 77, True),
+              (synth.CONFIG_KV_V, 1234, 1300, True)]]
+    for case in cases:
+        paths = [make(spec, n, nt, i) for i, (spec, n, nt, _) in enumerate(case)]
+        outs_b = [torch.full((nt, D), float("nan"), dtype=torch.bfloat16, device=DEV) for (_, _, nt, _) in case]
+        outs_s = [o.clone() for o in outs_b]
+        K.kv_reconstruct_batched([p.h for p, _ in paths], outs_b, [nt for (_, _, nt, _) in case],
+                                 [r for (*_, r) in case], hd, theta)
+        for (p, _), o, (_, _, nt, r) in zip(paths, outs_s, case):
+            p.reconstruct(o, nt, head_dim=hd, rope=r, theta=theta)
+        torch.cuda.synchronize()
+        for i, (ob, os_) in enumerate(zip(outs_b, outs_s)):
+            same = torch.equal(ob.view(torch.int16), os_.view(torch.int16))
+            assert same, (c16, i, case[i][1:])
+        # the first path against the oracle on the GPU's own factors (rows
+        # not covered by the compressed positions stay NaN in both outputs;
+        # the oracle fills them with zero exact rows, which are not compared)
+        (p0, pos0), (_, n0, nt0, r0) = paths[0], case[0]
+        C, B, _, pos, st = gpu_factors(p0)
+        assert st == 0 and np.array_equal(pos, pos0)
+        fac = O.Factor(U=C, sigma=np.ones(C.shape[1]), B=B, pos=pos)
+        rest = np.setdiff1d(np.arange(nt0), pos0).astype(np.int32)
+        ref = O.reconstruct(fac, np.zeros((rest.size, D), np.float32), rest, nt0, hd, r0, theta)
+        gb = outs_b[0].double().cpu().numpy()
+        assert rel(gb[pos0], ref[pos0]) < 5e-3, rel(gb[pos0], ref[pos0])
+        print(f"c16={c16} paths={[c[1] for c in case]}: identical to separate calls; path 0 rel to oracle "
+              f"{rel(gb[pos0], ref[pos0]):.3e}")
+        for p, _ in paths:
+            p.close()
+    # refused: no handles, too many, and a shape the streaming kernel does not serve
+    pa, _ = make(synth.CONFIG_KSTREAM, 64, 64, 0)
+    o = torch.empty((64, D), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(K.IskvError):
+        K.kv_reconstruct_batched([], [], [], [], hd, theta)
+    with pytest.raises(K.IskvError):
+        K.kv_reconstruct_batched([pa.h] * 33, [o] * 33, [64] * 33, [True] * 33, hd, theta)
+    with pytest.raises(K.IskvError):
+        K.kv_reconstruct_batched([pa.h], [o], [63], [True], hd, theta)   # n_total below the rows held
+    with pytest.raises(K.IskvError):
+        K.kv_reconstruct_batched([pa.h], [o], [64], [True], 48, theta)   # head_dim outside 32 / 64 / 128
+    pa.close()
+
+
 # --------------------------------------------------------------------------- attention
 @pytest.mark.parametrize("batch,n,hq,hkv", [(1, 1000, 32, 8), (2, 4096, 32, 8), (1, 63, 8, 8),
                                             (2, 33000, 16, 4), (1, 140000, 32, 8), (1, 3000, 32, 4)])
