@@ -265,6 +265,64 @@ def batch_leg(args, K, torch, dev):
             stage.append(bat.paths[0].stage_times())
         bat.paths[0].set_timing(False)
         st.synchronize()
+        # the decode step over the compressed caches: per sequence, its L
+        # layers' K and V histories rebuilt by kv_reconstruct_batched launches
+        # of 16 layers each (32 paths, RoPE on the keys), then one
+        # decode_attend over the L layers as a batch (32 query heads, 8 KV
+        # heads); every sequence in turn, timed with HIP events
+        dec = None
+        L = min(32, P // 2)  # layers per sequence (32: 16 sequences x 32 layers at P = 1024)
+        nseq = (P // 2) // L if L > 0 else 0
+        LC = 16  # layers per reconstruction launch (2 LC <= 32 paths)
+        if nseq > 0:
+            n_dec = bat.paths[0].n
+            Kall = torch.empty((L, n_dec, D), dtype=torch.bfloat16, device=dev)
+            Vall = torch.empty((L, n_dec, D), dtype=torch.bfloat16, device=dev)
+            qd = torch.from_numpy(np.random.default_rng(9).standard_normal((L, HQ, DH)).astype(np.float32)).to(
+                dev).bfloat16()
+            od = torch.empty((L, HQ, DH), dtype=torch.bfloat16, device=dev)
+            wsd = torch.empty(K.decode_attend_workspace_bytes(L, n_dec, HQ, DH), dtype=torch.uint8, device=dev)
+            ed = [torch.cuda.Event(enable_timing=True) for _ in range(3 * nseq)]
+            nlaunch = (L + LC - 1) // LC
+
+            def decode(sq, evs):
+                if evs:
+                    evs[0].record(st)
+                for l0 in range(0, L, LC):
+                    ls = range(l0, min(L, l0 + LC))
+                    hs = [bat.paths[sq * L + l].h for l in ls] + [bat.paths[P // 2 + sq * L + l].h for l in ls]
+                    K.kv_reconstruct_batched(hs, [Kall[l] for l in ls] + [Vall[l] for l in ls],
+                                             [n_dec] * (2 * len(ls)), [True] * len(ls) + [False] * len(ls), DH,
+                                             THETA, stream=st)
+                if evs:
+                    evs[1].record(st)
+                K.decode_attend(qd, Kall, Vall, L, n_dec, HQ, HKV, DH, DH ** -0.5, od, wsd, stream=st)
+                if evs:
+                    evs[2].record(st)
+
+            decode(0, None)
+            st.synchronize()
+            for sq in range(nseq):
+                decode(sq, ed[3 * sq:3 * sq + 3])
+            st.synchronize()
+            rec_ms = float(np.mean([ed[3 * i].elapsed_time(ed[3 * i + 1]) for i in range(nseq)])) / nlaunch
+            att_ms = float(np.mean([ed[3 * i + 1].elapsed_time(ed[3 * i + 2]) for i in range(nseq)]))
+            rec_bytes = 2 * LC * (n_dec * R * 4 + R * D * 2 + n_dec * D * 2)
+            att_bytes = 2 * L * n_dec * D * 2
+            dec = {"sequences": nseq, "layers": L, "rows": n_dec,
+                   "reconstruct_ms_per_launch": rec_ms, "paths_per_launch": 2 * LC,
+                   "reconstruct_launches_per_sequence": nlaunch,
+                   "reconstruct_algorithmic_bytes_per_launch": rec_bytes,
+                   "reconstruct_GBps": rec_bytes / (rec_ms * 1e-3) / 1e9,
+                   "reconstruct_hbm_frac": rec_bytes / (rec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                   "reconstruct_mfma_frac": 2 * LC * 2.0 * n_dec * R * D / (rec_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                   "attend_ms_per_launch": att_ms, "attend_batch": L,
+                   "attend_GBps": att_bytes / (att_ms * 1e-3) / 1e9,
+                   "decode_ms_all_sequences": nseq * (nlaunch * rec_ms + att_ms),
+                   "what": f"per sequence: kv_reconstruct_batched over its {L} layers' K (RoPE) and V paths, "
+                           f"{2 * LC} paths per launch, then one decode_attend over the {L} layers (batch {L}, "
+                           f"32 q / 8 kv heads, bf16)"}
+            del Kall, Vall, wsd
     ms = e0.elapsed_time(e1)
     states = [p.state() for p in bat.paths[:: max(1, P // 4)]]
     n_end = bat.paths[0].n
@@ -277,6 +335,7 @@ def batch_leg(args, K, torch, dev):
             "stage_ms_per_batched_merge": stage_ms,
             "coord_update_GBps": cu_bytes / (stage_ms["coord_update"] * 1e-3) / 1e9,
             "core_solver_flags_sampled": [c[11] for c in states], "rows_at_end": n_end,
+            "decode_step": dec,
             "workload": f"{P} independent paths ({P // 2} K, {P // 2} V spectra: 16 sequences x 32 layers x K/V "
                         f"when P = 1024), n={n0}, D={D}, r={R}, b={BLK}, reorth every 256 rows; paths start as "
                         f"copies of a K and a V factor of {n0} rows (fresh truncated SVD) and take their own "
