@@ -352,15 +352,18 @@ struct RsPath {
 struct RsPaths {
   RsPath p[ISKV_RECON_MAX_PATHS];
 };
-constexpr int RS_CS = 256 + 8;       // LDS row stride (bf16) of a staged C block
 constexpr int RS_PCH = 16;           // blocks whose positions are staged at once
 
-template <typename TC, int NW, int RS_BM>  // NW waves: a tile of 32 NW features; RS_BM rows per block
+template <typename TC, int NW, int RS_BM, int KC>  // NW waves: a tile of 32 NW features; RS_BM rows per block;
+                                                   // KC: staged columns of C (r_max <= KC: 256 or 512)
 __global__ __launch_bounds__(64 * NW, 2) void recon_stream_kernel(const RsPaths paths, int np,
                                                            int ldc, int ldb, int D, int dh, double log_theta,
                                                            int T, int S_all) {
   constexpr int NT = 64 * NW;          // threads
-  constexpr int PER = RS_BM * 64 / NT; // float4 (or 4-coordinate) loads per thread per block
+  constexpr int CQ = KC / 4;           // 4-coordinate groups per staged row
+  constexpr int KS = KC / 32;          // 32-deep MFMA steps
+  constexpr int CS = KC + 8;           // LDS row stride (bf16) of a staged C block
+  constexpr int PER = RS_BM * CQ / NT; // float4 (or 4-coordinate) loads per thread per block
   const int wg = blockIdx.x;
   const int ct = (wg / 8) % T, rs_all = wg % 8 + 8 * (wg / (8 * T));
   // row group rs_all serves path rs_all % np as its (rs_all / np)-th of S
@@ -375,7 +378,7 @@ __global__ __launch_bounds__(64 * NW, 2) void recon_stream_kernel(const RsPaths 
   const int c0 = ct * 32 * NW;
   const int nblk = (n + RS_BM - 1) / RS_BM;
   if (rs >= nblk) return;
-  __shared__ __attribute__((aligned(16))) uint16_t Cs[2][RS_BM * RS_CS];
+  __shared__ __attribute__((aligned(16))) uint16_t Cs[2][RS_BM * CS];
   __shared__ int posC[RS_PCH * RS_BM];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int half = dh >> 1;
@@ -392,12 +395,12 @@ __global__ __launch_bounds__(64 * NW, 2) void recon_stream_kernel(const RsPaths 
   }
   const int blk0 = lob, blk1 = lob + half / 16;
   // left MFMA operands: lane holds B(feature 16 blk + l%16, k 32 s + 8 (l/16) .. +7)
-  uint4 breg[2][8];
+  uint4 breg[2][KS];
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     const int f = c0 + 16 * (cb ? blk1 : blk0) + (lane & 15);
 #pragma unroll
-    for (int sk = 0; sk < 8; ++sk) {
+    for (int sk = 0; sk < KS; ++sk) {
       const int kk = 32 * sk + 8 * (lane >> 4);
       uint4 v = *(const uint4*)(Bbf + (size_t)f * ldb + min(kk, ldb - 8));
       if (kk + 8 > kdev) {  // zero depths >= k
@@ -416,8 +419,8 @@ __global__ __launch_bounds__(64 * NW, 2) void recon_stream_kernel(const RsPaths 
 #pragma unroll
   for (int e = 0; e < 4; ++e)
     rope_F[e] = rope_fraction(exp(-(2.0 * ((flo + e) % dh) / dh) * log_theta) * 0.15915494309189533577);
-  // C block staging: element u of this thread is row (t + NT u) / 64,
-  // columns 4 ((t + NT u) % 64) .. +3. Loads run two blocks ahead (a ring
+  // C block staging: element u of this thread is row (t + NT u) / CQ,
+  // columns 4 ((t + NT u) % CQ) .. +3. Loads run two blocks ahead (a ring
   // of two register sets).
   constexpr int ES = (int)sizeof(TC);  // bytes per stored coordinate
   // fp32 rows are held as float4, 2-byte rows as their raw bf16 bits
@@ -434,10 +437,10 @@ __global__ __launch_bounds__(64 * NW, 2) void recon_stream_kernel(const RsPaths 
   };
   // C rows through a buffer descriptor based at the block's first row and
   // bounded by the last row n - 1 (rows past n read as zero; a block past the
-  // end gets an empty descriptor); per-load offsets are fixed (row t / 64 +
-  // NW u, column 4 (t % 64)), so no address arithmetic runs per block.
-  const uint32_t voff0 = (uint32_t)(((t >> 6) * ldc + (t & 63) * 4) * ES);
-  const uint32_t vstep = (uint32_t)(NW * ldc * ES);
+  // end gets an empty descriptor); per-load offsets are fixed (row t / CQ +
+  // (NT / CQ) u, column 4 (t % CQ)), so no address arithmetic runs per block.
+  const uint32_t voff0 = (uint32_t)(((t / CQ) * ldc + (t % CQ) * 4) * ES);
+  const uint32_t vstep = (uint32_t)((NT / CQ) * ldc * ES);
   auto load_c = [&](int slot, int blk) {
     const bool live = blk < nblk;
     const int i0 = (live ? blk : 0) * RS_BM;
@@ -460,29 +463,29 @@ __global__ __launch_bounds__(64 * NW, 2) void recon_stream_kernel(const RsPaths 
     if (i0 + RS_BM <= n && kdev >= ldc) {  // full block: nothing to mask
 #pragma unroll
       for (int u = 0; u < PER; ++u) {
-        const int e = t + NT * u, r = e >> 6, c4 = (e & 63) * 4;
+        const int e = t + NT * u, r = e / CQ, c4 = (e % CQ) * 4;
         if constexpr (ES == 4) {
           const float4 v = creg[slot][u];
-          *(uint2*)(cs + r * RS_CS + c4) = uint2{pk_bf16(v.x, v.y), pk_bf16(v.z, v.w)};
+          *(uint2*)(cs + r * CS + c4) = uint2{pk_bf16(v.x, v.y), pk_bf16(v.z, v.w)};
         } else {
-          *(uint2*)(cs + r * RS_CS + c4) = to_bf4(creg[slot][u]);
+          *(uint2*)(cs + r * CS + c4) = to_bf4(creg[slot][u]);
         }
       }
     } else {
 #pragma unroll
       for (int u = 0; u < PER; ++u) {
-        const int e = t + NT * u, r = e >> 6, c4 = (e & 63) * 4;
+        const int e = t + NT * u, r = e / CQ, c4 = (e % CQ) * 4;
         const bool rv = i0 + r < n;
         if constexpr (ES == 4) {
           const float4 v = creg[slot][u];
           const float x0 = (rv && c4 < kdev) ? v.x : 0.f, x1 = (rv && c4 + 1 < kdev) ? v.y : 0.f;
           const float x2 = (rv && c4 + 2 < kdev) ? v.z : 0.f, x3 = (rv && c4 + 3 < kdev) ? v.w : 0.f;
-          *(uint2*)(cs + r * RS_CS + c4) = uint2{pk_bf16(x0, x1), pk_bf16(x2, x3)};
+          *(uint2*)(cs + r * CS + c4) = uint2{pk_bf16(x0, x1), pk_bf16(x2, x3)};
         } else {  // zero the 16-bit halves at columns >= k (rows past n read as zero)
           const uint2 v = to_bf4(creg[slot][u]);
           const uint32_t m0 = (c4 < kdev ? 0xffffu : 0u) | (c4 + 1 < kdev ? 0xffff0000u : 0u);
           const uint32_t m1 = (c4 + 2 < kdev ? 0xffffu : 0u) | (c4 + 3 < kdev ? 0xffff0000u : 0u);
-          *(uint2*)(cs + r * RS_CS + c4) = rv ? uint2{v.x & m0, v.y & m1} : uint2{0u, 0u};
+          *(uint2*)(cs + r * CS + c4) = rv ? uint2{v.x & m0, v.y & m1} : uint2{0u, 0u};
         }
       }
     }
@@ -507,19 +510,19 @@ __global__ __launch_bounds__(64 * NW, 2) void recon_stream_kernel(const RsPaths 
       const int ko = 32 * sk + 8 * (lane >> 4);
 #pragma unroll
       for (int a = 0; a < RT; ++a) {
-        const v8bf av = __builtin_bit_cast(v8bf, *(const uint4*)(cs + (16 * a + (lane & 15)) * RS_CS + ko));
+        const v8bf av = __builtin_bit_cast(v8bf, *(const uint4*)(cs + (16 * a + (lane & 15)) * CS + ko));
         acc[a][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, breg[0][sk]), av,
                                                             acc[a][0], 0, 0, 0);
         acc[a][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, breg[1][sk]), av,
                                                             acc[a][1], 0, 0, 0);
       }
     };
-    if (ks == 8) {  // the whole rank: no branch between the steps, reads issued ahead
+    if (ks == KS) {  // the whole rank: no branch between the steps, reads issued ahead
 #pragma unroll
-      for (int sk = 0; sk < 8; ++sk) kstep(sk);
+      for (int sk = 0; sk < KS; ++sk) kstep(sk);
     } else {
 #pragma unroll
-      for (int sk = 0; sk < 8; ++sk)
+      for (int sk = 0; sk < KS; ++sk)
         if (sk < ks) kstep(sk);
     }
     // epilogue: lane l, element e of acc[a][cb] holds feature 4 (l/16) + e of
@@ -630,13 +633,16 @@ __global__ void fill_pos_kernel(int32_t* pos, int count, int32_t v0, int32_t ste
 }  // namespace
 
 // Shapes the streaming kernel serves (bf16 output): r_max a multiple of 32
-// up to 256, D a multiple of 128 with whole heads in a 128-feature tile
+// up to 256, or up to 512 with 256-feature tiles (D a multiple of 256, head_dim
+// dividing 256), D a multiple of 128 with whole heads in a 128-feature tile
 // (head_dim 32, 64 or 128), and byte offsets of C and of the output within
 // the 32-bit range of a buffer descriptor.
+static bool recon_wide_tiles(int D, int head_dim) { return D % 256 == 0 && 256 % head_dim == 0; }
 bool iskv_recon_stream_ok(const isvd_handle* h, int32_t n_total, int32_t head_dim) {
   const int D = h->cfg.D, R = h->cfg.r_max;
   const size_t cb = (size_t)iskv_coord_bytes(h->cfg);
-  return D % RM_BN == 0 && head_dim % 32 == 0 && RM_BN % head_dim == 0 && R % 32 == 0 && R <= 256 &&
+  const int rmax = recon_wide_tiles(D, head_dim) ? 512 : 256;
+  return D % RM_BN == 0 && head_dim % 32 == 0 && RM_BN % head_dim == 0 && R % 32 == 0 && R <= rmax &&
          (size_t)h->n_host * R * cb < ((size_t)1 << 31) && (size_t)n_total * D * 2 < ((size_t)1 << 31);
 }
 
@@ -659,19 +665,23 @@ int iskv_launch_reconstruct_batched(const isvd_handle* const* hs, int32_t count,
   if (np > 0) {
     auto go = [&](auto* tag) {
       using TC = std::remove_pointer_t<decltype(tag)>;
-      if (D % 256 == 0 && 256 % head_dim == 0) {
+      if (recon_wide_tiles(D, head_dim)) {
         // 256-feature tiles (8 waves), one workgroup per CU
         const int T = D / 256;
         const int G = T >= 32 ? 1 : 32 / T;  // 256 workgroups when T divides 32
         const int S = std::max(8 * G, (np + 7) / 8 * 8);  // at least one row group per path
-        hipLaunchKernelGGL((recon_stream_kernel<TC, 8, RS_BM32>), dim3(T * S), dim3(512), 0, s, tab, np, R, R, D,
-                           head_dim, lt, T, S);
+        if (R <= 256)
+          hipLaunchKernelGGL((recon_stream_kernel<TC, 8, RS_BM32, 256>), dim3(T * S), dim3(512), 0, s, tab, np, R, R,
+                             D, head_dim, lt, T, S);
+        else  // 16-row blocks: the ring of staged rows fits beside the wider B operands
+          hipLaunchKernelGGL((recon_stream_kernel<TC, 8, 16, 512>), dim3(T * S), dim3(512), 0, s, tab, np, R, R, D,
+                             head_dim, lt, T, S);
       } else {
         const int T = D / 128;
         const int G = T >= 64 ? 1 : 64 / T;  // 512 workgroups when T divides 64
         const int S = std::max(8 * G, (np + 7) / 8 * 8);
-        hipLaunchKernelGGL((recon_stream_kernel<TC, 4, RS_BM32>), dim3(T * S), dim3(256), 0, s, tab, np, R, R, D,
-                           head_dim, lt, T, S);
+        hipLaunchKernelGGL((recon_stream_kernel<TC, 4, RS_BM32, 256>), dim3(T * S), dim3(256), 0, s, tab, np, R, R,
+                           D, head_dim, lt, T, S);
       }
     };
     if (iskv_bf16_coords(h0->cfg)) go((uint16_t*)nullptr);

@@ -870,6 +870,39 @@ def test_reconstruct_batched_matches_separate(K, c16):
     pa.close()
 
 
+@pytest.mark.parametrize("r", [384, 512])
+def test_reconstruct_high_rank_bf16(K, r):
+    """bf16 reconstruction with RoPE at ranks above 256 (Algorithm 3 steps
+    7-8; the 64K-row workload runs r = 512): the streaming kernel's wide form
+    stages 512 coordinate columns (r = 384 leaves the last 128 unused) in
+    16-row blocks. A fresh factor of 3,000 rows at shuffled positions,
+    compared with the oracle's rebuild of the GPU's own factors, and the
+    batched call bit for bit with the single one."""
+    D, hd, theta, n = 1024, 128, 500000.0, 3000
+    n_total = n + 61
+    rng = np.random.default_rng(r)
+    X = synth.kv_stream(synth.CONFIG_KV_K, n)
+    pos = rng.permutation(n_total)[:n].astype(np.int32)
+    p = K.IsvdPath(D=D, r_max=r, b_max=64, n_cap=n, reorth_every_rows=256, device=DEV)
+    p.refit(torch.from_numpy(X).to(DEV), torch.from_numpy(pos).to(DEV), iters=24)
+    out = torch.full((n_total, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    outb = out.clone()
+    p.reconstruct(out, n_total, head_dim=hd, rope=True, theta=theta)
+    K.kv_reconstruct_batched([p.h], [outb], [n_total], [True], hd, theta)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), outb.view(torch.int16))
+    C, B, _, gpos, st = gpu_factors(p)
+    assert st == 0 and C.shape == (n, r) and np.array_equal(gpos, pos)
+    fac = O.Factor(U=C, sigma=np.ones(C.shape[1]), B=B, pos=gpos)
+    rest = np.setdiff1d(np.arange(n_total), pos).astype(np.int32)
+    ref = O.reconstruct(fac, np.zeros((rest.size, D), np.float32), rest, n_total, hd, True, theta)
+    gb = out.double().cpu().numpy()
+    assert np.isfinite(gb[pos]).all()
+    assert rel(gb[pos], ref[pos]) < 5e-3, rel(gb[pos], ref[pos])
+    print(f"r={r}: bf16 rel to the oracle {rel(gb[pos], ref[pos]):.3e}")
+    p.close()
+
+
 # --------------------------------------------------------------------------- attention
 @pytest.mark.parametrize("batch,n,hq,hkv", [(1, 1000, 32, 8), (2, 4096, 32, 8), (1, 63, 8, 8),
                                             (2, 33000, 16, 4), (1, 140000, 32, 8), (1, 3000, 32, 4)])
