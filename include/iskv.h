@@ -295,7 +295,8 @@ int kv_reconstruct(const isvd_handle* h, const float* X_exact, const int32_t* po
  *   n_totals    host array: rows of each output, at least that handle's n.
  *   apply_rope  host array of count flags.
  *   head_dim    32, 64 or 128 (dividing 128); D a multiple of 128; r_max a
- *               multiple of 32, at most 256 (the bf16 matrix-core kernel's
+ *               multiple of 32, at most 256, or at most 512 when D is a
+ *               multiple of 256 (the streaming bf16 matrix-core kernel's
  *               shapes: any other shape is EINVAL, use kv_reconstruct).
  *   stream      hipStream_t as void* (NULL = hs[0]'s stream); the caller
  *               orders the call after every handle's pending merges.
