@@ -41,6 +41,17 @@ def test_host_only_calls():
     assert K.iskv_window_rows(10, 128, 32) == 170
     assert K.decode_attend_workspace_bytes(1, 1024, 32, 128) > 0
     assert K.decode_attend_workspace_bytes(1, 1024, 32, 64) == 0
+    # the batched reconstruction refuses missing arrays and counts outside
+    # 1 .. 32 before touching any handle or device memory
+    lib = K.lib
+    assert lib.kv_reconstruct_batched(None, 1, None, None, None, 128, 5e5, None) == -1
+    hs = (ctypes.c_void_p * 1)(None)
+    outs = (ctypes.c_void_p * 1)(None)
+    nt = (ctypes.c_int32 * 1)(0)
+    rp = (ctypes.c_int32 * 1)(0)
+    assert lib.kv_reconstruct_batched(hs, 0, outs, nt, rp, 128, 5e5, None) == -1
+    assert lib.kv_reconstruct_batched(hs, 33, outs, nt, rp, 128, 5e5, None) == -1
+    assert lib.kv_reconstruct_batched(hs, 1, outs, nt, rp, 128, 5e5, None) == -1  # null handle
 
 
 def test_no_cpu_fallback_in_product_package():
