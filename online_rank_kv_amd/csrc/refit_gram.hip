@@ -196,10 +196,9 @@ __global__ __launch_bounds__(256) void rg_scale_kernel(double* A, int ld, int m,
 // column; then L[r][c] = a[r][c] / sqrt(a[c][c]). Thread t owns column
 // t % 64 and the rows t / 64 + 4 u: a wave reads row c contiguously and
 // column c as broadcasts. A pivot below floor_ is raised to it. L is stored
-// back into M. Its inverse X (64 x 64, lower) goes to Li: lane j of the
-// first wave solves column j of L X = I by forward substitution (X in LDS,
-// read and written by that lane only, so no barrier; four partial sums
-// per dot product). Rows and columns past m are identity padding.
+// back into M. Its inverse X (64 x 64, lower) goes to Li, formed by
+// doubling from the 16 x 16 diagonal blocks (below). Rows and columns past m
+// are identity padding.
 constexpr int RG_CB = 64;
 
 __global__ __launch_bounds__(256) void rg_chol_diag_kernel(double* A, int ld, int m, int j0, double floor_,
@@ -249,23 +248,48 @@ __global__ __launch_bounds__(256) void rg_chol_diag_kernel(double* A, int ld, in
     }
     __syncthreads();
   }
+  // X = L^-1 by doubling: the four 16 x 16 diagonal blocks by forward
+  // substitution (a thread per column), then pairs of blocks with
+  // [[A, 0], [B, C]]^-1 = [[A^-1, 0], [-C^-1 B A^-1, C^-1]] at sizes 16 and 32,
+  // each off-diagonal block as two products over the whole workgroup. Only
+  // the lower triangle of X is read; the product B A^-1 is parked in the
+  // (unused) upper block beside it.
   if (t < RG_CB) {
-    const int j = t;
-    for (int i = 0; i < RG_CB; ++i) {
-      double a0 = i == j ? 1.0 : 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-      int qq = j;
-      for (; qq + 3 < i; qq += 4) {
-        a0 = fma(-Lu[i * RG_CB + qq], X[qq * RG_CB + j], a0);
-        a1 = fma(-Lu[i * RG_CB + qq + 1], X[(qq + 1) * RG_CB + j], a1);
-        a2 = fma(-Lu[i * RG_CB + qq + 2], X[(qq + 2) * RG_CB + j], a2);
-        a3 = fma(-Lu[i * RG_CB + qq + 3], X[(qq + 3) * RG_CB + j], a3);
+    const int o = 16 * (t >> 4), j = t & 15;
+    for (int i = j; i < 16; ++i) {
+      double a0 = i == j ? 1.0 : 0.0, a1 = 0.0;
+      int k = j;
+      for (; k + 1 < i; k += 2) {
+        a0 = fma(-Lu[(o + i) * RG_CB + o + k], X[(o + k) * RG_CB + o + j], a0);
+        a1 = fma(-Lu[(o + i) * RG_CB + o + k + 1], X[(o + k + 1) * RG_CB + o + j], a1);
       }
-      for (; qq < i; ++qq) a0 = fma(-Lu[i * RG_CB + qq], X[qq * RG_CB + j], a0);
-      X[i * RG_CB + j] = i < j ? 0.0 : ((a0 + a1) + (a2 + a3)) / Lu[i * RG_CB + i];
+      for (; k < i; ++k) a0 = fma(-Lu[(o + i) * RG_CB + o + k], X[(o + k) * RG_CB + o + j], a0);
+      X[(o + i) * RG_CB + o + j] = (a0 + a1) / Lu[(o + i) * RG_CB + o + i];
     }
   }
   __syncthreads();
-  for (int e = t; e < RG_CB * RG_CB; e += 256) Li[e] = X[e];
+  for (int h = 16; h < RG_CB; h *= 2) {  // blocks of size h combined into 2h
+    const int npairs = RG_CB / (2 * h);
+    // T = B A^-1 (B = L[o1 + r, o0 + k], A^-1 lower: k >= c), into X[o0 + r, o1 + c]
+    for (int e = t; e < npairs * h * h; e += 256) {
+      const int pr = e / (h * h), r = (e / h) % h, c = e % h;
+      const int o0 = 2 * h * pr, o1 = o0 + h;
+      double a = 0.0;
+      for (int k = c; k < h; ++k) a = fma(Lu[(o1 + r) * RG_CB + o0 + k], X[(o0 + k) * RG_CB + o0 + c], a);
+      X[(o0 + r) * RG_CB + o1 + c] = a;
+    }
+    __syncthreads();
+    // X[o1 + r, o0 + c] = -C^-1 T (C^-1 lower: k <= r)
+    for (int e = t; e < npairs * h * h; e += 256) {
+      const int pr = e / (h * h), r = (e / h) % h, c = e % h;
+      const int o0 = 2 * h * pr, o1 = o0 + h;
+      double a = 0.0;
+      for (int k = 0; k <= r; ++k) a = fma(X[(o1 + r) * RG_CB + o1 + k], X[(o0 + k) * RG_CB + o1 + c], a);
+      X[(o1 + r) * RG_CB + o0 + c] = -a;
+    }
+    __syncthreads();
+  }
+  for (int e = t; e < RG_CB * RG_CB; e += 256) Li[e] = (e / RG_CB) >= (e % RG_CB) ? X[e] : 0.0;
 }
 
 // Y[:, j] *= rs[j] over D rows of l columns (ld l).
