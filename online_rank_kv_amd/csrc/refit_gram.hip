@@ -189,107 +189,192 @@ __global__ __launch_bounds__(256) void rg_scale_kernel(double* A, int ld, int m,
 
 // Diagonal block of panel j0 of the right-looking Cholesky M = L L^T (one
 // workgroup, in LDS): factor the 64 x 64 block (already updated by the
-// earlier panels) and invert its factor. The block is factored in the
-// unscaled form on the whole symmetric square - step c subtracts
-// a[r][c] a[c][q] / a[c][c] from every trailing entry, reading row and
-// column c, which the step does not write - so there is one barrier per
-// column; then L[r][c] = a[r][c] / sqrt(a[c][c]). Thread t owns column
-// t % 64 and the rows t / 64 + 4 u: a wave reads row c contiguously and
-// column c as broadcasts. A pivot below floor_ is raised to it. L is stored
-// back into M. Its inverse X (64 x 64, lower) goes to Li, formed by
-// doubling from the 16 x 16 diagonal blocks (below). Rows and columns past m
-// are identity padding.
+// earlier panels) and invert its factor. Every phase keeps its dependency
+// chains in registers, so that LDS round trips do not serialise:
+// - elimination in the unscaled form (step c subtracts a[r][c] a[q][c] / p_c
+//   from every trailing entry, p_c = max(a[c][c], floor_)) in four
+//   16-column steps: wave 0 holds the 16 x 16 diagonal block as a full
+//   symmetric square in registers (lane 4 rr + g: row rr, columns 4 g..4 g+3)
+//   and eliminates it column by column with cross-lane reads; then a thread
+//   per row solves the panel below it from its 16 entries in registers, and
+//   the workgroup updates the trailing lower triangle;
+// - L[r][c] = a[r][c] / sqrt(p_c), stored back into M;
+// - X = L^-1 (lower) by doubling: the four 16 x 16 diagonal blocks by forward
+//   substitution (a thread per column, the column in registers), then pairs
+//   of blocks with [[A, 0], [B, C]]^-1 = [[A^-1, 0], [-C^-1 B A^-1, C^-1]] at
+//   sizes 16 and 32, each off-diagonal block as two workgroup-wide products;
+//   X goes to Li.
+// Rows and columns past m are identity padding.
 constexpr int RG_CB = 64;
+constexpr int RG_CS = RG_CB + 1;  // LDS row stride: a column walk spreads over the banks
 
 __global__ __launch_bounds__(256) void rg_chol_diag_kernel(double* A, int ld, int m, int j0, double floor_,
                                                            double* Li) {
-  __shared__ double Lu[RG_CB * RG_CB];
-  __shared__ double X[RG_CB * RG_CB];
-  const int t = threadIdx.x;
+  __shared__ double Lu[RG_CB * RG_CS];
+  __shared__ double X[RG_CB * RG_CS];
+  __shared__ double Tb[32 * 32];  // B A^-1 of the doubling step
+  __shared__ double ip[RG_CB];    // 1 / p_c
+  const int t = threadIdx.x, lane = t & 63;
   const int nb = min(RG_CB, m - j0);
   const int q = t & 63, r0 = t >> 6;
-  // the symmetric block from its lower triangle
+  // the lower triangle (the upper one is never read); X starts at zero
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
     const int r = r0 + 4 * u;
     double v = 0.0;
-    if (r < nb && q < nb) v = q <= r ? A[(size_t)(j0 + r) * ld + j0 + q] : A[(size_t)(j0 + q) * ld + j0 + r];
+    if (r < nb && q <= r) v = A[(size_t)(j0 + r) * ld + j0 + q];
     if (r >= nb && r == q) v = 1.0;
-    Lu[r * RG_CB + q] = v;
+    Lu[r * RG_CS + q] = v;
+    X[r * RG_CS + q] = 0.0;
   }
   __syncthreads();
-  for (int c = 0; c < RG_CB; ++c) {
-    const double inv = 1.0 / fmax(Lu[c * RG_CB + c], floor_);
-    if (q > c) {
-      const double g = Lu[c * RG_CB + q] * inv;
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int r = r0 + 4 * u;
-        if (r > c) Lu[r * RG_CB + q] -= Lu[r * RG_CB + c] * g;
+  for (int o = 0; o < RG_CB; o += 16) {
+    if (t < 64) {
+      const int rr = lane >> 2, g = lane & 3;
+      double a[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int cc = 4 * g + j;
+        a[j] = cc <= rr ? Lu[(o + rr) * RG_CS + o + cc] : Lu[(o + cc) * RG_CS + o + rr];
       }
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        // pivot a[c][c] (lane 4 c + c / 4), a[rr][c] (lane 4 rr + c / 4) and
+        // a[c][4 g + j] = a[4 g + j][c] (lane 4 c + g), all from slot c % 4
+        // or j, read before this column's update
+        const double dcc = a[c & 3];
+        const int lo = __builtin_amdgcn_readlane((int)__double2loint(dcc), 4 * c + (c >> 2));
+        const int hi = __builtin_amdgcn_readlane((int)__double2hiint(dcc), 4 * c + (c >> 2));
+        const double inv = 1.0 / fmax(__hiloint2double(hi, lo), floor_);
+        const double arc = __shfl(dcc, 4 * rr + (c >> 2));
+        double acq[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acq[j] = __shfl(a[j], 4 * c + g);
+        if (lane == 0) ip[o + c] = inv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (rr > c && 4 * g + j > c) a[j] = fma(-(arc * acq[j]), inv, a[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (4 * g + j <= rr) Lu[(o + rr) * RG_CS + o + 4 * g + j] = a[j];
     }
     __syncthreads();
+    if (o + 16 < RG_CB) {
+      // the panel below the block: row r, columns o..o+15
+      if (t < RG_CB - o - 16) {
+        const int r = o + 16 + t;
+        double x[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) x[k] = Lu[r * RG_CS + o + k];
+#pragma unroll
+        for (int c = 1; c < 16; ++c) {
+          double s0 = x[c], s1 = 0.0;
+#pragma unroll
+          for (int k = 0; k < c; ++k) {
+            const double f = Lu[(o + c) * RG_CS + o + k] * ip[o + k];
+            if (k & 1) s1 = fma(-x[k], f, s1);
+            else s0 = fma(-x[k], f, s0);
+          }
+          x[c] = s0 + s1;
+        }
+#pragma unroll
+        for (int k = 1; k < 16; ++k) Lu[r * RG_CS + o + k] = x[k];
+      }
+      __syncthreads();
+      // the trailing lower triangle
+      const int w2 = RG_CB - o - 16;
+      for (int e = t; e < w2 * w2; e += 256) {
+        const int r = o + 16 + e / w2, qq = o + 16 + e % w2;
+        if (qq > r) continue;
+        double s0 = Lu[r * RG_CS + qq], s1 = 0.0;
+#pragma unroll
+        for (int k = 0; k < 16; k += 2) {
+          s0 = fma(-(Lu[r * RG_CS + o + k] * Lu[qq * RG_CS + o + k]), ip[o + k], s0);
+          s1 = fma(-(Lu[r * RG_CS + o + k + 1] * Lu[qq * RG_CS + o + k + 1]), ip[o + k + 1], s1);
+        }
+        Lu[r * RG_CS + qq] = s0 + s1;
+      }
+      __syncthreads();
+    }
   }
   // L = column-scaled factor (lower), kept in Lu and stored to M
   {
-    const double dq = sqrt(fmax(Lu[q * RG_CB + q], floor_));
+    const double dq = sqrt(fmax(Lu[q * RG_CS + q], floor_));
+    const double rq = 1.0 / dq;
     double v[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int r = r0 + 4 * u;
-      v[u] = q < r ? Lu[r * RG_CB + q] / dq : (q == r ? dq : 0.0);
+      v[u] = q < r ? Lu[r * RG_CS + q] * rq : (q == r ? dq : 0.0);
     }
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int r = r0 + 4 * u;
-      Lu[r * RG_CB + q] = v[u];
+      Lu[r * RG_CS + q] = v[u];
       if (r < nb && q <= r) A[(size_t)(j0 + r) * ld + j0 + q] = v[u];
     }
     __syncthreads();
   }
-  // X = L^-1 by doubling: the four 16 x 16 diagonal blocks by forward
-  // substitution (a thread per column), then pairs of blocks with
-  // [[A, 0], [B, C]]^-1 = [[A^-1, 0], [-C^-1 B A^-1, C^-1]] at sizes 16 and 32,
-  // each off-diagonal block as two products over the whole workgroup. Only
-  // the lower triangle of X is read; the product B A^-1 is parked in the
-  // (unused) upper block beside it.
+  // the four diagonal 16 x 16 blocks of X, a thread per column j (the zeros
+  // above the diagonal included)
   if (t < RG_CB) {
     const int o = 16 * (t >> 4), j = t & 15;
-    for (int i = j; i < 16; ++i) {
-      double a0 = i == j ? 1.0 : 0.0, a1 = 0.0;
-      int k = j;
-      for (; k + 1 < i; k += 2) {
-        a0 = fma(-Lu[(o + i) * RG_CB + o + k], X[(o + k) * RG_CB + o + j], a0);
-        a1 = fma(-Lu[(o + i) * RG_CB + o + k + 1], X[(o + k + 1) * RG_CB + o + j], a1);
+    double x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      double s0 = i == j ? 1.0 : 0.0, s1 = 0.0;
+#pragma unroll
+      for (int k = 0; k < i; ++k) {
+        if (k & 1) s1 = fma(-Lu[(o + i) * RG_CS + o + k], x[k], s1);
+        else s0 = fma(-Lu[(o + i) * RG_CS + o + k], x[k], s0);
       }
-      for (; k < i; ++k) a0 = fma(-Lu[(o + i) * RG_CB + o + k], X[(o + k) * RG_CB + o + j], a0);
-      X[(o + i) * RG_CB + o + j] = (a0 + a1) / Lu[(o + i) * RG_CB + o + i];
+      x[i] = i >= j ? (s0 + s1) / Lu[(o + i) * RG_CS + o + i] : 0.0;
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) X[(o + i) * RG_CS + o + j] = x[i];
   }
   __syncthreads();
+#pragma unroll
   for (int h = 16; h < RG_CB; h *= 2) {  // blocks of size h combined into 2h
     const int npairs = RG_CB / (2 * h);
-    // T = B A^-1 (B = L[o1 + r, o0 + k], A^-1 lower: k >= c), into X[o0 + r, o1 + c]
-    for (int e = t; e < npairs * h * h; e += 256) {
+    // Tb = B A^-1 (B = L[o1 + r, o0 + k]; A^-1 is zero above its diagonal)
+#pragma unroll
+    for (int i = 0; i < npairs * h * h / 256; ++i) {
+      const int e = t + 256 * i;
       const int pr = e / (h * h), r = (e / h) % h, c = e % h;
       const int o0 = 2 * h * pr, o1 = o0 + h;
-      double a = 0.0;
-      for (int k = c; k < h; ++k) a = fma(Lu[(o1 + r) * RG_CB + o0 + k], X[(o0 + k) * RG_CB + o0 + c], a);
-      X[(o0 + r) * RG_CB + o1 + c] = a;
+      double s0 = 0.0, s1 = 0.0;
+#pragma unroll
+      for (int k = 0; k < h; k += 2) {
+        s0 = fma(Lu[(o1 + r) * RG_CS + o0 + k], X[(o0 + k) * RG_CS + o0 + c], s0);
+        s1 = fma(Lu[(o1 + r) * RG_CS + o0 + k + 1], X[(o0 + k + 1) * RG_CS + o0 + c], s1);
+      }
+      Tb[e] = s0 + s1;
     }
     __syncthreads();
-    // X[o1 + r, o0 + c] = -C^-1 T (C^-1 lower: k <= r)
-    for (int e = t; e < npairs * h * h; e += 256) {
+    // X[o1 + r, o0 + c] = -C^-1 Tb (C^-1 is zero above its diagonal)
+#pragma unroll
+    for (int i = 0; i < npairs * h * h / 256; ++i) {
+      const int e = t + 256 * i;
       const int pr = e / (h * h), r = (e / h) % h, c = e % h;
       const int o0 = 2 * h * pr, o1 = o0 + h;
-      double a = 0.0;
-      for (int k = 0; k <= r; ++k) a = fma(X[(o1 + r) * RG_CB + o1 + k], X[(o0 + k) * RG_CB + o1 + c], a);
-      X[(o1 + r) * RG_CB + o0 + c] = -a;
+      double s0 = 0.0, s1 = 0.0;
+#pragma unroll
+      for (int k = 0; k < h; k += 2) {
+        s0 = fma(X[(o1 + r) * RG_CS + o1 + k], Tb[pr * h * h + k * h + c], s0);
+        s1 = fma(X[(o1 + r) * RG_CS + o1 + k + 1], Tb[pr * h * h + (k + 1) * h + c], s1);
+      }
+      X[(o1 + r) * RG_CS + o0 + c] = -(s0 + s1);
     }
     __syncthreads();
   }
-  for (int e = t; e < RG_CB * RG_CB; e += 256) Li[e] = (e / RG_CB) >= (e % RG_CB) ? X[e] : 0.0;
+  for (int e = t; e < RG_CB * RG_CB; e += 256) {
+    const int r = e / RG_CB, c = e % RG_CB;
+    Li[e] = r >= c ? X[r * RG_CS + c] : 0.0;
+  }
 }
 
 // Y[:, j] *= rs[j] over D rows of l columns (ld l).
