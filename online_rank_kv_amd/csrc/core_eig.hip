@@ -1558,6 +1558,32 @@ __global__ __launch_bounds__(256) void bj_init_kernel(const double* __restrict__
 // |s_ij| / max(sqrt(|s_ii s_jj|), 0.01 max_i |s_ii|) (relative, with an
 // absolute floor at the rounding level of the largest entries), goes to
 // smax[0] (atomic max on the bits of a non-negative double).
+// A sweep is 63 rounds of 32 disjoint rotations (round-robin over the 64
+// indices). Within a round, thread (a, c) owns the 2 x 2 blocks of index
+// pairs i in {2a, 2a+1} and j in {2c, 2c+1}: it takes the rotations R_i, R_j
+// (formed once per wave from the round's diagonal entries), writes
+// R_i^T A[i, j] R_j (the row
+// rotation first, then the column one) into the other copy of A, and applies
+// R_i to Q's block (rows of pair j, columns of pair i). Blocks are disjoint,
+// so a round ends with a single barrier.
+// The annihilating rotation of rot2 with one division: with d = aqq - app,
+// t = sign(d) 2 apq / (|d| + sqrt(d^2 + 4 apq^2)) (tau = d / (2 apq) cleared
+// from rot2's t = sign(tau) / (|tau| + sqrt(1 + tau^2))), c = 1 / sqrt(1 + t^2).
+// For d = 0 either root t = +-1 annihilates; this takes sign(apq).
+__device__ __forceinline__ void bj_rot2(double app, double aqq, double apq, double* c, double* s) {
+  const double d = aqq - app;
+  const double tt = (d >= 0.0 ? 2.0 : -2.0) * apq / (fabs(d) + sqrt(fma(d, d, 4.0 * apq * apq)));
+  *c = rsqrt(fma(tt, tt, 1.0));
+  *s = tt * (*c);
+}
+
+__device__ __forceinline__ void bj_round_pair(int rr, int idx, int* p, int* q) {
+  const int x = idx == 0 ? BJ_P - 1 : (rr + idx) % (BJ_P - 1);
+  const int y = (rr - idx + BJ_P - 1) % (BJ_P - 1);
+  *p = x < y ? x : y;
+  *q = x < y ? y : x;
+}
+
 __global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict__ S, int ld, double* Qbuf,
                                                        int32_t* st, double* smax, int r, int NB, double tol,
                                                        const int64_t* __restrict__ bd) {
@@ -1571,10 +1597,9 @@ __global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict_
   int a, b;
   bj_pair(r, blockIdx.x, NB, &a, &b);
   extern __shared__ double bj_lds[];
-  double* A = bj_lds;               // [64][65]
-  double* Q = bj_lds + BJ_P * BJ_LD;  // [64][65]
-  __shared__ double cs[BJ_B], sn[BJ_B], red[4];
-  __shared__ int pp[BJ_B], qq[BJ_B];
+  double* Ab = bj_lds;                    // [2][64][65]: A, double-buffered across rounds
+  double* Q = bj_lds + 2 * BJ_P * BJ_LD;  // [64][65]
+  __shared__ double red[4];
   const int t = threadIdx.x;
   double cmax = 0.0;
   const double floor_d = 0.01 * smax[1];
@@ -1582,15 +1607,15 @@ __global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict_
     const int i = e / BJ_P, j = e % BJ_P;
     const int gi = bj_gidx(i, a, b), gj = bj_gidx(j, a, b);
     const double v = (gi < m && gj < m) ? S[(size_t)gi * ld + gj] : 0.0;
-    A[i * BJ_LD + j] = v;
+    Ab[i * BJ_LD + j] = v;
     Q[i * BJ_LD + j] = i == j ? 1.0 : 0.0;
   }
   __syncthreads();
   for (int e = t; e < BJ_P * BJ_P; e += 256) {
     const int i = e / BJ_P, j = e % BJ_P;
     if (j > i) {
-      const double den = fmax(sqrt(fabs(A[i * BJ_LD + i] * A[j * BJ_LD + j])), floor_d);
-      const double x = fabs(A[i * BJ_LD + j]);
+      const double den = fmax(sqrt(fabs(Ab[i * BJ_LD + i] * Ab[j * BJ_LD + j])), floor_d);
+      const double x = fabs(Ab[i * BJ_LD + j]);
       const double c = !isfinite(x) ? INFINITY : (den > 0.0 ? x / den : (x > 0.0 ? INFINITY : 0.0));
       cmax = fmax(cmax, c);
     }
@@ -1603,63 +1628,87 @@ __global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict_
     const double c = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
     atomicMax((unsigned long long*)smax, (unsigned long long)__double_as_longlong(c));
   }
-  // cyclic sweeps of 63 rounds of 32 disjoint rotations, until a sweep
-  // rotates nothing or BJ_INNER sweeps are done
+  const int ia = 2 * (t >> 4), jc = 2 * (t & 15), lane = t & 63, wave = t >> 6;
+  __shared__ double csw[4][BJ_B], snw[4][BJ_B];
   __shared__ int rotated;
+  int cur = 0;
   for (int inner = 0; inner < BJ_INNER; ++inner) {
-  if (t == 0) rotated = 0;
-  __syncthreads();
-  for (int rr = 0; rr < BJ_P - 1; ++rr) {
-    if (t < BJ_B) {
-      const int x = t == 0 ? BJ_P - 1 : (rr + t) % (BJ_P - 1);
-      const int y = (rr - t + BJ_P - 1) % (BJ_P - 1);
-      const int p = x < y ? x : y, q = x < y ? y : x;
-      const double app = A[p * BJ_LD + p], aqq = A[q * BJ_LD + q], apq = A[p * BJ_LD + q];
-      double c = 1.0, sv = 0.0;
-      if (apq != 0.0 && isfinite(apq) && fabs(apq) > tol * sqrt(fabs(app * aqq))) {
-        rot2(app, aqq, apq, &c, &sv);
-        rotated = 1;
+    if (t == 0) rotated = 0;
+    __syncthreads();
+    bool rot_any = false;
+    for (int rr = 0; rr < BJ_P - 1; ++rr) {
+      const double* A = Ab + cur * BJ_P * BJ_LD;
+      double* An = Ab + (cur ^ 1) * BJ_P * BJ_LD;
+      int pi[2], qi[2], pj[2], qj[2];
+      double ci[2], si[2], cj[2], sj[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bj_round_pair(rr, ia + u, &pi[u], &qi[u]);
+        bj_round_pair(rr, jc + u, &pj[u], &qj[u]);
       }
-      cs[t] = c;
-      sn[t] = sv;
-      pp[t] = p;
-      qq[t] = q;
+      // the round's 32 rotations, formed by lanes 0..31 of every wave (the
+      // same arithmetic in each) and shared through the wave's own LDS row:
+      // the wave's LDS operations complete in order, and the fence keeps
+      // the compiler from moving them
+      if (lane < BJ_B) {
+        int p, q;
+        bj_round_pair(rr, lane, &p, &q);
+        const double app = A[p * BJ_LD + p], aqq = A[q * BJ_LD + q], apq = A[p * BJ_LD + q];
+        double c = 1.0, sv = 0.0;
+        if (apq != 0.0 && isfinite(apq) && fabs(apq) > tol * sqrt(fabs(app * aqq))) {
+          bj_rot2(app, aqq, apq, &c, &sv);
+          rot_any = true;
+        }
+        csw[wave][lane] = c;
+        snw[wave][lane] = sv;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        ci[u] = csw[wave][ia + u];
+        si[u] = snw[wave][ia + u];
+        cj[u] = csw[wave][jc + u];
+        sj[u] = snw[wave][jc + u];
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+          const double x11 = A[pi[u] * BJ_LD + pj[v]], x12 = A[pi[u] * BJ_LD + qj[v]];
+          const double x21 = A[qi[u] * BJ_LD + pj[v]], x22 = A[qi[u] * BJ_LD + qj[v]];
+          const double y11 = ci[u] * x11 - si[u] * x21, y21 = si[u] * x11 + ci[u] * x21;
+          const double y12 = ci[u] * x12 - si[u] * x22, y22 = si[u] * x12 + ci[u] * x22;
+          An[pi[u] * BJ_LD + pj[v]] = cj[v] * y11 - sj[v] * y12;
+          An[pi[u] * BJ_LD + qj[v]] = sj[v] * y11 + cj[v] * y12;
+          An[qi[u] * BJ_LD + pj[v]] = cj[v] * y21 - sj[v] * y22;
+          An[qi[u] * BJ_LD + qj[v]] = sj[v] * y21 + cj[v] * y22;
+          // Q <- Q R_i on rows pj, qj
+          const double v1p = Q[pj[v] * BJ_LD + pi[u]], v1q = Q[pj[v] * BJ_LD + qi[u]];
+          const double v2p = Q[qj[v] * BJ_LD + pi[u]], v2q = Q[qj[v] * BJ_LD + qi[u]];
+          Q[pj[v] * BJ_LD + pi[u]] = ci[u] * v1p - si[u] * v1q;
+          Q[pj[v] * BJ_LD + qi[u]] = si[u] * v1p + ci[u] * v1q;
+          Q[qj[v] * BJ_LD + pi[u]] = ci[u] * v2p - si[u] * v2q;
+          Q[qj[v] * BJ_LD + qi[u]] = si[u] * v2p + ci[u] * v2q;
+        }
+      }
+      cur ^= 1;
+      __syncthreads();
     }
+    if (rot_any) rotated = 1;
     __syncthreads();
-    for (int e = t; e < BJ_B * BJ_P; e += 256) {  // rows p, q of A
-      const int i = e / BJ_P, j = e % BJ_P;
-      const int p = pp[i], q = qq[i];
-      const double c = cs[i], sv = sn[i];
-      const double xp = A[p * BJ_LD + j], xq = A[q * BJ_LD + j];
-      A[p * BJ_LD + j] = c * xp - sv * xq;
-      A[q * BJ_LD + j] = sv * xp + c * xq;
-    }
+    // every thread reads the flag before thread 0 may clear it for the next
+    // sweep, so the exit is uniform across the workgroup
+    const int any = rotated;
     __syncthreads();
-    for (int e = t; e < BJ_B * BJ_P; e += 256) {  // columns p, q of A and Q
-      const int i = e / BJ_P, j = e % BJ_P;
-      const int p = pp[i], q = qq[i];
-      const double c = cs[i], sv = sn[i];
-      const double xp = A[j * BJ_LD + p], xq = A[j * BJ_LD + q];
-      A[j * BJ_LD + p] = c * xp - sv * xq;
-      A[j * BJ_LD + q] = sv * xp + c * xq;
-      const double vp = Q[j * BJ_LD + p], vq = Q[j * BJ_LD + q];
-      Q[j * BJ_LD + p] = c * vp - sv * vq;
-      Q[j * BJ_LD + q] = sv * vp + c * vq;
-    }
-    __syncthreads();
-  }
-  // every thread reads the flag before thread 0 may clear it for the next
-  // sweep, so the exit is uniform across the workgroup
-  const int any = rotated;
-  __syncthreads();
-  if (!any) break;
+    if (!any) break;
   }
   double* Qo = Qbuf + (size_t)blockIdx.x * BJ_P * BJ_P;
   for (int e = t; e < BJ_P * BJ_P; e += 256) Qo[e] = Q[(e / BJ_P) * BJ_LD + e % BJ_P];
 }
 
 // Row pass: S[I, j0 .. j0+63] <- Q^T S[I, j0 .. j0+63] for the pair's 64
-// indices I. Grid (pairs, column tiles).
+// indices I, on the fp64 matrix cores. Grid (pairs, column tiles).
 __global__ __launch_bounds__(256) void bj_rows_kernel(double* S, int ld, const double* __restrict__ Qbuf,
                                                       const int32_t* st, int r, int NB,
                                                       const int64_t* __restrict__ bd) {
@@ -1683,19 +1732,32 @@ __global__ __launch_bounds__(256) void bj_rows_kernel(double* S, int ld, const d
     X[i][j] = (gi < m && gj < m) ? S[(size_t)gi * ld + gj] : 0.0;
   }
   __syncthreads();
-  for (int e = t; e < BJ_P * BJ_P; e += 256) {
-    const int i = e / BJ_P, j = e % BJ_P;  // output row i (local), column j
-    const int gi = bj_gidx(i, a, b), gj = j0 + j;
-    if (gi >= m || gj >= m) continue;
-    double acc = 0.0;
-#pragma unroll 8
-    for (int l = 0; l < BJ_P; ++l) acc = fma(Qs[l][i], X[l][j], acc);
-    S[(size_t)gi * ld + gj] = acc;
+  // wave w: output rows 16 w .. 16 w + 15, all 64 columns, as four 16 x 16
+  // tiles on v_mfma_f64_16x16x4f64 (lane layout as in dgemm_kernel)
+  const int lane = t & 63, w = t >> 6, rl = lane & 15, g = lane >> 4;
+  v4d acc[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) acc[u] = v4d{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+  for (int kk = 0; kk < BJ_P / 4; ++kk) {
+    const double av = Qs[4 * kk + g][16 * w + rl];  // (Q^T)[16 w + rl][4 kk + g]
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      acc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, X[4 * kk + g][16 * u + rl], acc[u], 0, 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * w + g + 4 * e, j = 16 * u + rl;
+      const int gi = bj_gidx(i, a, b), gj = j0 + j;
+      if (gi < m && gj < m) S[(size_t)gi * ld + gj] = acc[u][e];
+    }
   }
 }
 
 // Column pass: S[i, I] <- S[i, I] Q and V[i, I] <- V[i, I] Q for rows
-// i0 .. i0+63. Grid (pairs, row tiles).
+// i0 .. i0+63, on the fp64 matrix cores. Grid (pairs, row tiles).
 __global__ __launch_bounds__(256) void bj_cols_kernel(double* S, double* V, int ld, const double* __restrict__ Qbuf,
                                                       const int32_t* st, int r, int NB,
                                                       const int64_t* __restrict__ bd) {
@@ -1714,6 +1776,7 @@ __global__ __launch_bounds__(256) void bj_cols_kernel(double* S, double* V, int 
   const double* Qp = Qbuf + (size_t)blockIdx.x * BJ_P * BJ_P;
   const int t = threadIdx.x;
   for (int e = t; e < BJ_P * BJ_P; e += 256) Qs[e / BJ_P][e % BJ_P] = Qp[e];
+  const int lane = t & 63, w = t >> 6, rl = lane & 15, g = lane >> 4;
   for (int pass = 0; pass < 2; ++pass) {
     double* M = pass == 0 ? S : V;
     __syncthreads();
@@ -1723,14 +1786,24 @@ __global__ __launch_bounds__(256) void bj_cols_kernel(double* S, double* V, int 
       X[i][j] = (gi < m && gj < m) ? M[(size_t)gi * ld + gj] : 0.0;
     }
     __syncthreads();
-    for (int e = t; e < BJ_P * BJ_P; e += 256) {
-      const int i = e / BJ_P, j = e % BJ_P;
-      const int gi = i0 + i, gj = bj_gidx(j, a, b);
-      if (gi >= m || gj >= m) continue;
-      double acc = 0.0;
-#pragma unroll 8
-      for (int l = 0; l < BJ_P; ++l) acc = fma(X[i][l], Qs[l][j], acc);
-      M[(size_t)gi * ld + gj] = acc;
+    // wave w: rows 16 w .. 16 w + 15 of X Q as four 16 x 16 MFMA tiles
+    v4d acc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] = v4d{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+    for (int kk = 0; kk < BJ_P / 4; ++kk) {
+      const double av = X[16 * w + rl][4 * kk + g];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        acc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, Qs[4 * kk + g][16 * u + rl], acc[u], 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int gi = i0 + 16 * w + g + 4 * e, gj = bj_gidx(16 * u + rl, a, b);
+        if (gi < m && gj < m) M[(size_t)gi * ld + gj] = acc[u][e];
+      }
     }
   }
 }
@@ -1749,7 +1822,7 @@ __global__ void bj_check_kernel(int32_t* st, double* smax, double tol, int last,
   smax[0] = 0.0;
 }
 
-inline size_t bj_lds_bytes() { return (size_t)2 * BJ_P * BJ_LD * sizeof(double); }
+inline size_t bj_lds_bytes() { return (size_t)3 * BJ_P * BJ_LD * sizeof(double); }
 
 // A dense matrix goes straight to the block Jacobi (cold: S = A, V = I).
 __global__ void bj_force_kernel(int32_t* st) {
