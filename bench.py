@@ -62,6 +62,9 @@ def parse():
                     help="K and V carved from one allocation, merged as one batched launch sequence")
     ap.add_argument("--main-only", action="store_true",
                     help="only the timed K/V steps and their stage breakdown (for counter passes)")
+    ap.add_argument("--prompt-decode-only", action="store_true",
+                    help="only the 64K-row r = 512 prompt + decode leg, printed as its own JSON object "
+                         "(for kernel traces of the high-rank merge and the block Jacobi)")
     ap.add_argument("--no-graphs", action="store_true",
                     help="enqueue every kernel directly instead of replaying recorded HIP graphs "
                          "(same kernels; for kernel-trace profilers)")
@@ -482,6 +485,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.prompt_decode_only:
+        print(json.dumps({"prompt_decode_64k": prompt_decode_leg(args, K, torch, dev)}), flush=True)
+        return
     steps, warm = args.steps, args.warmup
     n_rows = N0 + (steps + warm + 4 + TIMED_MERGES + 3 * (MODE_MERGES + 2)) * BLK + WIN
     t_gen = time.perf_counter()

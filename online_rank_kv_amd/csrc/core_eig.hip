@@ -1558,14 +1558,18 @@ __global__ __launch_bounds__(256) void bj_init_kernel(const double* __restrict__
 // |s_ij| / max(sqrt(|s_ii s_jj|), 0.01 max_i |s_ii|) (relative, with an
 // absolute floor at the rounding level of the largest entries), goes to
 // smax[0] (atomic max on the bits of a non-negative double).
-// A sweep is 63 rounds of 32 disjoint rotations (round-robin over the 64
-// indices). Within a round, thread (a, c) owns the 2 x 2 blocks of index
-// pairs i in {2a, 2a+1} and j in {2c, 2c+1}: it takes the rotations R_i, R_j
-// (formed once per wave from the round's diagonal entries), writes
-// R_i^T A[i, j] R_j (the row
-// rotation first, then the column one) into the other copy of A, and applies
-// R_i to Q's block (rows of pair j, columns of pair i). Blocks are disjoint,
-// so a round ends with a single barrier.
+// A sweep is 63 rounds of 32 disjoint rotations in the round-robin order that
+// keeps every round's pairs at positions (2k, 2k+1): A is held by position,
+// and after a round the entry at positions (x, y) moves to (next(x), next(y))
+// (bj_next), which brings every index back to its own position after the
+// 63 rounds. Each wave forms the round's 32 rotations (a lane per pair, one
+// division and one rsqrt each) and shares them through its own LDS row; then
+// thread t takes pair column j = t % 32 and pair rows t / 32 + 8 u: it reads
+// the 2 x 2 blocks of A at positions (2i, 2j) as rows of two contiguous
+// doubles, writes R_i^T A_ij R_j (the row rotation first) to the moved
+// positions in the other copy of A, and applies R_j to the column pair at
+// positions (2j, 2j+1) of rows t / 32 + 8 v of Q (also double-buffered: the
+// columns move). One barrier per round.
 // The annihilating rotation of rot2 with one division: with d = aqq - app,
 // t = sign(d) 2 apq / (|d| + sqrt(d^2 + 4 apq^2)) (tau = d / (2 apq) cleared
 // from rot2's t = sign(tau) / (|tau| + sqrt(1 + tau^2))), c = 1 / sqrt(1 + t^2).
@@ -1577,11 +1581,11 @@ __device__ __forceinline__ void bj_rot2(double app, double aqq, double apq, doub
   *s = tt * (*c);
 }
 
-__device__ __forceinline__ void bj_round_pair(int rr, int idx, int* p, int* q) {
-  const int x = idx == 0 ? BJ_P - 1 : (rr + idx) % (BJ_P - 1);
-  const int y = (rr - idx + BJ_P - 1) % (BJ_P - 1);
-  *p = x < y ? x : y;
-  *q = x < y ? y : x;
+__device__ __forceinline__ int bj_next(int x) {
+  if (x == 0) return 0;
+  if (x == 1) return 2;
+  if ((x & 1) == 0) return x == BJ_P - 2 ? x + 1 : x + 2;
+  return x - 2;
 }
 
 __global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict__ S, int ld, double* Qbuf,
@@ -1596,9 +1600,10 @@ __global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict_
   const int m = st[ST_JM];
   int a, b;
   bj_pair(r, blockIdx.x, NB, &a, &b);
+  constexpr int BUF = BJ_P * BJ_LD;
   extern __shared__ double bj_lds[];
-  double* Ab = bj_lds;                    // [2][64][65]: A, double-buffered across rounds
-  double* Q = bj_lds + 2 * BJ_P * BJ_LD;  // [64][65]
+  double* Ab = bj_lds;            // [2][64][65]: A by position
+  double* Qb = bj_lds + 2 * BUF;  // [2][64][65]: Q, columns by position
   __shared__ double red[4];
   const int t = threadIdx.x;
   double cmax = 0.0;
@@ -1608,7 +1613,7 @@ __global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict_
     const int gi = bj_gidx(i, a, b), gj = bj_gidx(j, a, b);
     const double v = (gi < m && gj < m) ? S[(size_t)gi * ld + gj] : 0.0;
     Ab[i * BJ_LD + j] = v;
-    Q[i * BJ_LD + j] = i == j ? 1.0 : 0.0;
+    Qb[i * BJ_LD + j] = i == j ? 1.0 : 0.0;
   }
   __syncthreads();
   for (int e = t; e < BJ_P * BJ_P; e += 256) {
@@ -1628,7 +1633,8 @@ __global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict_
     const double c = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
     atomicMax((unsigned long long*)smax, (unsigned long long)__double_as_longlong(c));
   }
-  const int ia = 2 * (t >> 4), jc = 2 * (t & 15), lane = t & 63, wave = t >> 6;
+  const int jj = t & (BJ_B - 1), i0 = t >> 5, lane = t & 63, wave = t >> 6;
+  const int nj0 = bj_next(2 * jj), nj1 = bj_next(2 * jj + 1);
   __shared__ double csw[4][BJ_B], snw[4][BJ_B];
   __shared__ int rotated;
   int cur = 0;
@@ -1637,22 +1643,15 @@ __global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict_
     __syncthreads();
     bool rot_any = false;
     for (int rr = 0; rr < BJ_P - 1; ++rr) {
-      const double* A = Ab + cur * BJ_P * BJ_LD;
-      double* An = Ab + (cur ^ 1) * BJ_P * BJ_LD;
-      int pi[2], qi[2], pj[2], qj[2];
-      double ci[2], si[2], cj[2], sj[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        bj_round_pair(rr, ia + u, &pi[u], &qi[u]);
-        bj_round_pair(rr, jc + u, &pj[u], &qj[u]);
-      }
-      // the round's 32 rotations, formed by lanes 0..31 of every wave (the
-      // same arithmetic in each) and shared through the wave's own LDS row:
-      // the wave's LDS operations complete in order, and the fence keeps
-      // the compiler from moving them
+      const double* A = Ab + cur * BUF;
+      double* An = Ab + (cur ^ 1) * BUF;
+      const double* Qc = Qb + cur * BUF;
+      double* Qn = Qb + (cur ^ 1) * BUF;
+      // the round's rotations (pair k at positions 2k, 2k+1), the same
+      // arithmetic in every wave; the wave's LDS operations complete in
+      // order, and the fence keeps the compiler from moving them
       if (lane < BJ_B) {
-        int p, q;
-        bj_round_pair(rr, lane, &p, &q);
+        const int p = 2 * lane, q = p + 1;
         const double app = A[p * BJ_LD + p], aqq = A[q * BJ_LD + q], apq = A[p * BJ_LD + q];
         double c = 1.0, sv = 0.0;
         if (apq != 0.0 && isfinite(apq) && fabs(apq) > tol * sqrt(fabs(app * aqq))) {
@@ -1664,33 +1663,27 @@ __global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict_
       }
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
       __builtin_amdgcn_wave_barrier();
+      const double cj = csw[wave][jj], sj = snw[wave][jj];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        ci[u] = csw[wave][ia + u];
-        si[u] = snw[wave][ia + u];
-        cj[u] = csw[wave][jc + u];
-        sj[u] = snw[wave][jc + u];
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + 8 * u;
+        const double ci = csw[wave][i], si = snw[wave][i];
+        const double x11 = A[(2 * i) * BJ_LD + 2 * jj], x12 = A[(2 * i) * BJ_LD + 2 * jj + 1];
+        const double x21 = A[(2 * i + 1) * BJ_LD + 2 * jj], x22 = A[(2 * i + 1) * BJ_LD + 2 * jj + 1];
+        const double y11 = ci * x11 - si * x21, y21 = si * x11 + ci * x21;
+        const double y12 = ci * x12 - si * x22, y22 = si * x12 + ci * x22;
+        const int ni0 = bj_next(2 * i), ni1 = bj_next(2 * i + 1);
+        An[ni0 * BJ_LD + nj0] = cj * y11 - sj * y12;
+        An[ni0 * BJ_LD + nj1] = sj * y11 + cj * y12;
+        An[ni1 * BJ_LD + nj0] = cj * y21 - sj * y22;
+        An[ni1 * BJ_LD + nj1] = sj * y21 + cj * y22;
       }
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-#pragma unroll
-        for (int v = 0; v < 2; ++v) {
-          const double x11 = A[pi[u] * BJ_LD + pj[v]], x12 = A[pi[u] * BJ_LD + qj[v]];
-          const double x21 = A[qi[u] * BJ_LD + pj[v]], x22 = A[qi[u] * BJ_LD + qj[v]];
-          const double y11 = ci[u] * x11 - si[u] * x21, y21 = si[u] * x11 + ci[u] * x21;
-          const double y12 = ci[u] * x12 - si[u] * x22, y22 = si[u] * x12 + ci[u] * x22;
-          An[pi[u] * BJ_LD + pj[v]] = cj[v] * y11 - sj[v] * y12;
-          An[pi[u] * BJ_LD + qj[v]] = sj[v] * y11 + cj[v] * y12;
-          An[qi[u] * BJ_LD + pj[v]] = cj[v] * y21 - sj[v] * y22;
-          An[qi[u] * BJ_LD + qj[v]] = sj[v] * y21 + cj[v] * y22;
-          // Q <- Q R_i on rows pj, qj
-          const double v1p = Q[pj[v] * BJ_LD + pi[u]], v1q = Q[pj[v] * BJ_LD + qi[u]];
-          const double v2p = Q[qj[v] * BJ_LD + pi[u]], v2q = Q[qj[v] * BJ_LD + qi[u]];
-          Q[pj[v] * BJ_LD + pi[u]] = ci[u] * v1p - si[u] * v1q;
-          Q[pj[v] * BJ_LD + qi[u]] = si[u] * v1p + ci[u] * v1q;
-          Q[qj[v] * BJ_LD + pi[u]] = ci[u] * v2p - si[u] * v2q;
-          Q[qj[v] * BJ_LD + qi[u]] = si[u] * v2p + ci[u] * v2q;
-        }
+      for (int v = 0; v < 8; ++v) {
+        const int row = i0 + 8 * v;
+        const double vp = Qc[row * BJ_LD + 2 * jj], vq = Qc[row * BJ_LD + 2 * jj + 1];
+        Qn[row * BJ_LD + nj0] = cj * vp - sj * vq;
+        Qn[row * BJ_LD + nj1] = sj * vp + cj * vq;
       }
       cur ^= 1;
       __syncthreads();
@@ -1703,8 +1696,10 @@ __global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict_
     __syncthreads();
     if (!any) break;
   }
+  // whole sweeps only: every index is back at its own position
+  const double* Qf = Qb + cur * BUF;
   double* Qo = Qbuf + (size_t)blockIdx.x * BJ_P * BJ_P;
-  for (int e = t; e < BJ_P * BJ_P; e += 256) Qo[e] = Q[(e / BJ_P) * BJ_LD + e % BJ_P];
+  for (int e = t; e < BJ_P * BJ_P; e += 256) Qo[e] = Qf[(e / BJ_P) * BJ_LD + e % BJ_P];
 }
 
 // Row pass: S[I, j0 .. j0+63] <- Q^T S[I, j0 .. j0+63] for the pair's 64
@@ -1822,7 +1817,7 @@ __global__ void bj_check_kernel(int32_t* st, double* smax, double tol, int last,
   smax[0] = 0.0;
 }
 
-inline size_t bj_lds_bytes() { return (size_t)3 * BJ_P * BJ_LD * sizeof(double); }
+inline size_t bj_lds_bytes() { return (size_t)4 * BJ_P * BJ_LD * sizeof(double); }
 
 // A dense matrix goes straight to the block Jacobi (cold: S = A, V = I).
 __global__ void bj_force_kernel(int32_t* st) {
