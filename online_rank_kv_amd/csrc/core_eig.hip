@@ -1565,8 +1565,8 @@ __global__ __launch_bounds__(256) void bj_init_kernel(const double* __restrict__
 // 63 rounds. Each wave forms the round's 32 rotations (a lane per pair, one
 // division and one rsqrt each) and shares them through its own LDS row; then
 // thread t takes pair column j = t % 32 and pair rows t / 32 + 8 u: it reads
-// the 2 x 2 blocks of A at positions (2i, 2j) as rows of two contiguous
-// doubles, writes R_i^T A_ij R_j (the row rotation first) to the moved
+// the 2 x 2 blocks of A at positions (2i, 2j) (bj_col: lanes read and write
+// contiguous doubles), writes R_i^T A_ij R_j (the row rotation first) to the moved
 // positions in the other copy of A, and applies R_j to the column pair at
 // positions (2j, 2j+1) of rows t / 32 + 8 v of Q (also double-buffered: the
 // columns move). One barrier per round.
@@ -1580,6 +1580,11 @@ __device__ __forceinline__ void bj_rot2(double app, double aqq, double apq, doub
   *c = rsqrt(fma(tt, tt, 1.0));
   *s = tt * (*c);
 }
+
+// Storage column of position x in a row of A or Q: even positions first
+// (2j at column j), then odd ones (2j+1 at column 32 + j), so that a pair's
+// two columns and their moved columns are each contiguous across lanes.
+__device__ __forceinline__ int bj_col(int x) { return (x & 1) ? BJ_B + (x >> 1) : (x >> 1); }
 
 __device__ __forceinline__ int bj_next(int x) {
   if (x == 0) return 0;
@@ -1612,15 +1617,15 @@ __global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict_
     const int i = e / BJ_P, j = e % BJ_P;
     const int gi = bj_gidx(i, a, b), gj = bj_gidx(j, a, b);
     const double v = (gi < m && gj < m) ? S[(size_t)gi * ld + gj] : 0.0;
-    Ab[i * BJ_LD + j] = v;
-    Qb[i * BJ_LD + j] = i == j ? 1.0 : 0.0;
+    Ab[i * BJ_LD + bj_col(j)] = v;
+    Qb[i * BJ_LD + bj_col(j)] = i == j ? 1.0 : 0.0;
   }
   __syncthreads();
   for (int e = t; e < BJ_P * BJ_P; e += 256) {
     const int i = e / BJ_P, j = e % BJ_P;
     if (j > i) {
-      const double den = fmax(sqrt(fabs(Ab[i * BJ_LD + i] * Ab[j * BJ_LD + j])), floor_d);
-      const double x = fabs(Ab[i * BJ_LD + j]);
+      const double den = fmax(sqrt(fabs(Ab[i * BJ_LD + bj_col(i)] * Ab[j * BJ_LD + bj_col(j)])), floor_d);
+      const double x = fabs(Ab[i * BJ_LD + bj_col(j)]);
       const double c = !isfinite(x) ? INFINITY : (den > 0.0 ? x / den : (x > 0.0 ? INFINITY : 0.0));
       cmax = fmax(cmax, c);
     }
@@ -1634,7 +1639,7 @@ __global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict_
     atomicMax((unsigned long long*)smax, (unsigned long long)__double_as_longlong(c));
   }
   const int jj = t & (BJ_B - 1), i0 = t >> 5, lane = t & 63, wave = t >> 6;
-  const int nj0 = bj_next(2 * jj), nj1 = bj_next(2 * jj + 1);
+  const int nj0 = bj_col(bj_next(2 * jj)), nj1 = bj_col(bj_next(2 * jj + 1));
   __shared__ double csw[4][BJ_B], snw[4][BJ_B];
   __shared__ int rotated;
   int cur = 0;
@@ -1652,7 +1657,7 @@ __global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict_
       // order, and the fence keeps the compiler from moving them
       if (lane < BJ_B) {
         const int p = 2 * lane, q = p + 1;
-        const double app = A[p * BJ_LD + p], aqq = A[q * BJ_LD + q], apq = A[p * BJ_LD + q];
+        const double app = A[p * BJ_LD + lane], aqq = A[q * BJ_LD + BJ_B + lane], apq = A[p * BJ_LD + BJ_B + lane];
         double c = 1.0, sv = 0.0;
         if (apq != 0.0 && isfinite(apq) && fabs(apq) > tol * sqrt(fabs(app * aqq))) {
           bj_rot2(app, aqq, apq, &c, &sv);
@@ -1663,15 +1668,32 @@ __global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict_
       }
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
       __builtin_amdgcn_wave_barrier();
+      // every operand of the round is read before any result is written (the
+      // two copies share one LDS array, so a store would otherwise hold back
+      // the loads after it)
       const double cj = csw[wave][jj], sj = snw[wave][jj];
+      double ci[4], si[4], x[4][4], vq[8][2];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int i = i0 + 8 * u;
-        const double ci = csw[wave][i], si = snw[wave][i];
-        const double x11 = A[(2 * i) * BJ_LD + 2 * jj], x12 = A[(2 * i) * BJ_LD + 2 * jj + 1];
-        const double x21 = A[(2 * i + 1) * BJ_LD + 2 * jj], x22 = A[(2 * i + 1) * BJ_LD + 2 * jj + 1];
-        const double y11 = ci * x11 - si * x21, y21 = si * x11 + ci * x21;
-        const double y12 = ci * x12 - si * x22, y22 = si * x12 + ci * x22;
+        ci[u] = csw[wave][i];
+        si[u] = snw[wave][i];
+        x[u][0] = A[(2 * i) * BJ_LD + jj];
+        x[u][1] = A[(2 * i) * BJ_LD + BJ_B + jj];
+        x[u][2] = A[(2 * i + 1) * BJ_LD + jj];
+        x[u][3] = A[(2 * i + 1) * BJ_LD + BJ_B + jj];
+      }
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const int row = i0 + 8 * v;
+        vq[v][0] = Qc[row * BJ_LD + jj];
+        vq[v][1] = Qc[row * BJ_LD + BJ_B + jj];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + 8 * u;
+        const double y11 = ci[u] * x[u][0] - si[u] * x[u][2], y21 = si[u] * x[u][0] + ci[u] * x[u][2];
+        const double y12 = ci[u] * x[u][1] - si[u] * x[u][3], y22 = si[u] * x[u][1] + ci[u] * x[u][3];
         const int ni0 = bj_next(2 * i), ni1 = bj_next(2 * i + 1);
         An[ni0 * BJ_LD + nj0] = cj * y11 - sj * y12;
         An[ni0 * BJ_LD + nj1] = sj * y11 + cj * y12;
@@ -1681,9 +1703,8 @@ __global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict_
 #pragma unroll
       for (int v = 0; v < 8; ++v) {
         const int row = i0 + 8 * v;
-        const double vp = Qc[row * BJ_LD + 2 * jj], vq = Qc[row * BJ_LD + 2 * jj + 1];
-        Qn[row * BJ_LD + nj0] = cj * vp - sj * vq;
-        Qn[row * BJ_LD + nj1] = sj * vp + cj * vq;
+        Qn[row * BJ_LD + nj0] = cj * vq[v][0] - sj * vq[v][1];
+        Qn[row * BJ_LD + nj1] = sj * vq[v][0] + cj * vq[v][1];
       }
       cur ^= 1;
       __syncthreads();
@@ -1699,7 +1720,7 @@ __global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict_
   // whole sweeps only: every index is back at its own position
   const double* Qf = Qb + cur * BUF;
   double* Qo = Qbuf + (size_t)blockIdx.x * BJ_P * BJ_P;
-  for (int e = t; e < BJ_P * BJ_P; e += 256) Qo[e] = Qf[(e / BJ_P) * BJ_LD + e % BJ_P];
+  for (int e = t; e < BJ_P * BJ_P; e += 256) Qo[e] = Qf[(e / BJ_P) * BJ_LD + bj_col(e % BJ_P)];
 }
 
 // Row pass: S[I, j0 .. j0+63] <- Q^T S[I, j0 .. j0+63] for the pair's 64
