@@ -46,55 +46,64 @@ __device__ __forceinline__ double ld_elt(const float* p) { return (double)*p; }
 // op(A) is M x K: A stored M x K (lda), or K x M when TA. op(B) is K x N: B
 // stored K x N (ldb), or N x K when TB. Element types TEA / TEB are float or
 // double (widened exactly). A 256-thread workgroup owns a 64 x 64 tile; wave
-// w computes its 32 x 32 quarter as 2 x 2 blocks; K goes in chunks of 16
-// staged in LDS, the next chunk's loads in flight during the current one.
+// w computes its 32 x 32 quarter as 2 x 2 blocks; K goes in steps of 64
+// (four chunks of 16) staged in LDS, the next step's loads in flight during
+// the current one, so the K = 64 products of the Cholesky panels and the
+// triangular solves take one step.
 // lower_only: tiles strictly above the diagonal are skipped. beta == 0 never
 // reads C. C may be the A operand itself when N <= 64 (one tile column): a
 // workgroup reads all of its rows of A before it writes any of them.
 constexpr int RG_T = 64, RG_KC = 16, RG_LS = RG_T + 4;
+constexpr int RG_NCH = 4;  // 16-deep chunks staged per step (64 of K: one step for the K = 64 panel products)
 
 template <bool TA, bool TB, typename TEA, typename TEB>
 __global__ __launch_bounds__(256) void rg_gemm_kernel(const TEA* A, int lda, const TEB* B, int ldb, double* C, int ldc,
                                                       int M, int N, int K, double alpha, double beta, int lower_only) {
   const int i0 = blockIdx.y * RG_T, j0 = blockIdx.x * RG_T;
   if (lower_only && j0 > i0) return;
-  __shared__ double As[RG_KC][RG_LS], Bs[RG_KC][RG_LS];
+  __shared__ double As[RG_NCH][RG_KC][RG_LS], Bs[RG_NCH][RG_KC][RG_LS];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wr = wave >> 1, wc = wave & 1;
-  double ar[4], br[4];
+  double ar[RG_NCH][4], br[RG_NCH][4];
   // staging map: TA / !TB chunks are read along rows of 64 (k = t / 16,
   // 4 consecutive entries from 4 (t % 16)); !TA / TB along rows of 16
   // (entry = t / 4, 4 consecutive k from 4 (t % 4))
-  auto load = [&](int k0) {
+  auto load = [&](int k0s) {
+#pragma unroll
+    for (int ch = 0; ch < RG_NCH; ++ch) {
+    const int k0 = k0s + RG_KC * ch;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if (TA) {
         const int kk = t >> 4, i = ((t & 15) << 2) + q;
         const bool in = k0 + kk < K && i0 + i < M;
-        ar[q] = in ? ld_elt(A + (size_t)(k0 + kk) * lda + i0 + i) : 0.0;
+        ar[ch][q] = in ? ld_elt(A + (size_t)(k0 + kk) * lda + i0 + i) : 0.0;
       } else {
         const int i = t >> 2, kk = ((t & 3) << 2) + q;
         const bool in = k0 + kk < K && i0 + i < M;
-        ar[q] = in ? ld_elt(A + (size_t)(i0 + i) * lda + k0 + kk) : 0.0;
+        ar[ch][q] = in ? ld_elt(A + (size_t)(i0 + i) * lda + k0 + kk) : 0.0;
       }
       if (TB) {
         const int j = t >> 2, kk = ((t & 3) << 2) + q;
         const bool in = k0 + kk < K && j0 + j < N;
-        br[q] = in ? ld_elt(B + (size_t)(j0 + j) * ldb + k0 + kk) : 0.0;
+        br[ch][q] = in ? ld_elt(B + (size_t)(j0 + j) * ldb + k0 + kk) : 0.0;
       } else {
         const int kk = t >> 4, j = ((t & 15) << 2) + q;
         const bool in = k0 + kk < K && j0 + j < N;
-        br[q] = in ? ld_elt(B + (size_t)(k0 + kk) * ldb + j0 + j) : 0.0;
+        br[ch][q] = in ? ld_elt(B + (size_t)(k0 + kk) * ldb + j0 + j) : 0.0;
       }
+    }
     }
   };
   auto store = [&]() {
 #pragma unroll
+    for (int ch = 0; ch < RG_NCH; ++ch)
+#pragma unroll
     for (int q = 0; q < 4; ++q) {
-      if (TA) As[t >> 4][((t & 15) << 2) + q] = ar[q];
-      else As[((t & 3) << 2) + q][t >> 2] = ar[q];
-      if (TB) Bs[((t & 3) << 2) + q][t >> 2] = br[q];
-      else Bs[t >> 4][((t & 15) << 2) + q] = br[q];
+      if (TA) As[ch][t >> 4][((t & 15) << 2) + q] = ar[ch][q];
+      else As[ch][((t & 3) << 2) + q][t >> 2] = ar[ch][q];
+      if (TB) Bs[ch][((t & 3) << 2) + q][t >> 2] = br[ch][q];
+      else Bs[ch][t >> 4][((t & 15) << 2) + q] = br[ch][q];
     }
   };
   v4d_t acc[2][2];
@@ -103,19 +112,19 @@ __global__ __launch_bounds__(256) void rg_gemm_kernel(const TEA* A, int lda, con
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = v4d_t{0.0, 0.0, 0.0, 0.0};
   if (K > 0) load(0);
-  for (int k0 = 0; k0 < K; k0 += RG_KC) {
+  for (int k0 = 0; k0 < K; k0 += RG_NCH * RG_KC) {
     __syncthreads();
     store();
     __syncthreads();
-    if (k0 + RG_KC < K) load(k0 + RG_KC);
+    if (k0 + RG_NCH * RG_KC < K) load(k0 + RG_NCH * RG_KC);
 #pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
-      const int kk = 4 * k4 + (lane >> 4);
+    for (int k4 = 0; k4 < 4 * RG_NCH; ++k4) {
+      const int ch = k4 >> 2, kk = 4 * (k4 & 3) + (lane >> 4);
       double av[2], bv[2];
 #pragma unroll
-      for (int a = 0; a < 2; ++a) av[a] = As[kk][32 * wr + 16 * a + (lane & 15)];
+      for (int a = 0; a < 2; ++a) av[a] = As[ch][kk][32 * wr + 16 * a + (lane & 15)];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) bv[b] = Bs[kk][32 * wc + 16 * b + (lane & 15)];
+      for (int b = 0; b < 2; ++b) bv[b] = Bs[ch][kk][32 * wc + 16 * b + (lane & 15)];
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
