@@ -1788,27 +1788,30 @@ __global__ __launch_bounds__(256) void bj_cols_kernel(double* S, double* V, int 
   if (i0 >= m) return;
   int a, b;
   bj_pair(r, blockIdx.x, NB, &a, &b);
-  __shared__ double Qs[BJ_P][BJ_LD], X[BJ_P][BJ_LD];
+  // Q and both row tiles are staged at once, so their loads are in flight together
+  __shared__ double Qs[BJ_P][BJ_LD], X[2][BJ_P][BJ_LD];
   const double* Qp = Qbuf + (size_t)blockIdx.x * BJ_P * BJ_P;
   const int t = threadIdx.x;
-  for (int e = t; e < BJ_P * BJ_P; e += 256) Qs[e / BJ_P][e % BJ_P] = Qp[e];
+  for (int e = t; e < BJ_P * BJ_P; e += 256) {
+    const int i = e / BJ_P, j = e % BJ_P;
+    const int gi = i0 + i, gj = bj_gidx(j, a, b);
+    const bool in = gi < m && gj < m;
+    Qs[i][j] = Qp[e];
+    X[0][i][j] = in ? S[(size_t)gi * ld + gj] : 0.0;
+    X[1][i][j] = in ? V[(size_t)gi * ld + gj] : 0.0;
+  }
+  __syncthreads();
   const int lane = t & 63, w = t >> 6, rl = lane & 15, g = lane >> 4;
+#pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     double* M = pass == 0 ? S : V;
-    __syncthreads();
-    for (int e = t; e < BJ_P * BJ_P; e += 256) {
-      const int i = e / BJ_P, j = e % BJ_P;
-      const int gi = i0 + i, gj = bj_gidx(j, a, b);
-      X[i][j] = (gi < m && gj < m) ? M[(size_t)gi * ld + gj] : 0.0;
-    }
-    __syncthreads();
     // wave w: rows 16 w .. 16 w + 15 of X Q as four 16 x 16 MFMA tiles
     v4d acc[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) acc[u] = v4d{0.0, 0.0, 0.0, 0.0};
 #pragma unroll 4
     for (int kk = 0; kk < BJ_P / 4; ++kk) {
-      const double av = X[16 * w + rl][4 * kk + g];
+      const double av = X[pass][16 * w + rl][4 * kk + g];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         acc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, Qs[4 * kk + g][16 * u + rl], acc[u], 0, 0, 0);
