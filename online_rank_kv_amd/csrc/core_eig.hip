@@ -1475,6 +1475,7 @@ __global__ __launch_bounds__(1024) void core_jacobi_kernel(double* S, double* V,
 constexpr int BJ_B = 32;          // block size
 constexpr int BJ_P = 2 * BJ_B;    // pair size
 constexpr int BJ_LD = BJ_P + 1;   // LDS row stride (doubles)
+constexpr int BJ_NT = 512;        // threads of a pair solve (8 waves: two per SIMD)
 // Cores up to BJ_MIN_M keep the one-workgroup Jacobi: there the refinement
 // converges except in early merges, and a merge's recorded sequence would
 // otherwise carry the block Jacobi's ~1000 (mostly idle) launches.
@@ -1564,11 +1565,11 @@ __global__ __launch_bounds__(256) void bj_init_kernel(const double* __restrict__
 // (bj_next), which brings every index back to its own position after the
 // 63 rounds. Each wave forms the round's 32 rotations (a lane per pair, one
 // division and one rsqrt each) and shares them through its own LDS row; then
-// thread t takes pair column j = t % 32 and pair rows t / 32 + 8 u: it reads
+// thread t takes pair column j = t % 32 and pair rows t / 32 + 16 u: it reads
 // the 2 x 2 blocks of A at positions (2i, 2j) (bj_col: lanes read and write
 // contiguous doubles), writes R_i^T A_ij R_j (the row rotation first) to the moved
 // positions in the other copy of A, and applies R_j to the column pair at
-// positions (2j, 2j+1) of rows t / 32 + 8 v of Q (also double-buffered: the
+// positions (2j, 2j+1) of rows t / 32 + 16 v of Q (also double-buffered: the
 // columns move). One barrier per round.
 // The annihilating rotation of rot2 with one division: with d = aqq - app,
 // t = sign(d) 2 apq / (|d| + sqrt(d^2 + 4 apq^2)) (tau = d / (2 apq) cleared
@@ -1593,7 +1594,7 @@ __device__ __forceinline__ int bj_next(int x) {
   return x - 2;
 }
 
-__global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict__ S, int ld, double* Qbuf,
+__global__ __launch_bounds__(BJ_NT) void bj_solve_kernel(const double* __restrict__ S, int ld, double* Qbuf,
                                                        int32_t* st, double* smax, int r, int NB, double tol,
                                                        const int64_t* __restrict__ bd) {
   const int64_t bdel = bd ? bd[blockIdx.z] : 0;
@@ -1609,11 +1610,11 @@ __global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict_
   extern __shared__ double bj_lds[];
   double* Ab = bj_lds;            // [2][64][65]: A by position
   double* Qb = bj_lds + 2 * BUF;  // [2][64][65]: Q, columns by position
-  __shared__ double red[4];
+  __shared__ double red[BJ_NT / 64];
   const int t = threadIdx.x;
   double cmax = 0.0;
   const double floor_d = 0.01 * smax[1];
-  for (int e = t; e < BJ_P * BJ_P; e += 256) {
+  for (int e = t; e < BJ_P * BJ_P; e += BJ_NT) {
     const int i = e / BJ_P, j = e % BJ_P;
     const int gi = bj_gidx(i, a, b), gj = bj_gidx(j, a, b);
     const double v = (gi < m && gj < m) ? S[(size_t)gi * ld + gj] : 0.0;
@@ -1621,7 +1622,7 @@ __global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict_
     Qb[i * BJ_LD + bj_col(j)] = i == j ? 1.0 : 0.0;
   }
   __syncthreads();
-  for (int e = t; e < BJ_P * BJ_P; e += 256) {
+  for (int e = t; e < BJ_P * BJ_P; e += BJ_NT) {
     const int i = e / BJ_P, j = e % BJ_P;
     if (j > i) {
       const double den = fmax(sqrt(fabs(Ab[i * BJ_LD + bj_col(i)] * Ab[j * BJ_LD + bj_col(j)])), floor_d);
@@ -1635,12 +1636,14 @@ __global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict_
   if ((t & 63) == 0) red[t >> 6] = cmax;
   __syncthreads();
   if (t == 0) {
-    const double c = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+    double c = 0.0;
+    for (int w = 0; w < BJ_NT / 64; ++w) c = fmax(c, red[w]);
     atomicMax((unsigned long long*)smax, (unsigned long long)__double_as_longlong(c));
   }
-  const int jj = t & (BJ_B - 1), i0 = t >> 5, lane = t & 63, wave = t >> 6;
+  constexpr int IST = BJ_NT / BJ_B;  // pair rows (and Q rows) step between a thread's blocks
+  const int jj = t & (BJ_B - 1), i0 = t / BJ_B, lane = t & 63, wave = t >> 6;
   const int nj0 = bj_col(bj_next(2 * jj)), nj1 = bj_col(bj_next(2 * jj + 1));
-  __shared__ double csw[4][BJ_B], snw[4][BJ_B];
+  __shared__ double csw[BJ_NT / 64][BJ_B], snw[BJ_NT / 64][BJ_B];
   __shared__ int rotated;
   int cur = 0;
   for (int inner = 0; inner < BJ_INNER; ++inner) {
@@ -1672,10 +1675,11 @@ __global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict_
       // two copies share one LDS array, so a store would otherwise hold back
       // the loads after it)
       const double cj = csw[wave][jj], sj = snw[wave][jj];
-      double ci[4], si[4], x[4][4], vq[8][2];
+      constexpr int UA = BJ_B / IST, VQ = BJ_P / IST;
+      double ci[UA], si[UA], x[UA][4], vq[VQ][2];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + 8 * u;
+      for (int u = 0; u < UA; ++u) {
+        const int i = i0 + IST * u;
         ci[u] = csw[wave][i];
         si[u] = snw[wave][i];
         x[u][0] = A[(2 * i) * BJ_LD + jj];
@@ -1684,14 +1688,14 @@ __global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict_
         x[u][3] = A[(2 * i + 1) * BJ_LD + BJ_B + jj];
       }
 #pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        const int row = i0 + 8 * v;
+      for (int v = 0; v < VQ; ++v) {
+        const int row = i0 + IST * v;
         vq[v][0] = Qc[row * BJ_LD + jj];
         vq[v][1] = Qc[row * BJ_LD + BJ_B + jj];
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + 8 * u;
+      for (int u = 0; u < UA; ++u) {
+        const int i = i0 + IST * u;
         const double y11 = ci[u] * x[u][0] - si[u] * x[u][2], y21 = si[u] * x[u][0] + ci[u] * x[u][2];
         const double y12 = ci[u] * x[u][1] - si[u] * x[u][3], y22 = si[u] * x[u][1] + ci[u] * x[u][3];
         const int ni0 = bj_next(2 * i), ni1 = bj_next(2 * i + 1);
@@ -1701,8 +1705,8 @@ __global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict_
         An[ni1 * BJ_LD + nj1] = sj * y21 + cj * y22;
       }
 #pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        const int row = i0 + 8 * v;
+      for (int v = 0; v < VQ; ++v) {
+        const int row = i0 + IST * v;
         Qn[row * BJ_LD + nj0] = cj * vq[v][0] - sj * vq[v][1];
         Qn[row * BJ_LD + nj1] = sj * vq[v][0] + cj * vq[v][1];
       }
@@ -1720,7 +1724,7 @@ __global__ __launch_bounds__(256) void bj_solve_kernel(const double* __restrict_
   // whole sweeps only: every index is back at its own position
   const double* Qf = Qb + cur * BUF;
   double* Qo = Qbuf + (size_t)blockIdx.x * BJ_P * BJ_P;
-  for (int e = t; e < BJ_P * BJ_P; e += 256) Qo[e] = Qf[(e / BJ_P) * BJ_LD + bj_col(e % BJ_P)];
+  for (int e = t; e < BJ_P * BJ_P; e += BJ_NT) Qo[e] = Qf[(e / BJ_P) * BJ_LD + bj_col(e % BJ_P)];
 }
 
 // Row pass: S[I, j0 .. j0+63] <- Q^T S[I, j0 .. j0+63] for the pair's 64
@@ -1896,7 +1900,7 @@ int iskv_launch_core_eig(isvd_handle* h, double tol, int keep) {
                        h->bd);
     for (int sw = 0; sw < sweeps; ++sw) {
       for (int r = 0; r < NB - 1; ++r) {
-        hipLaunchKernelGGL(bj_solve_kernel, bz(dim3(NB / 2), h->bcount), dim3(256), bj_lds_bytes(), s, w.S, ld, w.Km,
+        hipLaunchKernelGGL(bj_solve_kernel, bz(dim3(NB / 2), h->bcount), dim3(BJ_NT), bj_lds_bytes(), s, w.S, ld, w.Km,
                            st, w.aux, r, NB, 1e-13, h->bd);
         hipLaunchKernelGGL(bj_rows_kernel, bz(dim3(NB / 2, tiles), h->bcount), dim3(256), 0, s, w.S, ld, w.Km, st, r,
                            NB, h->bd);
