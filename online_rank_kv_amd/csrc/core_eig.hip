@@ -1476,6 +1476,7 @@ constexpr int BJ_B = 32;          // block size
 constexpr int BJ_P = 2 * BJ_B;    // pair size
 constexpr int BJ_LD = BJ_P + 1;   // LDS row stride (doubles)
 constexpr int BJ_NT = 512;        // threads of a pair solve (8 waves: two per SIMD)
+constexpr int BJ_TW = 32;         // row / column tile of the row and column passes
 // Cores up to BJ_MIN_M keep the one-workgroup Jacobi: there the refinement
 // converges except in early merges, and a merge's recorded sequence would
 // otherwise carry the block Jacobi's ~1000 (mostly idle) launches.
@@ -1727,8 +1728,8 @@ __global__ __launch_bounds__(BJ_NT) void bj_solve_kernel(const double* __restric
   for (int e = t; e < BJ_P * BJ_P; e += BJ_NT) Qo[e] = Qf[(e / BJ_P) * BJ_LD + bj_col(e % BJ_P)];
 }
 
-// Row pass: S[I, j0 .. j0+63] <- Q^T S[I, j0 .. j0+63] for the pair's 64
-// indices I, on the fp64 matrix cores. Grid (pairs, column tiles).
+// Row pass: S[I, j0 .. j0+31] <- Q^T S[I, j0 .. j0+31] for the pair's 64
+// indices I, on the fp64 matrix cores. Grid (pairs, 32-column tiles).
 __global__ __launch_bounds__(256) void bj_rows_kernel(double* S, int ld, const double* __restrict__ Qbuf,
                                                       const int32_t* st, int r, int NB,
                                                       const int64_t* __restrict__ bd) {
@@ -1738,35 +1739,35 @@ __global__ __launch_bounds__(256) void bj_rows_kernel(double* S, int ld, const d
   st = iskv_rb(st, bdel);
   if (!bj_active(st)) return;
   const int m = st[ST_JM];
-  const int j0 = blockIdx.y * BJ_P;
+  const int j0 = blockIdx.y * BJ_TW;
   if (j0 >= m) return;
   int a, b;
   bj_pair(r, blockIdx.x, NB, &a, &b);
-  __shared__ double Qs[BJ_P][BJ_LD], X[BJ_P][BJ_LD];
+  __shared__ double Qs[BJ_P][BJ_LD], X[BJ_P][BJ_TW + 1];
   const double* Qp = Qbuf + (size_t)blockIdx.x * BJ_P * BJ_P;
   const int t = threadIdx.x;
-  for (int e = t; e < BJ_P * BJ_P; e += 256) {
-    const int i = e / BJ_P, j = e % BJ_P;
-    Qs[i][j] = Qp[e];
+  for (int e = t; e < BJ_P * BJ_P; e += 256) Qs[e / BJ_P][e % BJ_P] = Qp[e];
+  for (int e = t; e < BJ_P * BJ_TW; e += 256) {
+    const int i = e / BJ_TW, j = e % BJ_TW;
     const int gi = bj_gidx(i, a, b), gj = j0 + j;
     X[i][j] = (gi < m && gj < m) ? S[(size_t)gi * ld + gj] : 0.0;
   }
   __syncthreads();
-  // wave w: output rows 16 w .. 16 w + 15, all 64 columns, as four 16 x 16
-  // tiles on v_mfma_f64_16x16x4f64 (lane layout as in dgemm_kernel)
+  // wave w: output rows 16 w .. 16 w + 15 and the tile's 32 columns, as two
+  // 16 x 16 tiles on v_mfma_f64_16x16x4f64 (lane layout as in dgemm_kernel)
   const int lane = t & 63, w = t >> 6, rl = lane & 15, g = lane >> 4;
-  v4d acc[4];
+  v4d acc[2];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) acc[u] = v4d{0.0, 0.0, 0.0, 0.0};
+  for (int u = 0; u < 2; ++u) acc[u] = v4d{0.0, 0.0, 0.0, 0.0};
 #pragma unroll 4
   for (int kk = 0; kk < BJ_P / 4; ++kk) {
     const double av = Qs[4 * kk + g][16 * w + rl];  // (Q^T)[16 w + rl][4 kk + g]
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 2; ++u)
       acc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, X[4 * kk + g][16 * u + rl], acc[u], 0, 0, 0);
   }
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < 2; ++u) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 16 * w + g + 4 * e, j = 16 * u + rl;
@@ -1777,7 +1778,7 @@ __global__ __launch_bounds__(256) void bj_rows_kernel(double* S, int ld, const d
 }
 
 // Column pass: S[i, I] <- S[i, I] Q and V[i, I] <- V[i, I] Q for rows
-// i0 .. i0+63, on the fp64 matrix cores. Grid (pairs, row tiles).
+// i0 .. i0+31, on the fp64 matrix cores. Grid (pairs, 32-row tiles).
 __global__ __launch_bounds__(256) void bj_cols_kernel(double* S, double* V, int ld, const double* __restrict__ Qbuf,
                                                       const int32_t* st, int r, int NB,
                                                       const int64_t* __restrict__ bd) {
@@ -1788,43 +1789,45 @@ __global__ __launch_bounds__(256) void bj_cols_kernel(double* S, double* V, int 
   st = iskv_rb(st, bdel);
   if (!bj_active(st)) return;
   const int m = st[ST_JM];
-  const int i0 = blockIdx.y * BJ_P;
+  const int i0 = blockIdx.y * BJ_TW;
   if (i0 >= m) return;
   int a, b;
   bj_pair(r, blockIdx.x, NB, &a, &b);
   // Q and both row tiles are staged at once, so their loads are in flight together
-  __shared__ double Qs[BJ_P][BJ_LD], X[2][BJ_P][BJ_LD];
+  __shared__ double Qs[BJ_P][BJ_LD], X[2][BJ_TW][BJ_LD];
   const double* Qp = Qbuf + (size_t)blockIdx.x * BJ_P * BJ_P;
   const int t = threadIdx.x;
-  for (int e = t; e < BJ_P * BJ_P; e += 256) {
+  for (int e = t; e < BJ_P * BJ_P; e += 256) Qs[e / BJ_P][e % BJ_P] = Qp[e];
+  for (int e = t; e < BJ_TW * BJ_P; e += 256) {
     const int i = e / BJ_P, j = e % BJ_P;
     const int gi = i0 + i, gj = bj_gidx(j, a, b);
     const bool in = gi < m && gj < m;
-    Qs[i][j] = Qp[e];
     X[0][i][j] = in ? S[(size_t)gi * ld + gj] : 0.0;
     X[1][i][j] = in ? V[(size_t)gi * ld + gj] : 0.0;
   }
   __syncthreads();
+  // wave w: rows 16 (w % 2) .. + 15 and columns 32 (w / 2) .. + 31 of X Q, as
+  // two 16 x 16 MFMA tiles
   const int lane = t & 63, w = t >> 6, rl = lane & 15, g = lane >> 4;
+  const int rw = 16 * (w & 1), cu = 2 * (w >> 1);
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     double* M = pass == 0 ? S : V;
-    // wave w: rows 16 w .. 16 w + 15 of X Q as four 16 x 16 MFMA tiles
-    v4d acc[4];
+    v4d acc[2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc[u] = v4d{0.0, 0.0, 0.0, 0.0};
+    for (int u = 0; u < 2; ++u) acc[u] = v4d{0.0, 0.0, 0.0, 0.0};
 #pragma unroll 4
     for (int kk = 0; kk < BJ_P / 4; ++kk) {
-      const double av = X[pass][16 * w + rl][4 * kk + g];
+      const double av = X[pass][rw + rl][4 * kk + g];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        acc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, Qs[4 * kk + g][16 * u + rl], acc[u], 0, 0, 0);
+      for (int u = 0; u < 2; ++u)
+        acc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, Qs[4 * kk + g][16 * (cu + u) + rl], acc[u], 0, 0, 0);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 2; ++u) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int gi = i0 + 16 * w + g + 4 * e, gj = bj_gidx(16 * u + rl, a, b);
+        const int gi = i0 + rw + g + 4 * e, gj = bj_gidx(16 * (cu + u) + rl, a, b);
         if (gi < m && gj < m) M[(size_t)gi * ld + gj] = acc[u][e];
       }
     }
@@ -1892,7 +1895,7 @@ int iskv_launch_core_eig(isvd_handle* h, double tol, int keep) {
   const int nblk = (mm + 15) / 16;
   const size_t lds = sizeof(AnalyzeLds);
   const int NB = ((mm + BJ_B - 1) / BJ_B + 1) & ~1;
-  const int tiles = (mm + BJ_P - 1) / BJ_P;
+  const int tiles = (mm + BJ_TW - 1) / BJ_TW;
   // block Jacobi: Km (free once the refinement has ended) holds the pairs'
   // rotations, aux[0] the sweep's largest coupling
   auto block_jacobi = [&](int sweeps) {
