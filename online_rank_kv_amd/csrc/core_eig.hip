@@ -1555,7 +1555,8 @@ __global__ __launch_bounds__(256) void bj_init_kernel(const double* __restrict__
   }
 }
 
-// One cyclic sweep on the 64 x 64 subproblem of pair p (grid.x) in round r;
+// bj_solve_kernel (after its helpers below): one cyclic sweep on the 64 x 64
+// subproblem of pair p (grid.x) in round r;
 // Q (64 x 64, row-major) to Qbuf[p]. The largest scaled coupling found,
 // |s_ij| / max(sqrt(|s_ii s_jj|), 0.01 max_i |s_ii|) (relative, with an
 // absolute floor at the rounding level of the largest entries), goes to
@@ -1571,7 +1572,8 @@ __global__ __launch_bounds__(256) void bj_init_kernel(const double* __restrict__
 // contiguous doubles), writes R_i^T A_ij R_j (the row rotation first) to the moved
 // positions in the other copy of A, and applies R_j to the column pair at
 // positions (2j, 2j+1) of rows t / 32 + 16 v of Q (also double-buffered: the
-// columns move). One barrier per round.
+// columns move). One barrier per round, 8 waves (two per SIMD).
+
 // The annihilating rotation of rot2 with one division: with d = aqq - app,
 // t = sign(d) 2 apq / (|d| + sqrt(d^2 + 4 apq^2)) (tau = d / (2 apq) cleared
 // from rot2's t = sign(tau) / (|tau| + sqrt(1 + tau^2))), c = 1 / sqrt(1 + t^2).
