@@ -1476,7 +1476,7 @@ constexpr int BJ_B = 32;          // block size
 constexpr int BJ_P = 2 * BJ_B;    // pair size
 constexpr int BJ_LD = BJ_P + 1;   // LDS row stride (doubles)
 constexpr int BJ_NT = 512;        // threads of a pair solve (8 waves: two per SIMD)
-constexpr int BJ_TW = 32;         // row / column tile of the row and column passes
+constexpr int BJ_TW = 16;         // row / column tile of the row and column passes (16 or 32)
 // Cores up to BJ_MIN_M keep the one-workgroup Jacobi: there the refinement
 // converges except in early merges, and a merge's recorded sequence would
 // otherwise carry the block Jacobi's ~1000 (mostly idle) launches.
@@ -1730,8 +1730,8 @@ __global__ __launch_bounds__(BJ_NT) void bj_solve_kernel(const double* __restric
   for (int e = t; e < BJ_P * BJ_P; e += BJ_NT) Qo[e] = Qf[(e / BJ_P) * BJ_LD + bj_col(e % BJ_P)];
 }
 
-// Row pass: S[I, j0 .. j0+31] <- Q^T S[I, j0 .. j0+31] for the pair's 64
-// indices I, on the fp64 matrix cores. Grid (pairs, 32-column tiles).
+// Row pass: S[I, j0 .. j0+BJ_TW) <- Q^T S[I, j0 .. j0+BJ_TW) for the pair's 64
+// indices I, on the fp64 matrix cores. Grid (pairs, column tiles).
 __global__ __launch_bounds__(256) void bj_rows_kernel(double* S, int ld, const double* __restrict__ Qbuf,
                                                       const int32_t* st, int r, int NB,
                                                       const int64_t* __restrict__ bd) {
@@ -1755,21 +1755,22 @@ __global__ __launch_bounds__(256) void bj_rows_kernel(double* S, int ld, const d
     X[i][j] = (gi < m && gj < m) ? S[(size_t)gi * ld + gj] : 0.0;
   }
   __syncthreads();
-  // wave w: output rows 16 w .. 16 w + 15 and the tile's 32 columns, as two
-  // 16 x 16 tiles on v_mfma_f64_16x16x4f64 (lane layout as in dgemm_kernel)
+  // wave w: output rows 16 w .. 16 w + 15 and the tile's columns, as 16 x 16
+  // tiles on v_mfma_f64_16x16x4f64 (lane layout as in dgemm_kernel)
   const int lane = t & 63, w = t >> 6, rl = lane & 15, g = lane >> 4;
-  v4d acc[2];
+  constexpr int TPW = BJ_TW / 16;  // 16 x 16 tiles per wave
+  v4d acc[TPW];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) acc[u] = v4d{0.0, 0.0, 0.0, 0.0};
+  for (int u = 0; u < TPW; ++u) acc[u] = v4d{0.0, 0.0, 0.0, 0.0};
 #pragma unroll 4
   for (int kk = 0; kk < BJ_P / 4; ++kk) {
     const double av = Qs[4 * kk + g][16 * w + rl];  // (Q^T)[16 w + rl][4 kk + g]
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < TPW; ++u)
       acc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, X[4 * kk + g][16 * u + rl], acc[u], 0, 0, 0);
   }
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < TPW; ++u) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 16 * w + g + 4 * e, j = 16 * u + rl;
@@ -1780,7 +1781,7 @@ __global__ __launch_bounds__(256) void bj_rows_kernel(double* S, int ld, const d
 }
 
 // Column pass: S[i, I] <- S[i, I] Q and V[i, I] <- V[i, I] Q for rows
-// i0 .. i0+31, on the fp64 matrix cores. Grid (pairs, 32-row tiles).
+// i0 .. i0+BJ_TW-1, on the fp64 matrix cores. Grid (pairs, row tiles).
 __global__ __launch_bounds__(256) void bj_cols_kernel(double* S, double* V, int ld, const double* __restrict__ Qbuf,
                                                       const int32_t* st, int r, int NB,
                                                       const int64_t* __restrict__ bd) {
@@ -1808,25 +1809,25 @@ __global__ __launch_bounds__(256) void bj_cols_kernel(double* S, double* V, int 
     X[1][i][j] = in ? V[(size_t)gi * ld + gj] : 0.0;
   }
   __syncthreads();
-  // wave w: rows 16 (w % 2) .. + 15 and columns 32 (w / 2) .. + 31 of X Q, as
-  // two 16 x 16 MFMA tiles
+  // the tile's rows of X Q as 16 x 16 MFMA tiles, the same number per wave
   const int lane = t & 63, w = t >> 6, rl = lane & 15, g = lane >> 4;
-  const int rw = 16 * (w & 1), cu = 2 * (w >> 1);
+  constexpr int TPW = BJ_TW / 16;  // 16 x 16 tiles per wave
+  const int rw = 16 * (w % TPW), cu = TPW * (w / TPW);
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     double* M = pass == 0 ? S : V;
-    v4d acc[2];
+    v4d acc[TPW];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) acc[u] = v4d{0.0, 0.0, 0.0, 0.0};
+    for (int u = 0; u < TPW; ++u) acc[u] = v4d{0.0, 0.0, 0.0, 0.0};
 #pragma unroll 4
     for (int kk = 0; kk < BJ_P / 4; ++kk) {
       const double av = X[pass][rw + rl][4 * kk + g];
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < TPW; ++u)
         acc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, Qs[4 * kk + g][16 * (cu + u) + rl], acc[u], 0, 0, 0);
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < TPW; ++u) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int gi = i0 + rw + g + 4 * e, gj = bj_gidx(16 * (cu + u) + rl, a, b);
